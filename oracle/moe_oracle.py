@@ -1,0 +1,310 @@
+"""CPU oracle: the sparse MoE FFN layer forward and its balance statistics, in float64.
+
+TEST INFRASTRUCTURE ONLY. This module is the checker, not the product: only the test suite,
+the package smoke check and the benchmark's CPU-baseline leg may import or call it. It shares no
+code with the HIP library (no kernels, headers, helpers or tables); both sides are fed the same
+seeded inputs from the ``workloads`` module, which holds no arithmetic of the method.
+
+It computes the plain definitions, one step per function, in the notation of the source pages:
+
+  [ATLAS]  "MoE：条件计算与路由" (llm-knowledge-atlas.pages.dev, notes 04-04)
+  [AIATTN] "深入理解 MoE (混合专家模型)：稀疏激活与高效扩展" (aiattnstudio.link)
+  [CMP]    "MOE大模型对比篇" (llm.jiangnianmeng.cn)
+  [CSDN]   the adg.csdn.net MoE notes page (§四 "Deepseek MoE代码")
+  [T4]     "MoE" (t4mako.github.io)
+
+Readings taken where the pages are silent or disagree (each is repeated at the function that
+uses it):
+
+  * Top-k ties go to the lower expert index; slots are ordered by descending selection score.
+  * The load-balancing bias b_e is added to the softmax probability g_e and used only to pick the
+    experts; the gates come from the unbiased g, renormalised over the chosen set.
+  * f_e = n_e / (k T), so that sum_e f_e = 1 for any k and f_e is the argmax fraction at k = 1.
+  * P_e is the mean of the full (unmasked, unbiased) softmax probability.
+  * z = (1/T) sum_t (ln sum_e exp l_te)^2, natural log, raw logits, no coefficient.
+  * Capacity C = ceil(c k T / E) evaluated in float64 as ((c * k) * T) / E; overflow is decided in
+    ascending token order jointly over all k slots (first come, first kept); dropped slots add
+    nothing and the surviving gates are not renormalised again.
+  * Within an expert's segment, rows are in ascending token order (a stable sort by expert).
+  * S shared experts take the same x as the router, are added with weight 1, and are summed.
+  * Bias update: b_e <- b_e + gamma * sign(k T / E - n_e), sign(0) = 0, done in float32.
+
+Every function here is pinned by the CPU tests against closed forms, invariants, brute force or an
+independent formula from the pages.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+
+def _f64(a) -> np.ndarray:
+    """Host float64 copy of an array or torch tensor (bf16 inputs are upcast exactly)."""
+    if hasattr(a, "detach"):
+        a = a.detach().to("cpu")
+        if str(a.dtype) == "torch.bfloat16":
+            a = a.float()
+        a = a.numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------------------------
+# Router: [ATLAS] §原理与演进 "Router 如何让参数多、每 token 计算少": g(x) = softmax(W_r x)
+# ---------------------------------------------------------------------------------------------
+
+def router_logits(x: np.ndarray, W_r: np.ndarray) -> np.ndarray:
+    """l[t, e] = sum_i x[t, i] * W_r[e, i]  (the router projection W_r x, no bias term). [T, E]"""
+    return _f64(x) @ _f64(W_r).T
+
+
+def softmax_lse(l: np.ndarray):
+    """Max-subtracted softmax over experts and its log-sum-exp.
+
+    m_t = max_e l_te;  lse_t = m_t + ln sum_e exp(l_te - m_t);  g_te = exp(l_te - lse_t).
+    The max subtraction is the stability device of [T4] §训练不稳定 (2. 舍入误差); lse_t is the
+    inner term of the router z-loss of [CMP] §2.2.
+    Returns (g [T, E], lse [T]).
+    """
+    l = _f64(l)
+    m = l.max(axis=1, keepdims=True)
+    lse = m[:, 0] + np.log(np.exp(l - m).sum(axis=1))
+    g = np.exp(l - lse[:, None])
+    return g, lse
+
+
+def selection_scores(g: np.ndarray, b: Optional[np.ndarray]) -> np.ndarray:
+    """s_te = g_te + b_e ([ATLAS] §无辅助损失负载均衡（ALF-LB）: the per-expert bias is applied to
+    the routing score before Top-K); s = g when there is no bias."""
+    g = _f64(g)
+    if b is None:
+        return g.copy()
+    return g + _f64(b)[None, :]
+
+
+def top_k(s: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest s_te per token, ordered by descending score, ties to the lower
+    expert index ([ATLAS] §7 eq. (1) S = TopK(g(x))). A stable sort of -s along experts keeps
+    equal scores in ascending index order. [T, k] int64."""
+    s = _f64(s)
+    order = np.argsort(-s, axis=1, kind="stable")
+    return order[:, :k].astype(np.int64)
+
+
+def topk_margin(s: np.ndarray, k: int) -> np.ndarray:
+    """Gap between the k-th and (k+1)-th largest selection score per token (inf when k == E)."""
+    s = _f64(s)
+    if k >= s.shape[1]:
+        return np.full(s.shape[0], np.inf)
+    srt = -np.sort(-s, axis=1)
+    return srt[:, k - 1] - srt[:, k]
+
+
+def gate_weights(g: np.ndarray, S: np.ndarray, renorm: bool = True) -> np.ndarray:
+    """Gates of the chosen experts from the UNBIASED g: w_tj = g[t, S_tj], divided by
+    sum_j' g[t, S_tj'] when renormalising ([ATLAS] §7 eq. (2) g~_e = g_e / sum_{j in S} g_j).
+    [T, k]"""
+    g = _f64(g)
+    w = np.take_along_axis(g, S, axis=1)
+    if renorm:
+        w = w / w.sum(axis=1, keepdims=True)
+    return w
+
+
+# ---------------------------------------------------------------------------------------------
+# Loads and capacity: [ATLAS] §1 (n_e) and §3 (C = ceil(c B k / E))
+# ---------------------------------------------------------------------------------------------
+
+def expert_loads(S: np.ndarray, E: int) -> np.ndarray:
+    """n_e = sum_t 1[e in S_t] ([ATLAS] §1 "容量与激活计算为什么能分离"), before capacity. [E] int64"""
+    n = np.zeros(E, dtype=np.int64)
+    for e in S.reshape(-1):
+        n[int(e)] += 1
+    return n
+
+
+def capacity(c: Optional[float], k: int, T: int, E: int) -> Optional[int]:
+    """C = ceil(c B k / E) of [ATLAS] §3 (B = T tokens), in float64 as ((c*k)*T)/E with c taken as
+    the float32 value the caller passes. None (no limit) when c is None or c <= 0."""
+    if c is None:
+        return None
+    c32 = float(np.float32(c))
+    if c32 <= 0.0:
+        return None
+    return int(math.ceil(((c32 * k) * T) / E))
+
+
+def dispatch(S: np.ndarray, E: int, C: Optional[int]):
+    """Expert-contiguous placement of the (token, slot) assignments with capacity dropping.
+
+    For expert e, the tokens that chose it are listed in ascending token order; the assignment's
+    position p(t, e) is its index in that list and it is kept iff p < C. Kept assignments of e fill
+    rows off_e .. off_e + kept_e - 1 in that order, off_e = sum_{e' < e} kept_e'. This follows the
+    token-major flattening and per-expert truncation of [CSDN] §四 (the demo MoE's expert loop
+    with its capacity check) and the histogram-then-sort placement of its DeepseekV3MoE.moe_infer.
+
+    Returns dict with pos [T,k], row [T,k] (-1 = dropped), kept [E], overflow [E], offsets [E+1],
+    perm_token [P_kept].
+    """
+    T, k = S.shape
+    lists = [[] for _ in range(E)]          # (t, j) in ascending t for each expert
+    for t in range(T):
+        for j in range(k):
+            lists[int(S[t, j])].append((t, j))
+    pos = np.full((T, k), -1, dtype=np.int64)
+    kept = np.zeros(E, dtype=np.int64)
+    for e in range(E):
+        for p, (t, j) in enumerate(lists[e]):
+            pos[t, j] = p
+        kept[e] = len(lists[e]) if C is None else min(len(lists[e]), C)
+    n = np.array([len(l) for l in lists], dtype=np.int64)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(kept)
+    row = np.full((T, k), -1, dtype=np.int64)
+    perm_token = np.full(int(offsets[-1]), -1, dtype=np.int64)
+    for e in range(E):
+        for p, (t, j) in enumerate(lists[e]):
+            if p < kept[e]:
+                r = offsets[e] + p
+                row[t, j] = r
+                perm_token[r] = t
+    return {"pos": pos, "row": row, "kept": kept, "overflow": n - kept,
+            "offsets": offsets, "perm_token": perm_token}
+
+
+# ---------------------------------------------------------------------------------------------
+# Experts: [AIATTN] §10.2 与 SwiGLU 的结合 / §11: SwiGLU(x) = SiLU(W_1 x) ⊙ (W_3 x), then W_2
+# ---------------------------------------------------------------------------------------------
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z / (1 + exp(-z))."""
+    z = _f64(z)
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu_expert(X: np.ndarray, W_gate: np.ndarray, W_up: np.ndarray, W_down: np.ndarray) -> np.ndarray:
+    """E_e(X) = W_down (SiLU(W_gate X) ⊙ (W_up X)) for rows X [n, d]; W_gate, W_up [M, d]
+    (W_1 and W_3 of the page), W_down [d, M] (W_2); no biases. Returns [n, d]."""
+    X = _f64(X)
+    G = X @ _f64(W_gate).T
+    U = X @ _f64(W_up).T
+    h = silu(G) * U
+    return h @ _f64(W_down).T
+
+
+def shared_experts(x: np.ndarray, shared: Sequence) -> np.ndarray:
+    """sum_s E^s(x) over the S shared experts, each applied to every token with weight 1
+    ([CMP] §3.3 shared-expert isolation; [CSDN] §四 DeepseekV3MoE adds shared_experts(identity)
+    to the routed output)."""
+    x = _f64(x)
+    out = np.zeros_like(x)
+    for Wg, Wu, Wd in shared:
+        out += swiglu_expert(x, Wg, Wu, Wd)
+    return out
+
+
+def combine(T: int, d: int, row: np.ndarray, w: np.ndarray, out_perm: np.ndarray,
+            shared_out: Optional[np.ndarray] = None) -> np.ndarray:
+    """y_t = sum_{j : row_tj >= 0} w_tj * out_perm[row_tj] (+ shared_t)  ([ATLAS] §7 eq. (3))."""
+    y = np.zeros((T, d)) if shared_out is None else _f64(shared_out).copy()
+    for t in range(T):
+        for j in range(row.shape[1]):
+            r = int(row[t, j])
+            if r >= 0:
+                y[t] += w[t, j] * out_perm[r]
+    return y
+
+
+# ---------------------------------------------------------------------------------------------
+# Balance statistics and the loss-free-balancing bias update
+# ---------------------------------------------------------------------------------------------
+
+def balance_stats(n: np.ndarray, g: np.ndarray, lse: np.ndarray, k: int, lam: float):
+    """f_e = n_e / (k T);  P_e = (1/T) sum_t g_te;  aux = lambda * E * sum_e f_e P_e
+    ([ATLAS] §原理与演进, L_balance = lambda E sum_e f_e P_e; [AIATTN] §4.2.1; [CMP] §2.1);
+    z = (1/T) sum_t lse_t^2 ([CMP] §2.2 z-loss L_z). Returns dict of float64 values."""
+    g = _f64(g)
+    T, E = g.shape
+    f = _f64(n) / float(k * T)
+    P = g.sum(axis=0) / float(T)
+    aux = float(lam) * E * float((f * P).sum())
+    z = float((_f64(lse) ** 2).sum() / float(T))
+    return {"f": f, "P": P, "aux": aux, "z": z}
+
+
+def bias_update(b: np.ndarray, n: np.ndarray, k: int, T: int, gamma: float) -> np.ndarray:
+    """b_e <- b_e + gamma * sign(k T / E - n_e) in float32: an overloaded expert's bias goes down,
+    an underloaded one's goes up ([ATLAS] §无辅助损失负载均衡（ALF-LB）), sign(0) = 0."""
+    b32 = np.asarray(b, dtype=np.float32)
+    E = b32.shape[0]
+    mean_load = (k * T) / E
+    sgn = np.sign(mean_load - _f64(n)).astype(np.float32)
+    return (b32 + np.float32(gamma) * sgn).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------------------------
+# The whole layer
+# ---------------------------------------------------------------------------------------------
+
+def route(x, W_r, k: int, b=None, renorm: bool = True):
+    """Router stage for all tokens: logits, softmax, selection, gates and margins."""
+    l = router_logits(x, W_r)
+    g, lse = softmax_lse(l)
+    s = selection_scores(g, b)
+    S = top_k(s, k)
+    w = gate_weights(g, S, renorm)
+    return {"logits": l, "g": g, "lse": lse, "s": s, "topk_idx": S, "topk_w": w,
+            "margin": topk_margin(s, k)}
+
+
+def layer_forward(x, W_r, W_gate, W_up, W_down, k: int, b=None, shared=(), c=None,
+                  renorm: bool = True, lam: float = 0.01, gamma: float = 1e-3,
+                  topk_idx=None, tokens=None, expert_weights=None):
+    """y = sum_{e in S_t} w_te E_e(x_t) + sum_s E^s(x_t), plus loads, drops and statistics.
+
+    ``topk_idx`` (optional) replaces the oracle's own selection by a given one (to check the stages
+    after routing on exactly the assignments another implementation made); ``tokens`` (optional)
+    restricts y to those token indices (y_t depends on token t alone once dispatch is fixed);
+    ``expert_weights`` (optional) is a callable e -> (W_gate_e, W_up_e, W_down_e) used instead of
+    indexing the full weight tensors.
+    """
+    x64 = _f64(x)
+    T, d = x64.shape
+    r = route(x64, W_r, k, b, renorm)
+    E = r["g"].shape[1]
+    S = r["topk_idx"] if topk_idx is None else np.asarray(topk_idx, dtype=np.int64)
+    w = gate_weights(r["g"], S, renorm)
+    n = expert_loads(S, E)
+    C = capacity(c, k, T, E)
+    dsp = dispatch(S, E, C)
+    stats = balance_stats(n, r["g"], r["lse"], k, lam)
+    want = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    want_set = set(int(t) for t in want)
+    # expert outputs for the kept rows of the wanted tokens only
+    out_perm = {}
+    for e in range(E):
+        rows_e = [(int(dsp["offsets"][e]) + p, int(dsp["perm_token"][dsp["offsets"][e] + p]))
+                  for p in range(int(dsp["kept"][e]))]
+        rows_e = [(rr, t) for rr, t in rows_e if t in want_set]
+        if not rows_e:
+            continue
+        We = expert_weights(e) if expert_weights is not None else (W_gate[e], W_up[e], W_down[e])
+        X = x64[[t for _, t in rows_e]]
+        O = swiglu_expert(X, *We)
+        for i, (rr, _) in enumerate(rows_e):
+            out_perm[rr] = O[i]
+    y = np.zeros((len(want), d))
+    xs = x64[want]
+    if shared:
+        y += shared_experts(xs, shared)
+    for i, t in enumerate(want):
+        for j in range(k):
+            rr = int(dsp["row"][t, j])
+            if rr >= 0:
+                y[i] += w[t, j] * out_perm[rr]
+    res = {"y": y, "tokens": want, "topk_idx": S, "topk_w": w, "n": n, "C": C, **dsp, **stats,
+           "lse": r["lse"], "g": r["g"], "margin": r["margin"], "s": r["s"]}
+    if b is not None:
+        res["b_new"] = bias_update(b, n, k, T, gamma)
+    return res

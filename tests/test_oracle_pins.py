@@ -1,0 +1,440 @@
+"""Pins of the CPU oracle against what the source pages and mathematics fix (no GPU needed).
+
+Each test checks one oracle step against something other than the oracle itself: a closed form,
+an invariant the pages' formulas imply, brute force on tiny inputs, an independent formula from a
+page, or a library routine. ``test_planted_mistakes_are_caught`` plants plausible mistakes in the
+oracle and checks that these pins fail on each.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import moe_oracle as O
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")))
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# ------------------------------------------------------------------------------------- softmax
+
+def check_softmax(mod=O):
+    l = _rand((64, 12), 1, 3.0)
+    g, lse = mod.softmax_lse(l)
+    assert np.allclose(g.sum(1), 1.0, atol=1e-14)
+    # scipy's logsumexp is an independent library routine
+    from scipy.special import logsumexp
+    assert np.allclose(lse, logsumexp(l, axis=1), atol=1e-13, rtol=0)
+    # each probability against math.exp on one row, in plain Python
+    row = [float(v) for v in l[5]]
+    den = sum(math.exp(v) for v in row)
+    assert np.allclose(g[5], [math.exp(v) / den for v in row], rtol=1e-13)
+    # zero router => uniform probabilities, lse = ln E
+    g0, lse0 = mod.softmax_lse(np.zeros((3, 8)))
+    assert np.allclose(g0, 1.0 / 8, rtol=1e-15, atol=0) and np.allclose(lse0, math.log(8), rtol=1e-15)
+    # constant logits a => lse = a + ln E; huge logits stay finite (max subtraction)
+    g1, lse1 = mod.softmax_lse(np.full((2, 5), 1000.0))
+    assert np.allclose(lse1, 1000.0 + math.log(5), rtol=1e-15) and np.all(np.isfinite(g1))
+
+
+def test_softmax_pins():
+    check_softmax()
+
+
+# --------------------------------------------------------------------------------------- top-k
+
+def _topk_repeated_argmax(s_row, k):
+    """k rounds of 'take the largest remaining score, lowest index on ties' in plain Python."""
+    left = list(range(len(s_row)))
+    out = []
+    for _ in range(k):
+        best = left[0]
+        for e in left[1:]:
+            if s_row[e] > s_row[best]:
+                best = e
+        out.append(best)
+        left.remove(best)
+    return out
+
+
+def check_topk(mod=O):
+    rng = np.random.default_rng(2)
+    # scores on a coarse grid so that ties are frequent
+    s = rng.integers(0, 5, size=(200, 7)).astype(np.float64) / 4.0
+    for k in (1, 2, 3, 7):
+        S = mod.top_k(s, k)
+        for t in range(s.shape[0]):
+            assert list(S[t]) == _topk_repeated_argmax(list(s[t]), k)
+    # exhaustive over k-subsets on distinct scores: the top-k set maximises the score sum
+    s = rng.permutation(np.arange(6 * 40, dtype=np.float64)).reshape(40, 6)
+    for k in (1, 2, 3, 4):
+        S = mod.top_k(s, k)
+        for t in range(s.shape[0]):
+            best = max(itertools.combinations(range(6), k), key=lambda c: sum(s[t, list(c)]))
+            assert set(S[t]) == set(best)
+            assert all(s[t, S[t, j]] > s[t, S[t, j + 1]] for j in range(k - 1))
+    # library: torch.topk on distinct scores
+    s = _rand((50, 16), 3)
+    vals, idx = torch.topk(torch.from_numpy(s), 4, dim=1)
+    assert np.array_equal(mod.top_k(s, 4), idx.numpy())
+
+
+def test_topk_pins():
+    check_topk()
+
+
+def test_topk_margin():
+    s = np.array([[0.5, 0.1, 0.3, 0.2], [0.25, 0.25, 0.25, 0.25]])
+    assert np.allclose(O.topk_margin(s, 2), [0.1, 0.0])
+    assert np.all(np.isinf(O.topk_margin(s, 4)))
+
+
+# ---------------------------------------------------------------------------------- gates/renorm
+
+def check_gates(mod=O):
+    l = _rand((100, 10), 4, 2.0)
+    g, _ = mod.softmax_lse(l)
+    S = mod.top_k(g, 3)
+    w = mod.gate_weights(g, S, True)
+    assert np.allclose(w.sum(1), 1.0, atol=1e-14)
+    # "Softmax(TopK(W_g x, k))" with the others set to -inf ([AIATTN] §2.2): an independent form
+    masked = np.full_like(l, -np.inf)
+    np.put_along_axis(masked, S, np.take_along_axis(l, S, 1), 1)
+    ref = np.exp(masked - masked.max(1, keepdims=True))
+    ref /= ref.sum(1, keepdims=True)
+    assert np.allclose(w, np.take_along_axis(ref, S, 1), rtol=1e-13)
+    # without renormalisation the gates are the raw probabilities
+    assert np.array_equal(mod.gate_weights(g, S, False), np.take_along_axis(g, S, 1))
+
+
+def test_gate_pins():
+    check_gates()
+
+
+# --------------------------------------------------------------------------------- statistics
+
+def check_stats(mod=O):
+    T, E, lam = 96, 6, 0.01
+    l = _rand((T, E), 5)
+    g, lse = mod.softmax_lse(l)
+    for k in (1, 2, 3):
+        S = mod.top_k(g, k)
+        n = mod.expert_loads(S, E)
+        st = mod.balance_stats(n, g, lse, k, lam)
+        assert abs(st["f"].sum() - 1.0) < 1e-14 and abs(st["P"].sum() - 1.0) < 1e-14
+        assert n.sum() == k * T
+        if k == 1:  # the argmax-fraction form of [AIATTN] §4.2.1 and [CMP] §2.1
+            am = np.argmax(g, axis=1)
+            assert np.allclose(st["f"], [(am == e).mean() for e in range(E)])
+        # P_e against a plain Python mean of the column
+        assert math.isclose(st["P"][2], sum(float(v) for v in g[:, 2]) / T, rel_tol=1e-13)
+    # zero router: P uniform => aux = lambda exactly; z = (ln E)^2
+    g0, lse0 = mod.softmax_lse(np.zeros((40, 8)))
+    S0 = mod.top_k(g0, 2)
+    st0 = mod.balance_stats(mod.expert_loads(S0, 8), g0, lse0, 2, GOLDEN["uniform_router_aux"]["lambda"])
+    assert math.isclose(st0["aux"], GOLDEN["uniform_router_aux"]["aux"], rel_tol=1e-14)
+    assert math.isclose(st0["z"], GOLDEN["uniform_router_z"]["z"], rel_tol=1e-14)
+    # uniform loads by construction (token t prefers experts t%E and (t+1)%E) => aux = lambda
+    T2, E2, k2 = 48, 6, 2
+    l2 = np.zeros((T2, E2))
+    for t in range(T2):
+        l2[t, t % E2] = 3.0 + 0.1 * (t % 5)
+        l2[t, (t + 1) % E2] = 2.0
+    g2, lse2 = mod.softmax_lse(l2)
+    S2 = mod.top_k(g2, k2)
+    n2 = mod.expert_loads(S2, E2)
+    assert np.all(n2 == k2 * T2 // E2)
+    st2 = mod.balance_stats(n2, g2, lse2, k2, 0.01)
+    assert math.isclose(st2["aux"], 0.01, rel_tol=1e-14)
+
+
+def test_stats_pins():
+    check_stats()
+
+
+# ----------------------------------------------------------------------------- capacity/dispatch
+
+def test_capacity_closed_forms():
+    c = GOLDEN["capacity_skewed"]
+    assert O.capacity(c["c"], c["k"], c["T"], c["E"]) == c["C"]
+    c = GOLDEN["capacity_ceil"]
+    assert O.capacity(c["c"], c["k"], c["T"], c["E"]) == c["C"]
+    assert O.capacity(None, 2, 10, 3) is None and O.capacity(0.0, 2, 10, 3) is None
+    # c is the float32 the caller passes: fp32(0.05) is just above 0.05, so 0.05*2*40/4 rounds up to 2
+    assert O.capacity(0.05, 2, 40, 4) == 2 and O.capacity(0.03125, 2, 40, 4) == 1
+    cfg = workloads.CONFIGS["skewed_capacity"]
+    assert O.capacity(cfg.c, cfg.k, cfg.T, cfg.E) == GOLDEN["capacity_skewed"]["C"]
+
+
+def _counter_simulation(S, E, C):
+    """Sequential first-come-first-kept: walk tokens ascending, one counter per expert."""
+    T, k = S.shape
+    cnt = [0] * E
+    keep = np.zeros((T, k), dtype=bool)
+    for t in range(T):
+        for j in range(k):
+            e = int(S[t, j])
+            cnt[e] += 1
+            keep[t, j] = C is None or cnt[e] <= C
+    return keep, np.array(cnt)
+
+
+def _check_dispatch_against_simulation(mod, S, E, C):
+    dsp = mod.dispatch(S, E, C)
+    keep, n = _counter_simulation(S, E, C)
+    assert np.array_equal(dsp["row"] >= 0, keep)
+    assert np.array_equal(dsp["kept"] + dsp["overflow"], n)
+    assert dsp["kept"].sum() + dsp["overflow"].sum() == S.size
+    if C is not None:
+        assert np.all(dsp["kept"] <= C)
+        assert np.all(dsp["overflow"][n <= C] == 0)
+    # perm_token is a bijection onto the kept assignments, ascending tokens within a segment
+    rows = dsp["row"][keep]
+    assert sorted(rows.tolist()) == list(range(int(dsp["offsets"][-1])))
+    for e in range(E):
+        seg = dsp["perm_token"][dsp["offsets"][e]:dsp["offsets"][e + 1]]
+        assert np.all(np.diff(seg) > 0)
+        assert np.all([e in S[t] for t in seg])
+    for t in range(S.shape[0]):
+        for j in range(S.shape[1]):
+            if keep[t, j]:
+                r = dsp["row"][t, j]
+                assert dsp["perm_token"][r] == t
+                assert dsp["offsets"][S[t, j]] <= r < dsp["offsets"][S[t, j] + 1]
+
+
+def check_dispatch(mod=O, exhaustive=True):
+    T, E, k = 5, 4, 2
+    subsets = list(itertools.combinations(range(E), k))
+    cases = itertools.product(subsets, repeat=T) if exhaustive else \
+        [tuple(subsets[i] for i in np.random.default_rng(s).integers(0, len(subsets), T)) for s in range(200)]
+    for assign in cases:
+        S = np.array(assign, dtype=np.int64)
+        for C in (1, 2, None):
+            _check_dispatch_against_simulation(mod, S, E, C)
+    # a larger random case with slot order not sorted by index
+    rng = np.random.default_rng(7)
+    S = np.stack([rng.permutation(9)[:3] for _ in range(300)])
+    for C in (50, 100, 120, None):
+        _check_dispatch_against_simulation(mod, S, 9, C)
+
+
+def test_dispatch_exhaustive_tiny():
+    check_dispatch(exhaustive=True)
+
+
+# ------------------------------------------------------------------------------------- experts
+
+def check_experts(mod=O):
+    d = 6
+    rng = np.random.default_rng(8)
+    p1, p2, p3 = rng.permutation(d), rng.permutation(d), rng.permutation(d)
+    Pg, Pu, Pd = np.eye(d)[p1], np.eye(d)[p2], np.eye(d)[p3]   # (P x)_i = x[p[i]]
+    X = rng.standard_normal((4, d))
+    out = mod.swiglu_expert(X, Pg, Pu, Pd)
+    for r in range(4):
+        h = [X[r, p1[i]] / (1.0 + math.exp(-X[r, p1[i]])) * X[r, p2[i]] for i in range(d)]
+        assert np.allclose(out[r], [h[p3[i]] for i in range(d)], rtol=1e-14)
+    # SiLU closed values
+    assert mod.silu(np.array([0.0]))[0] == 0.0
+    assert math.isclose(mod.silu(np.array([50.0]))[0], 50.0, rel_tol=1e-15)
+    assert abs(mod.silu(np.array([-50.0]))[0]) < 1e-19
+    # zero gate projection => zero output
+    assert np.all(mod.swiglu_expert(X, np.zeros((3, d)), rng.standard_normal((3, d)),
+                                    rng.standard_normal((d, 3))) == 0.0)
+
+
+def test_expert_pins():
+    check_experts()
+
+
+def _tiny_layer(T=40, d=16, E=4, k=2, M=24, seed=0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    Wr = rng.standard_normal((E, d)) / math.sqrt(d)
+    Wg = rng.standard_normal((E, M, d)) / math.sqrt(d)
+    Wu = rng.standard_normal((E, M, d)) / math.sqrt(d)
+    Wd = rng.standard_normal((E, d, M)) / math.sqrt(M)
+    return x, Wr, Wg, Wu, Wd
+
+
+def check_layer(mod=O):
+    # E = 1, k = 1 collapses to the dense SwiGLU FFN
+    x, Wr, Wg, Wu, Wd = _tiny_layer(E=1)
+    res = mod.layer_forward(x, Wr, Wg, Wu, Wd, k=1)
+    assert np.allclose(res["y"], mod.swiglu_expert(x, Wg[0], Wu[0], Wd[0]), rtol=1e-13, atol=1e-14)
+    # identical experts + renorm + no drops => y = FFN(x) whatever the routing
+    x, Wr, Wg, Wu, Wd = _tiny_layer(E=5, k=3)
+    Wg[:], Wu[:], Wd[:] = Wg[0], Wu[0], Wd[0]
+    res = mod.layer_forward(x, Wr, Wg, Wu, Wd, k=3)
+    assert np.allclose(res["y"], mod.swiglu_expert(x, Wg[0], Wu[0], Wd[0]), rtol=1e-12, atol=1e-13)
+    # two shared experts of width M equal one of width 2M
+    x, Wr, Wg, Wu, Wd = _tiny_layer()
+    rng = np.random.default_rng(11)
+    sh = [(rng.standard_normal((8, 16)), rng.standard_normal((8, 16)), rng.standard_normal((16, 8)))
+          for _ in range(2)]
+    fused = (np.concatenate([s[0] for s in sh]), np.concatenate([s[1] for s in sh]),
+             np.concatenate([s[2] for s in sh], axis=1))
+    a = mod.layer_forward(x, Wr, Wg, Wu, Wd, k=2, shared=sh)
+    b = mod.layer_forward(x, Wr, Wg, Wu, Wd, k=2, shared=[fused])
+    assert np.allclose(a["y"], b["y"], rtol=1e-12, atol=1e-13)
+    # capacity 1 on 40 tokens drops most slots; a token whose slots are all dropped gets shared only
+    res = mod.layer_forward(x, Wr, Wg, Wu, Wd, k=2, shared=sh, c=1.0 / 32)  # C = ceil(0.625) = 1
+    assert res["C"] == 1 and res["kept"].sum() <= 4
+    none_kept = np.where((res["row"] < 0).all(1))[0]
+    assert len(none_kept) > 0
+    assert np.allclose(res["y"][none_kept], mod.shared_experts(x[none_kept], sh), rtol=1e-13)
+    # the token subset gives the same rows as the full pass
+    sub = mod.layer_forward(x, Wr, Wg, Wu, Wd, k=2, shared=sh, tokens=[3, 17, 39])
+    full = mod.layer_forward(x, Wr, Wg, Wu, Wd, k=2, shared=sh)
+    assert np.allclose(sub["y"], full["y"][[3, 17, 39]], rtol=1e-14, atol=0)
+
+
+def test_layer_pins():
+    check_layer()
+
+
+# --------------------------------------------------------------------------------- bias update
+
+def check_bias(mod=O):
+    rng = np.random.default_rng(9)
+    E, k, T = 10, 3, 40                  # mean load 12
+    b = (rng.random(E) * 0.1 - 0.05).astype(np.float32)
+    n = np.array([12, 0, 30, 11, 13, 12, 5, 20, 12, 5])
+    nb = mod.bias_update(b, n, k, T, 1e-3)
+    assert nb.dtype == np.float32
+    for e in range(E):
+        step = np.float32(1e-3) * (1 if n[e] < 12 else (-1 if n[e] > 12 else 0))
+        assert nb[e] == np.float32(b[e] + step)
+    assert np.all(nb[n > 12] < b[n > 12]) and np.all(nb[n < 12] > b[n < 12])
+    assert np.all(nb[n == 12] == b[n == 12])
+
+
+def test_bias_pins():
+    check_bias()
+
+
+def test_bias_changes_selection_not_gates():
+    l = _rand((30, 6), 12)
+    g, _ = O.softmax_lse(l)
+    b = np.array([0.0, 0.0, 10.0, 0.0, 0.0, 10.0])   # forces experts 2 and 5
+    S = O.top_k(O.selection_scores(g, b), 2)
+    assert all(set(r) == {2, 5} for r in S.tolist())
+    w = O.gate_weights(g, S, True)
+    for t in range(30):
+        for j in range(2):
+            assert math.isclose(w[t, j], g[t, S[t, j]] / (g[t, 2] + g[t, 5]), rel_tol=1e-14)
+
+
+# ------------------------------------------------------------------------- workloads vs pages
+
+def test_workload_shapes_match_pages():
+    c = workloads.CONFIGS
+    gm = GOLDEN["mixtral_shape"]
+    assert (c["mixtral_8x7b"].E, c["mixtral_8x7b"].k, c["mixtral_8x7b"].M) == (gm["E"], gm["k"], gm["M"])
+    gd = GOLDEN["deepseekmoe_16b_routing"]
+    assert (c["deepseekmoe_16b"].E, c["deepseekmoe_16b"].k) == (gd["E"], gd["k"])
+    gv = GOLDEN["deepseek_v2_routing"]
+    assert (c["deepseek_v2"].E, c["deepseek_v2"].k) == (gv["E"], gv["k"])
+    assert all(cfg.lam == GOLDEN["aux_coefficient"]["lambda"] for cfg in c.values())
+
+
+def test_workload_generator_is_seeded_and_per_expert():
+    cfg = workloads.CONFIGS["tiny_fp32"]
+    a = workloads.make_inputs(cfg)
+    b = workloads.make_inputs(cfg)
+    assert torch.equal(a.x, b.x) and torch.equal(a.W_gate, b.W_gate)
+    assert torch.equal(workloads.make_expert(cfg, 3)[0], a.W_gate[3])
+    cfg16 = workloads.CONFIGS["mixtral_8x7b"].with_(T=64, d=128, M=256)
+    x = workloads.make_x(cfg16)
+    assert x.dtype == torch.bfloat16 and x.shape == (64, 128)
+    assert abs(float(x.float().std()) - 1.0) < 0.05
+
+
+# ------------------------------------------------------------------ mutations must be caught
+
+class _Mutant:
+    """A copy of the oracle's namespace with one function replaced."""
+
+    def __init__(self, **repl):
+        self.__dict__.update({k: getattr(O, k) for k in dir(O) if not k.startswith("__")})
+        self.__dict__.update(repl)
+        # layer_forward looks its helpers up in the module, so rebind it to this namespace
+        import types
+        for name in ("layer_forward", "route"):
+            fn = getattr(O, name)
+            self.__dict__[name] = types.FunctionType(fn.__code__, self.__dict__, name, fn.__defaults__)
+
+
+def _no_renorm(g, S, renorm=True):
+    return np.take_along_axis(O._f64(g), S, axis=1)
+
+
+def _ties_high(s, k):
+    s = O._f64(s)
+    E = s.shape[1]
+    rev = np.argsort(-s[:, ::-1], axis=1, kind="stable")[:, :k]
+    return (E - 1) - rev
+
+
+def _f_over_T(n, g, lse, k, lam):
+    st = O.balance_stats(n, g, lse, 1, lam)
+    return st
+
+
+def _bias_wrong_sign(b, n, k, T, gamma):
+    b32 = np.asarray(b, dtype=np.float32)
+    return (b32 - np.float32(gamma) * np.sign((k * T) / b32.shape[0] - O._f64(n)).astype(np.float32)).astype(np.float32)
+
+
+def _swiglu_transposed_down(X, Wg, Wu, Wd):
+    X = O._f64(X)
+    h = O.silu(X @ O._f64(Wg).T) * (X @ O._f64(Wu).T)
+    return h @ O._f64(Wd)
+
+
+def _dispatch_last_kept(S, E, C):
+    # keep the LAST C tokens of each expert instead of the first C
+    rev = O.dispatch(S[::-1], E, C)
+    T, k = S.shape
+    row = np.full((T, k), -1, dtype=np.int64)
+    row[::-1] = np.where(rev["row"] >= 0, rev["row"], -1)
+    out = dict(rev)
+    out["row"] = row
+    return out
+
+
+def _lse_no_max(l):
+    l = O._f64(l)
+    lse = np.log(np.exp(l).sum(axis=1))
+    return np.exp(l - lse[:, None]), lse
+
+
+def _gate_from_biased(g, S, renorm=True):
+    return O.gate_weights(g + 0.01, S, renorm)
+
+
+@pytest.mark.parametrize("mutant,checks", [
+    (dict(gate_weights=_no_renorm), [check_gates]),
+    (dict(top_k=_ties_high), [check_topk]),
+    (dict(balance_stats=_f_over_T), [check_stats]),
+    (dict(bias_update=_bias_wrong_sign), [check_bias]),
+    (dict(swiglu_expert=_swiglu_transposed_down), [check_experts]),
+    (dict(dispatch=_dispatch_last_kept), [lambda m: check_dispatch(m, exhaustive=False)]),
+    (dict(softmax_lse=_lse_no_max), [check_softmax]),
+    (dict(gate_weights=_gate_from_biased), [check_gates]),
+])
+def test_planted_mistakes_are_caught(mutant, checks):
+    m = _Mutant(**mutant)
+    for chk in checks:
+        with pytest.raises((AssertionError, ValueError, IndexError, KeyError, FloatingPointError)):
+            with np.errstate(all="ignore"):
+                chk(m)
