@@ -1,0 +1,207 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts FFN layer forward.
+ *
+ * The layer computes, for every token x_t of a routing batch of T tokens,
+ *
+ *     y_t = sum_{e in S_t} w_te * E_e(x_t)  +  sum_{s < S} E^s(x_t)
+ *
+ * with router probabilities g_t = softmax(W_r x_t), selection S_t = TopK(g_t + b) over the routed
+ * experts, gates w_te = g_te renormalised over S_t, SwiGLU experts
+ * E_e(x) = W_down,e (SiLU(W_gate,e x) ⊙ (W_up,e x)), optional shared experts applied to every
+ * token, and an optional per-expert capacity C = ceil(c k T / E) that drops overflow assignments.
+ * Alongside it come the balance statistics f_e, P_e, aux = lambda E sum_e f_e P_e and the router
+ * z-loss. Sources (page title, section):
+ *   - "MoE：条件计算与路由": core formula; §原理与演进 (g = softmax(W_r x), TopK, L_balance);
+ *     §无辅助损失负载均衡（ALF-LB） (bias b_e before Top-K, rule-based update); §1 (loads n_e);
+ *     §3 (C = ceil(c B k / E), token dropping); §7 eqs. (1)-(3) (renormalised gates, y).
+ *   - "深入理解 MoE (混合专家模型)：稀疏激活与高效扩展": §4.2.1 (f_i, P_i, alpha = 0.01);
+ *     §10.2 / §11 (SwiGLU(x) = SiLU(W_1 x) ⊙ (W_3 x), W_2 projects back).
+ *   - "MOE大模型对比篇": §2.1 (balance loss), §2.2 (z-loss), §3.3 (shared experts).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device buffers are device pointers owned by the caller; tensors are dense,
+ *     row-major and 16-byte aligned. The library never allocates, frees or keeps a pointer past
+ *     the call. Scratch memory is the caller's workspace, sized by moe_workspace_size().
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is complete when
+ *     the caller synchronises that stream. No entry point synchronises.
+ *   - All argument checks run on the host before anything is enqueued: on an error the call
+ *     returns a status and enqueues nothing. A failed kernel launch returns MOE_ERR_HIP;
+ *     asynchronous faults surface at the caller's synchronisation.
+ *   - Results are deterministic: the same inputs give bit-identical outputs on every call.
+ *   - Entry points are stateless and re-entrant; concurrent calls must use distinct workspaces.
+ *   - dtype MOE_BF16: x, weights, intermediates and y are bf16, products accumulate in fp32, the
+ *     routing arithmetic is fp32, h and expert outputs are rounded to bf16, y is rounded once.
+ *     dtype MOE_F32: all of these are fp32.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1, /* a size, pointer, alignment or flag is invalid            */
+  MOE_ERR_UNSUPPORTED = 2,      /* valid, but beyond this build's limits (E, k, dtype)       */
+  MOE_ERR_WORKSPACE = 3,        /* workspace missing or smaller than moe_workspace_size()    */
+  MOE_ERR_HIP = 4               /* a kernel launch failed                                   */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Which entry point a workspace is sized for. */
+typedef enum {
+  MOE_CALL_ROUTE = 0,
+  MOE_CALL_DISPATCH = 1,
+  MOE_CALL_EXPERT_FFN = 2,
+  MOE_CALL_LAYER = 3
+} moe_call;
+
+#define MOE_E_MAX 256 /* routed experts per layer */
+#define MOE_K_MAX 16  /* experts chosen per token */
+
+/* Layer sizes, in the pages' notation. */
+typedef struct {
+  int64_t T;      /* tokens in the routing batch (B on the pages), >= 1                       */
+  int32_t d;      /* hidden size; multiple of 8 (bf16) or 4 (fp32)                            */
+  int32_t E;      /* routed experts, 1 <= E <= MOE_E_MAX                                      */
+  int32_t k;      /* experts chosen per token, 1 <= k <= min(E, MOE_K_MAX)                    */
+  int32_t M;      /* expert intermediate width; multiple of 8 (bf16) or 4 (fp32)              */
+  int32_t S;      /* shared experts, each of width M, >= 0; they run as one expert of width S*M */
+  float c;        /* capacity factor; <= 0 means no capacity limit; NaN is invalid            */
+  int32_t renorm; /* 1: renormalise the chosen gates over S_t; 0: use g_te as is               */
+  int32_t dtype;  /* moe_dtype                                                                */
+} moe_shape;
+
+/* Short text for a status code (static storage). */
+const char* moe_status_string(int status);
+
+/* Checks a shape as the entry points do; MOE_OK if every entry point accepts it. */
+moe_status moe_check_shape(const moe_shape* s);
+
+/* Capacity C = ceil(c k T / E) of "MoE：条件计算与路由" §3, computed in double precision as
+ * ((c * k) * T) / E from the float c; -1 when c <= 0 (no limit) or the shape is invalid. */
+int64_t moe_capacity(const moe_shape* s);
+
+/* Bytes of workspace entry point `call` needs for shape s (0 if the shape is invalid).
+ * For MOE_CALL_EXPERT_FFN the size is for groups = E (it also covers groups = 1). */
+size_t moe_workspace_size(const moe_shape* s, int call);
+
+/*
+ * moe_route -- router of "MoE：条件计算与路由" §原理与演进 and §无辅助损失负载均衡（ALF-LB）.
+ *
+ * For every token t: l_te = sum_i x_ti W_r,ei (no router bias); m = max_e l_te,
+ * lse_t = m + ln sum_e exp(l_te - m), g_te = exp(l_te - lse_t); s_te = g_te + b_e (b optional);
+ * S_t = the k experts of largest s_te, in descending s order, equal scores to the lower index;
+ * w_tj = g_t,S_tj / sum_j' g_t,S_tj' (or g_t,S_tj when renorm == 0).
+ *   x        device [T, d] (dtype)          W_r   device [E, d] (dtype)
+ *   b        device [E] fp32 or NULL (selection only; gates use the unbiased g)
+ *   topk_idx device out [T, k] int32        topk_w device out [T, k] fp32
+ *   n        device out [E] int32: loads n_e = #{t : e in S_t}, before any capacity limit
+ *   gsum     device out [E] double: sum_t g_te        lse2sum device out [1] double: sum_t lse_t^2
+ *   ws       device workspace of moe_workspace_size(s, MOE_CALL_ROUTE) bytes
+ */
+moe_status moe_route(const moe_shape* s, const void* x, const void* W_r, const float* b,
+                     int32_t* topk_idx, float* topk_w, int32_t* n, double* gsum, double* lse2sum,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_dispatch -- capacity and expert-contiguous placement ("MoE：条件计算与路由" §3; the
+ * per-expert histogram, sort and gather of the DeepseekV3MoE listing on the adg.csdn.net notes
+ * page, §四).
+ *
+ * Position p(t, e) = number of tokens t' < t with e in S_t'. The assignment (t, j), e = S_tj, is
+ * kept iff C < 0 or p < C; kept_e = min(n_e, C); overflow_e = n_e - kept_e;
+ * offsets_e = sum_{e' < e} kept_e'; its row is offsets_e + p. Rows of one expert are therefore in
+ * ascending token order.
+ *   x          device [T, d] (dtype)
+ *   topk_idx   device [T, k] int32, each row k distinct experts in [0, E)
+ *   x_perm     device out [T*k, d] (dtype) or NULL (row copy skipped): x_perm[row] = x[t]
+ *   perm_token device out [T*k] int32: perm_token[row] = t for rows < offsets[E]; others unset
+ *   inv_perm   device out [T, k] int32: row of (t, j), or -1 if dropped
+ *   offsets    device out [E+1] int32    counts device out [E] int32 (n_e)
+ *   overflow   device out [E] int32 (dropped assignments per expert)
+ *   ws         device workspace of moe_workspace_size(s, MOE_CALL_DISPATCH) bytes
+ * Out-of-range expert ids in topk_idx are a caller error (not detected).
+ */
+moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx, void* x_perm,
+                        int32_t* perm_token, int32_t* inv_perm, int32_t* offsets, int32_t* counts,
+                        int32_t* overflow, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn -- grouped SwiGLU experts ("深入理解 MoE ..." §10.2: SiLU(W_1 x) ⊙ (W_3 x),
+ * then W_2; no biases). Group g owns rows [offsets_g, offsets_{g+1}) of `rows` and weights
+ * W_gate[g], W_up[g] ([Mg, d] each) and W_down[g] ([d, Mg]):
+ *     h[r]   = SiLU(rows[r] W_gate[g]^T) ⊙ (rows[r] W_up[g]^T)      (rounded to dtype)
+ *     out[r] = h[r] W_down[g]^T                                     (rounded to dtype)
+ * Shared experts use groups = 1, offsets = {0, T}, rows = x and Mg = S*M.
+ *   groups   1 <= groups <= MOE_E_MAX      Mg  intermediate width of every group (mult. of 8/4)
+ *   rows     device [max_rows, d]          offsets device [groups+1] int32, non-decreasing,
+ *                                          offsets[0] = 0, offsets[groups] <= max_rows
+ *   W_gate, W_up device [groups, Mg, d]    W_down device [groups, d, Mg]
+ *   h        device out [max_rows, Mg]     out device out [max_rows, d]; rows >= offsets[groups]
+ *                                          are left untouched
+ *   ws       device workspace of moe_workspace_size(s, MOE_CALL_EXPERT_FFN) bytes
+ * The hidden size d and dtype come from s; s->M and s->E are not used.
+ */
+moe_status moe_expert_ffn(const moe_shape* s, int32_t groups, int32_t Mg, const void* rows,
+                          const int32_t* offsets, int64_t max_rows, const void* W_gate,
+                          const void* W_up, const void* W_down, void* h, void* out, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine -- gate-weighted un-permute and sum ("MoE：条件计算与路由" §7 eq. (3)):
+ *     y_t = sum_{j : inv_perm_tj >= 0} w_tj * out_perm[inv_perm_tj]  (+ shared_out_t)
+ * summed in fp32 in slot order j = 0..k-1, then the shared term, rounded once to dtype.
+ *   out_perm   device [rows, d] (dtype)    inv_perm device [T, k] int32 (-1 = dropped)
+ *   topk_w     device [T, k] fp32          shared_out device [T, d] (dtype) or NULL
+ *   y          device out [T, d] (dtype)
+ */
+moe_status moe_combine(const moe_shape* s, const void* out_perm, const int32_t* inv_perm,
+                       const float* topk_w, const void* shared_out, void* y, void* stream);
+
+/*
+ * moe_balance_stats -- balance statistics and the loss-free-balancing bias step.
+ *   f_e = n_e / (k T)   P_e = gsum_e / T   aux = lambda E sum_e f_e P_e
+ *   ("MoE：条件计算与路由" §原理与演进; "深入理解 MoE ..." §4.2.1; "MOE大模型对比篇" §2.1)
+ *   z = lse2sum / T   ("MOE大模型对比篇" §2.2 z-loss, natural log, raw router logits)
+ *   b_new_e = b_e + gamma * sign(k T / E - n_e) in fp32, sign(0) = 0 ("MoE：条件计算与路由"
+ *   §无辅助损失负载均衡（ALF-LB）: overloaded experts' bias goes down, underloaded up)
+ * f_e uses k T so that sum_e f_e = 1 for any k (the argmax fraction when k = 1).
+ *   n [E] int32, gsum [E] double, lse2sum [1] double: device, as written by moe_route
+ *   f, P device out [E] fp32 (nullable)    aux, z device out [1] fp32 (nullable)
+ *   b device [E] fp32 and b_new device out [E] fp32: both NULL, or both set (may alias)
+ */
+moe_status moe_balance_stats(const moe_shape* s, const int32_t* n, const double* gsum,
+                             const double* lse2sum, float lambda, float* f, float* P, float* aux,
+                             float* z, const float* b, float* b_new, float gamma, void* stream);
+
+/*
+ * moe_layer_forward -- the whole layer: route, dispatch, grouped experts, shared experts,
+ * combine and statistics, enqueued on one stream with no host synchronisation.
+ *   x device [T, d]; W_r device [E, d]; b device [E] fp32 or NULL
+ *   W_gate, W_up device [E, M, d]; W_down device [E, d, M]
+ *   Ws_gate, Ws_up device [S*M, d], Ws_down device [d, S*M]: the S shared experts stacked into one
+ *   of width S*M (NULL when S == 0)
+ *   y device out [T, d]
+ * Optional device outputs (NULL = not returned): topk_idx [T, k] int32, topk_w [T, k] fp32,
+ * counts [E] int32 (n_e), overflow [E] int32, f [E], P [E], aux [1], z [1] fp32, and
+ * b_new [E] fp32 = the updated bias (requires b; may alias b: it is written after selection).
+ *   ws device workspace of moe_workspace_size(s, MOE_CALL_LAYER) bytes
+ */
+moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r, const float* b,
+                             const void* W_gate, const void* W_up, const void* W_down,
+                             const void* Ws_gate, const void* Ws_up, const void* Ws_down, void* y,
+                             int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* overflow,
+                             float* f, float* P, float* aux, float* z, float* b_new, float lambda,
+                             float gamma, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,331 @@
+"""Python binding of the MI355X MoE layer library (``libmoe.so``, C ABI in ``include/moe.h``).
+
+The functions below carry the C entry points' names and do argument marshalling only: they check
+tensor shapes, dtypes and devices, allocate output tensors with torch (device memory is torch's
+plumbing), and pass raw device pointers plus torch's current HIP stream to the library. Every step
+of the layer runs in the library's HIP kernels. There is no fallback: if the library is missing or
+fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
+
+MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+CALL_ROUTE, CALL_DISPATCH, CALL_EXPERT_FFN, CALL_LAYER = range(4)
+E_MAX, K_MAX = 256, 16
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("M", ctypes.c_int32), ("S", ctypes.c_int32),
+                ("c", ctypes.c_float), ("renorm", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_SIG = {
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_check_shape": (ctypes.c_int, [ctypes.POINTER(Shape)]),
+    "moe_capacity": (ctypes.c_int64, [ctypes.POINTER(Shape)]),
+    "moe_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int]),
+    "moe_route": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                 ctypes.c_size_t, _P]),
+    "moe_dispatch": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    ctypes.c_size_t, _P]),
+    "moe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int32, _P,
+                                      _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                      _P]),
+    "moe_combine": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P]),
+    "moe_balance_stats": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, ctypes.c_float, _P, _P,
+                                         _P, _P, _P, _P, ctypes.c_float, _P]),
+    "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                         _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                         ctypes.c_float, _P, ctypes.c_size_t, _P]),
+}
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built (there is no fallback path)."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mixture_experts_layer_loss_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIG.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib_handle = h
+    return _lib_handle
+
+
+def header_functions() -> list:
+    """Names of the functions declared in include/moe.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != MOE_OK:
+        raise MoEError(status, what)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return MOE_BF16
+    if dt == torch.float32:
+        return MOE_F32
+    raise TypeError(f"unsupported dtype {dt}: the library takes bfloat16 or float32")
+
+
+def make_shape(T: int, d: int, E: int, k: int, M: int, S: int = 0, c: Optional[float] = None,
+               renorm: bool = True, dtype: torch.dtype = torch.bfloat16) -> Shape:
+    return Shape(int(T), int(d), int(E), int(k), int(M), int(S),
+                 float(c) if c is not None else 0.0, 1 if renorm else 0, _dtype_code(dtype))
+
+
+def check_shape(s: Shape) -> int:
+    return lib().moe_check_shape(ctypes.byref(s))
+
+
+def capacity(s: Shape) -> int:
+    return int(lib().moe_capacity(ctypes.byref(s)))
+
+
+def workspace_size(s: Shape, call: int) -> int:
+    return int(lib().moe_workspace_size(ctypes.byref(s), int(call)))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def workspace(s: Shape, call: int, device) -> torch.Tensor:
+    n = workspace_size(s, call)
+    if n == 0:
+        _check(check_shape(s), "workspace_size")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------------------- entry points
+
+def moe_route(x: torch.Tensor, W_r: torch.Tensor, k: int, b: Optional[torch.Tensor] = None,
+              renorm: bool = True, ws: Optional[torch.Tensor] = None) -> dict:
+    T, d = x.shape
+    E = W_r.shape[0]
+    s = make_shape(T, d, E, k, 8, renorm=renorm, dtype=x.dtype)
+    _dev(x, "x")
+    _dev(W_r, "W_r", x.dtype, (E, d))
+    if b is not None:
+        _dev(b, "b", torch.float32, (E,))
+    dev = x.device
+    out = {"topk_idx": torch.empty(T, k, dtype=torch.int32, device=dev),
+           "topk_w": torch.empty(T, k, dtype=torch.float32, device=dev),
+           "n": torch.empty(E, dtype=torch.int32, device=dev),
+           "gsum": torch.empty(E, dtype=torch.float64, device=dev),
+           "lse2sum": torch.empty(1, dtype=torch.float64, device=dev)}
+    if ws is None:
+        ws = workspace(s, CALL_ROUTE, dev)
+    _check(lib().moe_route(ctypes.byref(s), _ptr(x), _ptr(W_r), _ptr(b), _ptr(out["topk_idx"]),
+                           _ptr(out["topk_w"]), _ptr(out["n"]), _ptr(out["gsum"]),
+                           _ptr(out["lse2sum"]), _ptr(ws), ws.numel(), _stream()), "moe_route")
+    return out
+
+
+def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, c: Optional[float] = None,
+                 copy_rows: bool = True, ws: Optional[torch.Tensor] = None) -> dict:
+    T, d = x.shape
+    k = topk_idx.shape[1]
+    s = make_shape(T, d, E, k, 8, c=c, dtype=x.dtype)
+    _dev(x, "x")
+    _dev(topk_idx, "topk_idx", torch.int32, (T, k))
+    dev = x.device
+    rows = T * k
+    out = {"x_perm": torch.empty(rows, d, dtype=x.dtype, device=dev) if copy_rows else None,
+           "perm_token": torch.full((rows,), -1, dtype=torch.int32, device=dev),
+           "inv_perm": torch.empty(T, k, dtype=torch.int32, device=dev),
+           "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+           "counts": torch.empty(E, dtype=torch.int32, device=dev),
+           "overflow": torch.empty(E, dtype=torch.int32, device=dev)}
+    if ws is None:
+        ws = workspace(s, CALL_DISPATCH, dev)
+    _check(lib().moe_dispatch(ctypes.byref(s), _ptr(x), _ptr(topk_idx), _ptr(out["x_perm"]),
+                              _ptr(out["perm_token"]), _ptr(out["inv_perm"]), _ptr(out["offsets"]),
+                              _ptr(out["counts"]), _ptr(out["overflow"]), _ptr(ws), ws.numel(),
+                              _stream()), "moe_dispatch")
+    return out
+
+
+def moe_expert_ffn(rows: torch.Tensor, offsets: torch.Tensor, W_gate: torch.Tensor,
+                   W_up: torch.Tensor, W_down: torch.Tensor, ws: Optional[torch.Tensor] = None):
+    """Grouped SwiGLU over row groups [offsets[g], offsets[g+1]); returns (h, out)."""
+    R, d = rows.shape
+    G, Mg, d2 = W_gate.shape
+    if d2 != d:
+        raise ValueError("W_gate must be [groups, Mg, d]")
+    _dev(rows, "rows")
+    _dev(offsets, "offsets", torch.int32, (G + 1,))
+    _dev(W_gate, "W_gate", rows.dtype)
+    _dev(W_up, "W_up", rows.dtype, (G, Mg, d))
+    _dev(W_down, "W_down", rows.dtype, (G, d, Mg))
+    s = make_shape(max(R, 1), d, G, 1, Mg, dtype=rows.dtype)
+    h = torch.empty(R, Mg, dtype=rows.dtype, device=rows.device)
+    out = torch.empty(R, d, dtype=rows.dtype, device=rows.device)
+    if ws is None:
+        ws = workspace(s, CALL_EXPERT_FFN, rows.device)
+    _check(lib().moe_expert_ffn(ctypes.byref(s), G, Mg, _ptr(rows), _ptr(offsets), R, _ptr(W_gate),
+                                _ptr(W_up), _ptr(W_down), _ptr(h), _ptr(out), _ptr(ws), ws.numel(),
+                                _stream()), "moe_expert_ffn")
+    return h, out
+
+
+def moe_combine(out_perm: torch.Tensor, inv_perm: torch.Tensor, topk_w: torch.Tensor,
+                shared_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    T, k = inv_perm.shape
+    d = out_perm.shape[1]
+    _dev(out_perm, "out_perm")
+    _dev(inv_perm, "inv_perm", torch.int32)
+    _dev(topk_w, "topk_w", torch.float32, (T, k))
+    if shared_out is not None:
+        _dev(shared_out, "shared_out", out_perm.dtype, (T, d))
+    s = make_shape(T, d, max(k, 1), k, 8, dtype=out_perm.dtype)
+    y = torch.empty(T, d, dtype=out_perm.dtype, device=out_perm.device)
+    _check(lib().moe_combine(ctypes.byref(s), _ptr(out_perm), _ptr(inv_perm), _ptr(topk_w),
+                             _ptr(shared_out), _ptr(y), _stream()), "moe_combine")
+    return y
+
+
+def moe_balance_stats(T: int, k: int, n: torch.Tensor, gsum: torch.Tensor, lse2sum: torch.Tensor,
+                      lam: float = 0.01, b: Optional[torch.Tensor] = None,
+                      gamma: float = 1e-3) -> dict:
+    E = n.shape[0]
+    _dev(n, "n", torch.int32, (E,))
+    _dev(gsum, "gsum", torch.float64, (E,))
+    _dev(lse2sum, "lse2sum", torch.float64, (1,))
+    dev = n.device
+    s = make_shape(T, 8, E, k, 8, dtype=torch.float32)
+    out = {"f": torch.empty(E, dtype=torch.float32, device=dev),
+           "P": torch.empty(E, dtype=torch.float32, device=dev),
+           "aux": torch.empty(1, dtype=torch.float32, device=dev),
+           "z": torch.empty(1, dtype=torch.float32, device=dev),
+           "b_new": None if b is None else torch.empty(E, dtype=torch.float32, device=dev)}
+    if b is not None:
+        _dev(b, "b", torch.float32, (E,))
+    _check(lib().moe_balance_stats(ctypes.byref(s), _ptr(n), _ptr(gsum), _ptr(lse2sum), float(lam),
+                                   _ptr(out["f"]), _ptr(out["P"]), _ptr(out["aux"]), _ptr(out["z"]),
+                                   _ptr(b), _ptr(out["b_new"]), float(gamma), _stream()),
+           "moe_balance_stats")
+    return out
+
+
+class MoELayer:
+    """Holds the sizes and a preallocated workspace; ``forward`` calls moe_layer_forward."""
+
+    def __init__(self, T: int, d: int, E: int, k: int, M: int, S: int = 0,
+                 c: Optional[float] = None, renorm: bool = True,
+                 dtype: torch.dtype = torch.bfloat16, device="cuda"):
+        self.shape = make_shape(T, d, E, k, M, S, c, renorm, dtype)
+        _check(check_shape(self.shape), "MoELayer")
+        self.T, self.d, self.E, self.k, self.M, self.S = T, d, E, k, M, S
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.ws = workspace(self.shape, CALL_LAYER, self.device)
+
+    def alloc_outputs(self, with_bias: bool = False) -> dict:
+        dev, T, E, k = self.device, self.T, self.E, self.k
+        return {"y": torch.empty(T, self.d, dtype=self.dtype, device=dev),
+                "topk_idx": torch.empty(T, k, dtype=torch.int32, device=dev),
+                "topk_w": torch.empty(T, k, dtype=torch.float32, device=dev),
+                "counts": torch.empty(E, dtype=torch.int32, device=dev),
+                "overflow": torch.empty(E, dtype=torch.int32, device=dev),
+                "f": torch.empty(E, dtype=torch.float32, device=dev),
+                "P": torch.empty(E, dtype=torch.float32, device=dev),
+                "aux": torch.empty(1, dtype=torch.float32, device=dev),
+                "z": torch.empty(1, dtype=torch.float32, device=dev),
+                "b_new": torch.empty(E, dtype=torch.float32, device=dev) if with_bias else None}
+
+    def forward(self, x, W_r, W_gate, W_up, W_down, b=None, shared=None, lam: float = 0.01,
+                gamma: float = 1e-3, out: Optional[dict] = None) -> dict:
+        T, d, E, M, dt = self.T, self.d, self.E, self.M, self.dtype
+        _dev(x, "x", dt, (T, d))
+        _dev(W_r, "W_r", dt, (E, d))
+        _dev(W_gate, "W_gate", dt, (E, M, d))
+        _dev(W_up, "W_up", dt, (E, M, d))
+        _dev(W_down, "W_down", dt, (E, d, M))
+        if b is not None:
+            _dev(b, "b", torch.float32, (E,))
+        sg = su = sd = None
+        if self.S > 0:
+            if shared is None:
+                raise ValueError("this layer has shared experts: pass shared=(Ws_gate, Ws_up, Ws_down)")
+            sg, su, sd = shared
+            SM = self.S * M
+            _dev(sg, "Ws_gate", dt, (SM, d))
+            _dev(su, "Ws_up", dt, (SM, d))
+            _dev(sd, "Ws_down", dt, (d, SM))
+        if out is None:
+            out = self.alloc_outputs(with_bias=b is not None)
+        _check(lib().moe_layer_forward(
+            ctypes.byref(self.shape), _ptr(x), _ptr(W_r), _ptr(b), _ptr(W_gate), _ptr(W_up),
+            _ptr(W_down), _ptr(sg), _ptr(su), _ptr(sd), _ptr(out["y"]), _ptr(out.get("topk_idx")),
+            _ptr(out.get("topk_w")), _ptr(out.get("counts")), _ptr(out.get("overflow")),
+            _ptr(out.get("f")), _ptr(out.get("P")), _ptr(out.get("aux")), _ptr(out.get("z")),
+            _ptr(out.get("b_new") if b is not None else None), float(lam), float(gamma),
+            _ptr(self.ws), self.ws.numel(), _stream()), "moe_layer_forward")
+        return out
+
+
+def moe_layer_forward(x, W_r, W_gate, W_up, W_down, k: int, b=None, shared=None,
+                      c: Optional[float] = None, renorm: bool = True, lam: float = 0.01,
+                      gamma: float = 1e-3) -> dict:
+    """One call of the whole layer (allocates its workspace; use MoELayer to reuse one)."""
+    T, d = x.shape
+    E, M, _ = W_gate.shape
+    S = 0
+    if shared is not None:
+        S = shared[0].shape[0] // M
+    layer = MoELayer(T, d, E, k, M, S, c, renorm, x.dtype, x.device)
+    return layer.forward(x, W_r, W_gate, W_up, W_down, b, shared, lam, gamma)
+
+
+__all__ = ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_balance_stats",
+           "moe_layer_forward", "MoELayer", "make_shape", "capacity", "workspace_size",
+           "check_shape", "status_string", "lib", "MoEError", "Shape"]

@@ -1,0 +1,106 @@
+// Combine: y_t = sum_{j : inv_tj >= 0} w_tj * out_perm[inv_tj] (+ shared_t)
+// ("MoE：条件计算与路由" §7 eq. (3)), the un-permute and weighted sum of the DeepseekV3MoE
+// listing's last step on the adg.csdn.net notes page (§四), plus the shared-expert term.
+//
+// One wave per token: the k row indices and gates are wave-uniform; lanes walk the hidden
+// dimension in 16-byte chunks, accumulate in fp32 in slot order j = 0..k-1, add the shared term
+// last and round once to the output type.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+template <typename T>
+struct Vec;  // one 16-byte chunk
+template <>
+struct Vec<bf16_t> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void load(const bf16_t* p, float* v) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static void store(bf16_t* p, const float* v) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <>
+struct Vec<float> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void load(const float* p, float* v) {
+    const float4 u = *reinterpret_cast<const float4*>(p);
+    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+  }
+  __device__ __forceinline__ static void store(float* p, const float* v) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(int64_t Tn, int d, int k,
+                                                       const T* __restrict__ out_perm,
+                                                       const int32_t* __restrict__ inv_perm,
+                                                       const float* __restrict__ topk_w,
+                                                       const T* __restrict__ shared_out,
+                                                       T* __restrict__ y) {
+  constexpr int VN = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  int rows[MOE_K_MAX];
+  float w[MOE_K_MAX];
+#pragma unroll
+  for (int j = 0; j < MOE_K_MAX; ++j) {
+    rows[j] = j < k ? inv_perm[t * k + j] : -1;
+    w[j] = j < k ? topk_w[t * k + j] : 0.f;
+  }
+  for (int c = lane * VN; c < d; c += 64 * VN) {
+    float acc[VN];
+#pragma unroll
+    for (int i = 0; i < VN; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < MOE_K_MAX; ++j) {
+      if (rows[j] >= 0) {
+        float v[VN];
+        Vec<T>::load(out_perm + static_cast<int64_t>(rows[j]) * d + c, v);
+#pragma unroll
+        for (int i = 0; i < VN; ++i) acc[i] = fmaf(w[j], v[i], acc[i]);
+      }
+    }
+    if (shared_out != nullptr) {
+      float v[VN];
+      Vec<T>::load(shared_out + t * d + c, v);
+#pragma unroll
+      for (int i = 0; i < VN; ++i) acc[i] += v[i];
+    }
+    Vec<T>::store(y + t * d + c, acc);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(int dtype, int64_t T, int d, int k, const void* out_perm,
+                          const int32_t* inv_perm, const float* topk_w, const void* shared_out,
+                          void* y, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(cdiv(T, 4)));
+  if (dtype == MOE_F32)
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, st, T, d, k,
+                       static_cast<const float*>(out_perm), inv_perm, topk_w,
+                       static_cast<const float*>(shared_out), static_cast<float*>(y));
+  else
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(256), 0, st, T, d, k,
+                       static_cast<const bf16_t*>(out_perm), inv_perm, topk_w,
+                       static_cast<const bf16_t*>(shared_out), static_cast<bf16_t*>(y));
+  return hipGetLastError();
+}
+
+}  // namespace moe

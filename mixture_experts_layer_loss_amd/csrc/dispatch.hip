@@ -1,0 +1,255 @@
+// Dispatch: expert loads, capacity, expert-contiguous placement and row copies
+// ("MoE：条件计算与路由" §1 loads n_e and §3 capacity C = ceil(c B k / E); the histogram-then-sort
+// placement of the DeepseekV3MoE listing and the demo MoE's per-expert capacity cut on the
+// adg.csdn.net notes page, §四).
+//
+// Placement rule: assignment (t, j) with expert e = S_tj has position p = #{t' < t : e in S_t'};
+// it is kept iff there is no capacity or p < C, and then lands in row offsets_e + p. Positions are
+// computed without atomics on ordering: a block of 64 tokens builds, per expert, the 64-bit mask of
+// its tokens that chose the expert (LDS atomicOr is order-independent), so the in-block rank is a
+// popcount of the lower bits; the cross-block part is an exclusive scan of the block histograms
+// in block order. The result is identical on every run.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int RT = kRouteTokens;  // 64 tokens per block: one bit each in a 64-bit mask
+
+__device__ __forceinline__ bool valid_expert(int e, int E) { return e >= 0 && e < E; }
+
+__global__ __launch_bounds__(256) void count_kernel(int64_t T, int E, int k,
+                                                     const int32_t* __restrict__ topk_idx,
+                                                     int32_t* __restrict__ hist) {
+  __shared__ int cnt[MOE_E_MAX];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * RT;
+  for (int p = threadIdx.x; p < RT * k; p += blockDim.x) {
+    const int64_t t = t0 + p / k;
+    if (t < T) {
+      const int e = topk_idx[t * k + p % k];
+      if (valid_expert(e, E)) atomicAdd(&cnt[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
+}
+
+// Inclusive scan over 256 ints in LDS (Hillis-Steele); every thread of the block must call it.
+__device__ int block_scan_256(int v, int* buf) {
+  const int tid = threadIdx.x;
+  buf[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = tid >= off ? buf[tid - off] : 0;
+    __syncthreads();
+    buf[tid] += add;
+    __syncthreads();
+  }
+  const int r = buf[tid];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(256) void scan_kernel(
+    int64_t T, int E, int64_t C, int nblk, const int32_t* __restrict__ hist,
+    const float* __restrict__ gpart, const float* __restrict__ lpart,
+    int32_t* __restrict__ block_base, int32_t* __restrict__ n_out, double* __restrict__ gsum,
+    double* __restrict__ lse2sum, int32_t* __restrict__ kept_out, int32_t* __restrict__ overflow,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off, int BM) {
+  __shared__ int sbuf[256];
+  __shared__ double dbuf[256];
+  const int e = threadIdx.x;
+  int n = 0;
+  double gs = 0.0;
+  if (e < E) {
+    int b = 0;
+    for (; b + 4 <= nblk; b += 4) {  // four independent loads in flight per step
+      const int h0 = hist[static_cast<int64_t>(b) * E + e];
+      const int h1 = hist[static_cast<int64_t>(b + 1) * E + e];
+      const int h2 = hist[static_cast<int64_t>(b + 2) * E + e];
+      const int h3 = hist[static_cast<int64_t>(b + 3) * E + e];
+      if (block_base != nullptr) {
+        block_base[static_cast<int64_t>(b) * E + e] = n;
+        block_base[static_cast<int64_t>(b + 1) * E + e] = n + h0;
+        block_base[static_cast<int64_t>(b + 2) * E + e] = n + h0 + h1;
+        block_base[static_cast<int64_t>(b + 3) * E + e] = n + h0 + h1 + h2;
+      }
+      n += h0 + h1 + h2 + h3;
+      if (gpart != nullptr) {
+        gs += static_cast<double>(gpart[static_cast<int64_t>(b) * E + e]);
+        gs += static_cast<double>(gpart[static_cast<int64_t>(b + 1) * E + e]);
+        gs += static_cast<double>(gpart[static_cast<int64_t>(b + 2) * E + e]);
+        gs += static_cast<double>(gpart[static_cast<int64_t>(b + 3) * E + e]);
+      }
+    }
+    for (; b < nblk; ++b) {
+      const int h = hist[static_cast<int64_t>(b) * E + e];
+      if (block_base != nullptr) block_base[static_cast<int64_t>(b) * E + e] = n;
+      n += h;
+      if (gpart != nullptr) gs += static_cast<double>(gpart[static_cast<int64_t>(b) * E + e]);
+    }
+  }
+  const int kept = (e < E) ? ((C < 0 || n <= C) ? n : static_cast<int>(C)) : 0;
+  if (e < E) {
+    if (n_out != nullptr) n_out[e] = n;
+    if (gsum != nullptr) gsum[e] = gs;
+    if (kept_out != nullptr) kept_out[e] = kept;
+    if (overflow != nullptr) overflow[e] = n - kept;
+  }
+  const int incl = block_scan_256(kept, sbuf);
+  if (e < E && offsets != nullptr) {
+    offsets[e] = incl - kept;
+    if (e == E - 1) offsets[E] = incl;
+  }
+  const int mt = (e < E) ? (kept + BM - 1) / BM : 0;
+  const int tincl = block_scan_256(mt, sbuf);
+  if (e < E && tile_off != nullptr) {
+    tile_off[e] = tincl - mt;
+    if (e == E - 1) tile_off[E] = tincl;
+  }
+  if (lse2sum != nullptr) {
+    double ls = 0.0;
+    for (int b = e; b < nblk; b += 256) ls += static_cast<double>(lpart[b]);
+    dbuf[e] = ls;
+    __syncthreads();
+    for (int off = 128; off >= 1; off >>= 1) {
+      if (e < off) dbuf[e] += dbuf[e + off];
+      __syncthreads();
+    }
+    if (e == 0) *lse2sum = dbuf[0];
+  }
+}
+
+// Ranks and rows of one block of 64 tokens: inv_perm [T,k] and perm_token [rows].
+__global__ __launch_bounds__(256) void place_kernel(int64_t T, int E, int k, int64_t C,
+                                                     const int32_t* __restrict__ topk_idx,
+                                                     const int32_t* __restrict__ block_base,
+                                                     const int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ perm_token,
+                                                     int32_t* __restrict__ inv_perm) {
+  __shared__ unsigned int mask[MOE_E_MAX * 2];  // per expert: tokens 0..31, tokens 32..63
+  for (int i = threadIdx.x; i < 2 * E; i += blockDim.x) mask[i] = 0u;
+  __syncthreads();
+  const int64_t blk = blockIdx.x;
+  const int64_t t0 = blk * RT;
+  for (int p = threadIdx.x; p < RT * k; p += blockDim.x) {
+    const int tl = p / k;
+    const int64_t t = t0 + tl;
+    if (t < T) {
+      const int e = topk_idx[t * k + p % k];
+      if (valid_expert(e, E)) atomicOr(&mask[2 * e + (tl >> 5)], 1u << (tl & 31));
+    }
+  }
+  __syncthreads();
+  for (int p = threadIdx.x; p < RT * k; p += blockDim.x) {
+    const int tl = p / k, j = p % k;
+    const int64_t t = t0 + tl;
+    if (t >= T) continue;
+    const int e = topk_idx[t * k + j];
+    int row = -1;
+    if (valid_expert(e, E)) {
+      const unsigned long long m =
+          (static_cast<unsigned long long>(mask[2 * e + 1]) << 32) | mask[2 * e];
+      const unsigned long long lower = tl == 0 ? 0ull : (m & ((1ull << tl) - 1ull));
+      const int64_t pos = static_cast<int64_t>(block_base[blk * E + e]) + __popcll(lower);
+      if (C < 0 || pos < C) {
+        row = offsets[e] + static_cast<int>(pos);
+        perm_token[row] = static_cast<int32_t>(t);
+      }
+    }
+    inv_perm[t * k + j] = row;
+  }
+}
+
+// x_perm[inv_perm[t, j]] = x[t]: one wave per token, 16-byte chunks, read once, written k times.
+__global__ __launch_bounds__(256) void copy_rows_kernel(int64_t T, int k, int64_t row_chunks,
+                                                         const uint4* __restrict__ x,
+                                                         const int32_t* __restrict__ inv_perm,
+                                                         uint4* __restrict__ x_perm) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int rows[MOE_K_MAX];
+#pragma unroll
+  for (int j = 0; j < MOE_K_MAX; ++j) rows[j] = j < k ? inv_perm[t * k + j] : -1;
+  const uint4* src = x + t * row_chunks;
+  for (int64_t c = lane; c < row_chunks; c += 64) {
+    const uint4 v = src[c];
+#pragma unroll
+    for (int j = 0; j < MOE_K_MAX; ++j)
+      if (rows[j] >= 0) x_perm[static_cast<int64_t>(rows[j]) * row_chunks + c] = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void schedule_kernel(int groups, const int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ tile_off, int BM) {
+  __shared__ int sbuf[256];
+  const int g = threadIdx.x;
+  const int rows = g < groups ? offsets[g + 1] - offsets[g] : 0;
+  const int mt = rows > 0 ? (rows + BM - 1) / BM : 0;
+  const int incl = block_scan_256(mt, sbuf);
+  if (g < groups) {
+    tile_off[g] = incl - mt;
+    if (g == groups - 1) tile_off[groups] = incl;
+  }
+}
+
+// Tile table of the shared experts: one group of all T rows.
+__global__ void shared_table_kernel(int64_t T, int BM, int32_t* __restrict__ offsets,
+                                    int32_t* __restrict__ tile_off) {
+  if (threadIdx.x == 0) {
+    offsets[0] = 0;
+    offsets[1] = static_cast<int32_t>(T);
+    tile_off[0] = 0;
+    tile_off[1] = static_cast<int32_t>((T + BM - 1) / BM);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_shared_table(int64_t T, int BM, int32_t* offsets, int32_t* tile_off,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(shared_table_kernel, dim3(1), dim3(64), 0, st, T, BM, offsets, tile_off);
+  return hipGetLastError();
+}
+
+hipError_t launch_count(int64_t T, int E, int k, const int32_t* topk_idx, int32_t* hist,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(count_kernel, dim3(static_cast<unsigned>(cdiv(T, RT))), dim3(256), 0, st, T,
+                     E, k, topk_idx, hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(int64_t T, int E, int64_t C, int nblk, const int32_t* hist,
+                       const float* gpart, const float* lpart, int32_t* block_base, int32_t* n_out,
+                       double* gsum, double* lse2sum, int32_t* kept, int32_t* overflow,
+                       int32_t* offsets, int32_t* tile_off, int BM, hipStream_t st) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, st, T, E, C, nblk, hist, gpart, lpart,
+                     block_base, n_out, gsum, lse2sum, kept, overflow, offsets, tile_off, BM);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(int64_t T, int d, int E, int k, int64_t C, int elem_bytes,
+                          const void* x, const int32_t* topk_idx, const int32_t* block_base,
+                          const int32_t* offsets, void* x_perm, int32_t* perm_token,
+                          int32_t* inv_perm, hipStream_t st) {
+  hipLaunchKernelGGL(place_kernel, dim3(static_cast<unsigned>(cdiv(T, RT))), dim3(256), 0, st, T,
+                     E, k, C, topk_idx, block_base, offsets, perm_token, inv_perm);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || x_perm == nullptr) return err;
+  const int64_t row_chunks = static_cast<int64_t>(d) * elem_bytes / 16;
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(static_cast<unsigned>(cdiv(T, 4))), dim3(256), 0, st,
+                     T, k, row_chunks, static_cast<const uint4*>(x), inv_perm,
+                     static_cast<uint4*>(x_perm));
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule(int groups, const int32_t* offsets, int32_t* tile_off, int BM,
+                           hipStream_t st) {
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(256), 0, st, groups, offsets, tile_off, BM);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,240 @@
+// Grouped expert GEMMs on bf16 MFMA for gfx950 (the SwiGLU experts of "深入理解 MoE (混合专家模型)：
+// 稀疏激活与高效扩展" §10.2: h = SiLU(X W_1^T) ⊙ (X W_3^T), out = h W_2^T).
+//
+// Both products are "TN": every operand row is contiguous along the reduction dimension K, so A
+// rows and B rows are read with 16-byte vector loads. A block of 256 threads (4 waves, 2 x 2)
+// computes a 256 x 256 tile with v_mfma_f32_32x32x16_bf16; each wave owns 128 x 128 (16 MFMA
+// blocks, 256 fp32 accumulators per lane). K advances 64 at a time through two LDS stages of
+// 64 KiB (A and B slices, XOR-swizzled 16-byte chunks so the MFMA fragment reads and the stores
+// are bank-conflict-free) with the next slice prefetched into registers during the MFMAs.
+//
+// Gate/up fusion: the B tile's first 128 rows come from W_gate and the last 128 from W_up at the
+// same output columns, so a lane holds gate and up values of the same (row, column) and applies
+// SiLU(g) * u in registers; h leaves as bf16. The down projection uses 256 plain columns.
+//
+// Groups (experts) are ragged: the tile table tile_off[g] (exclusive prefix of ceil(rows_g/256))
+// lives on the device, the grid is an upper bound, and each block finds its (group, n-block,
+// m-tile) from its logical index. Logical tiles are ordered group-major, then n-block, with the
+// m-tiles of a group fastest, and consecutive logical tiles are kept on one XCD (blocks are dealt
+// to the 8 XCDs round-robin), so the blocks sharing a weight slice or a row slice share an L2.
+#include "moe_internal.h"
+
+#include <math.h>
+
+#include <atomic>
+
+namespace moe {
+namespace {
+
+constexpr int BM = kGemmBM;  // 256
+constexpr int BN = 256;      // B rows per tile
+constexpr int BK = 64;
+constexpr int NXCD = 8;
+constexpr int kStageElems = (BM + BN) * BK;  // bf16 elements per LDS stage (64 KiB)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// element offset of 16-byte chunk `c` (0..7) of row `r` in a [rows][64] swizzled slice
+__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ ((r >> 1) & 7)) << 3); }
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// EPI 0: SwiGLU (B0 = W_gate, B1 = W_up, 128 output columns per tile); EPI 1: plain (B0 = W_down).
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
+    const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ tile_off, int groups, const bf16_t* __restrict__ B0,
+    const bf16_t* __restrict__ B1, int64_t group_stride, int N, int K, bf16_t* __restrict__ C) {
+  constexpr int BNO = EPI == 0 ? BN / 2 : BN;  // output columns per tile
+  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+
+  // ---- which tile: XCD-contiguous logical index, then (group, n-block, m-tile)
+  const int nb_count = (N + BNO - 1) / BNO;
+  const int64_t ntiles = static_cast<int64_t>(tile_off[groups]) * nb_count;
+  const int64_t q = (ntiles + NXCD - 1) / NXCD;
+  const int64_t L = static_cast<int64_t>(blockIdx.x % NXCD) * q + blockIdx.x / NXCD;
+  if (blockIdx.x / NXCD >= q || L >= ntiles) return;
+  int lo = 0, hi = groups;  // largest g with tile_off[g] * nb_count <= L
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (static_cast<int64_t>(tile_off[mid]) * nb_count <= L) lo = mid; else hi = mid;
+  }
+  const int g = lo;
+  const int mt_g = tile_off[g + 1] - tile_off[g];
+  const int64_t local = L - static_cast<int64_t>(tile_off[g]) * nb_count;
+  const int nb = static_cast<int>(local / mt_g);
+  const int mt = static_cast<int>(local % mt_g);
+  const int row_begin = offsets[g] + mt * BM;
+  const int row_end = min(offsets[g] + (mt + 1) * BM, offsets[g + 1]);
+  const int n0 = nb * BNO;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- global source rows of this thread's 8 A chunks and 8 B chunks (fixed over K)
+  const bf16_t* a_src[8];
+  const bf16_t* b_src[8];
+  const bf16_t* Bg0 = B0 + static_cast<int64_t>(g) * group_stride;
+  const bf16_t* Bg1 = EPI == 0 ? B1 + static_cast<int64_t>(g) * group_stride : nullptr;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = i * 256 + tid, r = c >> 3, kc = (c & 7) * 8;
+    const int ar = min(row_begin + r, row_end - 1);
+    a_src[i] = A + static_cast<int64_t>(ar) * K + kc;
+    int br;
+    const bf16_t* base;
+    if (EPI == 0) {
+      base = r < BN / 2 ? Bg0 : Bg1;
+      br = min(n0 + (r & (BN / 2 - 1)), N - 1);
+    } else {
+      base = Bg0;
+      br = min(n0 + r, N - 1);
+    }
+    b_src[i] = base + static_cast<int64_t>(br) * K + kc;
+  }
+
+  uint4 ra[8], rb[8];
+  const int kc_t = (tid & 7) * 8;  // this thread's chunk column (the same for all 8 chunks)
+  auto gload = [&](int k0) {
+    // branch-free: a chunk past K reads the row's last chunk and is then zeroed
+    const bool in = k0 + kc_t < K;
+    const int ko = in ? k0 : K - 8 - kc_t;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 va = *reinterpret_cast<const uint4*>(a_src[i] + ko);
+      const uint4 vb = *reinterpret_cast<const uint4*>(b_src[i] + ko);
+      ra[i] = in ? va : make_uint4(0, 0, 0, 0);
+      rb[i] = in ? vb : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto lstore = [&](int stage) {
+    bf16_t* sa = smem + stage * kStageElems;
+    bf16_t* sb = sa + BM * BK;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = i * 256 + tid, r = c >> 3, kc = c & 7;
+      *reinterpret_cast<uint4*>(sa + swz(r, kc)) = ra[i];
+      *reinterpret_cast<uint4*>(sb + swz(r, kc)) = rb[i];
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // B-tile rows of this wave's four 32-column blocks
+  int brow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    brow[j] = EPI == 0 ? ((j < 2 ? 0 : BN / 2) + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32);
+  const int l32 = lane & 31, lk = lane >> 5;
+
+  const int nk = (K + BK - 1) / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+    const bf16_t* sa = smem + (kt & 1) * kStageElems;
+    const bf16_t* sb = sa + BM * BK;
+#pragma unroll
+    for (int sub = 0; sub < BK / 16; ++sub) {
+      const int ch = sub * 2 + lk;
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(sa + swz(wm * 128 + i * 32 + l32, ch));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(sb + swz(brow[j] + l32, ch));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) lstore((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: registers -> LDS tile [BM][BNO + 8] (bf16) -> coalesced 16-byte stores
+  constexpr int CS = BNO + 8;
+  bf16_t* ct = smem;
+  // accumulator layout of the 32x32 MFMA: register r of lane l holds
+  // row 8*(r/4) + 4*(l/32) + r%4, column l%32 of its 32x32 block
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int jj = 0; jj < (EPI == 0 ? 2 : 4); ++jj) {
+      const int col = (EPI == 0 ? wn * 64 + jj * 32 : wn * 128 + jj * 32) + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 128 + i * 32 + (r >> 2) * 8 + lk * 4 + (r & 3);
+        float v;
+        if (EPI == 0)
+          v = silu(acc[i][jj][r]) * acc[i][jj + 2][r];
+        else
+          v = acc[i][jj][r];
+        ct[row * CS + col] = f32_to_bf16(v);
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int CPR = BNO / 8;  // 16-byte chunks per tile row
+  const int rows_here = row_end - row_begin;
+  for (int c = tid; c < BM * CPR; c += 256) {
+    const int r = c / CPR, cc = (c % CPR) * 8;
+    if (r < rows_here && n0 + cc < N)
+      *reinterpret_cast<uint4*>(C + static_cast<int64_t>(row_begin + r) * N + n0 + cc) =
+          *reinterpret_cast<const uint4*>(ct + r * CS + cc);
+  }
+}
+
+template <int EPI>
+hipError_t launch_gemm(const bf16_t* A, const int32_t* offsets, const int32_t* tile_off, int groups,
+                       int64_t max_tiles, const bf16_t* B0, const bf16_t* B1, int64_t group_stride,
+                       int N, int K, bf16_t* C, hipStream_t st) {
+  constexpr int BNO = EPI == 0 ? BN / 2 : BN;
+  const int64_t nb = cdiv(N, BNO);
+  const int64_t grid = cdiv(max_tiles * nb, NXCD) * NXCD;
+  // two K stages (128 KiB) or the epilogue's output tile, whichever is larger
+  constexpr size_t kMain = 2 * kStageElems * sizeof(bf16_t);
+  constexpr size_t kEpi = static_cast<size_t>(BM) * (BNO + 8) * sizeof(bf16_t);
+  const size_t lds = kMain > kEpi ? kMain : kEpi;
+  static std::atomic<bool> attr_set{false};
+  if (!attr_set.load(std::memory_order_acquire)) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_kernel<EPI>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    attr_set.store(true, std::memory_order_release);
+  }
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(grouped_gemm_kernel<EPI>, dim3(static_cast<unsigned>(grid)), dim3(256), lds,
+                     st, A, offsets, tile_off, groups, B0, B1, group_stride, N, K, C);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_expert_ffn_bf16(int groups, int d, int Mg, const void* rows,
+                                  const int32_t* offsets, const int32_t* tile_off,
+                                  int64_t max_tiles, const void* W_gate, const void* W_up,
+                                  const void* W_down, void* h, void* out, hipStream_t st) {
+  const int64_t gs = static_cast<int64_t>(Mg) * d;
+  hipError_t e = launch_gemm<0>(static_cast<const bf16_t*>(rows), offsets, tile_off, groups,
+                                max_tiles, static_cast<const bf16_t*>(W_gate),
+                                static_cast<const bf16_t*>(W_up), gs, Mg, d,
+                                static_cast<bf16_t*>(h), st);
+  if (e != hipSuccess) return e;
+  return launch_gemm<1>(static_cast<const bf16_t*>(h), offsets, tile_off, groups, max_tiles,
+                        static_cast<const bf16_t*>(W_down), nullptr, gs, d, Mg,
+                        static_cast<bf16_t*>(out), st);
+}
+
+}  // namespace moe

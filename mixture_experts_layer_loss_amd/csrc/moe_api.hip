@@ -1,0 +1,345 @@
+// extern "C" entry points of the MoE layer library: argument checks, workspace planning and the
+// launch sequence of each call. Every check runs on the host before anything is enqueued; the
+// library allocates nothing and never synchronises.
+#include <math.h>
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+hipError_t launch_expert_ffn_bf16(int groups, int d, int Mg, const void* rows,
+                                  const int32_t* offsets, const int32_t* tile_off,
+                                  int64_t max_tiles, const void* W_gate, const void* W_up,
+                                  const void* W_down, void* h, void* out, hipStream_t st);
+hipError_t launch_expert_ffn_f32(int groups, int d, int Mg, const void* rows,
+                                 const int32_t* offsets, const int32_t* tile_off,
+                                 int64_t max_tiles, const void* W_gate, const void* W_up,
+                                 const void* W_down, void* h, void* out, hipStream_t st);
+hipError_t launch_shared_table(int64_t T, int BM, int32_t* offsets, int32_t* tile_off,
+                               hipStream_t st);
+
+hipError_t launch_expert_ffn(int dtype, int groups, int d, int Mg, const void* rows,
+                             const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
+                             const void* W_gate, const void* W_up, const void* W_down, void* h,
+                             void* out, hipStream_t st) {
+  if (dtype == MOE_F32)
+    return launch_expert_ffn_f32(groups, d, Mg, rows, offsets, tile_off, max_tiles, W_gate, W_up,
+                                 W_down, h, out, st);
+  return launch_expert_ffn_bf16(groups, d, Mg, rows, offsets, tile_off, max_tiles, W_gate, W_up,
+                                W_down, h, out, st);
+}
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(const moe_shape* s) { return s->dtype == MOE_F32 ? 4 : 2; }
+int gemm_bm(const moe_shape* s) { return s->dtype == MOE_F32 ? kGemmF32BM : kGemmBM; }
+int64_t nblocks(const moe_shape* s) { return cdiv(s->T, kRouteTokens); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Bump allocator over a caller workspace (or a dry run that only measures).
+struct Carve {
+  unsigned char* base;
+  size_t used = 0;
+  explicit Carve(void* b) : base(static_cast<unsigned char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+int64_t capacity_of(const moe_shape* s) {
+  if (!(s->c > 0.0f)) return -1;
+  return static_cast<int64_t>(
+      ceil(((static_cast<double>(s->c) * s->k) * static_cast<double>(s->T)) / s->E));
+}
+
+// Rows the routed-expert buffers need: every assignment, or at most C per expert.
+int64_t routed_rows(const moe_shape* s) {
+  const int64_t P = s->T * s->k;
+  const int64_t C = capacity_of(s);
+  return C >= 0 && C * s->E < P ? C * s->E : P;
+}
+
+struct RoutePlan {
+  int32_t* hist;
+  float* gpart;
+  float* lpart;
+};
+RoutePlan plan_route(Carve& c, const moe_shape* s) {
+  const size_t nb = static_cast<size_t>(nblocks(s));
+  RoutePlan p;
+  p.hist = c.take<int32_t>(nb * s->E);
+  p.gpart = c.take<float>(nb * s->E);
+  p.lpart = c.take<float>(nb);
+  return p;
+}
+
+struct DispatchPlan {
+  int32_t* hist;
+  int32_t* block_base;
+};
+DispatchPlan plan_dispatch(Carve& c, const moe_shape* s) {
+  const size_t nb = static_cast<size_t>(nblocks(s));
+  DispatchPlan p;
+  p.hist = c.take<int32_t>(nb * s->E);
+  p.block_base = c.take<int32_t>(nb * s->E);
+  return p;
+}
+
+struct LayerPlan {
+  RoutePlan r;
+  int32_t *block_base, *topk_idx, *n, *kept, *overflow, *offsets, *tile_off, *perm_token,
+      *inv_perm, *sh_offsets, *sh_tile_off;
+  float* topk_w;
+  double *gsum, *lse2sum;
+  void *x_perm, *h, *out_perm, *h_sh, *sh;
+};
+LayerPlan plan_layer(Carve& c, const moe_shape* s) {
+  const size_t nb = static_cast<size_t>(nblocks(s));
+  const size_t P = static_cast<size_t>(s->T) * s->k;
+  const size_t R = static_cast<size_t>(routed_rows(s));
+  const size_t eb = static_cast<size_t>(elem_bytes(s));
+  LayerPlan p;
+  p.r = plan_route(c, s);
+  p.block_base = c.take<int32_t>(nb * s->E);
+  p.topk_idx = c.take<int32_t>(P);
+  p.topk_w = c.take<float>(P);
+  p.n = c.take<int32_t>(s->E);
+  p.gsum = c.take<double>(s->E);
+  p.lse2sum = c.take<double>(1);
+  p.kept = c.take<int32_t>(s->E);
+  p.overflow = c.take<int32_t>(s->E);
+  p.offsets = c.take<int32_t>(s->E + 1);
+  p.tile_off = c.take<int32_t>(s->E + 1);
+  p.sh_offsets = c.take<int32_t>(2);
+  p.sh_tile_off = c.take<int32_t>(2);
+  p.perm_token = c.take<int32_t>(R);
+  p.inv_perm = c.take<int32_t>(P);
+  p.x_perm = c.take<unsigned char>(R * s->d * eb);
+  p.h = c.take<unsigned char>(R * s->M * eb);
+  p.out_perm = c.take<unsigned char>(R * s->d * eb);
+  if (s->S > 0) {
+    p.h_sh = c.take<unsigned char>(static_cast<size_t>(s->T) * s->S * s->M * eb);
+    p.sh = c.take<unsigned char>(static_cast<size_t>(s->T) * s->d * eb);
+  } else {
+    p.h_sh = p.sh = nullptr;
+  }
+  return p;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+moe_status moe_check_shape(const moe_shape* s) {
+  if (s == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->T < 1 || s->d < 1 || s->E < 1 || s->k < 1 || s->M < 1 || s->S < 0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (isnan(s->c) || (s->renorm != 0 && s->renorm != 1)) return MOE_ERR_INVALID_ARGUMENT;
+  if (s->k > s->E) return MOE_ERR_INVALID_ARGUMENT;
+  if (s->E > MOE_E_MAX || s->k > MOE_K_MAX) return MOE_ERR_UNSUPPORTED;
+  const int vec = s->dtype == MOE_F32 ? 4 : 8;  // elements per 16-byte chunk
+  if (s->d % vec != 0 || s->M % vec != 0) return MOE_ERR_INVALID_ARGUMENT;
+  // row indices are int32
+  if (s->T * static_cast<int64_t>(s->k) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(s->S) * s->M > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int64_t moe_capacity(const moe_shape* s) {
+  if (moe_check_shape(s) != MOE_OK) return -1;
+  return capacity_of(s);
+}
+
+size_t moe_workspace_size(const moe_shape* s, int call) {
+  if (moe_check_shape(s) != MOE_OK) return 0;
+  Carve c(nullptr);
+  switch (call) {
+    case MOE_CALL_ROUTE: plan_route(c, s); break;
+    case MOE_CALL_DISPATCH: plan_dispatch(c, s); break;
+    case MOE_CALL_EXPERT_FFN: c.take<int32_t>(MOE_E_MAX + 1); break;
+    case MOE_CALL_LAYER: plan_layer(c, s); break;
+    default: return 0;
+  }
+  return c.used;
+}
+
+moe_status moe_route(const moe_shape* s, const void* x, const void* W_r, const float* b,
+                     int32_t* topk_idx, float* topk_w, int32_t* n, double* gsum, double* lse2sum,
+                     void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = moe_check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!x || !W_r || !topk_idx || !topk_w || !n || !gsum || !lse2sum)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(W_r) || !aligned16(topk_idx) || !aligned16(topk_w))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!ws || ws_bytes < moe_workspace_size(s, MOE_CALL_ROUTE)) return MOE_ERR_WORKSPACE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  Carve c(ws);
+  RoutePlan p = plan_route(c, s);
+  hipError_t e = launch_route(s->dtype, s->T, s->d, s->E, s->k, s->renorm, x, W_r, b, topk_idx,
+                              topk_w, p.hist, p.gpart, p.lpart, hs);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_scan(s->T, s->E, -1, static_cast<int>(nblocks(s)), p.hist, p.gpart, p.lpart, nullptr,
+                  n, gsum, lse2sum, nullptr, nullptr, nullptr, nullptr, gemm_bm(s), hs);
+  return hip_status(e);
+}
+
+moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx, void* x_perm,
+                        int32_t* perm_token, int32_t* inv_perm, int32_t* offsets, int32_t* counts,
+                        int32_t* overflow, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = moe_check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !perm_token || !inv_perm || !offsets || !counts || !overflow)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (x_perm != nullptr && (!x || !aligned16(x) || !aligned16(x_perm)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!ws || ws_bytes < moe_workspace_size(s, MOE_CALL_DISPATCH)) return MOE_ERR_WORKSPACE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  Carve c(ws);
+  DispatchPlan p = plan_dispatch(c, s);
+  const int64_t C = capacity_of(s);
+  hipError_t e = launch_count(s->T, s->E, s->k, topk_idx, p.hist, hs);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_scan(s->T, s->E, C, static_cast<int>(nblocks(s)), p.hist, nullptr, nullptr,
+                  p.block_base, counts, nullptr, nullptr, nullptr, overflow, offsets, nullptr,
+                  gemm_bm(s), hs);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_scatter(s->T, s->d, s->E, s->k, C, elem_bytes(s), x, topk_idx, p.block_base, offsets,
+                     x_perm, perm_token, inv_perm, hs);
+  return hip_status(e);
+}
+
+moe_status moe_expert_ffn(const moe_shape* s, int32_t groups, int32_t Mg, const void* rows,
+                          const int32_t* offsets, int64_t max_rows, const void* W_gate,
+                          const void* W_up, const void* W_down, void* h, void* out, void* ws,
+                          size_t ws_bytes, void* stream) {
+  moe_status st = moe_check_shape(s);
+  if (st != MOE_OK) return st;
+  if (groups < 1 || groups > MOE_E_MAX || Mg < 1 || max_rows < 0 || max_rows > INT32_MAX)
+    return groups > MOE_E_MAX ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_ARGUMENT;
+  if (Mg % (s->dtype == MOE_F32 ? 4 : 8) != 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (!rows || !offsets || !W_gate || !W_up || !W_down || !h || !out)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(rows) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_down) ||
+      !aligned16(h) || !aligned16(out))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!ws || ws_bytes < moe_workspace_size(s, MOE_CALL_EXPERT_FFN)) return MOE_ERR_WORKSPACE;
+  if (max_rows == 0) return MOE_OK;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int32_t* tile_off = static_cast<int32_t*>(ws);
+  const int BM = gemm_bm(s);
+  hipError_t e = launch_schedule(groups, offsets, tile_off, BM, hs);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  const int64_t max_tiles = cdiv(max_rows, BM) + groups;
+  e = launch_expert_ffn(s->dtype, groups, s->d, Mg, rows, offsets, tile_off, max_tiles, W_gate,
+                        W_up, W_down, h, out, hs);
+  return hip_status(e);
+}
+
+moe_status moe_combine(const moe_shape* s, const void* out_perm, const int32_t* inv_perm,
+                       const float* topk_w, const void* shared_out, void* y, void* stream) {
+  moe_status st = moe_check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!out_perm || !inv_perm || !topk_w || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(out_perm) || !aligned16(y) || (shared_out && !aligned16(shared_out)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_combine(s->dtype, s->T, s->d, s->k, out_perm, inv_perm, topk_w,
+                                   shared_out, y, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_balance_stats(const moe_shape* s, const int32_t* n, const double* gsum,
+                             const double* lse2sum, float lambda, float* f, float* P, float* aux,
+                             float* z, const float* b, float* b_new, float gamma, void* stream) {
+  moe_status st = moe_check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!n || !gsum || !lse2sum) return MOE_ERR_INVALID_ARGUMENT;
+  if ((b == nullptr) != (b_new == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (isnan(lambda) || isnan(gamma)) return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_stats(s->T, s->E, s->k, n, gsum, lse2sum, lambda, f, P, aux, z, b,
+                                 b_new, gamma, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r, const float* b,
+                             const void* W_gate, const void* W_up, const void* W_down,
+                             const void* Ws_gate, const void* Ws_up, const void* Ws_down, void* y,
+                             int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* overflow,
+                             float* f, float* P, float* aux, float* z, float* b_new, float lambda,
+                             float gamma, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = moe_check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!x || !W_r || !W_gate || !W_up || !W_down || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (s->S > 0 && (!Ws_gate || !Ws_up || !Ws_down)) return MOE_ERR_INVALID_ARGUMENT;
+  if (b_new != nullptr && b == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if (isnan(lambda) || isnan(gamma)) return MOE_ERR_INVALID_ARGUMENT;
+  const void* tensors[] = {x, W_r, W_gate, W_up, W_down, y, topk_idx, topk_w};
+  for (const void* t : tensors)
+    if (t && !aligned16(t)) return MOE_ERR_INVALID_ARGUMENT;
+  if (s->S > 0 && (!aligned16(Ws_gate) || !aligned16(Ws_up) || !aligned16(Ws_down)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!ws || ws_bytes < moe_workspace_size(s, MOE_CALL_LAYER)) return MOE_ERR_WORKSPACE;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  Carve c(ws);
+  LayerPlan p = plan_layer(c, s);
+  int32_t* idx = topk_idx ? topk_idx : p.topk_idx;
+  float* w = topk_w ? topk_w : p.topk_w;
+  int32_t* n = counts ? counts : p.n;
+  int32_t* ovf = overflow ? overflow : p.overflow;
+  const int64_t C = capacity_of(s);
+  const int BM = gemm_bm(s);
+  const int nblk = static_cast<int>(nblocks(s));
+  const int eb = elem_bytes(s);
+
+  hipError_t e = launch_route(s->dtype, s->T, s->d, s->E, s->k, s->renorm, x, W_r, b, idx, w,
+                              p.r.hist, p.r.gpart, p.r.lpart, hs);
+  if (e == hipSuccess)
+    e = launch_scan(s->T, s->E, C, nblk, p.r.hist, p.r.gpart, p.r.lpart, p.block_base, n, p.gsum,
+                    p.lse2sum, p.kept, ovf, p.offsets, p.tile_off, BM, hs);
+  if (e == hipSuccess)
+    e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx, p.block_base, p.offsets, p.x_perm,
+                       p.perm_token, p.inv_perm, hs);
+  if (e == hipSuccess)
+    e = launch_expert_ffn(s->dtype, s->E, s->d, s->M, p.x_perm, p.offsets, p.tile_off,
+                          cdiv(routed_rows(s), BM) + s->E, W_gate, W_up, W_down, p.h, p.out_perm,
+                          hs);
+  if (e == hipSuccess && s->S > 0) {
+    e = launch_shared_table(s->T, BM, p.sh_offsets, p.sh_tile_off, hs);
+    if (e == hipSuccess)
+      e = launch_expert_ffn(s->dtype, 1, s->d, s->S * s->M, x, p.sh_offsets, p.sh_tile_off,
+                            cdiv(s->T, BM), Ws_gate, Ws_up, Ws_down, p.h_sh, p.sh, hs);
+  }
+  if (e == hipSuccess)
+    e = launch_combine(s->dtype, s->T, s->d, s->k, p.out_perm, p.inv_perm, w,
+                       s->S > 0 ? p.sh : nullptr, y, hs);
+  if (e == hipSuccess && (f || P || aux || z || b_new))
+    e = launch_stats(s->T, s->E, s->k, n, p.gsum, p.lse2sum, lambda, f, P, aux, z,
+                     b_new ? b : nullptr, b_new, gamma, hs);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Internal declarations shared by the HIP translation units of the MoE layer library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------------------ tiling constants
+constexpr int kRouteTokens = 64;   // tokens per route / dispatch block (one bit per token in a u64)
+constexpr int kGemmBM = 256;       // rows per grouped-GEMM tile (bf16 path)
+constexpr int kGemmF32BM = 64;     // rows per grouped-GEMM tile (fp32 path)
+
+// ------------------------------------------------------------------------------ element helpers
+typedef uint16_t bf16_t;  // raw bf16 bits
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static float to_f32(float v) { return v; }
+  __device__ __forceinline__ static float from_f32(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  __device__ __forceinline__ static float to_f32(bf16_t v) { return bf16_to_f32(v); }
+  __device__ __forceinline__ static bf16_t from_f32(float v) { return f32_to_bf16(v); }
+};
+
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error; all enqueue on `st`.
+
+// Router: logits, softmax/LSE, biased top-k, gates, per-block partial statistics and histograms.
+//   hist  [nblk, E] int32, gpart [nblk, E] fp32, lpart [nblk] fp32, nblk = ceil(T / kRouteTokens)
+hipError_t launch_route(int dtype, int64_t T, int d, int E, int k, int renorm, const void* x,
+                        const void* W_r, const float* b, int32_t* topk_idx, float* topk_w,
+                        int32_t* hist, float* gpart, float* lpart, hipStream_t st);
+
+// Per-block expert histograms of a given selection (for a stand-alone dispatch).
+hipError_t launch_count(int64_t T, int E, int k, const int32_t* topk_idx, int32_t* hist,
+                        hipStream_t st);
+
+// One block: reduces the per-block partials (fp64, fixed order), scans loads over blocks, applies
+// the capacity and builds offsets and the grouped-GEMM tile table.
+//   block_base [nblk, E]; gsum/lse2sum/gpart/lpart may be NULL (dispatch-only use).
+//   tile_off [E+1]: exclusive prefix of ceil(kept_e / BM); written when non-NULL.
+hipError_t launch_scan(int64_t T, int E, int64_t C, int nblk, const int32_t* hist,
+                       const float* gpart, const float* lpart, int32_t* block_base, int32_t* n_out,
+                       double* gsum, double* lse2sum, int32_t* kept, int32_t* overflow,
+                       int32_t* offsets, int32_t* tile_off, int BM, hipStream_t st);
+
+// Places assignments: inv_perm, perm_token and (when x_perm != NULL) the x row copies.
+hipError_t launch_scatter(int64_t T, int d, int E, int k, int64_t C, int elem_bytes,
+                          const void* x, const int32_t* topk_idx, const int32_t* block_base,
+                          const int32_t* offsets, void* x_perm, int32_t* perm_token,
+                          int32_t* inv_perm, hipStream_t st);
+
+// Tile table of a grouped GEMM from device row offsets (stand-alone expert FFN).
+hipError_t launch_schedule(int groups, const int32_t* offsets, int32_t* tile_off, int BM,
+                           hipStream_t st);
+
+// Grouped SwiGLU FFN. max_tiles = upper bound of sum_g ceil(rows_g / BM).
+hipError_t launch_expert_ffn(int dtype, int groups, int d, int Mg, const void* rows,
+                             const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
+                             const void* W_gate, const void* W_up, const void* W_down, void* h,
+                             void* out, hipStream_t st);
+
+// y_t = sum_j w_tj out_perm[inv_tj] (+ shared_t).
+hipError_t launch_combine(int dtype, int64_t T, int d, int k, const void* out_perm,
+                          const int32_t* inv_perm, const float* topk_w, const void* shared_out,
+                          void* y, hipStream_t st);
+
+// f, P, aux, z and the bias step from reduced route statistics.
+hipError_t launch_stats(int64_t T, int E, int k, const int32_t* n, const double* gsum,
+                        const double* lse2sum, float lambda, float* f, float* P, float* aux,
+                        float* z, const float* b, float* b_new, float gamma, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,144 @@
+"""The C ABI on the host (no GPU): the library loads, exports every declared entry point, and every
+argument check returns its status before anything would be enqueued."""
+import ctypes
+import math
+import random
+
+import numpy as np
+import pytest
+
+import mixture_experts_layer_loss_amd as moe
+from oracle import moe_oracle as O
+
+
+def test_library_exports_every_declared_symbol():
+    names = moe.header_functions()
+    assert set(names) >= {"moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
+                          "moe_balance_stats", "moe_layer_forward", "moe_workspace_size",
+                          "moe_capacity", "moe_status_string", "moe_check_shape"}
+    h = ctypes.CDLL(moe.LIB_PATH)
+    for n in names:
+        assert hasattr(h, n), n
+    assert moe.status_string(0) == "ok"
+    assert "workspace" in moe.status_string(moe.MOE_ERR_WORKSPACE)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), moe.MOE_ERR_INVALID_ARGUMENT),
+    (dict(d=0), moe.MOE_ERR_INVALID_ARGUMENT),
+    (dict(k=0), moe.MOE_ERR_INVALID_ARGUMENT),
+    (dict(k=9), moe.MOE_ERR_INVALID_ARGUMENT),          # k > E
+    (dict(E=257, k=2), moe.MOE_ERR_UNSUPPORTED),       # E > E_MAX
+    (dict(E=32, k=17), moe.MOE_ERR_UNSUPPORTED),       # k > K_MAX
+    (dict(M=0), moe.MOE_ERR_INVALID_ARGUMENT),
+    (dict(S=-1), moe.MOE_ERR_INVALID_ARGUMENT),
+    (dict(d=100), moe.MOE_ERR_INVALID_ARGUMENT),       # bf16 rows need d % 8 == 0
+    (dict(M=1404), moe.MOE_ERR_INVALID_ARGUMENT),
+    (dict(c=float("nan")), moe.MOE_ERR_INVALID_ARGUMENT),
+    (dict(T=2**31, k=2), moe.MOE_ERR_UNSUPPORTED),     # rows are int32
+    (dict(), moe.MOE_OK),
+    (dict(E=256, k=16), moe.MOE_OK),
+    (dict(E=1, k=1), moe.MOE_OK),
+])
+def test_check_shape(kw, status):
+    args = dict(T=64, d=128, E=8, k=2, M=256)
+    args.update(kw)
+    s = moe.make_shape(**args)
+    assert moe.check_shape(s) == status
+
+
+def test_bad_renorm_and_dtype():
+    s = moe.make_shape(64, 128, 8, 2, 256)
+    s.renorm = 2
+    assert moe.check_shape(s) == moe.MOE_ERR_INVALID_ARGUMENT
+    s = moe.make_shape(64, 128, 8, 2, 256)
+    s.dtype = 7
+    assert moe.check_shape(s) == moe.MOE_ERR_UNSUPPORTED
+    s = moe.make_shape(64, 12, 8, 2, 12, dtype=__import__("torch").float32)
+    assert moe.check_shape(s) == moe.MOE_OK  # fp32 rows need d % 4 == 0 only
+
+
+def test_capacity_matches_oracle_rounding():
+    rng = random.Random(5)
+    cases = [(1.25, 2, 32768, 64), (1.0, 2, 10, 3), (0.05, 2, 40, 4), (0.03125, 2, 40, 4),
+             (1.0, 6, 16384, 160), (2.0, 8, 8192, 64)]
+    for _ in range(300):
+        cases.append((rng.choice([rng.uniform(0.01, 4.0), rng.randint(1, 8) / 4]),
+                      rng.randint(1, 8), rng.randint(1, 100000), rng.randint(8, 256)))
+    for c, k, T, E in cases:
+        k = min(k, E)
+        s = moe.make_shape(T, 128, E, k, 256, c=c)
+        assert moe.capacity(s) == O.capacity(c, k, T, E), (c, k, T, E)
+    assert moe.capacity(moe.make_shape(64, 128, 8, 2, 256)) == -1
+    assert moe.capacity(moe.make_shape(64, 128, 8, 2, 256, c=-1.0)) == -1
+
+
+def test_workspace_sizes():
+    s = moe.make_shape(4096, 4096, 8, 2, 14336)
+    sizes = [moe.workspace_size(s, c) for c in range(4)]
+    assert all(v > 0 for v in sizes)
+    assert sizes[moe.CALL_LAYER] > 3 * 4096 * 2 * 4096 * 2  # x_perm + out_perm + h at least
+    assert moe.workspace_size(s, 99) == 0
+    bad = moe.make_shape(0, 4096, 8, 2, 14336)
+    assert all(moe.workspace_size(bad, c) == 0 for c in range(4))
+    # capacity shrinks the routed buffers
+    capped = moe.make_shape(32768, 4096, 64, 2, 2048, c=1.0)
+    free = moe.make_shape(32768, 4096, 64, 2, 2048)
+    assert moe.workspace_size(capped, moe.CALL_LAYER) <= moe.workspace_size(free, moe.CALL_LAYER)
+
+
+def _fake(n=1):
+    # a well-aligned non-null address; never dereferenced because every call here fails its checks
+    return ctypes.c_void_p(4096 * n)
+
+
+def test_entry_points_reject_before_launch():
+    L = moe.lib()
+    s = moe.make_shape(64, 128, 8, 2, 256)
+    sp = ctypes.byref(s)
+    F = _fake
+    # missing required pointers
+    assert L.moe_route(sp, None, F(), None, F(), F(), F(), F(), F(), F(), 1 << 20, None) == 1
+    assert L.moe_dispatch(sp, F(), None, None, F(), F(), F(), F(), F(), F(), 1 << 20, None) == 1
+    assert L.moe_combine(sp, None, F(), F(), None, F(), None) == 1
+    assert L.moe_balance_stats(sp, None, F(), F(), 0.01, None, None, None, None, None, None,
+                               1e-3, None) == 1
+    # b without b_new
+    assert L.moe_balance_stats(sp, F(), F(), F(), 0.01, None, None, None, None, F(), None,
+                               1e-3, None) == 1
+    # misaligned tensor
+    assert L.moe_combine(sp, ctypes.c_void_p(4096 + 4), F(), F(), None, F(), None) == 1
+    # workspace missing or too small
+    assert L.moe_route(sp, F(), F(), None, F(), F(), F(), F(), F(), None, 0, None) == 3
+    need = moe.workspace_size(s, moe.CALL_ROUTE)
+    assert L.moe_route(sp, F(), F(), None, F(), F(), F(), F(), F(), F(), need - 1, None) == 3
+    assert L.moe_dispatch(sp, F(), F(), None, F(), F(), F(), F(), F(), None, 0, None) == 3
+    assert L.moe_expert_ffn(sp, 8, 256, F(), F(), 128, F(), F(), F(), F(), F(), None, 0, None) == 3
+    # expert FFN argument checks
+    assert L.moe_expert_ffn(sp, 0, 256, F(), F(), 128, F(), F(), F(), F(), F(), F(), 1 << 20,
+                            None) == 1
+    assert L.moe_expert_ffn(sp, 300, 256, F(), F(), 128, F(), F(), F(), F(), F(), F(), 1 << 20,
+                            None) == 2
+    assert L.moe_expert_ffn(sp, 8, 250, F(), F(), 128, F(), F(), F(), F(), F(), F(), 1 << 20,
+                            None) == 1
+    # layer: shared experts required when S > 0; b_new requires b
+    s2 = moe.make_shape(64, 128, 8, 2, 256, S=2)
+    ws = moe.workspace_size(s2, moe.CALL_LAYER)
+    # x, W_r, b, W_gate, W_up, W_down, Ws_gate/up/down, y, 9 optional outputs, lambda, gamma, ws
+    args = [F()] * 2 + [None] + [F()] * 3 + [None] * 3 + [F()] + [None] * 9 + [0.01, 1e-3, F(), ws,
+                                                                              None]
+    assert L.moe_layer_forward(ctypes.byref(s2), *args) == 1
+    args = [F()] * 2 + [None] + [F()] * 3 + [None] * 3 + [F()] + [None] * 8 + [F(), 0.01, 1e-3,
+                                                                              F(), ws, None]
+    assert L.moe_layer_forward(sp, *args) == 1
+    # invalid shape short-circuits everything
+    bad = moe.make_shape(64, 128, 8, 9, 256)
+    assert L.moe_route(ctypes.byref(bad), F(), F(), None, F(), F(), F(), F(), F(), F(), 1 << 30,
+                       None) == 1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(moe, "_lib_handle", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        moe.lib()
