@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""MoE-layer forward benchmark on one MI355X.
+
+A step is one moe_layer_forward over the whole routing batch (route, dispatch, grouped SwiGLU
+experts, shared experts, combine, statistics) with every input already resident in HBM. The
+default workload is the Mixtral-8x7B-shaped layer (T=4096, d=4096, E=8, k=2, M=14336, bf16).
+
+Prints one JSON line: tokens/s, the dominant kernel's roofline (per-launch duration from HIP
+events recorded between the library's stages on its stream), per-stage figures, and the CPU
+oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "MoE-layer fwd tokens/sec + % bf16 MFMA peak, Mixtral-8x7B-shaped layer"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_up_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="also run one plain device copy of this many bytes (counter calibration)")
+    return ap.parse_args()
+
+
+def gemm_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm_bf16.hip", "moe_internal.h"):
+        with open(os.path.join(ROOT, "mixture_experts_layer_loss_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """Counter-measured HBM bytes per launch of the gate/up GEMM, if taken on the current source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    entry = t.get(workload)
+    if not entry or entry.get("source_sha") != gemm_source_sha():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, seconds: float):
+    """The oracle as it stands, on the first T' tokens of the same inputs (fp64, host BLAS)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as O
+
+    shared = [tuple(t for t in s) for s in inp.shared]
+
+    def run(n):
+        t0 = time.perf_counter()
+        O.layer_forward(inp.x[:n], inp.W_r, inp.W_gate, inp.W_up, inp.W_down, cfg.k,
+                        b=inp.b, shared=shared, c=cfg.c, renorm=cfg.renorm, lam=cfg.lam,
+                        gamma=cfg.gamma)
+        return time.perf_counter() - t0
+
+    # fixed cost (weight upcasts) plus a per-token cost, from two probes
+    p1, p2 = min(cfg.T, 32), min(cfg.T, 96)
+    t1, t2 = run(p1), run(p2)
+    per_tok = max((t2 - t1) / max(p2 - p1, 1), 1e-6)
+    fixed = max(t1 - per_tok * p1, 0.0)
+    n = int(min(cfg.T, max(p2, (seconds - fixed) / per_tok)))
+    n = max(32, (n // 32) * 32)
+    dt = run(n)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    note = "" if cfg.c is None else "; capacity applied within the sample"
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of {cfg.T} tokens of the same layer (all {cfg.E} experts' weights), "
+                      f"fp64 NumPy oracle, {dt:.1f} s{note}",
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the layer on a single MI355X and "
+              "has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_loss_amd as moe
+    import workloads
+
+    name = args.workload or workloads.HEADLINE
+    cfg = workloads.CONFIGS[name]
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    print(f"[bench] generating {name} inputs", file=sys.stderr, flush=True)
+    host = workloads.make_inputs(cfg)
+    x = host.x.to(dev)
+    W_r = host.W_r.to(dev)
+    Wg = host.W_gate.to(dev)
+    Wu = host.W_up.to(dev)
+    Wd = host.W_down.to(dev)
+    b = None if host.b is None else host.b.to(dev)
+    sh = host.shared_fused()
+    sh = None if sh is None else tuple(t.to(dev) for t in sh)
+
+    layer = moe.MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.M, cfg.S, cfg.c, cfg.renorm, dt, dev)
+    out = layer.alloc_outputs(with_bias=b is not None)
+
+    def step():
+        layer.forward(x, W_r, Wg, Wu, Wd, b, sh, cfg.lam, cfg.gamma, out=out)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # stage events for every timed step (recorded by the library on its stream)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.STAGE_COUNT)]
+              for _ in range(args.steps)]
+    stream = torch.cuda.current_stream()
+    for evs in events:
+        for ev in evs:
+            ev.record(stream)
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        moe.moe_set_stage_events(events[i])
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    moe.moe_set_stage_events(None)
+
+    if args.copy_bytes > 0:  # one plain copy of known size, for counter calibration
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = np.zeros(len(moe.STAGES))
+    for evs in events:
+        for s_ in range(1, moe.STAGE_COUNT):
+            stage_ms[s_ - 1] += evs[s_ - 1].elapsed_time(evs[s_])
+    stage_ms /= args.steps
+
+    counts = out["counts"].cpu().numpy().astype(np.int64)
+    overflow = out["overflow"].cpu().numpy().astype(np.int64)
+    kept = int((counts - overflow).sum())
+    T, d, E, k, M, S = cfg.T, cfg.d, cfg.E, cfg.k, cfg.M, cfg.S
+    eb = 2 if cfg.dtype == "bf16" else 4
+    fl = {"gemm_up": 4.0 * d * M * kept, "gemm_down": 2.0 * d * M * kept,
+          "shared": 6.0 * d * S * M * T, "route": 2.0 * d * E * T}
+    by = {"route": T * d * eb + E * d * eb + T * k * 8,
+          "dispatch": T * d * eb + kept * d * eb + T * k * 8 + kept * 4,
+          "combine": kept * d * eb + T * k * 8 + (T * d * eb if S else 0) + T * d * eb}
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    stages = {}
+    for i, nm in enumerate(moe.STAGES):
+        ms = float(stage_ms[i])
+        st = {"ms": round(ms, 4)}
+        if nm in fl and ms > 0 and fl[nm] > 0:
+            tf = fl[nm] / (ms * 1e-3) / 1e12
+            st.update({"tflops": round(tf, 1), "mfma_frac": round(tf / peak, 4)})
+        if nm in by and ms > 0:
+            gb = by[nm] / (ms * 1e-3) / 1e9
+            st.update({"gbs": round(gb, 1), "hbm_frac": round(gb / PEAK_HBM_GBS, 4)})
+        stages[nm] = st
+
+    total_flops = fl["gemm_up"] + fl["gemm_down"] + fl["shared"] + fl["route"]
+    layer_tf = total_flops / (ms_step * 1e-3) / 1e12
+    up_ms = float(stage_ms[moe.STAGES.index("gemm_up")])
+    achieved = fl["gemm_up"] / (up_ms * 1e-3) / 1e12
+    traffic = load_traffic(name)
+    roofline = {"bound": "mfma", "kernel": "grouped_gemm_kernel<0> (routed gate/up + SwiGLU)",
+                "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "flops_per_launch": fl["gemm_up"], "ms_per_launch": round(up_ms, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, host, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(T / (ms_step * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": name, "T": T, "d": d, "E": E, "k": k, "M": M, "S": S,
+                   "capacity_factor": cfg.c, "bias": cfg.bias, "kept_assignments": kept,
+                   "dropped_assignments": int(overflow.sum()), "max_load": int(counts.max())},
+        "mfma_peak_frac_layer": round(layer_tf / peak, 4), "layer_tflops": round(layer_tf, 1),
+        "roofline": roofline, "stages": stages, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -200,6 +200,17 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
                              float* f, float* P, float* aux, float* z, float* b_new, float lambda,
                              float gamma, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * moe_set_stage_events -- profiling aid for moe_layer_forward (not a step of the method).
+ * When `events` is non-NULL, later moe_layer_forward calls record events[i] (hipEvent_t handles
+ * owned by the caller, count >= MOE_STAGE_COUNT) on their stream at the end of each stage:
+ *   0 start, 1 route, 2 scan + placement + row copies, 3 routed gate/up GEMM (SwiGLU),
+ *   4 routed down GEMM, 5 shared experts (both GEMMs), 6 combine, 7 statistics.
+ * NULL turns recording off. Process-wide setting; not thread-safe.
+ */
+#define MOE_STAGE_COUNT 8
+moe_status moe_set_stage_events(void* const* events, int count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -56,7 +56,11 @@ _SIG = {
     "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                          _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                          ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "moe_set_stage_events": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]),
 }
+
+STAGES = ["route", "dispatch", "gemm_up", "gemm_down", "shared", "combine", "stats"]
+STAGE_COUNT = 8
 
 _lib_handle = None
 
@@ -313,6 +317,21 @@ class MoELayer:
         return out
 
 
+def moe_set_stage_events(events) -> None:
+    """Profiling aid: record ``events`` (8 torch.cuda.Event, timing enabled) at the end of each
+    stage of later moe_layer_forward calls; None switches recording off."""
+    if events is None:
+        _check(lib().moe_set_stage_events(None, 0), "moe_set_stage_events")
+        return
+    arr = (ctypes.c_void_p * len(events))()
+    stream = torch.cuda.current_stream()
+    for i, ev in enumerate(events):
+        if not ev.cuda_event:
+            ev.record(stream)  # torch creates the HIP event on its first record
+        arr[i] = ev.cuda_event
+    _check(lib().moe_set_stage_events(arr, len(events)), "moe_set_stage_events")
+
+
 def moe_layer_forward(x, W_r, W_gate, W_up, W_down, k: int, b=None, shared=None,
                       c: Optional[float] = None, renorm: bool = True, lam: float = 0.01,
                       gamma: float = 1e-3) -> dict:
@@ -328,4 +347,4 @@ def moe_layer_forward(x, W_r, W_gate, W_up, W_down, k: int, b=None, shared=None,
 
 __all__ = ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_balance_stats",
            "moe_layer_forward", "MoELayer", "make_shape", "capacity", "workspace_size",
-           "check_shape", "status_string", "lib", "MoEError", "Shape"]
+           "check_shape", "status_string", "lib", "MoEError", "Shape", "moe_set_stage_events"]

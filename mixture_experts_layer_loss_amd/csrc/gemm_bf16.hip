@@ -222,19 +222,20 @@ hipError_t launch_gemm(const bf16_t* A, const int32_t* offsets, const int32_t* t
 
 }  // namespace
 
-hipError_t launch_expert_ffn_bf16(int groups, int d, int Mg, const void* rows,
-                                  const int32_t* offsets, const int32_t* tile_off,
-                                  int64_t max_tiles, const void* W_gate, const void* W_up,
-                                  const void* W_down, void* h, void* out, hipStream_t st) {
-  const int64_t gs = static_cast<int64_t>(Mg) * d;
-  hipError_t e = launch_gemm<0>(static_cast<const bf16_t*>(rows), offsets, tile_off, groups,
-                                max_tiles, static_cast<const bf16_t*>(W_gate),
-                                static_cast<const bf16_t*>(W_up), gs, Mg, d,
-                                static_cast<bf16_t*>(h), st);
-  if (e != hipSuccess) return e;
+hipError_t launch_gemm_up_bf16(int groups, int d, int Mg, const void* rows,
+                               const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
+                               const void* W_gate, const void* W_up, void* h, hipStream_t st) {
+  return launch_gemm<0>(static_cast<const bf16_t*>(rows), offsets, tile_off, groups, max_tiles,
+                        static_cast<const bf16_t*>(W_gate), static_cast<const bf16_t*>(W_up),
+                        static_cast<int64_t>(Mg) * d, Mg, d, static_cast<bf16_t*>(h), st);
+}
+
+hipError_t launch_gemm_down_bf16(int groups, int d, int Mg, const int32_t* offsets,
+                                 const int32_t* tile_off, int64_t max_tiles, const void* W_down,
+                                 const void* h, void* out, hipStream_t st) {
   return launch_gemm<1>(static_cast<const bf16_t*>(h), offsets, tile_off, groups, max_tiles,
-                        static_cast<const bf16_t*>(W_down), nullptr, gs, d, Mg,
-                        static_cast<bf16_t*>(out), st);
+                        static_cast<const bf16_t*>(W_down), nullptr,
+                        static_cast<int64_t>(Mg) * d, d, Mg, static_cast<bf16_t*>(out), st);
 }
 
 }  // namespace moe

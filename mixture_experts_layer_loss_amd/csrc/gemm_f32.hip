@@ -87,29 +87,28 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
 
 }  // namespace
 
-hipError_t launch_expert_ffn_f32(int groups, int d, int Mg, const void* rows,
-                                 const int32_t* offsets, const int32_t* tile_off,
-                                 int64_t max_tiles, const void* W_gate, const void* W_up,
-                                 const void* W_down, void* h, void* out, hipStream_t st) {
-  const int64_t gs = static_cast<int64_t>(Mg) * d;
-  int64_t grid = max_tiles * cdiv(Mg, BN);
-  if (grid > 0) {
-    hipLaunchKernelGGL(grouped_gemm_f32_kernel<0>, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
-                       st, static_cast<const float*>(rows), offsets, tile_off, groups,
-                       static_cast<const float*>(W_gate), static_cast<const float*>(W_up), gs, Mg,
-                       d, static_cast<float*>(h));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  grid = max_tiles * cdiv(d, BN);
-  if (grid > 0) {
-    hipLaunchKernelGGL(grouped_gemm_f32_kernel<1>, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
-                       st, static_cast<const float*>(h), offsets, tile_off, groups,
-                       static_cast<const float*>(W_down), nullptr, gs, d, Mg,
-                       static_cast<float*>(out));
-    return hipGetLastError();
-  }
-  return hipSuccess;
+hipError_t launch_gemm_up_f32(int groups, int d, int Mg, const void* rows,
+                              const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
+                              const void* W_gate, const void* W_up, void* h, hipStream_t st) {
+  const int64_t grid = max_tiles * cdiv(Mg, BN);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(grouped_gemm_f32_kernel<0>, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                     st, static_cast<const float*>(rows), offsets, tile_off, groups,
+                     static_cast<const float*>(W_gate), static_cast<const float*>(W_up),
+                     static_cast<int64_t>(Mg) * d, Mg, d, static_cast<float*>(h));
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_down_f32(int groups, int d, int Mg, const int32_t* offsets,
+                                const int32_t* tile_off, int64_t max_tiles, const void* W_down,
+                                const void* h, void* out, hipStream_t st) {
+  const int64_t grid = max_tiles * cdiv(d, BN);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(grouped_gemm_f32_kernel<1>, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                     st, static_cast<const float*>(h), offsets, tile_off, groups,
+                     static_cast<const float*>(W_down), nullptr, static_cast<int64_t>(Mg) * d, d,
+                     Mg, static_cast<float*>(out));
+  return hipGetLastError();
 }
 
 }  // namespace moe

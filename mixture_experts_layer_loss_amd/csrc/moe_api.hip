@@ -7,26 +7,36 @@
 #include "moe_internal.h"
 
 namespace moe {
-hipError_t launch_expert_ffn_bf16(int groups, int d, int Mg, const void* rows,
-                                  const int32_t* offsets, const int32_t* tile_off,
-                                  int64_t max_tiles, const void* W_gate, const void* W_up,
-                                  const void* W_down, void* h, void* out, hipStream_t st);
-hipError_t launch_expert_ffn_f32(int groups, int d, int Mg, const void* rows,
-                                 const int32_t* offsets, const int32_t* tile_off,
-                                 int64_t max_tiles, const void* W_gate, const void* W_up,
-                                 const void* W_down, void* h, void* out, hipStream_t st);
-hipError_t launch_shared_table(int64_t T, int BM, int32_t* offsets, int32_t* tile_off,
-                               hipStream_t st);
+hipError_t launch_gemm_up_bf16(int groups, int d, int Mg, const void* rows,
+                               const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
+                               const void* W_gate, const void* W_up, void* h, hipStream_t st);
+hipError_t launch_gemm_down_bf16(int groups, int d, int Mg, const int32_t* offsets,
+                                 const int32_t* tile_off, int64_t max_tiles, const void* W_down,
+                                 const void* h, void* out, hipStream_t st);
+hipError_t launch_gemm_up_f32(int groups, int d, int Mg, const void* rows,
+                              const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
+                              const void* W_gate, const void* W_up, void* h, hipStream_t st);
+hipError_t launch_gemm_down_f32(int groups, int d, int Mg, const int32_t* offsets,
+                                const int32_t* tile_off, int64_t max_tiles, const void* W_down,
+                                const void* h, void* out, hipStream_t st);
 
-hipError_t launch_expert_ffn(int dtype, int groups, int d, int Mg, const void* rows,
-                             const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
-                             const void* W_gate, const void* W_up, const void* W_down, void* h,
-                             void* out, hipStream_t st) {
-  if (dtype == MOE_F32)
-    return launch_expert_ffn_f32(groups, d, Mg, rows, offsets, tile_off, max_tiles, W_gate, W_up,
-                                 W_down, h, out, st);
-  return launch_expert_ffn_bf16(groups, d, Mg, rows, offsets, tile_off, max_tiles, W_gate, W_up,
-                                W_down, h, out, st);
+hipError_t launch_gemm_up(int dtype, int groups, int d, int Mg, const void* rows,
+                          const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
+                          const void* W_gate, const void* W_up, void* h, hipStream_t st) {
+  return dtype == MOE_F32
+             ? launch_gemm_up_f32(groups, d, Mg, rows, offsets, tile_off, max_tiles, W_gate, W_up,
+                                  h, st)
+             : launch_gemm_up_bf16(groups, d, Mg, rows, offsets, tile_off, max_tiles, W_gate,
+                                   W_up, h, st);
+}
+
+hipError_t launch_gemm_down(int dtype, int groups, int d, int Mg, const int32_t* offsets,
+                            const int32_t* tile_off, int64_t max_tiles, const void* W_down,
+                            const void* h, void* out, hipStream_t st) {
+  return dtype == MOE_F32 ? launch_gemm_down_f32(groups, d, Mg, offsets, tile_off, max_tiles,
+                                                 W_down, h, out, st)
+                          : launch_gemm_down_bf16(groups, d, Mg, offsets, tile_off, max_tiles,
+                                                  W_down, h, out, st);
 }
 }  // namespace moe
 
@@ -138,6 +148,14 @@ LayerPlan plan_layer(Carve& c, const moe_shape* s) {
 }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Profiling aid: events recorded at the end of each moe_layer_forward stage (see moe.h).
+hipEvent_t g_stage_events[MOE_STAGE_COUNT] = {};
+bool g_stage_on = false;
+
+void mark_stage(int i, hipStream_t st) {
+  if (g_stage_on && g_stage_events[i] != nullptr) (void)hipEventRecord(g_stage_events[i], st);
+}
 
 }  // namespace
 
@@ -256,8 +274,11 @@ moe_status moe_expert_ffn(const moe_shape* s, int32_t groups, int32_t Mg, const 
   hipError_t e = launch_schedule(groups, offsets, tile_off, BM, hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
   const int64_t max_tiles = cdiv(max_rows, BM) + groups;
-  e = launch_expert_ffn(s->dtype, groups, s->d, Mg, rows, offsets, tile_off, max_tiles, W_gate,
-                        W_up, W_down, h, out, hs);
+  e = launch_gemm_up(s->dtype, groups, s->d, Mg, rows, offsets, tile_off, max_tiles, W_gate, W_up,
+                     h, hs);
+  if (e == hipSuccess)
+    e = launch_gemm_down(s->dtype, groups, s->d, Mg, offsets, tile_off, max_tiles, W_down, h, out,
+                         hs);
   return hip_status(e);
 }
 
@@ -315,31 +336,59 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
   const int nblk = static_cast<int>(nblocks(s));
   const int eb = elem_bytes(s);
 
+  const int64_t max_tiles = cdiv(routed_rows(s), BM) + s->E;
+
+  mark_stage(0, hs);
   hipError_t e = launch_route(s->dtype, s->T, s->d, s->E, s->k, s->renorm, x, W_r, b, idx, w,
                               p.r.hist, p.r.gpart, p.r.lpart, hs);
+  mark_stage(1, hs);
   if (e == hipSuccess)
     e = launch_scan(s->T, s->E, C, nblk, p.r.hist, p.r.gpart, p.r.lpart, p.block_base, n, p.gsum,
                     p.lse2sum, p.kept, ovf, p.offsets, p.tile_off, BM, hs);
   if (e == hipSuccess)
     e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx, p.block_base, p.offsets, p.x_perm,
                        p.perm_token, p.inv_perm, hs);
+  mark_stage(2, hs);
   if (e == hipSuccess)
-    e = launch_expert_ffn(s->dtype, s->E, s->d, s->M, p.x_perm, p.offsets, p.tile_off,
-                          cdiv(routed_rows(s), BM) + s->E, W_gate, W_up, W_down, p.h, p.out_perm,
-                          hs);
+    e = launch_gemm_up(s->dtype, s->E, s->d, s->M, p.x_perm, p.offsets, p.tile_off, max_tiles,
+                       W_gate, W_up, p.h, hs);
+  mark_stage(3, hs);
+  if (e == hipSuccess)
+    e = launch_gemm_down(s->dtype, s->E, s->d, s->M, p.offsets, p.tile_off, max_tiles, W_down,
+                         p.h, p.out_perm, hs);
+  mark_stage(4, hs);
   if (e == hipSuccess && s->S > 0) {
+    const int SM = s->S * s->M;
+    const int64_t sh_tiles = cdiv(s->T, BM);
     e = launch_shared_table(s->T, BM, p.sh_offsets, p.sh_tile_off, hs);
     if (e == hipSuccess)
-      e = launch_expert_ffn(s->dtype, 1, s->d, s->S * s->M, x, p.sh_offsets, p.sh_tile_off,
-                            cdiv(s->T, BM), Ws_gate, Ws_up, Ws_down, p.h_sh, p.sh, hs);
+      e = launch_gemm_up(s->dtype, 1, s->d, SM, x, p.sh_offsets, p.sh_tile_off, sh_tiles, Ws_gate,
+                         Ws_up, p.h_sh, hs);
+    if (e == hipSuccess)
+      e = launch_gemm_down(s->dtype, 1, s->d, SM, p.sh_offsets, p.sh_tile_off, sh_tiles, Ws_down,
+                           p.h_sh, p.sh, hs);
   }
+  mark_stage(5, hs);
   if (e == hipSuccess)
     e = launch_combine(s->dtype, s->T, s->d, s->k, p.out_perm, p.inv_perm, w,
                        s->S > 0 ? p.sh : nullptr, y, hs);
+  mark_stage(6, hs);
   if (e == hipSuccess && (f || P || aux || z || b_new))
     e = launch_stats(s->T, s->E, s->k, n, p.gsum, p.lse2sum, lambda, f, P, aux, z,
                      b_new ? b : nullptr, b_new, gamma, hs);
+  mark_stage(7, hs);
   return hip_status(e);
+}
+
+moe_status moe_set_stage_events(void* const* events, int count) {
+  if (events == nullptr) {
+    g_stage_on = false;
+    return MOE_OK;
+  }
+  if (count < MOE_STAGE_COUNT) return MOE_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < MOE_STAGE_COUNT; ++i) g_stage_events[i] = static_cast<hipEvent_t>(events[i]);
+  g_stage_on = true;
+  return MOE_OK;
 }
 
 }  // extern "C"

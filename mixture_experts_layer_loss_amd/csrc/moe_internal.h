@@ -73,11 +73,19 @@ hipError_t launch_scatter(int64_t T, int d, int E, int k, int64_t C, int elem_by
 hipError_t launch_schedule(int groups, const int32_t* offsets, int32_t* tile_off, int BM,
                            hipStream_t st);
 
-// Grouped SwiGLU FFN. max_tiles = upper bound of sum_g ceil(rows_g / BM).
-hipError_t launch_expert_ffn(int dtype, int groups, int d, int Mg, const void* rows,
-                             const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
-                             const void* W_gate, const void* W_up, const void* W_down, void* h,
-                             void* out, hipStream_t st);
+// Grouped SwiGLU FFN in two launches. max_tiles = upper bound of sum_g ceil(rows_g / BM).
+//   gate/up: h[r] = SiLU(rows[r] W_gate[g]^T) * (rows[r] W_up[g]^T)
+//   down:    out[r] = h[r] W_down[g]^T
+hipError_t launch_gemm_up(int dtype, int groups, int d, int Mg, const void* rows,
+                          const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
+                          const void* W_gate, const void* W_up, void* h, hipStream_t st);
+hipError_t launch_gemm_down(int dtype, int groups, int d, int Mg, const int32_t* offsets,
+                            const int32_t* tile_off, int64_t max_tiles, const void* W_down,
+                            const void* h, void* out, hipStream_t st);
+
+// Tile table of the shared experts (one group of all T rows).
+hipError_t launch_shared_table(int64_t T, int BM, int32_t* offsets, int32_t* tile_off,
+                               hipStream_t st);
 
 // y_t = sum_j w_tj out_perm[inv_tj] (+ shared_t).
 hipError_t launch_combine(int dtype, int64_t T, int d, int k, const void* out_perm,
