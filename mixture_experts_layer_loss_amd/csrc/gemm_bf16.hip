@@ -22,6 +22,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <type_traits>
 
 namespace moe {
 namespace {
@@ -33,6 +34,7 @@ constexpr int NXCD = 8;
 constexpr int kStageElems = (BM + BN) * BK;  // bf16 elements per LDS stage (64 KiB)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native 16-byte value (no struct copy)
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // element offset of 16-byte chunk `c` (0..7) of row `r` in a [rows][64] swizzled slice
@@ -40,8 +42,28 @@ __device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ ((r >> 
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100, kSgDsWrite = 0x200;
+
+// Schedule of one sub-step: one MFMA then one fragment read (x8), then 8 MFMAs each followed by
+// EXTRA_PER instructions of group EXTRA_MASK (LDS stores or global loads), if any.
+template <int EXTRA_MASK, int EXTRA_PER>
+__device__ __forceinline__ void sched_substep() {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    if (EXTRA_PER > 0) __builtin_amdgcn_sched_group_barrier(EXTRA_MASK, EXTRA_PER, 0);
+  }
+}
+
 // EPI 0: SwiGLU (B0 = W_gate, B1 = W_up, 128 output columns per tile); EPI 1: plain (B0 = W_down).
-template <int EPI>
+// KTAIL: K is not a multiple of 64 (the last k-slice is zero-padded).
+template <int EPI, bool KTAIL>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tile_off, int groups, const bf16_t* __restrict__ B0,
@@ -71,51 +93,63 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  const int rows_here = row_end - row_begin;
+  unsigned char* lds = reinterpret_cast<unsigned char*>(smem);
 
-  // ---- global source rows of this thread's 8 A chunks and 8 B chunks (fixed over K)
-  const bf16_t* a_src[8];
-  const bf16_t* b_src[8];
-  const bf16_t* Bg0 = B0 + static_cast<int64_t>(g) * group_stride;
-  const bf16_t* Bg1 = EPI == 0 ? B1 + static_cast<int64_t>(g) * group_stride : nullptr;
+  // ---- global loads: thread `tid` moves chunk (tid & 7) of rows r0 + 32 i (i = 0..7) of the A and
+  // B k-slices. Addresses are uniform tile bases plus 32-bit byte offsets fixed over K; rows past
+  // the group (A) or past N (B) re-read the last valid row and never reach a stored output.
+  const int r0 = tid >> 3, kc_t = (tid & 7) * 8;
+  const char* a_base = reinterpret_cast<const char*>(A + static_cast<int64_t>(row_begin) * K);
+  const bf16_t* Bg0 = B0 + static_cast<int64_t>(g) * group_stride + static_cast<int64_t>(n0) * K;
+  const bf16_t* Bg1 =
+      EPI == 0 ? B1 + static_cast<int64_t>(g) * group_stride + static_cast<int64_t>(n0) * K : Bg0;
+  const char* b_base0 = reinterpret_cast<const char*>(Bg0);
+  const char* b_base1 = reinterpret_cast<const char*>(Bg1);
+  const int b_rows = min(EPI == 0 ? BN / 2 : BN, N - n0);
+  uint32_t a_off[8], b_off[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int c = i * 256 + tid, r = c >> 3, kc = (c & 7) * 8;
-    const int ar = min(row_begin + r, row_end - 1);
-    a_src[i] = A + static_cast<int64_t>(ar) * K + kc;
-    int br;
-    const bf16_t* base;
-    if (EPI == 0) {
-      base = r < BN / 2 ? Bg0 : Bg1;
-      br = min(n0 + (r & (BN / 2 - 1)), N - 1);
-    } else {
-      base = Bg0;
-      br = min(n0 + r, N - 1);
-    }
-    b_src[i] = base + static_cast<int64_t>(br) * K + kc;
+    const int r = i * 32 + r0;
+    a_off[i] = static_cast<uint32_t>((min(r, rows_here - 1) * K + kc_t) * 2);
+    const int rb_ = EPI == 0 ? (r & (BN / 2 - 1)) : r;
+    b_off[i] = static_cast<uint32_t>((min(rb_, b_rows - 1) * K + kc_t) * 2);
   }
-
-  uint4 ra[8], rb[8];
-  const int kc_t = (tid & 7) * 8;  // this thread's chunk column (the same for all 8 chunks)
-  auto gload = [&](int k0) {
-    // branch-free: a chunk past K reads the row's last chunk and is then zeroed
-    const bool in = k0 + kc_t < K;
-    const int ko = in ? k0 : K - 8 - kc_t;
+  u32x4 ra[8], rb[8];
+  auto gload = [&](int k0) __attribute__((always_inline)) {
+    if (KTAIL) {
+      // a chunk past K re-reads the row's last chunk and is then zeroed
+      const bool in = k0 + kc_t < K;
+      const uint32_t kb = static_cast<uint32_t>((in ? k0 : K - 8 - kc_t) * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint4 va = *reinterpret_cast<const uint4*>(a_src[i] + ko);
-      const uint4 vb = *reinterpret_cast<const uint4*>(b_src[i] + ko);
-      ra[i] = in ? va : make_uint4(0, 0, 0, 0);
-      rb[i] = in ? vb : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < 8; ++i) {
+        const char* bb = (EPI == 0 && i >= 4) ? b_base1 : b_base0;
+        const u32x4 va = *reinterpret_cast<const u32x4*>(a_base + (a_off[i] + kb));
+        const u32x4 vb = *reinterpret_cast<const u32x4*>(bb + (b_off[i] + kb));
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        ra[i] = in ? va : zero;
+        rb[i] = in ? vb : zero;
+      }
+    } else {
+      const uint32_t kb = static_cast<uint32_t>(k0 * 2);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const char* bb = (EPI == 0 && i >= 4) ? b_base1 : b_base0;
+        ra[i] = *reinterpret_cast<const u32x4*>(a_base + (a_off[i] + kb));
+        rb[i] = *reinterpret_cast<const u32x4*>(bb + (b_off[i] + kb));
+      }
     }
   };
-  auto lstore = [&](int stage) {
-    bf16_t* sa = smem + stage * kStageElems;
-    bf16_t* sb = sa + BM * BK;
+  // LDS byte offset of this thread's chunk of row r0; row r0 + 32 i sits 32 * 128 B further on
+  // (the swizzle term depends on (r >> 1) & 7, which is the same for all i)
+  const uint32_t st_off = static_cast<uint32_t>(swz(r0, tid & 7) * 2);
+  constexpr uint32_t kStageBytes = kStageElems * 2, kBBytes = BM * BK * 2;
+  auto lstore = [&](int stage) __attribute__((always_inline)) {
+    unsigned char* sa = lds + stage * kStageBytes + st_off;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int c = i * 256 + tid, r = c >> 3, kc = c & 7;
-      *reinterpret_cast<uint4*>(sa + swz(r, kc)) = ra[i];
-      *reinterpret_cast<uint4*>(sb + swz(r, kc)) = rb[i];
+      *reinterpret_cast<u32x4*>(sa + i * 32 * BK * 2) = ra[i];
+      *reinterpret_cast<u32x4*>(sa + kBBytes + i * 32 * BK * 2) = rb[i];
     }
   };
 
@@ -127,40 +161,87 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // B-tile rows of this wave's four 32-column blocks
-  int brow[4];
+  // ---- MFMA fragments: lane l reads row (l % 32) of a 32-row block, k-chunk 2*sub + l/32.
+  // Every block starts at a multiple of 32 rows, so the swizzle term is the lane's own.
+  const int l32 = lane & 31, lk = lane >> 5, sw = (l32 >> 1) & 7;
+  uint32_t fo[4];
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub)
+    fo[sub] = static_cast<uint32_t>((l32 * BK + (((sub * 2 + lk) ^ sw) << 3)) * 2);
+  int brow[4];  // B-tile rows of this wave's four 32-column blocks
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     brow[j] = EPI == 0 ? ((j < 2 ? 0 : BN / 2) + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32);
-  const int l32 = lane & 31, lk = lane >> 5;
-
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    const bf16_t* sa = smem + (kt & 1) * kStageElems;
-    const bf16_t* sb = sa + BM * BK;
+  bf16x8 fa[2][4], fb[2][4];
+  auto lfrag = [&](int set, int stage, int sub) __attribute__((always_inline)) {
+    const unsigned char* sa = lds + stage * kStageBytes + fo[sub];
 #pragma unroll
-    for (int sub = 0; sub < BK / 16; ++sub) {
-      const int ch = sub * 2 + lk;
-      bf16x8 af[4], bfr[4];
+    for (int i = 0; i < 4; ++i)
+      fa[set][i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 128 + i * 32) * BK * 2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(sa + swz(wm * 128 + i * 32 + l32, ch));
+    for (int j = 0; j < 4; ++j)
+      fb[set][j] = *reinterpret_cast<const bf16x8*>(sa + kBBytes + brow[j] * BK * 2);
+  };
+  auto mfmas = [&](int set) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(sb + swz(brow[j] + l32, ch));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+  };
+  // ---- main loop. A k-step (64 of K) is 4 sub-steps of 16 MFMAs on stage `cur`:
+  //   sub 0: read fragments of sub 1                    | MFMAs of sub 0
+  //   sub 1: read fragments of sub 2, store stage cur^1 | MFMAs of sub 1
+  //   sub 2: read fragments of sub 3, load k-step +2    | MFMAs of sub 2
+  //   barrier (stage cur^1 complete; every read of stage cur issued)
+  //   sub 3: read fragments of sub 0 of stage cur^1     | MFMAs of sub 3
+  // Global loads run ~1.5 k-steps ahead; no LDS read waits on a barrier.
+  auto kstep = [&](int kt, auto has_next, auto has_load) __attribute__((always_inline)) {
+    constexpr bool NEXT = decltype(has_next)::value;  // a following k-step exists
+    constexpr bool LOAD = decltype(has_load)::value;  // k-step kt + 2 exists
+    const int cur = kt & 1;
+    lfrag(1, cur, 1);
+    mfmas(0);
+    sched_substep<0, 0>();
+    lfrag(0, cur, 2);
+    mfmas(1);
+    if constexpr (NEXT) {
+      lstore(cur ^ 1);
+      sched_substep<kSgDsWrite, 2>();
+    } else {
+      sched_substep<0, 0>();
     }
-    if (kt + 1 < nk) lstore((kt + 1) & 1);
+    lfrag(1, cur, 3);
+    mfmas(0);
+    if constexpr (LOAD) {
+      gload((kt + 2) * BK);
+      sched_substep<kSgVmemRead, 2>();
+    } else {
+      sched_substep<0, 0>();
+    }
     __syncthreads();
-  }
+    if constexpr (NEXT) {
+      lfrag(0, cur ^ 1, 0);
+      mfmas(1);
+      sched_substep<0, 0>();
+    } else {
+      mfmas(1);
+    }
+  };
+
+  const int nk = (K + BK - 1) / BK;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  gload(0);
+  lstore(0);
+  if (nk > 1) gload(BK);
+  __syncthreads();
+  lfrag(0, 0, 0);
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) kstep(kt, T_{}, T_{});
+  if (kt + 1 < nk) kstep(kt++, T_{}, F_{});
+  kstep(kt, F_{}, F_{});
+  __syncthreads();
 
   // ---- epilogue: registers -> LDS tile [BM][BNO + 8] (bf16) -> coalesced 16-byte stores
   constexpr int CS = BNO + 8;
@@ -186,7 +267,6 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
   }
   __syncthreads();
   constexpr int CPR = BNO / 8;  // 16-byte chunks per tile row
-  const int rows_here = row_end - row_begin;
   for (int c = tid; c < BM * CPR; c += 256) {
     const int r = c / CPR, cc = (c % CPR) * 8;
     if (r < rows_here && n0 + cc < N)
@@ -195,10 +275,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
   }
 }
 
-template <int EPI>
-hipError_t launch_gemm(const bf16_t* A, const int32_t* offsets, const int32_t* tile_off, int groups,
-                       int64_t max_tiles, const bf16_t* B0, const bf16_t* B1, int64_t group_stride,
-                       int N, int K, bf16_t* C, hipStream_t st) {
+template <int EPI, bool KTAIL>
+hipError_t launch_gemm_t(const bf16_t* A, const int32_t* offsets, const int32_t* tile_off, int groups,
+                         int64_t max_tiles, const bf16_t* B0, const bf16_t* B1, int64_t group_stride,
+                         int N, int K, bf16_t* C, hipStream_t st) {
   constexpr int BNO = EPI == 0 ? BN / 2 : BN;
   const int64_t nb = cdiv(N, BNO);
   const int64_t grid = cdiv(max_tiles * nb, NXCD) * NXCD;
@@ -208,16 +288,27 @@ hipError_t launch_gemm(const bf16_t* A, const int32_t* offsets, const int32_t* t
   const size_t lds = kMain > kEpi ? kMain : kEpi;
   static std::atomic<bool> attr_set{false};
   if (!attr_set.load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_kernel<EPI>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&grouped_gemm_kernel<EPI, KTAIL>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     attr_set.store(true, std::memory_order_release);
   }
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(grouped_gemm_kernel<EPI>, dim3(static_cast<unsigned>(grid)), dim3(256), lds,
+  hipLaunchKernelGGL((grouped_gemm_kernel<EPI, KTAIL>), dim3(static_cast<unsigned>(grid)), dim3(256), lds,
                      st, A, offsets, tile_off, groups, B0, B1, group_stride, N, K, C);
   return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_gemm(const bf16_t* A, const int32_t* offsets, const int32_t* tile_off, int groups,
+                       int64_t max_tiles, const bf16_t* B0, const bf16_t* B1, int64_t group_stride,
+                       int N, int K, bf16_t* C, hipStream_t st) {
+  if (K % BK == 0)
+    return launch_gemm_t<EPI, false>(A, offsets, tile_off, groups, max_tiles, B0, B1, group_stride,
+                                     N, K, C, st);
+  return launch_gemm_t<EPI, true>(A, offsets, tile_off, groups, max_tiles, B0, B1, group_stride, N,
+                                  K, C, st);
 }
 
 }  // namespace
