@@ -36,6 +36,21 @@ __global__ __launch_bounds__(256) void count_kernel(int64_t T, int E, int k,
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
 }
 
+// Tiles of a group of `rows` rows in the grouped GEMM's three classes (BM = 256): full 256-row
+// tiles, plus a remainder of 129..255 rows as one more 256-row tile, of 65..128 rows as a 128-row
+// tile, or of 1..64 rows as a 64-row tile. With any other BM all tiles are BM rows.
+__device__ __forceinline__ void tile_counts(int rows, int BM, int& t_main, int& t128, int& t64) {
+  if (BM != 256) {
+    t_main = (rows + BM - 1) / BM;
+    t128 = t64 = 0;
+    return;
+  }
+  const int rem = rows & 255;
+  t_main = (rows >> 8) + (rem > 128 ? 1 : 0);
+  t128 = (rem > 64 && rem <= 128) ? 1 : 0;
+  t64 = (rem > 0 && rem <= 64) ? 1 : 0;
+}
+
 // Inclusive scan over 256 ints in LDS (Hillis-Steele); every thread of the block must call it.
 __device__ int block_scan_256(int v, int* buf) {
   const int tid = threadIdx.x;
@@ -103,11 +118,21 @@ __global__ __launch_bounds__(256) void scan_kernel(
     offsets[e] = incl - kept;
     if (e == E - 1) offsets[E] = incl;
   }
-  const int mt = (e < E) ? (kept + BM - 1) / BM : 0;
-  const int tincl = block_scan_256(mt, sbuf);
+  // grouped-GEMM tile tables: [E+1] 256-row (or BM-row) tiles, [E+1] 128-row, [E+1] 64-row
+  int c0 = 0, c1 = 0, c2 = 0;
+  if (e < E) tile_counts(kept, BM, c0, c1, c2);
+  const int i0 = block_scan_256(c0, sbuf);
+  const int i1 = block_scan_256(c1, sbuf);
+  const int i2 = block_scan_256(c2, sbuf);
   if (e < E && tile_off != nullptr) {
-    tile_off[e] = tincl - mt;
-    if (e == E - 1) tile_off[E] = tincl;
+    tile_off[e] = i0 - c0;
+    tile_off[E + 1 + e] = i1 - c1;
+    tile_off[2 * (E + 1) + e] = i2 - c2;
+    if (e == E - 1) {
+      tile_off[E] = i0;
+      tile_off[2 * E + 1] = i1;
+      tile_off[3 * E + 2] = i2;
+    }
   }
   if (lse2sum != nullptr) {
     double ls = 0.0;
@@ -188,22 +213,37 @@ __global__ __launch_bounds__(256) void schedule_kernel(int groups, const int32_t
   __shared__ int sbuf[256];
   const int g = threadIdx.x;
   const int rows = g < groups ? offsets[g + 1] - offsets[g] : 0;
-  const int mt = rows > 0 ? (rows + BM - 1) / BM : 0;
-  const int incl = block_scan_256(mt, sbuf);
+  int c0 = 0, c1 = 0, c2 = 0;
+  if (g < groups && rows > 0) tile_counts(rows, BM, c0, c1, c2);
+  const int i0 = block_scan_256(c0, sbuf);
+  const int i1 = block_scan_256(c1, sbuf);
+  const int i2 = block_scan_256(c2, sbuf);
   if (g < groups) {
-    tile_off[g] = incl - mt;
-    if (g == groups - 1) tile_off[groups] = incl;
+    tile_off[g] = i0 - c0;
+    tile_off[groups + 1 + g] = i1 - c1;
+    tile_off[2 * (groups + 1) + g] = i2 - c2;
+    if (g == groups - 1) {
+      tile_off[groups] = i0;
+      tile_off[2 * groups + 1] = i1;
+      tile_off[3 * groups + 2] = i2;
+    }
   }
 }
 
-// Tile table of the shared experts: one group of all T rows.
+// Tile tables of the shared experts: one group of all T rows.
 __global__ void shared_table_kernel(int64_t T, int BM, int32_t* __restrict__ offsets,
                                     int32_t* __restrict__ tile_off) {
   if (threadIdx.x == 0) {
+    int c0, c1, c2;
+    tile_counts(static_cast<int>(T), BM, c0, c1, c2);
     offsets[0] = 0;
     offsets[1] = static_cast<int32_t>(T);
     tile_off[0] = 0;
-    tile_off[1] = static_cast<int32_t>((T + BM - 1) / BM);
+    tile_off[1] = c0;
+    tile_off[2] = 0;
+    tile_off[3] = c1;
+    tile_off[4] = 0;
+    tile_off[5] = c2;
   }
 }
 

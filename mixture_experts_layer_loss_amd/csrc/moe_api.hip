@@ -130,9 +130,9 @@ LayerPlan plan_layer(Carve& c, const moe_shape* s) {
   p.kept = c.take<int32_t>(s->E);
   p.overflow = c.take<int32_t>(s->E);
   p.offsets = c.take<int32_t>(s->E + 1);
-  p.tile_off = c.take<int32_t>(s->E + 1);
+  p.tile_off = c.take<int32_t>(3 * (s->E + 1));  // three tile classes of the grouped GEMM
   p.sh_offsets = c.take<int32_t>(2);
-  p.sh_tile_off = c.take<int32_t>(2);
+  p.sh_tile_off = c.take<int32_t>(3 * 2);
   p.perm_token = c.take<int32_t>(R);
   p.inv_perm = c.take<int32_t>(P);
   p.x_perm = c.take<unsigned char>(R * s->d * eb);
@@ -199,7 +199,7 @@ size_t moe_workspace_size(const moe_shape* s, int call) {
   switch (call) {
     case MOE_CALL_ROUTE: plan_route(c, s); break;
     case MOE_CALL_DISPATCH: plan_dispatch(c, s); break;
-    case MOE_CALL_EXPERT_FFN: c.take<int32_t>(MOE_E_MAX + 1); break;
+    case MOE_CALL_EXPERT_FFN: c.take<int32_t>(3 * (MOE_E_MAX + 1)); break;
     case MOE_CALL_LAYER: plan_layer(c, s); break;
     default: return 0;
   }

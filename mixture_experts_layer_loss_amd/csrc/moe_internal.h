@@ -57,7 +57,8 @@ hipError_t launch_count(int64_t T, int E, int k, const int32_t* topk_idx, int32_
 // One block: reduces the per-block partials (fp64, fixed order), scans loads over blocks, applies
 // the capacity and builds offsets and the grouped-GEMM tile table.
 //   block_base [nblk, E]; gsum/lse2sum/gpart/lpart may be NULL (dispatch-only use).
-//   tile_off [E+1]: exclusive prefix of ceil(kept_e / BM); written when non-NULL.
+//   tile_off [3 (E+1)]: grouped-GEMM tile tables (exclusive prefixes over groups) of 256-row,
+//   128-row and 64-row tiles when BM = 256, else of BM-row tiles and two zero tables.
 hipError_t launch_scan(int64_t T, int E, int64_t C, int nblk, const int32_t* hist,
                        const float* gpart, const float* lpart, int32_t* block_base, int32_t* n_out,
                        double* gsum, double* lse2sum, int32_t* kept, int32_t* overflow,
@@ -69,7 +70,7 @@ hipError_t launch_scatter(int64_t T, int d, int E, int k, int64_t C, int elem_by
                           const int32_t* offsets, void* x_perm, int32_t* perm_token,
                           int32_t* inv_perm, hipStream_t st);
 
-// Tile table of a grouped GEMM from device row offsets (stand-alone expert FFN).
+// Tile tables [3 (groups+1)] of a grouped GEMM from device row offsets (stand-alone expert FFN).
 hipError_t launch_schedule(int groups, const int32_t* offsets, int32_t* tile_off, int BM,
                            hipStream_t st);
 

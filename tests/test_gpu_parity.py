@@ -121,6 +121,9 @@ def test_dispatch(gpu, T, d, E, k, c, dtype):
     ([1000], 128, 256, torch.bfloat16),
     ([70, 0, 64, 3], 128, 96, torch.float32),
     ([0, 0, 5], 64, 64, torch.bfloat16),
+    # every tile class and its boundaries: remainders of 64, 65, 127, 128, 129, 192 rows
+    ([383, 129, 192, 65, 64, 128, 320, 449, 0, 640], 256, 384, torch.bfloat16),
+    ([64, 65, 127, 128, 129, 1], 200, 136, torch.bfloat16),   # with K and N tails
 ])
 def test_expert_ffn(gpu, sizes, d, Mg, dtype):
     say(f"[expert_ffn] sizes={sizes} d={d} Mg={Mg} {dtype}")
