@@ -2,7 +2,7 @@
 // 稀疏激活与高效扩展" §10.2: h = SiLU(X W_1^T) ⊙ (X W_3^T), out = h W_2^T).
 //
 // Both products are "TN": every operand row is contiguous along the reduction dimension K, so A
-// rows and B rows are read with 16-byte vector loads. A block of 256 threads (4 waves) computes an
+// rows and B rows are read with 16-byte vector loads. A block of 512 threads (8 waves) computes an
 // MR x 256 tile with v_mfma_f32_32x32x16_bf16. K advances 64 at a time through two LDS stages (A
 // and B slices with XOR-swizzled 16-byte chunks, so fragment reads and stores are bank-conflict-
 // free); the next slice is prefetched into registers while the MFMAs run, fragments of the next
@@ -37,18 +37,29 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native 16-byte value (no struct copy)
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// Threads per block of the grouped GEMM: 8 waves, two per SIMD, so one wave's MFMAs cover the
+// other's load, store and barrier waits (4 waves also build: -DMOE_GEMM_THREADS=256).
+#ifndef MOE_GEMM_THREADS
+#define MOE_GEMM_THREADS 512
+#endif
+constexpr int NT = MOE_GEMM_THREADS;
+
 // Geometry of a tile class with MR rows: waves laid out WM x WN, each owning a block of
 // MI x NJ MFMA tiles of 32 x 32.
 template <int MR>
 struct Geo {
-  static constexpr int WM = MR == 256 ? 2 : 1;
-  static constexpr int WN = 4 / WM;
-  static constexpr int WROWS = MR / WM;       // 128, 128, 64
-  static constexpr int WCOLS = BN / WN;       // 128, 64, 64 (B rows per wave)
-  static constexpr int MI = WROWS / 32;       // 4, 4, 2
-  static constexpr int NJ = WCOLS / 32;       // 4, 2, 2
-  static constexpr int ACH = MR / 32;         // A chunks per thread per k-slice: 8, 4, 2
+  static constexpr int NW = NT / 64;                              // waves per block
+  static constexpr int WM = (NW == 4) ? (MR == 256 ? 2 : 1) : 2;  // waves along rows
+  static constexpr int WN = NW / WM;                              // waves along B rows
+  static constexpr int WROWS = MR / WM;
+  static constexpr int WCOLS = BN / WN;  // B rows per wave
+  static constexpr int MI = WROWS / 32;
+  static constexpr int NJ = WCOLS / 32;
+  static constexpr int RSTEP = NT / 8;      // rows covered by one load pass of the block
+  static constexpr int ACH = MR / RSTEP;    // A chunks per thread per k-slice
+  static constexpr int BCH = BN / RSTEP;    // B chunks per thread per k-slice
   static constexpr int STAGE = (MR + BN) * BK * 2;  // bytes per LDS stage
+  static_assert(MI >= 1 && NJ >= 2 && NJ % 2 == 0 && ACH >= 1, "tile geometry");
 };
 
 // element offset of 16-byte chunk `c` (0..7) of row `r` in a [rows][64] swizzled slice
@@ -84,12 +95,12 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
                                          int row_begin, int rows_here, int n0) {
   using G = Geo<MR>;
   constexpr int BNO = EPI == 0 ? BN / 2 : BN;  // output columns per tile
-  constexpr int MI = G::MI, NJ = G::NJ, ACH = G::ACH;
+  constexpr int MI = G::MI, NJ = G::NJ, ACH = G::ACH, BCH = G::BCH, RS = G::RSTEP;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / G::WN, wn = wave % G::WN;
 
-  // ---- global loads: thread `tid` moves chunk (tid & 7) of rows r0 + 32 i of the A slice
-  // (i < ACH) and of the B slice (i < 8). Addresses are uniform tile bases plus 32-bit byte
+  // ---- global loads: thread `tid` moves chunk (tid & 7) of rows r0 + RS i of the A slice
+  // (i < ACH) and of the B slice (i < BCH). Addresses are uniform tile bases plus 32-bit byte
   // offsets fixed over K; rows past the group (A) or past N (B) re-read the last valid row and
   // never reach a stored output.
   const int r0 = tid >> 3, kc_t = (tid & 7) * 8;
@@ -100,17 +111,17 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
   const char* b_base0 = reinterpret_cast<const char*>(Bg0);
   const char* b_base1 = reinterpret_cast<const char*>(Bg1);
   const int b_rows = min(EPI == 0 ? BN / 2 : BN, N - n0);
-  uint32_t a_off[ACH], b_off[8];
+  uint32_t a_off[ACH], b_off[BCH];
 #pragma unroll
   for (int i = 0; i < ACH; ++i)
-    a_off[i] = static_cast<uint32_t>((min(i * 32 + r0, rows_here - 1) * K + kc_t) * 2);
+    a_off[i] = static_cast<uint32_t>((min(i * RS + r0, rows_here - 1) * K + kc_t) * 2);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = i * 32 + r0;
+  for (int i = 0; i < BCH; ++i) {
+    const int r = i * RS + r0;
     const int rb_ = EPI == 0 ? (r & (BN / 2 - 1)) : r;
     b_off[i] = static_cast<uint32_t>((min(rb_, b_rows - 1) * K + kc_t) * 2);
   }
-  u32x4 ra[ACH], rb[8];
+  u32x4 ra[ACH], rb[BCH];
   auto gload = [&](int k0) __attribute__((always_inline)) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
     const bool in = !KTAIL || k0 + kc_t < K;
@@ -122,23 +133,23 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
       ra[i] = KTAIL ? (in ? v : zero) : v;
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const char* bb = (EPI == 0 && i >= 4) ? b_base1 : b_base0;
+    for (int i = 0; i < BCH; ++i) {
+      const char* bb = (EPI == 0 && i >= BCH / 2) ? b_base1 : b_base0;
       const u32x4 v = *reinterpret_cast<const u32x4*>(bb + (b_off[i] + kb));
       rb[i] = KTAIL ? (in ? v : zero) : v;
     }
   };
-  // LDS byte offset of this thread's chunk of row r0; row r0 + 32 i sits 32 * 128 B further on
+  // LDS byte offset of this thread's chunk of row r0; row r0 + RS i sits RS * 128 B further on
   // (the swizzle term depends on (r >> 1) & 7, which is the same for all i)
   const uint32_t st_off = static_cast<uint32_t>(swz(r0, tid & 7) * 2);
   constexpr uint32_t kStageBytes = G::STAGE, kBBytes = MR * BK * 2;
   auto lstore = [&](int stage) __attribute__((always_inline)) {
     unsigned char* sa = lds + stage * kStageBytes + st_off;
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4*>(sa + i * 32 * BK * 2) = ra[i];
+    for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4*>(sa + i * RS * BK * 2) = ra[i];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4*>(sa + kBBytes + i * 32 * BK * 2) = rb[i];
+    for (int i = 0; i < BCH; ++i)
+      *reinterpret_cast<u32x4*>(sa + kBBytes + i * RS * BK * 2) = rb[i];
   };
 
   f32x16 acc[MI][NJ];
@@ -180,7 +191,7 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
       for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
   };
-  constexpr int NMF = MI * NJ, NR = MI + NJ, NX = ACH + 8;
+  constexpr int NMF = MI * NJ, NR = MI + NJ, NX = ACH + BCH;
 
   // ---- one k-step (64 of K) = 4 sub-steps on stage `cur`:
   //   sub 0: read fragments of sub 1                    | MFMAs of sub 0
@@ -260,7 +271,7 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
   }
   __syncthreads();
   constexpr int CPR = BNO / 8;  // 16-byte chunks per tile row
-  for (int c = tid; c < MR * CPR; c += 256) {
+  for (int c = tid; c < MR * CPR; c += NT) {
     const int r = c / CPR, cc = (c % CPR) * 8;
     if (r < rows_here && n0 + cc < N)
       *reinterpret_cast<uint4*>(C + static_cast<int64_t>(row_begin + r) * N + n0 + cc) =
@@ -282,7 +293,7 @@ __device__ __forceinline__ int find_group(const int32_t* __restrict__ table, int
 // tile_off: three tables of groups + 1 entries: 256-row tiles, 128-row tiles, 64-row tiles.
 // Blocks [0, main_blocks) serve the 256-row tiles, the rest the smaller ones.
 template <int EPI, bool KTAIL>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
+__global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tile_off, int groups, int main_blocks,
     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, int64_t group_stride, int N,
@@ -353,7 +364,7 @@ hipError_t launch_gemm_t(const bf16_t* A, const int32_t* offsets, const int32_t*
   if (max_tiles <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((grouped_gemm_kernel<EPI, KTAIL>), dim3(static_cast<unsigned>(grid)),
-                     dim3(256), lds, st, A, offsets, tile_off, groups,
+                     dim3(NT), lds, st, A, offsets, tile_off, groups,
                      static_cast<int>(main_blocks), B0, B1, group_stride, N, K, C);
   return hipGetLastError();
 }
