@@ -67,68 +67,96 @@ __device__ int block_scan_256(int v, int* buf) {
   return r;
 }
 
-__global__ __launch_bounds__(256) void scan_kernel(
+// One block of 1024 threads. Thread (p, e) owns expert e (< EP, the power of two >= E) and part p
+// of the block range; parts are summed, scanned over p and walked again to write the per-block
+// bases, so every sum is taken in a fixed order.
+__global__ __launch_bounds__(1024) void scan_kernel(
     int64_t T, int E, int64_t C, int nblk, const int32_t* __restrict__ hist,
-    const float* __restrict__ gpart, const float* __restrict__ lpart,
+    const float* __restrict__ gpart, int nblk_g, const float* __restrict__ lpart,
     int32_t* __restrict__ block_base, int32_t* __restrict__ n_out, double* __restrict__ gsum,
     double* __restrict__ lse2sum, int32_t* __restrict__ kept_out, int32_t* __restrict__ overflow,
     int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off, int BM) {
+  __shared__ int psum[1024];
+  __shared__ double pg[1024];
   __shared__ int sbuf[256];
-  __shared__ double dbuf[256];
-  const int e = threadIdx.x;
-  int n = 0;
+  const int tid = threadIdx.x;
+  int EP = 1;
+  while (EP < E) EP <<= 1;
+  const int P = 1024 / EP;
+  const int e = tid % EP, p = tid / EP;
+  // load counts over this part's blocks
+  const int b0 = static_cast<int>(static_cast<int64_t>(p) * nblk / P);
+  const int b1 = static_cast<int>(static_cast<int64_t>(p + 1) * nblk / P);
+  int cnt = 0;
+  if (e < E)
+    for (int b = b0; b < b1; ++b) cnt += hist[static_cast<int64_t>(b) * E + e];
+  psum[tid] = cnt;
+  // sum of g over this part's (router) blocks
   double gs = 0.0;
+  if (gpart != nullptr && e < E) {
+    const int g0 = static_cast<int>(static_cast<int64_t>(p) * nblk_g / P);
+    const int g1 = static_cast<int>(static_cast<int64_t>(p + 1) * nblk_g / P);
+    for (int b = g0; b < g1; ++b) gs += static_cast<double>(gpart[static_cast<int64_t>(b) * E + e]);
+  }
+  pg[tid] = gs;
+  __syncthreads();
   if (e < E) {
-    int b = 0;
-    for (; b + 4 <= nblk; b += 4) {  // four independent loads in flight per step
-      const int h0 = hist[static_cast<int64_t>(b) * E + e];
-      const int h1 = hist[static_cast<int64_t>(b + 1) * E + e];
-      const int h2 = hist[static_cast<int64_t>(b + 2) * E + e];
-      const int h3 = hist[static_cast<int64_t>(b + 3) * E + e];
-      if (block_base != nullptr) {
-        block_base[static_cast<int64_t>(b) * E + e] = n;
-        block_base[static_cast<int64_t>(b + 1) * E + e] = n + h0;
-        block_base[static_cast<int64_t>(b + 2) * E + e] = n + h0 + h1;
-        block_base[static_cast<int64_t>(b + 3) * E + e] = n + h0 + h1 + h2;
+    int base = 0;
+    for (int q = 0; q < p; ++q) base += psum[q * EP + e];
+    if (block_base != nullptr) {
+      for (int b = b0; b < b1; ++b) {
+        block_base[static_cast<int64_t>(b) * E + e] = base;
+        base += hist[static_cast<int64_t>(b) * E + e];
       }
-      n += h0 + h1 + h2 + h3;
-      if (gpart != nullptr) {
-        gs += static_cast<double>(gpart[static_cast<int64_t>(b) * E + e]);
-        gs += static_cast<double>(gpart[static_cast<int64_t>(b + 1) * E + e]);
-        gs += static_cast<double>(gpart[static_cast<int64_t>(b + 2) * E + e]);
-        gs += static_cast<double>(gpart[static_cast<int64_t>(b + 3) * E + e]);
-      }
-    }
-    for (; b < nblk; ++b) {
-      const int h = hist[static_cast<int64_t>(b) * E + e];
-      if (block_base != nullptr) block_base[static_cast<int64_t>(b) * E + e] = n;
-      n += h;
-      if (gpart != nullptr) gs += static_cast<double>(gpart[static_cast<int64_t>(b) * E + e]);
     }
   }
-  const int kept = (e < E) ? ((C < 0 || n <= C) ? n : static_cast<int>(C)) : 0;
-  if (e < E) {
+  // per-expert totals (threads of part 0)
+  int n = 0, kept = 0;
+  if (p == 0 && e < E) {
+    double g = 0.0;
+    for (int q = 0; q < P; ++q) {
+      n += psum[q * EP + e];
+      g += pg[q * EP + e];
+    }
+    kept = (C < 0 || n <= C) ? n : static_cast<int>(C);
     if (n_out != nullptr) n_out[e] = n;
-    if (gsum != nullptr) gsum[e] = gs;
+    if (gsum != nullptr) gsum[e] = g;
     if (kept_out != nullptr) kept_out[e] = kept;
     if (overflow != nullptr) overflow[e] = n - kept;
   }
-  const int incl = block_scan_256(kept, sbuf);
-  if (e < E && offsets != nullptr) {
-    offsets[e] = incl - kept;
-    if (e == E - 1) offsets[E] = incl;
+  // exclusive scans over experts: expert e's totals sit in thread e (part 0 is threads [0, EP))
+  const int ee = tid < 256 ? tid : 0;
+  const bool mine = tid < E;
+  const int kept_e = mine ? kept : 0;
+  auto scan256 = [&](int v) -> int {
+    if (tid < 256) sbuf[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int add = (tid < 256 && tid >= off) ? sbuf[tid - off] : 0;
+      __syncthreads();
+      if (tid < 256) sbuf[tid] += add;
+      __syncthreads();
+    }
+    const int r = tid < 256 ? sbuf[tid] : 0;
+    __syncthreads();
+    return r;
+  };
+  const int incl = scan256(kept_e);
+  if (mine && offsets != nullptr) {
+    offsets[ee] = incl - kept_e;
+    if (ee == E - 1) offsets[E] = incl;
   }
   // grouped-GEMM tile tables: [E+1] 256-row (or BM-row) tiles, [E+1] 128-row, [E+1] 64-row
   int c0 = 0, c1 = 0, c2 = 0;
-  if (e < E) tile_counts(kept, BM, c0, c1, c2);
-  const int i0 = block_scan_256(c0, sbuf);
-  const int i1 = block_scan_256(c1, sbuf);
-  const int i2 = block_scan_256(c2, sbuf);
-  if (e < E && tile_off != nullptr) {
-    tile_off[e] = i0 - c0;
-    tile_off[E + 1 + e] = i1 - c1;
-    tile_off[2 * (E + 1) + e] = i2 - c2;
-    if (e == E - 1) {
+  if (mine) tile_counts(kept_e, BM, c0, c1, c2);
+  const int i0 = scan256(c0);
+  const int i1 = scan256(c1);
+  const int i2 = scan256(c2);
+  if (mine && tile_off != nullptr) {
+    tile_off[ee] = i0 - c0;
+    tile_off[E + 1 + ee] = i1 - c1;
+    tile_off[2 * (E + 1) + ee] = i2 - c2;
+    if (ee == E - 1) {
       tile_off[E] = i0;
       tile_off[2 * E + 1] = i1;
       tile_off[3 * E + 2] = i2;
@@ -136,20 +164,23 @@ __global__ __launch_bounds__(256) void scan_kernel(
   }
   if (lse2sum != nullptr) {
     double ls = 0.0;
-    for (int b = e; b < nblk; b += 256) ls += static_cast<double>(lpart[b]);
-    dbuf[e] = ls;
+    for (int b = tid; b < nblk_g; b += 1024) ls += static_cast<double>(lpart[b]);
+    pg[tid] = ls;
     __syncthreads();
-    for (int off = 128; off >= 1; off >>= 1) {
-      if (e < off) dbuf[e] += dbuf[e + off];
+    for (int off = 512; off >= 1; off >>= 1) {
+      if (tid < off) pg[tid] += pg[tid + off];
       __syncthreads();
     }
-    if (e == 0) *lse2sum = dbuf[0];
+    if (tid == 0) *lse2sum = pg[0];
   }
 }
 
 // Ranks and rows of one block of 64 tokens: inv_perm [T,k] and perm_token [rows].
+// block_base rows are per histogram block of 64 / base_sub tokens: this 64-token block starts at
+// histogram block blk * base_sub.
 __global__ __launch_bounds__(256) void place_kernel(int64_t T, int E, int k, int64_t C,
                                                      const int32_t* __restrict__ topk_idx,
+                                                     int base_sub,
                                                      const int32_t* __restrict__ block_base,
                                                      const int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ perm_token,
@@ -178,7 +209,7 @@ __global__ __launch_bounds__(256) void place_kernel(int64_t T, int E, int k, int
       const unsigned long long m =
           (static_cast<unsigned long long>(mask[2 * e + 1]) << 32) | mask[2 * e];
       const unsigned long long lower = tl == 0 ? 0ull : (m & ((1ull << tl) - 1ull));
-      const int64_t pos = static_cast<int64_t>(block_base[blk * E + e]) + __popcll(lower);
+      const int64_t pos = static_cast<int64_t>(block_base[blk * base_sub * E + e]) + __popcll(lower);
       if (C < 0 || pos < C) {
         row = offsets[e] + static_cast<int>(pos);
         perm_token[row] = static_cast<int32_t>(t);
@@ -266,17 +297,18 @@ hipError_t launch_scan(int64_t T, int E, int64_t C, int nblk, const int32_t* his
                        const float* gpart, const float* lpart, int32_t* block_base, int32_t* n_out,
                        double* gsum, double* lse2sum, int32_t* kept, int32_t* overflow,
                        int32_t* offsets, int32_t* tile_off, int BM, hipStream_t st) {
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, st, T, E, C, nblk, hist, gpart, lpart,
-                     block_base, n_out, gsum, lse2sum, kept, overflow, offsets, tile_off, BM);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, T, E, C, nblk, hist, gpart, nblk,
+                     lpart, block_base, n_out, gsum, lse2sum, kept, overflow, offsets, tile_off, BM);
   return hipGetLastError();
 }
 
 hipError_t launch_scatter(int64_t T, int d, int E, int k, int64_t C, int elem_bytes,
-                          const void* x, const int32_t* topk_idx, const int32_t* block_base,
-                          const int32_t* offsets, void* x_perm, int32_t* perm_token,
-                          int32_t* inv_perm, hipStream_t st) {
+                          const void* x, const int32_t* topk_idx, int hist_block_tokens,
+                          const int32_t* block_base, const int32_t* offsets, void* x_perm,
+                          int32_t* perm_token, int32_t* inv_perm, hipStream_t st) {
   hipLaunchKernelGGL(place_kernel, dim3(static_cast<unsigned>(cdiv(T, RT))), dim3(256), 0, st, T,
-                     E, k, C, topk_idx, block_base, offsets, perm_token, inv_perm);
+                     E, k, C, topk_idx, RT / hist_block_tokens, block_base, offsets, perm_token,
+                     inv_perm);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || x_perm == nullptr) return err;
   const int64_t row_chunks = static_cast<int64_t>(d) * elem_bytes / 16;

@@ -51,6 +51,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 int elem_bytes(const moe_shape* s) { return s->dtype == MOE_F32 ? 4 : 2; }
 int gemm_bm(const moe_shape* s) { return s->dtype == MOE_F32 ? kGemmF32BM : kGemmBM; }
 int64_t nblocks(const moe_shape* s) { return cdiv(s->T, kRouteTokens); }
+int64_t route_blocks(const moe_shape* s) { return cdiv(s->T, route_block_tokens(s->dtype, s->E)); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -86,7 +87,7 @@ struct RoutePlan {
   float* lpart;
 };
 RoutePlan plan_route(Carve& c, const moe_shape* s) {
-  const size_t nb = static_cast<size_t>(nblocks(s));
+  const size_t nb = static_cast<size_t>(route_blocks(s));
   RoutePlan p;
   p.hist = c.take<int32_t>(nb * s->E);
   p.gpart = c.take<float>(nb * s->E);
@@ -115,13 +116,12 @@ struct LayerPlan {
   void *x_perm, *h, *out_perm, *h_sh, *sh;
 };
 LayerPlan plan_layer(Carve& c, const moe_shape* s) {
-  const size_t nb = static_cast<size_t>(nblocks(s));
   const size_t P = static_cast<size_t>(s->T) * s->k;
   const size_t R = static_cast<size_t>(routed_rows(s));
   const size_t eb = static_cast<size_t>(elem_bytes(s));
   LayerPlan p;
   p.r = plan_route(c, s);
-  p.block_base = c.take<int32_t>(nb * s->E);
+  p.block_base = c.take<int32_t>(static_cast<size_t>(route_blocks(s)) * s->E);
   p.topk_idx = c.take<int32_t>(P);
   p.topk_w = c.take<float>(P);
   p.n = c.take<int32_t>(s->E);
@@ -222,7 +222,7 @@ moe_status moe_route(const moe_shape* s, const void* x, const void* W_r, const f
   hipError_t e = launch_route(s->dtype, s->T, s->d, s->E, s->k, s->renorm, x, W_r, b, topk_idx,
                               topk_w, p.hist, p.gpart, p.lpart, hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = launch_scan(s->T, s->E, -1, static_cast<int>(nblocks(s)), p.hist, p.gpart, p.lpart, nullptr,
+  e = launch_scan(s->T, s->E, -1, static_cast<int>(route_blocks(s)), p.hist, p.gpart, p.lpart, nullptr,
                   n, gsum, lse2sum, nullptr, nullptr, nullptr, nullptr, gemm_bm(s), hs);
   return hip_status(e);
 }
@@ -247,8 +247,8 @@ moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_i
                   p.block_base, counts, nullptr, nullptr, nullptr, overflow, offsets, nullptr,
                   gemm_bm(s), hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = launch_scatter(s->T, s->d, s->E, s->k, C, elem_bytes(s), x, topk_idx, p.block_base, offsets,
-                     x_perm, perm_token, inv_perm, hs);
+  e = launch_scatter(s->T, s->d, s->E, s->k, C, elem_bytes(s), x, topk_idx, kRouteTokens,
+                     p.block_base, offsets, x_perm, perm_token, inv_perm, hs);
   return hip_status(e);
 }
 
@@ -333,7 +333,7 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
   int32_t* ovf = overflow ? overflow : p.overflow;
   const int64_t C = capacity_of(s);
   const int BM = gemm_bm(s);
-  const int nblk = static_cast<int>(nblocks(s));
+  const int nblk = static_cast<int>(route_blocks(s));
   const int eb = elem_bytes(s);
 
   const int64_t max_tiles = cdiv(routed_rows(s), BM) + s->E;
@@ -346,8 +346,8 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
     e = launch_scan(s->T, s->E, C, nblk, p.r.hist, p.r.gpart, p.r.lpart, p.block_base, n, p.gsum,
                     p.lse2sum, p.kept, ovf, p.offsets, p.tile_off, BM, hs);
   if (e == hipSuccess)
-    e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx, p.block_base, p.offsets, p.x_perm,
-                       p.perm_token, p.inv_perm, hs);
+    e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx, route_block_tokens(s->dtype, s->E),
+                       p.block_base, p.offsets, p.x_perm, p.perm_token, p.inv_perm, hs);
   mark_stage(2, hs);
   if (e == hipSuccess)
     e = launch_gemm_up(s->dtype, s->E, s->d, s->M, p.x_perm, p.offsets, p.tile_off, max_tiles,

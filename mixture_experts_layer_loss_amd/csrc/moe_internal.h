@@ -44,8 +44,13 @@ __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 
 // ------------------------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error; all enqueue on `st`.
 
+// Tokens per router block: the router writes its partial statistics and expert histogram per
+// block of this many tokens (a divisor of kRouteTokens).
+int route_block_tokens(int dtype, int E);
+
 // Router: logits, softmax/LSE, biased top-k, gates, per-block partial statistics and histograms.
-//   hist  [nblk, E] int32, gpart [nblk, E] fp32, lpart [nblk] fp32, nblk = ceil(T / kRouteTokens)
+//   hist  [nblk, E] int32, gpart [nblk, E] fp32, lpart [nblk] fp32,
+//   nblk = ceil(T / route_block_tokens(dtype, E))
 hipError_t launch_route(int dtype, int64_t T, int d, int E, int k, int renorm, const void* x,
                         const void* W_r, const float* b, int32_t* topk_idx, float* topk_w,
                         int32_t* hist, float* gpart, float* lpart, hipStream_t st);
@@ -65,10 +70,12 @@ hipError_t launch_scan(int64_t T, int E, int64_t C, int nblk, const int32_t* his
                        int32_t* offsets, int32_t* tile_off, int BM, hipStream_t st);
 
 // Places assignments: inv_perm, perm_token and (when x_perm != NULL) the x row copies.
+// block_base holds one row per histogram block of hist_block_tokens tokens (a divisor of
+// kRouteTokens).
 hipError_t launch_scatter(int64_t T, int d, int E, int k, int64_t C, int elem_bytes,
-                          const void* x, const int32_t* topk_idx, const int32_t* block_base,
-                          const int32_t* offsets, void* x_perm, int32_t* perm_token,
-                          int32_t* inv_perm, hipStream_t st);
+                          const void* x, const int32_t* topk_idx, int hist_block_tokens,
+                          const int32_t* block_base, const int32_t* offsets, void* x_perm,
+                          int32_t* perm_token, int32_t* inv_perm, hipStream_t st);
 
 // Tile tables [3 (groups+1)] of a grouped GEMM from device row offsets (stand-alone expert FFN).
 hipError_t launch_schedule(int groups, const int32_t* offsets, int32_t* tile_off, int BM,

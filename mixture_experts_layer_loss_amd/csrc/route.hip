@@ -2,13 +2,14 @@
 // renormalised gates and per-block partial statistics ("MoE：条件计算与路由" §原理与演进,
 // §无辅助损失负载均衡（ALF-LB）, §7 eqs. (1)-(2); "MOE大模型对比篇" §2.2 for the LSE term).
 //
-// One block of 256 threads (4 waves) owns kRouteTokens = 64 consecutive tokens. The logits tile
-// [64 x E] never leaves the chip: bf16 inputs go through v_mfma_f32_16x16x32_bf16 with x and W_r
-// k-slices staged in LDS; fp32 inputs use plain FMA loops. Each wave then walks 16 tokens: lanes
-// own experts e = lane + 64 i, the softmax maximum / sum and the k argmax rounds are wave
-// reductions, and equal scores go to the lower expert index. Statistics leave as per-block
-// partials (expert histogram, sum of g, sum of lse^2) reduced later in a fixed order, so every
-// result is bit-reproducible.
+// A block owns TB consecutive tokens (bf16: 8 waves, 16 tokens when E <= 16, else 64; fp32: 4
+// waves, 64 tokens). The logits tile [TB x E] never leaves the chip: bf16 inputs go through
+// v_mfma_f32_16x16x32_bf16 with the hidden dimension split across the waves; fp32 inputs use
+// plain FMA loops. Then one lane per token walks the experts in index order (softmax maximum and
+// sum, then a sorted top-k insertion in registers), so equal scores go to the lower expert index
+// and no cross-lane operation sits on the per-token path. Statistics leave as per-block partials
+// (expert histogram, sum of g, sum of lse^2) reduced later in a fixed order, so every result is
+// bit-reproducible.
 #include "moe_internal.h"
 
 #include <math.h>
@@ -16,264 +17,249 @@
 namespace moe {
 namespace {
 
-constexpr int RT = kRouteTokens;  // 64 tokens per block
-constexpr int RK = 64;            // K elements staged per step
-constexpr int RKP = RK + 8;       // padded LDS row (bf16 elements): 144 B keeps MFMA reads conflict-free
+constexpr int RT = kRouteTokens;  // 64 tokens per fp32 block
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-struct ArgMax {
-  float v;
-  int e;
-};
-
-__device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b) {
-  // larger score wins; equal scores go to the lower expert index
-  return (b.v > a.v || (b.v == a.v && b.e < a.e)) ? b : a;
-}
-
-__device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
+// Insert score v of expert e into a list of KM scores sorted in descending order. Experts arrive
+// in ascending index order and only a strictly larger score moves an entry down, so equal scores
+// stay ordered by index (ties go to the lower expert index). Branch-free; NaN never enters.
+template <int KM>
+__device__ __forceinline__ void topk_insert(float v, int e, float (&tv)[KM], int (&ti)[KM]) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    ArgMax o;
-    o.v = __shfl_xor(a.v, off, 64);
-    o.e = __shfl_xor(a.e, off, 64);
-    a = better(a, o);
+  for (int j = KM - 1; j >= 1; --j) {
+    const bool beats_prev = v > tv[j - 1];  // entry j-1 moves down to j
+    const bool beats = v > tv[j];
+    tv[j] = beats_prev ? tv[j - 1] : (beats ? v : tv[j]);
+    ti[j] = beats_prev ? ti[j - 1] : (beats ? e : ti[j]);
   }
-  return a;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  const bool top = v > tv[0];
+  tv[0] = top ? v : tv[0];
+  ti[0] = top ? e : ti[0];
 }
 
 // ------------------------------------------------------------------------------------------
-// Per-token routing over the logits tile in LDS, shared by both dtypes.
-//   L: [RT][Ls] fp32 logits of this block's tokens.
+// Per-token routing over the logits tile in LDS, shared by both dtypes. One lane per token:
+// wave w takes tokens [w TB/4, (w+1) TB/4) of the block's TB. The lane walks the experts in index
+// order: maximum, sum of exp(l - m) (so lse = m + ln sum), then g_e = exp(l_e - lse) (written back
+// over the logit), s_e = g_e + b_e and the sorted top-KM insertion; k <= KM. Block partials: the
+// expert histogram (LDS integer atomics: order-free), sum of g per expert and sum of lse^2, the
+// latter two summed over tokens in token order.
+//   L: [TB][Ls] fp32; scratch: >= MOE_E_MAX ints + 64 floats.
 // ------------------------------------------------------------------------------------------
-__device__ void route_tokens(const float* L, int Ls, int64_t t0, int64_t T, int E, int k,
-                             int renorm, const float* __restrict__ b, int32_t* __restrict__ topk_idx,
-                             float* __restrict__ topk_w, int32_t* __restrict__ hist,
-                             float* __restrict__ gpart, float* __restrict__ lpart, float* red) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  constexpr int EPL = MOE_E_MAX / 64;  // experts per lane, at most 4
-  float gacc[EPL];
-  int hcnt[EPL];
-  float bias[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    gacc[i] = 0.f;
-    hcnt[i] = 0;
-    const int e = lane + 64 * i;
-    bias[i] = (b != nullptr && e < E) ? b[e] : 0.f;
-  }
-  float lacc = 0.f;
-
-  for (int tl = wave * 16; tl < wave * 16 + 16; ++tl) {
-    const int64_t t = t0 + tl;
-    if (t >= T) break;
-    float v[EPL], g[EPL], s[EPL];
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
-      v[i] = (e < E) ? L[tl * Ls + e] : -INFINITY;
-      mloc = fmaxf(mloc, v[i]);
-    }
-    const float m = wave_max(mloc);
-    float sloc = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) sloc += (lane + 64 * i < E) ? expf(v[i] - m) : 0.f;
-    const float lse = m + logf(wave_sum(sloc));
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
-      g[i] = (e < E) ? expf(v[i] - lse) : 0.f;
-      s[i] = (e < E) ? g[i] + bias[i] : -INFINITY;
-      gacc[i] += g[i];
-    }
-    lacc += lse * lse;
-
-    int sel[MOE_K_MAX];
-    float gsel[MOE_K_MAX];
-    float wsum = 0.f;
-#pragma unroll
-    for (int j = 0; j < MOE_K_MAX; ++j) {
-      sel[j] = 0;
-      gsel[j] = 0.f;
-      if (j < k) {
-        ArgMax a{-INFINITY, 0x7fffffff};
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) a = better(a, ArgMax{s[i], lane + 64 * i});
-        a = wave_argmax(a);
-        const int owner = a.e & 63, slot = a.e >> 6;
-        float gi = 0.f;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) gi = (slot == i) ? g[i] : gi;
-        const float gs = __shfl(gi, owner, 64);
-        if (lane == owner) {
-#pragma unroll
-          for (int i = 0; i < EPL; ++i) {
-            if (slot == i) {
-              s[i] = -INFINITY;
-              hcnt[i] += 1;
-            }
-          }
-        }
-        sel[j] = a.e;
-        gsel[j] = gs;
-        wsum += gs;
-      }
-    }
-    if (lane < k) {
-      int my_e = 0;
-      float my_g = 0.f;
-#pragma unroll
-      for (int j = 0; j < MOE_K_MAX; ++j) {
-        if (lane == j) {
-          my_e = sel[j];
-          my_g = gsel[j];
-        }
-      }
-      topk_idx[t * k + lane] = my_e;
-      topk_w[t * k + lane] = renorm ? my_g / wsum : my_g;
-    }
-  }
-
-  // block partials: sum the 4 waves in a fixed order
-  float* gred = red;                          // [4][E_MAX]
-  int* hred = reinterpret_cast<int*>(red + 4 * MOE_E_MAX);  // [4][E_MAX]
-  float* lred = red + 8 * MOE_E_MAX;          // [4]
+template <int KM>
+__device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, int E, int k,
+                             int renorm, const float* __restrict__ b,
+                             int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                             int32_t* __restrict__ hist, float* __restrict__ gpart,
+                             float* __restrict__ lpart, int* hcnt, float* lsq) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int tpw = TB / nw;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hcnt[e] = 0;
   __syncthreads();
+  if (lane < tpw) {
+    const int tl = wave * tpw + lane;
+    const int64_t t = t0 + tl;
+    float lse2 = 0.f;
+    if (t < T) {
+      float* row = L + tl * Ls;  // Ls % 4 == 0: 16-byte aligned; the pad past E holds -inf
+      const int E4 = (E + 3) & ~3;
+      float m = -INFINITY;
+#pragma unroll 4
+      for (int e = 0; e < E4; e += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(row + e);
+        m = fmaxf(m, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+      }
+      float sum = 0.f;
+#pragma unroll 4
+      for (int e = 0; e < E4; e += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(row + e);
+        sum += expf(v.x - m);
+        sum += expf(v.y - m);
+        sum += expf(v.z - m);
+        sum += expf(v.w - m);
+      }
+      const float lse = m + logf(sum);
+      lse2 = lse * lse;
+      float tv[KM];
+      int ti[KM];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + 64 * i;
-    gred[wave * MOE_E_MAX + e] = gacc[i];
-    hred[wave * MOE_E_MAX + e] = hcnt[i];
+      for (int j = 0; j < KM; ++j) {
+        tv[j] = -INFINITY;
+        ti[j] = 0;
+      }
+      for (int e = 0; e < E4; e += 4) {
+        float4 v = *reinterpret_cast<const float4*>(row + e);
+        v.x = expf(v.x - lse);
+        v.y = expf(v.y - lse);
+        v.z = expf(v.z - lse);
+        v.w = expf(v.w - lse);
+        *reinterpret_cast<float4*>(row + e) = v;
+        const float g4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ee = e + q;
+          if (ee < E) topk_insert<KM>(b != nullptr ? g4[q] + b[ee] : g4[q], ee, tv, ti);
+        }
+      }
+      float wsum = 0.f;
+#pragma unroll
+      for (int j = 0; j < KM; ++j)
+        if (j < k) wsum += row[ti[j]];
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        if (j < k) {
+          const float gj = row[ti[j]];
+          topk_idx[t * k + j] = ti[j];
+          topk_w[t * k + j] = renorm ? gj / wsum : gj;
+          atomicAdd(&hcnt[ti[j]], 1);
+        }
+      }
+    }
+    lsq[tl] = lse2;
   }
-  if (lane == 0) lred[wave] = lacc;
   __syncthreads();
   const int64_t blk = blockIdx.x;
+  const int nt = static_cast<int>(min<int64_t>(TB, T - t0));
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    float gs = gred[e];
-    int hs = hred[e];
-    for (int w = 1; w < 4; ++w) {
-      gs += gred[w * MOE_E_MAX + e];
-      hs += hred[w * MOE_E_MAX + e];
-    }
+    float gs = 0.f;
+    for (int tl = 0; tl < nt; ++tl) gs += L[tl * Ls + e];
     gpart[blk * E + e] = gs;
-    hist[blk * E + e] = hs;
+    hist[blk * E + e] = hcnt[e];
   }
-  if (threadIdx.x == 0) lpart[blk] = ((lred[0] + lred[1]) + lred[2]) + lred[3];
+  if (threadIdx.x == 0) {
+    float ls = 0.f;
+    for (int tl = 0; tl < nt; ++tl) ls += lsq[tl];
+    lpart[blk] = ls;
+  }
 }
 
-// LDS budget: max(logits tile, staged k-slices) plus the reduction scratch.
+// the top-k list length used for k (2, 8 or 16 slots)
+#define MOE_ROUTE_TOKENS_KM(CALL) \
+  do {                            \
+    if (k <= 2) {                 \
+      CALL(2);                    \
+    } else if (k <= 8) {          \
+      CALL(8);                    \
+    } else {                      \
+      CALL(16);                   \
+    }                             \
+  } while (0)
+
+// logits row stride: a multiple of 4 floats (16-byte reads); with at most 16 lanes walking 16
+// rows, the rows' 4-bank groups are all distinct
 constexpr int kLogitsStride = MOE_E_MAX + 4;
-constexpr int kTileBytes = (RT + MOE_E_MAX) * RKP * 2;
-constexpr int kLogitsBytes = RT * kLogitsStride * 4;
-constexpr int kUnionBytes = kTileBytes > kLogitsBytes ? kTileBytes : kLogitsBytes;
-constexpr int kRedFloats = 8 * MOE_E_MAX + 4;
 
 // ------------------------------------------------------------------------------------------
-// bf16: logits on MFMA. Wave w computes tokens [16w, 16w+16) against all NEB expert blocks of 16.
-// Fragment layout of v_mfma_f32_16x16x32_bf16: lane l supplies row (l % 16) of A and column
-// (l % 16) of B with 8 consecutive k values of k-group (l / 16); the result element
+// bf16: logits on MFMA. A block owns TB = 16 MB tokens; its eight waves split the hidden dimension
+// into eight contiguous ranges of 32-wide k-steps and load their MFMA operands straight from
+// global memory (x rows of the block's tokens, W_r rows of every expert), so no barrier sits in
+// the k loop. The four partial logit tiles are summed in LDS in wave order (fixed, so results are
+// reproducible). Fragment layout of v_mfma_f32_16x16x32_bf16: lane l supplies row (l % 16) of A
+// and column (l % 16) of B with 8 consecutive k of k-group (l / 16); result element
 // (row 4*(l/16) + j, column l % 16) lands in lane l, register j.
 // ------------------------------------------------------------------------------------------
-template <int NEB>
-__global__ __launch_bounds__(256) void route_bf16_kernel(
+constexpr int kRouteThreads = 512;  // 8 waves: K is split 8 ways, two waves per SIMD
+
+template <int MB, int NEB, int NG>
+__global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ b,
     int64_t T, int d, int E, int k, int renorm, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ hist, float* __restrict__ gpart,
     float* __restrict__ lpart) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kUnionBytes];
-  __shared__ float red[kRedFloats];
-  bf16_t* xs = reinterpret_cast<bf16_t*>(smem);  // [RT][RKP]
-  bf16_t* ws = xs + RT * RKP;                    // [NEB*16][RKP]
-  constexpr int ER = NEB * 16;                   // padded expert rows
-  constexpr int XCH = RT * (RK / 8);             // 16-byte chunks of the x slice (512)
-  constexpr int WCH = ER * (RK / 8);             // 16-byte chunks of the W_r slice
-  constexpr int XPT = XCH / 256;                 // per thread (2)
-  constexpr int WPT = (WCH + 255) / 256;         // per thread (<= 8)
-
+  constexpr int TB = 16 * MB;
+  constexpr int NW = kRouteThreads / 64;
+  constexpr int NWK = NW / NG;                // waves splitting K within an expert group
+  constexpr int NEBG = (NEB + NG - 1) / NG;   // expert blocks of 16 per group
+  __shared__ float L[TB * kLogitsStride];
+  __shared__ int hcnt[MOE_E_MAX];
+  __shared__ float lsq[TB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * RT;
-
-  uint4 xr[XPT], wr[WPT];
-  auto load_slices = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int c = i * 256 + tid, row = c >> 3, col = (c & 7) * 8;
-      int64_t t = t0 + row;
-      t = t < T ? t : T - 1;
-      xr[i] = (k0 + col < d) ? *reinterpret_cast<const uint4*>(x + t * d + k0 + col)
-                             : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < WPT; ++i) {
-      const int c = i * 256 + tid, row = c >> 3, col = (c & 7) * 8;
-      wr[i] = (c < WCH && row < E && k0 + col < d)
-                  ? *reinterpret_cast<const uint4*>(W + static_cast<int64_t>(row) * d + k0 + col)
-                  : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_slices = [&]() {
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int c = i * 256 + tid, row = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<uint4*>(xs + row * RKP + col) = xr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < WPT; ++i) {
-      const int c = i * 256 + tid, row = c >> 3, col = (c & 7) * 8;
-      if (c < WCH) *reinterpret_cast<uint4*>(ws + row * RKP + col) = wr[i];
-    }
-  };
-
-  f32x4 acc[NEB];
-#pragma unroll
-  for (int j = 0; j < NEB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+  const int grp = wave / NWK, kw = wave % NWK;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TB;
   const int r16 = lane & 15, kg = lane >> 4;
-  load_slices(0);
-  for (int k0 = 0; k0 < d; k0 += RK) {
-    __syncthreads();  // previous step's LDS reads are done
-    store_slices();
+
+  const bf16_t* xr[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    int64_t t = t0 + m * 16 + r16;
+    t = t < T ? t : T - 1;
+    xr[m] = x + t * d + kg * 8;
+  }
+  const bf16_t* wr[NEBG];
+  bool wv[NEBG];
+#pragma unroll
+  for (int j = 0; j < NEBG; ++j) {
+    const int e = (grp * NEBG + j) * 16 + r16;
+    wv[j] = e < E;
+    wr[j] = W + static_cast<int64_t>(wv[j] ? e : 0) * d + kg * 8;
+  }
+  f32x4 acc[MB][NEBG];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int j = 0; j < NEBG; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nks = (d + 31) / 32;
+  const int s0 = kw * nks / NWK, s1 = (kw + 1) * nks / NWK;
+  const bf16x8 zero = {};
+  auto load = [&](int s, bf16x8* a, bf16x8* bb) __attribute__((always_inline)) {
+    const int kk = s * 32;
+    const bool in = kk + kg * 8 < d;  // d is a multiple of 8: a lane's 8 values are all in or out
+#pragma unroll
+    for (int m = 0; m < MB; ++m) a[m] = in ? *reinterpret_cast<const bf16x8*>(xr[m] + kk) : zero;
+#pragma unroll
+    for (int j = 0; j < NEBG; ++j)
+      bb[j] = (in && wv[j]) ? *reinterpret_cast<const bf16x8*>(wr[j] + kk) : zero;
+  };
+  auto mma = [&](const bf16x8* a, const bf16x8* bb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int j = 0; j < NEBG; ++j)
+        acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], bb[j], acc[m][j], 0, 0, 0);
+  };
+  bf16x8 a0[MB], b0[NEBG], a1[MB], b1[NEBG];
+  int s = s0;
+  if (s < s1) load(s, a0, b0);
+  for (; s + 1 < s1; s += 2) {
+    load(s + 1, a1, b1);
+    mma(a0, b0);
+    if (s + 2 < s1) load(s + 2, a0, b0);
+    mma(a1, b1);
+  }
+  if (s < s1) mma(a0, b0);
+
+  // sum the partial tiles of each expert group in wave (K) order; groups own disjoint columns
+  for (int w = 0; w < NW; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int j = 0; j < NEBG; ++j) {
+          const int col = (grp * NEBG + j) * 16 + r16;
+          if ((grp * NEBG + j) < NEB) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float* dst = &L[(m * 16 + kg * 4 + r) * kLogitsStride + col];
+              *dst = (kw == 0) ? acc[m][j][r] : *dst + acc[m][j][r];
+            }
+          }
+        }
+    }
     __syncthreads();
-    if (k0 + RK < d) load_slices(k0 + RK);  // next slice in flight during the MFMAs
-#pragma unroll
-    for (int sub = 0; sub < RK / 32; ++sub) {
-      const int kc = sub * 32 + kg * 8;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(xs + (wave * 16 + r16) * RKP + kc);
-#pragma unroll
-      for (int j = 0; j < NEB; ++j) {
-        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(ws + (j * 16 + r16) * RKP + kc);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, acc[j], 0, 0, 0);
-      }
-    }
+  }
+  for (int i = tid; i < TB * 4; i += kRouteThreads) {
+    const int e = ((E + 3) & ~3) - 4 + (i & 3);
+    if (e >= E) L[(i >> 2) * kLogitsStride + e] = -INFINITY;
   }
   __syncthreads();
-  float* L = reinterpret_cast<float*>(smem);  // [RT][kLogitsStride], reuses the slice buffers
-#pragma unroll
-  for (int j = 0; j < NEB; ++j) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = wave * 16 + kg * 4 + r, col = j * 16 + r16;
-      L[row * kLogitsStride + col] = acc[j][r];
-    }
-  }
-  __syncthreads();
-  route_tokens(L, kLogitsStride, t0, T, E, k, renorm, b, topk_idx, topk_w, hist, gpart, lpart, red);
+#define MOE_CALL(KM) \
+  route_tokens<KM>(L, kLogitsStride, TB, t0, T, E, k, renorm, b, topk_idx, topk_w, hist, gpart, \
+                   lpart, hcnt, lsq)
+  MOE_ROUTE_TOKENS_KM(MOE_CALL);
+#undef MOE_CALL
 }
 
 // ------------------------------------------------------------------------------------------
@@ -285,8 +271,9 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
     float* __restrict__ topk_w, int32_t* __restrict__ hist, float* __restrict__ gpart,
     float* __restrict__ lpart) {
   __shared__ float L[RT * kLogitsStride];
-  __shared__ float red[kRedFloats];
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * RT;
+  __shared__ int hcnt[MOE_E_MAX];
+  __shared__ float lsq[RT];
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * RT;  // fp32 blocks are 64 tokens
   for (int p = threadIdx.x; p < RT * E; p += blockDim.x) {
     const int tl = p / E, e = p % E;
     int64_t t = t0 + tl;
@@ -297,15 +284,158 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
     for (int i = 0; i < d; ++i) acc = fmaf(xr[i], wr[i], acc);
     L[tl * kLogitsStride + e] = acc;
   }
+  for (int i = threadIdx.x; i < RT * 4; i += blockDim.x) {
+    const int e = ((E + 3) & ~3) - 4 + (i & 3);
+    if (e >= E) L[(i >> 2) * kLogitsStride + e] = -INFINITY;
+  }
   __syncthreads();
-  route_tokens(L, kLogitsStride, t0, T, E, k, renorm, b, topk_idx, topk_w, hist, gpart, lpart, red);
+#define MOE_CALL(KM) \
+  route_tokens<KM>(L, kLogitsStride, RT, t0, T, E, k, renorm, b, topk_idx, topk_w, hist, gpart, \
+                   lpart, hcnt, lsq)
+  MOE_ROUTE_TOKENS_KM(MOE_CALL);
+#undef MOE_CALL
+}
+
+// ------------------------------------------------------------------------------------------
+// bf16 with many experts (E > 16): W_r is shared through LDS. A block owns 64 tokens; its eight
+// waves are 4 token blocks of 16 x 2 expert halves and each runs the whole hidden dimension, so
+// x is streamed once per block and W_r once per block. The x and W_r k-slices (64 wide) pass
+// through two LDS stages (row stride 72 bf16 = 144 bytes: the 16x16x32 fragment reads are bank-
+// conflict-free) with the next slice prefetched into registers; one barrier per k-step.
+// ------------------------------------------------------------------------------------------
+constexpr int kSK = 64;         // k per step
+constexpr int kSKP = kSK + 8;   // padded LDS row (bf16 elements)
+
+template <int NEB>
+__global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ b,
+    int64_t T, int d, int E, int k, int renorm, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, int32_t* __restrict__ hist, float* __restrict__ gpart,
+    float* __restrict__ lpart) {
+  constexpr int TB = 64;
+  constexpr int ROWS = TB + 16 * NEB;                 // x rows then W_r rows of a stage
+  constexpr int STAGE = ROWS * kSKP;                  // bf16 elements
+  constexpr int CH = ROWS * (kSK / 8);                // 16-byte chunks per stage
+  constexpr int CPT = (CH + kRouteThreads - 1) / kRouteThreads;
+  constexpr int NEBH = (NEB + 1) / 2;                 // expert blocks per wave
+  constexpr int kStagesBytes = 2 * STAGE * 2;
+  constexpr int kLBytes = TB * kLogitsStride * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kStagesBytes > kLBytes ? kStagesBytes : kLBytes];
+  __shared__ int hcnt[MOE_E_MAX];
+  __shared__ float lsq[TB];
+  bf16_t* st = reinterpret_cast<bf16_t*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tb = wave & 3, eh = wave >> 2;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TB;
+  const int r16 = lane & 15, kg = lane >> 4;
+
+  // chunk c of a stage: row c / 8 (x rows 0..63, then W_r rows), 8 bf16 at column (c % 8) * 8
+  const bf16_t* src[CPT];
+  bool ok[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = i * kRouteThreads + tid, r = c >> 3, col = (c & 7) * 8;
+    ok[i] = c < CH;
+    if (r < TB) {
+      int64_t t = t0 + r;
+      t = t < T ? t : T - 1;
+      src[i] = x + t * d + col;
+    } else {
+      const int e = r - TB;
+      ok[i] = ok[i] && e < E;
+      src[i] = W + static_cast<int64_t>(e < E ? e : 0) * d + col;
+    }
+  }
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 rg[CPT];
+  auto gload = [&](int k0) __attribute__((always_inline)) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int col = ((i * kRouteThreads + tid) & 7) * 8;
+      rg[i] = (ok[i] && k0 + col < d) ? *reinterpret_cast<const u32x4*>(src[i] + k0) : zero;
+    }
+  };
+  auto lstore = [&](int stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = i * kRouteThreads + tid;
+      if (c < CH) *reinterpret_cast<u32x4*>(st + stage * STAGE + (c >> 3) * kSKP + (c & 7) * 8) = rg[i];
+    }
+  };
+  f32x4 acc[NEBH];
+#pragma unroll
+  for (int j = 0; j < NEBH; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int stage) __attribute__((always_inline)) {
+    const bf16_t* sx = st + stage * STAGE + (tb * 16 + r16) * kSKP;
+    const bf16_t* sw = st + stage * STAGE + (TB + r16) * kSKP;
+#pragma unroll
+    for (int sub = 0; sub < kSK / 32; ++sub) {
+      const int kc = sub * 32 + kg * 8;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sx + kc);
+#pragma unroll
+      for (int j = 0; j < NEBH; ++j) {
+        const int eb = eh * NEBH + j;
+        if (eb < NEB) {
+          const bf16x8 bb = *reinterpret_cast<const bf16x8*>(sw + eb * 16 * kSKP + kc);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, acc[j], 0, 0, 0);
+        }
+      }
+    }
+  };
+  const int nk = (d + kSK - 1) / kSK;
+  gload(0);
+  lstore(0);
+  if (nk > 1) gload(kSK);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    if (ks + 1 < nk) {
+      lstore((ks + 1) & 1);                  // stage read by k-step ks - 1, behind the barrier
+      if (ks + 2 < nk) gload((ks + 2) * kSK);
+    }
+    compute(ks & 1);
+    __syncthreads();
+  }
+  float* L = reinterpret_cast<float*>(smem);  // reuses the stages
+#pragma unroll
+  for (int j = 0; j < NEBH; ++j) {
+    const int eb = eh * NEBH + j;
+    if (eb < NEB) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) L[(tb * 16 + kg * 4 + r) * kLogitsStride + eb * 16 + r16] = acc[j][r];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < TB * 4; i += kRouteThreads) {
+    const int e = ((E + 3) & ~3) - 4 + (i & 3);
+    if (e >= E) L[(i >> 2) * kLogitsStride + e] = -INFINITY;
+  }
+  __syncthreads();
+#define MOE_CALL(KM) \
+  route_tokens<KM>(L, kLogitsStride, TB, t0, T, E, k, renorm, b, topk_idx, topk_w, hist, gpart, \
+                   lpart, hcnt, lsq)
+  MOE_ROUTE_TOKENS_KM(MOE_CALL);
+#undef MOE_CALL
 }
 
 template <int NEB>
-hipError_t launch_bf16(int64_t nblk, hipStream_t st, const void* x, const void* W, const float* b,
+hipError_t launch_bf16_lds(hipStream_t st, const void* x, const void* W, const float* b, int64_t T,
+                           int d, int E, int k, int renorm, int32_t* topk_idx, float* topk_w,
+                           int32_t* hist, float* gpart, float* lpart) {
+  hipLaunchKernelGGL((route_bf16_lds_kernel<NEB>), dim3(static_cast<unsigned>(cdiv(T, 64))),
+                     dim3(kRouteThreads), 0, st, static_cast<const bf16_t*>(x),
+                     static_cast<const bf16_t*>(W), b, T, d, E, k, renorm, topk_idx, topk_w, hist,
+                     gpart, lpart);
+  return hipGetLastError();
+}
+
+template <int MB, int NEB, int NG>
+hipError_t launch_bf16(hipStream_t st, const void* x, const void* W, const float* b,
                        int64_t T, int d, int E, int k, int renorm, int32_t* topk_idx,
                        float* topk_w, int32_t* hist, float* gpart, float* lpart) {
-  hipLaunchKernelGGL(route_bf16_kernel<NEB>, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
+  const int64_t nblk = cdiv(T, 16 * MB);
+  hipLaunchKernelGGL((route_bf16_kernel<MB, NEB, NG>), dim3(static_cast<unsigned>(nblk)),
+                     dim3(kRouteThreads), 0, st,
                      static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W), b, T, d, E, k,
                      renorm, topk_idx, topk_w, hist, gpart, lpart);
   return hipGetLastError();
@@ -313,27 +443,33 @@ hipError_t launch_bf16(int64_t nblk, hipStream_t st, const void* x, const void* 
 
 }  // namespace
 
+int route_block_tokens(int dtype, int E) { return dtype == MOE_F32 ? RT : (E <= 16 ? 16 : 64); }
+
 hipError_t launch_route(int dtype, int64_t T, int d, int E, int k, int renorm, const void* x,
                         const void* W_r, const float* b, int32_t* topk_idx, float* topk_w,
                         int32_t* hist, float* gpart, float* lpart, hipStream_t st) {
-  const int64_t nblk = cdiv(T, RT);
   if (dtype == MOE_F32) {
+    const int64_t nblk = cdiv(T, RT);
     hipLaunchKernelGGL(route_f32_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
                        static_cast<const float*>(x), static_cast<const float*>(W_r), b, T, d, E,
                        k, renorm, topk_idx, topk_w, hist, gpart, lpart);
     return hipGetLastError();
   }
   const int neb = static_cast<int>(cdiv(E, 16));
-#define MOE_ROUTE_CASE(N) \
-  case N:                 \
-    return launch_bf16<N>(nblk, st, x, W_r, b, T, d, E, k, renorm, topk_idx, topk_w, hist, gpart, lpart);
+#define MOE_ROUTE_CASE(N)                                                                   \
+  case N:                                                                                   \
+    return launch_bf16_lds<N>(st, x, W_r, b, T, d, E, k, renorm, topk_idx, topk_w, hist, gpart, \
+                              lpart);
+  // up to 16 experts: 16-token blocks with the hidden dimension split over the waves (more blocks
+  // in flight); more: 64-token blocks with W_r shared through LDS
+  if (E <= 16)
+    return launch_bf16<1, 1, 1>(st, x, W_r, b, T, d, E, k, renorm, topk_idx, topk_w, hist, gpart,
+                                lpart);
   switch (neb) {
-    MOE_ROUTE_CASE(1) MOE_ROUTE_CASE(2) MOE_ROUTE_CASE(3) MOE_ROUTE_CASE(4)
-    MOE_ROUTE_CASE(5) MOE_ROUTE_CASE(6) MOE_ROUTE_CASE(7) MOE_ROUTE_CASE(8)
-    MOE_ROUTE_CASE(9) MOE_ROUTE_CASE(10) MOE_ROUTE_CASE(11) MOE_ROUTE_CASE(12)
-    MOE_ROUTE_CASE(13) MOE_ROUTE_CASE(14) MOE_ROUTE_CASE(15) MOE_ROUTE_CASE(16)
-    default:
-      return hipErrorInvalidValue;
+    MOE_ROUTE_CASE(2) MOE_ROUTE_CASE(3) MOE_ROUTE_CASE(4) MOE_ROUTE_CASE(5) MOE_ROUTE_CASE(6)
+    MOE_ROUTE_CASE(7) MOE_ROUTE_CASE(8) MOE_ROUTE_CASE(9) MOE_ROUTE_CASE(10) MOE_ROUTE_CASE(11)
+    MOE_ROUTE_CASE(12) MOE_ROUTE_CASE(13) MOE_ROUTE_CASE(14) MOE_ROUTE_CASE(15) MOE_ROUTE_CASE(16)
+    default: return hipErrorInvalidValue;
   }
 #undef MOE_ROUTE_CASE
 }
