@@ -82,6 +82,9 @@ __device__ __forceinline__ void sched_substep() {
     if (q * RPER < NR) __builtin_amdgcn_sched_group_barrier(kSgDsRead, RPER, 0);
     if (XPER > 0) __builtin_amdgcn_sched_group_barrier(XMASK, XPER, 0);
   }
+  // nothing crosses sub-step boundaries: a sub-step's MFMAs only use fragments read earlier, so
+  // the scheduler cannot pull an MFMA next to the LDS read that feeds it
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // One MR x 256 output tile of group g: rows [row_begin, row_begin + rows_here), output columns
