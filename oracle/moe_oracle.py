@@ -13,6 +13,9 @@ It computes the plain definitions, one step per function, in the notation of the
   [CSDN]   the adg.csdn.net MoE notes page (§四 "Deepseek MoE代码")
   [T4]     "MoE" (t4mako.github.io)
 
+The router scores the experts with a softmax over the logits (the pages' main form) or, as the
+DeepSeek-V3 variant of [CSDN] §九 does, with an independent sigmoid per expert.
+
 Readings taken where the pages are silent or disagree (each is repeated at the function that
 uses it):
 
@@ -21,6 +24,10 @@ uses it):
     experts; the gates come from the unbiased g, renormalised over the chosen set.
   * f_e = n_e / (k T), so that sum_e f_e = 1 for any k and f_e is the argmax fraction at k = 1.
   * P_e is the mean of the full (unmasked, unbiased) softmax probability.
+  * Sigmoid scoring: s_te = sigmoid(l_te); the bias is added to s for selection only; the gates are
+    the chosen unbiased scores renormalised over the chosen set; P_e is the mean of the scores
+    normalised over all experts per token (s_te / sum_e' s_te'), which keeps sum_e P_e = 1 and
+    aux = lambda under uniform routing as in the softmax case; z still uses the raw logits.
   * z = (1/T) sum_t (ln sum_e exp l_te)^2, natural log, raw logits, no coefficient.
   * Capacity C = ceil(c k T / E) evaluated in float64 as ((c * k) * T) / E; overflow is decided in
     ascending token order jointly over all k slots (first come, first kept); dropped slots add
@@ -72,6 +79,25 @@ def softmax_lse(l: np.ndarray):
     lse = m[:, 0] + np.log(np.exp(l - m).sum(axis=1))
     g = np.exp(l - lse[:, None])
     return g, lse
+
+
+def sigmoid_scores(l: np.ndarray) -> np.ndarray:
+    """s_te = 1 / (1 + exp(-l_te)): every expert scored on its own, with no sum over experts
+    ([CSDN] §九, why DeepSeek-V3 moved its gate from softmax to sigmoid). [T, E]"""
+    l = _f64(l)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-l))
+
+
+def score_distribution(g: np.ndarray, scoring: str = "softmax") -> np.ndarray:
+    """Per-token distribution over experts whose mean is P_e: the softmax probabilities
+    themselves, or the sigmoid scores divided by their sum over all experts. [T, E]"""
+    g = _f64(g)
+    if scoring == "softmax":
+        return g
+    if scoring == "sigmoid":
+        return g / g.sum(axis=1, keepdims=True)
+    raise ValueError(f"unknown scoring {scoring!r}")
 
 
 def selection_scores(g: np.ndarray, b: Optional[np.ndarray]) -> np.ndarray:
@@ -223,7 +249,8 @@ def combine(T: int, d: int, row: np.ndarray, w: np.ndarray, out_perm: np.ndarray
 def balance_stats(n: np.ndarray, g: np.ndarray, lse: np.ndarray, k: int, lam: float):
     """f_e = n_e / (k T);  P_e = (1/T) sum_t g_te;  aux = lambda * E * sum_e f_e P_e
     ([ATLAS] §原理与演进, L_balance = lambda E sum_e f_e P_e; [AIATTN] §4.2.1; [CMP] §2.1);
-    z = (1/T) sum_t lse_t^2 ([CMP] §2.2 z-loss L_z). Returns dict of float64 values."""
+    z = (1/T) sum_t lse_t^2 ([CMP] §2.2 z-loss L_z). g is the per-token distribution of
+    score_distribution. Returns dict of float64 values."""
     g = _f64(g)
     T, E = g.shape
     f = _f64(n) / float(k * T)
@@ -247,20 +274,25 @@ def bias_update(b: np.ndarray, n: np.ndarray, k: int, T: int, gamma: float) -> n
 # The whole layer
 # ---------------------------------------------------------------------------------------------
 
-def route(x, W_r, k: int, b=None, renorm: bool = True):
-    """Router stage for all tokens: logits, softmax, selection, gates and margins."""
+def route(x, W_r, k: int, b=None, renorm: bool = True, scoring: str = "softmax"):
+    """Router stage for all tokens: logits, scores (softmax or per-expert sigmoid), selection,
+    gates and margins. lse always comes from the raw logits (z-loss)."""
     l = router_logits(x, W_r)
     g, lse = softmax_lse(l)
+    if scoring == "sigmoid":
+        g = sigmoid_scores(l)
+    elif scoring != "softmax":
+        raise ValueError(f"unknown scoring {scoring!r}")
     s = selection_scores(g, b)
     S = top_k(s, k)
     w = gate_weights(g, S, renorm)
     return {"logits": l, "g": g, "lse": lse, "s": s, "topk_idx": S, "topk_w": w,
-            "margin": topk_margin(s, k)}
+            "margin": topk_margin(s, k), "probs": score_distribution(g, scoring)}
 
 
 def layer_forward(x, W_r, W_gate, W_up, W_down, k: int, b=None, shared=(), c=None,
                   renorm: bool = True, lam: float = 0.01, gamma: float = 1e-3,
-                  topk_idx=None, tokens=None, expert_weights=None):
+                  topk_idx=None, tokens=None, expert_weights=None, scoring: str = "softmax"):
     """y = sum_{e in S_t} w_te E_e(x_t) + sum_s E^s(x_t), plus loads, drops and statistics.
 
     ``topk_idx`` (optional) replaces the oracle's own selection by a given one (to check the stages
@@ -271,14 +303,14 @@ def layer_forward(x, W_r, W_gate, W_up, W_down, k: int, b=None, shared=(), c=Non
     """
     x64 = _f64(x)
     T, d = x64.shape
-    r = route(x64, W_r, k, b, renorm)
+    r = route(x64, W_r, k, b, renorm, scoring)
     E = r["g"].shape[1]
     S = r["topk_idx"] if topk_idx is None else np.asarray(topk_idx, dtype=np.int64)
     w = gate_weights(r["g"], S, renorm)
     n = expert_loads(S, E)
     C = capacity(c, k, T, E)
     dsp = dispatch(S, E, C)
-    stats = balance_stats(n, r["g"], r["lse"], k, lam)
+    stats = balance_stats(n, r["probs"], r["lse"], k, lam)
     want = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     want_set = set(int(t) for t in want)
     # expert outputs for the kept rows of the wanted tokens only

@@ -119,6 +119,89 @@ def test_gate_pins():
     check_gates()
 
 
+# ----------------------------------------------------------------------- sigmoid scoring (V3)
+
+def check_sigmoid(mod=O):
+    l = _rand((80, 16), 11, 4.0)
+    l[3, :4] = [0.0, math.log(3.0), -math.log(3.0), 60.0]
+    s = mod.sigmoid_scores(l)
+    # scipy's logistic function is an independent library routine
+    from scipy.special import expit
+    assert np.allclose(s, expit(l), rtol=1e-15, atol=0)
+    # closed forms: sigma(0) = 1/2, sigma(ln 3) = 3/4, sigma(-ln 3) = 1/4; sigma(l) + sigma(-l) = 1
+    assert s[3, 0] == 0.5
+    assert math.isclose(s[3, 1], 0.75, rel_tol=1e-15) and math.isclose(s[3, 2], 0.25, rel_tol=1e-15)
+    assert np.allclose(s + mod.sigmoid_scores(-l), 1.0, atol=1e-15)
+    # no bias: sigmoid is increasing, so it picks the same experts in the same order as softmax
+    g, _ = mod.softmax_lse(l)
+    for k in (1, 2, 6):
+        assert np.array_equal(mod.top_k(s, k), mod.top_k(g, k))
+    # gates: the chosen scores renormalised; with every expert chosen they are s / sum_e s
+    S = mod.top_k(s, 16)
+    w = mod.gate_weights(s, S, True)
+    dist = mod.score_distribution(s, "sigmoid")
+    assert np.allclose(w, np.take_along_axis(dist, S, 1), rtol=1e-14)
+    # zero router: every score 1/2, renormalised gates 1/k exactly
+    s0 = mod.sigmoid_scores(np.zeros((10, 6)))
+    assert np.all(s0 == 0.5)
+    w0 = mod.gate_weights(s0, mod.top_k(s0, 4), True)
+    assert np.all(w0 == 0.25)
+
+
+def test_sigmoid_pins():
+    check_sigmoid()
+
+
+def check_sigmoid_stats(mod=O):
+    T, E, k = 64, 8, 2
+    l = _rand((T, E), 12, 2.0)
+    r = mod.route(l, np.eye(E), k, scoring="sigmoid")  # x = l, W_r = I: logits are l itself
+    assert np.allclose(r["logits"], l)
+    st = mod.balance_stats(mod.expert_loads(r["topk_idx"], E), r["probs"], r["lse"], k, 0.01)
+    assert abs(st["P"].sum() - 1.0) < 1e-14 and abs(st["f"].sum() - 1.0) < 1e-14
+    # P_e against a plain Python mean of s_te / sum_e' s_te'
+    srow = [[1.0 / (1.0 + math.exp(-float(v))) for v in row] for row in l]
+    ref = sum(row[5] / sum(row) for row in srow) / T
+    assert math.isclose(st["P"][5], ref, rel_tol=1e-13)
+    # z is the softmax lse of the raw logits, whatever the scoring
+    from scipy.special import logsumexp
+    assert math.isclose(st["z"], float((logsumexp(l, axis=1) ** 2).mean()), rel_tol=1e-13)
+    # zero router: uniform scores => aux = lambda exactly
+    r0 = mod.route(np.zeros((T, E)), np.eye(E), k, scoring="sigmoid")
+    st0 = mod.balance_stats(mod.expert_loads(r0["topk_idx"], E), r0["probs"], r0["lse"], k,
+                            GOLDEN["uniform_router_aux"]["lambda"])
+    assert math.isclose(st0["aux"], GOLDEN["uniform_router_aux"]["aux"], rel_tol=1e-14)
+
+
+def test_sigmoid_stats_pins():
+    check_sigmoid_stats()
+
+
+def test_sigmoid_bias_changes_selection_not_gates():
+    # ALF-LB with sigmoid scores: a large bias on expert 0 forces it into every selection, while
+    # each chosen gate stays the unbiased score renormalised over the chosen set
+    T, E, k = 30, 6, 2
+    l = _rand((T, E), 13)
+    b = np.zeros(E)
+    b[0] = 5.0
+    r = O.route(l, np.eye(E), k, b=b, scoring="sigmoid")
+    assert np.all(r["topk_idx"][:, 0] == 0)
+    s = O.sigmoid_scores(l)
+    sel = np.take_along_axis(s, r["topk_idx"], 1)
+    assert np.allclose(r["topk_w"], sel / sel.sum(1, keepdims=True), rtol=1e-14)
+
+
+def test_sigmoid_layer_matches_softmax_when_selection_agrees():
+    # no bias and k = 1: both scorings pick the argmax and the renormalised gate is 1, so the whole
+    # layer output is identical
+    x, W_r, Wg, Wu, Wd = _tiny_layer(k=1)
+    a = O.layer_forward(x, W_r, Wg, Wu, Wd, 1, scoring="softmax")
+    bb = O.layer_forward(x, W_r, Wg, Wu, Wd, 1, scoring="sigmoid")
+    assert np.array_equal(a["topk_idx"], bb["topk_idx"])
+    assert np.allclose(a["y"], bb["y"], rtol=1e-13, atol=1e-13)
+    assert np.array_equal(a["n"], bb["n"]) and math.isclose(a["z"], bb["z"], rel_tol=1e-15)
+
+
 # --------------------------------------------------------------------------------- statistics
 
 def check_stats(mod=O):
@@ -422,6 +505,15 @@ def _gate_from_biased(g, S, renorm=True):
     return O.gate_weights(g + 0.01, S, renorm)
 
 
+def _sigmoid_wrong_sign(l):
+    l = O._f64(l)
+    return 1.0 / (1.0 + np.exp(l))
+
+
+def _sigmoid_unnormalised_P(g, scoring="softmax"):
+    return O._f64(g)
+
+
 @pytest.mark.parametrize("mutant,checks", [
     (dict(gate_weights=_no_renorm), [check_gates]),
     (dict(top_k=_ties_high), [check_topk]),
@@ -431,6 +523,8 @@ def _gate_from_biased(g, S, renorm=True):
     (dict(dispatch=_dispatch_last_kept), [lambda m: check_dispatch(m, exhaustive=False)]),
     (dict(softmax_lse=_lse_no_max), [check_softmax]),
     (dict(gate_weights=_gate_from_biased), [check_gates]),
+    (dict(sigmoid_scores=_sigmoid_wrong_sign), [check_sigmoid]),
+    (dict(score_distribution=_sigmoid_unnormalised_P), [check_sigmoid_stats]),
 ])
 def test_planted_mistakes_are_caught(mutant, checks):
     m = _Mutant(**mutant)
