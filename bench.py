@@ -76,6 +76,7 @@ def cpu_baseline(cfg, inp, seconds: float):
         t0 = time.perf_counter()
         O.layer_forward(inp.x[:n], inp.W_r, inp.W_gate, inp.W_up, inp.W_down, cfg.k,
                         b=inp.b, shared=shared, c=cfg.c, renorm=cfg.renorm, lam=cfg.lam,
+                        scoring=cfg.scoring,
                         gamma=cfg.gamma)
         return time.perf_counter() - t0
 
@@ -123,7 +124,8 @@ def main():
     sh = host.shared_fused()
     sh = None if sh is None else tuple(t.to(dev) for t in sh)
 
-    layer = moe.MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.M, cfg.S, cfg.c, cfg.renorm, dt, dev)
+    layer = moe.MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.M, cfg.S, cfg.c, cfg.renorm, dt, dev,
+                         cfg.scoring)
     out = layer.alloc_outputs(with_bias=b is not None)
 
     def step():
@@ -211,7 +213,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": name, "T": T, "d": d, "E": E, "k": k, "M": M, "S": S,
-                   "capacity_factor": cfg.c, "bias": cfg.bias, "kept_assignments": kept,
+                   "capacity_factor": cfg.c, "bias": cfg.bias, "scoring": cfg.scoring,
+                   "kept_assignments": kept,
                    "dropped_assignments": int(overflow.sum()), "max_load": int(counts.max())},
         "mfma_peak_frac_layer": round(layer_tf / peak, 4), "layer_tflops": round(layer_tf, 1),
         "roofline": roofline, "stages": stages, "cpu_baseline": cpu,

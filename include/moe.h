@@ -5,8 +5,9 @@
  *
  *     y_t = sum_{e in S_t} w_te * E_e(x_t)  +  sum_{s < S} E^s(x_t)
  *
- * with router probabilities g_t = softmax(W_r x_t), selection S_t = TopK(g_t + b) over the routed
- * experts, gates w_te = g_te renormalised over S_t, SwiGLU experts
+ * with router probabilities g_t = softmax(W_r x_t) (or per-expert sigmoid scores, the DeepSeek-V3
+ * gate), selection S_t = TopK(g_t + b) over the routed experts, gates w_te = g_te renormalised
+ * over S_t, SwiGLU experts
  * E_e(x) = W_down,e (SiLU(W_gate,e x) ⊙ (W_up,e x)), optional shared experts applied to every
  * token, and an optional per-expert capacity C = ceil(c k T / E) that drops overflow assignments.
  * Alongside it come the balance statistics f_e, P_e, aux = lambda E sum_e f_e P_e and the router
@@ -17,6 +18,7 @@
  *   - "深入理解 MoE (混合专家模型)：稀疏激活与高效扩展": §4.2.1 (f_i, P_i, alpha = 0.01);
  *     §10.2 / §11 (SwiGLU(x) = SiLU(W_1 x) ⊙ (W_3 x), W_2 projects back).
  *   - "MOE大模型对比篇": §2.1 (balance loss), §2.2 (z-loss), §3.3 (shared experts).
+ *   - the adg.csdn.net MoE notes page: §九 (DeepSeek-V3 scores experts with a sigmoid).
  *
  * Conventions for every entry point:
  *   - Pointers named as device buffers are device pointers owned by the caller; tensors are dense,
@@ -53,6 +55,12 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* How the router scores the experts from the logits l_te. */
+typedef enum {
+  MOE_SCORE_SOFTMAX = 0, /* g_te = softmax_e(l_t)                                        */
+  MOE_SCORE_SIGMOID = 1  /* g_te = 1 / (1 + exp(-l_te)), each expert on its own          */
+} moe_scoring;
+
 /* Which entry point a workspace is sized for. */
 typedef enum {
   MOE_CALL_ROUTE = 0,
@@ -75,6 +83,7 @@ typedef struct {
   float c;        /* capacity factor; <= 0 means no capacity limit; NaN is invalid            */
   int32_t renorm; /* 1: renormalise the chosen gates over S_t; 0: use g_te as is               */
   int32_t dtype;  /* moe_dtype                                                                */
+  int32_t scoring; /* moe_scoring                                                             */
 } moe_shape;
 
 /* Short text for a status code (static storage). */
@@ -95,14 +104,16 @@ size_t moe_workspace_size(const moe_shape* s, int call);
  * moe_route -- router of "MoE：条件计算与路由" §原理与演进 and §无辅助损失负载均衡（ALF-LB）.
  *
  * For every token t: l_te = sum_i x_ti W_r,ei (no router bias); m = max_e l_te,
- * lse_t = m + ln sum_e exp(l_te - m), g_te = exp(l_te - lse_t); s_te = g_te + b_e (b optional);
+ * lse_t = m + ln sum_e exp(l_te - m), g_te = exp(l_te - lse_t) (MOE_SCORE_SOFTMAX) or
+ * g_te = 1 / (1 + exp(-l_te)) (MOE_SCORE_SIGMOID); s_te = g_te + b_e (b optional);
  * S_t = the k experts of largest s_te, in descending s order, equal scores to the lower index;
  * w_tj = g_t,S_tj / sum_j' g_t,S_tj' (or g_t,S_tj when renorm == 0).
  *   x        device [T, d] (dtype)          W_r   device [E, d] (dtype)
  *   b        device [E] fp32 or NULL (selection only; gates use the unbiased g)
  *   topk_idx device out [T, k] int32        topk_w device out [T, k] fp32
  *   n        device out [E] int32: loads n_e = #{t : e in S_t}, before any capacity limit
- *   gsum     device out [E] double: sum_t g_te        lse2sum device out [1] double: sum_t lse_t^2
+ *   gsum     device out [E] double: sum_t p_te, p = g (softmax) or g_te / sum_e' g_te' (sigmoid)
+ *   lse2sum  device out [1] double: sum_t lse_t^2 (raw logits, either scoring)
  *   ws       device workspace of moe_workspace_size(s, MOE_CALL_ROUTE) bytes
  */
 moe_status moe_route(const moe_shape* s, const void* x, const void* W_r, const float* b,

@@ -34,7 +34,11 @@ class MoEError(RuntimeError):
 class Shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("M", ctypes.c_int32), ("S", ctypes.c_int32),
-                ("c", ctypes.c_float), ("renorm", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("c", ctypes.c_float), ("renorm", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("scoring", ctypes.c_int32)]
+
+
+SCORING = {"softmax": 0, "sigmoid": 1}  # moe_scoring
 
 
 _P = ctypes.c_void_p
@@ -105,9 +109,13 @@ def _dtype_code(dt: torch.dtype) -> int:
 
 
 def make_shape(T: int, d: int, E: int, k: int, M: int, S: int = 0, c: Optional[float] = None,
-               renorm: bool = True, dtype: torch.dtype = torch.bfloat16) -> Shape:
+               renorm: bool = True, dtype: torch.dtype = torch.bfloat16,
+               scoring: str = "softmax") -> Shape:
+    if scoring not in SCORING:
+        raise ValueError(f"scoring must be one of {sorted(SCORING)}, got {scoring!r}")
     return Shape(int(T), int(d), int(E), int(k), int(M), int(S),
-                 float(c) if c is not None else 0.0, 1 if renorm else 0, _dtype_code(dtype))
+                 float(c) if c is not None else 0.0, 1 if renorm else 0, _dtype_code(dtype),
+                 SCORING[scoring])
 
 
 def check_shape(s: Shape) -> int:
@@ -152,10 +160,11 @@ def workspace(s: Shape, call: int, device) -> torch.Tensor:
 # --------------------------------------------------------------------------------- entry points
 
 def moe_route(x: torch.Tensor, W_r: torch.Tensor, k: int, b: Optional[torch.Tensor] = None,
-              renorm: bool = True, ws: Optional[torch.Tensor] = None) -> dict:
+              renorm: bool = True, ws: Optional[torch.Tensor] = None,
+              scoring: str = "softmax") -> dict:
     T, d = x.shape
     E = W_r.shape[0]
-    s = make_shape(T, d, E, k, 8, renorm=renorm, dtype=x.dtype)
+    s = make_shape(T, d, E, k, 8, renorm=renorm, dtype=x.dtype, scoring=scoring)
     _dev(x, "x")
     _dev(W_r, "W_r", x.dtype, (E, d))
     if b is not None:
@@ -265,8 +274,8 @@ class MoELayer:
 
     def __init__(self, T: int, d: int, E: int, k: int, M: int, S: int = 0,
                  c: Optional[float] = None, renorm: bool = True,
-                 dtype: torch.dtype = torch.bfloat16, device="cuda"):
-        self.shape = make_shape(T, d, E, k, M, S, c, renorm, dtype)
+                 dtype: torch.dtype = torch.bfloat16, device="cuda", scoring: str = "softmax"):
+        self.shape = make_shape(T, d, E, k, M, S, c, renorm, dtype, scoring)
         _check(check_shape(self.shape), "MoELayer")
         self.T, self.d, self.E, self.k, self.M, self.S = T, d, E, k, M, S
         self.dtype = dtype
@@ -334,14 +343,14 @@ def moe_set_stage_events(events) -> None:
 
 def moe_layer_forward(x, W_r, W_gate, W_up, W_down, k: int, b=None, shared=None,
                       c: Optional[float] = None, renorm: bool = True, lam: float = 0.01,
-                      gamma: float = 1e-3) -> dict:
+                      gamma: float = 1e-3, scoring: str = "softmax") -> dict:
     """One call of the whole layer (allocates its workspace; use MoELayer to reuse one)."""
     T, d = x.shape
     E, M, _ = W_gate.shape
     S = 0
     if shared is not None:
         S = shared[0].shape[0] // M
-    layer = MoELayer(T, d, E, k, M, S, c, renorm, x.dtype, x.device)
+    layer = MoELayer(T, d, E, k, M, S, c, renorm, x.dtype, x.device, scoring)
     return layer.forward(x, W_r, W_gate, W_up, W_down, b, shared, lam, gamma)
 
 

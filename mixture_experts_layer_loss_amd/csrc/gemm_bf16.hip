@@ -13,6 +13,9 @@
 // same output columns, so a lane holds gate and up values of the same (row, column) and applies
 // SiLU(g) * u in registers; h leaves as bf16. The down projection uses 256 plain columns.
 //
+// Row gather: with a gather list the A rows are read in place from the token matrix (row r of
+// the group layout is x[gather[r]]), so the dispatch never materialises the permuted copy of x.
+//
 // Ragged groups (experts): a group's rows are cut into 256-row tiles; a remainder of 65..128 rows
 // becomes a 128-row tile and one of 1..64 rows a 64-row tile, each with its own wave layout, so
 // padding rows cost at most half of their tile. The three tile tables (exclusive prefixes per
@@ -90,8 +93,9 @@ __device__ __forceinline__ void sched_substep() {
 // One MR x 256 output tile of group g: rows [row_begin, row_begin + rows_here), output columns
 // [n0, n0 + BNO). EPI 0: SwiGLU (B0 = W_gate, B1 = W_up); EPI 1: plain (B0 = W_down).
 // KTAIL: K is not a multiple of 64 (the last k-slice is zero-padded).
-template <int EPI, bool KTAIL, int MR>
+template <int EPI, bool KTAIL, bool GATHER, int MR>
 __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __restrict__ A,
+                                         const int32_t* __restrict__ gather,
                                          const bf16_t* __restrict__ B0,
                                          const bf16_t* __restrict__ B1, int64_t group_stride,
                                          int N, int K, bf16_t* __restrict__ C, int g,
@@ -104,10 +108,18 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
 
   // ---- global loads: thread `tid` moves chunk (tid & 7) of rows r0 + RS i of the A slice
   // (i < ACH) and of the B slice (i < BCH). Addresses are uniform tile bases plus 32-bit byte
-  // offsets fixed over K; rows past the group (A) or past N (B) re-read the last valid row and
-  // never reach a stored output.
+  // offsets fixed over K (gathered A rows: one 64-bit row address each); rows past the group (A)
+  // or past N (B) re-read the last valid row and never reach a stored output.
   const int r0 = tid >> 3, kc_t = (tid & 7) * 8;
   const char* a_base = reinterpret_cast<const char*>(A + static_cast<int64_t>(row_begin) * K);
+  const char* a_row[GATHER ? ACH : 1];
+  if constexpr (GATHER) {
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+      const int t = gather[row_begin + min(i * RS + r0, rows_here - 1)];
+      a_row[i] = reinterpret_cast<const char*>(A + static_cast<int64_t>(t) * K + kc_t);
+    }
+  }
   const bf16_t* Bg0 = B0 + static_cast<int64_t>(g) * group_stride + static_cast<int64_t>(n0) * K;
   const bf16_t* Bg1 =
       EPI == 0 ? B1 + static_cast<int64_t>(g) * group_stride + static_cast<int64_t>(n0) * K : Bg0;
@@ -132,7 +144,8 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
     const uint32_t kb = static_cast<uint32_t>((in ? k0 : K - 8 - kc_t) * 2);
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(a_base + (a_off[i] + kb));
+      const char* ap = GATHER ? a_row[GATHER ? i : 0] + kb : a_base + (a_off[i] + kb);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ap);
       ra[i] = KTAIL ? (in ? v : zero) : v;
     }
 #pragma unroll
@@ -295,9 +308,10 @@ __device__ __forceinline__ int find_group(const int32_t* __restrict__ table, int
 
 // tile_off: three tables of groups + 1 entries: 256-row tiles, 128-row tiles, 64-row tiles.
 // Blocks [0, main_blocks) serve the 256-row tiles, the rest the smaller ones.
-template <int EPI, bool KTAIL>
+template <int EPI, bool KTAIL, bool GATHER>
 __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
-    const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+    const bf16_t* __restrict__ A, const int32_t* __restrict__ gather,
+    const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tile_off, int groups, int main_blocks,
     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, int64_t group_stride, int N,
     int K, bf16_t* __restrict__ C) {
@@ -318,8 +332,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     const int nb = static_cast<int>(local / mt_g), mt = static_cast<int>(local % mt_g);
     const int row_begin = offsets[g] + mt * 256;
     const int rows = min(256, offsets[g + 1] - row_begin);
-    run_tile<EPI, KTAIL, 256>(lds, A, B0, B1, group_stride, N, K, C, g, row_begin, rows,
-                              nb * BNO);
+    run_tile<EPI, KTAIL, GATHER, 256>(lds, A, gather, B0, B1, group_stride, N, K, C, g,
+                                      row_begin, rows, nb * BNO);
     return;
   }
   // a group's remainder tile (at most one per group and class): n-blocks in order
@@ -338,13 +352,16 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
   const int rows = rows_g & 255;
   const int n0 = static_cast<int>(local) * BNO;
   if (table == t128)
-    run_tile<EPI, KTAIL, 128>(lds, A, B0, B1, group_stride, N, K, C, g, row_begin, rows, n0);
+    run_tile<EPI, KTAIL, GATHER, 128>(lds, A, gather, B0, B1, group_stride, N, K, C, g, row_begin,
+                                      rows, n0);
   else
-    run_tile<EPI, KTAIL, 64>(lds, A, B0, B1, group_stride, N, K, C, g, row_begin, rows, n0);
+    run_tile<EPI, KTAIL, GATHER, 64>(lds, A, gather, B0, B1, group_stride, N, K, C, g, row_begin,
+                                     rows, n0);
 }
 
-template <int EPI, bool KTAIL>
-hipError_t launch_gemm_t(const bf16_t* A, const int32_t* offsets, const int32_t* tile_off,
+template <int EPI, bool KTAIL, bool GATHER>
+hipError_t launch_gemm_t(const bf16_t* A, const int32_t* gather, const int32_t* offsets,
+                         const int32_t* tile_off,
                          int groups, int64_t max_tiles, const bf16_t* B0, const bf16_t* B1,
                          int64_t group_stride, int N, int K, bf16_t* C, hipStream_t st) {
   constexpr int BNO = EPI == 0 ? BN / 2 : BN;
@@ -359,46 +376,55 @@ hipError_t launch_gemm_t(const bf16_t* A, const int32_t* offsets, const int32_t*
   static std::atomic<bool> attr_set{false};
   if (!attr_set.load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&grouped_gemm_kernel<EPI, KTAIL>),
+        reinterpret_cast<const void*>(&grouped_gemm_kernel<EPI, KTAIL, GATHER>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     attr_set.store(true, std::memory_order_release);
   }
   if (max_tiles <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((grouped_gemm_kernel<EPI, KTAIL>), dim3(static_cast<unsigned>(grid)),
-                     dim3(NT), lds, st, A, offsets, tile_off, groups,
+  hipLaunchKernelGGL((grouped_gemm_kernel<EPI, KTAIL, GATHER>), dim3(static_cast<unsigned>(grid)),
+                     dim3(NT), lds, st, A, gather, offsets, tile_off, groups,
                      static_cast<int>(main_blocks), B0, B1, group_stride, N, K, C);
   return hipGetLastError();
 }
 
-template <int EPI>
-hipError_t launch_gemm(const bf16_t* A, const int32_t* offsets, const int32_t* tile_off, int groups,
-                       int64_t max_tiles, const bf16_t* B0, const bf16_t* B1, int64_t group_stride,
-                       int N, int K, bf16_t* C, hipStream_t st) {
+template <int EPI, bool GATHER>
+hipError_t launch_gemm(const bf16_t* A, const int32_t* gather, const int32_t* offsets,
+                       const int32_t* tile_off, int groups, int64_t max_tiles, const bf16_t* B0,
+                       const bf16_t* B1, int64_t group_stride, int N, int K, bf16_t* C,
+                       hipStream_t st) {
   if (K % BK == 0)
-    return launch_gemm_t<EPI, false>(A, offsets, tile_off, groups, max_tiles, B0, B1, group_stride,
-                                     N, K, C, st);
-  return launch_gemm_t<EPI, true>(A, offsets, tile_off, groups, max_tiles, B0, B1, group_stride, N,
-                                  K, C, st);
+    return launch_gemm_t<EPI, false, GATHER>(A, gather, offsets, tile_off, groups, max_tiles, B0,
+                                             B1, group_stride, N, K, C, st);
+  return launch_gemm_t<EPI, true, GATHER>(A, gather, offsets, tile_off, groups, max_tiles, B0, B1,
+                                          group_stride, N, K, C, st);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_up_bf16(int groups, int d, int Mg, const void* rows,
-                               const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
-                               const void* W_gate, const void* W_up, void* h, hipStream_t st) {
-  return launch_gemm<0>(static_cast<const bf16_t*>(rows), offsets, tile_off, groups, max_tiles,
-                        static_cast<const bf16_t*>(W_gate), static_cast<const bf16_t*>(W_up),
-                        static_cast<int64_t>(Mg) * d, Mg, d, static_cast<bf16_t*>(h), st);
+                               const int32_t* gather, const int32_t* offsets,
+                               const int32_t* tile_off, int64_t max_tiles, const void* W_gate,
+                               const void* W_up, void* h, hipStream_t st) {
+  const bf16_t* A = static_cast<const bf16_t*>(rows);
+  const bf16_t* Wg = static_cast<const bf16_t*>(W_gate);
+  const bf16_t* Wu = static_cast<const bf16_t*>(W_up);
+  const int64_t gs = static_cast<int64_t>(Mg) * d;
+  bf16_t* H = static_cast<bf16_t*>(h);
+  if (gather != nullptr)
+    return launch_gemm<0, true>(A, gather, offsets, tile_off, groups, max_tiles, Wg, Wu, gs, Mg, d,
+                                H, st);
+  return launch_gemm<0, false>(A, nullptr, offsets, tile_off, groups, max_tiles, Wg, Wu, gs, Mg, d,
+                               H, st);
 }
 
 hipError_t launch_gemm_down_bf16(int groups, int d, int Mg, const int32_t* offsets,
                                  const int32_t* tile_off, int64_t max_tiles, const void* W_down,
                                  const void* h, void* out, hipStream_t st) {
-  return launch_gemm<1>(static_cast<const bf16_t*>(h), offsets, tile_off, groups, max_tiles,
-                        static_cast<const bf16_t*>(W_down), nullptr,
-                        static_cast<int64_t>(Mg) * d, d, Mg, static_cast<bf16_t*>(out), st);
+  return launch_gemm<1, false>(static_cast<const bf16_t*>(h), nullptr, offsets, tile_off, groups,
+                               max_tiles, static_cast<const bf16_t*>(W_down), nullptr,
+                               static_cast<int64_t>(Mg) * d, d, Mg, static_cast<bf16_t*>(out), st);
 }
 
 }  // namespace moe

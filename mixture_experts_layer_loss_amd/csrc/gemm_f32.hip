@@ -13,9 +13,12 @@ constexpr int BM = kGemmF32BM;  // 64
 constexpr int BN = 64;
 constexpr int BK = 16;
 
-template <int EPI>  // 0: SwiGLU (B0 = W_gate, B1 = W_up), 1: plain (B0 = W_down)
+// EPI 0: SwiGLU (B0 = W_gate, B1 = W_up), 1: plain (B0 = W_down). gather (may be NULL): A row r
+// is A[gather[r]].
+template <int EPI>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
-    const float* __restrict__ A, const int32_t* __restrict__ offsets,
+    const float* __restrict__ A, const int32_t* __restrict__ gather,
+    const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tile_off, int groups, const float* __restrict__ B0,
     const float* __restrict__ B1, int64_t group_stride, int N, int K, float* __restrict__ C) {
   __shared__ float As[BK][BM + 1];
@@ -43,7 +46,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
   for (int k0 = 0; k0 < K; k0 += BK) {
     for (int c = tid; c < BM * BK; c += 256) {
       const int r = c / BK, kk = c % BK;
-      const int ar = min(row_begin + r, row_end - 1);
+      int ar = min(row_begin + r, row_end - 1);
+      if (gather != nullptr) ar = gather[ar];
       As[kk][r] = (k0 + kk < K) ? A[static_cast<int64_t>(ar) * K + k0 + kk] : 0.f;
 #pragma unroll
       for (int m = 0; m < (EPI == 0 ? 2 : 1); ++m) {
@@ -88,12 +92,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
 }  // namespace
 
 hipError_t launch_gemm_up_f32(int groups, int d, int Mg, const void* rows,
-                              const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
-                              const void* W_gate, const void* W_up, void* h, hipStream_t st) {
+                              const int32_t* gather, const int32_t* offsets,
+                              const int32_t* tile_off, int64_t max_tiles, const void* W_gate,
+                              const void* W_up, void* h, hipStream_t st) {
   const int64_t grid = max_tiles * cdiv(Mg, BN);
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(grouped_gemm_f32_kernel<0>, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
-                     st, static_cast<const float*>(rows), offsets, tile_off, groups,
+                     st, static_cast<const float*>(rows), gather, offsets, tile_off, groups,
                      static_cast<const float*>(W_gate), static_cast<const float*>(W_up),
                      static_cast<int64_t>(Mg) * d, Mg, d, static_cast<float*>(h));
   return hipGetLastError();
@@ -105,7 +110,7 @@ hipError_t launch_gemm_down_f32(int groups, int d, int Mg, const int32_t* offset
   const int64_t grid = max_tiles * cdiv(d, BN);
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(grouped_gemm_f32_kernel<1>, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
-                     st, static_cast<const float*>(h), offsets, tile_off, groups,
+                     st, static_cast<const float*>(h), nullptr, offsets, tile_off, groups,
                      static_cast<const float*>(W_down), nullptr, static_cast<int64_t>(Mg) * d, d,
                      Mg, static_cast<float*>(out));
   return hipGetLastError();

@@ -8,26 +8,29 @@
 
 namespace moe {
 hipError_t launch_gemm_up_bf16(int groups, int d, int Mg, const void* rows,
-                               const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
-                               const void* W_gate, const void* W_up, void* h, hipStream_t st);
+                               const int32_t* gather, const int32_t* offsets,
+                               const int32_t* tile_off, int64_t max_tiles, const void* W_gate,
+                               const void* W_up, void* h, hipStream_t st);
 hipError_t launch_gemm_down_bf16(int groups, int d, int Mg, const int32_t* offsets,
                                  const int32_t* tile_off, int64_t max_tiles, const void* W_down,
                                  const void* h, void* out, hipStream_t st);
 hipError_t launch_gemm_up_f32(int groups, int d, int Mg, const void* rows,
-                              const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
-                              const void* W_gate, const void* W_up, void* h, hipStream_t st);
+                              const int32_t* gather, const int32_t* offsets,
+                              const int32_t* tile_off, int64_t max_tiles, const void* W_gate,
+                              const void* W_up, void* h, hipStream_t st);
 hipError_t launch_gemm_down_f32(int groups, int d, int Mg, const int32_t* offsets,
                                 const int32_t* tile_off, int64_t max_tiles, const void* W_down,
                                 const void* h, void* out, hipStream_t st);
 
 hipError_t launch_gemm_up(int dtype, int groups, int d, int Mg, const void* rows,
-                          const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
-                          const void* W_gate, const void* W_up, void* h, hipStream_t st) {
+                          const int32_t* gather, const int32_t* offsets, const int32_t* tile_off,
+                          int64_t max_tiles, const void* W_gate, const void* W_up, void* h,
+                          hipStream_t st) {
   return dtype == MOE_F32
-             ? launch_gemm_up_f32(groups, d, Mg, rows, offsets, tile_off, max_tiles, W_gate, W_up,
-                                  h, st)
-             : launch_gemm_up_bf16(groups, d, Mg, rows, offsets, tile_off, max_tiles, W_gate,
-                                   W_up, h, st);
+             ? launch_gemm_up_f32(groups, d, Mg, rows, gather, offsets, tile_off, max_tiles,
+                                  W_gate, W_up, h, st)
+             : launch_gemm_up_bf16(groups, d, Mg, rows, gather, offsets, tile_off, max_tiles,
+                                   W_gate, W_up, h, st);
 }
 
 hipError_t launch_gemm_down(int dtype, int groups, int d, int Mg, const int32_t* offsets,
@@ -49,6 +52,9 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 int elem_bytes(const moe_shape* s) { return s->dtype == MOE_F32 ? 4 : 2; }
+int route_flags(const moe_shape* s) {
+  return (s->renorm ? kRouteRenorm : 0) | (s->scoring == MOE_SCORE_SIGMOID ? kRouteSigmoid : 0);
+}
 int gemm_bm(const moe_shape* s) { return s->dtype == MOE_F32 ? kGemmF32BM : kGemmBM; }
 int64_t nblocks(const moe_shape* s) { return cdiv(s->T, kRouteTokens); }
 int64_t route_blocks(const moe_shape* s) { return cdiv(s->T, route_block_tokens(s->dtype, s->E)); }
@@ -113,7 +119,7 @@ struct LayerPlan {
       *inv_perm, *sh_offsets, *sh_tile_off;
   float* topk_w;
   double *gsum, *lse2sum;
-  void *x_perm, *h, *out_perm, *h_sh, *sh;
+  void *h, *out_perm, *h_sh, *sh;
 };
 LayerPlan plan_layer(Carve& c, const moe_shape* s) {
   const size_t P = static_cast<size_t>(s->T) * s->k;
@@ -135,7 +141,6 @@ LayerPlan plan_layer(Carve& c, const moe_shape* s) {
   p.sh_tile_off = c.take<int32_t>(3 * 2);
   p.perm_token = c.take<int32_t>(R);
   p.inv_perm = c.take<int32_t>(P);
-  p.x_perm = c.take<unsigned char>(R * s->d * eb);
   p.h = c.take<unsigned char>(R * s->M * eb);
   p.out_perm = c.take<unsigned char>(R * s->d * eb);
   if (s->S > 0) {
@@ -178,6 +183,8 @@ moe_status moe_check_shape(const moe_shape* s) {
   if (s->T < 1 || s->d < 1 || s->E < 1 || s->k < 1 || s->M < 1 || s->S < 0)
     return MOE_ERR_INVALID_ARGUMENT;
   if (isnan(s->c) || (s->renorm != 0 && s->renorm != 1)) return MOE_ERR_INVALID_ARGUMENT;
+  if (s->scoring != MOE_SCORE_SOFTMAX && s->scoring != MOE_SCORE_SIGMOID)
+    return MOE_ERR_INVALID_ARGUMENT;
   if (s->k > s->E) return MOE_ERR_INVALID_ARGUMENT;
   if (s->E > MOE_E_MAX || s->k > MOE_K_MAX) return MOE_ERR_UNSUPPORTED;
   const int vec = s->dtype == MOE_F32 ? 4 : 8;  // elements per 16-byte chunk
@@ -219,7 +226,7 @@ moe_status moe_route(const moe_shape* s, const void* x, const void* W_r, const f
   hipStream_t hs = static_cast<hipStream_t>(stream);
   Carve c(ws);
   RoutePlan p = plan_route(c, s);
-  hipError_t e = launch_route(s->dtype, s->T, s->d, s->E, s->k, s->renorm, x, W_r, b, topk_idx,
+  hipError_t e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s), x, W_r, b, topk_idx,
                               topk_w, p.hist, p.gpart, p.lpart, hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = launch_scan(s->T, s->E, -1, static_cast<int>(route_blocks(s)), p.hist, p.gpart, p.lpart, nullptr,
@@ -274,8 +281,8 @@ moe_status moe_expert_ffn(const moe_shape* s, int32_t groups, int32_t Mg, const 
   hipError_t e = launch_schedule(groups, offsets, tile_off, BM, hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
   const int64_t max_tiles = cdiv(max_rows, BM) + groups;
-  e = launch_gemm_up(s->dtype, groups, s->d, Mg, rows, offsets, tile_off, max_tiles, W_gate, W_up,
-                     h, hs);
+  e = launch_gemm_up(s->dtype, groups, s->d, Mg, rows, nullptr, offsets, tile_off, max_tiles,
+                     W_gate, W_up, h, hs);
   if (e == hipSuccess)
     e = launch_gemm_down(s->dtype, groups, s->d, Mg, offsets, tile_off, max_tiles, W_down, h, out,
                          hs);
@@ -339,19 +346,20 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
   const int64_t max_tiles = cdiv(routed_rows(s), BM) + s->E;
 
   mark_stage(0, hs);
-  hipError_t e = launch_route(s->dtype, s->T, s->d, s->E, s->k, s->renorm, x, W_r, b, idx, w,
+  hipError_t e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s), x, W_r, b, idx, w,
                               p.r.hist, p.r.gpart, p.r.lpart, hs);
   mark_stage(1, hs);
   if (e == hipSuccess)
     e = launch_scan(s->T, s->E, C, nblk, p.r.hist, p.r.gpart, p.r.lpart, p.block_base, n, p.gsum,
                     p.lse2sum, p.kept, ovf, p.offsets, p.tile_off, BM, hs);
+  // placement only: the gate/up GEMM gathers its rows from x through perm_token
   if (e == hipSuccess)
     e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx, route_block_tokens(s->dtype, s->E),
-                       p.block_base, p.offsets, p.x_perm, p.perm_token, p.inv_perm, hs);
+                       p.block_base, p.offsets, nullptr, p.perm_token, p.inv_perm, hs);
   mark_stage(2, hs);
   if (e == hipSuccess)
-    e = launch_gemm_up(s->dtype, s->E, s->d, s->M, p.x_perm, p.offsets, p.tile_off, max_tiles,
-                       W_gate, W_up, p.h, hs);
+    e = launch_gemm_up(s->dtype, s->E, s->d, s->M, x, p.perm_token, p.offsets, p.tile_off,
+                       max_tiles, W_gate, W_up, p.h, hs);
   mark_stage(3, hs);
   if (e == hipSuccess)
     e = launch_gemm_down(s->dtype, s->E, s->d, s->M, p.offsets, p.tile_off, max_tiles, W_down,
@@ -362,8 +370,8 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
     const int64_t sh_tiles = cdiv(s->T, BM);
     e = launch_shared_table(s->T, BM, p.sh_offsets, p.sh_tile_off, hs);
     if (e == hipSuccess)
-      e = launch_gemm_up(s->dtype, 1, s->d, SM, x, p.sh_offsets, p.sh_tile_off, sh_tiles, Ws_gate,
-                         Ws_up, p.h_sh, hs);
+      e = launch_gemm_up(s->dtype, 1, s->d, SM, x, nullptr, p.sh_offsets, p.sh_tile_off, sh_tiles,
+                         Ws_gate, Ws_up, p.h_sh, hs);
     if (e == hipSuccess)
       e = launch_gemm_down(s->dtype, 1, s->d, SM, p.sh_offsets, p.sh_tile_off, sh_tiles, Ws_down,
                            p.h_sh, p.sh, hs);

@@ -48,10 +48,13 @@ __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 
 // block of this many tokens (a divisor of kRouteTokens).
 int route_block_tokens(int dtype, int E);
 
+// Router flags: renormalise the chosen gates; score the experts with a sigmoid (else softmax).
+constexpr int kRouteRenorm = 1, kRouteSigmoid = 2;
+
 // Router: logits, softmax/LSE, biased top-k, gates, per-block partial statistics and histograms.
 //   hist  [nblk, E] int32, gpart [nblk, E] fp32, lpart [nblk] fp32,
 //   nblk = ceil(T / route_block_tokens(dtype, E))
-hipError_t launch_route(int dtype, int64_t T, int d, int E, int k, int renorm, const void* x,
+hipError_t launch_route(int dtype, int64_t T, int d, int E, int k, int flags, const void* x,
                         const void* W_r, const float* b, int32_t* topk_idx, float* topk_w,
                         int32_t* hist, float* gpart, float* lpart, hipStream_t st);
 
@@ -82,11 +85,13 @@ hipError_t launch_schedule(int groups, const int32_t* offsets, int32_t* tile_off
                            hipStream_t st);
 
 // Grouped SwiGLU FFN in two launches. max_tiles = upper bound of sum_g ceil(rows_g / BM).
-//   gate/up: h[r] = SiLU(rows[r] W_gate[g]^T) * (rows[r] W_up[g]^T)
+//   gate/up: h[r] = SiLU(a_r W_gate[g]^T) * (a_r W_up[g]^T), a_r = rows[r], or rows[gather[r]]
+//            when gather != NULL (rows is then the token matrix)
 //   down:    out[r] = h[r] W_down[g]^T
 hipError_t launch_gemm_up(int dtype, int groups, int d, int Mg, const void* rows,
-                          const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
-                          const void* W_gate, const void* W_up, void* h, hipStream_t st);
+                          const int32_t* gather, const int32_t* offsets, const int32_t* tile_off,
+                          int64_t max_tiles, const void* W_gate, const void* W_up, void* h,
+                          hipStream_t st);
 hipError_t launch_gemm_down(int dtype, int groups, int d, int Mg, const int32_t* offsets,
                             const int32_t* tile_off, int64_t max_tiles, const void* W_down,
                             const void* h, void* out, hipStream_t st);

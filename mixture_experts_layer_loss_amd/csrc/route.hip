@@ -1,6 +1,9 @@
 // Router kernel: l = x W_r^T, max-subtracted softmax with log-sum-exp, biased top-k selection,
 // renormalised gates and per-block partial statistics ("MoE：条件计算与路由" §原理与演进,
 // §无辅助损失负载均衡（ALF-LB）, §7 eqs. (1)-(2); "MOE大模型对比篇" §2.2 for the LSE term).
+// With sigmoid scoring (the DeepSeek-V3 gate of the adg.csdn.net notes page, §九) each expert's
+// score is 1 / (1 + exp(-l)) on its own; selection, bias and renormalisation are unchanged, the
+// probability statistic uses the scores normalised over the experts, and lse still feeds z.
 //
 // A block owns TB consecutive tokens (bf16: 8 waves, 16 tokens when E <= 16, else 64; fp32: 4
 // waves, 64 tokens). The logits tile [TB x E] never leaves the chip: bf16 inputs go through
@@ -13,6 +16,8 @@
 #include "moe_internal.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace moe {
 namespace {
@@ -39,18 +44,28 @@ __device__ __forceinline__ void topk_insert(float v, int e, float (&tv)[KM], int
   ti[0] = top ? e : ti[0];
 }
 
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1 (register rings need constant slots).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // Per-token routing over the logits tile in LDS, shared by both dtypes. One lane per token:
 // wave w takes tokens [w TB/4, (w+1) TB/4) of the block's TB. The lane walks the experts in index
-// order: maximum, sum of exp(l - m) (so lse = m + ln sum), then g_e = exp(l_e - lse) (written back
-// over the logit), s_e = g_e + b_e and the sorted top-KM insertion; k <= KM. Block partials: the
-// expert histogram (LDS integer atomics: order-free), sum of g per expert and sum of lse^2, the
-// latter two summed over tokens in token order.
-//   L: [TB][Ls] fp32; scratch: >= MOE_E_MAX ints + 64 floats.
+// order: maximum, sum of exp(l - m) (so lse = m + ln sum), then g_e = exp(l_e - lse) or, with
+// sigmoid scoring, g_e = 1 / (1 + exp(-l_e)) (written back over the logit), s_e = g_e + b_e and the
+// sorted top-KM insertion; k <= KM. Block partials: the expert histogram (LDS integer atomics:
+// order-free), sum over tokens of g_e (sigmoid: g_e / sum_e' g_e') per expert and sum of lse^2,
+// the latter two summed in token order.
+//   L: [TB][Ls] fp32; scratch: >= MOE_E_MAX ints + 64 floats. flags: kRouteRenorm | kRouteSigmoid.
 // ------------------------------------------------------------------------------------------
 template <int KM>
 __device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, int E, int k,
-                             int renorm, const float* __restrict__ b,
+                             int flags, const float* __restrict__ b,
                              int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
                              int32_t* __restrict__ hist, float* __restrict__ gpart,
                              float* __restrict__ lpart, int* hcnt, float* lsq) {
@@ -89,12 +104,25 @@ __device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, in
         tv[j] = -INFINITY;
         ti[j] = 0;
       }
+      const bool sig = (flags & kRouteSigmoid) != 0;
+      float ssum = 0.f;  // sigmoid: sum of the scores over the experts (the pad adds 0)
       for (int e = 0; e < E4; e += 4) {
         float4 v = *reinterpret_cast<const float4*>(row + e);
-        v.x = expf(v.x - lse);
-        v.y = expf(v.y - lse);
-        v.z = expf(v.z - lse);
-        v.w = expf(v.w - lse);
+        if (sig) {
+          v.x = 1.f / (1.f + expf(-v.x));
+          v.y = 1.f / (1.f + expf(-v.y));
+          v.z = 1.f / (1.f + expf(-v.z));
+          v.w = 1.f / (1.f + expf(-v.w));
+          ssum += v.x;
+          ssum += v.y;
+          ssum += v.z;
+          ssum += v.w;
+        } else {
+          v.x = expf(v.x - lse);
+          v.y = expf(v.y - lse);
+          v.z = expf(v.z - lse);
+          v.w = expf(v.w - lse);
+        }
         *reinterpret_cast<float4*>(row + e) = v;
         const float g4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -112,9 +140,13 @@ __device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, in
         if (j < k) {
           const float gj = row[ti[j]];
           topk_idx[t * k + j] = ti[j];
-          topk_w[t * k + j] = renorm ? gj / wsum : gj;
+          topk_w[t * k + j] = (flags & kRouteRenorm) ? gj / wsum : gj;
           atomicAdd(&hcnt[ti[j]], 1);
         }
+      }
+      if (sig) {  // the probability statistic uses the scores normalised over the experts
+        const float inv = 1.f / ssum;
+        for (int e = 0; e < E4; ++e) row[e] *= inv;
       }
     }
     lsq[tl] = lse2;
@@ -165,7 +197,7 @@ constexpr int kRouteThreads = 512;  // 8 waves: K is split 8 ways, two waves per
 template <int MB, int NEB, int NG>
 __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ b,
-    int64_t T, int d, int E, int k, int renorm, int32_t* __restrict__ topk_idx,
+    int64_t T, int d, int E, int k, int flags, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ hist, float* __restrict__ gpart,
     float* __restrict__ lpart) {
   constexpr int TB = 16 * MB;
@@ -220,16 +252,24 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
       for (int j = 0; j < NEBG; ++j)
         acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], bb[j], acc[m][j], 0, 0, 0);
   };
-  bf16x8 a0[MB], b0[NEBG], a1[MB], b1[NEBG];
-  int s = s0;
-  if (s < s1) load(s, a0, b0);
-  for (; s + 1 < s1; s += 2) {
-    load(s + 1, a1, b1);
-    mma(a0, b0);
-    if (s + 2 < s1) load(s + 2, a0, b0);
-    mma(a1, b1);
+  // a ring of PF k-steps of operands in registers: the loads run PF steps ahead of the MFMAs, so a
+  // wave's whole K range (16 steps at d = 4096) is in flight after two turns of the ring
+  constexpr int PF = 8;
+  bf16x8 ra[PF][MB], rb[PF][NEBG];
+  static_for<0, PF>([&](auto pc) __attribute__((always_inline)) {
+    constexpr int P = decltype(pc)::value;
+    if (s0 + P < s1) load(s0 + P, ra[P], rb[P]);
+  });
+  for (int base = s0; base < s1; base += PF) {
+    static_for<0, PF>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int J = decltype(jc)::value;
+      const int s = base + J;
+      if (s < s1) {
+        mma(ra[J], rb[J]);
+        if (s + PF < s1) load(s + PF, ra[J], rb[J]);
+      }
+    });
   }
-  if (s < s1) mma(a0, b0);
 
   // sum the partial tiles of each expert group in wave (K) order; groups own disjoint columns
   for (int w = 0; w < NW; ++w) {
@@ -256,7 +296,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
   }
   __syncthreads();
 #define MOE_CALL(KM) \
-  route_tokens<KM>(L, kLogitsStride, TB, t0, T, E, k, renorm, b, topk_idx, topk_w, hist, gpart, \
+  route_tokens<KM>(L, kLogitsStride, TB, t0, T, E, k, flags, b, topk_idx, topk_w, hist, gpart, \
                    lpart, hcnt, lsq)
   MOE_ROUTE_TOKENS_KM(MOE_CALL);
 #undef MOE_CALL
@@ -267,7 +307,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void route_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ W, const float* __restrict__ b,
-    int64_t T, int d, int E, int k, int renorm, int32_t* __restrict__ topk_idx,
+    int64_t T, int d, int E, int k, int flags, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ hist, float* __restrict__ gpart,
     float* __restrict__ lpart) {
   __shared__ float L[RT * kLogitsStride];
@@ -290,7 +330,7 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
   }
   __syncthreads();
 #define MOE_CALL(KM) \
-  route_tokens<KM>(L, kLogitsStride, RT, t0, T, E, k, renorm, b, topk_idx, topk_w, hist, gpart, \
+  route_tokens<KM>(L, kLogitsStride, RT, t0, T, E, k, flags, b, topk_idx, topk_w, hist, gpart, \
                    lpart, hcnt, lsq)
   MOE_ROUTE_TOKENS_KM(MOE_CALL);
 #undef MOE_CALL
@@ -309,7 +349,7 @@ constexpr int kSKP = kSK + 8;   // padded LDS row (bf16 elements)
 template <int NEB>
 __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ b,
-    int64_t T, int d, int E, int k, int renorm, int32_t* __restrict__ topk_idx,
+    int64_t T, int d, int E, int k, int flags, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ hist, float* __restrict__ gpart,
     float* __restrict__ lpart) {
   constexpr int TB = 64;
@@ -347,20 +387,23 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
     }
   }
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 rg[CPT];
-  auto gload = [&](int k0) __attribute__((always_inline)) {
+  // a ring of PF k-slices in registers ahead of the two LDS stages: a k-step's MFMA work is short
+  // next to the memory latency, so several slices must be in flight
+  constexpr int PF = 4;
+  u32x4 rg[PF][CPT];
+  auto gload = [&](u32x4 (&r)[CPT], int k0) __attribute__((always_inline)) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int col = ((i * kRouteThreads + tid) & 7) * 8;
-      rg[i] = (ok[i] && k0 + col < d) ? *reinterpret_cast<const u32x4*>(src[i] + k0) : zero;
+      r[i] = (ok[i] && k0 + col < d) ? *reinterpret_cast<const u32x4*>(src[i] + k0) : zero;
     }
   };
-  auto lstore = [&](int stage) __attribute__((always_inline)) {
+  auto lstore = [&](const u32x4 (&r)[CPT], int stage) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = i * kRouteThreads + tid;
-      if (c < CH) *reinterpret_cast<u32x4*>(st + stage * STAGE + (c >> 3) * kSKP + (c & 7) * 8) = rg[i];
+      if (c < CH) *reinterpret_cast<u32x4*>(st + stage * STAGE + (c >> 3) * kSKP + (c & 7) * 8) = r[i];
     }
   };
   f32x4 acc[NEBH];
@@ -384,17 +427,28 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
     }
   };
   const int nk = (d + kSK - 1) / kSK;
-  gload(0);
-  lstore(0);
-  if (nk > 1) gload(kSK);
+  // k-slice j sits in ring slot j % PF from its load until its LDS store one k-step before use
+  static_for<0, PF>([&](auto pc) __attribute__((always_inline)) {
+    constexpr int P = decltype(pc)::value;
+    if (P < nk) gload(rg[P], P * kSK);
+  });
+  lstore(rg[0], 0);
+  if (PF < nk) gload(rg[0], PF * kSK);
   __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    if (ks + 1 < nk) {
-      lstore((ks + 1) & 1);                  // stage read by k-step ks - 1, behind the barrier
-      if (ks + 2 < nk) gload((ks + 2) * kSK);
-    }
-    compute(ks & 1);
-    __syncthreads();
+  for (int base = 0; base < nk; base += PF) {
+    static_for<0, PF>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int J = decltype(jc)::value;
+      constexpr int NEXT = (J + 1) % PF;  // ring slot of k-slice ks + 1
+      const int ks = base + J;
+      if (ks < nk) {
+        if (ks + 1 < nk) {
+          lstore(rg[NEXT], (ks + 1) & 1);  // stage read by k-step ks - 1, behind the barrier
+          if (ks + 1 + PF < nk) gload(rg[NEXT], (ks + 1 + PF) * kSK);
+        }
+        compute(ks & 1);
+        __syncthreads();
+      }
+    });
   }
   float* L = reinterpret_cast<float*>(smem);  // reuses the stages
 #pragma unroll
@@ -412,7 +466,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
   }
   __syncthreads();
 #define MOE_CALL(KM) \
-  route_tokens<KM>(L, kLogitsStride, TB, t0, T, E, k, renorm, b, topk_idx, topk_w, hist, gpart, \
+  route_tokens<KM>(L, kLogitsStride, TB, t0, T, E, k, flags, b, topk_idx, topk_w, hist, gpart, \
                    lpart, hcnt, lsq)
   MOE_ROUTE_TOKENS_KM(MOE_CALL);
 #undef MOE_CALL
@@ -420,24 +474,24 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
 
 template <int NEB>
 hipError_t launch_bf16_lds(hipStream_t st, const void* x, const void* W, const float* b, int64_t T,
-                           int d, int E, int k, int renorm, int32_t* topk_idx, float* topk_w,
+                           int d, int E, int k, int flags, int32_t* topk_idx, float* topk_w,
                            int32_t* hist, float* gpart, float* lpart) {
   hipLaunchKernelGGL((route_bf16_lds_kernel<NEB>), dim3(static_cast<unsigned>(cdiv(T, 64))),
                      dim3(kRouteThreads), 0, st, static_cast<const bf16_t*>(x),
-                     static_cast<const bf16_t*>(W), b, T, d, E, k, renorm, topk_idx, topk_w, hist,
+                     static_cast<const bf16_t*>(W), b, T, d, E, k, flags, topk_idx, topk_w, hist,
                      gpart, lpart);
   return hipGetLastError();
 }
 
 template <int MB, int NEB, int NG>
 hipError_t launch_bf16(hipStream_t st, const void* x, const void* W, const float* b,
-                       int64_t T, int d, int E, int k, int renorm, int32_t* topk_idx,
+                       int64_t T, int d, int E, int k, int flags, int32_t* topk_idx,
                        float* topk_w, int32_t* hist, float* gpart, float* lpart) {
   const int64_t nblk = cdiv(T, 16 * MB);
   hipLaunchKernelGGL((route_bf16_kernel<MB, NEB, NG>), dim3(static_cast<unsigned>(nblk)),
                      dim3(kRouteThreads), 0, st,
                      static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W), b, T, d, E, k,
-                     renorm, topk_idx, topk_w, hist, gpart, lpart);
+                     flags, topk_idx, topk_w, hist, gpart, lpart);
   return hipGetLastError();
 }
 
@@ -445,25 +499,25 @@ hipError_t launch_bf16(hipStream_t st, const void* x, const void* W, const float
 
 int route_block_tokens(int dtype, int E) { return dtype == MOE_F32 ? RT : (E <= 16 ? 16 : 64); }
 
-hipError_t launch_route(int dtype, int64_t T, int d, int E, int k, int renorm, const void* x,
+hipError_t launch_route(int dtype, int64_t T, int d, int E, int k, int flags, const void* x,
                         const void* W_r, const float* b, int32_t* topk_idx, float* topk_w,
                         int32_t* hist, float* gpart, float* lpart, hipStream_t st) {
   if (dtype == MOE_F32) {
     const int64_t nblk = cdiv(T, RT);
     hipLaunchKernelGGL(route_f32_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
                        static_cast<const float*>(x), static_cast<const float*>(W_r), b, T, d, E,
-                       k, renorm, topk_idx, topk_w, hist, gpart, lpart);
+                       k, flags, topk_idx, topk_w, hist, gpart, lpart);
     return hipGetLastError();
   }
   const int neb = static_cast<int>(cdiv(E, 16));
 #define MOE_ROUTE_CASE(N)                                                                   \
   case N:                                                                                   \
-    return launch_bf16_lds<N>(st, x, W_r, b, T, d, E, k, renorm, topk_idx, topk_w, hist, gpart, \
+    return launch_bf16_lds<N>(st, x, W_r, b, T, d, E, k, flags, topk_idx, topk_w, hist, gpart, \
                               lpart);
   // up to 16 experts: 16-token blocks with the hidden dimension split over the waves (more blocks
   // in flight); more: 64-token blocks with W_r shared through LDS
   if (E <= 16)
-    return launch_bf16<1, 1, 1>(st, x, W_r, b, T, d, E, k, renorm, topk_idx, topk_w, hist, gpart,
+    return launch_bf16<1, 1, 1>(st, x, W_r, b, T, d, E, k, flags, topk_idx, topk_w, hist, gpart,
                                 lpart);
   switch (neb) {
     MOE_ROUTE_CASE(2) MOE_ROUTE_CASE(3) MOE_ROUTE_CASE(4) MOE_ROUTE_CASE(5) MOE_ROUTE_CASE(6)

@@ -58,6 +58,18 @@ def test_bad_renorm_and_dtype():
     assert moe.check_shape(s) == moe.MOE_OK  # fp32 rows need d % 4 == 0 only
 
 
+def test_scoring_flag():
+    assert moe.check_shape(moe.make_shape(64, 128, 8, 2, 256, scoring="sigmoid")) == moe.MOE_OK
+    s = moe.make_shape(64, 128, 8, 2, 256)
+    assert s.scoring == 0
+    s.scoring = 2
+    assert moe.check_shape(s) == moe.MOE_ERR_INVALID_ARGUMENT
+    s.scoring = -1
+    assert moe.check_shape(s) == moe.MOE_ERR_INVALID_ARGUMENT
+    with pytest.raises(ValueError):
+        moe.make_shape(64, 128, 8, 2, 256, scoring="tanh")
+
+
 def test_capacity_matches_oracle_rounding():
     rng = random.Random(5)
     cases = [(1.25, 2, 32768, 64), (1.0, 2, 10, 3), (0.05, 2, 40, 4), (0.03125, 2, 40, 4),

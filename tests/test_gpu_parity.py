@@ -55,6 +55,12 @@ ROUTE_CASES = [
     ("mixtral_8x7b", dict(T=100, d=128, E=8, k=8)),
     ("mixtral_8x7b", dict(T=129, d=200, E=20, k=3)),
     ("skewed_capacity", dict(T=400, d=256)),
+    # sigmoid scoring (with the bias of deepseek_v2 and sigmoid_v3; without it for mixtral)
+    ("tiny_fp32", dict(scoring="sigmoid")),
+    ("mixtral_8x7b", dict(T=300, d=512, scoring="sigmoid")),
+    ("deepseek_v2", dict(T=150, d=320, scoring="sigmoid")),
+    ("sigmoid_v3", dict(T=140, d=256)),
+    ("mixtral_8x7b", dict(T=70, d=128, E=256, k=16, scoring="sigmoid", renorm=False)),
 ]
 
 
@@ -65,9 +71,11 @@ def test_route(gpu, base, kw):
     x = workloads.make_x(cfg)
     Wr = workloads.make_router(cfg)
     b = workloads.make_bias(cfg)
-    r = moe.moe_route(x.to(gpu), Wr.to(gpu), cfg.k, None if b is None else b.to(gpu), cfg.renorm)
+    r = moe.moe_route(x.to(gpu), Wr.to(gpu), cfg.k, None if b is None else b.to(gpu), cfg.renorm,
+                      scoring=cfg.scoring)
     torch.cuda.synchronize()
-    orc = O.route(O._f64(x), O._f64(Wr), cfg.k, None if b is None else O._f64(b), cfg.renorm)
+    orc = O.route(O._f64(x), O._f64(Wr), cfg.k, None if b is None else O._f64(b), cfg.renorm,
+                  cfg.scoring)
     idx = r["topk_idx"].cpu().numpy().astype(np.int64)
     n_ex, n_diff = check_selection(idx, orc, cfg.k)
     say(f"    exempt={n_ex} differ={n_diff}")
@@ -76,7 +84,7 @@ def test_route(gpu, base, kw):
     assert max_rel_err(r["topk_w"], w_ref) < 1e-5
     # loads are the histogram of the GPU selection, bit-exact
     assert np.array_equal(r["n"].cpu().numpy(), O.expert_loads(idx, cfg.E))
-    assert rel(r["gsum"], orc["g"].sum(0)) < TOL_STATS
+    assert rel(r["gsum"], orc["probs"].sum(0)) < TOL_STATS
     assert rel(r["lse2sum"], [np.sum(orc["lse"] ** 2)]) < TOL_STATS
 
 
@@ -222,7 +230,8 @@ def run_layer(cfg, dev, inp=None):
     inp = inp or workloads.make_inputs(cfg)
     d = to_dev(inp, dev)
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-    layer = moe.MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.M, cfg.S, cfg.c, cfg.renorm, dt, dev)
+    layer = moe.MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.M, cfg.S, cfg.c, cfg.renorm, dt, dev,
+                         cfg.scoring)
     out = layer.forward(d.x, d.W_r, d.W_gate, d.W_up, d.W_down, d.b, d.shared_fused(), cfg.lam,
                         cfg.gamma)
     torch.cuda.synchronize()
@@ -232,7 +241,8 @@ def run_layer(cfg, dev, inp=None):
 def check_layer(cfg, inp, out, tokens=None):
     """Staged parity: selection (near ties exempt), then every later stage on the GPU's selection."""
     x64 = O._f64(inp.x)
-    orc_route = O.route(x64, O._f64(inp.W_r), cfg.k, None if inp.b is None else O._f64(inp.b), cfg.renorm)
+    orc_route = O.route(x64, O._f64(inp.W_r), cfg.k, None if inp.b is None else O._f64(inp.b),
+                        cfg.renorm, cfg.scoring)
     gidx = out["topk_idx"].cpu().numpy().astype(np.int64)
     n_ex, n_diff = check_selection(gidx, orc_route, cfg.k)
     cache = {}
@@ -246,7 +256,7 @@ def check_layer(cfg, inp, out, tokens=None):
     res = O.layer_forward(x64, O._f64(inp.W_r), None, None, None, cfg.k,
                           b=None if inp.b is None else O._f64(inp.b), shared=shared, c=cfg.c,
                           renorm=cfg.renorm, lam=cfg.lam, gamma=cfg.gamma, topk_idx=gidx,
-                          tokens=tokens, expert_weights=expert)
+                          tokens=tokens, expert_weights=expert, scoring=cfg.scoring)
     assert np.array_equal(out["counts"].cpu().numpy(), res["n"])
     assert np.array_equal(out["overflow"].cpu().numpy(), res["overflow"])
     assert max_rel_err(out["topk_w"], res["topk_w"]) < 1e-5
@@ -272,6 +282,9 @@ LAYER_CASES = [
     ("skewed_capacity", dict(T=2000, d=256, M=256)),
     ("mixtral_8x7b", dict(T=333, d=200, M=136, E=5, k=2)),   # K tail (200) and N tail (136)
     ("deepseekmoe_16b", dict(T=100, d=64, M=64, renorm=False)),
+    ("tiny_fp32", dict(scoring="sigmoid")),
+    ("deepseek_v2", dict(T=600, d=320, M=136, scoring="sigmoid")),
+    ("sigmoid_v3", dict(T=700, d=256, M=128)),
 ]
 
 
@@ -305,7 +318,8 @@ def test_layer_all_dropped_gives_shared_only(gpu):
 
 # ------------------------------------------------------------------------- full-size workloads
 
-FULL = ["tiny_fp32", "mixtral_8x7b", "deepseekmoe_16b", "deepseek_v2", "skewed_capacity"]
+FULL = ["tiny_fp32", "mixtral_8x7b", "deepseekmoe_16b", "deepseek_v2", "skewed_capacity",
+        "sigmoid_v3"]
 
 
 @pytest.mark.slow

@@ -427,6 +427,8 @@ def test_workload_shapes_match_pages():
     assert (c["deepseekmoe_16b"].E, c["deepseekmoe_16b"].k) == (gd["E"], gd["k"])
     gv = GOLDEN["deepseek_v2_routing"]
     assert (c["deepseek_v2"].E, c["deepseek_v2"].k) == (gv["E"], gv["k"])
+    g3 = GOLDEN["sigmoid_v3_routing"]
+    assert (c["sigmoid_v3"].E, c["sigmoid_v3"].scoring) == (g3["E"], g3["scoring"])
     assert all(cfg.lam == GOLDEN["aux_coefficient"]["lambda"] for cfg in c.values())
 
 

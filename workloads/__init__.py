@@ -62,6 +62,7 @@ class MoEConfig:
     renorm: bool = True         # renormalise the top-k gates
     zipf_s: Optional[float] = None  # Zipf exponent of the router-logit skew (None = none)
     seed: int = 0
+    scoring: str = "softmax"    # router scores: "softmax" or per-expert "sigmoid"
 
     def with_(self, **kw) -> "MoEConfig":
         return replace(self, **kw)
@@ -74,6 +75,10 @@ CONFIGS: Dict[str, MoEConfig] = {
     "deepseek_v2": MoEConfig("deepseek_v2", T=16384, d=5120, E=160, k=6, M=1536, S=2, bias=True),
     "skewed_capacity": MoEConfig("skewed_capacity", T=32768, d=4096, E=64, k=2, M=2048, c=1.25,
                                  zipf_s=1.2),
+    # the DeepSeek-V3 gate: 256 routed experts scored by a sigmoid, loss-free-balancing bias, one
+    # shared expert; hidden and expert widths as the DeepSeek-V2 layer above, 8 chosen per token
+    "sigmoid_v3": MoEConfig("sigmoid_v3", T=16384, d=5120, E=256, k=8, M=1536, S=1, bias=True,
+                            scoring="sigmoid"),
 }
 
 # the configuration the headline metric is quoted on
