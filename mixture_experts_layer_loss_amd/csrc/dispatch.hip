@@ -87,15 +87,19 @@ __global__ __launch_bounds__(1024) void scan_kernel(
   // load counts over this part's blocks
   const int b0 = static_cast<int>(static_cast<int64_t>(p) * nblk / P);
   const int b1 = static_cast<int>(static_cast<int64_t>(p + 1) * nblk / P);
+  // the loops over blocks are unrolled so that many independent loads are in flight at once
   int cnt = 0;
-  if (e < E)
+  if (e < E) {
+#pragma unroll 16
     for (int b = b0; b < b1; ++b) cnt += hist[static_cast<int64_t>(b) * E + e];
+  }
   psum[tid] = cnt;
   // sum of g over this part's (router) blocks
   double gs = 0.0;
   if (gpart != nullptr && e < E) {
     const int g0 = static_cast<int>(static_cast<int64_t>(p) * nblk_g / P);
     const int g1 = static_cast<int>(static_cast<int64_t>(p + 1) * nblk_g / P);
+#pragma unroll 16
     for (int b = g0; b < g1; ++b) gs += static_cast<double>(gpart[static_cast<int64_t>(b) * E + e]);
   }
   pg[tid] = gs;
@@ -104,6 +108,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(
     int base = 0;
     for (int q = 0; q < p; ++q) base += psum[q * EP + e];
     if (block_base != nullptr) {
+#pragma unroll 16
       for (int b = b0; b < b1; ++b) {
         block_base[static_cast<int64_t>(b) * E + e] = base;
         base += hist[static_cast<int64_t>(b) * E + e];

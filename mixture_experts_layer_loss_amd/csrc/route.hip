@@ -167,6 +167,157 @@ __device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, in
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Per-token routing of a 64-token block by all eight waves (many experts): lane l owns token l
+// and wave w a slice of the experts, so every lane works. Each wave forms its slice's partial
+// maximum and exp-sum (combined over the waves in wave order, so lse is the same in every wave and
+// reproducible), writes g back over its logits and keeps a sorted top-KM list of its slice. The
+// lists then merge pairwise in three rounds through LDS: the list of the lower expert range takes
+// the other's entries by strict-greater insertion, so equal scores still go to the lower expert
+// index and the merged order is the one a single walk over all experts gives. Wave 0 ends with
+// every token's list and writes the gates. Same outputs and partials as route_tokens.
+//   L: [64][Ls] fp32; part: [8][64] floats; xv/xi: [4][64][KM] exchange lists.
+// ------------------------------------------------------------------------------------------
+template <int KM>
+__device__ void route_tokens_split(float* L, int Ls, int64_t t0, int64_t T, int E, int k,
+                                   int flags, const float* __restrict__ b,
+                                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                   int32_t* __restrict__ hist, float* __restrict__ gpart,
+                                   float* __restrict__ lpart, int* hcnt, float* lsq, float* part,
+                                   float* xv, int* xi) {
+  constexpr int TB = 64, NW = 8;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tl = lane;
+  const int64_t t = t0 + tl;
+  const bool live = t < T;
+  const int E4 = (E + 3) & ~3;
+  const int SL = ((E4 / 4 + NW - 1) / NW) * 4;  // experts per wave, a multiple of 4
+  const int e0 = min(wave * SL, E4), e1 = min(e0 + SL, E4);
+  float* row = L + tl * Ls;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hcnt[e] = 0;
+  // maximum over the experts: slice partials, combined in wave order
+  float m = -INFINITY;
+  for (int e = e0; e < e1; e += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(row + e);
+    m = fmaxf(m, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+  }
+  part[wave * TB + tl] = m;
+  __syncthreads();
+  m = part[tl];
+  for (int w = 1; w < NW; ++w) m = fmaxf(m, part[w * TB + tl]);
+  float sum = 0.f;
+  for (int e = e0; e < e1; e += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(row + e);
+    sum += expf(v.x - m);
+    sum += expf(v.y - m);
+    sum += expf(v.z - m);
+    sum += expf(v.w - m);
+  }
+  __syncthreads();  // every wave has read the maxima
+  part[wave * TB + tl] = sum;
+  __syncthreads();
+  sum = 0.f;
+  for (int w = 0; w < NW; ++w) sum += part[w * TB + tl];
+  const float lse = m + logf(sum);
+  // scores of the slice, written back over the logits, and the slice's sorted top-KM
+  const bool sig = (flags & kRouteSigmoid) != 0;
+  float ssum = 0.f;
+  float tv[KM];
+  int ti[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    tv[j] = -INFINITY;
+    ti[j] = 0;
+  }
+  for (int e = e0; e < e1; e += 4) {
+    float4 v = *reinterpret_cast<const float4*>(row + e);
+    if (sig) {
+      v.x = 1.f / (1.f + expf(-v.x));
+      v.y = 1.f / (1.f + expf(-v.y));
+      v.z = 1.f / (1.f + expf(-v.z));
+      v.w = 1.f / (1.f + expf(-v.w));
+      ssum += v.x;
+      ssum += v.y;
+      ssum += v.z;
+      ssum += v.w;
+    } else {
+      v.x = expf(v.x - lse);
+      v.y = expf(v.y - lse);
+      v.z = expf(v.z - lse);
+      v.w = expf(v.w - lse);
+    }
+    *reinterpret_cast<float4*>(row + e) = v;
+    const float g4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ee = e + q;
+      if (ee < E) topk_insert<KM>(b != nullptr ? g4[q] + b[ee] : g4[q], ee, tv, ti);
+    }
+  }
+  // pairwise merges: round r, waves w with w % 2^(r+1) == 0 take the list of wave w + 2^r
+  for (int r = 0; r < 3; ++r) {
+    const int stride = 1 << r;
+    __syncthreads();  // the exchange buffer is free (and, first time, the partials were read)
+    const bool sender = (wave & (2 * stride - 1)) == stride;
+    const int slot = wave >> (r + 1);  // 0..3 at most
+    if (sender) {
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        xv[(slot * TB + tl) * KM + j] = tv[j];
+        xi[(slot * TB + tl) * KM + j] = ti[j];
+      }
+    }
+    __syncthreads();
+    if ((wave & (2 * stride - 1)) == 0) {
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        const float v = xv[(slot * TB + tl) * KM + j];
+        if (v > tv[KM - 1]) topk_insert<KM>(v, xi[(slot * TB + tl) * KM + j], tv, ti);
+      }
+    }
+  }
+  // the sigmoid probability statistic normalises by the sum over all experts
+  if (sig) part[wave * TB + tl] = ssum;
+  __syncthreads();
+  if (wave == 0 && live) {
+    float wsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < k) wsum += row[ti[j]];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (j < k) {
+        const float gj = row[ti[j]];
+        topk_idx[t * k + j] = ti[j];
+        topk_w[t * k + j] = (flags & kRouteRenorm) ? gj / wsum : gj;
+        atomicAdd(&hcnt[ti[j]], 1);
+      }
+    }
+  }
+  if (wave == 0) lsq[tl] = live ? lse * lse : 0.f;
+  if (sig) {
+    float tot = 0.f;
+    for (int w = 0; w < NW; ++w) tot += part[w * TB + tl];
+    __syncthreads();  // wave 0 has read the raw scores of every slice
+    const float inv = 1.f / tot;
+    for (int e = e0; e < e1; ++e) row[e] *= inv;
+  }
+  __syncthreads();
+  const int64_t blk = blockIdx.x;
+  const int nt = static_cast<int>(min<int64_t>(TB, T - t0));
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    float gs = 0.f;
+    for (int q = 0; q < nt; ++q) gs += L[q * Ls + e];
+    gpart[blk * E + e] = gs;
+    hist[blk * E + e] = hcnt[e];
+  }
+  if (threadIdx.x == 0) {
+    float ls = 0.f;
+    for (int q = 0; q < nt; ++q) ls += lsq[q];
+    lpart[blk] = ls;
+  }
+}
+
 // the top-k list length used for k (2, 8 or 16 slots)
 #define MOE_ROUTE_TOKENS_KM(CALL) \
   do {                            \
@@ -346,7 +497,9 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
 constexpr int kSK = 64;         // k per step
 constexpr int kSKP = kSK + 8;   // padded LDS row (bf16 elements)
 
-template <int NEB>
+// SPLIT: per-token routing by all waves (route_tokens_split) rather than one lane per token; its
+// exchange buffers are only allocated then, so that the other variant keeps two blocks per CU.
+template <int NEB, bool SPLIT>
 __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ b,
     int64_t T, int d, int E, int k, int flags, int32_t* __restrict__ topk_idx,
@@ -363,6 +516,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStagesBytes > kLBytes ? kStagesBytes : kLBytes];
   __shared__ int hcnt[MOE_E_MAX];
   __shared__ float lsq[TB];
+  __shared__ float part[SPLIT ? 8 * TB : 1];         // per-wave partials of the split routing
+  __shared__ float xv[SPLIT ? 4 * TB * 16 : 1];      // its exchange lists (KM <= 16)
+  __shared__ int xi[SPLIT ? 4 * TB * 16 : 1];
   bf16_t* st = reinterpret_cast<bf16_t*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tb = wave & 3, eh = wave >> 2;
@@ -465,9 +621,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
     if (e >= E) L[(i >> 2) * kLogitsStride + e] = -INFINITY;
   }
   __syncthreads();
-#define MOE_CALL(KM) \
-  route_tokens<KM>(L, kLogitsStride, TB, t0, T, E, k, flags, b, topk_idx, topk_w, hist, gpart, \
-                   lpart, hcnt, lsq)
+#define MOE_CALL(KM)                                                                           \
+  if constexpr (SPLIT)                                                                         \
+    route_tokens_split<KM>(L, kLogitsStride, t0, T, E, k, flags, b, topk_idx, topk_w, hist,     \
+                           gpart, lpart, hcnt, lsq, part, xv, xi);                             \
+  else                                                                                         \
+    route_tokens<KM>(L, kLogitsStride, TB, t0, T, E, k, flags, b, topk_idx, topk_w, hist, gpart, \
+                     lpart, hcnt, lsq)
   MOE_ROUTE_TOKENS_KM(MOE_CALL);
 #undef MOE_CALL
 }
@@ -476,10 +636,16 @@ template <int NEB>
 hipError_t launch_bf16_lds(hipStream_t st, const void* x, const void* W, const float* b, int64_t T,
                            int d, int E, int k, int flags, int32_t* topk_idx, float* topk_w,
                            int32_t* hist, float* gpart, float* lpart) {
-  hipLaunchKernelGGL((route_bf16_lds_kernel<NEB>), dim3(static_cast<unsigned>(cdiv(T, 64))),
-                     dim3(kRouteThreads), 0, st, static_cast<const bf16_t*>(x),
-                     static_cast<const bf16_t*>(W), b, T, d, E, k, flags, topk_idx, topk_w, hist,
-                     gpart, lpart);
+  // short lists over at most 128 experts stay one lane per token (cheaper than the merge rounds)
+  const dim3 grid(static_cast<unsigned>(cdiv(T, 64)));
+  if (NEB <= 8 && k <= 2)
+    hipLaunchKernelGGL((route_bf16_lds_kernel<NEB, false>), grid, dim3(kRouteThreads), 0, st,
+                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W), b, T, d, E,
+                       k, flags, topk_idx, topk_w, hist, gpart, lpart);
+  else
+    hipLaunchKernelGGL((route_bf16_lds_kernel<NEB, true>), grid, dim3(kRouteThreads), 0, st,
+                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W), b, T, d, E,
+                       k, flags, topk_idx, topk_w, hist, gpart, lpart);
   return hipGetLastError();
 }
 
