@@ -35,6 +35,10 @@ uses it):
   * Within an expert's segment, rows are in ascending token order (a stable sort by expert).
   * S shared experts take the same x as the router, are added with weight 1, and are summed.
   * Bias update: b_e <- b_e + gamma * sign(k T / E - n_e), sign(0) = 0, done in float32.
+  * Diagnostics: routing entropy is the token mean of H(p_t) = -sum_e p_te ln p_te (natural log,
+    0 ln 0 = 0) of the same per-token distribution P_e averages; the load Gini coefficient is
+    sum_ij |n_i - n_j| / (2 E sum_e n_e); max/mean load is max_e n_e / (sum_e n_e / E); the
+    importance CV^2 uses the population variance of Importance_e = sum_t p_te.
 
 Every function here is pinned by the CPU tests against closed forms, invariants, brute force or an
 independent formula from the pages.
@@ -260,6 +264,48 @@ def balance_stats(n: np.ndarray, g: np.ndarray, lse: np.ndarray, k: int, lam: fl
     return {"f": f, "P": P, "aux": aux, "z": z}
 
 
+def routing_entropy(probs: np.ndarray) -> float:
+    """Mean over tokens of H(g(x)) = -sum_e g_e ln g_e ([ATLAS] §9 专业化是否真的发生: the routing
+    entropy describes how concentrated the choice is), with 0 ln 0 = 0."""
+    p = _f64(probs)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        terms = np.where(p > 0.0, p * np.log(p), 0.0)
+    return float(-terms.sum(axis=1).mean())
+
+
+def load_gini(n: np.ndarray) -> float:
+    """Gini coefficient of the expert loads ([ATLAS] §10 MoE 评估的标准化: the load distribution
+    by its Gini coefficient or the max/mean ratio): sum_i sum_j |n_i - n_j| / (2 E sum_e n_e)."""
+    x = _f64(n)
+    E = x.shape[0]
+    tot = x.sum()
+    if tot == 0.0:
+        return 0.0
+    return float(np.abs(x[:, None] - x[None, :]).sum() / (2.0 * E * tot))
+
+
+def load_max_over_mean(n: np.ndarray) -> float:
+    """max_e n_e / mean_e n_e ([ATLAS] §10; the critical path waits for the busiest expert, §8)."""
+    x = _f64(n)
+    mean = x.sum() / x.shape[0]
+    return float(x.max() / mean) if mean > 0.0 else 0.0
+
+
+def importance_cv2(importance: np.ndarray) -> float:
+    """CV(Importance)^2 = Var / Mean^2 of Importance_e = sum_t G_e(x_t) ([CSDN] 平衡专家利用率:
+    the importance loss is w_importance times this square), population variance."""
+    x = _f64(importance)
+    mean = x.mean()
+    return float(((x - mean) ** 2).mean() / (mean * mean)) if mean != 0.0 else 0.0
+
+
+def diagnostics(n: np.ndarray, probs: np.ndarray) -> dict:
+    """Routing entropy, load Gini, max/mean load and importance CV^2 of one batch."""
+    p = _f64(probs)
+    return {"entropy": routing_entropy(p), "gini": load_gini(n),
+            "max_over_mean": load_max_over_mean(n), "importance_cv2": importance_cv2(p.sum(axis=0))}
+
+
 def bias_update(b: np.ndarray, n: np.ndarray, k: int, T: int, gamma: float) -> np.ndarray:
     """b_e <- b_e + gamma * sign(k T / E - n_e) in float32: an overloaded expert's bias goes down,
     an underloaded one's goes up ([ATLAS] §无辅助损失负载均衡（ALF-LB）), sign(0) = 0."""
@@ -336,6 +382,7 @@ def layer_forward(x, W_r, W_gate, W_up, W_down, k: int, b=None, shared=(), c=Non
             if rr >= 0:
                 y[i] += w[t, j] * out_perm[rr]
     res = {"y": y, "tokens": want, "topk_idx": S, "topk_w": w, "n": n, "C": C, **dsp, **stats,
+           "diag": diagnostics(n, r["probs"]),
            "lse": r["lse"], "g": r["g"], "margin": r["margin"], "s": r["s"]}
     if b is not None:
         res["b_new"] = bias_update(b, n, k, T, gamma)

@@ -243,6 +243,36 @@ def test_stats_pins():
     check_stats()
 
 
+# ---------------------------------------------------------------------------------- diagnostics
+
+def check_diagnostics(mod=O):
+    E = 8
+    # entropy: uniform probabilities give ln E, one-hot rows give 0; scipy's entropy (natural log)
+    assert math.isclose(mod.routing_entropy(np.full((5, E), 1.0 / E)), math.log(E), rel_tol=1e-14)
+    assert mod.routing_entropy(np.eye(E)) == 0.0
+    from scipy.stats import entropy
+    g, _ = mod.softmax_lse(_rand((50, E), 21, 2.0))
+    assert math.isclose(mod.routing_entropy(g), float(np.mean([entropy(r) for r in g])), rel_tol=1e-13)
+    # Gini: equal loads 0; one expert with everything (E-1)/E; the sorted closed form
+    # G = 2 sum_i i x_(i) / (E sum x) - (E + 1) / E  (x ascending, i = 1..E)
+    assert mod.load_gini(np.full(E, 7)) == 0.0
+    assert math.isclose(mod.load_gini(np.array([0] * (E - 1) + [40])), (E - 1) / E, rel_tol=1e-14)
+    x = np.array([3, 9, 0, 14, 5, 5, 1, 27])
+    xs = np.sort(x)
+    ref = 2.0 * sum((i + 1) * v for i, v in enumerate(xs)) / (E * xs.sum()) - (E + 1) / E
+    assert math.isclose(mod.load_gini(x), ref, rel_tol=1e-13)
+    # max/mean load
+    assert math.isclose(mod.load_max_over_mean(x), 27 / (x.sum() / E), rel_tol=1e-14)
+    assert mod.load_max_over_mean(np.full(E, 3)) == 1.0
+    # importance CV^2: equal importance 0; two experts (a, b) give ((a - b) / (a + b))^2
+    assert mod.importance_cv2(np.full(E, 2.5)) == 0.0
+    assert math.isclose(mod.importance_cv2(np.array([3.0, 1.0])), 0.25, rel_tol=1e-14)
+
+
+def test_diagnostics_pins():
+    check_diagnostics()
+
+
 # ----------------------------------------------------------------------------- capacity/dispatch
 
 def test_capacity_closed_forms():
@@ -507,6 +537,17 @@ def _gate_from_biased(g, S, renorm=True):
     return O.gate_weights(g + 0.01, S, renorm)
 
 
+def _gini_half(n):
+    x = O._f64(n)
+    return float(np.abs(x[:, None] - x[None, :]).sum() / (4.0 * x.shape[0] * x.sum()))
+
+
+def _entropy_log2(probs):
+    p = O._f64(probs)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return float(-np.where(p > 0, p * np.log2(p), 0.0).sum(axis=1).mean())
+
+
 def _sigmoid_wrong_sign(l):
     l = O._f64(l)
     return 1.0 / (1.0 + np.exp(l))
@@ -527,6 +568,8 @@ def _sigmoid_unnormalised_P(g, scoring="softmax"):
     (dict(gate_weights=_gate_from_biased), [check_gates]),
     (dict(sigmoid_scores=_sigmoid_wrong_sign), [check_sigmoid]),
     (dict(score_distribution=_sigmoid_unnormalised_P), [check_sigmoid_stats]),
+    (dict(load_gini=_gini_half), [check_diagnostics]),
+    (dict(routing_entropy=_entropy_log2), [check_diagnostics]),
 ])
 def test_planted_mistakes_are_caught(mutant, checks):
     m = _Mutant(**mutant)
