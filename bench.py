@@ -170,6 +170,9 @@ def main():
     stage_ms /= args.steps
 
     counts = out["counts"].cpu().numpy().astype(np.int64)
+    dg = out["diag"].cpu().numpy().astype(float)
+    diag = {"entropy": round(dg[0], 5), "load_gini": round(dg[1], 5),
+            "max_over_mean_load": round(dg[2], 4), "importance_cv2": round(dg[3], 6)}
     overflow = out["overflow"].cpu().numpy().astype(np.int64)
     kept = int((counts - overflow).sum())
     T, d, E, k, M, S = cfg.T, cfg.d, cfg.E, cfg.k, cfg.M, cfg.S
@@ -215,7 +218,8 @@ def main():
         "config": {"workload": name, "T": T, "d": d, "E": E, "k": k, "M": M, "S": S,
                    "capacity_factor": cfg.c, "bias": cfg.bias, "scoring": cfg.scoring,
                    "kept_assignments": kept,
-                   "dropped_assignments": int(overflow.sum()), "max_load": int(counts.max())},
+                   "dropped_assignments": int(overflow.sum()), "max_load": int(counts.max()),
+                   "routing_diagnostics": diag},
         "mfma_peak_frac_layer": round(layer_tf / peak, 4), "layer_tflops": round(layer_tf, 1),
         "roofline": roofline, "stages": stages, "cpu_baseline": cpu,
     }

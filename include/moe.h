@@ -114,11 +114,13 @@ size_t moe_workspace_size(const moe_shape* s, int call);
  *   n        device out [E] int32: loads n_e = #{t : e in S_t}, before any capacity limit
  *   gsum     device out [E] double: sum_t p_te, p = g (softmax) or g_te / sum_e' g_te' (sigmoid)
  *   lse2sum  device out [1] double: sum_t lse_t^2 (raw logits, either scoring)
+ *   hsum     device out [1] double or NULL: sum_t H(p_t), H(p) = -sum_e p_e ln p_e, the routing
+ *            entropy of "MoE：条件计算与路由" §9
  *   ws       device workspace of moe_workspace_size(s, MOE_CALL_ROUTE) bytes
  */
 moe_status moe_route(const moe_shape* s, const void* x, const void* W_r, const float* b,
                      int32_t* topk_idx, float* topk_w, int32_t* n, double* gsum, double* lse2sum,
-                     void* ws, size_t ws_bytes, void* stream);
+                     double* hsum, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_dispatch -- capacity and expert-contiguous placement ("MoE：条件计算与路由" §3; the
@@ -183,13 +185,20 @@ moe_status moe_combine(const moe_shape* s, const void* out_perm, const int32_t* 
  *   b_new_e = b_e + gamma * sign(k T / E - n_e) in fp32, sign(0) = 0 ("MoE：条件计算与路由"
  *   §无辅助损失负载均衡（ALF-LB）: overloaded experts' bias goes down, underloaded up)
  * f_e uses k T so that sum_e f_e = 1 for any k (the argmax fraction when k = 1).
- *   n [E] int32, gsum [E] double, lse2sum [1] double: device, as written by moe_route
+ * Routing diagnostics (diag, nullable; "MoE：条件计算与路由" §9-§10; importance CV^2 of the
+ * adg.csdn.net notes page): diag[0] = hsum / T (mean routing entropy, natural log),
+ *   diag[1] = sum_ij |n_i - n_j| / (2 E sum_e n_e) (load Gini coefficient),
+ *   diag[2] = max_e n_e / mean_e n_e, diag[3] = Var_e(gsum) / Mean_e(gsum)^2 (population).
+ *   n [E] int32, gsum [E] double, lse2sum [1] double, hsum [1] double: device, as written by
+ *   moe_route (hsum may be NULL when diag is NULL)
  *   f, P device out [E] fp32 (nullable)    aux, z device out [1] fp32 (nullable)
+ *   diag device out [4] fp32 (nullable)
  *   b device [E] fp32 and b_new device out [E] fp32: both NULL, or both set (may alias)
  */
 moe_status moe_balance_stats(const moe_shape* s, const int32_t* n, const double* gsum,
-                             const double* lse2sum, float lambda, float* f, float* P, float* aux,
-                             float* z, const float* b, float* b_new, float gamma, void* stream);
+                             const double* lse2sum, const double* hsum, float lambda, float* f,
+                             float* P, float* aux, float* z, float* diag, const float* b,
+                             float* b_new, float gamma, void* stream);
 
 /*
  * moe_layer_forward -- the whole layer: route, dispatch, grouped experts, shared experts,
@@ -200,22 +209,23 @@ moe_status moe_balance_stats(const moe_shape* s, const int32_t* n, const double*
  *   of width S*M (NULL when S == 0)
  *   y device out [T, d]
  * Optional device outputs (NULL = not returned): topk_idx [T, k] int32, topk_w [T, k] fp32,
- * counts [E] int32 (n_e), overflow [E] int32, f [E], P [E], aux [1], z [1] fp32, and
- * b_new [E] fp32 = the updated bias (requires b; may alias b: it is written after selection).
+ * counts [E] int32 (n_e), overflow [E] int32, f [E], P [E], aux [1], z [1] fp32, diag [4] fp32
+ * (routing diagnostics as in moe_balance_stats), and b_new [E] fp32 = the updated bias
+ * (requires b; may alias b: it is written after selection).
  *   ws device workspace of moe_workspace_size(s, MOE_CALL_LAYER) bytes
  */
 moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r, const float* b,
                              const void* W_gate, const void* W_up, const void* W_down,
                              const void* Ws_gate, const void* Ws_up, const void* Ws_down, void* y,
                              int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* overflow,
-                             float* f, float* P, float* aux, float* z, float* b_new, float lambda,
-                             float gamma, void* ws, size_t ws_bytes, void* stream);
+                             float* f, float* P, float* aux, float* z, float* diag, float* b_new,
+                             float lambda, float gamma, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_set_stage_events -- profiling aid for moe_layer_forward (not a step of the method).
  * When `events` is non-NULL, later moe_layer_forward calls record events[i] (hipEvent_t handles
  * owned by the caller, count >= MOE_STAGE_COUNT) on their stream at the end of each stage:
- *   0 start, 1 route, 2 scan + placement + row copies, 3 routed gate/up GEMM (SwiGLU),
+ *   0 start, 1 route, 2 scan + placement, 3 routed gate/up GEMM (SwiGLU, rows gathered from x),
  *   4 routed down GEMM, 5 shared experts (both GEMMs), 6 combine, 7 statistics.
  * NULL turns recording off. Process-wide setting; not thread-safe.
  */

@@ -47,7 +47,7 @@ _SIG = {
     "moe_check_shape": (ctypes.c_int, [ctypes.POINTER(Shape)]),
     "moe_capacity": (ctypes.c_int64, [ctypes.POINTER(Shape)]),
     "moe_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int]),
-    "moe_route": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+    "moe_route": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                  ctypes.c_size_t, _P]),
     "moe_dispatch": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     ctypes.c_size_t, _P]),
@@ -55,11 +55,11 @@ _SIG = {
                                       _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                       _P]),
     "moe_combine": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P]),
-    "moe_balance_stats": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, ctypes.c_float, _P, _P,
-                                         _P, _P, _P, _P, ctypes.c_float, _P]),
+    "moe_balance_stats": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, ctypes.c_float, _P,
+                                         _P, _P, _P, _P, _P, _P, ctypes.c_float, _P]),
     "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                         _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
-                                         ctypes.c_float, _P, ctypes.c_size_t, _P]),
+                                         _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                         ctypes.c_float, ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "moe_set_stage_events": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]),
 }
 
@@ -174,12 +174,14 @@ def moe_route(x: torch.Tensor, W_r: torch.Tensor, k: int, b: Optional[torch.Tens
            "topk_w": torch.empty(T, k, dtype=torch.float32, device=dev),
            "n": torch.empty(E, dtype=torch.int32, device=dev),
            "gsum": torch.empty(E, dtype=torch.float64, device=dev),
-           "lse2sum": torch.empty(1, dtype=torch.float64, device=dev)}
+           "lse2sum": torch.empty(1, dtype=torch.float64, device=dev),
+           "hsum": torch.empty(1, dtype=torch.float64, device=dev)}
     if ws is None:
         ws = workspace(s, CALL_ROUTE, dev)
     _check(lib().moe_route(ctypes.byref(s), _ptr(x), _ptr(W_r), _ptr(b), _ptr(out["topk_idx"]),
                            _ptr(out["topk_w"]), _ptr(out["n"]), _ptr(out["gsum"]),
-                           _ptr(out["lse2sum"]), _ptr(ws), ws.numel(), _stream()), "moe_route")
+                           _ptr(out["lse2sum"]), _ptr(out["hsum"]), _ptr(ws), ws.numel(),
+                           _stream()), "moe_route")
     return out
 
 
@@ -248,23 +250,29 @@ def moe_combine(out_perm: torch.Tensor, inv_perm: torch.Tensor, topk_w: torch.Te
 
 def moe_balance_stats(T: int, k: int, n: torch.Tensor, gsum: torch.Tensor, lse2sum: torch.Tensor,
                       lam: float = 0.01, b: Optional[torch.Tensor] = None,
-                      gamma: float = 1e-3) -> dict:
+                      gamma: float = 1e-3, hsum: Optional[torch.Tensor] = None) -> dict:
+    """Balance statistics; with ``hsum`` (from moe_route) also the routing diagnostics ``diag``:
+    [mean routing entropy, load Gini, max/mean load, importance CV^2]."""
     E = n.shape[0]
     _dev(n, "n", torch.int32, (E,))
     _dev(gsum, "gsum", torch.float64, (E,))
     _dev(lse2sum, "lse2sum", torch.float64, (1,))
+    if hsum is not None:
+        _dev(hsum, "hsum", torch.float64, (1,))
     dev = n.device
     s = make_shape(T, 8, E, k, 8, dtype=torch.float32)
     out = {"f": torch.empty(E, dtype=torch.float32, device=dev),
            "P": torch.empty(E, dtype=torch.float32, device=dev),
            "aux": torch.empty(1, dtype=torch.float32, device=dev),
            "z": torch.empty(1, dtype=torch.float32, device=dev),
+           "diag": None if hsum is None else torch.empty(4, dtype=torch.float32, device=dev),
            "b_new": None if b is None else torch.empty(E, dtype=torch.float32, device=dev)}
     if b is not None:
         _dev(b, "b", torch.float32, (E,))
-    _check(lib().moe_balance_stats(ctypes.byref(s), _ptr(n), _ptr(gsum), _ptr(lse2sum), float(lam),
-                                   _ptr(out["f"]), _ptr(out["P"]), _ptr(out["aux"]), _ptr(out["z"]),
-                                   _ptr(b), _ptr(out["b_new"]), float(gamma), _stream()),
+    _check(lib().moe_balance_stats(ctypes.byref(s), _ptr(n), _ptr(gsum), _ptr(lse2sum), _ptr(hsum),
+                                   float(lam), _ptr(out["f"]), _ptr(out["P"]), _ptr(out["aux"]),
+                                   _ptr(out["z"]), _ptr(out["diag"]), _ptr(b), _ptr(out["b_new"]),
+                                   float(gamma), _stream()),
            "moe_balance_stats")
     return out
 
@@ -293,6 +301,7 @@ class MoELayer:
                 "P": torch.empty(E, dtype=torch.float32, device=dev),
                 "aux": torch.empty(1, dtype=torch.float32, device=dev),
                 "z": torch.empty(1, dtype=torch.float32, device=dev),
+                "diag": torch.empty(4, dtype=torch.float32, device=dev),
                 "b_new": torch.empty(E, dtype=torch.float32, device=dev) if with_bias else None}
 
     def forward(self, x, W_r, W_gate, W_up, W_down, b=None, shared=None, lam: float = 0.01,
@@ -321,7 +330,8 @@ class MoELayer:
             _ptr(W_down), _ptr(sg), _ptr(su), _ptr(sd), _ptr(out["y"]), _ptr(out.get("topk_idx")),
             _ptr(out.get("topk_w")), _ptr(out.get("counts")), _ptr(out.get("overflow")),
             _ptr(out.get("f")), _ptr(out.get("P")), _ptr(out.get("aux")), _ptr(out.get("z")),
-            _ptr(out.get("b_new") if b is not None else None), float(lam), float(gamma),
+            _ptr(out.get("diag")), _ptr(out.get("b_new") if b is not None else None), float(lam),
+            float(gamma),
             _ptr(self.ws), self.ws.numel(), _stream()), "moe_layer_forward")
         return out
 

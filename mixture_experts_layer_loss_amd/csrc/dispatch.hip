@@ -73,8 +73,9 @@ __device__ int block_scan_256(int v, int* buf) {
 __global__ __launch_bounds__(1024) void scan_kernel(
     int64_t T, int E, int64_t C, int nblk, const int32_t* __restrict__ hist,
     const float* __restrict__ gpart, int nblk_g, const float* __restrict__ lpart,
-    int32_t* __restrict__ block_base, int32_t* __restrict__ n_out, double* __restrict__ gsum,
-    double* __restrict__ lse2sum, int32_t* __restrict__ kept_out, int32_t* __restrict__ overflow,
+    const float* __restrict__ hpart, int32_t* __restrict__ block_base,
+    int32_t* __restrict__ n_out, double* __restrict__ gsum, double* __restrict__ lse2sum,
+    double* __restrict__ hsum, int32_t* __restrict__ kept_out, int32_t* __restrict__ overflow,
     int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off, int BM) {
   __shared__ int psum[1024];
   __shared__ double pg[1024];
@@ -167,17 +168,21 @@ __global__ __launch_bounds__(1024) void scan_kernel(
       tile_off[3 * E + 2] = i2;
     }
   }
-  if (lse2sum != nullptr) {
+  // block sums of lse^2 and of the routing entropy: strided partials, then a fixed tree
+  auto tree = [&](const float* part, double* out) {
     double ls = 0.0;
-    for (int b = tid; b < nblk_g; b += 1024) ls += static_cast<double>(lpart[b]);
+    for (int b = tid; b < nblk_g; b += 1024) ls += static_cast<double>(part[b]);
     pg[tid] = ls;
     __syncthreads();
     for (int off = 512; off >= 1; off >>= 1) {
       if (tid < off) pg[tid] += pg[tid + off];
       __syncthreads();
     }
-    if (tid == 0) *lse2sum = pg[0];
-  }
+    if (tid == 0) *out = pg[0];
+    __syncthreads();
+  };
+  if (lse2sum != nullptr) tree(lpart, lse2sum);
+  if (hsum != nullptr) tree(hpart, hsum);
 }
 
 // Ranks and rows of one block of 64 tokens: inv_perm [T,k] and perm_token [rows].
@@ -299,11 +304,13 @@ hipError_t launch_count(int64_t T, int E, int k, const int32_t* topk_idx, int32_
 }
 
 hipError_t launch_scan(int64_t T, int E, int64_t C, int nblk, const int32_t* hist,
-                       const float* gpart, const float* lpart, int32_t* block_base, int32_t* n_out,
-                       double* gsum, double* lse2sum, int32_t* kept, int32_t* overflow,
-                       int32_t* offsets, int32_t* tile_off, int BM, hipStream_t st) {
+                       const float* gpart, const float* lpart, const float* hpart,
+                       int32_t* block_base, int32_t* n_out, double* gsum, double* lse2sum,
+                       double* hsum, int32_t* kept, int32_t* overflow, int32_t* offsets,
+                       int32_t* tile_off, int BM, hipStream_t st) {
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, T, E, C, nblk, hist, gpart, nblk,
-                     lpart, block_base, n_out, gsum, lse2sum, kept, overflow, offsets, tile_off, BM);
+                     lpart, hpart, block_base, n_out, gsum, lse2sum, hsum, kept, overflow, offsets,
+                     tile_off, BM);
   return hipGetLastError();
 }
 

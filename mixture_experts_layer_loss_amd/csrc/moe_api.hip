@@ -91,6 +91,7 @@ struct RoutePlan {
   int32_t* hist;
   float* gpart;
   float* lpart;
+  float* hpart;
 };
 RoutePlan plan_route(Carve& c, const moe_shape* s) {
   const size_t nb = static_cast<size_t>(route_blocks(s));
@@ -98,6 +99,7 @@ RoutePlan plan_route(Carve& c, const moe_shape* s) {
   p.hist = c.take<int32_t>(nb * s->E);
   p.gpart = c.take<float>(nb * s->E);
   p.lpart = c.take<float>(nb);
+  p.hpart = c.take<float>(nb);
   return p;
 }
 
@@ -118,7 +120,7 @@ struct LayerPlan {
   int32_t *block_base, *topk_idx, *n, *kept, *overflow, *offsets, *tile_off, *perm_token,
       *inv_perm, *sh_offsets, *sh_tile_off;
   float* topk_w;
-  double *gsum, *lse2sum;
+  double *gsum, *lse2sum, *hsum;
   void *h, *out_perm, *h_sh, *sh;
 };
 LayerPlan plan_layer(Carve& c, const moe_shape* s) {
@@ -133,6 +135,7 @@ LayerPlan plan_layer(Carve& c, const moe_shape* s) {
   p.n = c.take<int32_t>(s->E);
   p.gsum = c.take<double>(s->E);
   p.lse2sum = c.take<double>(1);
+  p.hsum = c.take<double>(1);
   p.kept = c.take<int32_t>(s->E);
   p.overflow = c.take<int32_t>(s->E);
   p.offsets = c.take<int32_t>(s->E + 1);
@@ -215,7 +218,7 @@ size_t moe_workspace_size(const moe_shape* s, int call) {
 
 moe_status moe_route(const moe_shape* s, const void* x, const void* W_r, const float* b,
                      int32_t* topk_idx, float* topk_w, int32_t* n, double* gsum, double* lse2sum,
-                     void* ws, size_t ws_bytes, void* stream) {
+                     double* hsum, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = moe_check_shape(s);
   if (st != MOE_OK) return st;
   if (!x || !W_r || !topk_idx || !topk_w || !n || !gsum || !lse2sum)
@@ -227,10 +230,11 @@ moe_status moe_route(const moe_shape* s, const void* x, const void* W_r, const f
   Carve c(ws);
   RoutePlan p = plan_route(c, s);
   hipError_t e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s), x, W_r, b, topk_idx,
-                              topk_w, p.hist, p.gpart, p.lpart, hs);
+                              topk_w, p.hist, p.gpart, p.lpart, p.hpart, hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = launch_scan(s->T, s->E, -1, static_cast<int>(route_blocks(s)), p.hist, p.gpart, p.lpart, nullptr,
-                  n, gsum, lse2sum, nullptr, nullptr, nullptr, nullptr, gemm_bm(s), hs);
+  e = launch_scan(s->T, s->E, -1, static_cast<int>(route_blocks(s)), p.hist, p.gpart, p.lpart,
+                  p.hpart, nullptr, n, gsum, lse2sum, hsum, nullptr, nullptr, nullptr, nullptr,
+                  gemm_bm(s), hs);
   return hip_status(e);
 }
 
@@ -250,9 +254,9 @@ moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_i
   const int64_t C = capacity_of(s);
   hipError_t e = launch_count(s->T, s->E, s->k, topk_idx, p.hist, hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = launch_scan(s->T, s->E, C, static_cast<int>(nblocks(s)), p.hist, nullptr, nullptr,
-                  p.block_base, counts, nullptr, nullptr, nullptr, overflow, offsets, nullptr,
-                  gemm_bm(s), hs);
+  e = launch_scan(s->T, s->E, C, static_cast<int>(nblocks(s)), p.hist, nullptr, nullptr, nullptr,
+                  p.block_base, counts, nullptr, nullptr, nullptr, nullptr, overflow, offsets,
+                  nullptr, gemm_bm(s), hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = launch_scatter(s->T, s->d, s->E, s->k, C, elem_bytes(s), x, topk_idx, kRouteTokens,
                      p.block_base, offsets, x_perm, perm_token, inv_perm, hs);
@@ -301,23 +305,25 @@ moe_status moe_combine(const moe_shape* s, const void* out_perm, const int32_t* 
 }
 
 moe_status moe_balance_stats(const moe_shape* s, const int32_t* n, const double* gsum,
-                             const double* lse2sum, float lambda, float* f, float* P, float* aux,
-                             float* z, const float* b, float* b_new, float gamma, void* stream) {
+                             const double* lse2sum, const double* hsum, float lambda, float* f,
+                             float* P, float* aux, float* z, float* diag, const float* b,
+                             float* b_new, float gamma, void* stream) {
   moe_status st = moe_check_shape(s);
   if (st != MOE_OK) return st;
   if (!n || !gsum || !lse2sum) return MOE_ERR_INVALID_ARGUMENT;
+  if (diag != nullptr && hsum == nullptr) return MOE_ERR_INVALID_ARGUMENT;
   if ((b == nullptr) != (b_new == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
   if (isnan(lambda) || isnan(gamma)) return MOE_ERR_INVALID_ARGUMENT;
-  return hip_status(launch_stats(s->T, s->E, s->k, n, gsum, lse2sum, lambda, f, P, aux, z, b,
-                                 b_new, gamma, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_stats(s->T, s->E, s->k, n, gsum, lse2sum, hsum, lambda, f, P, aux, z,
+                                 diag, b, b_new, gamma, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r, const float* b,
                              const void* W_gate, const void* W_up, const void* W_down,
                              const void* Ws_gate, const void* Ws_up, const void* Ws_down, void* y,
                              int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* overflow,
-                             float* f, float* P, float* aux, float* z, float* b_new, float lambda,
-                             float gamma, void* ws, size_t ws_bytes, void* stream) {
+                             float* f, float* P, float* aux, float* z, float* diag, float* b_new,
+                             float lambda, float gamma, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = moe_check_shape(s);
   if (st != MOE_OK) return st;
   if (!x || !W_r || !W_gate || !W_up || !W_down || !y) return MOE_ERR_INVALID_ARGUMENT;
@@ -347,11 +353,11 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
 
   mark_stage(0, hs);
   hipError_t e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s), x, W_r, b, idx, w,
-                              p.r.hist, p.r.gpart, p.r.lpart, hs);
+                              p.r.hist, p.r.gpart, p.r.lpart, p.r.hpart, hs);
   mark_stage(1, hs);
   if (e == hipSuccess)
-    e = launch_scan(s->T, s->E, C, nblk, p.r.hist, p.r.gpart, p.r.lpart, p.block_base, n, p.gsum,
-                    p.lse2sum, p.kept, ovf, p.offsets, p.tile_off, BM, hs);
+    e = launch_scan(s->T, s->E, C, nblk, p.r.hist, p.r.gpart, p.r.lpart, p.r.hpart, p.block_base,
+                    n, p.gsum, p.lse2sum, p.hsum, p.kept, ovf, p.offsets, p.tile_off, BM, hs);
   // placement only: the gate/up GEMM gathers its rows from x through perm_token
   if (e == hipSuccess)
     e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx, route_block_tokens(s->dtype, s->E),
@@ -381,8 +387,8 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
     e = launch_combine(s->dtype, s->T, s->d, s->k, p.out_perm, p.inv_perm, w,
                        s->S > 0 ? p.sh : nullptr, y, hs);
   mark_stage(6, hs);
-  if (e == hipSuccess && (f || P || aux || z || b_new))
-    e = launch_stats(s->T, s->E, s->k, n, p.gsum, p.lse2sum, lambda, f, P, aux, z,
+  if (e == hipSuccess && (f || P || aux || z || diag || b_new))
+    e = launch_stats(s->T, s->E, s->k, n, p.gsum, p.lse2sum, p.hsum, lambda, f, P, aux, z, diag,
                      b_new ? b : nullptr, b_new, gamma, hs);
   mark_stage(7, hs);
   return hip_status(e);

@@ -52,11 +52,11 @@ int route_block_tokens(int dtype, int E);
 constexpr int kRouteRenorm = 1, kRouteSigmoid = 2;
 
 // Router: logits, softmax/LSE, biased top-k, gates, per-block partial statistics and histograms.
-//   hist  [nblk, E] int32, gpart [nblk, E] fp32, lpart [nblk] fp32,
-//   nblk = ceil(T / route_block_tokens(dtype, E))
+//   hist  [nblk, E] int32, gpart [nblk, E] fp32, lpart [nblk] fp32 (sum of lse^2),
+//   hpart [nblk] fp32 (sum of the per-token routing entropies), nblk = ceil(T / route_block_tokens)
 hipError_t launch_route(int dtype, int64_t T, int d, int E, int k, int flags, const void* x,
                         const void* W_r, const float* b, int32_t* topk_idx, float* topk_w,
-                        int32_t* hist, float* gpart, float* lpart, hipStream_t st);
+                        int32_t* hist, float* gpart, float* lpart, float* hpart, hipStream_t st);
 
 // Per-block expert histograms of a given selection (for a stand-alone dispatch).
 hipError_t launch_count(int64_t T, int E, int k, const int32_t* topk_idx, int32_t* hist,
@@ -64,13 +64,14 @@ hipError_t launch_count(int64_t T, int E, int k, const int32_t* topk_idx, int32_
 
 // One block: reduces the per-block partials (fp64, fixed order), scans loads over blocks, applies
 // the capacity and builds offsets and the grouped-GEMM tile table.
-//   block_base [nblk, E]; gsum/lse2sum/gpart/lpart may be NULL (dispatch-only use).
+//   block_base [nblk, E]; gsum/lse2sum/hsum/gpart/lpart/hpart may be NULL (dispatch-only use).
 //   tile_off [3 (E+1)]: grouped-GEMM tile tables (exclusive prefixes over groups) of 256-row,
 //   128-row and 64-row tiles when BM = 256, else of BM-row tiles and two zero tables.
 hipError_t launch_scan(int64_t T, int E, int64_t C, int nblk, const int32_t* hist,
-                       const float* gpart, const float* lpart, int32_t* block_base, int32_t* n_out,
-                       double* gsum, double* lse2sum, int32_t* kept, int32_t* overflow,
-                       int32_t* offsets, int32_t* tile_off, int BM, hipStream_t st);
+                       const float* gpart, const float* lpart, const float* hpart,
+                       int32_t* block_base, int32_t* n_out, double* gsum, double* lse2sum,
+                       double* hsum, int32_t* kept, int32_t* overflow, int32_t* offsets,
+                       int32_t* tile_off, int BM, hipStream_t st);
 
 // Places assignments: inv_perm, perm_token and (when x_perm != NULL) the x row copies.
 // block_base holds one row per histogram block of hist_block_tokens tokens (a divisor of
@@ -106,8 +107,10 @@ hipError_t launch_combine(int dtype, int64_t T, int d, int k, const void* out_pe
                           void* y, hipStream_t st);
 
 // f, P, aux, z and the bias step from reduced route statistics.
+// diag (may be NULL) [4]: routing entropy (hsum / T), load Gini, max/mean load, importance CV^2.
 hipError_t launch_stats(int64_t T, int E, int k, const int32_t* n, const double* gsum,
-                        const double* lse2sum, float lambda, float* f, float* P, float* aux,
-                        float* z, const float* b, float* b_new, float gamma, hipStream_t st);
+                        const double* lse2sum, const double* hsum, float lambda, float* f,
+                        float* P, float* aux, float* z, float* diag, const float* b, float* b_new,
+                        float gamma, hipStream_t st);
 
 }  // namespace moe

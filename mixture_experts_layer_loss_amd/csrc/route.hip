@@ -68,7 +68,8 @@ __device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, in
                              int flags, const float* __restrict__ b,
                              int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
                              int32_t* __restrict__ hist, float* __restrict__ gpart,
-                             float* __restrict__ lpart, int* hcnt, float* lsq) {
+                             float* __restrict__ lpart, float* __restrict__ hpart, int* hcnt,
+                             float* lsq, float* hsq) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int tpw = TB / nw;
   for (int e = threadIdx.x; e < E; e += blockDim.x) hcnt[e] = 0;
@@ -76,7 +77,7 @@ __device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, in
   if (lane < tpw) {
     const int tl = wave * tpw + lane;
     const int64_t t = t0 + tl;
-    float lse2 = 0.f;
+    float lse2 = 0.f, ent = 0.f;
     if (t < T) {
       float* row = L + tl * Ls;  // Ls % 4 == 0: 16-byte aligned; the pad past E holds -inf
       const int E4 = (E + 3) & ~3;
@@ -106,8 +107,10 @@ __device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, in
       }
       const bool sig = (flags & kRouteSigmoid) != 0;
       float ssum = 0.f;  // sigmoid: sum of the scores over the experts (the pad adds 0)
+      float hacc = 0.f;  // entropy term: softmax sum g (l - lse); sigmoid sum s ln s
       for (int e = 0; e < E4; e += 4) {
         float4 v = *reinterpret_cast<const float4*>(row + e);
+        const float l4[4] = {v.x, v.y, v.z, v.w};
         if (sig) {
           v.x = 1.f / (1.f + expf(-v.x));
           v.y = 1.f / (1.f + expf(-v.y));
@@ -128,9 +131,14 @@ __device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, in
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int ee = e + q;
-          if (ee < E) topk_insert<KM>(b != nullptr ? g4[q] + b[ee] : g4[q], ee, tv, ti);
+          if (ee < E) {
+            topk_insert<KM>(b != nullptr ? g4[q] + b[ee] : g4[q], ee, tv, ti);
+            hacc += sig ? (g4[q] > 0.f ? g4[q] * logf(g4[q]) : 0.f) : g4[q] * (l4[q] - lse);
+          }
         }
       }
+      // routing entropy of the token's distribution (softmax g, or s / sum s)
+      ent = sig ? logf(ssum) - hacc / ssum : -hacc;
       float wsum = 0.f;
 #pragma unroll
       for (int j = 0; j < KM; ++j)
@@ -150,6 +158,7 @@ __device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, in
       }
     }
     lsq[tl] = lse2;
+    hsq[tl] = ent;
   }
   __syncthreads();
   const int64_t blk = blockIdx.x;
@@ -161,9 +170,13 @@ __device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, in
     hist[blk * E + e] = hcnt[e];
   }
   if (threadIdx.x == 0) {
-    float ls = 0.f;
-    for (int tl = 0; tl < nt; ++tl) ls += lsq[tl];
+    float ls = 0.f, hs = 0.f;
+    for (int tl = 0; tl < nt; ++tl) {
+      ls += lsq[tl];
+      hs += hsq[tl];
+    }
     lpart[blk] = ls;
+    hpart[blk] = hs;
   }
 }
 
@@ -183,7 +196,8 @@ __device__ void route_tokens_split(float* L, int Ls, int64_t t0, int64_t T, int 
                                    int flags, const float* __restrict__ b,
                                    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
                                    int32_t* __restrict__ hist, float* __restrict__ gpart,
-                                   float* __restrict__ lpart, int* hcnt, float* lsq, float* part,
+                                   float* __restrict__ lpart, float* __restrict__ hpart, int* hcnt,
+                                   float* lsq, float* hsq, float* part, float* part2,
                                    float* xv, int* xi) {
   constexpr int TB = 64, NW = 8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -222,6 +236,7 @@ __device__ void route_tokens_split(float* L, int Ls, int64_t t0, int64_t T, int 
   // scores of the slice, written back over the logits, and the slice's sorted top-KM
   const bool sig = (flags & kRouteSigmoid) != 0;
   float ssum = 0.f;
+  float hacc = 0.f;  // entropy term of the slice: softmax sum g (l - lse); sigmoid sum s ln s
   float tv[KM];
   int ti[KM];
 #pragma unroll
@@ -231,6 +246,7 @@ __device__ void route_tokens_split(float* L, int Ls, int64_t t0, int64_t T, int 
   }
   for (int e = e0; e < e1; e += 4) {
     float4 v = *reinterpret_cast<const float4*>(row + e);
+    const float l4[4] = {v.x, v.y, v.z, v.w};
     if (sig) {
       v.x = 1.f / (1.f + expf(-v.x));
       v.y = 1.f / (1.f + expf(-v.y));
@@ -251,7 +267,10 @@ __device__ void route_tokens_split(float* L, int Ls, int64_t t0, int64_t T, int 
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int ee = e + q;
-      if (ee < E) topk_insert<KM>(b != nullptr ? g4[q] + b[ee] : g4[q], ee, tv, ti);
+      if (ee < E) {
+        topk_insert<KM>(b != nullptr ? g4[q] + b[ee] : g4[q], ee, tv, ti);
+        hacc += sig ? (g4[q] > 0.f ? g4[q] * logf(g4[q]) : 0.f) : g4[q] * (l4[q] - lse);
+      }
     }
   }
   // pairwise merges: round r, waves w with w % 2^(r+1) == 0 take the list of wave w + 2^r
@@ -276,8 +295,9 @@ __device__ void route_tokens_split(float* L, int Ls, int64_t t0, int64_t T, int 
       }
     }
   }
-  // the sigmoid probability statistic normalises by the sum over all experts
-  if (sig) part[wave * TB + tl] = ssum;
+  // slice partials of the score sum (sigmoid) and of the entropy term, combined in wave order
+  part[wave * TB + tl] = ssum;
+  part2[wave * TB + tl] = hacc;
   __syncthreads();
   if (wave == 0 && live) {
     float wsum = 0.f;
@@ -294,10 +314,16 @@ __device__ void route_tokens_split(float* L, int Ls, int64_t t0, int64_t T, int 
       }
     }
   }
-  if (wave == 0) lsq[tl] = live ? lse * lse : 0.f;
-  if (sig) {
-    float tot = 0.f;
-    for (int w = 0; w < NW; ++w) tot += part[w * TB + tl];
+  float tot = 0.f, htot = 0.f;
+  for (int w = 0; w < NW; ++w) {
+    tot += part[w * TB + tl];
+    htot += part2[w * TB + tl];
+  }
+  if (wave == 0) {
+    lsq[tl] = live ? lse * lse : 0.f;
+    hsq[tl] = live ? (sig ? logf(tot) - htot / tot : -htot) : 0.f;
+  }
+  if (sig) {  // the sigmoid probability statistic normalises by the sum over all experts
     __syncthreads();  // wave 0 has read the raw scores of every slice
     const float inv = 1.f / tot;
     for (int e = e0; e < e1; ++e) row[e] *= inv;
@@ -312,9 +338,13 @@ __device__ void route_tokens_split(float* L, int Ls, int64_t t0, int64_t T, int 
     hist[blk * E + e] = hcnt[e];
   }
   if (threadIdx.x == 0) {
-    float ls = 0.f;
-    for (int q = 0; q < nt; ++q) ls += lsq[q];
+    float ls = 0.f, hs = 0.f;
+    for (int q = 0; q < nt; ++q) {
+      ls += lsq[q];
+      hs += hsq[q];
+    }
     lpart[blk] = ls;
+    hpart[blk] = hs;
   }
 }
 
@@ -350,7 +380,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ b,
     int64_t T, int d, int E, int k, int flags, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ hist, float* __restrict__ gpart,
-    float* __restrict__ lpart) {
+    float* __restrict__ lpart, float* __restrict__ hpart) {
   constexpr int TB = 16 * MB;
   constexpr int NW = kRouteThreads / 64;
   constexpr int NWK = NW / NG;                // waves splitting K within an expert group
@@ -358,6 +388,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
   __shared__ float L[TB * kLogitsStride];
   __shared__ int hcnt[MOE_E_MAX];
   __shared__ float lsq[TB];
+  __shared__ float hsq[TB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = wave / NWK, kw = wave % NWK;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TB;
@@ -448,7 +479,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
   __syncthreads();
 #define MOE_CALL(KM) \
   route_tokens<KM>(L, kLogitsStride, TB, t0, T, E, k, flags, b, topk_idx, topk_w, hist, gpart, \
-                   lpart, hcnt, lsq)
+                   lpart, hpart, hcnt, lsq, hsq)
   MOE_ROUTE_TOKENS_KM(MOE_CALL);
 #undef MOE_CALL
 }
@@ -460,10 +491,11 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ W, const float* __restrict__ b,
     int64_t T, int d, int E, int k, int flags, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ hist, float* __restrict__ gpart,
-    float* __restrict__ lpart) {
+    float* __restrict__ lpart, float* __restrict__ hpart) {
   __shared__ float L[RT * kLogitsStride];
   __shared__ int hcnt[MOE_E_MAX];
   __shared__ float lsq[RT];
+  __shared__ float hsq[RT];
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * RT;  // fp32 blocks are 64 tokens
   for (int p = threadIdx.x; p < RT * E; p += blockDim.x) {
     const int tl = p / E, e = p % E;
@@ -482,7 +514,7 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
   __syncthreads();
 #define MOE_CALL(KM) \
   route_tokens<KM>(L, kLogitsStride, RT, t0, T, E, k, flags, b, topk_idx, topk_w, hist, gpart, \
-                   lpart, hcnt, lsq)
+                   lpart, hpart, hcnt, lsq, hsq)
   MOE_ROUTE_TOKENS_KM(MOE_CALL);
 #undef MOE_CALL
 }
@@ -504,7 +536,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ b,
     int64_t T, int d, int E, int k, int flags, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ hist, float* __restrict__ gpart,
-    float* __restrict__ lpart) {
+    float* __restrict__ lpart, float* __restrict__ hpart) {
   constexpr int TB = 64;
   constexpr int ROWS = TB + 16 * NEB;                 // x rows then W_r rows of a stage
   constexpr int STAGE = ROWS * kSKP;                  // bf16 elements
@@ -516,7 +548,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStagesBytes > kLBytes ? kStagesBytes : kLBytes];
   __shared__ int hcnt[MOE_E_MAX];
   __shared__ float lsq[TB];
+  __shared__ float hsq[TB];
   __shared__ float part[SPLIT ? 8 * TB : 1];         // per-wave partials of the split routing
+  __shared__ float part2[SPLIT ? 8 * TB : 1];
   __shared__ float xv[SPLIT ? 4 * TB * 16 : 1];      // its exchange lists (KM <= 16)
   __shared__ int xi[SPLIT ? 4 * TB * 16 : 1];
   bf16_t* st = reinterpret_cast<bf16_t*>(smem);
@@ -624,10 +658,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
 #define MOE_CALL(KM)                                                                           \
   if constexpr (SPLIT)                                                                         \
     route_tokens_split<KM>(L, kLogitsStride, t0, T, E, k, flags, b, topk_idx, topk_w, hist,     \
-                           gpart, lpart, hcnt, lsq, part, xv, xi);                             \
+                           gpart, lpart, hpart, hcnt, lsq, hsq, part, part2, xv, xi);                             \
   else                                                                                         \
     route_tokens<KM>(L, kLogitsStride, TB, t0, T, E, k, flags, b, topk_idx, topk_w, hist, gpart, \
-                     lpart, hcnt, lsq)
+                     lpart, hpart, hcnt, lsq, hsq)
   MOE_ROUTE_TOKENS_KM(MOE_CALL);
 #undef MOE_CALL
 }
@@ -635,29 +669,29 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
 template <int NEB>
 hipError_t launch_bf16_lds(hipStream_t st, const void* x, const void* W, const float* b, int64_t T,
                            int d, int E, int k, int flags, int32_t* topk_idx, float* topk_w,
-                           int32_t* hist, float* gpart, float* lpart) {
+                           int32_t* hist, float* gpart, float* lpart, float* hpart) {
   // short lists over at most 128 experts stay one lane per token (cheaper than the merge rounds)
   const dim3 grid(static_cast<unsigned>(cdiv(T, 64)));
   if (NEB <= 8 && k <= 2)
     hipLaunchKernelGGL((route_bf16_lds_kernel<NEB, false>), grid, dim3(kRouteThreads), 0, st,
                        static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W), b, T, d, E,
-                       k, flags, topk_idx, topk_w, hist, gpart, lpart);
+                       k, flags, topk_idx, topk_w, hist, gpart, lpart, hpart);
   else
     hipLaunchKernelGGL((route_bf16_lds_kernel<NEB, true>), grid, dim3(kRouteThreads), 0, st,
                        static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W), b, T, d, E,
-                       k, flags, topk_idx, topk_w, hist, gpart, lpart);
+                       k, flags, topk_idx, topk_w, hist, gpart, lpart, hpart);
   return hipGetLastError();
 }
 
 template <int MB, int NEB, int NG>
 hipError_t launch_bf16(hipStream_t st, const void* x, const void* W, const float* b,
                        int64_t T, int d, int E, int k, int flags, int32_t* topk_idx,
-                       float* topk_w, int32_t* hist, float* gpart, float* lpart) {
+                       float* topk_w, int32_t* hist, float* gpart, float* lpart, float* hpart) {
   const int64_t nblk = cdiv(T, 16 * MB);
   hipLaunchKernelGGL((route_bf16_kernel<MB, NEB, NG>), dim3(static_cast<unsigned>(nblk)),
                      dim3(kRouteThreads), 0, st,
                      static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W), b, T, d, E, k,
-                     flags, topk_idx, topk_w, hist, gpart, lpart);
+                     flags, topk_idx, topk_w, hist, gpart, lpart, hpart);
   return hipGetLastError();
 }
 
@@ -667,24 +701,25 @@ int route_block_tokens(int dtype, int E) { return dtype == MOE_F32 ? RT : (E <= 
 
 hipError_t launch_route(int dtype, int64_t T, int d, int E, int k, int flags, const void* x,
                         const void* W_r, const float* b, int32_t* topk_idx, float* topk_w,
-                        int32_t* hist, float* gpart, float* lpart, hipStream_t st) {
+                        int32_t* hist, float* gpart, float* lpart, float* hpart,
+                        hipStream_t st) {
   if (dtype == MOE_F32) {
     const int64_t nblk = cdiv(T, RT);
     hipLaunchKernelGGL(route_f32_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
                        static_cast<const float*>(x), static_cast<const float*>(W_r), b, T, d, E,
-                       k, flags, topk_idx, topk_w, hist, gpart, lpart);
+                       k, flags, topk_idx, topk_w, hist, gpart, lpart, hpart);
     return hipGetLastError();
   }
   const int neb = static_cast<int>(cdiv(E, 16));
 #define MOE_ROUTE_CASE(N)                                                                   \
   case N:                                                                                   \
     return launch_bf16_lds<N>(st, x, W_r, b, T, d, E, k, flags, topk_idx, topk_w, hist, gpart, \
-                              lpart);
+                              lpart, hpart);
   // up to 16 experts: 16-token blocks with the hidden dimension split over the waves (more blocks
   // in flight); more: 64-token blocks with W_r shared through LDS
   if (E <= 16)
     return launch_bf16<1, 1, 1>(st, x, W_r, b, T, d, E, k, flags, topk_idx, topk_w, hist, gpart,
-                                lpart);
+                                lpart, hpart);
   switch (neb) {
     MOE_ROUTE_CASE(2) MOE_ROUTE_CASE(3) MOE_ROUTE_CASE(4) MOE_ROUTE_CASE(5) MOE_ROUTE_CASE(6)
     MOE_ROUTE_CASE(7) MOE_ROUTE_CASE(8) MOE_ROUTE_CASE(9) MOE_ROUTE_CASE(10) MOE_ROUTE_CASE(11)

@@ -3,7 +3,11 @@
 //   ("MoE：条件计算与路由" §原理与演进; "深入理解 MoE (混合专家模型)：稀疏激活与高效扩展" §4.2.1;
 //   "MOE大模型对比篇" §2.1), z = lse2sum / T ("MOE大模型对比篇" §2.2), and
 //   b_e <- b_e + gamma * sign(k T / E - n_e) ("MoE：条件计算与路由" §无辅助损失负载均衡（ALF-LB）).
-// One block; fp64 inside, the sum over experts is a fixed-order tree, outputs are fp32. The sign
+// Routing diagnostics ("MoE：条件计算与路由" §9 routing entropy, §10 load Gini coefficient and
+// max/mean load; the adg.csdn.net notes page, importance CV^2 of Importance_e = gsum_e):
+//   entropy = hsum / T, Gini = sum_ij |n_i - n_j| / (2 E sum_e n_e) (integer sums, exact),
+//   max/mean = max_e n_e E / sum_e n_e, CV^2 = Var_e(gsum) / Mean_e(gsum)^2 (population variance).
+// One block; fp64 inside, sums over experts are fixed-order trees, outputs are fp32. The sign
 // compares the integers k T and n_e E, so it is exact; the bias step is a single fp32 addition of
 // +-gamma or 0.
 #include "moe_internal.h"
@@ -11,17 +15,38 @@
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(256) void stats_kernel(int64_t T, int E, int k,
-                                                     const int32_t* __restrict__ n,
-                                                     const double* __restrict__ gsum,
-                                                     const double* __restrict__ lse2sum,
-                                                     float lambda, float* __restrict__ f,
-                                                     float* __restrict__ P, float* __restrict__ aux,
-                                                     float* __restrict__ z,
-                                                     const float* __restrict__ b,
-                                                     float* __restrict__ b_new, float gamma) {
+__global__ __launch_bounds__(256) void stats_kernel(
+    int64_t T, int E, int k, const int32_t* __restrict__ n, const double* __restrict__ gsum,
+    const double* __restrict__ lse2sum, const double* __restrict__ hsum, float lambda,
+    float* __restrict__ f, float* __restrict__ P, float* __restrict__ aux, float* __restrict__ z,
+    float* __restrict__ diag, const float* __restrict__ b, float* __restrict__ b_new,
+    float gamma) {
   __shared__ double red[256];
+  __shared__ long long ired[256];
   const int e = threadIdx.x;
+  // fixed-order tree sum over the 256 slots of red (every thread returns the total)
+  auto tree = [&](double v) -> double {
+    red[e] = v;
+    __syncthreads();
+    for (int off = 128; off >= 1; off >>= 1) {
+      if (e < off) red[e] += red[e + off];
+      __syncthreads();
+    }
+    const double r = red[0];
+    __syncthreads();
+    return r;
+  };
+  auto itree = [&](long long v, bool take_max) -> long long {
+    ired[e] = v;
+    __syncthreads();
+    for (int off = 128; off >= 1; off >>= 1) {
+      if (e < off) ired[e] = take_max ? max(ired[e], ired[e + off]) : ired[e] + ired[e + off];
+      __syncthreads();
+    }
+    const long long r = ired[0];
+    __syncthreads();
+    return r;
+  };
   double prod = 0.0;
   float bnew = 0.f;
   if (e < E) {
@@ -36,26 +61,46 @@ __global__ __launch_bounds__(256) void stats_kernel(int64_t T, int E, int k,
       bnew = b[e] + gamma * sgn;
     }
   }
-  red[e] = prod;
   __syncthreads();  // every read of b is done before any write of b_new (they may alias)
   if (e < E && b_new != nullptr) b_new[e] = bnew;
-  for (int off = 128; off >= 1; off >>= 1) {
-    if (e < off) red[e] += red[e + off];
-    __syncthreads();
-  }
+  const double fp = tree(prod);
   if (e == 0) {
-    if (aux != nullptr) *aux = static_cast<float>(static_cast<double>(lambda) * E * red[0]);
+    if (aux != nullptr) *aux = static_cast<float>(static_cast<double>(lambda) * E * fp);
     if (z != nullptr) *z = static_cast<float>(*lse2sum / static_cast<double>(T));
+  }
+  if (diag == nullptr) return;
+  // Gini: sum over pairs of |n_i - n_j| (integers), over 2 E sum_e n_e
+  long long pairs = 0;
+  const long long ne = e < E ? n[e] : 0;
+  if (e < E)
+    for (int j = 0; j < E; ++j) {
+      const long long d = ne - static_cast<long long>(n[j]);
+      pairs += d < 0 ? -d : d;
+    }
+  const long long psum = itree(pairs, false);
+  const long long ntot = itree(ne, false);
+  const long long nmax = itree(ne, true);
+  // importance CV^2: population variance over experts of gsum, over the squared mean
+  const double imp = e < E ? gsum[e] : 0.0;
+  const double mean = tree(imp) / E;
+  const double dv = e < E ? imp - mean : 0.0;
+  const double var = tree(dv * dv) / E;
+  if (e == 0) {
+    diag[0] = static_cast<float>(*hsum / static_cast<double>(T));
+    diag[1] = ntot > 0 ? static_cast<float>(static_cast<double>(psum) / (2.0 * E * ntot)) : 0.f;
+    diag[2] = ntot > 0 ? static_cast<float>(static_cast<double>(nmax) * E / ntot) : 0.f;
+    diag[3] = mean != 0.0 ? static_cast<float>(var / (mean * mean)) : 0.f;
   }
 }
 
 }  // namespace
 
 hipError_t launch_stats(int64_t T, int E, int k, const int32_t* n, const double* gsum,
-                        const double* lse2sum, float lambda, float* f, float* P, float* aux,
-                        float* z, const float* b, float* b_new, float gamma, hipStream_t st) {
-  hipLaunchKernelGGL(stats_kernel, dim3(1), dim3(256), 0, st, T, E, k, n, gsum, lse2sum, lambda, f,
-                     P, aux, z, b, b_new, gamma);
+                        const double* lse2sum, const double* hsum, float lambda, float* f,
+                        float* P, float* aux, float* z, float* diag, const float* b, float* b_new,
+                        float gamma, hipStream_t st) {
+  hipLaunchKernelGGL(stats_kernel, dim3(1), dim3(256), 0, st, T, E, k, n, gsum, lse2sum, hsum,
+                     lambda, f, P, aux, z, diag, b, b_new, gamma);
   return hipGetLastError();
 }
 

@@ -110,20 +110,23 @@ def test_entry_points_reject_before_launch():
     sp = ctypes.byref(s)
     F = _fake
     # missing required pointers
-    assert L.moe_route(sp, None, F(), None, F(), F(), F(), F(), F(), F(), 1 << 20, None) == 1
+    assert L.moe_route(sp, None, F(), None, F(), F(), F(), F(), F(), None, F(), 1 << 20, None) == 1
     assert L.moe_dispatch(sp, F(), None, None, F(), F(), F(), F(), F(), F(), 1 << 20, None) == 1
     assert L.moe_combine(sp, None, F(), F(), None, F(), None) == 1
-    assert L.moe_balance_stats(sp, None, F(), F(), 0.01, None, None, None, None, None, None,
-                               1e-3, None) == 1
+    assert L.moe_balance_stats(sp, None, F(), F(), None, 0.01, None, None, None, None, None, None,
+                               None, 1e-3, None) == 1
     # b without b_new
-    assert L.moe_balance_stats(sp, F(), F(), F(), 0.01, None, None, None, None, F(), None,
-                               1e-3, None) == 1
+    assert L.moe_balance_stats(sp, F(), F(), F(), None, 0.01, None, None, None, None, None, F(),
+                               None, 1e-3, None) == 1
+    # diagnostics need the entropy sum
+    assert L.moe_balance_stats(sp, F(), F(), F(), None, 0.01, None, None, None, None, F(), None,
+                               None, 1e-3, None) == 1
     # misaligned tensor
     assert L.moe_combine(sp, ctypes.c_void_p(4096 + 4), F(), F(), None, F(), None) == 1
     # workspace missing or too small
-    assert L.moe_route(sp, F(), F(), None, F(), F(), F(), F(), F(), None, 0, None) == 3
+    assert L.moe_route(sp, F(), F(), None, F(), F(), F(), F(), F(), None, None, 0, None) == 3
     need = moe.workspace_size(s, moe.CALL_ROUTE)
-    assert L.moe_route(sp, F(), F(), None, F(), F(), F(), F(), F(), F(), need - 1, None) == 3
+    assert L.moe_route(sp, F(), F(), None, F(), F(), F(), F(), F(), None, F(), need - 1, None) == 3
     assert L.moe_dispatch(sp, F(), F(), None, F(), F(), F(), F(), F(), None, 0, None) == 3
     assert L.moe_expert_ffn(sp, 8, 256, F(), F(), 128, F(), F(), F(), F(), F(), None, 0, None) == 3
     # expert FFN argument checks
@@ -136,17 +139,17 @@ def test_entry_points_reject_before_launch():
     # layer: shared experts required when S > 0; b_new requires b
     s2 = moe.make_shape(64, 128, 8, 2, 256, S=2)
     ws = moe.workspace_size(s2, moe.CALL_LAYER)
-    # x, W_r, b, W_gate, W_up, W_down, Ws_gate/up/down, y, 9 optional outputs, lambda, gamma, ws
-    args = [F()] * 2 + [None] + [F()] * 3 + [None] * 3 + [F()] + [None] * 9 + [0.01, 1e-3, F(), ws,
-                                                                              None]
+    # x, W_r, b, W_gate, W_up, W_down, Ws_gate/up/down, y, 10 optional outputs, lambda, gamma, ws
+    args = [F()] * 2 + [None] + [F()] * 3 + [None] * 3 + [F()] + [None] * 10 + [0.01, 1e-3, F(), ws,
+                                                                               None]
     assert L.moe_layer_forward(ctypes.byref(s2), *args) == 1
-    args = [F()] * 2 + [None] + [F()] * 3 + [None] * 3 + [F()] + [None] * 8 + [F(), 0.01, 1e-3,
+    args = [F()] * 2 + [None] + [F()] * 3 + [None] * 3 + [F()] + [None] * 9 + [F(), 0.01, 1e-3,
                                                                               F(), ws, None]
     assert L.moe_layer_forward(sp, *args) == 1
     # invalid shape short-circuits everything
     bad = moe.make_shape(64, 128, 8, 9, 256)
-    assert L.moe_route(ctypes.byref(bad), F(), F(), None, F(), F(), F(), F(), F(), F(), 1 << 30,
-                       None) == 1
+    assert L.moe_route(ctypes.byref(bad), F(), F(), None, F(), F(), F(), F(), F(), None, F(),
+                       1 << 30, None) == 1
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

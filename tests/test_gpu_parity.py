@@ -86,6 +86,7 @@ def test_route(gpu, base, kw):
     assert np.array_equal(r["n"].cpu().numpy(), O.expert_loads(idx, cfg.E))
     assert rel(r["gsum"], orc["probs"].sum(0)) < TOL_STATS
     assert rel(r["lse2sum"], [np.sum(orc["lse"] ** 2)]) < TOL_STATS
+    assert rel(r["hsum"], [cfg.T * O.routing_entropy(orc["probs"])]) < TOL_STATS
 
 
 # ---------------------------------------------------------------------------------- dispatch
@@ -195,11 +196,17 @@ def test_balance_stats(gpu):
     n[:3] = k * T // E  # k T / E = 187.5 here, never an integer: no zero step
     gsum = rng.random(E) * T / E
     lse2 = np.array([T * 9.3])
+    hsum = np.array([T * 4.1])
     b = (rng.random(E) * 0.1 - 0.05).astype(np.float32)
     dev = gpu
     r = moe.moe_balance_stats(T, k, torch.from_numpy(n).to(dev), torch.from_numpy(gsum).to(dev),
-                              torch.from_numpy(lse2).to(dev), 0.01, torch.from_numpy(b).to(dev), 1e-3)
+                              torch.from_numpy(lse2).to(dev), 0.01, torch.from_numpy(b).to(dev), 1e-3,
+                              hsum=torch.from_numpy(hsum).to(dev))
     torch.cuda.synchronize()
+    # diagnostics from the same fp64 inputs: float32 rounding of fp64 results
+    dg = r["diag"].cpu().numpy().astype(np.float64)
+    ref = [hsum[0] / T, O.load_gini(n), O.load_max_over_mean(n), O.importance_cv2(gsum)]
+    assert np.allclose(dg, ref, rtol=1e-6, atol=0), (dg, ref)
     g_fake = np.zeros((T, E))
     g_fake[0] = gsum  # sum over tokens = gsum
     st = O.balance_stats(n, g_fake, np.sqrt(np.full(T, lse2[0] / T)), k, 0.01)
@@ -268,6 +275,15 @@ def check_layer(cfg, inp, out, tokens=None):
     assert rel(out["P"], res["P"]) < TOL_STATS
     assert rel(out["aux"], [res["aux"]]) < TOL_STATS
     assert rel(out["z"], [res["z"]]) < TOL_STATS
+    # diagnostics: entropy within the statistics bound; Gini and max/mean come from the integer
+    # loads; the importance CV^2 is Var/Mean^2 of the fp32-summed importances, whose relative
+    # errors (~1e-6) perturb a small CV^2 by about 2 sqrt(CV^2) 1e-6: allow 1e-5 relative + 1e-6
+    dg = out["diag"].cpu().numpy().astype(np.float64)
+    rd = res["diag"]
+    assert rel([dg[0]], [rd["entropy"]]) < TOL_STATS
+    assert abs(dg[1] - rd["gini"]) <= 1e-6 * max(rd["gini"], 1e-3)
+    assert abs(dg[2] - rd["max_over_mean"]) <= 1e-6 * rd["max_over_mean"]
+    assert abs(dg[3] - rd["importance_cv2"]) <= 1e-5 * rd["importance_cv2"] + 1e-6
     if inp.b is not None:
         assert np.array_equal(out["b_new"].cpu().numpy(), res["b_new"])
     return {"y_err": err, "exempt": n_ex, "differ": n_diff,
