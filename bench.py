@@ -180,7 +180,8 @@ def main():
     fl = {"gemm_up": 4.0 * d * M * kept, "gemm_down": 2.0 * d * M * kept,
           "shared": 6.0 * d * S * M * T, "route": 2.0 * d * E * T}
     by = {"route": T * d * eb + E * d * eb + T * k * 8,
-          "dispatch": T * d * eb + kept * d * eb + T * k * 8 + kept * 4,
+          # placement only (indices); the gate/up GEMM gathers the x rows itself
+          "dispatch": T * k * 8 + kept * 4,
           "combine": kept * d * eb + T * k * 8 + (T * d * eb if S else 0) + T * d * eb}
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     stages = {}
