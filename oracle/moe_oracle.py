@@ -35,6 +35,12 @@ uses it):
   * Within an expert's segment, rows are in ascending token order (a stable sort by expert).
   * S shared experts take the same x as the router, are added with weight 1, and are summed.
   * Bias update: b_e <- b_e + gamma * sign(k T / E - n_e), sign(0) = 0, done in float32.
+  * Expert choice: each expert takes the r tokens with the largest router logit for it (the score
+    the listing ranks by), ties to the lower token index, r = C = ceil(c k T / E) (c <= 0 reads as
+    c = 1), at most T; a token's gates are its scores g_te over the experts that took it,
+    renormalised over that set when renorm is on; a token no expert took gets only the shared
+    term. Rows of an expert are in ascending token order; loads n_e = r; the load-balancing bias
+    does not apply (a per-expert shift leaves every expert's ranking of tokens unchanged).
   * Diagnostics: routing entropy is the token mean of H(p_t) = -sum_e p_te ln p_te (natural log,
     0 ln 0 = 0) of the same per-token distribution P_e averages; the load Gini coefficient is
     sum_ij |n_i - n_j| / (2 E sum_e n_e); max/mean load is max_e n_e / (sum_e n_e / E); the
@@ -163,6 +169,24 @@ def capacity(c: Optional[float], k: int, T: int, E: int) -> Optional[int]:
     if c32 <= 0.0:
         return None
     return int(math.ceil(((c32 * k) * T) / E))
+
+
+def expert_choice(l: np.ndarray, r: int) -> np.ndarray:
+    """Expert-choice selection ([AIATTN] §9.2 Expert Choice MoE: every expert picks the top tokens
+    by its score column; [ATLAS] §路由机制的演进, experts choose top-r_e tokens): for each expert, the
+    r tokens of largest l[t, e] (a stable sort of -l down the column keeps equal scores in
+    ascending token order), returned in ascending token order. [E, r] int64"""
+    l = _f64(l)
+    order = np.argsort(-l, axis=0, kind="stable")
+    return np.sort(order[:r, :].T, axis=1).astype(np.int64)
+
+
+def expert_choice_capacity(c: Optional[float], k: int, T: int, E: int) -> int:
+    """r = ceil(c k T / E) as for token choice, with c <= 0 (or None) read as 1, at most T."""
+    C = capacity(c, k, T, E)
+    if C is None:
+        C = capacity(1.0, k, T, E)
+    return min(C, T)
 
 
 def dispatch(S: np.ndarray, E: int, C: Optional[int]):
@@ -334,6 +358,51 @@ def route(x, W_r, k: int, b=None, renorm: bool = True, scoring: str = "softmax")
     w = gate_weights(g, S, renorm)
     return {"logits": l, "g": g, "lse": lse, "s": s, "topk_idx": S, "topk_w": w,
             "margin": topk_margin(s, k), "probs": score_distribution(g, scoring)}
+
+
+def layer_forward_expert_choice(x, W_r, W_gate, W_up, W_down, k: int, shared=(), c=None,
+                                renorm: bool = True, lam: float = 0.01, tokens=None,
+                                expert_weights=None, scoring: str = "softmax"):
+    """Expert-choice layer: expert e applies E_e to the r tokens it chose; y_t sums w_te E_e(x_t)
+    over the experts that chose t, in ascending expert order, plus the shared experts."""
+    x64 = _f64(x)
+    T, d = x64.shape
+    r_ = route(x64, W_r, 1, None, renorm, scoring)
+    l, g = r_["logits"], r_["g"]
+    E = g.shape[1]
+    r = expert_choice_capacity(c, k, T, E)
+    chosen = expert_choice(l, r)
+    member = np.zeros((T, E), dtype=bool)
+    for e in range(E):
+        member[chosen[e], e] = True
+    w = np.where(member, g, 0.0)
+    if renorm:
+        den = w.sum(axis=1, keepdims=True)
+        w = np.divide(w, den, out=np.zeros_like(w), where=den > 0)
+    n = np.full(E, r, dtype=np.int64)
+    want = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    y = np.zeros((len(want), d))
+    xs = x64[want]
+    if shared:
+        y += shared_experts(xs, shared)
+    pos = {int(t): i for i, t in enumerate(want)}
+    for e in range(E):
+        rows = [int(t) for t in chosen[e] if int(t) in pos]
+        if not rows:
+            continue
+        We = expert_weights(e) if expert_weights is not None else (W_gate[e], W_up[e], W_down[e])
+        O = swiglu_expert(x64[rows], *We)
+        for i, t in enumerate(rows):
+            y[pos[t]] += w[t, e] * O[i]
+    # f_e = n_e / sum_e n_e (equal loads: 1 / E), P_e from the same distribution as token choice
+    f = n / float(n.sum())
+    P = r_["probs"].sum(axis=0) / float(T)
+    aux = float(lam) * E * float((f * P).sum())
+    z = float((r_["lse"] ** 2).sum() / float(T))
+    return {"y": y, "tokens": want, "chosen": chosen, "r": r, "w": w, "n": n, "f": f, "P": P,
+            "aux": aux, "z": z, "lse": r_["lse"], "g": g, "logits": l,
+            "diag": diagnostics(n, r_["probs"]),
+            "uncovered": int((~member.any(axis=1)).sum())}
 
 
 def layer_forward(x, W_r, W_gate, W_up, W_down, k: int, b=None, shared=(), c=None,

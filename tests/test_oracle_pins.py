@@ -273,6 +273,64 @@ def test_diagnostics_pins():
     check_diagnostics()
 
 
+# ----------------------------------------------------------------------------- expert choice
+
+def check_expert_choice(mod=O):
+    T, E, r = 50, 6, 7
+    l = _rand((T, E), 31, 2.0)
+    ch = mod.expert_choice(l, r)
+    assert ch.shape == (E, r)
+    for e in range(E):
+        assert np.all(np.diff(ch[e]) > 0)  # ascending, distinct
+        # torch.topk on distinct values is an independent library routine
+        ref = torch.topk(torch.from_numpy(l[:, e]), r).indices.numpy()
+        assert set(ch[e].tolist()) == set(ref.tolist())
+    # characterisation with ties: t is taken iff fewer than r tokens beat it (larger score, or
+    # equal score and lower index); integer scores make many ties
+    li = np.random.default_rng(32).integers(0, 4, size=(20, 3)).astype(np.float64)
+    ch2 = mod.expert_choice(li, 5)
+    for e in range(3):
+        for t in range(20):
+            beat = sum(1 for u in range(20) if li[u, e] > li[t, e] or (li[u, e] == li[t, e] and u < t))
+            assert (t in set(ch2[e].tolist())) == (beat < 5)
+    # all scores equal: the first r tokens
+    assert np.array_equal(mod.expert_choice(np.zeros((9, 2)), 4), [[0, 1, 2, 3]] * 2)
+    # r = ceil(c k T / E), c <= 0 read as 1, at most T
+    assert mod.expert_choice_capacity(1.0, 2, 10, 3) == GOLDEN["capacity_ceil"]["C"]
+    assert mod.expert_choice_capacity(None, 2, 10, 3) == 7 and mod.expert_choice_capacity(0.0, 2, 10, 3) == 7
+    assert mod.expert_choice_capacity(8.0, 2, 10, 3) == 10
+
+
+def test_expert_choice_pins():
+    check_expert_choice()
+
+
+def test_expert_choice_layer_pins():
+    x, W_r, Wg, Wu, Wd = _tiny_layer(T=30, E=4, k=2)
+    T, E = 30, 4
+    # r = T: every expert takes every token; renormalised gates are the softmax itself, so y is the
+    # dense soft mixture sum_e g_te E_e(x_t), computed here without any selection
+    res = O.layer_forward_expert_choice(x, W_r, Wg, Wu, Wd, 2, c=E / 2.0)
+    assert res["r"] == T and res["uncovered"] == 0
+    from scipy.special import softmax
+    g = softmax(x @ W_r.T, axis=1)
+    dense = sum(g[:, e:e + 1] * O.swiglu_expert(x, Wg[e], Wu[e], Wd[e]) for e in range(E))
+    assert np.allclose(res["y"], dense, rtol=1e-12, atol=1e-12)
+    # identical experts + renorm: every covered token gets FFN(x); uncovered tokens get 0
+    Wg1, Wu1, Wd1 = (np.repeat(W[:1], E, axis=0) for W in (Wg, Wu, Wd))
+    res2 = O.layer_forward_expert_choice(x, W_r, Wg1, Wu1, Wd1, 1, c=0.5)
+    ffn = O.swiglu_expert(x, Wg1[0], Wu1[0], Wd1[0])
+    covered = np.zeros(T, dtype=bool)
+    for e in range(E):
+        covered[res2["chosen"][e]] = True
+    assert res2["uncovered"] == int((~covered).sum()) > 0
+    assert np.allclose(res2["y"][covered], ffn[covered], rtol=1e-12, atol=1e-12)
+    assert np.all(res2["y"][~covered] == 0.0)
+    # equal loads: f = 1/E, Gini 0, max/mean 1
+    assert np.allclose(res2["f"], 1.0 / E) and res2["diag"]["gini"] == 0.0
+    assert res2["diag"]["max_over_mean"] == 1.0
+
+
 # ----------------------------------------------------------------------------- capacity/dispatch
 
 def test_capacity_closed_forms():
@@ -548,6 +606,17 @@ def _entropy_log2(probs):
         return float(-np.where(p > 0, p * np.log2(p), 0.0).sum(axis=1).mean())
 
 
+def _ec_ties_high(l, r):
+    l = O._f64(l)
+    T = l.shape[0]
+    order = np.argsort(-l[::-1], axis=0, kind="stable")
+    return np.sort(((T - 1) - order[:r, :]).T, axis=1).astype(np.int64)
+
+
+def _ec_smallest(l, r):
+    return O.expert_choice(-O._f64(l), r)
+
+
 def _sigmoid_wrong_sign(l):
     l = O._f64(l)
     return 1.0 / (1.0 + np.exp(l))
@@ -570,6 +639,8 @@ def _sigmoid_unnormalised_P(g, scoring="softmax"):
     (dict(score_distribution=_sigmoid_unnormalised_P), [check_sigmoid_stats]),
     (dict(load_gini=_gini_half), [check_diagnostics]),
     (dict(routing_entropy=_entropy_log2), [check_diagnostics]),
+    (dict(expert_choice=_ec_ties_high), [check_expert_choice]),
+    (dict(expert_choice=_ec_smallest), [check_expert_choice]),
 ])
 def test_planted_mistakes_are_caught(mutant, checks):
     m = _Mutant(**mutant)
