@@ -74,10 +74,14 @@ def cpu_baseline(cfg, inp, seconds: float):
 
     def run(n):
         t0 = time.perf_counter()
-        O.layer_forward(inp.x[:n], inp.W_r, inp.W_gate, inp.W_up, inp.W_down, cfg.k,
-                        b=inp.b, shared=shared, c=cfg.c, renorm=cfg.renorm, lam=cfg.lam,
-                        scoring=cfg.scoring,
-                        gamma=cfg.gamma)
+        if cfg.routing == "expert":
+            O.layer_forward_expert_choice(inp.x[:n], inp.W_r, inp.W_gate, inp.W_up, inp.W_down,
+                                          cfg.k, shared=shared, c=cfg.c, renorm=cfg.renorm,
+                                          lam=cfg.lam, scoring=cfg.scoring)
+        else:
+            O.layer_forward(inp.x[:n], inp.W_r, inp.W_gate, inp.W_up, inp.W_down, cfg.k,
+                            b=inp.b, shared=shared, c=cfg.c, renorm=cfg.renorm, lam=cfg.lam,
+                            scoring=cfg.scoring, gamma=cfg.gamma)
         return time.perf_counter() - t0
 
     # fixed cost (weight upcasts) plus a per-token cost, from two probes
@@ -125,7 +129,7 @@ def main():
     sh = None if sh is None else tuple(t.to(dev) for t in sh)
 
     layer = moe.MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.M, cfg.S, cfg.c, cfg.renorm, dt, dev,
-                         cfg.scoring)
+                         cfg.scoring, cfg.routing)
     out = layer.alloc_outputs(with_bias=b is not None)
 
     def step():
@@ -218,6 +222,7 @@ def main():
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": name, "T": T, "d": d, "E": E, "k": k, "M": M, "S": S,
                    "capacity_factor": cfg.c, "bias": cfg.bias, "scoring": cfg.scoring,
+                   "routing": cfg.routing,
                    "kept_assignments": kept,
                    "dropped_assignments": int(overflow.sum()), "max_load": int(counts.max()),
                    "routing_diagnostics": diag},

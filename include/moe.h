@@ -55,6 +55,12 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* Who chooses: every token its top-k experts, or every expert its top-r tokens. */
+typedef enum {
+  MOE_ROUTE_TOKEN_CHOICE = 0,  /* S_t = TopK_e(g_t + b), capacity C drops the overflow         */
+  MOE_ROUTE_EXPERT_CHOICE = 1  /* expert e takes the r = min(C, T) tokens of largest l_te      */
+} moe_routing;
+
 /* How the router scores the experts from the logits l_te. */
 typedef enum {
   MOE_SCORE_SOFTMAX = 0, /* g_te = softmax_e(l_t)                                        */
@@ -84,6 +90,7 @@ typedef struct {
   int32_t renorm; /* 1: renormalise the chosen gates over S_t; 0: use g_te as is               */
   int32_t dtype;  /* moe_dtype                                                                */
   int32_t scoring; /* moe_scoring                                                             */
+  int32_t routing; /* moe_routing; expert choice runs only through moe_layer_forward          */
 } moe_shape;
 
 /* Short text for a status code (static storage). */
@@ -212,6 +219,12 @@ moe_status moe_balance_stats(const moe_shape* s, const int32_t* n, const double*
  * counts [E] int32 (n_e), overflow [E] int32, f [E], P [E], aux [1], z [1] fp32, diag [4] fp32
  * (routing diagnostics as in moe_balance_stats), and b_new [E] fp32 = the updated bias
  * (requires b; may alias b: it is written after selection).
+ * Expert choice (s->routing == MOE_ROUTE_EXPERT_CHOICE; "深入理解 MoE ..." §9.2, "MoE：条件计算与
+ * 路由" §路由机制的演进): expert e takes the r = min(ceil(c k T / E), T) tokens of largest logit
+ * l_te (c <= 0 reads as 1; equal logits to the lower token index); token t's output sums
+ * w_te E_e(x_t) over the experts that took it, in ascending e, w_te = g_te (renormalised over
+ * those experts when renorm); a token no expert took gets the shared term only. b must be NULL;
+ * topk_idx and topk_w are not written; counts = r, overflow = 0, f_e = n_e / (E r).
  *   ws device workspace of moe_workspace_size(s, MOE_CALL_LAYER) bytes
  */
 moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r, const float* b,

@@ -35,10 +35,11 @@ class Shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("M", ctypes.c_int32), ("S", ctypes.c_int32),
                 ("c", ctypes.c_float), ("renorm", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("scoring", ctypes.c_int32)]
+                ("scoring", ctypes.c_int32), ("routing", ctypes.c_int32)]
 
 
 SCORING = {"softmax": 0, "sigmoid": 1}  # moe_scoring
+ROUTING = {"token": 0, "expert": 1}     # moe_routing: token choice, expert choice
 
 
 _P = ctypes.c_void_p
@@ -110,12 +111,14 @@ def _dtype_code(dt: torch.dtype) -> int:
 
 def make_shape(T: int, d: int, E: int, k: int, M: int, S: int = 0, c: Optional[float] = None,
                renorm: bool = True, dtype: torch.dtype = torch.bfloat16,
-               scoring: str = "softmax") -> Shape:
+               scoring: str = "softmax", routing: str = "token") -> Shape:
     if scoring not in SCORING:
         raise ValueError(f"scoring must be one of {sorted(SCORING)}, got {scoring!r}")
+    if routing not in ROUTING:
+        raise ValueError(f"routing must be one of {sorted(ROUTING)}, got {routing!r}")
     return Shape(int(T), int(d), int(E), int(k), int(M), int(S),
                  float(c) if c is not None else 0.0, 1 if renorm else 0, _dtype_code(dtype),
-                 SCORING[scoring])
+                 SCORING[scoring], ROUTING[routing])
 
 
 def check_shape(s: Shape) -> int:
@@ -282,8 +285,9 @@ class MoELayer:
 
     def __init__(self, T: int, d: int, E: int, k: int, M: int, S: int = 0,
                  c: Optional[float] = None, renorm: bool = True,
-                 dtype: torch.dtype = torch.bfloat16, device="cuda", scoring: str = "softmax"):
-        self.shape = make_shape(T, d, E, k, M, S, c, renorm, dtype, scoring)
+                 dtype: torch.dtype = torch.bfloat16, device="cuda", scoring: str = "softmax",
+                 routing: str = "token"):
+        self.shape = make_shape(T, d, E, k, M, S, c, renorm, dtype, scoring, routing)
         _check(check_shape(self.shape), "MoELayer")
         self.T, self.d, self.E, self.k, self.M, self.S = T, d, E, k, M, S
         self.dtype = dtype
@@ -353,14 +357,14 @@ def moe_set_stage_events(events) -> None:
 
 def moe_layer_forward(x, W_r, W_gate, W_up, W_down, k: int, b=None, shared=None,
                       c: Optional[float] = None, renorm: bool = True, lam: float = 0.01,
-                      gamma: float = 1e-3, scoring: str = "softmax") -> dict:
+                      gamma: float = 1e-3, scoring: str = "softmax", routing: str = "token") -> dict:
     """One call of the whole layer (allocates its workspace; use MoELayer to reuse one)."""
     T, d = x.shape
     E, M, _ = W_gate.shape
     S = 0
     if shared is not None:
         S = shared[0].shape[0] // M
-    layer = MoELayer(T, d, E, k, M, S, c, renorm, x.dtype, x.device, scoring)
+    layer = MoELayer(T, d, E, k, M, S, c, renorm, x.dtype, x.device, scoring, routing)
     return layer.forward(x, W_r, W_gate, W_up, W_down, b, shared, lam, gamma)
 
 

@@ -86,7 +86,84 @@ __global__ __launch_bounds__(256) void combine_kernel(int64_t Tn, int d, int k,
   }
 }
 
+// Expert-choice combine: y_t = sum over the experts e that took token t, in ascending e, of
+// w_te out[row(t, e)] (+ shared_t); w_te = g_te, divided by sum of g_te' over those experts when
+// renormalising. One wave per token: the lanes read the token's row and score of 64 experts at a
+// time, a ballot compacts the taken ones in expert order into the wave's LDS list (and lane 0 sums
+// the gates in that order), then the lanes walk the hidden dimension as in combine_kernel.
+//   row_of, gcol [E][T] (row or -1; score)
+template <typename T>
+__global__ __launch_bounds__(256) void combine_ec_kernel(int64_t Tn, int d, int E, int renorm,
+                                                          const T* __restrict__ out_perm,
+                                                          const int32_t* __restrict__ row_of,
+                                                          const float* __restrict__ gcol,
+                                                          const T* __restrict__ shared_out,
+                                                          T* __restrict__ y) {
+  constexpr int VN = Vec<T>::N;
+  __shared__ int lrow[4][MOE_E_MAX];
+  __shared__ float lw[4][MOE_E_MAX];
+  __shared__ float lden[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (t >= Tn) return;  // whole waves only: no block barrier below
+  int cnt = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    const int row = e < E ? row_of[static_cast<int64_t>(e) * Tn + t] : -1;
+    const float g = e < E ? gcol[static_cast<int64_t>(e) * Tn + t] : 0.f;
+    const unsigned long long m = __ballot(row >= 0);
+    if (row >= 0) {
+      const int pos = cnt + __popcll(m & ((1ull << lane) - 1ull));
+      lrow[wave][pos] = row;
+      lw[wave][pos] = g;
+    }
+    cnt += __popcll(m);
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (lane == 0) {
+    float den = 0.f;
+    for (int i = 0; i < cnt; ++i) den += lw[wave][i];
+    lden[wave] = renorm && den > 0.f ? den : 1.f;
+  }
+  __builtin_amdgcn_wave_barrier();
+  const float den = lden[wave];
+  for (int c = lane * VN; c < d; c += 64 * VN) {
+    float acc[VN];
+#pragma unroll
+    for (int i = 0; i < VN; ++i) acc[i] = 0.f;
+    for (int j = 0; j < cnt; ++j) {
+      const float w = lw[wave][j] / den;
+      float v[VN];
+      Vec<T>::load(out_perm + static_cast<int64_t>(lrow[wave][j]) * d + c, v);
+#pragma unroll
+      for (int i = 0; i < VN; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+    }
+    if (shared_out != nullptr) {
+      float v[VN];
+      Vec<T>::load(shared_out + t * d + c, v);
+#pragma unroll
+      for (int i = 0; i < VN; ++i) acc[i] += v[i];
+    }
+    Vec<T>::store(y + t * d + c, acc);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_combine_ec(int dtype, int64_t T, int d, int E, int renorm, const void* out_perm,
+                             const int32_t* row_of, const float* gcol, const void* shared_out,
+                             void* y, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(cdiv(T, 4)));
+  if (dtype == MOE_F32)
+    hipLaunchKernelGGL(combine_ec_kernel<float>, grid, dim3(256), 0, st, T, d, E, renorm,
+                       static_cast<const float*>(out_perm), row_of, gcol,
+                       static_cast<const float*>(shared_out), static_cast<float*>(y));
+  else
+    hipLaunchKernelGGL(combine_ec_kernel<bf16_t>, grid, dim3(256), 0, st, T, d, E, renorm,
+                       static_cast<const bf16_t*>(out_perm), row_of, gcol,
+                       static_cast<const bf16_t*>(shared_out), static_cast<bf16_t*>(y));
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(int dtype, int64_t T, int d, int k, const void* out_perm,
                           const int32_t* inv_perm, const float* topk_w, const void* shared_out,

@@ -288,9 +288,129 @@ __global__ void shared_table_kernel(int64_t T, int BM, int32_t* __restrict__ off
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Expert-choice selection ("深入理解 MoE (混合专家模型)：稀疏激活与高效扩展" §9.2: every expert
+// picks its top tokens by its score column; "MoE：条件计算与路由" §路由机制的演进): one block per
+// expert takes the r tokens of largest logit, equal logits to the lower token index, and lays
+// them out in ascending token order at rows [e r, (e + 1) r).
+//   The r-th largest key is found by a 4-pass MSB-first radix select over order-preserving
+//   uint32 keys (8 bits a pass, LDS histograms); then the tokens are walked in chunks of 1024
+//   in index order with two block scans per chunk: the rank among keys equal to the threshold
+//   (ties: the lowest indices are taken) and the row of each taken token.
+//   lcol [E][T] logits; perm_token [E r]; row_of [E][T] (row or -1); offsets [E+1]; counts,
+//   overflow [E].
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t order_key(float v) {
+  if (v == 0.f) v = 0.f;  // -0 and +0 compare equal: one key
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// exclusive prefix sum of v over the 1024 threads of the block, and the block total
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int c = wsum[w];
+      wsum[w] = acc;
+      acc += c;
+    }
+    wsum[16] = acc;
+  }
+  __syncthreads();
+  const int r = wsum[wave] + x - v;
+  total = wsum[16];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(1024) void ec_select_kernel(int64_t T, int E, int r,
+                                                          const float* __restrict__ lcol,
+                                                          int32_t* __restrict__ perm_token,
+                                                          int32_t* __restrict__ row_of,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ overflow) {
+  __shared__ int hist[256];
+  __shared__ int wsum[17];
+  __shared__ int sel[2];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const float* col = lcol + static_cast<int64_t>(e) * T;
+  // radix select of the r-th largest key
+  uint32_t prefix = 0, pmask = 0;
+  int remaining = r;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int64_t t = tid; t < T; t += 1024) {
+      const uint32_t key = order_key(col[t]);
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int above = 0, bin = 255;
+      for (; bin > 0; --bin) {
+        if (above + hist[bin] >= remaining) break;
+        above += hist[bin];
+      }
+      sel[0] = bin;
+      sel[1] = remaining - above;
+    }
+    __syncthreads();
+    prefix |= static_cast<uint32_t>(sel[0]) << shift;
+    pmask |= 255u << shift;
+    remaining = sel[1];
+    __syncthreads();
+  }
+  // prefix is the threshold key; `remaining` tokens equal to it are taken, lowest indices first
+  int eq_carry = 0, row_carry = 0;
+  for (int64_t base = 0; base < T; base += 1024) {
+    const int64_t t = base + tid;
+    const uint32_t key = t < T ? order_key(col[t]) : 0u;
+    const int eq = (t < T && key == prefix) ? 1 : 0;
+    int eq_tot = 0;
+    const int eq_rank = eq_carry + block_excl_scan(eq, wsum, eq_tot);
+    const int take = (t < T && (key > prefix || (eq && eq_rank < remaining))) ? 1 : 0;
+    int take_tot = 0;
+    const int row = row_carry + block_excl_scan(take, wsum, take_tot);
+    if (t < T) {
+      const bool kept = take && row < r;  // exactly r are taken; the bound guards the row buffer
+      const int out = kept ? e * r + row : -1;
+      row_of[static_cast<int64_t>(e) * T + t] = out;
+      if (kept) perm_token[out] = static_cast<int32_t>(t);
+    }
+    eq_carry += eq_tot;
+    row_carry += take_tot;
+  }
+  if (tid == 0) {
+    offsets[e] = e * r;
+    if (e == E - 1) offsets[E] = E * r;
+    counts[e] = r;
+    overflow[e] = 0;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_shared_table(int64_t T, int BM, int32_t* offsets, int32_t* tile_off,
+hipError_t launch_ec_select(int64_t T, int E, int r, const float* lcol, int32_t* perm_token,
+                            int32_t* row_of, int32_t* offsets, int32_t* counts,
+                            int32_t* overflow, hipStream_t st) {
+  hipLaunchKernelGGL(ec_select_kernel, dim3(E), dim3(1024), 0, st, T, E, r, lcol, perm_token,
+                     row_of, offsets, counts, overflow);
+  return hipGetLastError();
+}
+
+hipError_t launch_shared_table(
+int64_t T, int BM, int32_t* offsets, int32_t* tile_off,
                                hipStream_t st) {
   hipLaunchKernelGGL(shared_table_kernel, dim3(1), dim3(64), 0, st, T, BM, offsets, tile_off);
   return hipGetLastError();

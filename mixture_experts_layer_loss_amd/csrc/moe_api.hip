@@ -52,8 +52,16 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 int elem_bytes(const moe_shape* s) { return s->dtype == MOE_F32 ? 4 : 2; }
+bool expert_choice(const moe_shape* s);
+int64_t ec_tokens(const moe_shape* s);
+// denominator of f_e: k T assignments (token choice) or E r (expert choice)
+double stats_fden(const moe_shape* s) {
+  return expert_choice(s) ? static_cast<double>(ec_tokens(s)) * s->E
+                          : static_cast<double>(s->k) * static_cast<double>(s->T);
+}
 int route_flags(const moe_shape* s) {
-  return (s->renorm ? kRouteRenorm : 0) | (s->scoring == MOE_SCORE_SIGMOID ? kRouteSigmoid : 0);
+  return (s->renorm ? kRouteRenorm : 0) | (s->scoring == MOE_SCORE_SIGMOID ? kRouteSigmoid : 0) |
+         (s->routing == MOE_ROUTE_EXPERT_CHOICE ? kRouteExpertChoice : 0);
 }
 int gemm_bm(const moe_shape* s) { return s->dtype == MOE_F32 ? kGemmF32BM : kGemmBM; }
 int64_t nblocks(const moe_shape* s) { return cdiv(s->T, kRouteTokens); }
@@ -80,8 +88,19 @@ int64_t capacity_of(const moe_shape* s) {
       ceil(((static_cast<double>(s->c) * s->k) * static_cast<double>(s->T)) / s->E));
 }
 
-// Rows the routed-expert buffers need: every assignment, or at most C per expert.
+bool expert_choice(const moe_shape* s) { return s->routing == MOE_ROUTE_EXPERT_CHOICE; }
+
+// Tokens each expert takes under expert choice: C = ceil(c k T / E), c <= 0 read as 1, at most T.
+int64_t ec_tokens(const moe_shape* s) {
+  const double c = s->c > 0.0f ? static_cast<double>(s->c) : 1.0;
+  const int64_t C = static_cast<int64_t>(ceil(((c * s->k) * static_cast<double>(s->T)) / s->E));
+  return C < s->T ? C : s->T;
+}
+
+// Rows the routed-expert buffers need: every assignment, or at most C per expert (expert choice:
+// exactly r per expert).
 int64_t routed_rows(const moe_shape* s) {
+  if (expert_choice(s)) return ec_tokens(s) * s->E;
   const int64_t P = s->T * s->k;
   const int64_t C = capacity_of(s);
   return C >= 0 && C * s->E < P ? C * s->E : P;
@@ -122,6 +141,8 @@ struct LayerPlan {
   float* topk_w;
   double *gsum, *lse2sum, *hsum;
   void *h, *out_perm, *h_sh, *sh;
+  float* cols;      // expert choice: [2][E][T] logits and scores
+  int32_t* row_of;  // expert choice: [E][T] row of (t, e) or -1
 };
 LayerPlan plan_layer(Carve& c, const moe_shape* s) {
   const size_t P = static_cast<size_t>(s->T) * s->k;
@@ -151,6 +172,13 @@ LayerPlan plan_layer(Carve& c, const moe_shape* s) {
     p.sh = c.take<unsigned char>(static_cast<size_t>(s->T) * s->d * eb);
   } else {
     p.h_sh = p.sh = nullptr;
+  }
+  if (expert_choice(s)) {
+    p.cols = c.take<float>(2 * static_cast<size_t>(s->E) * s->T);
+    p.row_of = c.take<int32_t>(static_cast<size_t>(s->E) * s->T);
+  } else {
+    p.cols = nullptr;
+    p.row_of = nullptr;
   }
   return p;
 }
@@ -188,12 +216,15 @@ moe_status moe_check_shape(const moe_shape* s) {
   if (isnan(s->c) || (s->renorm != 0 && s->renorm != 1)) return MOE_ERR_INVALID_ARGUMENT;
   if (s->scoring != MOE_SCORE_SOFTMAX && s->scoring != MOE_SCORE_SIGMOID)
     return MOE_ERR_INVALID_ARGUMENT;
+  if (s->routing != MOE_ROUTE_TOKEN_CHOICE && s->routing != MOE_ROUTE_EXPERT_CHOICE)
+    return MOE_ERR_INVALID_ARGUMENT;
   if (s->k > s->E) return MOE_ERR_INVALID_ARGUMENT;
   if (s->E > MOE_E_MAX || s->k > MOE_K_MAX) return MOE_ERR_UNSUPPORTED;
   const int vec = s->dtype == MOE_F32 ? 4 : 8;  // elements per 16-byte chunk
   if (s->d % vec != 0 || s->M % vec != 0) return MOE_ERR_INVALID_ARGUMENT;
   // row indices are int32
   if (s->T * static_cast<int64_t>(s->k) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (expert_choice(s) && s->T * static_cast<int64_t>(s->E) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(s->S) * s->M > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -221,6 +252,7 @@ moe_status moe_route(const moe_shape* s, const void* x, const void* W_r, const f
                      double* hsum, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = moe_check_shape(s);
   if (st != MOE_OK) return st;
+  if (expert_choice(s)) return MOE_ERR_UNSUPPORTED;  // runs only through the layer call
   if (!x || !W_r || !topk_idx || !topk_w || !n || !gsum || !lse2sum)
     return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(x) || !aligned16(W_r) || !aligned16(topk_idx) || !aligned16(topk_w))
@@ -230,7 +262,7 @@ moe_status moe_route(const moe_shape* s, const void* x, const void* W_r, const f
   Carve c(ws);
   RoutePlan p = plan_route(c, s);
   hipError_t e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s), x, W_r, b, topk_idx,
-                              topk_w, p.hist, p.gpart, p.lpart, p.hpart, hs);
+                              topk_w, p.hist, p.gpart, p.lpart, p.hpart, nullptr, hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = launch_scan(s->T, s->E, -1, static_cast<int>(route_blocks(s)), p.hist, p.gpart, p.lpart,
                   p.hpart, nullptr, n, gsum, lse2sum, hsum, nullptr, nullptr, nullptr, nullptr,
@@ -243,6 +275,7 @@ moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_i
                         int32_t* overflow, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = moe_check_shape(s);
   if (st != MOE_OK) return st;
+  if (expert_choice(s)) return MOE_ERR_UNSUPPORTED;  // runs only through the layer call
   if (!topk_idx || !perm_token || !inv_perm || !offsets || !counts || !overflow)
     return MOE_ERR_INVALID_ARGUMENT;
   if (x_perm != nullptr && (!x || !aligned16(x) || !aligned16(x_perm)))
@@ -297,6 +330,7 @@ moe_status moe_combine(const moe_shape* s, const void* out_perm, const int32_t* 
                        const float* topk_w, const void* shared_out, void* y, void* stream) {
   moe_status st = moe_check_shape(s);
   if (st != MOE_OK) return st;
+  if (expert_choice(s)) return MOE_ERR_UNSUPPORTED;  // runs only through the layer call
   if (!out_perm || !inv_perm || !topk_w || !y) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(out_perm) || !aligned16(y) || (shared_out && !aligned16(shared_out)))
     return MOE_ERR_INVALID_ARGUMENT;
@@ -314,8 +348,8 @@ moe_status moe_balance_stats(const moe_shape* s, const int32_t* n, const double*
   if (diag != nullptr && hsum == nullptr) return MOE_ERR_INVALID_ARGUMENT;
   if ((b == nullptr) != (b_new == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
   if (isnan(lambda) || isnan(gamma)) return MOE_ERR_INVALID_ARGUMENT;
-  return hip_status(launch_stats(s->T, s->E, s->k, n, gsum, lse2sum, hsum, lambda, f, P, aux, z,
-                                 diag, b, b_new, gamma, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_stats(s->T, s->E, stats_fden(s), n, gsum, lse2sum, hsum, lambda, f, P,
+                                 aux, z, diag, b, b_new, gamma, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r, const float* b,
@@ -329,6 +363,9 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
   if (!x || !W_r || !W_gate || !W_up || !W_down || !y) return MOE_ERR_INVALID_ARGUMENT;
   if (s->S > 0 && (!Ws_gate || !Ws_up || !Ws_down)) return MOE_ERR_INVALID_ARGUMENT;
   if (b_new != nullptr && b == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  // the load-balancing bias is a token-choice device: a per-expert shift cannot change which
+  // tokens an expert ranks highest
+  if (expert_choice(s) && b != nullptr) return MOE_ERR_INVALID_ARGUMENT;
   if (isnan(lambda) || isnan(gamma)) return MOE_ERR_INVALID_ARGUMENT;
   const void* tensors[] = {x, W_r, W_gate, W_up, W_down, y, topk_idx, topk_w};
   for (const void* t : tensors)
@@ -353,15 +390,27 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
 
   mark_stage(0, hs);
   hipError_t e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s), x, W_r, b, idx, w,
-                              p.r.hist, p.r.gpart, p.r.lpart, p.r.hpart, hs);
+                              p.r.hist, p.r.gpart, p.r.lpart, p.r.hpart, p.cols, hs);
   mark_stage(1, hs);
-  if (e == hipSuccess)
-    e = launch_scan(s->T, s->E, C, nblk, p.r.hist, p.r.gpart, p.r.lpart, p.r.hpart, p.block_base,
-                    n, p.gsum, p.lse2sum, p.hsum, p.kept, ovf, p.offsets, p.tile_off, BM, hs);
-  // placement only: the gate/up GEMM gathers its rows from x through perm_token
-  if (e == hipSuccess)
-    e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx, route_block_tokens(s->dtype, s->E),
-                       p.block_base, p.offsets, nullptr, p.perm_token, p.inv_perm, hs);
+  if (expert_choice(s)) {
+    // the statistics partials, then every expert's top-r tokens and their tile tables
+    if (e == hipSuccess)
+      e = launch_scan(s->T, s->E, -1, nblk, p.r.hist, p.r.gpart, p.r.lpart, p.r.hpart, nullptr,
+                      nullptr, p.gsum, p.lse2sum, p.hsum, nullptr, nullptr, nullptr, nullptr, BM,
+                      hs);
+    if (e == hipSuccess)
+      e = launch_ec_select(s->T, s->E, static_cast<int>(ec_tokens(s)), p.cols, p.perm_token,
+                           p.row_of, p.offsets, n, ovf, hs);
+    if (e == hipSuccess) e = launch_schedule(s->E, p.offsets, p.tile_off, BM, hs);
+  } else {
+    if (e == hipSuccess)
+      e = launch_scan(s->T, s->E, C, nblk, p.r.hist, p.r.gpart, p.r.lpart, p.r.hpart, p.block_base,
+                      n, p.gsum, p.lse2sum, p.hsum, p.kept, ovf, p.offsets, p.tile_off, BM, hs);
+    // placement only: the gate/up GEMM gathers its rows from x through perm_token
+    if (e == hipSuccess)
+      e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx, route_block_tokens(s->dtype, s->E),
+                         p.block_base, p.offsets, nullptr, p.perm_token, p.inv_perm, hs);
+  }
   mark_stage(2, hs);
   if (e == hipSuccess)
     e = launch_gemm_up(s->dtype, s->E, s->d, s->M, x, p.perm_token, p.offsets, p.tile_off,
@@ -383,12 +432,17 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
                            p.h_sh, p.sh, hs);
   }
   mark_stage(5, hs);
-  if (e == hipSuccess)
+  if (e == hipSuccess && expert_choice(s))
+    e = launch_combine_ec(s->dtype, s->T, s->d, s->E, s->renorm, p.out_perm, p.row_of,
+                          p.cols + static_cast<size_t>(s->E) * s->T, s->S > 0 ? p.sh : nullptr, y,
+                          hs);
+  else if (e == hipSuccess)
     e = launch_combine(s->dtype, s->T, s->d, s->k, p.out_perm, p.inv_perm, w,
                        s->S > 0 ? p.sh : nullptr, y, hs);
   mark_stage(6, hs);
   if (e == hipSuccess && (f || P || aux || z || diag || b_new))
-    e = launch_stats(s->T, s->E, s->k, n, p.gsum, p.lse2sum, p.hsum, lambda, f, P, aux, z, diag,
+    e = launch_stats(s->T, s->E, stats_fden(s), n, p.gsum, p.lse2sum, p.hsum, lambda, f, P, aux, z,
+                     diag,
                      b_new ? b : nullptr, b_new, gamma, hs);
   mark_stage(7, hs);
   return hip_status(e);

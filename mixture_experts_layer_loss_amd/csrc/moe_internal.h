@@ -48,15 +48,18 @@ __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 
 // block of this many tokens (a divisor of kRouteTokens).
 int route_block_tokens(int dtype, int E);
 
-// Router flags: renormalise the chosen gates; score the experts with a sigmoid (else softmax).
-constexpr int kRouteRenorm = 1, kRouteSigmoid = 2;
+// Router flags: renormalise the chosen gates; score the experts with a sigmoid (else softmax);
+// expert choice (no per-token top-k: the logits and scores leave as [E][T] columns instead).
+constexpr int kRouteRenorm = 1, kRouteSigmoid = 2, kRouteExpertChoice = 4;
 
 // Router: logits, softmax/LSE, biased top-k, gates, per-block partial statistics and histograms.
 //   hist  [nblk, E] int32, gpart [nblk, E] fp32, lpart [nblk] fp32 (sum of lse^2),
 //   hpart [nblk] fp32 (sum of the per-token routing entropies), nblk = ceil(T / route_block_tokens)
+//   cols [2][E][T] fp32 (expert choice only, else NULL): logits, then scores, expert-major
 hipError_t launch_route(int dtype, int64_t T, int d, int E, int k, int flags, const void* x,
                         const void* W_r, const float* b, int32_t* topk_idx, float* topk_w,
-                        int32_t* hist, float* gpart, float* lpart, float* hpart, hipStream_t st);
+                        int32_t* hist, float* gpart, float* lpart, float* hpart, float* cols,
+                        hipStream_t st);
 
 // Per-block expert histograms of a given selection (for a stand-alone dispatch).
 hipError_t launch_count(int64_t T, int E, int k, const int32_t* topk_idx, int32_t* hist,
@@ -80,6 +83,19 @@ hipError_t launch_scatter(int64_t T, int d, int E, int k, int64_t C, int elem_by
                           const void* x, const int32_t* topk_idx, int hist_block_tokens,
                           const int32_t* block_base, const int32_t* offsets, void* x_perm,
                           int32_t* perm_token, int32_t* inv_perm, hipStream_t st);
+
+// Expert-choice selection: expert e takes the r tokens of largest lcol[e][t] (ties: lower t) at
+// rows e r .. e r + r - 1 in ascending token order; row_of [E][T] = row or -1; offsets [E+1] = e r;
+// counts = r, overflow = 0.
+hipError_t launch_ec_select(int64_t T, int E, int r, const float* lcol, int32_t* perm_token,
+                            int32_t* row_of, int32_t* offsets, int32_t* counts,
+                            int32_t* overflow, hipStream_t st);
+
+// Expert-choice combine: y_t = sum over experts e (ascending) with row_of[e][t] >= 0 of
+// w_te out_perm[row] + shared_t, w_te = gcol[e][t] (renormalised over those experts if renorm).
+hipError_t launch_combine_ec(int dtype, int64_t T, int d, int E, int renorm, const void* out_perm,
+                             const int32_t* row_of, const float* gcol, const void* shared_out,
+                             void* y, hipStream_t st);
 
 // Tile tables [3 (groups+1)] of a grouped GEMM from device row offsets (stand-alone expert FFN).
 hipError_t launch_schedule(int groups, const int32_t* offsets, int32_t* tile_off, int BM,
@@ -107,8 +123,9 @@ hipError_t launch_combine(int dtype, int64_t T, int d, int k, const void* out_pe
                           void* y, hipStream_t st);
 
 // f, P, aux, z and the bias step from reduced route statistics.
-// diag (may be NULL) [4]: routing entropy (hsum / T), load Gini, max/mean load, importance CV^2.
-hipError_t launch_stats(int64_t T, int E, int k, const int32_t* n, const double* gsum,
+// fden: the f_e denominator (k T; E r for expert choice). diag (may be NULL) [4]: routing entropy
+// (hsum / T), load Gini, max/mean load, importance CV^2.
+hipError_t launch_stats(int64_t T, int E, double fden, const int32_t* n, const double* gsum,
                         const double* lse2sum, const double* hsum, float lambda, float* f,
                         float* P, float* aux, float* z, float* diag, const float* b, float* b_new,
                         float gamma, hipStream_t st);

@@ -68,8 +68,8 @@ __device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, in
                              int flags, const float* __restrict__ b,
                              int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
                              int32_t* __restrict__ hist, float* __restrict__ gpart,
-                             float* __restrict__ lpart, float* __restrict__ hpart, int* hcnt,
-                             float* lsq, float* hsq) {
+                             float* __restrict__ lpart, float* __restrict__ hpart,
+                             float* __restrict__ cols, int* hcnt, float* lsq, float* hsq) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int tpw = TB / nw;
   for (int e = threadIdx.x; e < E; e += blockDim.x) hcnt[e] = 0;
@@ -106,6 +106,7 @@ __device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, in
         ti[j] = 0;
       }
       const bool sig = (flags & kRouteSigmoid) != 0;
+      const bool ec = (flags & kRouteExpertChoice) != 0;
       float ssum = 0.f;  // sigmoid: sum of the scores over the experts (the pad adds 0)
       float hacc = 0.f;  // entropy term: softmax sum g (l - lse); sigmoid sum s ln s
       for (int e = 0; e < E4; e += 4) {
@@ -132,7 +133,12 @@ __device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, in
         for (int q = 0; q < 4; ++q) {
           const int ee = e + q;
           if (ee < E) {
-            topk_insert<KM>(b != nullptr ? g4[q] + b[ee] : g4[q], ee, tv, ti);
+            if (ec) {  // expert choice: columns of logits and scores for the per-expert selection
+              cols[static_cast<int64_t>(ee) * T + t] = l4[q];
+              cols[(static_cast<int64_t>(E) + ee) * T + t] = g4[q];
+            } else {
+              topk_insert<KM>(b != nullptr ? g4[q] + b[ee] : g4[q], ee, tv, ti);
+            }
             hacc += sig ? (g4[q] > 0.f ? g4[q] * logf(g4[q]) : 0.f) : g4[q] * (l4[q] - lse);
           }
         }
@@ -145,7 +151,7 @@ __device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, in
         if (j < k) wsum += row[ti[j]];
 #pragma unroll
       for (int j = 0; j < KM; ++j) {
-        if (j < k) {
+        if (j < k && !ec) {
           const float gj = row[ti[j]];
           topk_idx[t * k + j] = ti[j];
           topk_w[t * k + j] = (flags & kRouteRenorm) ? gj / wsum : gj;
@@ -196,8 +202,9 @@ __device__ void route_tokens_split(float* L, int Ls, int64_t t0, int64_t T, int 
                                    int flags, const float* __restrict__ b,
                                    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
                                    int32_t* __restrict__ hist, float* __restrict__ gpart,
-                                   float* __restrict__ lpart, float* __restrict__ hpart, int* hcnt,
-                                   float* lsq, float* hsq, float* part, float* part2,
+                                   float* __restrict__ lpart, float* __restrict__ hpart,
+                                   float* __restrict__ cols, int* hcnt, float* lsq, float* hsq,
+                                   float* part, float* part2,
                                    float* xv, int* xi) {
   constexpr int TB = 64, NW = 8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -235,6 +242,7 @@ __device__ void route_tokens_split(float* L, int Ls, int64_t t0, int64_t T, int 
   const float lse = m + logf(sum);
   // scores of the slice, written back over the logits, and the slice's sorted top-KM
   const bool sig = (flags & kRouteSigmoid) != 0;
+  const bool ec = (flags & kRouteExpertChoice) != 0;
   float ssum = 0.f;
   float hacc = 0.f;  // entropy term of the slice: softmax sum g (l - lse); sigmoid sum s ln s
   float tv[KM];
@@ -268,7 +276,14 @@ __device__ void route_tokens_split(float* L, int Ls, int64_t t0, int64_t T, int 
     for (int q = 0; q < 4; ++q) {
       const int ee = e + q;
       if (ee < E) {
-        topk_insert<KM>(b != nullptr ? g4[q] + b[ee] : g4[q], ee, tv, ti);
+        if (ec) {  // expert choice: columns of logits and scores for the per-expert selection
+          if (live) {
+            cols[static_cast<int64_t>(ee) * T + t] = l4[q];
+            cols[(static_cast<int64_t>(E) + ee) * T + t] = g4[q];
+          }
+        } else {
+          topk_insert<KM>(b != nullptr ? g4[q] + b[ee] : g4[q], ee, tv, ti);
+        }
         hacc += sig ? (g4[q] > 0.f ? g4[q] * logf(g4[q]) : 0.f) : g4[q] * (l4[q] - lse);
       }
     }
@@ -299,7 +314,7 @@ __device__ void route_tokens_split(float* L, int Ls, int64_t t0, int64_t T, int 
   part[wave * TB + tl] = ssum;
   part2[wave * TB + tl] = hacc;
   __syncthreads();
-  if (wave == 0 && live) {
+  if (wave == 0 && live && !ec) {
     float wsum = 0.f;
 #pragma unroll
     for (int j = 0; j < KM; ++j)
@@ -380,7 +395,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ b,
     int64_t T, int d, int E, int k, int flags, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ hist, float* __restrict__ gpart,
-    float* __restrict__ lpart, float* __restrict__ hpart) {
+    float* __restrict__ lpart, float* __restrict__ hpart, float* __restrict__ cols) {
   constexpr int TB = 16 * MB;
   constexpr int NW = kRouteThreads / 64;
   constexpr int NWK = NW / NG;                // waves splitting K within an expert group
@@ -479,7 +494,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
   __syncthreads();
 #define MOE_CALL(KM) \
   route_tokens<KM>(L, kLogitsStride, TB, t0, T, E, k, flags, b, topk_idx, topk_w, hist, gpart, \
-                   lpart, hpart, hcnt, lsq, hsq)
+                   lpart, hpart, cols, hcnt, lsq, hsq)
   MOE_ROUTE_TOKENS_KM(MOE_CALL);
 #undef MOE_CALL
 }
@@ -491,7 +506,7 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ W, const float* __restrict__ b,
     int64_t T, int d, int E, int k, int flags, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ hist, float* __restrict__ gpart,
-    float* __restrict__ lpart, float* __restrict__ hpart) {
+    float* __restrict__ lpart, float* __restrict__ hpart, float* __restrict__ cols) {
   __shared__ float L[RT * kLogitsStride];
   __shared__ int hcnt[MOE_E_MAX];
   __shared__ float lsq[RT];
@@ -514,7 +529,7 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
   __syncthreads();
 #define MOE_CALL(KM) \
   route_tokens<KM>(L, kLogitsStride, RT, t0, T, E, k, flags, b, topk_idx, topk_w, hist, gpart, \
-                   lpart, hpart, hcnt, lsq, hsq)
+                   lpart, hpart, cols, hcnt, lsq, hsq)
   MOE_ROUTE_TOKENS_KM(MOE_CALL);
 #undef MOE_CALL
 }
@@ -536,7 +551,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ b,
     int64_t T, int d, int E, int k, int flags, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ hist, float* __restrict__ gpart,
-    float* __restrict__ lpart, float* __restrict__ hpart) {
+    float* __restrict__ lpart, float* __restrict__ hpart, float* __restrict__ cols) {
   constexpr int TB = 64;
   constexpr int ROWS = TB + 16 * NEB;                 // x rows then W_r rows of a stage
   constexpr int STAGE = ROWS * kSKP;                  // bf16 elements
@@ -658,10 +673,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
 #define MOE_CALL(KM)                                                                           \
   if constexpr (SPLIT)                                                                         \
     route_tokens_split<KM>(L, kLogitsStride, t0, T, E, k, flags, b, topk_idx, topk_w, hist,     \
-                           gpart, lpart, hpart, hcnt, lsq, hsq, part, part2, xv, xi);                             \
+                           gpart, lpart, hpart, cols, hcnt, lsq, hsq, part, part2, xv, xi);                             \
   else                                                                                         \
     route_tokens<KM>(L, kLogitsStride, TB, t0, T, E, k, flags, b, topk_idx, topk_w, hist, gpart, \
-                     lpart, hpart, hcnt, lsq, hsq)
+                     lpart, hpart, cols, hcnt, lsq, hsq)
   MOE_ROUTE_TOKENS_KM(MOE_CALL);
 #undef MOE_CALL
 }
@@ -669,29 +684,31 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
 template <int NEB>
 hipError_t launch_bf16_lds(hipStream_t st, const void* x, const void* W, const float* b, int64_t T,
                            int d, int E, int k, int flags, int32_t* topk_idx, float* topk_w,
-                           int32_t* hist, float* gpart, float* lpart, float* hpart) {
+                           int32_t* hist, float* gpart, float* lpart, float* hpart,
+                           float* cols) {
   // short lists over at most 128 experts stay one lane per token (cheaper than the merge rounds)
   const dim3 grid(static_cast<unsigned>(cdiv(T, 64)));
   if (NEB <= 8 && k <= 2)
     hipLaunchKernelGGL((route_bf16_lds_kernel<NEB, false>), grid, dim3(kRouteThreads), 0, st,
                        static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W), b, T, d, E,
-                       k, flags, topk_idx, topk_w, hist, gpart, lpart, hpart);
+                       k, flags, topk_idx, topk_w, hist, gpart, lpart, hpart, cols);
   else
     hipLaunchKernelGGL((route_bf16_lds_kernel<NEB, true>), grid, dim3(kRouteThreads), 0, st,
                        static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W), b, T, d, E,
-                       k, flags, topk_idx, topk_w, hist, gpart, lpart, hpart);
+                       k, flags, topk_idx, topk_w, hist, gpart, lpart, hpart, cols);
   return hipGetLastError();
 }
 
 template <int MB, int NEB, int NG>
 hipError_t launch_bf16(hipStream_t st, const void* x, const void* W, const float* b,
                        int64_t T, int d, int E, int k, int flags, int32_t* topk_idx,
-                       float* topk_w, int32_t* hist, float* gpart, float* lpart, float* hpart) {
+                       float* topk_w, int32_t* hist, float* gpart, float* lpart, float* hpart,
+                           float* cols) {
   const int64_t nblk = cdiv(T, 16 * MB);
   hipLaunchKernelGGL((route_bf16_kernel<MB, NEB, NG>), dim3(static_cast<unsigned>(nblk)),
                      dim3(kRouteThreads), 0, st,
                      static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W), b, T, d, E, k,
-                     flags, topk_idx, topk_w, hist, gpart, lpart, hpart);
+                     flags, topk_idx, topk_w, hist, gpart, lpart, hpart, cols);
   return hipGetLastError();
 }
 
@@ -702,24 +719,24 @@ int route_block_tokens(int dtype, int E) { return dtype == MOE_F32 ? RT : (E <= 
 hipError_t launch_route(int dtype, int64_t T, int d, int E, int k, int flags, const void* x,
                         const void* W_r, const float* b, int32_t* topk_idx, float* topk_w,
                         int32_t* hist, float* gpart, float* lpart, float* hpart,
-                        hipStream_t st) {
+                        float* cols, hipStream_t st) {
   if (dtype == MOE_F32) {
     const int64_t nblk = cdiv(T, RT);
     hipLaunchKernelGGL(route_f32_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
                        static_cast<const float*>(x), static_cast<const float*>(W_r), b, T, d, E,
-                       k, flags, topk_idx, topk_w, hist, gpart, lpart, hpart);
+                       k, flags, topk_idx, topk_w, hist, gpart, lpart, hpart, cols);
     return hipGetLastError();
   }
   const int neb = static_cast<int>(cdiv(E, 16));
 #define MOE_ROUTE_CASE(N)                                                                   \
   case N:                                                                                   \
     return launch_bf16_lds<N>(st, x, W_r, b, T, d, E, k, flags, topk_idx, topk_w, hist, gpart, \
-                              lpart, hpart);
+                              lpart, hpart, cols);
   // up to 16 experts: 16-token blocks with the hidden dimension split over the waves (more blocks
   // in flight); more: 64-token blocks with W_r shared through LDS
   if (E <= 16)
     return launch_bf16<1, 1, 1>(st, x, W_r, b, T, d, E, k, flags, topk_idx, topk_w, hist, gpart,
-                                lpart, hpart);
+                                lpart, hpart, cols);
   switch (neb) {
     MOE_ROUTE_CASE(2) MOE_ROUTE_CASE(3) MOE_ROUTE_CASE(4) MOE_ROUTE_CASE(5) MOE_ROUTE_CASE(6)
     MOE_ROUTE_CASE(7) MOE_ROUTE_CASE(8) MOE_ROUTE_CASE(9) MOE_ROUTE_CASE(10) MOE_ROUTE_CASE(11)

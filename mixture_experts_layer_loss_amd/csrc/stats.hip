@@ -1,5 +1,6 @@
 // Balance statistics and the loss-free-balancing bias step, from the reduced route statistics:
-//   f_e = n_e / (k T), P_e = gsum_e / T, aux = lambda E sum_e f_e P_e
+//   f_e = n_e / (k T) (token choice; expert choice: n_e / (E r)), P_e = gsum_e / T,
+//   aux = lambda E sum_e f_e P_e
 //   ("MoE：条件计算与路由" §原理与演进; "深入理解 MoE (混合专家模型)：稀疏激活与高效扩展" §4.2.1;
 //   "MOE大模型对比篇" §2.1), z = lse2sum / T ("MOE大模型对比篇" §2.2), and
 //   b_e <- b_e + gamma * sign(k T / E - n_e) ("MoE：条件计算与路由" §无辅助损失负载均衡（ALF-LB）).
@@ -16,7 +17,7 @@ namespace moe {
 namespace {
 
 __global__ __launch_bounds__(256) void stats_kernel(
-    int64_t T, int E, int k, const int32_t* __restrict__ n, const double* __restrict__ gsum,
+    int64_t T, int E, double fden, const int32_t* __restrict__ n, const double* __restrict__ gsum,
     const double* __restrict__ lse2sum, const double* __restrict__ hsum, float lambda,
     float* __restrict__ f, float* __restrict__ P, float* __restrict__ aux, float* __restrict__ z,
     float* __restrict__ diag, const float* __restrict__ b, float* __restrict__ b_new,
@@ -47,17 +48,19 @@ __global__ __launch_bounds__(256) void stats_kernel(
     __syncthreads();
     return r;
   };
+  const long long ne = e < E ? n[e] : 0;
   double prod = 0.0;
   float bnew = 0.f;
   if (e < E) {
-    const double fe = static_cast<double>(n[e]) / (static_cast<double>(k) * static_cast<double>(T));
+    const double fe = static_cast<double>(n[e]) / fden;
     const double pe = gsum[e] / static_cast<double>(T);
     prod = fe * pe;
     if (f != nullptr) f[e] = static_cast<float>(fe);
     if (P != nullptr) P[e] = static_cast<float>(pe);
     if (b != nullptr) {
-      const int64_t kt = static_cast<int64_t>(k) * T, ne = static_cast<int64_t>(n[e]) * E;
-      const float sgn = kt > ne ? 1.f : (kt < ne ? -1.f : 0.f);
+      // sign(k T / E - n_e) as an integer comparison of k T and n_e E (fden = k T here)
+      const int64_t kt = static_cast<int64_t>(fden), nE = static_cast<int64_t>(n[e]) * E;
+      const float sgn = kt > nE ? 1.f : (kt < nE ? -1.f : 0.f);
       bnew = b[e] + gamma * sgn;
     }
   }
@@ -71,7 +74,6 @@ __global__ __launch_bounds__(256) void stats_kernel(
   if (diag == nullptr) return;
   // Gini: sum over pairs of |n_i - n_j| (integers), over 2 E sum_e n_e
   long long pairs = 0;
-  const long long ne = e < E ? n[e] : 0;
   if (e < E)
     for (int j = 0; j < E; ++j) {
       const long long d = ne - static_cast<long long>(n[j]);
@@ -95,11 +97,11 @@ __global__ __launch_bounds__(256) void stats_kernel(
 
 }  // namespace
 
-hipError_t launch_stats(int64_t T, int E, int k, const int32_t* n, const double* gsum,
+hipError_t launch_stats(int64_t T, int E, double fden, const int32_t* n, const double* gsum,
                         const double* lse2sum, const double* hsum, float lambda, float* f,
                         float* P, float* aux, float* z, float* diag, const float* b, float* b_new,
                         float gamma, hipStream_t st) {
-  hipLaunchKernelGGL(stats_kernel, dim3(1), dim3(256), 0, st, T, E, k, n, gsum, lse2sum, hsum,
+  hipLaunchKernelGGL(stats_kernel, dim3(1), dim3(256), 0, st, T, E, fden, n, gsum, lse2sum, hsum,
                      lambda, f, P, aux, z, diag, b, b_new, gamma);
   return hipGetLastError();
 }

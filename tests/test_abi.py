@@ -70,6 +70,30 @@ def test_scoring_flag():
         moe.make_shape(64, 128, 8, 2, 256, scoring="tanh")
 
 
+def test_routing_flag_and_expert_choice_limits():
+    L = moe.lib()
+    F = _fake
+    assert moe.check_shape(moe.make_shape(64, 128, 8, 2, 256, routing="expert")) == moe.MOE_OK
+    s = moe.make_shape(64, 128, 8, 2, 256)
+    s.routing = 3
+    assert moe.check_shape(s) == moe.MOE_ERR_INVALID_ARGUMENT
+    with pytest.raises(ValueError):
+        moe.make_shape(64, 128, 8, 2, 256, routing="both")
+    ec = moe.make_shape(64, 128, 8, 2, 256, routing="expert")
+    sp = ctypes.byref(ec)
+    # expert choice runs only through the layer call
+    assert L.moe_route(sp, F(), F(), None, F(), F(), F(), F(), F(), None, F(), 1 << 30, None) == 2
+    assert L.moe_dispatch(sp, F(), F(), None, F(), F(), F(), F(), F(), F(), 1 << 30, None) == 2
+    assert L.moe_combine(sp, F(), F(), F(), None, F(), None) == 2
+    # and takes no load-balancing bias
+    ws = moe.workspace_size(ec, moe.CALL_LAYER)
+    args = [F(), F(), F()] + [F()] * 3 + [None] * 3 + [F()] + [None] * 10 + [0.01, 1e-3, F(), ws,
+                                                                          None]
+    assert L.moe_layer_forward(sp, *args) == 1
+    # its workspace holds the [E, T] score columns and row map
+    assert ws > moe.workspace_size(moe.make_shape(64, 128, 8, 2, 256), moe.CALL_LAYER)
+
+
 def test_capacity_matches_oracle_rounding():
     rng = random.Random(5)
     cases = [(1.25, 2, 32768, 64), (1.0, 2, 10, 3), (0.05, 2, 40, 4), (0.03125, 2, 40, 4),

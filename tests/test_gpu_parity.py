@@ -238,7 +238,7 @@ def run_layer(cfg, dev, inp=None):
     d = to_dev(inp, dev)
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     layer = moe.MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.M, cfg.S, cfg.c, cfg.renorm, dt, dev,
-                         cfg.scoring)
+                         cfg.scoring, cfg.routing)
     out = layer.forward(d.x, d.W_r, d.W_gate, d.W_up, d.W_down, d.b, d.shared_fused(), cfg.lam,
                         cfg.gamma)
     torch.cuda.synchronize()
@@ -247,6 +247,8 @@ def run_layer(cfg, dev, inp=None):
 
 def check_layer(cfg, inp, out, tokens=None):
     """Staged parity: selection (near ties exempt), then every later stage on the GPU's selection."""
+    if cfg.routing == "expert":
+        return check_layer_ec(cfg, inp, out, tokens)
     x64 = O._f64(inp.x)
     orc_route = O.route(x64, O._f64(inp.W_r), cfg.k, None if inp.b is None else O._f64(inp.b),
                         cfg.renorm, cfg.scoring)
@@ -290,6 +292,65 @@ def check_layer(cfg, inp, out, tokens=None):
             "dropped": int(res["overflow"].sum()), "max_load": int(res["n"].max())}
 
 
+def check_layer_ec(cfg, inp, out, tokens=None, exact_ties=False):
+    """Expert choice: y_t depends only on which experts took token t, so y is compared on every
+    token whose membership is unambiguous: for each expert whose r-th and (r+1)-th largest oracle
+    logits are closer than DELTA (the fp32 logits may order them differently), tokens with a logit
+    within DELTA of that gap are set aside. With exact ties (all logits equal) both sides take the
+    lowest indices and every token is compared. Loads, statistics and diagnostics on all tokens."""
+    DELTA = 1e-4
+    x64 = O._f64(inp.x)
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            cache[e] = (O._f64(inp.W_gate[e]), O._f64(inp.W_up[e]), O._f64(inp.W_down[e]))
+        return cache[e]
+
+    shared = [tuple(O._f64(t) for t in s) for s in inp.shared]
+    res = O.layer_forward_expert_choice(x64, O._f64(inp.W_r), None, None, None, cfg.k,
+                                        shared=shared, c=cfg.c, renorm=cfg.renorm, lam=cfg.lam,
+                                        tokens=tokens, expert_weights=expert, scoring=cfg.scoring)
+    T, E, r = cfg.T, cfg.E, res["r"]
+    l = res["logits"]
+    srt = -np.sort(-l, axis=0)
+    hi = srt[r - 1]
+    lo = srt[r] if r < T else np.full(E, -np.inf)
+    near = (hi - lo) < DELTA
+    amb = np.any(near[None, :] & (l >= lo[None, :] - DELTA) & (l <= hi[None, :] + DELTA), axis=1)
+    if exact_ties:
+        amb[:] = False
+    want = res["tokens"]
+    sure = ~amb[want]
+    assert np.all(out["counts"].cpu().numpy() == r) and np.all(out["overflow"].cpu().numpy() == 0)
+    # tokens no expert took carry only the shared term: exactly 0 without shared experts; they
+    # are checked apart so that their zeros do not deflate the RMS floor of the error measure
+    taken = np.zeros(T, dtype=bool)
+    for e in range(E):
+        taken[res["chosen"][e]] = True
+    cov = taken[want] & sure
+    unc = ~taken[want]
+    y = out["y"].cpu()[torch.as_tensor(want)]
+    err = max_rel_err(y[torch.as_tensor(cov)], res["y"][cov]) if cov.any() else 0.0
+    assert err < TOL_Y[cfg.dtype], err
+    if unc.any():
+        if cfg.S == 0:
+            assert torch.all(y[torch.as_tensor(unc)] == 0)
+        else:
+            assert max_rel_err(y[torch.as_tensor(unc)], res["y"][unc]) < TOL_Y[cfg.dtype]
+    assert rel(out["f"], res["f"]) < TOL_STATS
+    assert rel(out["P"], res["P"]) < TOL_STATS
+    assert rel(out["aux"], [res["aux"]]) < TOL_STATS
+    assert rel(out["z"], [res["z"]]) < TOL_STATS
+    dg = out["diag"].cpu().numpy().astype(np.float64)
+    rd = res["diag"]
+    assert rel([dg[0]], [rd["entropy"]]) < TOL_STATS
+    assert dg[1] == 0.0 and dg[2] == 1.0  # equal loads
+    assert abs(dg[3] - rd["importance_cv2"]) <= 1e-5 * rd["importance_cv2"] + 1e-6
+    return {"y_err": err, "compared": int(sure.sum()), "set_aside": int((~sure).sum()), "r": r,
+            "uncovered": res["uncovered"]}
+
+
 LAYER_CASES = [
     ("tiny_fp32", {}),
     ("mixtral_8x7b", dict(T=1200, d=256, M=384)),
@@ -301,6 +362,12 @@ LAYER_CASES = [
     ("tiny_fp32", dict(scoring="sigmoid")),
     ("deepseek_v2", dict(T=600, d=320, M=136, scoring="sigmoid")),
     ("sigmoid_v3", dict(T=700, d=256, M=128)),
+    # expert choice: shared experts; fp32; ragged K/N tails with uncovered tokens; sigmoid scores
+    ("expert_choice", dict(T=600, d=256, M=128)),
+    ("tiny_fp32", dict(routing="expert")),
+    ("expert_choice", dict(T=333, d=200, M=136, E=5, k=2, S=0, c=0.5)),
+    ("expert_choice", dict(T=300, d=128, M=64, E=8, S=1, scoring="sigmoid")),
+    ("expert_choice", dict(T=200, d=64, M=64, E=256, k=8, S=0)),
 ]
 
 
@@ -310,6 +377,19 @@ def test_layer(gpu, base, kw):
     say(f"[layer] {cfg}")
     inp, out = run_layer(cfg, gpu)
     info = check_layer(cfg, inp, out)
+    say(f"    {info}")
+
+
+def test_expert_choice_exact_ties(gpu):
+    # a zero router: every logit is 0, so every expert takes the first r tokens on both sides
+    cfg = cfg_of("expert_choice", T=257, d=64, M=64, E=6, k=2, S=0)
+    say(f"[expert choice ties] {cfg}")
+    inp = workloads.make_inputs(cfg)
+    inp = workloads.MoEInputs(cfg, inp.x, torch.zeros_like(inp.W_r), inp.W_gate, inp.W_up,
+                              inp.W_down, inp.b, inp.shared)
+    _, out = run_layer(cfg, gpu, inp)
+    info = check_layer_ec(cfg, inp, out, exact_ties=True)
+    assert info["uncovered"] > 0 and info["set_aside"] == 0
     say(f"    {info}")
 
 
@@ -335,7 +415,7 @@ def test_layer_all_dropped_gives_shared_only(gpu):
 # ------------------------------------------------------------------------- full-size workloads
 
 FULL = ["tiny_fp32", "mixtral_8x7b", "deepseekmoe_16b", "deepseek_v2", "skewed_capacity",
-        "sigmoid_v3"]
+        "sigmoid_v3", "expert_choice"]
 
 
 @pytest.mark.slow

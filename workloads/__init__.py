@@ -63,6 +63,7 @@ class MoEConfig:
     zipf_s: Optional[float] = None  # Zipf exponent of the router-logit skew (None = none)
     seed: int = 0
     scoring: str = "softmax"    # router scores: "softmax" or per-expert "sigmoid"
+    routing: str = "token"      # "token" choice (top-k experts) or "expert" choice (top-r tokens)
 
     def with_(self, **kw) -> "MoEConfig":
         return replace(self, **kw)
@@ -79,6 +80,10 @@ CONFIGS: Dict[str, MoEConfig] = {
     # shared expert; hidden and expert widths as the DeepSeek-V2 layer above, 8 chosen per token
     "sigmoid_v3": MoEConfig("sigmoid_v3", T=16384, d=5120, E=256, k=8, M=1536, S=1, bias=True,
                             scoring="sigmoid"),
+    # expert-choice routing on the DeepSeekMoE layer: 64 experts each take r = 2 T / 64 tokens
+    # (the same number of assignments as top-2 token choice), two shared experts
+    "expert_choice": MoEConfig("expert_choice", T=8192, d=2048, E=64, k=2, M=1408, S=2,
+                               routing="expert"),
 }
 
 # the configuration the headline metric is quoted on
