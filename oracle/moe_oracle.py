@@ -41,6 +41,9 @@ uses it):
     renormalised over that set when renorm is on; a token no expert took gets only the shared
     term. Rows of an expert are in ascending token order; loads n_e = r; the load-balancing bias
     does not apply (a per-expert shift leaves every expert's ranking of tokens unchanged).
+  * Loss backward: the gradient of L = aux + z_coef * z with respect to the logits, W_r and x,
+    with every f_e held fixed (it counts discrete selections, so no gradient flows through it;
+    the gradient reaches the router through P_e and the z-loss).
   * Diagnostics: routing entropy is the token mean of H(p_t) = -sum_e p_te ln p_te (natural log,
     0 ln 0 = 0) of the same per-token distribution P_e averages; the load Gini coefficient is
     sum_ij |n_i - n_j| / (2 E sum_e n_e); max/mean load is max_e n_e / (sum_e n_e / E); the
@@ -286,6 +289,37 @@ def balance_stats(n: np.ndarray, g: np.ndarray, lse: np.ndarray, k: int, lam: fl
     aux = float(lam) * E * float((f * P).sum())
     z = float((_f64(lse) ** 2).sum() / float(T))
     return {"f": f, "P": P, "aux": aux, "z": z}
+
+
+def balance_loss_grad_logits(l: np.ndarray, f: np.ndarray, lam: float, z_coef: float,
+                             scoring: str = "softmax") -> np.ndarray:
+    """dL/dl for L = aux + z_coef z, aux = lambda E sum_e f_e P_e, P_e = (1/T) sum_t p_te,
+    z = (1/T) sum_t lse_t^2, with f held fixed ([ATLAS] §原理与演进: f_e is a count and the
+    gradient flows through P_e; [CMP] §2.2 z-loss). With a_e = lambda E f_e / T:
+      softmax p = g:          dL/dl_te = g_te (a_e - sum_e' g_te' a_e') + z_coef (2/T) lse_t g_te
+      sigmoid p = s / sum s:  dL/dl_te = s_te (1 - s_te) (a_e - sum_e' p_te' a_e') / sum_e' s_te'
+                              + z_coef (2/T) lse_t softmax(l_t)_e   [T, E]"""
+    l = _f64(l)
+    T, E = l.shape
+    a = float(lam) * E * _f64(f) / T
+    g, lse = softmax_lse(l)
+    dz = float(z_coef) * (2.0 / T) * lse[:, None] * g
+    if scoring == "softmax":
+        return g * (a[None, :] - (g * a[None, :]).sum(axis=1, keepdims=True)) + dz
+    if scoring == "sigmoid":
+        s = sigmoid_scores(l)
+        S = s.sum(axis=1, keepdims=True)
+        p = s / S
+        return s * (1.0 - s) * (a[None, :] - (p * a[None, :]).sum(axis=1, keepdims=True)) / S + dz
+    raise ValueError(f"unknown scoring {scoring!r}")
+
+
+def balance_loss_backward(x, W_r, f, lam: float, z_coef: float, scoring: str = "softmax"):
+    """Router gradients of L: dl (as above), dW_r = dl^T x [E, d], dx = dl W_r [T, d]."""
+    x64 = _f64(x)
+    W64 = _f64(W_r)
+    dl = balance_loss_grad_logits(router_logits(x64, W64), f, lam, z_coef, scoring)
+    return {"dlogits": dl, "dW_r": dl.T @ x64, "dx": dl @ W64}
 
 
 def routing_entropy(probs: np.ndarray) -> float:

@@ -331,6 +331,67 @@ def test_expert_choice_layer_pins():
     assert res2["diag"]["max_over_mean"] == 1.0
 
 
+# -------------------------------------------------------------------------- loss backward
+
+def _balance_loss(mod, l, f, lam, zc, scoring):
+    # L = aux + zc z evaluated from its forward definitions (f held fixed)
+    l = np.asarray(l, dtype=np.float64)
+    g, lse = mod.softmax_lse(l)
+    p = g if scoring == "softmax" else mod.score_distribution(mod.sigmoid_scores(l), "sigmoid")
+    T, E = l.shape
+    aux = lam * E * float((f * p.sum(axis=0) / T).sum())
+    return aux + zc * float((lse ** 2).mean())
+
+
+def check_loss_backward(mod=O):
+    T, E = 9, 5
+    l = _rand((T, E), 41, 1.5)
+    f = np.array([0.3, 0.1, 0.25, 0.05, 0.3])
+    lam, zc = 0.37, 0.8
+    for scoring in ("softmax", "sigmoid"):
+        dl = mod.balance_loss_grad_logits(l, f, lam, zc, scoring)
+        # central finite differences of the forward loss
+        h = 1e-6
+        fd = np.zeros_like(l)
+        for t in range(T):
+            for e in range(E):
+                lp, lm = l.copy(), l.copy()
+                lp[t, e] += h
+                lm[t, e] -= h
+                fd[t, e] = (_balance_loss(mod, lp, f, lam, zc, scoring) -
+                            _balance_loss(mod, lm, f, lam, zc, scoring)) / (2 * h)
+        assert np.allclose(dl, fd, rtol=1e-6, atol=1e-9), scoring
+        # torch autograd in float64 on the same loss written with torch ops
+        lt = torch.tensor(l, requires_grad=True)
+        ft = torch.tensor(f)
+        if scoring == "softmax":
+            p = torch.softmax(lt, dim=1)
+        else:
+            sg = torch.sigmoid(lt)
+            p = sg / sg.sum(dim=1, keepdim=True)
+        L = lam * E * (ft * p.mean(dim=0)).sum() + zc * (torch.logsumexp(lt, dim=1) ** 2).mean()
+        L.backward()
+        assert np.allclose(dl, lt.grad.numpy(), rtol=1e-12, atol=1e-15), scoring
+    # zero router and equal f: the aux term has zero gradient (uniform P is stationary)
+    dl0 = mod.balance_loss_grad_logits(np.zeros((4, E)), np.full(E, 1.0 / E), 1.0, 0.0)
+    assert np.allclose(dl0, 0.0, atol=1e-15)
+    # the chain through the router: dW_r = dl^T x and dx = dl W_r, against autograd
+    x = _rand((T, 6), 42)
+    W = _rand((E, 6), 43, 0.4)
+    out = mod.balance_loss_backward(x, W, f, lam, zc)
+    xt = torch.tensor(x, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    lt = xt @ Wt.T
+    L = lam * E * (torch.tensor(f) * torch.softmax(lt, 1).mean(0)).sum() + zc * (torch.logsumexp(lt, 1) ** 2).mean()
+    L.backward()
+    assert np.allclose(out["dW_r"], Wt.grad.numpy(), rtol=1e-12, atol=1e-15)
+    assert np.allclose(out["dx"], xt.grad.numpy(), rtol=1e-12, atol=1e-15)
+
+
+def test_loss_backward_pins():
+    check_loss_backward()
+
+
 # ----------------------------------------------------------------------------- capacity/dispatch
 
 def test_capacity_closed_forms():
@@ -617,6 +678,13 @@ def _ec_smallest(l, r):
     return O.expert_choice(-O._f64(l), r)
 
 
+def _grad_no_centering(l, f, lam, z_coef, scoring="softmax"):
+    l = O._f64(l)
+    T, E = l.shape
+    g, lse = O.softmax_lse(l)
+    return g * (lam * E * O._f64(f) / T)[None, :] + z_coef * (2.0 / T) * lse[:, None] * g
+
+
 def _sigmoid_wrong_sign(l):
     l = O._f64(l)
     return 1.0 / (1.0 + np.exp(l))
@@ -641,6 +709,7 @@ def _sigmoid_unnormalised_P(g, scoring="softmax"):
     (dict(routing_entropy=_entropy_log2), [check_diagnostics]),
     (dict(expert_choice=_ec_ties_high), [check_expert_choice]),
     (dict(expert_choice=_ec_smallest), [check_expert_choice]),
+    (dict(balance_loss_grad_logits=_grad_no_centering), [check_loss_backward]),
 ])
 def test_planted_mistakes_are_caught(mutant, checks):
     m = _Mutant(**mutant)
