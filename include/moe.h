@@ -72,7 +72,8 @@ typedef enum {
   MOE_CALL_ROUTE = 0,
   MOE_CALL_DISPATCH = 1,
   MOE_CALL_EXPERT_FFN = 2,
-  MOE_CALL_LAYER = 3
+  MOE_CALL_LAYER = 3,
+  MOE_CALL_LOSS_BACKWARD = 4
 } moe_call;
 
 #define MOE_E_MAX 256 /* routed experts per layer */
@@ -233,6 +234,26 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
                              int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* overflow,
                              float* f, float* P, float* aux, float* z, float* diag, float* b_new,
                              float lambda, float gamma, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_balance_loss_backward -- gradient of the layer's balance losses through the router.
+ * L = aux + z_coef z, aux = lambda E sum_e f_e P_e, z = mean_t lse_t^2, as moe_balance_stats
+ * computes them, with every f_e = n_e / (k T) (expert choice: n_e / (E r)) held fixed: f counts
+ * discrete choices, so the gradient reaches the router through P_e and through z
+ * ("MoE：条件计算与路由" §原理与演进; "MOE大模型对比篇" §2.1-§2.2). With a_e = lambda E f_e / T:
+ *   softmax: dL/dl_te = g_te (a_e - sum_e' g_te' a_e') + z_coef (2/T) lse_t g_te
+ *   sigmoid: dL/dl_te = s_te (1 - s_te) (a_e - sum_e' p_te' a_e') / sum_e' s_te'
+ *            + z_coef (2/T) lse_t softmax(l_t)_e,   p = s / sum s
+ *   dW_r = dl^T x,  dx = dl W_r.
+ *   x device [T, d] (dtype); W_r device [E, d] (dtype); n device [E] int32 (the forward's loads)
+ *   dlogits device out [T, E] fp32, dW_r device out [E, d] fp32, dx device out [T, d] fp32: each
+ *   nullable (at least one set)
+ *   ws device workspace of moe_workspace_size(s, MOE_CALL_LOSS_BACKWARD) bytes
+ */
+moe_status moe_balance_loss_backward(const moe_shape* s, const void* x, const void* W_r,
+                                     const int32_t* n, float lambda, float z_coef,
+                                     float* dlogits, float* dW_r, float* dx, void* ws,
+                                     size_t ws_bytes, void* stream);
 
 /*
  * moe_set_stage_events -- profiling aid for moe_layer_forward (not a step of the method).

@@ -21,7 +21,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
-CALL_ROUTE, CALL_DISPATCH, CALL_EXPERT_FFN, CALL_LAYER = range(4)
+CALL_ROUTE, CALL_DISPATCH, CALL_EXPERT_FFN, CALL_LAYER, CALL_LOSS_BACKWARD = range(5)
 E_MAX, K_MAX = 256, 16
 
 
@@ -62,6 +62,9 @@ _SIG = {
                                          _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                          ctypes.c_float, ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "moe_set_stage_events": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]),
+    "moe_balance_loss_backward": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, ctypes.c_float,
+                                                 ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t,
+                                                 _P]),
 }
 
 STAGES = ["route", "dispatch", "gemm_up", "gemm_down", "shared", "combine", "stats"]
@@ -280,6 +283,31 @@ def moe_balance_stats(T: int, k: int, n: torch.Tensor, gsum: torch.Tensor, lse2s
     return out
 
 
+def moe_balance_loss_backward(x: torch.Tensor, W_r: torch.Tensor, n: torch.Tensor, k: int,
+                              lam: float = 0.01, z_coef: float = 1.0, c: Optional[float] = None,
+                              scoring: str = "softmax", routing: str = "token",
+                              want=("dlogits", "dW_r", "dx"), ws: Optional[torch.Tensor] = None) -> dict:
+    """Gradients of aux + z_coef z with respect to the router logits, W_r and x (fp32), f fixed
+    at the forward's loads n."""
+    T, d = x.shape
+    E = W_r.shape[0]
+    s = make_shape(T, d, E, k, 8, c=c, dtype=x.dtype, scoring=scoring, routing=routing)
+    _dev(x, "x")
+    _dev(W_r, "W_r", x.dtype, (E, d))
+    _dev(n, "n", torch.int32, (E,))
+    dev = x.device
+    out = {"dlogits": torch.empty(T, E, dtype=torch.float32, device=dev) if "dlogits" in want else None,
+           "dW_r": torch.empty(E, d, dtype=torch.float32, device=dev) if "dW_r" in want else None,
+           "dx": torch.empty(T, d, dtype=torch.float32, device=dev) if "dx" in want else None}
+    if ws is None:
+        ws = workspace(s, CALL_LOSS_BACKWARD, dev)
+    _check(lib().moe_balance_loss_backward(ctypes.byref(s), _ptr(x), _ptr(W_r), _ptr(n), float(lam),
+                                           float(z_coef), _ptr(out["dlogits"]), _ptr(out["dW_r"]),
+                                           _ptr(out["dx"]), _ptr(ws), ws.numel(), _stream()),
+           "moe_balance_loss_backward")
+    return out
+
+
 class MoELayer:
     """Holds the sizes and a preallocated workspace; ``forward`` calls moe_layer_forward."""
 
@@ -369,5 +397,6 @@ def moe_layer_forward(x, W_r, W_gate, W_up, W_down, k: int, b=None, shared=None,
 
 
 __all__ = ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_balance_stats",
+           "moe_balance_loss_backward",
            "moe_layer_forward", "MoELayer", "make_shape", "capacity", "workspace_size",
            "check_shape", "status_string", "lib", "MoEError", "Shape", "moe_set_stage_events"]

@@ -183,6 +183,20 @@ LayerPlan plan_layer(Carve& c, const moe_shape* s) {
   return p;
 }
 
+struct LossBackwardPlan {
+  RoutePlan r;
+  float *cols, *dl, *dlT;
+};
+LossBackwardPlan plan_loss_backward(Carve& c, const moe_shape* s) {
+  const size_t ET = static_cast<size_t>(s->E) * s->T;
+  LossBackwardPlan p;
+  p.r = plan_route(c, s);
+  p.cols = c.take<float>(2 * ET);
+  p.dl = c.take<float>(ET);
+  p.dlT = c.take<float>(ET);
+  return p;
+}
+
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // Profiling aid: events recorded at the end of each moe_layer_forward stage (see moe.h).
@@ -242,6 +256,7 @@ size_t moe_workspace_size(const moe_shape* s, int call) {
     case MOE_CALL_DISPATCH: plan_dispatch(c, s); break;
     case MOE_CALL_EXPERT_FFN: c.take<int32_t>(3 * (MOE_E_MAX + 1)); break;
     case MOE_CALL_LAYER: plan_layer(c, s); break;
+    case MOE_CALL_LOSS_BACKWARD: plan_loss_backward(c, s); break;
     default: return 0;
   }
   return c.used;
@@ -445,6 +460,35 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
                      diag,
                      b_new ? b : nullptr, b_new, gamma, hs);
   mark_stage(7, hs);
+  return hip_status(e);
+}
+
+moe_status moe_balance_loss_backward(const moe_shape* s, const void* x, const void* W_r,
+                                     const int32_t* n, float lambda, float z_coef,
+                                     float* dlogits, float* dW_r, float* dx, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  moe_status st = moe_check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!x || !W_r || !n || (!dlogits && !dW_r && !dx)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(W_r)) return MOE_ERR_INVALID_ARGUMENT;
+  if (isnan(lambda) || isnan(z_coef)) return MOE_ERR_INVALID_ARGUMENT;
+  if (s->T * static_cast<int64_t>(s->E) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < moe_workspace_size(s, MOE_CALL_LOSS_BACKWARD)) return MOE_ERR_WORKSPACE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  Carve c(ws);
+  LossBackwardPlan p = plan_loss_backward(c, s);
+  const size_t ET = static_cast<size_t>(s->E) * s->T;
+  // the router in its column mode recomputes the logits and scores
+  hipError_t e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s) | kRouteExpertChoice,
+                              x, W_r, nullptr, nullptr, nullptr, p.r.hist, p.r.gpart, p.r.lpart,
+                              p.r.hpart, p.cols, hs);
+  if (e == hipSuccess)
+    e = launch_loss_grad(s->T, s->E, s->scoring == MOE_SCORE_SIGMOID, p.cols, p.cols + ET, n,
+                         stats_fden(s), lambda, z_coef, dlogits ? dlogits : p.dl, p.dlT, hs);
+  if (e == hipSuccess && dW_r)  // dW_r [E][d] = sum_t dl[t][e] x[t][:]
+    e = launch_kmajor_gemm(s->dtype, s->E, s->d, s->T, dlogits ? dlogits : p.dl, x, dW_r, hs);
+  if (e == hipSuccess && dx)  // dx [T][d] = sum_e dl[e][t] W_r[e][:]
+    e = launch_kmajor_gemm(s->dtype, s->T, s->d, s->E, p.dlT, W_r, dx, hs);
   return hip_status(e);
 }
 

@@ -15,6 +15,7 @@ def test_library_exports_every_declared_symbol():
     names = moe.header_functions()
     assert set(names) >= {"moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
                           "moe_balance_stats", "moe_layer_forward", "moe_workspace_size",
+                          "moe_balance_loss_backward",
                           "moe_capacity", "moe_status_string", "moe_check_shape"}
     h = ctypes.CDLL(moe.LIB_PATH)
     for n in names:
@@ -174,6 +175,24 @@ def test_entry_points_reject_before_launch():
     bad = moe.make_shape(64, 128, 8, 9, 256)
     assert L.moe_route(ctypes.byref(bad), F(), F(), None, F(), F(), F(), F(), F(), None, F(),
                        1 << 30, None) == 1
+
+
+def test_loss_backward_rejects_before_launch():
+    L = moe.lib()
+    F = _fake
+    s = moe.make_shape(64, 128, 8, 2, 256)
+    sp = ctypes.byref(s)
+    ws = moe.workspace_size(s, moe.CALL_LOSS_BACKWARD)
+    assert ws > 0
+    # no output requested / missing loads / workspace too small / NaN coefficient
+    assert L.moe_balance_loss_backward(sp, F(), F(), F(), 0.01, 1.0, None, None, None, F(), ws,
+                                       None) == 1
+    assert L.moe_balance_loss_backward(sp, F(), F(), None, 0.01, 1.0, F(), None, None, F(), ws,
+                                       None) == 1
+    assert L.moe_balance_loss_backward(sp, F(), F(), F(), 0.01, 1.0, F(), None, None, F(), ws - 1,
+                                       None) == 3
+    assert L.moe_balance_loss_backward(sp, F(), F(), F(), float("nan"), 1.0, F(), None, None, F(),
+                                       ws, None) == 1
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

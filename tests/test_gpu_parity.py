@@ -231,6 +231,44 @@ def test_balance_stats(gpu):
     assert np.array_equal(nb[2:], b2[2:])
 
 
+# --------------------------------------------------------------------- balance-loss backward
+
+LOSS_BW_CASES = [
+    ("tiny_fp32", {}),
+    ("mixtral_8x7b", dict(T=300, d=256)),
+    ("deepseek_v2", dict(T=200, d=320, scoring="sigmoid")),
+    ("expert_choice", dict(T=250, d=128, E=20, k=3)),
+    ("mixtral_8x7b", dict(T=70, d=64, E=256, k=16)),
+]
+
+
+@pytest.mark.parametrize("base,kw", LOSS_BW_CASES)
+def test_balance_loss_backward(gpu, base, kw):
+    """Gradients of aux + z_coef z through the router against the fp64 oracle (f fixed at given
+    loads). Bound: the logits carry fp32 accumulation error (~1e-6 relative) and dW_r sums T fp32
+    products, so 2e-4 in the max relative error of every output (R17 measure)."""
+    cfg = cfg_of(base, **kw)
+    say(f"[loss backward] {cfg}")
+    x = workloads.make_x(cfg)
+    Wr = workloads.make_router(cfg)
+    rng = np.random.default_rng(7)
+    fden = cfg.k * cfg.T
+    n = rng.multinomial(fden, np.ones(cfg.E) / cfg.E).astype(np.int32)
+    if cfg.routing == "expert":  # loads are r each
+        r = O.expert_choice_capacity(cfg.c, cfg.k, cfg.T, cfg.E)
+        n = np.full(cfg.E, r, dtype=np.int32)
+        fden = cfg.E * r
+    lam, zc = 0.01, 0.37
+    out = moe.moe_balance_loss_backward(x.to(gpu), Wr.to(gpu), torch.from_numpy(n).to(gpu), cfg.k,
+                                        lam, zc, c=cfg.c, scoring=cfg.scoring, routing=cfg.routing)
+    torch.cuda.synchronize()
+    ref = O.balance_loss_backward(O._f64(x), O._f64(Wr), n / fden, lam, zc, cfg.scoring)
+    errs = {key: max_rel_err(out[key], ref[key]) for key in ("dlogits", "dW_r", "dx")}
+    say(f"    {errs}")
+    for key, e in errs.items():
+        assert e < 2e-4, (key, e)
+
+
 # ------------------------------------------------------------------------------ whole layer
 
 def run_layer(cfg, dev, inp=None):
