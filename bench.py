@@ -159,6 +159,24 @@ def main():
     t1 = time.perf_counter()
     moe.moe_set_stage_events(None)
 
+    # the balance-loss backward through the router (a separate entry point; not part of a step)
+    lb_ws = moe.workspace(moe.make_shape(cfg.T, cfg.d, cfg.E, cfg.k, 8, c=cfg.c, dtype=dt,
+                                         scoring=cfg.scoring, routing=cfg.routing),
+                          moe.CALL_LOSS_BACKWARD, dev)
+    n_fwd = out["counts"]
+    for _ in range(2):
+        lb = moe.moe_balance_loss_backward(x, W_r, n_fwd, cfg.k, cfg.lam, 1.0, c=cfg.c,
+                                           scoring=cfg.scoring, routing=cfg.routing, ws=lb_ws)
+    lb_s, lb_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    lb_s.record()
+    for _ in range(5):
+        lb = moe.moe_balance_loss_backward(x, W_r, n_fwd, cfg.k, cfg.lam, 1.0, c=cfg.c,
+                                           scoring=cfg.scoring, routing=cfg.routing, ws=lb_ws)
+    lb_e.record()
+    torch.cuda.synchronize()
+    lb_ms = lb_s.elapsed_time(lb_e) / 5
+    del lb, lb_ws
+
     if args.copy_bytes > 0:  # one plain copy of known size, for counter calibration
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -228,6 +246,9 @@ def main():
                    "routing_diagnostics": diag},
         "mfma_peak_frac_layer": round(layer_tf / peak, 4), "layer_tflops": round(layer_tf, 1),
         "roofline": roofline, "stages": stages, "cpu_baseline": cpu,
+        # router gradients of aux + z (dlogits, dW_r, dx): route in column mode + 2 fp32 GEMMs
+        "balance_loss_backward": {"ms": round(lb_ms, 4),
+                                  "flops": 2.0 * 3 * T * d * E},
     }
     print(json.dumps(line), flush=True)
 

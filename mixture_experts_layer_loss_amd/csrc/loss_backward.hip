@@ -11,7 +11,9 @@
 //   [T][E] and [E][T] layouts, so that both products below read K-major operands.
 //   kmajor_gemm_kernel: C[M][N] = sum_k A[k][m] B[k][n] with fp32 A and bf16/fp32 B, both stored
 //   K-major; 64 x 64 tiles, 256 threads with 4 x 4 outputs each, K staged 16 at a time in LDS,
-//   fp32 accumulation in k order. (These products are ~1% of the forward's flops.)
+//   fp32 accumulation in k order. A long K (dW_r sums over all T tokens) is split into KS ranges
+//   whose partial tiles are summed afterwards in range order (reproducible). (These products
+//   are ~1% of the forward's flops.)
 #include "moe_internal.h"
 
 #include <math.h>
@@ -94,8 +96,11 @@ __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v
 
 constexpr int GM = 64, GN = 64, GK = 16;
 
+// blockIdx.y = K range ks of KS (each kc long, a multiple of GK); its partial tile goes to
+// C + ks M N (KS = 1: the result itself)
 template <typename TB>
 __global__ __launch_bounds__(256) void kmajor_gemm_kernel(int64_t M, int64_t N, int64_t K,
+                                                           int64_t kc,
                                                            const float* __restrict__ A,
                                                            const TB* __restrict__ B,
                                                            float* __restrict__ C) {
@@ -104,18 +109,21 @@ __global__ __launch_bounds__(256) void kmajor_gemm_kernel(int64_t M, int64_t N, 
   const int64_t nb = (N + GN - 1) / GN;
   const int64_t m0 = static_cast<int64_t>(blockIdx.x / nb) * GM;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x % nb) * GN;
+  const int64_t kbeg = static_cast<int64_t>(blockIdx.y) * kc;
+  const int64_t kend = min(K, kbeg + kc);
+  C += static_cast<int64_t>(blockIdx.y) * M * N;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   float acc[4][4] = {};
-  for (int64_t k0 = 0; k0 < K; k0 += GK) {
+  for (int64_t k0 = kbeg; k0 < kend; k0 += GK) {
     for (int c = tid; c < GK * GM; c += 256) {
       const int kk = c / GM, mm = c % GM;
       const int64_t k = k0 + kk, m = m0 + mm;
-      As[kk][mm] = (k < K && m < M) ? A[k * M + m] : 0.f;
+      As[kk][mm] = (k < kend && m < M) ? A[k * M + m] : 0.f;
     }
     for (int c = tid; c < GK * GN; c += 256) {
       const int kk = c / GN, nn = c % GN;
       const int64_t k = k0 + kk, n = n0 + nn;
-      Bs[kk][nn] = (k < K && n < N) ? to_f32<TB>(B[k * N + n]) : 0.f;
+      Bs[kk][nn] = (k < kend && n < N) ? to_f32<TB>(B[k * N + n]) : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -144,14 +152,30 @@ __global__ __launch_bounds__(256) void kmajor_gemm_kernel(int64_t M, int64_t N, 
   }
 }
 
+// C[i] = sum_s P[s][i] in s order
+__global__ __launch_bounds__(256) void sum_ranges_kernel(int64_t count, int KS,
+                                                          const float* __restrict__ P,
+                                                          float* __restrict__ C) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= count) return;
+  float v = 0.f;
+  for (int s = 0; s < KS; ++s) v += P[s * count + i];
+  C[i] = v;
+}
+
 template <typename TB>
-hipError_t launch_kmajor(int64_t M, int64_t N, int64_t K, const float* A, const void* B, float* C,
-                         hipStream_t st) {
-  const int64_t grid = ((M + GM - 1) / GM) * ((N + GN - 1) / GN);
-  if (grid == 0) return hipSuccess;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kmajor_gemm_kernel<TB>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
-                     M, N, K, A, static_cast<const TB*>(B), C);
+hipError_t launch_kmajor(int64_t M, int64_t N, int64_t K, int KS, const float* A, const void* B,
+                         float* C, float* partial, hipStream_t st) {
+  const int64_t tiles = ((M + GM - 1) / GM) * ((N + GN - 1) / GN);
+  if (tiles == 0) return hipSuccess;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t kc = ((cdiv(K, KS) + GK - 1) / GK) * GK;
+  hipLaunchKernelGGL(kmajor_gemm_kernel<TB>, dim3(static_cast<unsigned>(tiles), KS), dim3(256), 0,
+                     st, M, N, K, kc, A, static_cast<const TB*>(B), KS > 1 ? partial : C);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || KS == 1) return e;
+  hipLaunchKernelGGL(sum_ranges_kernel, dim3(static_cast<unsigned>(cdiv(M * N, 256))), dim3(256),
+                     0, st, M * N, KS, partial, C);
   return hipGetLastError();
 }
 
@@ -165,10 +189,20 @@ hipError_t launch_loss_grad(int64_t T, int E, int sigmoid, const float* lcol, co
   return hipGetLastError();
 }
 
-hipError_t launch_kmajor_gemm(int dtype_b, int64_t M, int64_t N, int64_t K, const float* A,
-                              const void* B, float* C, hipStream_t st) {
-  return dtype_b == MOE_F32 ? launch_kmajor<float>(M, N, K, A, B, C, st)
-                            : launch_kmajor<bf16_t>(M, N, K, A, B, C, st);
+int kmajor_splits(int64_t M, int64_t N, int64_t K) {
+  // enough K ranges for ~1024 blocks, each range at least 256 long
+  const int64_t tiles = ((M + GM - 1) / GM) * ((N + GN - 1) / GN);
+  int64_t ks = cdiv(1024, tiles);
+  const int64_t by_len = K / 256 > 1 ? K / 256 : 1;
+  if (ks > by_len) ks = by_len;
+  if (ks > 64) ks = 64;
+  return static_cast<int>(ks < 1 ? 1 : ks);
+}
+
+hipError_t launch_kmajor_gemm(int dtype_b, int64_t M, int64_t N, int64_t K, int KS, const float* A,
+                              const void* B, float* C, float* partial, hipStream_t st) {
+  return dtype_b == MOE_F32 ? launch_kmajor<float>(M, N, K, KS, A, B, C, partial, st)
+                            : launch_kmajor<bf16_t>(M, N, K, KS, A, B, C, partial, st);
 }
 
 }  // namespace moe

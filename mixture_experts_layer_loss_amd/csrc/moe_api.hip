@@ -185,7 +185,8 @@ LayerPlan plan_layer(Carve& c, const moe_shape* s) {
 
 struct LossBackwardPlan {
   RoutePlan r;
-  float *cols, *dl, *dlT;
+  float *cols, *dl, *dlT, *partial;
+  int ks_w;  // K ranges of the dW_r product
 };
 LossBackwardPlan plan_loss_backward(Carve& c, const moe_shape* s) {
   const size_t ET = static_cast<size_t>(s->E) * s->T;
@@ -194,6 +195,8 @@ LossBackwardPlan plan_loss_backward(Carve& c, const moe_shape* s) {
   p.cols = c.take<float>(2 * ET);
   p.dl = c.take<float>(ET);
   p.dlT = c.take<float>(ET);
+  p.ks_w = kmajor_splits(s->E, s->d, s->T);
+  p.partial = c.take<float>(p.ks_w > 1 ? static_cast<size_t>(p.ks_w) * s->E * s->d : 1);
   return p;
 }
 
@@ -485,10 +488,11 @@ moe_status moe_balance_loss_backward(const moe_shape* s, const void* x, const vo
   if (e == hipSuccess)
     e = launch_loss_grad(s->T, s->E, s->scoring == MOE_SCORE_SIGMOID, p.cols, p.cols + ET, n,
                          stats_fden(s), lambda, z_coef, dlogits ? dlogits : p.dl, p.dlT, hs);
-  if (e == hipSuccess && dW_r)  // dW_r [E][d] = sum_t dl[t][e] x[t][:]
-    e = launch_kmajor_gemm(s->dtype, s->E, s->d, s->T, dlogits ? dlogits : p.dl, x, dW_r, hs);
+  if (e == hipSuccess && dW_r)  // dW_r [E][d] = sum_t dl[t][e] x[t][:], over token ranges
+    e = launch_kmajor_gemm(s->dtype, s->E, s->d, s->T, p.ks_w, dlogits ? dlogits : p.dl, x, dW_r,
+                           p.partial, hs);
   if (e == hipSuccess && dx)  // dx [T][d] = sum_e dl[e][t] W_r[e][:]
-    e = launch_kmajor_gemm(s->dtype, s->T, s->d, s->E, p.dlT, W_r, dx, hs);
+    e = launch_kmajor_gemm(s->dtype, s->T, s->d, s->E, 1, p.dlT, W_r, dx, nullptr, hs);
   return hip_status(e);
 }
 

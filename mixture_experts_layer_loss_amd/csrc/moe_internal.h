@@ -118,9 +118,12 @@ hipError_t launch_gemm_down(int dtype, int groups, int d, int Mg, const int32_t*
 hipError_t launch_loss_grad(int64_t T, int E, int sigmoid, const float* lcol, const float* scol,
                             const int32_t* n, double fden, float lambda, float z_coef, float* dl,
                             float* dlT, hipStream_t st);
-// C[M][N] fp32 = sum_k A[k][m] B[k][n]; A fp32 [K][M], B [K][N] of dtype_b (bf16 or fp32).
-hipError_t launch_kmajor_gemm(int dtype_b, int64_t M, int64_t N, int64_t K, const float* A,
-                              const void* B, float* C, hipStream_t st);
+// C[M][N] fp32 = sum_k A[k][m] B[k][n]; A fp32 [K][M], B [K][N] of dtype_b (bf16 or fp32). K is
+// split into KS ranges (kmajor_splits) whose partials (KS M N floats of `partial`, unused when
+// KS = 1) are summed in range order.
+int kmajor_splits(int64_t M, int64_t N, int64_t K);
+hipError_t launch_kmajor_gemm(int dtype_b, int64_t M, int64_t N, int64_t K, int KS, const float* A,
+                              const void* B, float* C, float* partial, hipStream_t st);
 
 // Tile table of the shared experts (one group of all T rows).
 hipError_t launch_shared_table(int64_t T, int BM, int32_t* offsets, int32_t* tile_off,

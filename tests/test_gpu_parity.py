@@ -239,6 +239,7 @@ LOSS_BW_CASES = [
     ("deepseek_v2", dict(T=200, d=320, scoring="sigmoid")),
     ("expert_choice", dict(T=250, d=128, E=20, k=3)),
     ("mixtral_8x7b", dict(T=70, d=64, E=256, k=16)),
+    ("deepseek_v2", dict(T=3000, d=320)),   # dW_r over 11 token ranges
 ]
 
 
