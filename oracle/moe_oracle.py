@@ -322,6 +322,99 @@ def balance_loss_backward(x, W_r, f, lam: float, z_coef: float, scoring: str = "
     return {"dlogits": dl, "dW_r": dl.T @ x64, "dx": dl @ W64}
 
 
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    """d SiLU / dz = sigma(z) (1 + z (1 - sigma(z)))."""
+    z = _f64(z)
+    sg = 1.0 / (1.0 + np.exp(-z))
+    return sg * (1.0 + z * (1.0 - sg))
+
+
+def layer_backward(x, W_r, W_gate, W_up, W_down, dy, k: int, b=None, shared=(), c=None,
+                   renorm: bool = True, lam: float = 0.01, z_coef: float = 0.0,
+                   scoring: str = "softmax", topk_idx=None):
+    """Gradients of <dy, y> + aux + z_coef z with respect to x, W_r and every expert weight, for
+    the token-choice layer of layer_forward (selection, capacity and f held fixed: they are
+    discrete). The chain, step by step:
+      d out[row(t,j)] = w_tj dy_t;   d w_tj = <dy_t, out[row(t,j)]>   (kept slots; dropped add 0)
+      gates: w_j = g_j / sum_S g (renorm) -> dg_e = (dw_e - sum_j w_j dw_j) / sum_S g, else dg = dw
+      scores: softmax dl = g (dg - sum_e g dg); sigmoid dl = s (1 - s) dg; plus the balance-loss
+      gradient (balance_loss_grad_logits); dW_r = dl^T x, dx += dl W_r
+      per kept row: dh = d out W_down; dW_down += d out^T h; dG = dh U SiLU'(G), dU = dh SiLU(G);
+      dx_t += dG W_gate + dU W_up; dW_gate += dG^T x_t, dW_up += dU^T x_t
+      shared experts: the same with d out = dy_t and weight 1.
+    Returns dict of float64 arrays."""
+    x64 = _f64(x)
+    T, d = x64.shape
+    r = route(x64, W_r, k, b, renorm, scoring)
+    l, g = r["logits"], r["g"]
+    E = g.shape[1]
+    S = r["topk_idx"] if topk_idx is None else np.asarray(topk_idx, dtype=np.int64)
+    w = gate_weights(g, S, renorm)
+    n = expert_loads(S, E)
+    dsp = dispatch(S, E, capacity(c, k, T, E))
+    dy64 = _f64(dy)
+    out = {"dx": np.zeros((T, d)), "dW_gate": np.zeros_like(_f64(W_gate)),
+           "dW_up": np.zeros_like(_f64(W_up)), "dW_down": np.zeros_like(_f64(W_down))}
+    dw = np.zeros((T, k))
+    for e in range(E):
+        rows = [(int(dsp["offsets"][e]) + p, int(dsp["perm_token"][dsp["offsets"][e] + p]))
+                for p in range(int(dsp["kept"][e]))]
+        if not rows:
+            continue
+        Wg, Wu, Wd = _f64(W_gate[e]), _f64(W_up[e]), _f64(W_down[e])
+        toks = [t for _, t in rows]
+        X = x64[toks]
+        G = X @ Wg.T
+        U = X @ Wu.T
+        h = silu(G) * U
+        O = h @ Wd.T
+        # the slot of each row, for its gate
+        slot = np.array([int(np.nonzero(dsp["row"][t] == rr)[0][0]) for rr, t in rows])
+        wt = w[toks, slot]
+        dO = wt[:, None] * dy64[toks]
+        dw[toks, slot] = (dy64[toks] * O).sum(axis=1)
+        dh = dO @ Wd
+        out["dW_down"][e] = dO.T @ h
+        dG = dh * U * silu_grad(G)
+        dU = dh * silu(G)
+        out["dW_gate"][e] = dG.T @ X
+        out["dW_up"][e] = dU.T @ X
+        np.add.at(out["dx"], toks, dG @ Wg + dU @ Wu)
+    # router: gates -> scores -> logits
+    dg = np.zeros((T, E))
+    gS = np.take_along_axis(g, S, axis=1)
+    if renorm:
+        den = gS.sum(axis=1, keepdims=True)
+        dgS = (dw - (w * dw).sum(axis=1, keepdims=True)) / den
+    else:
+        dgS = dw
+    np.put_along_axis(dg, S, dgS, axis=1)
+    if scoring == "softmax":
+        dl = g * (dg - (g * dg).sum(axis=1, keepdims=True))
+    else:
+        dl = g * (1.0 - g) * dg
+    f = n / float(k * T)
+    dl = dl + balance_loss_grad_logits(l, f, lam, z_coef, scoring)
+    W64 = _f64(W_r)
+    out["dW_r"] = dl.T @ x64
+    out["dx"] += dl @ W64
+    out["dlogits"] = dl
+    sh_grads = []
+    for Wg, Wu, Wd in shared:
+        Wg, Wu, Wd = _f64(Wg), _f64(Wu), _f64(Wd)
+        G = x64 @ Wg.T
+        U = x64 @ Wu.T
+        h = silu(G) * U
+        dh = dy64 @ Wd
+        dG = dh * U * silu_grad(G)
+        dU = dh * silu(G)
+        out["dx"] += dG @ Wg + dU @ Wu
+        sh_grads.append((dG.T @ x64, dU.T @ x64, dy64.T @ h))
+    out["shared"] = sh_grads
+    out["topk_idx"] = S
+    return out
+
+
 def routing_entropy(probs: np.ndarray) -> float:
     """Mean over tokens of H(g(x)) = -sum_e g_e ln g_e ([ATLAS] §9 专业化是否真的发生: the routing
     entropy describes how concentrated the choice is), with 0 ln 0 = 0."""

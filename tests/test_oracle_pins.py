@@ -392,6 +392,79 @@ def test_loss_backward_pins():
     check_loss_backward()
 
 
+# ---------------------------------------------------------------------------- layer backward
+
+def _torch_layer_loss(x, Wr, Wg, Wu, Wd, dy, S, kept, f, k, renorm, lam, zc, scoring, shared):
+    # the layer written densely with torch ops: every expert on every token, masked by the fixed
+    # selection and capacity; L = <dy, y> + aux + zc z with f fixed
+    l = x @ Wr.T
+    if scoring == "softmax":
+        g = torch.softmax(l, dim=1)
+        p = g
+    else:
+        g = torch.sigmoid(l)
+        p = g / g.sum(dim=1, keepdim=True)
+    T, E = g.shape
+    mask = torch.zeros(T, E, dtype=torch.float64)
+    for t in range(T):
+        for j in range(k):
+            if kept[t, j]:
+                mask[t, S[t, j]] = 1.0
+    sel = torch.zeros(T, E, dtype=torch.float64)
+    for t in range(T):
+        for j in range(k):
+            sel[t, S[t, j]] = 1.0
+    gw = g * sel
+    w = gw / gw.sum(dim=1, keepdim=True) if renorm else gw
+    y = torch.zeros_like(x)
+    for e in range(E):
+        h = torch.nn.functional.silu(x @ Wg[e].T) * (x @ Wu[e].T)
+        y = y + (w[:, e] * mask[:, e])[:, None] * (h @ Wd[e].T)
+    for sg, su, sd in shared:
+        y = y + (torch.nn.functional.silu(x @ sg.T) * (x @ su.T)) @ sd.T
+    aux = lam * E * (f * p.mean(dim=0)).sum()
+    z = (torch.logsumexp(l, dim=1) ** 2).mean()
+    return (dy * y).sum() + aux + zc * z
+
+
+def check_layer_backward(mod=O):
+    T, d, E, k, M = 14, 6, 4, 2, 5
+    rng = np.random.default_rng(51)
+    x = rng.standard_normal((T, d))
+    Wr = rng.standard_normal((E, d)) * 0.5
+    Wg = rng.standard_normal((E, M, d)) * 0.4
+    Wu = rng.standard_normal((E, M, d)) * 0.4
+    Wd = rng.standard_normal((E, d, M)) * 0.4
+    dy = rng.standard_normal((T, d))
+    sh = [tuple(rng.standard_normal(sz) * 0.4 for sz in ((M, d), (M, d), (d, M)))]
+    for scoring, renorm, c, shared in (("softmax", True, None, ()), ("sigmoid", False, 0.75, sh),
+                                       ("softmax", True, 0.6, sh)):
+        ref = mod.layer_backward(x, Wr, Wg, Wu, Wd, dy, k, shared=shared, c=c, renorm=renorm,
+                                 lam=0.3, z_coef=0.7, scoring=scoring)
+        fw = O.layer_forward(x, Wr, Wg, Wu, Wd, k, c=c, renorm=renorm, scoring=scoring)
+        S = fw["topk_idx"]
+        kept = fw["row"] >= 0
+        f = torch.tensor(fw["n"] / float(k * T))
+        ts = [torch.tensor(a, requires_grad=True) for a in (x, Wr, Wg, Wu, Wd)]
+        tsh = [tuple(torch.tensor(a, requires_grad=True) for a in s_) for s_ in shared]
+        L = _torch_layer_loss(*ts, torch.tensor(dy), S, kept, f, k, renorm, 0.3, 0.7, scoring, tsh)
+        L.backward()
+        for name, t_ in zip(("dx", "dW_r", "dW_gate", "dW_up", "dW_down"), ts):
+            assert np.allclose(ref[name], t_.grad.numpy(), rtol=1e-10, atol=1e-12), (scoring, name)
+        for (a, b_, c_), (tg, tu, td) in zip(ref["shared"], tsh):
+            assert np.allclose(a, tg.grad.numpy(), rtol=1e-10, atol=1e-12)
+            assert np.allclose(b_, tu.grad.numpy(), rtol=1e-10, atol=1e-12)
+            assert np.allclose(c_, td.grad.numpy(), rtol=1e-10, atol=1e-12)
+    # SiLU' against a central difference
+    zz = np.linspace(-6, 6, 25)
+    fd = (O.silu(zz + 1e-6) - O.silu(zz - 1e-6)) / 2e-6
+    assert np.allclose(mod.silu_grad(zz), fd, rtol=1e-7, atol=1e-9)
+
+
+def test_layer_backward_pins():
+    check_layer_backward()
+
+
 # ----------------------------------------------------------------------------- capacity/dispatch
 
 def test_capacity_closed_forms():
@@ -603,7 +676,8 @@ class _Mutant:
         self.__dict__.update(repl)
         # layer_forward looks its helpers up in the module, so rebind it to this namespace
         import types
-        for name in ("layer_forward", "route"):
+        for name in ("layer_forward", "route", "layer_backward", "balance_loss_backward",
+                     "layer_forward_expert_choice", "diagnostics"):
             fn = getattr(O, name)
             self.__dict__[name] = types.FunctionType(fn.__code__, self.__dict__, name, fn.__defaults__)
 
@@ -685,6 +759,11 @@ def _grad_no_centering(l, f, lam, z_coef, scoring="softmax"):
     return g * (lam * E * O._f64(f) / T)[None, :] + z_coef * (2.0 / T) * lse[:, None] * g
 
 
+def _silu_grad_wrong(z):
+    z = O._f64(z)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
 def _sigmoid_wrong_sign(l):
     l = O._f64(l)
     return 1.0 / (1.0 + np.exp(l))
@@ -710,6 +789,7 @@ def _sigmoid_unnormalised_P(g, scoring="softmax"):
     (dict(expert_choice=_ec_ties_high), [check_expert_choice]),
     (dict(expert_choice=_ec_smallest), [check_expert_choice]),
     (dict(balance_loss_grad_logits=_grad_no_centering), [check_loss_backward]),
+    (dict(silu_grad=_silu_grad_wrong), [check_layer_backward]),
 ])
 def test_planted_mistakes_are_caught(mutant, checks):
     m = _Mutant(**mutant)
