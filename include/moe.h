@@ -73,7 +73,8 @@ typedef enum {
   MOE_CALL_DISPATCH = 1,
   MOE_CALL_EXPERT_FFN = 2,
   MOE_CALL_LAYER = 3,
-  MOE_CALL_LOSS_BACKWARD = 4
+  MOE_CALL_LOSS_BACKWARD = 4,
+  MOE_CALL_LAYER_BACKWARD = 5
 } moe_call;
 
 #define MOE_E_MAX 256 /* routed experts per layer */
@@ -254,6 +255,33 @@ moe_status moe_balance_loss_backward(const moe_shape* s, const void* x, const vo
                                      const int32_t* n, float lambda, float z_coef,
                                      float* dlogits, float* dW_r, float* dx, void* ws,
                                      size_t ws_bytes, void* stream);
+
+/*
+ * moe_layer_backward -- gradients of <dy, y> + aux + z_coef z for the token-choice layer, with
+ * the selection, the capacity cut and f held fixed (they are discrete). Recomputes the forward
+ * (the same routing, placement and expert outputs as moe_layer_forward), then:
+ *   d out[row(t,j)] = w_tj dy_t, d w_tj = <dy_t, out[row(t,j)]>; gates through the
+ *   renormalisation ("MoE：条件计算与路由" §7 eq. (2)) and the softmax or sigmoid to the logits,
+ *   plus the balance-loss gradient of moe_balance_loss_backward; dW_r = dl^T x;
+ *   per kept row (SwiGLU of "深入理解 MoE ..." §10.2): dh = d out W_down[e],
+ *   dG = dh U SiLU'(G), dU = dh SiLU(G); dW_down[e] = sum d out^T h, dW_gate[e] = sum dG^T x,
+ *   dW_up[e] = sum dU^T x; dx_t = (dl W_r)_t + sum_j (dG W_gate + dU W_up)_row(t,j) + shared;
+ *   the shared experts take dy_t with weight 1.
+ * The recomputed h and out are rounded to dtype as in the forward; gradients are fp32.
+ *   x, W_r, b, W_gate, W_up, W_down, Ws_*: as moe_layer_forward; dy device [T, d] (dtype)
+ *   dx [T, d], dW_r [E, d], dW_gate, dW_up [E, M, d], dW_down [E, d, M] fp32 device out;
+ *   dWs_gate, dWs_up [S*M, d], dWs_down [d, S*M] fp32 device out (required when S > 0)
+ *   topk_idx device out [T, k] int32 or NULL: the selection the gradients were taken at
+ *   ws device workspace of moe_workspace_size(s, MOE_CALL_LAYER_BACKWARD) bytes
+ * Token choice only (expert choice: MOE_ERR_UNSUPPORTED).
+ */
+moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r, const float* b,
+                              const void* W_gate, const void* W_up, const void* W_down,
+                              const void* Ws_gate, const void* Ws_up, const void* Ws_down,
+                              const void* dy, float lambda, float z_coef, float* dx, float* dW_r,
+                              float* dW_gate, float* dW_up, float* dW_down, float* dWs_gate,
+                              float* dWs_up, float* dWs_down, int32_t* topk_idx, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /*
  * moe_set_stage_events -- profiling aid for moe_layer_forward (not a step of the method).

@@ -21,7 +21,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
-CALL_ROUTE, CALL_DISPATCH, CALL_EXPERT_FFN, CALL_LAYER, CALL_LOSS_BACKWARD = range(5)
+CALL_ROUTE, CALL_DISPATCH, CALL_EXPERT_FFN, CALL_LAYER, CALL_LOSS_BACKWARD, CALL_LAYER_BACKWARD = range(6)
 E_MAX, K_MAX = 256, 16
 
 
@@ -65,6 +65,9 @@ _SIG = {
     "moe_balance_loss_backward": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, ctypes.c_float,
                                                  ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t,
                                                  _P]),
+    "moe_layer_backward": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                          _P, ctypes.c_float, ctypes.c_float, _P, _P, _P, _P, _P,
+                                          _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
 }
 
 STAGES = ["route", "dispatch", "gemm_up", "gemm_down", "shared", "combine", "stats"]
@@ -308,6 +311,46 @@ def moe_balance_loss_backward(x: torch.Tensor, W_r: torch.Tensor, n: torch.Tenso
     return out
 
 
+def moe_layer_backward(x, W_r, W_gate, W_up, W_down, dy, k: int, b=None, shared=None,
+                       c: Optional[float] = None, renorm: bool = True, lam: float = 0.01,
+                       z_coef: float = 0.0, scoring: str = "softmax",
+                       ws: Optional[torch.Tensor] = None) -> dict:
+    """Gradients (fp32) of <dy, y> + aux + z_coef z for the token-choice layer; ``shared`` is the
+    stacked (Ws_gate, Ws_up, Ws_down) when the layer has shared experts."""
+    T, d = x.shape
+    E, M, _ = W_gate.shape
+    S = 0 if shared is None else shared[0].shape[0] // M
+    s = make_shape(T, d, E, k, M, S, c, renorm, x.dtype, scoring)
+    _check(check_shape(s), "moe_layer_backward")
+    dt = x.dtype
+    for name, t, shp in (("x", x, (T, d)), ("W_r", W_r, (E, d)), ("W_gate", W_gate, (E, M, d)),
+                         ("W_up", W_up, (E, M, d)), ("W_down", W_down, (E, d, M)),
+                         ("dy", dy, (T, d))):
+        _dev(t, name, dt, shp)
+    if b is not None:
+        _dev(b, "b", torch.float32, (E,))
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dx": torch.empty(T, d, **f32), "dW_r": torch.empty(E, d, **f32),
+           "dW_gate": torch.empty(E, M, d, **f32), "dW_up": torch.empty(E, M, d, **f32),
+           "dW_down": torch.empty(E, d, M, **f32),
+           "topk_idx": torch.empty(T, k, dtype=torch.int32, device=dev)}
+    sg = su = sd = None
+    if S > 0:
+        sg, su, sd = shared
+        out.update({"dWs_gate": torch.empty(S * M, d, **f32), "dWs_up": torch.empty(S * M, d, **f32),
+                    "dWs_down": torch.empty(d, S * M, **f32)})
+    if ws is None:
+        ws = workspace(s, CALL_LAYER_BACKWARD, dev)
+    _check(lib().moe_layer_backward(
+        ctypes.byref(s), _ptr(x), _ptr(W_r), _ptr(b), _ptr(W_gate), _ptr(W_up), _ptr(W_down),
+        _ptr(sg), _ptr(su), _ptr(sd), _ptr(dy), float(lam), float(z_coef), _ptr(out["dx"]),
+        _ptr(out["dW_r"]), _ptr(out["dW_gate"]), _ptr(out["dW_up"]), _ptr(out["dW_down"]),
+        _ptr(out.get("dWs_gate")), _ptr(out.get("dWs_up")), _ptr(out.get("dWs_down")),
+        _ptr(out["topk_idx"]), _ptr(ws), ws.numel(), _stream()), "moe_layer_backward")
+    return out
+
+
 class MoELayer:
     """Holds the sizes and a preallocated workspace; ``forward`` calls moe_layer_forward."""
 
@@ -397,6 +440,6 @@ def moe_layer_forward(x, W_r, W_gate, W_up, W_down, k: int, b=None, shared=None,
 
 
 __all__ = ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_balance_stats",
-           "moe_balance_loss_backward",
+           "moe_balance_loss_backward", "moe_layer_backward",
            "moe_layer_forward", "MoELayer", "make_shape", "capacity", "workspace_size",
            "check_shape", "status_string", "lib", "MoEError", "Shape", "moe_set_stage_events"]

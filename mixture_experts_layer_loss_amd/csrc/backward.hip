@@ -1,0 +1,456 @@
+// Backward of the token-choice layer: gradients of <dy, y> + aux + z_coef z with respect to x,
+// W_r and every expert weight, with the selection, the capacity cut and f held fixed (they are
+// discrete). The chain ("MoE：条件计算与路由" §7 eqs. (1)-(3) for y and the gates; "深入理解 MoE
+// (混合专家模型)：稀疏激活与高效扩展" §10.2 for SwiGLU; the balance-loss part as in
+// loss_backward.hip):
+//   combine:  d out[row(t,j)] = w_tj dy_t,  d w_tj = <dy_t, out[row(t,j)]> = <dy_t W_down[e], h>
+//             (kept slots; P_row = dy_t W_down[e] is formed once and gives both d w and dh)
+//   gates:    renorm: dg_e = (dw_e - sum_j w_j dw_j) / sum_S g;  else dg_e = dw_e   (e in S_t)
+//   scores:   softmax dl = g (dg - sum_e g dg);  sigmoid dl = s (1 - s) dg;  + balance-loss term
+//   down:     dh = w_tj P_row,  dW_down[e] = sum_rows d out^T h
+//   SwiGLU:   dG = dh U SiLU'(G),  dU = dh SiLU(G),  SiLU'(z) = sigma(z) (1 + z (1 - sigma(z)))
+//   up:       dx_row = dG W_gate[e] + dU W_up[e],  dW_gate[e] = sum_rows dG^T x,  dW_up likewise
+//   tokens:   dx_t = (dl W_r)_t + sum_j dx_row(t,j) (slot order) + shared experts' dx_t
+// Products run as fp32 SIMT tiles (64 x 64 outputs, 256 threads, 4 x 4 each, K staged 16 at a
+// time in LDS, accumulation in k order): "NN" products read A row-major and the weight K-major
+// (B[k][n]); weight gradients reduce over a group's rows with both operands K-major (rows), the
+// x operand gathered through perm_token. Groups never share a 64-row tile (tile table per group).
+// The pre-activations G, U are recomputed in fp32 and h = SiLU(G) U is formed in fp32 from them,
+// so the gradients follow the real-valued chain (the forward's bf16 roundings of h and of the
+// expert outputs are not differentiated).
+#include "moe_internal.h"
+
+#include <math.h>
+
+namespace moe {
+namespace {
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float ld<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float ld<bf16_t>(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Per kept row (one wave): t = perm_token[row], its slot j, gate w; d w_tj = <P_row, h_row>,
+// dh_row = w P_row, d out_row = w dy_t.
+template <typename T>
+__global__ __launch_bounds__(256) void bw_rows_kernel(const int32_t* __restrict__ offsets, int E,
+                                                       int d, int M, int k,
+                                                       const int32_t* __restrict__ perm_token,
+                                                       const int32_t* __restrict__ inv_perm,
+                                                       const float* __restrict__ topk_w,
+                                                       const T* __restrict__ dy,
+                                                       const float* __restrict__ P,
+                                                       const float* __restrict__ h,
+                                                       float* __restrict__ dw,
+                                                       float* __restrict__ dh,
+                                                       float* __restrict__ dout) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= offsets[E]) return;
+  const int64_t t = perm_token[row];
+  int slot = 0;
+  for (int j = 0; j < k; ++j)
+    if (inv_perm[t * k + j] == row) slot = j;
+  const float w = topk_w[t * k + slot];
+  float dot = 0.f;
+  for (int m = lane; m < M; m += 64) {
+    const float p = P[row * M + m];
+    dot = fmaf(p, h[row * M + m], dot);
+    dh[row * M + m] = w * p;
+  }
+  for (int i = lane; i < d; i += 64) dout[row * d + i] = w * ld<T>(dy, t * d + i);
+  dot = wave_sum(dot);
+  if (lane == 0) dw[t * k + slot] = dot;
+}
+
+// h = SiLU(G) U in fp32
+__global__ __launch_bounds__(256) void swiglu_fwd_kernel(int64_t count, const float* __restrict__ G,
+                                                          const float* __restrict__ U,
+                                                          float* __restrict__ h) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= count) return;
+  const float z = G[i];
+  h[i] = z / (1.f + expf(-z)) * U[i];
+}
+
+constexpr int kEPL = MOE_E_MAX / 64;
+
+// router: gates -> scores -> logits, plus the balance-loss gradient; one wave per token
+__global__ __launch_bounds__(256) void bw_router_kernel(
+    int64_t T, int E, int k, int renorm, int sigmoid, const float* __restrict__ lcol,
+    const float* __restrict__ scol, const int32_t* __restrict__ topk_idx,
+    const int32_t* __restrict__ inv_perm, const float* __restrict__ topk_w,
+    const float* __restrict__ dw, const int32_t* __restrict__ n,
+    double fden, float lambda, float z_coef, float* __restrict__ dl, float* __restrict__ dlT) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  // dg over the chosen experts (wave-uniform, slot order)
+  // d w of a dropped slot is 0 (it adds nothing to y)
+  float gsel = 0.f, wdw = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int e = topk_idx[t * k + j];
+    const float dwj = inv_perm[t * k + j] >= 0 ? dw[t * k + j] : 0.f;
+    gsel += scol[static_cast<int64_t>(e) * T + t];
+    wdw += topk_w[t * k + j] * dwj;
+  }
+  float l[kEPL], s[kEPL], a[kEPL], dg[kEPL];
+  float m = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < kEPL; ++q) {
+    const int e = lane + 64 * q;
+    const bool in = e < E;
+    l[q] = in ? lcol[static_cast<int64_t>(e) * T + t] : -INFINITY;
+    s[q] = in ? scol[static_cast<int64_t>(e) * T + t] : 0.f;
+    a[q] = in ? static_cast<float>(static_cast<double>(lambda) * E *
+                                   (static_cast<double>(n[e]) / fden) / static_cast<double>(T))
+              : 0.f;
+    dg[q] = 0.f;
+    m = fmaxf(m, l[q]);
+  }
+  for (int j = 0; j < k; ++j) {
+    const int e = topk_idx[t * k + j];
+    const float dwj = inv_perm[t * k + j] >= 0 ? dw[t * k + j] : 0.f;
+    const float v = renorm ? (dwj - wdw) / gsel : dwj;
+#pragma unroll
+    for (int q = 0; q < kEPL; ++q)
+      if (e == lane + 64 * q) dg[q] = v;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  float se = 0.f, S = 0.f, ca = 0.f, cg = 0.f;
+#pragma unroll
+  for (int q = 0; q < kEPL; ++q) {
+    se += expf(l[q] - m);
+    S += s[q];
+    ca += s[q] * a[q];
+    cg += s[q] * dg[q];
+  }
+  const float lse = m + logf(wave_sum(se));
+  S = sigmoid ? wave_sum(S) : 1.f;
+  const float c = wave_sum(ca) / S;
+  cg = wave_sum(cg);
+  const float zc = z_coef * 2.f * lse / static_cast<float>(T);
+#pragma unroll
+  for (int q = 0; q < kEPL; ++q) {
+    const int e = lane + 64 * q;
+    if (e < E) {
+      const float soft = expf(l[q] - lse);
+      float v = sigmoid ? s[q] * (1.f - s[q]) * ((a[q] - c) / S + dg[q])
+                        : s[q] * ((a[q] - c) + (dg[q] - cg));
+      v += zc * soft;
+      dl[t * E + e] = v;
+      dlT[static_cast<int64_t>(e) * T + t] = v;
+    }
+  }
+}
+
+constexpr int BMt = 64, BNt = 64, BKt = 16;
+
+__device__ __forceinline__ int find_group64(const int32_t* __restrict__ table, int groups,
+                                            int nb, int64_t L) {
+  int lo = 0, hi = groups;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (static_cast<int64_t>(table[mid]) * nb <= L) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// C[r][n] = sum_k A[r][k] B_g[k][n] (+ A2[r][k] B2_g[k][n]) for the rows r of group g
+template <typename TA, typename TB, bool TWO>
+__global__ __launch_bounds__(256) void nn_gemm_kernel(
+    const TA* __restrict__ A, const TA* __restrict__ A2, const int32_t* __restrict__ gather_a,
+    const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ tile_off, int groups, const TB* __restrict__ B,
+    const TB* __restrict__ B2, int64_t gstride, int N, int K, float* __restrict__ C) {
+  __shared__ float As[BKt][BMt + 4];
+  __shared__ float Bs[BKt][BNt + 4];
+  const int nb = (N + BNt - 1) / BNt;
+  const int64_t L = blockIdx.x;
+  if (L >= static_cast<int64_t>(tile_off[groups]) * nb) return;
+  const int g = find_group64(tile_off, groups, nb, L);
+  const int mt_g = tile_off[g + 1] - tile_off[g];
+  const int64_t local = L - static_cast<int64_t>(tile_off[g]) * nb;
+  const int n0 = static_cast<int>(local / mt_g) * BNt;
+  const int r0 = offsets[g] + static_cast<int>(local % mt_g) * BMt;
+  const int r1 = min(r0 + BMt, offsets[g + 1]);
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  float acc[4][4] = {};
+  for (int pass = 0; pass < (TWO ? 2 : 1); ++pass) {
+    const TA* Ap = pass == 0 ? A : A2;
+    const TB* Bp = (pass == 0 ? B : B2) + static_cast<int64_t>(g) * gstride;
+    for (int k0 = 0; k0 < K; k0 += BKt) {
+      for (int c = tid; c < BKt * BMt; c += 256) {
+        const int mm = c / BKt, kk = c % BKt;
+        const int r = r0 + mm, kx = k0 + kk;
+        float v = 0.f;
+        if (r < r1 && kx < K) {
+          const int64_t ar = gather_a != nullptr ? gather_a[r] : r;
+          v = ld<TA>(Ap, ar * K + kx);
+        }
+        As[kk][mm] = v;
+      }
+      for (int c = tid; c < BKt * BNt; c += 256) {
+        const int kk = c / BNt, nn = c % BNt;
+        const int kx = k0 + kk, n = n0 + nn;
+        Bs[kk][nn] = (kx < K && n < N) ? ld<TB>(Bp, static_cast<int64_t>(kx) * N + n) : 0.f;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < BKt; ++kk) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+      }
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + ty * 4 + i;
+    if (r >= r1) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n < N) C[static_cast<int64_t>(r) * N + n] = acc[i][j];
+    }
+  }
+}
+
+// C_g[m][n] = sum over the rows r of group g of A[r][m] B[b(r)][n], b(r) = gather[r] or r;
+// C is [groups][Ma][Nb]
+template <typename TA, typename TB>
+__global__ __launch_bounds__(256) void kk_gemm_kernel(const TA* __restrict__ A, int Ma,
+                                                       const TB* __restrict__ B, int Nb,
+                                                       const int32_t* __restrict__ gather,
+                                                       const int32_t* __restrict__ offsets,
+                                                       float* __restrict__ C) {
+  __shared__ float As[BKt][BMt + 4];
+  __shared__ float Bs[BKt][BNt + 4];
+  const int g = blockIdx.y;
+  const int nb = (Nb + BNt - 1) / BNt;
+  const int m0 = static_cast<int>(blockIdx.x / nb) * BMt;
+  const int n0 = static_cast<int>(blockIdx.x % nb) * BNt;
+  const int rb = offsets[g], re = offsets[g + 1];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  float acc[4][4] = {};
+  for (int k0 = rb; k0 < re; k0 += BKt) {
+    for (int c = tid; c < BKt * BMt; c += 256) {
+      const int kk = c / BMt, mm = c % BMt;
+      const int r = k0 + kk, m = m0 + mm;
+      As[kk][mm] = (r < re && m < Ma) ? ld<TA>(A, static_cast<int64_t>(r) * Ma + m) : 0.f;
+    }
+    for (int c = tid; c < BKt * BNt; c += 256) {
+      const int kk = c / BNt, nn = c % BNt;
+      const int r = k0 + kk, n = n0 + nn;
+      float v = 0.f;
+      if (r < re && n < Nb) {
+        const int64_t br = gather != nullptr ? gather[r] : r;
+        v = ld<TB>(B, br * Nb + n);
+      }
+      Bs[kk][nn] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BKt; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  float* Cg = C + static_cast<int64_t>(g) * Ma * Nb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m >= Ma) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n < Nb) Cg[static_cast<int64_t>(m) * Nb + n] = acc[i][j];
+    }
+  }
+}
+
+// dG = dh U SiLU'(G), dU = dh SiLU(G), elementwise over count values (G, U in the layer dtype)
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_bw_kernel(int64_t count, const float* __restrict__ dh,
+                                                         const T* __restrict__ G,
+                                                         const T* __restrict__ U,
+                                                         float* __restrict__ dG,
+                                                         float* __restrict__ dU) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= count) return;
+  const float z = ld<T>(G, i), u = ld<T>(U, i), gh = dh[i];
+  const float sg = 1.f / (1.f + expf(-z));
+  dG[i] = gh * u * sg * (1.f + z * (1.f - sg));
+  dU[i] = gh * z * sg;
+}
+
+// dx_t += sum_j dx_perm[row(t,j)] (slot order) + dx_sh[t]; one wave per token
+__global__ __launch_bounds__(256) void bw_dx_kernel(int64_t Tn, int d, int k,
+                                                     const int32_t* __restrict__ inv_perm,
+                                                     const float* __restrict__ dx_perm,
+                                                     const float* __restrict__ dx_sh,
+                                                     float* __restrict__ dx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  for (int i = lane; i < d; i += 64) {
+    float v = dx[t * d + i];
+    for (int j = 0; j < k; ++j) {
+      const int row = inv_perm[t * k + j];
+      if (row >= 0) v += dx_perm[static_cast<int64_t>(row) * d + i];
+    }
+    if (dx_sh != nullptr) v += dx_sh[t * d + i];
+    dx[t * d + i] = v;
+  }
+}
+
+template <typename TA>
+hipError_t nn_dispatch(int dtype_b, bool two, const void* A, const void* A2,
+                       const int32_t* gather_a, const int32_t* offsets, const int32_t* tile_off, int groups,
+                       int64_t max_tiles, const void* B, const void* B2, int64_t gstride, int N,
+                       int K, float* C, hipStream_t st) {
+  const int64_t grid = max_tiles * ((N + BNt - 1) / BNt);
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 gd(static_cast<unsigned>(grid)), bd(256);
+  const TA* a = static_cast<const TA*>(A);
+  const TA* a2 = static_cast<const TA*>(A2);
+  if (dtype_b == MOE_F32) {
+    const float* b = static_cast<const float*>(B);
+    const float* b2 = static_cast<const float*>(B2);
+    if (two)
+      hipLaunchKernelGGL((nn_gemm_kernel<TA, float, true>), gd, bd, 0, st, a, a2, gather_a,
+                         offsets, tile_off, groups, b, b2, gstride, N, K, C);
+    else
+      hipLaunchKernelGGL((nn_gemm_kernel<TA, float, false>), gd, bd, 0, st, a, a2, gather_a,
+                         offsets, tile_off, groups, b, b2, gstride, N, K, C);
+  } else {
+    const bf16_t* b = static_cast<const bf16_t*>(B);
+    const bf16_t* b2 = static_cast<const bf16_t*>(B2);
+    if (two)
+      hipLaunchKernelGGL((nn_gemm_kernel<TA, bf16_t, true>), gd, bd, 0, st, a, a2, gather_a,
+                         offsets, tile_off, groups, b, b2, gstride, N, K, C);
+    else
+      hipLaunchKernelGGL((nn_gemm_kernel<TA, bf16_t, false>), gd, bd, 0, st, a, a2, gather_a,
+                         offsets, tile_off, groups, b, b2, gstride, N, K, C);
+  }
+  return hipGetLastError();
+}
+
+template <typename TA>
+hipError_t kk_dispatch(int dtype_b, const void* A, int Ma, const void* B, int Nb,
+                       const int32_t* gather, const int32_t* offsets, int groups, float* C,
+                       hipStream_t st) {
+  const int64_t tiles = static_cast<int64_t>((Ma + BMt - 1) / BMt) * ((Nb + BNt - 1) / BNt);
+  if (tiles <= 0 || groups <= 0) return hipSuccess;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 gd(static_cast<unsigned>(tiles), static_cast<unsigned>(groups)), bd(256);
+  if (dtype_b == MOE_F32)
+    hipLaunchKernelGGL((kk_gemm_kernel<TA, float>), gd, bd, 0, st, static_cast<const TA*>(A), Ma,
+                       static_cast<const float*>(B), Nb, gather, offsets, C);
+  else
+    hipLaunchKernelGGL((kk_gemm_kernel<TA, bf16_t>), gd, bd, 0, st, static_cast<const TA*>(A), Ma,
+                       static_cast<const bf16_t*>(B), Nb, gather, offsets, C);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bw_rows(int dtype, const int32_t* offsets, int E, int64_t R, int d, int M,
+                          int k, const int32_t* perm_token, const int32_t* inv_perm,
+                          const float* topk_w, const void* dy, const float* P, const float* h,
+                          float* dw, float* dh, float* dout, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(cdiv(R, 4)));
+  if (R <= 0) return hipSuccess;
+  if (dtype == MOE_F32)
+    hipLaunchKernelGGL(bw_rows_kernel<float>, grid, dim3(256), 0, st, offsets, E, d, M, k,
+                       perm_token, inv_perm, topk_w, static_cast<const float*>(dy), P, h, dw, dh,
+                       dout);
+  else
+    hipLaunchKernelGGL(bw_rows_kernel<bf16_t>, grid, dim3(256), 0, st, offsets, E, d, M, k,
+                       perm_token, inv_perm, topk_w, static_cast<const bf16_t*>(dy), P, h, dw,
+                       dh, dout);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_fwd(int64_t count, const float* G, const float* U, float* h,
+                             hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(static_cast<unsigned>(cdiv(count, 256))), dim3(256),
+                     0, st, count, G, U, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_router(int64_t T, int E, int k, int renorm, int sigmoid, const float* lcol,
+                            const float* scol, const int32_t* topk_idx, const int32_t* inv_perm,
+                            const float* topk_w, const float* dw, const int32_t* n, double fden,
+                            float lambda, float z_coef, float* dl, float* dlT, hipStream_t st) {
+  hipLaunchKernelGGL(bw_router_kernel, dim3(static_cast<unsigned>(cdiv(T, 4))), dim3(256), 0, st,
+                     T, E, k, renorm, sigmoid, lcol, scol, topk_idx, inv_perm, topk_w, dw, n, fden,
+                     lambda, z_coef, dl, dlT);
+  return hipGetLastError();
+}
+
+hipError_t launch_nn_gemm(int dtype_a, int dtype_b, bool two, const void* A, const void* A2,
+                          const int32_t* gather_a, const int32_t* offsets, const int32_t* tile_off,
+                          int groups, int64_t max_tiles, const void* B, const void* B2,
+                          int64_t gstride, int N, int K, float* C, hipStream_t st) {
+  return dtype_a == MOE_F32
+             ? nn_dispatch<float>(dtype_b, two, A, A2, gather_a, offsets, tile_off, groups,
+                                  max_tiles, B, B2, gstride, N, K, C, st)
+             : nn_dispatch<bf16_t>(dtype_b, two, A, A2, gather_a, offsets, tile_off, groups,
+                                   max_tiles, B, B2, gstride, N, K, C, st);
+}
+
+hipError_t launch_kk_gemm(int dtype_a, int dtype_b, const void* A, int Ma, const void* B, int Nb,
+                          const int32_t* gather, const int32_t* offsets, int groups, float* C,
+                          hipStream_t st) {
+  return dtype_a == MOE_F32
+             ? kk_dispatch<float>(dtype_b, A, Ma, B, Nb, gather, offsets, groups, C, st)
+             : kk_dispatch<bf16_t>(dtype_b, A, Ma, B, Nb, gather, offsets, groups, C, st);
+}
+
+hipError_t launch_swiglu_bw(int dtype, int64_t count, const float* dh, const void* G,
+                            const void* U, float* dG, float* dU, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(cdiv(count, 256)));
+  if (dtype == MOE_F32)
+    hipLaunchKernelGGL(swiglu_bw_kernel<float>, grid, dim3(256), 0, st, count, dh,
+                       static_cast<const float*>(G), static_cast<const float*>(U), dG, dU);
+  else
+    hipLaunchKernelGGL(swiglu_bw_kernel<bf16_t>, grid, dim3(256), 0, st, count, dh,
+                       static_cast<const bf16_t*>(G), static_cast<const bf16_t*>(U), dG, dU);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_dx(int64_t T, int d, int k, const int32_t* inv_perm, const float* dx_perm,
+                        const float* dx_sh, float* dx, hipStream_t st) {
+  hipLaunchKernelGGL(bw_dx_kernel, dim3(static_cast<unsigned>(cdiv(T, 4))), dim3(256), 0, st, T,
+                     d, k, inv_perm, dx_perm, dx_sh, dx);
+  return hipGetLastError();
+}
+
+}  // namespace moe

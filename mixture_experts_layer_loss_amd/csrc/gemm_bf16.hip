@@ -91,7 +91,8 @@ __device__ __forceinline__ void sched_substep() {
 }
 
 // One MR x 256 output tile of group g: rows [row_begin, row_begin + rows_here), output columns
-// [n0, n0 + BNO). EPI 0: SwiGLU (B0 = W_gate, B1 = W_up); EPI 1: plain (B0 = W_down).
+// [n0, n0 + BNO). EPI 0: SwiGLU (B0 = W_gate, B1 = W_up); EPI 1: plain (B0 = W_down); EPI 2:
+// plain with fp32 output (C is then float), stored straight from the accumulators.
 // KTAIL: K is not a multiple of 64 (the last k-slice is zero-padded).
 template <int EPI, bool KTAIL, bool GATHER, int MR>
 __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __restrict__ A,
@@ -261,6 +262,23 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
   for (; kt + 2 < nk; ++kt) kstep(kt, T_{}, T_{});
   if (kt + 1 < nk) kstep(kt++, T_{}, F_{});
   kstep(kt, F_{}, F_{});
+  if constexpr (EPI == 2) {
+    // fp32 output: each lane stores its accumulators (32 consecutive columns per row and wave)
+    float* C32 = reinterpret_cast<float*>(C);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int col = n0 + wn * G::WCOLS + j * 32 + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * G::WROWS + i * 32 + (r >> 2) * 8 + lk * 4 + (r & 3);
+          if (row < rows_here && col < N)
+            C32[static_cast<int64_t>(row_begin + row) * N + col] = acc[i][j][r];
+        }
+      }
+    return;
+  }
   __syncthreads();
 
   // ---- epilogue: registers -> LDS tile [MR][BNO + 8] (bf16) -> coalesced 16-byte stores
@@ -417,6 +435,23 @@ hipError_t launch_gemm_up_bf16(int groups, int d, int Mg, const void* rows,
                                 H, st);
   return launch_gemm<0, false>(A, nullptr, offsets, tile_off, groups, max_tiles, Wg, Wu, gs, Mg, d,
                                H, st);
+}
+
+// C[r] = A_r B_g^T for the rows of group g (A_r = rows[gather[r]] when gather != NULL): the plain
+// epilogue with any N and K (the backward recomputes the gate and up pre-activations with it)
+// (fp32 output)
+hipError_t launch_gemm_plain_bf16(int groups, const void* rows, const int32_t* gather,
+                                  const int32_t* offsets, const int32_t* tile_off,
+                                  int64_t max_tiles, const void* B, int64_t group_stride, int N,
+                                  int K, void* C, hipStream_t st) {
+  const bf16_t* A = static_cast<const bf16_t*>(rows);
+  const bf16_t* Bp = static_cast<const bf16_t*>(B);
+  bf16_t* Cp = static_cast<bf16_t*>(C);  // holds floats (EPI 2)
+  if (gather != nullptr)
+    return launch_gemm<2, true>(A, gather, offsets, tile_off, groups, max_tiles, Bp, nullptr,
+                                group_stride, N, K, Cp, st);
+  return launch_gemm<2, false>(A, nullptr, offsets, tile_off, groups, max_tiles, Bp, nullptr,
+                               group_stride, N, K, Cp, st);
 }
 
 hipError_t launch_gemm_down_bf16(int groups, int d, int Mg, const int32_t* offsets,

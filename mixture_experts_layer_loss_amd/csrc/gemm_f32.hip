@@ -104,6 +104,19 @@ hipError_t launch_gemm_up_f32(int groups, int d, int Mg, const void* rows,
   return hipGetLastError();
 }
 
+hipError_t launch_gemm_plain_f32(int groups, const void* rows, const int32_t* gather,
+                                 const int32_t* offsets, const int32_t* tile_off,
+                                 int64_t max_tiles, const void* B, int64_t group_stride, int N,
+                                 int K, void* C, hipStream_t st) {
+  const int64_t grid = max_tiles * cdiv(N, BN);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(grouped_gemm_f32_kernel<1>, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                     st, static_cast<const float*>(rows), gather, offsets, tile_off, groups,
+                     static_cast<const float*>(B), nullptr, group_stride, N, K,
+                     static_cast<float*>(C));
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_down_f32(int groups, int d, int Mg, const int32_t* offsets,
                                 const int32_t* tile_off, int64_t max_tiles, const void* W_down,
                                 const void* h, void* out, hipStream_t st) {

@@ -18,6 +18,25 @@ hipError_t launch_gemm_up_f32(int groups, int d, int Mg, const void* rows,
                               const int32_t* gather, const int32_t* offsets,
                               const int32_t* tile_off, int64_t max_tiles, const void* W_gate,
                               const void* W_up, void* h, hipStream_t st);
+hipError_t launch_gemm_plain_bf16(int groups, const void* rows, const int32_t* gather,
+                                  const int32_t* offsets, const int32_t* tile_off,
+                                  int64_t max_tiles, const void* B, int64_t group_stride, int N,
+                                  int K, void* C, hipStream_t st);
+hipError_t launch_gemm_plain_f32(int groups, const void* rows, const int32_t* gather,
+                                 const int32_t* offsets, const int32_t* tile_off,
+                                 int64_t max_tiles, const void* B, int64_t group_stride, int N,
+                                 int K, void* C, hipStream_t st);
+
+hipError_t launch_gemm_plain(int dtype, int groups, const void* rows, const int32_t* gather,
+                             const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
+                             const void* B, int64_t group_stride, int N, int K, void* C,
+                             hipStream_t st) {
+  return dtype == MOE_F32 ? launch_gemm_plain_f32(groups, rows, gather, offsets, tile_off,
+                                                  max_tiles, B, group_stride, N, K, C, st)
+                          : launch_gemm_plain_bf16(groups, rows, gather, offsets, tile_off,
+                                                   max_tiles, B, group_stride, N, K, C, st);
+}
+
 hipError_t launch_gemm_down_f32(int groups, int d, int Mg, const int32_t* offsets,
                                 const int32_t* tile_off, int64_t max_tiles, const void* W_down,
                                 const void* h, void* out, hipStream_t st);
@@ -200,6 +219,57 @@ LossBackwardPlan plan_loss_backward(Carve& c, const moe_shape* s) {
   return p;
 }
 
+// The backward recomputes the forward (LayerPlan) and keeps, per routed row, the gate and up
+// pre-activations (dtype) and the fp32 gradients d out, dh, dG, dU and dx_row.
+struct LayerBackwardPlan {
+  LayerPlan f;
+  float* cols;                    // [2][E][T] logits and scores
+  int32_t *tile64, *sh_tile64;    // 64-row tile tables of the fp32 products
+  float *G, *U;                   // [R, M] fp32 pre-activations
+  float *h, *P;                   // [R, M] fp32: SiLU(G) U and dy_t W_down[e]
+  float *dout, *dw, *dl, *dlT, *dh, *dG, *dU, *dxr, *partial;
+  int ks_w;
+  float *Gs, *Us;                 // shared experts [T, S M] fp32
+  float *hs, *dhs, *dGs, *dUs, *dxs;   // [T, S M] and [T, d]
+};
+LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
+  LayerBackwardPlan p;
+  p.f = plan_layer(c, s);
+  const size_t R = static_cast<size_t>(routed_rows(s)), T = static_cast<size_t>(s->T);
+  const size_t d = s->d, M = s->M, E = s->E;
+  p.cols = c.take<float>(2 * E * T);
+  p.tile64 = c.take<int32_t>(3 * (E + 1));
+  p.sh_tile64 = c.take<int32_t>(3 * 2);
+  p.G = c.take<float>(R * M);
+  p.U = c.take<float>(R * M);
+  p.h = c.take<float>(R * M);
+  p.P = c.take<float>(R * M);
+  p.dout = c.take<float>(R * d);
+  p.dw = c.take<float>(T * s->k);
+  p.dl = c.take<float>(T * E);
+  p.dlT = c.take<float>(T * E);
+  p.dh = c.take<float>(R * M);
+  p.dG = c.take<float>(R * M);
+  p.dU = c.take<float>(R * M);
+  p.dxr = c.take<float>(R * d);
+  p.ks_w = kmajor_splits(s->E, s->d, s->T);
+  p.partial = c.take<float>(p.ks_w > 1 ? static_cast<size_t>(p.ks_w) * E * d : 1);
+  if (s->S > 0) {
+    const size_t SM = static_cast<size_t>(s->S) * M;
+    p.Gs = c.take<float>(T * SM);
+    p.Us = c.take<float>(T * SM);
+    p.hs = c.take<float>(T * SM);
+    p.dhs = c.take<float>(T * SM);
+    p.dGs = c.take<float>(T * SM);
+    p.dUs = c.take<float>(T * SM);
+    p.dxs = c.take<float>(T * d);
+  } else {
+    p.Gs = p.Us = nullptr;
+    p.hs = p.dhs = p.dGs = p.dUs = p.dxs = nullptr;
+  }
+  return p;
+}
+
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // Profiling aid: events recorded at the end of each moe_layer_forward stage (see moe.h).
@@ -260,6 +330,7 @@ size_t moe_workspace_size(const moe_shape* s, int call) {
     case MOE_CALL_EXPERT_FFN: c.take<int32_t>(3 * (MOE_E_MAX + 1)); break;
     case MOE_CALL_LAYER: plan_layer(c, s); break;
     case MOE_CALL_LOSS_BACKWARD: plan_loss_backward(c, s); break;
+    case MOE_CALL_LAYER_BACKWARD: plan_layer_backward(c, s); break;
     default: return 0;
   }
   return c.used;
@@ -493,6 +564,135 @@ moe_status moe_balance_loss_backward(const moe_shape* s, const void* x, const vo
                            p.partial, hs);
   if (e == hipSuccess && dx)  // dx [T][d] = sum_e dl[e][t] W_r[e][:]
     e = launch_kmajor_gemm(s->dtype, s->T, s->d, s->E, 1, p.dlT, W_r, dx, nullptr, hs);
+  return hip_status(e);
+}
+
+moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r, const float* b,
+                              const void* W_gate, const void* W_up, const void* W_down,
+                              const void* Ws_gate, const void* Ws_up, const void* Ws_down,
+                              const void* dy, float lambda, float z_coef, float* dx, float* dW_r,
+                              float* dW_gate, float* dW_up, float* dW_down, float* dWs_gate,
+                              float* dWs_up, float* dWs_down, int32_t* topk_idx, void* ws,
+                              size_t ws_bytes, void* stream) {
+  moe_status st = moe_check_shape(s);
+  if (st != MOE_OK) return st;
+  if (expert_choice(s)) return MOE_ERR_UNSUPPORTED;
+  if (!x || !W_r || !W_gate || !W_up || !W_down || !dy) return MOE_ERR_INVALID_ARGUMENT;
+  if (!dx || !dW_r || !dW_gate || !dW_up || !dW_down) return MOE_ERR_INVALID_ARGUMENT;
+  if (s->S > 0 && (!Ws_gate || !Ws_up || !Ws_down || !dWs_gate || !dWs_up || !dWs_down))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (isnan(lambda) || isnan(z_coef)) return MOE_ERR_INVALID_ARGUMENT;
+  if (s->T * static_cast<int64_t>(s->E) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  const void* tensors[] = {x, W_r, W_gate, W_up, W_down, dy};
+  for (const void* t : tensors)
+    if (!aligned16(t)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!ws || ws_bytes < moe_workspace_size(s, MOE_CALL_LAYER_BACKWARD)) return MOE_ERR_WORKSPACE;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  Carve c(ws);
+  LayerBackwardPlan p = plan_layer_backward(c, s);
+  LayerPlan& f = p.f;
+  int32_t* idx = topk_idx ? topk_idx : f.topk_idx;
+  const int64_t C = capacity_of(s);
+  const int BM = gemm_bm(s);
+  const int nblk = static_cast<int>(route_blocks(s));
+  const int eb = elem_bytes(s);
+  const int64_t R = routed_rows(s);
+  const int64_t max_tiles = cdiv(R, BM) + s->E;
+  const int64_t max_t64 = cdiv(R, 64) + s->E;
+  const int64_t dM = static_cast<int64_t>(s->d) * s->M;
+  const size_t ET = static_cast<size_t>(s->E) * s->T;
+  // ---- forward recompute: routing, placement, fp32 pre-activations and h, score columns
+  hipError_t e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s), x, W_r, b, idx,
+                              f.topk_w, f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart, nullptr, hs);
+  if (e == hipSuccess)
+    e = launch_scan(s->T, s->E, C, nblk, f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart, f.block_base,
+                    f.n, f.gsum, f.lse2sum, f.hsum, f.kept, f.overflow, f.offsets, f.tile_off, BM,
+                    hs);
+  if (e == hipSuccess)
+    e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx, route_block_tokens(s->dtype, s->E),
+                       f.block_base, f.offsets, nullptr, f.perm_token, f.inv_perm, hs);
+  if (e == hipSuccess)
+    e = launch_gemm_plain(s->dtype, s->E, x, f.perm_token, f.offsets, f.tile_off, max_tiles,
+                          W_gate, dM, s->M, s->d, p.G, hs);
+  if (e == hipSuccess)
+    e = launch_gemm_plain(s->dtype, s->E, x, f.perm_token, f.offsets, f.tile_off, max_tiles, W_up,
+                          dM, s->M, s->d, p.U, hs);
+  if (e == hipSuccess) e = launch_swiglu_fwd(R * s->M, p.G, p.U, p.h, hs);
+  if (e == hipSuccess)
+    e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s) | kRouteExpertChoice, x, W_r,
+                     nullptr, nullptr, nullptr, f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart, p.cols,
+                     hs);
+  if (e == hipSuccess) e = launch_schedule(s->E, f.offsets, p.tile64, 64, hs);
+  // ---- combine: P_row = dy_t W_down[e] gives d w = <P, h> and dh = w P; d out = w dy_t
+  if (e == hipSuccess)
+    e = launch_nn_gemm(s->dtype, s->dtype, false, dy, nullptr, f.perm_token, f.offsets, p.tile64,
+                       s->E, max_t64, W_down, nullptr, dM, s->M, s->d, p.P, hs);
+  if (e == hipSuccess)
+    e = launch_bw_rows(s->dtype, f.offsets, s->E, R, s->d, s->M, s->k, f.perm_token, f.inv_perm,
+                       f.topk_w, dy, p.P, p.h, p.dw, p.dh, p.dout, hs);
+  if (e == hipSuccess)
+    e = launch_bw_router(s->T, s->E, s->k, s->renorm, s->scoring == MOE_SCORE_SIGMOID, p.cols,
+                         p.cols + ET, idx, f.inv_perm, f.topk_w, p.dw, f.n, stats_fden(s), lambda,
+                         z_coef, p.dl, p.dlT, hs);
+  // ---- routed experts
+  if (e == hipSuccess)
+    e = launch_swiglu_bw(MOE_F32, R * s->M, p.dh, p.G, p.U, p.dG, p.dU, hs);
+  if (e == hipSuccess)  // dx_row = dG W_gate[e] + dU W_up[e]
+    e = launch_nn_gemm(MOE_F32, s->dtype, true, p.dG, p.dU, nullptr, f.offsets, p.tile64, s->E,
+                       max_t64, W_gate, W_up, dM, s->d, s->M, p.dxr, hs);
+  if (e == hipSuccess)  // dW_down[e] = sum_rows d out^T h
+    e = launch_kk_gemm(MOE_F32, MOE_F32, p.dout, s->d, p.h, s->M, nullptr, f.offsets, s->E,
+                       dW_down, hs);
+  if (e == hipSuccess)  // dW_gate[e] = sum_rows dG^T x
+    e = launch_kk_gemm(MOE_F32, s->dtype, p.dG, s->M, x, s->d, f.perm_token, f.offsets, s->E,
+                       dW_gate, hs);
+  if (e == hipSuccess)
+    e = launch_kk_gemm(MOE_F32, s->dtype, p.dU, s->M, x, s->d, f.perm_token, f.offsets, s->E,
+                       dW_up, hs);
+  // ---- router weights and the router part of dx
+  if (e == hipSuccess)
+    e = launch_kmajor_gemm(s->dtype, s->E, s->d, s->T, p.ks_w, p.dl, x, dW_r, p.partial, hs);
+  if (e == hipSuccess)
+    e = launch_kmajor_gemm(s->dtype, s->T, s->d, s->E, 1, p.dlT, W_r, dx, nullptr, hs);
+  // ---- shared experts: one group of all T rows, output gradient dy
+  if (e == hipSuccess && s->S > 0) {
+    const int SM = s->S * s->M;
+    const int64_t sh_tiles = cdiv(s->T, BM);
+    const int64_t dSM = static_cast<int64_t>(s->d) * SM;
+    e = launch_shared_table(s->T, BM, f.sh_offsets, f.sh_tile_off, hs);
+    if (e == hipSuccess)
+      e = launch_gemm_plain(s->dtype, 1, x, nullptr, f.sh_offsets, f.sh_tile_off, sh_tiles,
+                            Ws_gate, dSM, SM, s->d, p.Gs, hs);
+    if (e == hipSuccess)
+      e = launch_gemm_plain(s->dtype, 1, x, nullptr, f.sh_offsets, f.sh_tile_off, sh_tiles, Ws_up,
+                            dSM, SM, s->d, p.Us, hs);
+    if (e == hipSuccess)
+      e = launch_swiglu_fwd(static_cast<int64_t>(s->T) * SM, p.Gs, p.Us, p.hs, hs);
+    if (e == hipSuccess) e = launch_schedule(1, f.sh_offsets, p.sh_tile64, 64, hs);
+    const int64_t sh_t64 = cdiv(s->T, 64) + 1;
+    if (e == hipSuccess)
+      e = launch_nn_gemm(s->dtype, s->dtype, false, dy, nullptr, nullptr, f.sh_offsets,
+                         p.sh_tile64, 1, sh_t64, Ws_down, nullptr, dSM, SM, s->d, p.dhs, hs);
+    if (e == hipSuccess)
+      e = launch_swiglu_bw(MOE_F32, static_cast<int64_t>(s->T) * SM, p.dhs, p.Gs, p.Us, p.dGs,
+                           p.dUs, hs);
+    if (e == hipSuccess)
+      e = launch_nn_gemm(MOE_F32, s->dtype, true, p.dGs, p.dUs, nullptr, f.sh_offsets,
+                         p.sh_tile64, 1, sh_t64, Ws_gate, Ws_up, dSM, s->d, SM, p.dxs, hs);
+    if (e == hipSuccess)
+      e = launch_kk_gemm(s->dtype, MOE_F32, dy, s->d, p.hs, SM, nullptr, f.sh_offsets, 1,
+                         dWs_down, hs);
+    if (e == hipSuccess)
+      e = launch_kk_gemm(MOE_F32, s->dtype, p.dGs, SM, x, s->d, nullptr, f.sh_offsets, 1,
+                         dWs_gate, hs);
+    if (e == hipSuccess)
+      e = launch_kk_gemm(MOE_F32, s->dtype, p.dUs, SM, x, s->d, nullptr, f.sh_offsets, 1, dWs_up,
+                         hs);
+  }
+  // ---- tokens
+  if (e == hipSuccess)
+    e = launch_bw_dx(s->T, s->d, s->k, f.inv_perm, p.dxr, s->S > 0 ? p.dxs : nullptr, dx, hs);
   return hip_status(e);
 }
 

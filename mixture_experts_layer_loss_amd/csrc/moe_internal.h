@@ -125,6 +125,39 @@ int kmajor_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_kmajor_gemm(int dtype_b, int64_t M, int64_t N, int64_t K, int KS, const float* A,
                               const void* B, float* C, float* partial, hipStream_t st);
 
+// Plain grouped GEMM C[r] = A_r B_g^T (A_r = rows[gather[r]] when gather != NULL), dtype in,
+// fp32 out.
+hipError_t launch_gemm_plain(int dtype, int groups, const void* rows, const int32_t* gather,
+                             const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
+                             const void* B, int64_t group_stride, int N, int K, void* C,
+                             hipStream_t st);
+
+// Backward (backward.hip). Per kept row: dw [T, k] (slot of the row), dh = w P, dout = w dy_t.
+hipError_t launch_bw_rows(int dtype, const int32_t* offsets, int E, int64_t R, int d, int M,
+                          int k, const int32_t* perm_token, const int32_t* inv_perm,
+                          const float* topk_w, const void* dy, const float* P, const float* h,
+                          float* dw, float* dh, float* dout, hipStream_t st);
+hipError_t launch_swiglu_fwd(int64_t count, const float* G, const float* U, float* h,
+                             hipStream_t st);
+hipError_t launch_bw_router(int64_t T, int E, int k, int renorm, int sigmoid, const float* lcol,
+                            const float* scol, const int32_t* topk_idx, const int32_t* inv_perm,
+                            const float* topk_w, const float* dw, const int32_t* n, double fden,
+                            float lambda, float z_coef, float* dl, float* dlT, hipStream_t st);
+// C[r][n] (fp32) = sum_k A[a(r)][k] B_g[k][n] (+ A2 B2_g), a(r) = gather_a[r] or r; 64-row tile
+// table tile_off per group
+hipError_t launch_nn_gemm(int dtype_a, int dtype_b, bool two, const void* A, const void* A2,
+                          const int32_t* gather_a, const int32_t* offsets, const int32_t* tile_off,
+                          int groups, int64_t max_tiles, const void* B, const void* B2,
+                          int64_t gstride, int N, int K, float* C, hipStream_t st);
+// C_g[m][n] (fp32, [groups][Ma][Nb]) = sum over rows r of group g of A[r][m] B[b(r)][n]
+hipError_t launch_kk_gemm(int dtype_a, int dtype_b, const void* A, int Ma, const void* B, int Nb,
+                          const int32_t* gather, const int32_t* offsets, int groups, float* C,
+                          hipStream_t st);
+hipError_t launch_swiglu_bw(int dtype, int64_t count, const float* dh, const void* G,
+                            const void* U, float* dG, float* dU, hipStream_t st);
+hipError_t launch_bw_dx(int64_t T, int d, int k, const int32_t* inv_perm, const float* dx_perm,
+                        const float* dx_sh, float* dx, hipStream_t st);
+
 // Tile table of the shared experts (one group of all T rows).
 hipError_t launch_shared_table(int64_t T, int BM, int32_t* offsets, int32_t* tile_off,
                                hipStream_t st);

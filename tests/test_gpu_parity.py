@@ -270,6 +270,56 @@ def test_balance_loss_backward(gpu, base, kw):
         assert e < 2e-4, (key, e)
 
 
+# -------------------------------------------------------------------------- layer backward
+
+LAYER_BW_CASES = [
+    ("tiny_fp32", {}),
+    ("mixtral_8x7b", dict(T=300, d=256, M=192)),
+    ("deepseekmoe_16b", dict(T=200, d=128, M=136, c=1.0)),        # shared experts, drops, N tail
+    ("deepseek_v2", dict(T=150, d=200, M=72, scoring="sigmoid")),  # bias, sigmoid, K tail
+    ("mixtral_8x7b", dict(T=100, d=64, M=64, E=6, k=3, renorm=False)),
+]
+
+
+@pytest.mark.parametrize("base,kw", LAYER_BW_CASES)
+def test_layer_backward(gpu, base, kw):
+    """Every gradient against the fp64 oracle fed the GPU's selection (the same staged parity as
+    the forward). The GPU follows the real-valued chain in fp32 (pre-activations, h and
+    P = dy W_down are fp32; the inputs are the same bf16 values on both sides), so what remains is
+    fp32 accumulation over at most a few thousand terms per output (~1e-5 relative): bound 1e-4 in
+    the max relative error of every output, for bf16 and fp32 layers alike."""
+    cfg = cfg_of(base, **kw)
+    say(f"[layer backward] {cfg}")
+    inp = workloads.make_inputs(cfg)
+    d_ = to_dev(inp, gpu)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dy = (torch.randn(cfg.T, cfg.d, generator=torch.Generator().manual_seed(11))).to(dt)
+    out = moe.moe_layer_backward(d_.x, d_.W_r, d_.W_gate, d_.W_up, d_.W_down, dy.to(gpu), cfg.k,
+                                 b=d_.b, shared=d_.shared_fused(), c=cfg.c, renorm=cfg.renorm,
+                                 lam=cfg.lam, z_coef=0.3, scoring=cfg.scoring)
+    torch.cuda.synchronize()
+    gidx = out["topk_idx"].cpu().numpy().astype(np.int64)
+    orc_route = O.route(O._f64(inp.x), O._f64(inp.W_r), cfg.k,
+                        None if inp.b is None else O._f64(inp.b), cfg.renorm, cfg.scoring)
+    check_selection(gidx, orc_route, cfg.k)
+    shared = [tuple(O._f64(t) for t in s_) for s_ in inp.shared]
+    ref = O.layer_backward(O._f64(inp.x), O._f64(inp.W_r), O._f64(inp.W_gate), O._f64(inp.W_up),
+                           O._f64(inp.W_down), O._f64(dy), cfg.k,
+                           b=None if inp.b is None else O._f64(inp.b), shared=shared, c=cfg.c,
+                           renorm=cfg.renorm, lam=cfg.lam, z_coef=0.3, scoring=cfg.scoring,
+                           topk_idx=gidx)
+    tol = 1e-4
+    errs = {key: max_rel_err(out[key], ref[key]) for key in ("dx", "dW_r", "dW_gate", "dW_up", "dW_down")}
+    if cfg.S > 0:
+        # the S shared experts stacked: gate/up rows and down columns in expert order
+        errs["dWs_gate"] = max_rel_err(out["dWs_gate"], np.concatenate([g[0] for g in ref["shared"]], 0))
+        errs["dWs_up"] = max_rel_err(out["dWs_up"], np.concatenate([g[1] for g in ref["shared"]], 0))
+        errs["dWs_down"] = max_rel_err(out["dWs_down"], np.concatenate([g[2] for g in ref["shared"]], 1))
+    say(f"    {errs}")
+    for key, e in errs.items():
+        assert e < tol, (key, e)
+
+
 # ------------------------------------------------------------------------------ whole layer
 
 def run_layer(cfg, dev, inp=None):
