@@ -15,7 +15,7 @@ def test_library_exports_every_declared_symbol():
     names = moe.header_functions()
     assert set(names) >= {"moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
                           "moe_balance_stats", "moe_layer_forward", "moe_workspace_size",
-                          "moe_balance_loss_backward",
+                          "moe_balance_loss_backward", "moe_layer_backward",
                           "moe_capacity", "moe_status_string", "moe_check_shape"}
     h = ctypes.CDLL(moe.LIB_PATH)
     for n in names:
@@ -193,6 +193,36 @@ def test_loss_backward_rejects_before_launch():
                                        None) == 3
     assert L.moe_balance_loss_backward(sp, F(), F(), F(), float("nan"), 1.0, F(), None, None, F(),
                                        ws, None) == 1
+
+
+def test_layer_backward_rejects_before_launch():
+    L = moe.lib()
+    F = _fake
+    s = moe.make_shape(64, 128, 8, 2, 256, S=1)
+    sp = ctypes.byref(s)
+    ws = moe.workspace_size(s, moe.CALL_LAYER_BACKWARD)
+    assert ws > 0
+
+    def call(shape=sp, ws_bytes=ws, lam=0.01, z=1e-3, drop=None):
+        # x W_r b W_gate W_up W_down Ws_gate Ws_up Ws_down dy | dx dW_r dWg dWu dWd dWsg dWsu dWsd
+        ins = [F(), F(), None, F(), F(), F(), F(), F(), F(), F()]
+        outs = [F() for _ in range(8)]
+        if drop is not None:
+            (ins if drop < 10 else outs)[drop if drop < 10 else drop - 10] = None
+        return L.moe_layer_backward(shape, *ins, lam, z, *outs, None, F(), ws_bytes, None)
+
+    assert call(drop=0) == 1                 # no x
+    assert call(drop=9) == 1                 # no dy
+    assert call(drop=6) == 1                 # S > 0 but no shared gate weights
+    assert call(drop=10) == 1                # no dx
+    assert call(drop=17) == 1                # S > 0 but no dWs_down
+    assert call(lam=float("nan")) == 1
+    assert call(z=float("nan")) == 1
+    assert call(ws_bytes=ws - 1) == 3
+    ec = moe.make_shape(64, 128, 8, 2, 256, S=1, routing="expert")
+    assert call(shape=ctypes.byref(ec)) == 2  # expert choice has no backward here
+    bad = moe.make_shape(64, 128, 8, 9, 256)
+    assert call(shape=ctypes.byref(bad)) == 1
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
