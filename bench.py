@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing the layer backward")
+    ap.add_argument("--backward-steps", type=int, default=3)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="also run one plain device copy of this many bytes (counter calibration)")
     return ap.parse_args()
@@ -177,6 +180,33 @@ def main():
     lb_ms = lb_s.elapsed_time(lb_e) / 5
     del lb, lb_ws
 
+    # the full layer backward (token choice): gradients of <dy, y> + aux + z for x, W_r and every
+    # expert weight, forward recompute included (a separate entry point; not part of a step)
+    bw_ms = None
+    if cfg.routing == "token" and not args.no_backward:
+        print("[bench] layer backward", file=sys.stderr, flush=True)
+        dy = torch.randn(cfg.T, cfg.d, generator=torch.Generator().manual_seed(11)).to(dt).to(dev)
+        bw_ws = moe.workspace(moe.make_shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.M, cfg.S, cfg.c,
+                                             cfg.renorm, dt, cfg.scoring),
+                              moe.CALL_LAYER_BACKWARD, dev)
+        shared_w = sh
+        def bw():
+            return moe.moe_layer_backward(x, W_r, Wg, Wu, Wd, dy, cfg.k, b=b, shared=shared_w,
+                                          c=cfg.c, renorm=cfg.renorm, lam=cfg.lam, z_coef=1.0,
+                                          scoring=cfg.scoring, ws=bw_ws)
+        g = bw()
+        torch.cuda.synchronize()
+        del g
+        bw_s, bw_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        bw_s.record()
+        for _ in range(args.backward_steps):
+            g = bw()
+            del g
+        bw_e.record()
+        torch.cuda.synchronize()
+        bw_ms = bw_s.elapsed_time(bw_e) / args.backward_steps
+        del bw_ws, dy
+
     if args.copy_bytes > 0:  # one plain copy of known size, for counter calibration
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -250,6 +280,15 @@ def main():
         "balance_loss_backward": {"ms": round(lb_ms, 4),
                                   "flops": 2.0 * 3 * T * d * E},
     }
+    if bw_ms is not None:
+        # algorithmic products: gate/up recompute 4dM, P = dy W_down 2dM, dx rows 4dM, weight
+        # gradients 6dM per kept row; shared experts the same per token; router 2dE (logits) +
+        # 4dE (dW_r, dx) per token
+        bw_fl = 16.0 * d * M * kept + 16.0 * d * S * M * T + 6.0 * d * E * T
+        bw_tf = bw_fl / (bw_ms * 1e-3) / 1e12
+        line["layer_backward"] = {"ms": round(bw_ms, 3), "flops": bw_fl,
+                                  "tflops": round(bw_tf, 1), "mfma_frac": round(bw_tf / peak, 4),
+                                  "steps": args.backward_steps}
     print(json.dumps(line), flush=True)
 
 

@@ -39,7 +39,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Per kept row (one wave): t = perm_token[row], its slot j, gate w; d w_tj = <P_row, h_row>,
-// dh_row = w P_row, d out_row = w dy_t.
+// dh_row = w P_row, d out_row = w dy_t (when dout != NULL), and the row's gate (when wrow != NULL).
 template <typename T>
 __global__ __launch_bounds__(256) void bw_rows_kernel(const int32_t* __restrict__ offsets, int E,
                                                        int d, int M, int k,
@@ -51,7 +51,8 @@ __global__ __launch_bounds__(256) void bw_rows_kernel(const int32_t* __restrict_
                                                        const float* __restrict__ h,
                                                        float* __restrict__ dw,
                                                        float* __restrict__ dh,
-                                                       float* __restrict__ dout) {
+                                                       float* __restrict__ dout,
+                                                       float* __restrict__ wrow) {
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= offsets[E]) return;
@@ -66,9 +67,13 @@ __global__ __launch_bounds__(256) void bw_rows_kernel(const int32_t* __restrict_
     dot = fmaf(p, h[row * M + m], dot);
     dh[row * M + m] = w * p;
   }
-  for (int i = lane; i < d; i += 64) dout[row * d + i] = w * ld<T>(dy, t * d + i);
+  if (dout != nullptr)
+    for (int i = lane; i < d; i += 64) dout[row * d + i] = w * ld<T>(dy, t * d + i);
   dot = wave_sum(dot);
-  if (lane == 0) dw[t * k + slot] = dot;
+  if (lane == 0) {
+    dw[t * k + slot] = dot;
+    if (wrow != nullptr) wrow[row] = w;
+  }
 }
 
 // h = SiLU(G) U in fp32
@@ -383,17 +388,17 @@ hipError_t kk_dispatch(int dtype_b, const void* A, int Ma, const void* B, int Nb
 hipError_t launch_bw_rows(int dtype, const int32_t* offsets, int E, int64_t R, int d, int M,
                           int k, const int32_t* perm_token, const int32_t* inv_perm,
                           const float* topk_w, const void* dy, const float* P, const float* h,
-                          float* dw, float* dh, float* dout, hipStream_t st) {
+                          float* dw, float* dh, float* dout, float* wrow, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(cdiv(R, 4)));
   if (R <= 0) return hipSuccess;
   if (dtype == MOE_F32)
     hipLaunchKernelGGL(bw_rows_kernel<float>, grid, dim3(256), 0, st, offsets, E, d, M, k,
                        perm_token, inv_perm, topk_w, static_cast<const float*>(dy), P, h, dw, dh,
-                       dout);
+                       dout, wrow);
   else
     hipLaunchKernelGGL(bw_rows_kernel<bf16_t>, grid, dim3(256), 0, st, offsets, E, d, M, k,
                        perm_token, inv_perm, topk_w, static_cast<const bf16_t*>(dy), P, h, dw,
-                       dh, dout);
+                       dh, dout, wrow);
   return hipGetLastError();
 }
 

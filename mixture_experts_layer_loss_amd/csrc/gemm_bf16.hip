@@ -93,14 +93,16 @@ __device__ __forceinline__ void sched_substep() {
 // One MR x 256 output tile of group g: rows [row_begin, row_begin + rows_here), output columns
 // [n0, n0 + BNO). EPI 0: SwiGLU (B0 = W_gate, B1 = W_up); EPI 1: plain (B0 = W_down); EPI 2:
 // plain with fp32 output (C is then float), stored straight from the accumulators.
-// KTAIL: K is not a multiple of 64 (the last k-slice is zero-padded).
+// KTAIL: K is not a multiple of 64 (the last k-slice is zero-padded). Row r of A starts at
+// A + r lda (gathered: A + gather[r] lda), row n of group g's B at B + g group_stride + n ldb, and
+// output row r at C + r ldc.
 template <int EPI, bool KTAIL, bool GATHER, int MR>
 __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __restrict__ A,
-                                         const int32_t* __restrict__ gather,
+                                         int lda, const int32_t* __restrict__ gather,
                                          const bf16_t* __restrict__ B0,
                                          const bf16_t* __restrict__ B1, int64_t group_stride,
-                                         int N, int K, bf16_t* __restrict__ C, int g,
-                                         int row_begin, int rows_here, int n0) {
+                                         int ldb, int N, int K, bf16_t* __restrict__ C, int ldc,
+                                         int g, int row_begin, int rows_here, int n0) {
   using G = Geo<MR>;
   constexpr int BNO = EPI == 0 ? BN / 2 : BN;  // output columns per tile
   constexpr int MI = G::MI, NJ = G::NJ, ACH = G::ACH, BCH = G::BCH, RS = G::RSTEP;
@@ -112,30 +114,30 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
   // offsets fixed over K (gathered A rows: one 64-bit row address each); rows past the group (A)
   // or past N (B) re-read the last valid row and never reach a stored output.
   const int r0 = tid >> 3, kc_t = (tid & 7) * 8;
-  const char* a_base = reinterpret_cast<const char*>(A + static_cast<int64_t>(row_begin) * K);
+  const char* a_base = reinterpret_cast<const char*>(A + static_cast<int64_t>(row_begin) * lda);
   const char* a_row[GATHER ? ACH : 1];
   if constexpr (GATHER) {
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
       const int t = gather[row_begin + min(i * RS + r0, rows_here - 1)];
-      a_row[i] = reinterpret_cast<const char*>(A + static_cast<int64_t>(t) * K + kc_t);
+      a_row[i] = reinterpret_cast<const char*>(A + static_cast<int64_t>(t) * lda + kc_t);
     }
   }
-  const bf16_t* Bg0 = B0 + static_cast<int64_t>(g) * group_stride + static_cast<int64_t>(n0) * K;
+  const bf16_t* Bg0 = B0 + static_cast<int64_t>(g) * group_stride + static_cast<int64_t>(n0) * ldb;
   const bf16_t* Bg1 =
-      EPI == 0 ? B1 + static_cast<int64_t>(g) * group_stride + static_cast<int64_t>(n0) * K : Bg0;
+      EPI == 0 ? B1 + static_cast<int64_t>(g) * group_stride + static_cast<int64_t>(n0) * ldb : Bg0;
   const char* b_base0 = reinterpret_cast<const char*>(Bg0);
   const char* b_base1 = reinterpret_cast<const char*>(Bg1);
   const int b_rows = min(EPI == 0 ? BN / 2 : BN, N - n0);
   uint32_t a_off[ACH], b_off[BCH];
 #pragma unroll
   for (int i = 0; i < ACH; ++i)
-    a_off[i] = static_cast<uint32_t>((min(i * RS + r0, rows_here - 1) * K + kc_t) * 2);
+    a_off[i] = static_cast<uint32_t>((min(i * RS + r0, rows_here - 1) * lda + kc_t) * 2);
 #pragma unroll
   for (int i = 0; i < BCH; ++i) {
     const int r = i * RS + r0;
     const int rb_ = EPI == 0 ? (r & (BN / 2 - 1)) : r;
-    b_off[i] = static_cast<uint32_t>((min(rb_, b_rows - 1) * K + kc_t) * 2);
+    b_off[i] = static_cast<uint32_t>((min(rb_, b_rows - 1) * ldb + kc_t) * 2);
   }
   u32x4 ra[ACH], rb[BCH];
   auto gload = [&](int k0) __attribute__((always_inline)) {
@@ -274,7 +276,7 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
         for (int r = 0; r < 16; ++r) {
           const int row = wm * G::WROWS + i * 32 + (r >> 2) * 8 + lk * 4 + (r & 3);
           if (row < rows_here && col < N)
-            C32[static_cast<int64_t>(row_begin + row) * N + col] = acc[i][j][r];
+            C32[static_cast<int64_t>(row_begin + row) * ldc + col] = acc[i][j][r];
         }
       }
     return;
@@ -308,7 +310,7 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
   for (int c = tid; c < MR * CPR; c += NT) {
     const int r = c / CPR, cc = (c % CPR) * 8;
     if (r < rows_here && n0 + cc < N)
-      *reinterpret_cast<uint4*>(C + static_cast<int64_t>(row_begin + r) * N + n0 + cc) =
+      *reinterpret_cast<uint4*>(C + static_cast<int64_t>(row_begin + r) * ldc + n0 + cc) =
           *reinterpret_cast<const uint4*>(ct + r * CS + cc);
   }
 }
@@ -350,7 +352,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     const int nb = static_cast<int>(local / mt_g), mt = static_cast<int>(local % mt_g);
     const int row_begin = offsets[g] + mt * 256;
     const int rows = min(256, offsets[g + 1] - row_begin);
-    run_tile<EPI, KTAIL, GATHER, 256>(lds, A, gather, B0, B1, group_stride, N, K, C, g,
+    run_tile<EPI, KTAIL, GATHER, 256>(lds, A, K, gather, B0, B1, group_stride, K, N, K, C, N, g,
                                       row_begin, rows, nb * BNO);
     return;
   }
@@ -370,11 +372,46 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
   const int rows = rows_g & 255;
   const int n0 = static_cast<int>(local) * BNO;
   if (table == t128)
-    run_tile<EPI, KTAIL, GATHER, 128>(lds, A, gather, B0, B1, group_stride, N, K, C, g, row_begin,
-                                      rows, n0);
+    run_tile<EPI, KTAIL, GATHER, 128>(lds, A, K, gather, B0, B1, group_stride, K, N, K, C, N, g,
+                                      row_begin, rows, n0);
   else
-    run_tile<EPI, KTAIL, GATHER, 64>(lds, A, gather, B0, B1, group_stride, N, K, C, g, row_begin,
-                                     rows, n0);
+    run_tile<EPI, KTAIL, GATHER, 64>(lds, A, K, gather, B0, B1, group_stride, K, N, K, C, N, g,
+                                     row_begin, rows, n0);
+}
+
+// Weight gradients: C_g [Ma][Nb] (fp32) = sum over k in [64 kt[g], 64 kt[g+1]) of A[m][k] B[n][k],
+// for the operands A [Ma][lda] and B [Nb][ldb] whose columns are the rows of the groups, each
+// group padded with zeros to a multiple of 64 (so no k-slice is partial). 256 x 256 output tiles,
+// m fastest (neighbouring tiles share the B slab), dealt to the XCDs in runs; a group without rows
+// gets zeros.
+__global__ __launch_bounds__(NT, 1) void wgrad_gemm_kernel(const bf16_t* __restrict__ A, int lda,
+                                                           const bf16_t* __restrict__ B, int ldb,
+                                                           const int32_t* __restrict__ kt,
+                                                           int groups, int Ma, int Nb,
+                                                           float* __restrict__ C) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int mt = (Ma + 255) / 256, nt = (Nb + 255) / 256;
+  const int64_t per_group = static_cast<int64_t>(mt) * nt;
+  const int64_t ntiles = static_cast<int64_t>(groups) * per_group;
+  const int64_t q = (ntiles + NXCD - 1) / NXCD;
+  const int64_t L = static_cast<int64_t>(blockIdx.x % NXCD) * q + blockIdx.x / NXCD;
+  if (blockIdx.x / NXCD >= q || L >= ntiles) return;
+  const int g = static_cast<int>(L / per_group);
+  const int local = static_cast<int>(L % per_group);
+  const int m0 = (local % mt) * 256, n0 = (local / mt) * 256;
+  const int k0 = 64 * kt[g], K = 64 * (kt[g + 1] - kt[g]);
+  float* Cg = C + static_cast<int64_t>(g) * Ma * Nb;
+  if (K == 0) {
+    for (int c = threadIdx.x; c < 256 * 64; c += NT) {
+      const int r = m0 + c / 64, cc = n0 + (c % 64) * 4;
+      if (r < Ma && cc < Nb)
+        *reinterpret_cast<float4*>(Cg + static_cast<int64_t>(r) * Nb + cc) =
+            make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
+  run_tile<2, false, false, 256>(lds, A + k0, lda, nullptr, B + k0, nullptr, 0, ldb, Nb, K,
+                                 reinterpret_cast<bf16_t*>(Cg), Nb, 0, m0, min(256, Ma - m0), n0);
 }
 
 template <int EPI, bool KTAIL, bool GATHER>
@@ -452,6 +489,29 @@ hipError_t launch_gemm_plain_bf16(int groups, const void* rows, const int32_t* g
                                 group_stride, N, K, Cp, st);
   return launch_gemm<2, false>(A, nullptr, offsets, tile_off, groups, max_tiles, Bp, nullptr,
                                group_stride, N, K, Cp, st);
+}
+
+// C_g = A_g B_g^T over each group's zero-padded column range (weight gradients, fp32 output)
+hipError_t launch_gemm_wgrad_bf16(const void* A, int lda, const void* B, int ldb,
+                                  const int32_t* kt, int groups, int Ma, int Nb, float* C,
+                                  hipStream_t st) {
+  constexpr size_t lds = 2 * Geo<256>::STAGE;
+  static std::atomic<bool> attr_set{false};
+  if (!attr_set.load(std::memory_order_acquire)) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_gemm_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    attr_set.store(true, std::memory_order_release);
+  }
+  const int64_t tiles = static_cast<int64_t>(groups) * cdiv(Ma, 256) * cdiv(Nb, 256);
+  if (tiles <= 0) return hipSuccess;
+  const int64_t grid = cdiv(tiles, NXCD) * NXCD;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(wgrad_gemm_kernel, dim3(static_cast<unsigned>(grid)), dim3(NT), lds, st,
+                     static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B), ldb, kt,
+                     groups, Ma, Nb, C);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_down_bf16(int groups, int d, int Mg, const int32_t* offsets,

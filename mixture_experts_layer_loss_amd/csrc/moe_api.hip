@@ -231,6 +231,12 @@ struct LayerBackwardPlan {
   int ks_w;
   float *Gs, *Us;                 // shared experts [T, S M] fp32
   float *hs, *dhs, *dGs, *dUs, *dxs;   // [T, S M] and [T, d]
+  // bf16 layers (MFMA products): transposed weights, [dG | dU] rows, and the weight-gradient
+  // operands with each group's rows as a zero-padded column range (ldp / ldps columns)
+  int64_t ldp, ldps;
+  float* wrow;                                            // gate of each kept row
+  void *WdT, *WguT, *dGU, *whT, *dGT, *dUT, *dyT, *xT;    // routed experts
+  void *WsdT, *WsguT, *dGUs, *hsT, *dGsT, *dUsT, *dysT, *xsT;  // shared experts
 };
 LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
   LayerBackwardPlan p;
@@ -244,14 +250,32 @@ LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
   p.U = c.take<float>(R * M);
   p.h = c.take<float>(R * M);
   p.P = c.take<float>(R * M);
-  p.dout = c.take<float>(R * d);
+  p.dout = s->dtype == MOE_BF16 ? nullptr : c.take<float>(R * d);
   p.dw = c.take<float>(T * s->k);
   p.dl = c.take<float>(T * E);
   p.dlT = c.take<float>(T * E);
   p.dh = c.take<float>(R * M);
-  p.dG = c.take<float>(R * M);
-  p.dU = c.take<float>(R * M);
+  const bool mfma = s->dtype == MOE_BF16;
+  p.dG = mfma ? nullptr : c.take<float>(R * M);
+  p.dU = mfma ? nullptr : c.take<float>(R * M);
   p.dxr = c.take<float>(R * d);
+  p.ldp = 64 * (static_cast<int64_t>(cdiv(static_cast<int64_t>(R), 64)) + s->E);
+  p.ldps = 64 * cdiv(s->T, 64);
+  const size_t lp = static_cast<size_t>(p.ldp), lps = static_cast<size_t>(p.ldps);
+  p.wrow = nullptr;
+  p.WdT = p.WguT = p.dGU = p.whT = p.dGT = p.dUT = p.dyT = p.xT = nullptr;
+  p.WsdT = p.WsguT = p.dGUs = p.hsT = p.dGsT = p.dUsT = p.dysT = p.xsT = nullptr;
+  if (mfma) {
+    p.WdT = c.take<bf16_t>(E * M * d);
+    p.WguT = c.take<bf16_t>(E * d * 2 * M);
+    p.wrow = c.take<float>(R);
+    p.dGU = c.take<bf16_t>(R * 2 * M);
+    p.whT = c.take<bf16_t>(M * lp);
+    p.dGT = c.take<bf16_t>(M * lp);
+    p.dUT = c.take<bf16_t>(M * lp);
+    p.dyT = c.take<bf16_t>(d * lp);
+    p.xT = c.take<bf16_t>(d * lp);
+  }
   p.ks_w = kmajor_splits(s->E, s->d, s->T);
   p.partial = c.take<float>(p.ks_w > 1 ? static_cast<size_t>(p.ks_w) * E * d : 1);
   if (s->S > 0) {
@@ -260,9 +284,19 @@ LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
     p.Us = c.take<float>(T * SM);
     p.hs = c.take<float>(T * SM);
     p.dhs = c.take<float>(T * SM);
-    p.dGs = c.take<float>(T * SM);
-    p.dUs = c.take<float>(T * SM);
+    p.dGs = mfma ? nullptr : c.take<float>(T * SM);
+    p.dUs = mfma ? nullptr : c.take<float>(T * SM);
     p.dxs = c.take<float>(T * d);
+    if (mfma) {
+      p.WsdT = c.take<bf16_t>(SM * d);
+      p.WsguT = c.take<bf16_t>(d * 2 * SM);
+      p.dGUs = c.take<bf16_t>(T * 2 * SM);
+      p.hsT = c.take<bf16_t>(SM * lps);
+      p.dGsT = c.take<bf16_t>(SM * lps);
+      p.dUsT = c.take<bf16_t>(SM * lps);
+      p.dysT = c.take<bf16_t>(d * lps);
+      p.xsT = c.take<bf16_t>(d * lps);
+    }
   } else {
     p.Gs = p.Us = nullptr;
     p.hs = p.dhs = p.dGs = p.dUs = p.dxs = nullptr;
@@ -624,30 +658,76 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
                      nullptr, nullptr, nullptr, f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart, p.cols,
                      hs);
   if (e == hipSuccess) e = launch_schedule(s->E, f.offsets, p.tile64, 64, hs);
+  const bool mfma = s->dtype == MOE_BF16;
+  const int d = s->d, M = s->M;
+  if (mfma) {  // weights transposed for the products that reduce over d or M
+    if (e == hipSuccess)  // W_down[e]^T [M][d]
+      e = launch_transpose_bf16(W_down, d, M, dM, s->E, p.WdT, d, 0, dM, hs);
+    if (e == hipSuccess)  // [W_gate[e] W_up[e]]^T [d][2M]
+      e = launch_transpose_bf16(W_gate, M, d, dM, s->E, p.WguT, 2 * M, 0, 2 * dM, hs);
+    if (e == hipSuccess)
+      e = launch_transpose_bf16(W_up, M, d, dM, s->E, p.WguT, 2 * M, M, 2 * dM, hs);
+  }
   // ---- combine: P_row = dy_t W_down[e] gives d w = <P, h> and dh = w P; d out = w dy_t
-  if (e == hipSuccess)
+  if (e == hipSuccess && mfma)
+    e = launch_gemm_plain(s->dtype, s->E, dy, f.perm_token, f.offsets, f.tile_off, max_tiles,
+                          p.WdT, dM, M, d, p.P, hs);
+  else if (e == hipSuccess)
     e = launch_nn_gemm(s->dtype, s->dtype, false, dy, nullptr, f.perm_token, f.offsets, p.tile64,
                        s->E, max_t64, W_down, nullptr, dM, s->M, s->d, p.P, hs);
   if (e == hipSuccess)
     e = launch_bw_rows(s->dtype, f.offsets, s->E, R, s->d, s->M, s->k, f.perm_token, f.inv_perm,
-                       f.topk_w, dy, p.P, p.h, p.dw, p.dh, p.dout, hs);
+                       f.topk_w, dy, p.P, p.h, p.dw, p.dh, p.dout, p.wrow, hs);
   if (e == hipSuccess)
     e = launch_bw_router(s->T, s->E, s->k, s->renorm, s->scoring == MOE_SCORE_SIGMOID, p.cols,
                          p.cols + ET, idx, f.inv_perm, f.topk_w, p.dw, f.n, stats_fden(s), lambda,
                          z_coef, p.dl, p.dlT, hs);
   // ---- routed experts
-  if (e == hipSuccess)
+  if (mfma) {
+    if (e == hipSuccess) e = launch_swiglu_bw_cat(R, M, p.dh, p.G, p.U, p.dGU, hs);
+    if (e == hipSuccess)  // dx_row = [dG dU] [W_gate[e] W_up[e]]^T^T over K = 2M
+      e = launch_gemm_plain(s->dtype, s->E, p.dGU, nullptr, f.offsets, f.tile_off, max_tiles,
+                            p.WguT, 2 * dM, d, 2 * M, p.dxr, hs);
+    // weight-gradient operands: each expert's rows as a zero-padded column range
+    const int64_t lp = p.ldp;
+    const bf16_t* dGU = static_cast<const bf16_t*>(p.dGU);
+    if (e == hipSuccess)  // (w h)^T
+      e = launch_pad_transpose(MOE_F32, p.h, M, nullptr, p.wrow, f.offsets, p.tile64, s->E,
+                               max_t64, M, p.whT, lp, hs);
+    if (e == hipSuccess)
+      e = launch_pad_transpose(MOE_BF16, dGU, 2 * M, nullptr, nullptr, f.offsets, p.tile64, s->E,
+                               max_t64, M, p.dGT, lp, hs);
+    if (e == hipSuccess)
+      e = launch_pad_transpose(MOE_BF16, dGU + M, 2 * M, nullptr, nullptr, f.offsets, p.tile64,
+                               s->E, max_t64, M, p.dUT, lp, hs);
+    if (e == hipSuccess)  // dy rows of the kept slots (exact bf16)
+      e = launch_pad_transpose(MOE_BF16, dy, d, f.perm_token, nullptr, f.offsets, p.tile64, s->E,
+                               max_t64, d, p.dyT, lp, hs);
+    if (e == hipSuccess)
+      e = launch_pad_transpose(MOE_BF16, x, d, f.perm_token, nullptr, f.offsets, p.tile64, s->E,
+                               max_t64, d, p.xT, lp, hs);
+    if (e == hipSuccess)  // dW_down[e] = sum over its rows of dy_t^T (w h)
+      e = launch_gemm_wgrad_bf16(p.dyT, static_cast<int>(lp), p.whT, static_cast<int>(lp),
+                                 p.tile64, s->E, d, M, dW_down, hs);
+    if (e == hipSuccess)  // dW_gate[e] = dG_e^T x_e
+      e = launch_gemm_wgrad_bf16(p.dGT, static_cast<int>(lp), p.xT, static_cast<int>(lp),
+                                 p.tile64, s->E, M, d, dW_gate, hs);
+    if (e == hipSuccess)
+      e = launch_gemm_wgrad_bf16(p.dUT, static_cast<int>(lp), p.xT, static_cast<int>(lp),
+                                 p.tile64, s->E, M, d, dW_up, hs);
+  }
+  if (e == hipSuccess && !mfma)
     e = launch_swiglu_bw(MOE_F32, R * s->M, p.dh, p.G, p.U, p.dG, p.dU, hs);
-  if (e == hipSuccess)  // dx_row = dG W_gate[e] + dU W_up[e]
+  if (e == hipSuccess && !mfma)  // dx_row = dG W_gate[e] + dU W_up[e]
     e = launch_nn_gemm(MOE_F32, s->dtype, true, p.dG, p.dU, nullptr, f.offsets, p.tile64, s->E,
                        max_t64, W_gate, W_up, dM, s->d, s->M, p.dxr, hs);
-  if (e == hipSuccess)  // dW_down[e] = sum_rows d out^T h
+  if (e == hipSuccess && !mfma)  // dW_down[e] = sum_rows d out^T h
     e = launch_kk_gemm(MOE_F32, MOE_F32, p.dout, s->d, p.h, s->M, nullptr, f.offsets, s->E,
                        dW_down, hs);
-  if (e == hipSuccess)  // dW_gate[e] = sum_rows dG^T x
+  if (e == hipSuccess && !mfma)  // dW_gate[e] = sum_rows dG^T x
     e = launch_kk_gemm(MOE_F32, s->dtype, p.dG, s->M, x, s->d, f.perm_token, f.offsets, s->E,
                        dW_gate, hs);
-  if (e == hipSuccess)
+  if (e == hipSuccess && !mfma)
     e = launch_kk_gemm(MOE_F32, s->dtype, p.dU, s->M, x, s->d, f.perm_token, f.offsets, s->E,
                        dW_up, hs);
   // ---- router weights and the router part of dx
@@ -671,24 +751,67 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
       e = launch_swiglu_fwd(static_cast<int64_t>(s->T) * SM, p.Gs, p.Us, p.hs, hs);
     if (e == hipSuccess) e = launch_schedule(1, f.sh_offsets, p.sh_tile64, 64, hs);
     const int64_t sh_t64 = cdiv(s->T, 64) + 1;
-    if (e == hipSuccess)
-      e = launch_nn_gemm(s->dtype, s->dtype, false, dy, nullptr, nullptr, f.sh_offsets,
-                         p.sh_tile64, 1, sh_t64, Ws_down, nullptr, dSM, SM, s->d, p.dhs, hs);
-    if (e == hipSuccess)
-      e = launch_swiglu_bw(MOE_F32, static_cast<int64_t>(s->T) * SM, p.dhs, p.Gs, p.Us, p.dGs,
-                           p.dUs, hs);
-    if (e == hipSuccess)
-      e = launch_nn_gemm(MOE_F32, s->dtype, true, p.dGs, p.dUs, nullptr, f.sh_offsets,
-                         p.sh_tile64, 1, sh_t64, Ws_gate, Ws_up, dSM, s->d, SM, p.dxs, hs);
-    if (e == hipSuccess)
-      e = launch_kk_gemm(s->dtype, MOE_F32, dy, s->d, p.hs, SM, nullptr, f.sh_offsets, 1,
-                         dWs_down, hs);
-    if (e == hipSuccess)
-      e = launch_kk_gemm(MOE_F32, s->dtype, p.dGs, SM, x, s->d, nullptr, f.sh_offsets, 1,
-                         dWs_gate, hs);
-    if (e == hipSuccess)
-      e = launch_kk_gemm(MOE_F32, s->dtype, p.dUs, SM, x, s->d, nullptr, f.sh_offsets, 1, dWs_up,
-                         hs);
+    if (mfma) {
+      const int64_t lps = p.ldps;
+      const bf16_t* dGUs = static_cast<const bf16_t*>(p.dGUs);
+      if (e == hipSuccess)  // Ws_down^T [SM][d]
+        e = launch_transpose_bf16(Ws_down, d, SM, 0, 1, p.WsdT, d, 0, 0, hs);
+      if (e == hipSuccess)  // [Ws_gate Ws_up]^T [d][2 SM]
+        e = launch_transpose_bf16(Ws_gate, SM, d, 0, 1, p.WsguT, 2 * SM, 0, 0, hs);
+      if (e == hipSuccess)
+        e = launch_transpose_bf16(Ws_up, SM, d, 0, 1, p.WsguT, 2 * SM, SM, 0, hs);
+      if (e == hipSuccess)  // dhs = dy Ws_down
+        e = launch_gemm_plain(s->dtype, 1, dy, nullptr, f.sh_offsets, f.sh_tile_off, sh_tiles,
+                              p.WsdT, 0, SM, d, p.dhs, hs);
+      if (e == hipSuccess) e = launch_swiglu_bw_cat(s->T, SM, p.dhs, p.Gs, p.Us, p.dGUs, hs);
+      if (e == hipSuccess)
+        e = launch_gemm_plain(s->dtype, 1, p.dGUs, nullptr, f.sh_offsets, f.sh_tile_off, sh_tiles,
+                              p.WsguT, 0, d, 2 * SM, p.dxs, hs);
+      const int64_t pt = cdiv(s->T, 64);
+      if (e == hipSuccess)
+        e = launch_pad_transpose(MOE_BF16, dy, d, nullptr, nullptr, f.sh_offsets, p.sh_tile64, 1, pt, d,
+                                 p.dysT, lps, hs);
+      if (e == hipSuccess)
+        e = launch_pad_transpose(MOE_F32, p.hs, SM, nullptr, nullptr, f.sh_offsets, p.sh_tile64, 1, pt, SM,
+                                 p.hsT, lps, hs);
+      if (e == hipSuccess)
+        e = launch_pad_transpose(MOE_BF16, dGUs, 2 * SM, nullptr, nullptr, f.sh_offsets, p.sh_tile64, 1, pt,
+                                 SM, p.dGsT, lps, hs);
+      if (e == hipSuccess)
+        e = launch_pad_transpose(MOE_BF16, dGUs + SM, 2 * SM, nullptr, nullptr, f.sh_offsets, p.sh_tile64, 1,
+                                 pt, SM, p.dUsT, lps, hs);
+      if (e == hipSuccess)
+        e = launch_pad_transpose(MOE_BF16, x, d, nullptr, nullptr, f.sh_offsets, p.sh_tile64, 1, pt, d,
+                                 p.xsT, lps, hs);
+      if (e == hipSuccess)
+        e = launch_gemm_wgrad_bf16(p.dysT, static_cast<int>(lps), p.hsT, static_cast<int>(lps),
+                                   p.sh_tile64, 1, d, SM, dWs_down, hs);
+      if (e == hipSuccess)
+        e = launch_gemm_wgrad_bf16(p.dGsT, static_cast<int>(lps), p.xsT, static_cast<int>(lps),
+                                   p.sh_tile64, 1, SM, d, dWs_gate, hs);
+      if (e == hipSuccess)
+        e = launch_gemm_wgrad_bf16(p.dUsT, static_cast<int>(lps), p.xsT, static_cast<int>(lps),
+                                   p.sh_tile64, 1, SM, d, dWs_up, hs);
+    } else {
+      if (e == hipSuccess)
+        e = launch_nn_gemm(s->dtype, s->dtype, false, dy, nullptr, nullptr, f.sh_offsets,
+                           p.sh_tile64, 1, sh_t64, Ws_down, nullptr, dSM, SM, s->d, p.dhs, hs);
+      if (e == hipSuccess)
+        e = launch_swiglu_bw(MOE_F32, static_cast<int64_t>(s->T) * SM, p.dhs, p.Gs, p.Us, p.dGs,
+                             p.dUs, hs);
+      if (e == hipSuccess)
+        e = launch_nn_gemm(MOE_F32, s->dtype, true, p.dGs, p.dUs, nullptr, f.sh_offsets,
+                           p.sh_tile64, 1, sh_t64, Ws_gate, Ws_up, dSM, s->d, SM, p.dxs, hs);
+      if (e == hipSuccess)
+        e = launch_kk_gemm(s->dtype, MOE_F32, dy, s->d, p.hs, SM, nullptr, f.sh_offsets, 1,
+                           dWs_down, hs);
+      if (e == hipSuccess)
+        e = launch_kk_gemm(MOE_F32, s->dtype, p.dGs, SM, x, s->d, nullptr, f.sh_offsets, 1,
+                           dWs_gate, hs);
+      if (e == hipSuccess)
+        e = launch_kk_gemm(MOE_F32, s->dtype, p.dUs, SM, x, s->d, nullptr, f.sh_offsets, 1, dWs_up,
+                           hs);
+    }
   }
   // ---- tokens
   if (e == hipSuccess)

@@ -132,11 +132,12 @@ hipError_t launch_gemm_plain(int dtype, int groups, const void* rows, const int3
                              const void* B, int64_t group_stride, int N, int K, void* C,
                              hipStream_t st);
 
-// Backward (backward.hip). Per kept row: dw [T, k] (slot of the row), dh = w P, dout = w dy_t.
+// Backward (backward.hip). Per kept row: dw [T, k] (slot of the row), dh = w P, and when not
+// NULL dout = w dy_t and wrow = w.
 hipError_t launch_bw_rows(int dtype, const int32_t* offsets, int E, int64_t R, int d, int M,
                           int k, const int32_t* perm_token, const int32_t* inv_perm,
                           const float* topk_w, const void* dy, const float* P, const float* h,
-                          float* dw, float* dh, float* dout, hipStream_t st);
+                          float* dw, float* dh, float* dout, float* wrow, hipStream_t st);
 hipError_t launch_swiglu_fwd(int64_t count, const float* G, const float* U, float* h,
                              hipStream_t st);
 hipError_t launch_bw_router(int64_t T, int E, int k, int renorm, int sigmoid, const float* lcol,
@@ -157,6 +158,27 @@ hipError_t launch_swiglu_bw(int dtype, int64_t count, const float* dh, const voi
                             const void* U, float* dG, float* dU, hipStream_t st);
 hipError_t launch_bw_dx(int64_t T, int d, int k, const int32_t* inv_perm, const float* dx_perm,
                         const float* dx_sh, float* dx, hipStream_t st);
+
+// bf16 backward on MFMA (backward_layout.hip, gemm_bf16.hip).
+// dst[b][c][coff + r] = src[b][r][c] for batch matrices [rows][cols] (sizes multiples of 8).
+hipError_t launch_transpose_bf16(const void* src, int rows, int cols, int64_t src_batch,
+                                 int batch, void* dst, int ldd, int coff, int64_t dst_batch,
+                                 hipStream_t st);
+// dst [cols][ldp] bf16: column p of group g (64 kt[g] <= p < 64 kt[g+1]) = source row
+// i = offsets[g] + p - 64 kt[g] (row gather[i] of src when gather != NULL), times scale[i] when
+// scale != NULL; zeros past the group's rows.
+hipError_t launch_pad_transpose(int dtype_src, const void* src, int64_t ld_src,
+                                const int32_t* gather, const float* scale,
+                                const int32_t* offsets, const int32_t* kt, int groups,
+                                int64_t max_ptiles, int cols, void* dst, int64_t ldp,
+                                hipStream_t st);
+// dGU [R][2M] bf16 = [dh U SiLU'(G) | dh SiLU(G)] from fp32 [R][M] inputs
+hipError_t launch_swiglu_bw_cat(int64_t R, int M, const float* dh, const float* G, const float* U,
+                                void* dGU, hipStream_t st);
+// C_g [Ma][Nb] fp32 = sum over k in [64 kt[g], 64 kt[g+1]) of A[m][k] B[n][k]
+hipError_t launch_gemm_wgrad_bf16(const void* A, int lda, const void* B, int ldb,
+                                  const int32_t* kt, int groups, int Ma, int Nb, float* C,
+                                  hipStream_t st);
 
 // Tile table of the shared experts (one group of all T rows).
 hipError_t launch_shared_table(int64_t T, int BM, int32_t* offsets, int32_t* tile_off,

@@ -331,7 +331,7 @@ def silu_grad(z: np.ndarray) -> np.ndarray:
 
 def layer_backward(x, W_r, W_gate, W_up, W_down, dy, k: int, b=None, shared=(), c=None,
                    renorm: bool = True, lam: float = 0.01, z_coef: float = 0.0,
-                   scoring: str = "softmax", topk_idx=None):
+                   scoring: str = "softmax", topk_idx=None, magnitudes: bool = False):
     """Gradients of <dy, y> + aux + z_coef z with respect to x, W_r and every expert weight, for
     the token-choice layer of layer_forward (selection, capacity and f held fixed: they are
     discrete). The chain, step by step:
@@ -342,7 +342,10 @@ def layer_backward(x, W_r, W_gate, W_up, W_down, dy, k: int, b=None, shared=(), 
       per kept row: dh = d out W_down; dW_down += d out^T h; dG = dh U SiLU'(G), dU = dh SiLU(G);
       dx_t += dG W_gate + dU W_up; dW_gate += dG^T x_t, dW_up += dU^T x_t
       shared experts: the same with d out = dy_t and weight 1.
-    Returns dict of float64 arrays."""
+    Returns dict of float64 arrays. With magnitudes=True, out["magnitude"] holds, for dx, dW_r and
+    every weight gradient, the sum of the absolute values of the terms the gradient is a sum of
+    (the same products taken over |.|): the scale of the rounding bound of any evaluation that
+    rounds one factor of each term."""
     x64 = _f64(x)
     T, d = x64.shape
     r = route(x64, W_r, k, b, renorm, scoring)
@@ -356,6 +359,7 @@ def layer_backward(x, W_r, W_gate, W_up, W_down, dy, k: int, b=None, shared=(), 
     out = {"dx": np.zeros((T, d)), "dW_gate": np.zeros_like(_f64(W_gate)),
            "dW_up": np.zeros_like(_f64(W_up)), "dW_down": np.zeros_like(_f64(W_down))}
     dw = np.zeros((T, k))
+    mag = {key: np.zeros_like(val) for key, val in out.items()}
     for e in range(E):
         rows = [(int(dsp["offsets"][e]) + p, int(dsp["perm_token"][dsp["offsets"][e] + p]))
                 for p in range(int(dsp["kept"][e]))]
@@ -380,6 +384,11 @@ def layer_backward(x, W_r, W_gate, W_up, W_down, dy, k: int, b=None, shared=(), 
         out["dW_gate"][e] = dG.T @ X
         out["dW_up"][e] = dU.T @ X
         np.add.at(out["dx"], toks, dG @ Wg + dU @ Wu)
+        if magnitudes:
+            mag["dW_down"][e] = np.abs(dO).T @ np.abs(h)
+            mag["dW_gate"][e] = np.abs(dG).T @ np.abs(X)
+            mag["dW_up"][e] = np.abs(dU).T @ np.abs(X)
+            np.add.at(mag["dx"], toks, np.abs(dG) @ np.abs(Wg) + np.abs(dU) @ np.abs(Wu))
     # router: gates -> scores -> logits
     dg = np.zeros((T, E))
     gS = np.take_along_axis(g, S, axis=1)
@@ -399,7 +408,10 @@ def layer_backward(x, W_r, W_gate, W_up, W_down, dy, k: int, b=None, shared=(), 
     out["dW_r"] = dl.T @ x64
     out["dx"] += dl @ W64
     out["dlogits"] = dl
-    sh_grads = []
+    if magnitudes:
+        mag["dW_r"] = np.abs(dl).T @ np.abs(x64)
+        mag["dx"] += np.abs(dl) @ np.abs(W64)
+    sh_grads, sh_mag = [], []
     for Wg, Wu, Wd in shared:
         Wg, Wu, Wd = _f64(Wg), _f64(Wu), _f64(Wd)
         G = x64 @ Wg.T
@@ -410,7 +422,14 @@ def layer_backward(x, W_r, W_gate, W_up, W_down, dy, k: int, b=None, shared=(), 
         dU = dh * silu(G)
         out["dx"] += dG @ Wg + dU @ Wu
         sh_grads.append((dG.T @ x64, dU.T @ x64, dy64.T @ h))
+        if magnitudes:
+            mag["dx"] += np.abs(dG) @ np.abs(Wg) + np.abs(dU) @ np.abs(Wu)
+            ax = np.abs(x64)
+            sh_mag.append((np.abs(dG).T @ ax, np.abs(dU).T @ ax, np.abs(dy64).T @ np.abs(h)))
     out["shared"] = sh_grads
+    if magnitudes:
+        mag["shared"] = sh_mag
+        out["magnitude"] = mag
     out["topk_idx"] = S
     return out
 

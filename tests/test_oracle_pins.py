@@ -465,6 +465,27 @@ def test_layer_backward_pins():
     check_layer_backward()
 
 
+def test_layer_backward_magnitudes_dominate():
+    # the rounding-bound scales: same gradients with or without them, and each scale is at least
+    # the absolute value of its gradient (a sum is bounded by the sum of its terms' magnitudes)
+    T, d, E, k, M = 12, 5, 3, 2, 4
+    rng = np.random.default_rng(77)
+    args = (rng.standard_normal((T, d)), rng.standard_normal((E, d)) * 0.5,
+            rng.standard_normal((E, M, d)) * 0.4, rng.standard_normal((E, M, d)) * 0.4,
+            rng.standard_normal((E, d, M)) * 0.4, rng.standard_normal((T, d)))
+    sh = [tuple(rng.standard_normal(sz) * 0.4 for sz in ((M, d), (M, d), (d, M)))]
+    a = O.layer_backward(*args, k, shared=sh, c=0.8, lam=0.2, z_coef=0.5)
+    b = O.layer_backward(*args, k, shared=sh, c=0.8, lam=0.2, z_coef=0.5, magnitudes=True)
+    mag = b["magnitude"]
+    for key in ("dx", "dW_r", "dW_gate", "dW_up", "dW_down"):
+        assert np.array_equal(a[key], b[key])
+        assert (mag[key] >= np.abs(b[key]) * (1 - 1e-12)).all(), key
+        assert mag[key].max() > 0
+    for grads, mags in zip(b["shared"], mag["shared"]):
+        for g_, m_ in zip(grads, mags):
+            assert (m_ >= np.abs(g_) * (1 - 1e-12)).all()
+
+
 # ----------------------------------------------------------------------------- capacity/dispatch
 
 def test_capacity_closed_forms():
