@@ -38,21 +38,19 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Per kept row (one wave): t = perm_token[row], its slot j, gate w; d w_tj = <P_row, h_row>,
-// dh_row = w P_row, d out_row = w dy_t (when dout != NULL), and the row's gate (when wrow != NULL).
-template <typename T>
-__global__ __launch_bounds__(256) void bw_rows_kernel(const int32_t* __restrict__ offsets, int E,
-                                                       int d, int M, int k,
-                                                       const int32_t* __restrict__ perm_token,
-                                                       const int32_t* __restrict__ inv_perm,
-                                                       const float* __restrict__ topk_w,
-                                                       const T* __restrict__ dy,
-                                                       const float* __restrict__ P,
-                                                       const float* __restrict__ h,
-                                                       float* __restrict__ dw,
-                                                       float* __restrict__ dh,
-                                                       float* __restrict__ dout,
-                                                       float* __restrict__ wrow) {
+// Per kept row (one wave): t = perm_token[row], its slot j and gate w. From P_row = dy_t W_down[e]
+// and the fp32 pre-activations G, U of the row: h = SiLU(G) U, d w_tj = <P_row, h>, dh = w P_row,
+// and the SwiGLU derivative dG = dh U SiLU'(G), dU = dh SiLU(G) with SiLU'(z) = s (1 + z (1 - s)),
+// s = sigma(z). CAT: one bf16 row [dG | dU] of 2M (M a multiple of 4; lanes take 4 columns at a
+// time); else fp32 rows dG, dU. When not NULL: d out_row = w dy_t, wrow[row] = w.
+template <typename T, bool CAT>
+__global__ __launch_bounds__(256) void bw_rows_kernel(
+    const int32_t* __restrict__ offsets, int E, int d, int M, int k,
+    const int32_t* __restrict__ perm_token, const int32_t* __restrict__ inv_perm,
+    const float* __restrict__ topk_w, const T* __restrict__ dy, const float* __restrict__ P,
+    const float* __restrict__ G, const float* __restrict__ U, float* __restrict__ dw,
+    float* __restrict__ dG, float* __restrict__ dU, bf16_t* __restrict__ dGU,
+    float* __restrict__ dout, float* __restrict__ wrow) {
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= offsets[E]) return;
@@ -62,10 +60,42 @@ __global__ __launch_bounds__(256) void bw_rows_kernel(const int32_t* __restrict_
     if (inv_perm[t * k + j] == row) slot = j;
   const float w = topk_w[t * k + slot];
   float dot = 0.f;
-  for (int m = lane; m < M; m += 64) {
-    const float p = P[row * M + m];
-    dot = fmaf(p, h[row * M + m], dot);
-    dh[row * M + m] = w * p;
+  auto one = [&](float p, float z, float u, float& vg, float& vu) __attribute__((always_inline)) {
+    const float sg = 1.f / (1.f + expf(-z));
+    const float si = z * sg;
+    dot = fmaf(p, si * u, dot);
+    const float gh = w * p;
+    vg = gh * u * sg * (1.f + z * (1.f - sg));
+    vu = gh * si;
+  };
+  if constexpr (CAT) {
+    for (int m = lane * 4; m < M; m += 256) {
+      const int64_t i = row * M + m;
+      const float4 p = *reinterpret_cast<const float4*>(P + i);
+      const float4 z = *reinterpret_cast<const float4*>(G + i);
+      const float4 u = *reinterpret_cast<const float4*>(U + i);
+      float vg[4], vu[4];
+      one(p.x, z.x, u.x, vg[0], vu[0]);
+      one(p.y, z.y, u.y, vg[1], vu[1]);
+      one(p.z, z.z, u.z, vg[2], vu[2]);
+      one(p.w, z.w, u.w, vg[3], vu[3]);
+      const uint2 og = make_uint2(
+          static_cast<uint32_t>(f32_to_bf16(vg[0])) | (static_cast<uint32_t>(f32_to_bf16(vg[1])) << 16),
+          static_cast<uint32_t>(f32_to_bf16(vg[2])) | (static_cast<uint32_t>(f32_to_bf16(vg[3])) << 16));
+      const uint2 ou = make_uint2(
+          static_cast<uint32_t>(f32_to_bf16(vu[0])) | (static_cast<uint32_t>(f32_to_bf16(vu[1])) << 16),
+          static_cast<uint32_t>(f32_to_bf16(vu[2])) | (static_cast<uint32_t>(f32_to_bf16(vu[3])) << 16));
+      *reinterpret_cast<uint2*>(dGU + row * 2 * M + m) = og;
+      *reinterpret_cast<uint2*>(dGU + row * 2 * M + M + m) = ou;
+    }
+  } else {
+    for (int m = lane; m < M; m += 64) {
+      const int64_t i = row * M + m;
+      float vg, vu;
+      one(P[i], G[i], U[i], vg, vu);
+      dG[i] = vg;
+      dU[i] = vu;
+    }
   }
   if (dout != nullptr)
     for (int i = lane; i < d; i += 64) dout[row * d + i] = w * ld<T>(dy, t * d + i);
@@ -387,18 +417,29 @@ hipError_t kk_dispatch(int dtype_b, const void* A, int Ma, const void* B, int Nb
 
 hipError_t launch_bw_rows(int dtype, const int32_t* offsets, int E, int64_t R, int d, int M,
                           int k, const int32_t* perm_token, const int32_t* inv_perm,
-                          const float* topk_w, const void* dy, const float* P, const float* h,
-                          float* dw, float* dh, float* dout, float* wrow, hipStream_t st) {
+                          const float* topk_w, const void* dy, const float* P, const float* G,
+                          const float* U, float* dw, float* dG, float* dU, void* dGU, float* dout,
+                          float* wrow, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(cdiv(R, 4)));
   if (R <= 0) return hipSuccess;
-  if (dtype == MOE_F32)
-    hipLaunchKernelGGL(bw_rows_kernel<float>, grid, dim3(256), 0, st, offsets, E, d, M, k,
-                       perm_token, inv_perm, topk_w, static_cast<const float*>(dy), P, h, dw, dh,
-                       dout, wrow);
-  else
-    hipLaunchKernelGGL(bw_rows_kernel<bf16_t>, grid, dim3(256), 0, st, offsets, E, d, M, k,
-                       perm_token, inv_perm, topk_w, static_cast<const bf16_t*>(dy), P, h, dw,
-                       dh, dout, wrow);
+  bf16_t* cat = static_cast<bf16_t*>(dGU);
+  if (dtype == MOE_F32) {
+    const float* y = static_cast<const float*>(dy);
+    if (cat != nullptr)
+      hipLaunchKernelGGL((bw_rows_kernel<float, true>), grid, dim3(256), 0, st, offsets, E, d, M, k,
+                         perm_token, inv_perm, topk_w, y, P, G, U, dw, dG, dU, cat, dout, wrow);
+    else
+      hipLaunchKernelGGL((bw_rows_kernel<float, false>), grid, dim3(256), 0, st, offsets, E, d, M,
+                         k, perm_token, inv_perm, topk_w, y, P, G, U, dw, dG, dU, cat, dout, wrow);
+  } else {
+    const bf16_t* y = static_cast<const bf16_t*>(dy);
+    if (cat != nullptr)
+      hipLaunchKernelGGL((bw_rows_kernel<bf16_t, true>), grid, dim3(256), 0, st, offsets, E, d, M,
+                         k, perm_token, inv_perm, topk_w, y, P, G, U, dw, dG, dU, cat, dout, wrow);
+    else
+      hipLaunchKernelGGL((bw_rows_kernel<bf16_t, false>), grid, dim3(256), 0, st, offsets, E, d, M,
+                         k, perm_token, inv_perm, topk_w, y, P, G, U, dw, dG, dU, cat, dout, wrow);
+  }
   return hipGetLastError();
 }
 

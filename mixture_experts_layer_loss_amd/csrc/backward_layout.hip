@@ -84,11 +84,13 @@ __device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float* v) {
 
 // dst [cols][ldp] bf16: column p of group g (p in [64 kt[g], 64 kt[g+1])) holds source row
 // i = off[g] + p - 64 kt[g] (row gather[i] of src when gather != NULL; src rows ld_src apart),
-// times scale[i] when scale != NULL, or zeros past the group's rows; rounded once to bf16. cols a
-// multiple of 8. Tiles past 64 kt[groups] are left alone.
-template <typename TS>
+// times scale[i] when scale != NULL, or zeros past the group's rows; rounded once to bf16. SWI: the
+// source value is SiLU(src) src2 (fp32 pre-activations G, U). cols a multiple of 8. Tiles past
+// 64 kt[groups] are left alone.
+template <typename TS, bool SWI>
 __global__ __launch_bounds__(256) void pad_transpose_kernel(
-    const TS* __restrict__ src, int64_t ld_src, const int32_t* __restrict__ gather,
+    const TS* __restrict__ src, const float* __restrict__ src2, int64_t ld_src,
+    const int32_t* __restrict__ gather,
     const float* __restrict__ scale, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ kt, int groups, int cols, bf16_t* __restrict__ dst,
     int64_t ldp) {
@@ -112,6 +114,12 @@ __global__ __launch_bounds__(256) void pad_transpose_kernel(
     if (row < row_end && c0 + cc < cols) {
       const int64_t sr = gather != nullptr ? gather[row] : row;
       load8<TS>(src + sr * ld_src + c0 + cc, v);
+      if constexpr (SWI) {
+        float u[8];
+        load8<float>(src2 + sr * ld_src + c0 + cc, u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = v[i] / (1.f + expf(-v[i])) * u[i];
+      }
       if (scale != nullptr) {
         const float sc = scale[row];
 #pragma unroll
@@ -171,21 +179,27 @@ hipError_t launch_transpose_bf16(const void* src, int rows, int cols, int64_t sr
   return hipGetLastError();
 }
 
-hipError_t launch_pad_transpose(int dtype_src, const void* src, int64_t ld_src,
+hipError_t launch_pad_transpose(int dtype_src, const void* src, const float* src2, int64_t ld_src,
                                 const int32_t* gather, const float* scale,
                                 const int32_t* offsets, const int32_t* kt, int groups,
                                 int64_t max_ptiles, int cols, void* dst, int64_t ldp,
                                 hipStream_t st) {
   if (max_ptiles <= 0 || cols <= 0) return hipSuccess;
+  if (src2 != nullptr && dtype_src != MOE_F32) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(max_ptiles), static_cast<unsigned>(cdiv(cols, TT)));
-  if (dtype_src == MOE_F32)
-    hipLaunchKernelGGL(pad_transpose_kernel<float>, grid, dim3(256), 0, st,
-                       static_cast<const float*>(src), ld_src, gather, scale, offsets, kt, groups,
-                       cols, static_cast<bf16_t*>(dst), ldp);
+  bf16_t* o = static_cast<bf16_t*>(dst);
+  if (src2 != nullptr)
+    hipLaunchKernelGGL((pad_transpose_kernel<float, true>), grid, dim3(256), 0, st,
+                       static_cast<const float*>(src), src2, ld_src, gather, scale, offsets, kt,
+                       groups, cols, o, ldp);
+  else if (dtype_src == MOE_F32)
+    hipLaunchKernelGGL((pad_transpose_kernel<float, false>), grid, dim3(256), 0, st,
+                       static_cast<const float*>(src), nullptr, ld_src, gather, scale, offsets, kt,
+                       groups, cols, o, ldp);
   else
-    hipLaunchKernelGGL(pad_transpose_kernel<bf16_t>, grid, dim3(256), 0, st,
-                       static_cast<const bf16_t*>(src), ld_src, gather, scale, offsets, kt,
-                       groups, cols, static_cast<bf16_t*>(dst), ldp);
+    hipLaunchKernelGGL((pad_transpose_kernel<bf16_t, false>), grid, dim3(256), 0, st,
+                       static_cast<const bf16_t*>(src), nullptr, ld_src, gather, scale, offsets,
+                       kt, groups, cols, o, ldp);
   return hipGetLastError();
 }
 

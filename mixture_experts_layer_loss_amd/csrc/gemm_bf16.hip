@@ -92,7 +92,8 @@ __device__ __forceinline__ void sched_substep() {
 
 // One MR x 256 output tile of group g: rows [row_begin, row_begin + rows_here), output columns
 // [n0, n0 + BNO). EPI 0: SwiGLU (B0 = W_gate, B1 = W_up); EPI 1: plain (B0 = W_down); EPI 2:
-// plain with fp32 output (C is then float), stored straight from the accumulators.
+// plain with fp32 output (C is then float), stored straight from the accumulators; EPI 3: the
+// gate and up pre-activations of EPI 0 stored as fp32 to C and C2.
 // KTAIL: K is not a multiple of 64 (the last k-slice is zero-padded). Row r of A starts at
 // A + r lda (gathered: A + gather[r] lda), row n of group g's B at B + g group_stride + n ldb, and
 // output row r at C + r ldc.
@@ -102,9 +103,11 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
                                          const bf16_t* __restrict__ B0,
                                          const bf16_t* __restrict__ B1, int64_t group_stride,
                                          int ldb, int N, int K, bf16_t* __restrict__ C, int ldc,
-                                         int g, int row_begin, int rows_here, int n0) {
+                                         float* __restrict__ C2, int g, int row_begin,
+                                         int rows_here, int n0) {
   using G = Geo<MR>;
-  constexpr int BNO = EPI == 0 ? BN / 2 : BN;  // output columns per tile
+  constexpr bool PAIRED = EPI == 0 || EPI == 3;  // B rows: 128 gate + 128 up
+  constexpr int BNO = PAIRED ? BN / 2 : BN;      // output columns per tile
   constexpr int MI = G::MI, NJ = G::NJ, ACH = G::ACH, BCH = G::BCH, RS = G::RSTEP;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / G::WN, wn = wave % G::WN;
@@ -125,10 +128,10 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
   }
   const bf16_t* Bg0 = B0 + static_cast<int64_t>(g) * group_stride + static_cast<int64_t>(n0) * ldb;
   const bf16_t* Bg1 =
-      EPI == 0 ? B1 + static_cast<int64_t>(g) * group_stride + static_cast<int64_t>(n0) * ldb : Bg0;
+      PAIRED ? B1 + static_cast<int64_t>(g) * group_stride + static_cast<int64_t>(n0) * ldb : Bg0;
   const char* b_base0 = reinterpret_cast<const char*>(Bg0);
   const char* b_base1 = reinterpret_cast<const char*>(Bg1);
-  const int b_rows = min(EPI == 0 ? BN / 2 : BN, N - n0);
+  const int b_rows = min(PAIRED ? BN / 2 : BN, N - n0);
   uint32_t a_off[ACH], b_off[BCH];
 #pragma unroll
   for (int i = 0; i < ACH; ++i)
@@ -136,7 +139,7 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
 #pragma unroll
   for (int i = 0; i < BCH; ++i) {
     const int r = i * RS + r0;
-    const int rb_ = EPI == 0 ? (r & (BN / 2 - 1)) : r;
+    const int rb_ = PAIRED ? (r & (BN / 2 - 1)) : r;
     b_off[i] = static_cast<uint32_t>((min(rb_, b_rows - 1) * ldb + kc_t) * 2);
   }
   u32x4 ra[ACH], rb[BCH];
@@ -153,7 +156,7 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
     }
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
-      const char* bb = (EPI == 0 && i >= BCH / 2) ? b_base1 : b_base0;
+      const char* bb = (PAIRED && i >= BCH / 2) ? b_base1 : b_base0;
       const u32x4 v = *reinterpret_cast<const u32x4*>(bb + (b_off[i] + kb));
       rb[i] = KTAIL ? (in ? v : zero) : v;
     }
@@ -191,7 +194,7 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
   int brow[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j)
-    brow[j] = EPI == 0 ? ((j < NJ / 2 ? 0 : BN / 2) + wn * (G::WCOLS / 2) + (j % (NJ / 2)) * 32)
+    brow[j] = PAIRED ? ((j < NJ / 2 ? 0 : BN / 2) + wn * (G::WCOLS / 2) + (j % (NJ / 2)) * 32)
                        : (wn * G::WCOLS + j * 32);
   bf16x8 fa[2][MI], fb[2][NJ];
   auto lfrag = [&](int set, int stage, int sub) __attribute__((always_inline)) {
@@ -281,6 +284,26 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
       }
     return;
   }
+  if constexpr (EPI == 3) {
+    // fp32 gate (C) and up (C2) pre-activations of the same output columns
+    float* Cg = reinterpret_cast<float*>(C);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < NJ / 2; ++jj) {
+        const int col = n0 + wn * (G::WCOLS / 2) + jj * 32 + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * G::WROWS + i * 32 + (r >> 2) * 8 + lk * 4 + (r & 3);
+          if (row < rows_here && col < N) {
+            const int64_t o = static_cast<int64_t>(row_begin + row) * ldc + col;
+            Cg[o] = acc[i][jj][r];
+            C2[o] = acc[i][jj + NJ / 2][r];
+          }
+        }
+      }
+    return;
+  }
   __syncthreads();
 
   // ---- epilogue: registers -> LDS tile [MR][BNO + 8] (bf16) -> coalesced 16-byte stores
@@ -334,8 +357,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tile_off, int groups, int main_blocks,
     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, int64_t group_stride, int N,
-    int K, bf16_t* __restrict__ C) {
-  constexpr int BNO = EPI == 0 ? BN / 2 : BN;
+    int K, bf16_t* __restrict__ C, float* __restrict__ C2) {
+  constexpr int BNO = (EPI == 0 || EPI == 3) ? BN / 2 : BN;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int nb_count = (N + BNO - 1) / BNO;
   const int32_t* t256 = tile_off;
@@ -352,8 +375,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     const int nb = static_cast<int>(local / mt_g), mt = static_cast<int>(local % mt_g);
     const int row_begin = offsets[g] + mt * 256;
     const int rows = min(256, offsets[g + 1] - row_begin);
-    run_tile<EPI, KTAIL, GATHER, 256>(lds, A, K, gather, B0, B1, group_stride, K, N, K, C, N, g,
-                                      row_begin, rows, nb * BNO);
+    run_tile<EPI, KTAIL, GATHER, 256>(lds, A, K, gather, B0, B1, group_stride, K, N, K, C, N, C2,
+                                      g, row_begin, rows, nb * BNO);
     return;
   }
   // a group's remainder tile (at most one per group and class): n-blocks in order
@@ -372,11 +395,11 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
   const int rows = rows_g & 255;
   const int n0 = static_cast<int>(local) * BNO;
   if (table == t128)
-    run_tile<EPI, KTAIL, GATHER, 128>(lds, A, K, gather, B0, B1, group_stride, K, N, K, C, N, g,
-                                      row_begin, rows, n0);
+    run_tile<EPI, KTAIL, GATHER, 128>(lds, A, K, gather, B0, B1, group_stride, K, N, K, C, N, C2,
+                                      g, row_begin, rows, n0);
   else
-    run_tile<EPI, KTAIL, GATHER, 64>(lds, A, K, gather, B0, B1, group_stride, K, N, K, C, N, g,
-                                     row_begin, rows, n0);
+    run_tile<EPI, KTAIL, GATHER, 64>(lds, A, K, gather, B0, B1, group_stride, K, N, K, C, N, C2,
+                                     g, row_begin, rows, n0);
 }
 
 // Weight gradients: C_g [Ma][Nb] (fp32) = sum over k in [64 kt[g], 64 kt[g+1]) of A[m][k] B[n][k],
@@ -411,15 +434,17 @@ __global__ __launch_bounds__(NT, 1) void wgrad_gemm_kernel(const bf16_t* __restr
     return;
   }
   run_tile<2, false, false, 256>(lds, A + k0, lda, nullptr, B + k0, nullptr, 0, ldb, Nb, K,
-                                 reinterpret_cast<bf16_t*>(Cg), Nb, 0, m0, min(256, Ma - m0), n0);
+                                 reinterpret_cast<bf16_t*>(Cg), Nb, nullptr, 0, m0,
+                                 min(256, Ma - m0), n0);
 }
 
 template <int EPI, bool KTAIL, bool GATHER>
 hipError_t launch_gemm_t(const bf16_t* A, const int32_t* gather, const int32_t* offsets,
                          const int32_t* tile_off,
                          int groups, int64_t max_tiles, const bf16_t* B0, const bf16_t* B1,
-                         int64_t group_stride, int N, int K, bf16_t* C, hipStream_t st) {
-  constexpr int BNO = EPI == 0 ? BN / 2 : BN;
+                         int64_t group_stride, int N, int K, bf16_t* C, float* C2,
+                         hipStream_t st) {
+  constexpr int BNO = (EPI == 0 || EPI == 3) ? BN / 2 : BN;
   const int64_t nb = cdiv(N, BNO);
   // the 256-row tiles, then at most one 128-row and one 64-row tile per group
   const int64_t main_blocks = cdiv(max_tiles * nb, NXCD) * NXCD;
@@ -440,7 +465,7 @@ hipError_t launch_gemm_t(const bf16_t* A, const int32_t* gather, const int32_t* 
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((grouped_gemm_kernel<EPI, KTAIL, GATHER>), dim3(static_cast<unsigned>(grid)),
                      dim3(NT), lds, st, A, gather, offsets, tile_off, groups,
-                     static_cast<int>(main_blocks), B0, B1, group_stride, N, K, C);
+                     static_cast<int>(main_blocks), B0, B1, group_stride, N, K, C, C2);
   return hipGetLastError();
 }
 
@@ -448,12 +473,12 @@ template <int EPI, bool GATHER>
 hipError_t launch_gemm(const bf16_t* A, const int32_t* gather, const int32_t* offsets,
                        const int32_t* tile_off, int groups, int64_t max_tiles, const bf16_t* B0,
                        const bf16_t* B1, int64_t group_stride, int N, int K, bf16_t* C,
-                       hipStream_t st) {
+                       hipStream_t st, float* C2 = nullptr) {
   if (K % BK == 0)
     return launch_gemm_t<EPI, false, GATHER>(A, gather, offsets, tile_off, groups, max_tiles, B0,
-                                             B1, group_stride, N, K, C, st);
+                                             B1, group_stride, N, K, C, C2, st);
   return launch_gemm_t<EPI, true, GATHER>(A, gather, offsets, tile_off, groups, max_tiles, B0, B1,
-                                          group_stride, N, K, C, st);
+                                          group_stride, N, K, C, C2, st);
 }
 
 }  // namespace
@@ -472,6 +497,26 @@ hipError_t launch_gemm_up_bf16(int groups, int d, int Mg, const void* rows,
                                 H, st);
   return launch_gemm<0, false>(A, nullptr, offsets, tile_off, groups, max_tiles, Wg, Wu, gs, Mg, d,
                                H, st);
+}
+
+// G[r] = A_r W_gate[g]^T and U[r] = A_r W_up[g]^T in fp32 (A_r = rows[gather[r]] when gather !=
+// NULL): the gate/up tile of the SwiGLU GEMM with the pre-activations stored instead of h (the
+// backward's recompute)
+hipError_t launch_gemm_gu_f32out_bf16(int groups, int d, int Mg, const void* rows,
+                                      const int32_t* gather, const int32_t* offsets,
+                                      const int32_t* tile_off, int64_t max_tiles,
+                                      const void* W_gate, const void* W_up, float* G, float* U,
+                                      hipStream_t st) {
+  const bf16_t* A = static_cast<const bf16_t*>(rows);
+  const bf16_t* Wg = static_cast<const bf16_t*>(W_gate);
+  const bf16_t* Wu = static_cast<const bf16_t*>(W_up);
+  const int64_t gs = static_cast<int64_t>(Mg) * d;
+  bf16_t* Gp = reinterpret_cast<bf16_t*>(G);  // holds floats (EPI 3)
+  if (gather != nullptr)
+    return launch_gemm<3, true>(A, gather, offsets, tile_off, groups, max_tiles, Wg, Wu, gs, Mg, d,
+                                Gp, st, U);
+  return launch_gemm<3, false>(A, nullptr, offsets, tile_off, groups, max_tiles, Wg, Wu, gs, Mg, d,
+                               Gp, st, U);
 }
 
 // C[r] = A_r B_g^T for the rows of group g (A_r = rows[gather[r]] when gather != NULL): the plain

@@ -226,8 +226,8 @@ struct LayerBackwardPlan {
   float* cols;                    // [2][E][T] logits and scores
   int32_t *tile64, *sh_tile64;    // 64-row tile tables of the fp32 products
   float *G, *U;                   // [R, M] fp32 pre-activations
-  float *h, *P;                   // [R, M] fp32: SiLU(G) U and dy_t W_down[e]
-  float *dout, *dw, *dl, *dlT, *dh, *dG, *dU, *dxr, *partial;
+  float *h, *P;                   // [R, M] fp32: SiLU(G) U (fp32 layers) and dy_t W_down[e]
+  float *dout, *dw, *dl, *dlT, *dG, *dU, *dxr, *partial;
   int ks_w;
   float *Gs, *Us;                 // shared experts [T, S M] fp32
   float *hs, *dhs, *dGs, *dUs, *dxs;   // [T, S M] and [T, d]
@@ -246,16 +246,15 @@ LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
   p.cols = c.take<float>(2 * E * T);
   p.tile64 = c.take<int32_t>(3 * (E + 1));
   p.sh_tile64 = c.take<int32_t>(3 * 2);
+  const bool mfma = s->dtype == MOE_BF16;
   p.G = c.take<float>(R * M);
   p.U = c.take<float>(R * M);
-  p.h = c.take<float>(R * M);
+  p.h = mfma ? nullptr : c.take<float>(R * M);
   p.P = c.take<float>(R * M);
-  p.dout = s->dtype == MOE_BF16 ? nullptr : c.take<float>(R * d);
+  p.dout = mfma ? nullptr : c.take<float>(R * d);
   p.dw = c.take<float>(T * s->k);
   p.dl = c.take<float>(T * E);
   p.dlT = c.take<float>(T * E);
-  p.dh = c.take<float>(R * M);
-  const bool mfma = s->dtype == MOE_BF16;
   p.dG = mfma ? nullptr : c.take<float>(R * M);
   p.dU = mfma ? nullptr : c.take<float>(R * M);
   p.dxr = c.take<float>(R * d);
@@ -282,7 +281,7 @@ LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
     const size_t SM = static_cast<size_t>(s->S) * M;
     p.Gs = c.take<float>(T * SM);
     p.Us = c.take<float>(T * SM);
-    p.hs = c.take<float>(T * SM);
+    p.hs = mfma ? nullptr : c.take<float>(T * SM);
     p.dhs = c.take<float>(T * SM);
     p.dGs = mfma ? nullptr : c.take<float>(T * SM);
     p.dUs = mfma ? nullptr : c.take<float>(T * SM);
@@ -646,19 +645,25 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
   if (e == hipSuccess)
     e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx, route_block_tokens(s->dtype, s->E),
                        f.block_base, f.offsets, nullptr, f.perm_token, f.inv_perm, hs);
-  if (e == hipSuccess)
-    e = launch_gemm_plain(s->dtype, s->E, x, f.perm_token, f.offsets, f.tile_off, max_tiles,
-                          W_gate, dM, s->M, s->d, p.G, hs);
-  if (e == hipSuccess)
-    e = launch_gemm_plain(s->dtype, s->E, x, f.perm_token, f.offsets, f.tile_off, max_tiles, W_up,
-                          dM, s->M, s->d, p.U, hs);
-  if (e == hipSuccess) e = launch_swiglu_fwd(R * s->M, p.G, p.U, p.h, hs);
+  const bool mfma = s->dtype == MOE_BF16;
+  if (mfma) {  // G and U in one launch (gate and up tiles paired)
+    if (e == hipSuccess)
+      e = launch_gemm_gu_f32out_bf16(s->E, s->d, s->M, x, f.perm_token, f.offsets, f.tile_off,
+                                     max_tiles, W_gate, W_up, p.G, p.U, hs);
+  } else {
+    if (e == hipSuccess)
+      e = launch_gemm_plain(s->dtype, s->E, x, f.perm_token, f.offsets, f.tile_off, max_tiles,
+                            W_gate, dM, s->M, s->d, p.G, hs);
+    if (e == hipSuccess)
+      e = launch_gemm_plain(s->dtype, s->E, x, f.perm_token, f.offsets, f.tile_off, max_tiles,
+                            W_up, dM, s->M, s->d, p.U, hs);
+    if (e == hipSuccess) e = launch_swiglu_fwd(R * s->M, p.G, p.U, p.h, hs);
+  }
   if (e == hipSuccess)
     e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s) | kRouteExpertChoice, x, W_r,
                      nullptr, nullptr, nullptr, f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart, p.cols,
                      hs);
   if (e == hipSuccess) e = launch_schedule(s->E, f.offsets, p.tile64, 64, hs);
-  const bool mfma = s->dtype == MOE_BF16;
   const int d = s->d, M = s->M;
   if (mfma) {  // weights transposed for the products that reduce over d or M
     if (e == hipSuccess)  // W_down[e]^T [M][d]
@@ -668,7 +673,7 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
     if (e == hipSuccess)
       e = launch_transpose_bf16(W_up, M, d, dM, s->E, p.WguT, 2 * M, M, 2 * dM, hs);
   }
-  // ---- combine: P_row = dy_t W_down[e] gives d w = <P, h> and dh = w P; d out = w dy_t
+  // ---- combine: P_row = dy_t W_down[e] gives d w = <P, h> and dh = w P, hence dG, dU
   if (e == hipSuccess && mfma)
     e = launch_gemm_plain(s->dtype, s->E, dy, f.perm_token, f.offsets, f.tile_off, max_tiles,
                           p.WdT, dM, M, d, p.P, hs);
@@ -677,35 +682,34 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
                        s->E, max_t64, W_down, nullptr, dM, s->M, s->d, p.P, hs);
   if (e == hipSuccess)
     e = launch_bw_rows(s->dtype, f.offsets, s->E, R, s->d, s->M, s->k, f.perm_token, f.inv_perm,
-                       f.topk_w, dy, p.P, p.h, p.dw, p.dh, p.dout, p.wrow, hs);
+                       f.topk_w, dy, p.P, p.G, p.U, p.dw, p.dG, p.dU, p.dGU, p.dout, p.wrow, hs);
   if (e == hipSuccess)
     e = launch_bw_router(s->T, s->E, s->k, s->renorm, s->scoring == MOE_SCORE_SIGMOID, p.cols,
                          p.cols + ET, idx, f.inv_perm, f.topk_w, p.dw, f.n, stats_fden(s), lambda,
                          z_coef, p.dl, p.dlT, hs);
   // ---- routed experts
   if (mfma) {
-    if (e == hipSuccess) e = launch_swiglu_bw_cat(R, M, p.dh, p.G, p.U, p.dGU, hs);
     if (e == hipSuccess)  // dx_row = [dG dU] [W_gate[e] W_up[e]]^T^T over K = 2M
       e = launch_gemm_plain(s->dtype, s->E, p.dGU, nullptr, f.offsets, f.tile_off, max_tiles,
                             p.WguT, 2 * dM, d, 2 * M, p.dxr, hs);
     // weight-gradient operands: each expert's rows as a zero-padded column range
     const int64_t lp = p.ldp;
     const bf16_t* dGU = static_cast<const bf16_t*>(p.dGU);
-    if (e == hipSuccess)  // (w h)^T
-      e = launch_pad_transpose(MOE_F32, p.h, M, nullptr, p.wrow, f.offsets, p.tile64, s->E,
+    if (e == hipSuccess)  // (w h)^T with h = SiLU(G) U
+      e = launch_pad_transpose(MOE_F32, p.G, p.U, M, nullptr, p.wrow, f.offsets, p.tile64, s->E,
                                max_t64, M, p.whT, lp, hs);
     if (e == hipSuccess)
-      e = launch_pad_transpose(MOE_BF16, dGU, 2 * M, nullptr, nullptr, f.offsets, p.tile64, s->E,
-                               max_t64, M, p.dGT, lp, hs);
+      e = launch_pad_transpose(MOE_BF16, dGU, nullptr, 2 * M, nullptr, nullptr, f.offsets,
+                               p.tile64, s->E, max_t64, M, p.dGT, lp, hs);
     if (e == hipSuccess)
-      e = launch_pad_transpose(MOE_BF16, dGU + M, 2 * M, nullptr, nullptr, f.offsets, p.tile64,
-                               s->E, max_t64, M, p.dUT, lp, hs);
+      e = launch_pad_transpose(MOE_BF16, dGU + M, nullptr, 2 * M, nullptr, nullptr, f.offsets,
+                               p.tile64, s->E, max_t64, M, p.dUT, lp, hs);
     if (e == hipSuccess)  // dy rows of the kept slots (exact bf16)
-      e = launch_pad_transpose(MOE_BF16, dy, d, f.perm_token, nullptr, f.offsets, p.tile64, s->E,
-                               max_t64, d, p.dyT, lp, hs);
+      e = launch_pad_transpose(MOE_BF16, dy, nullptr, d, f.perm_token, nullptr, f.offsets,
+                               p.tile64, s->E, max_t64, d, p.dyT, lp, hs);
     if (e == hipSuccess)
-      e = launch_pad_transpose(MOE_BF16, x, d, f.perm_token, nullptr, f.offsets, p.tile64, s->E,
-                               max_t64, d, p.xT, lp, hs);
+      e = launch_pad_transpose(MOE_BF16, x, nullptr, d, f.perm_token, nullptr, f.offsets,
+                               p.tile64, s->E, max_t64, d, p.xT, lp, hs);
     if (e == hipSuccess)  // dW_down[e] = sum over its rows of dy_t^T (w h)
       e = launch_gemm_wgrad_bf16(p.dyT, static_cast<int>(lp), p.whT, static_cast<int>(lp),
                                  p.tile64, s->E, d, M, dW_down, hs);
@@ -716,8 +720,6 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
       e = launch_gemm_wgrad_bf16(p.dUT, static_cast<int>(lp), p.xT, static_cast<int>(lp),
                                  p.tile64, s->E, M, d, dW_up, hs);
   }
-  if (e == hipSuccess && !mfma)
-    e = launch_swiglu_bw(MOE_F32, R * s->M, p.dh, p.G, p.U, p.dG, p.dU, hs);
   if (e == hipSuccess && !mfma)  // dx_row = dG W_gate[e] + dU W_up[e]
     e = launch_nn_gemm(MOE_F32, s->dtype, true, p.dG, p.dU, nullptr, f.offsets, p.tile64, s->E,
                        max_t64, W_gate, W_up, dM, s->d, s->M, p.dxr, hs);
@@ -741,14 +743,20 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
     const int64_t sh_tiles = cdiv(s->T, BM);
     const int64_t dSM = static_cast<int64_t>(s->d) * SM;
     e = launch_shared_table(s->T, BM, f.sh_offsets, f.sh_tile_off, hs);
-    if (e == hipSuccess)
-      e = launch_gemm_plain(s->dtype, 1, x, nullptr, f.sh_offsets, f.sh_tile_off, sh_tiles,
-                            Ws_gate, dSM, SM, s->d, p.Gs, hs);
-    if (e == hipSuccess)
-      e = launch_gemm_plain(s->dtype, 1, x, nullptr, f.sh_offsets, f.sh_tile_off, sh_tiles, Ws_up,
-                            dSM, SM, s->d, p.Us, hs);
-    if (e == hipSuccess)
-      e = launch_swiglu_fwd(static_cast<int64_t>(s->T) * SM, p.Gs, p.Us, p.hs, hs);
+    if (mfma) {
+      if (e == hipSuccess)
+        e = launch_gemm_gu_f32out_bf16(1, s->d, SM, x, nullptr, f.sh_offsets, f.sh_tile_off,
+                                       sh_tiles, Ws_gate, Ws_up, p.Gs, p.Us, hs);
+    } else {
+      if (e == hipSuccess)
+        e = launch_gemm_plain(s->dtype, 1, x, nullptr, f.sh_offsets, f.sh_tile_off, sh_tiles,
+                              Ws_gate, dSM, SM, s->d, p.Gs, hs);
+      if (e == hipSuccess)
+        e = launch_gemm_plain(s->dtype, 1, x, nullptr, f.sh_offsets, f.sh_tile_off, sh_tiles,
+                              Ws_up, dSM, SM, s->d, p.Us, hs);
+      if (e == hipSuccess)
+        e = launch_swiglu_fwd(static_cast<int64_t>(s->T) * SM, p.Gs, p.Us, p.hs, hs);
+    }
     if (e == hipSuccess) e = launch_schedule(1, f.sh_offsets, p.sh_tile64, 64, hs);
     const int64_t sh_t64 = cdiv(s->T, 64) + 1;
     if (mfma) {
@@ -768,21 +776,22 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
         e = launch_gemm_plain(s->dtype, 1, p.dGUs, nullptr, f.sh_offsets, f.sh_tile_off, sh_tiles,
                               p.WsguT, 0, d, 2 * SM, p.dxs, hs);
       const int64_t pt = cdiv(s->T, 64);
+      const int32_t* so = f.sh_offsets;
       if (e == hipSuccess)
-        e = launch_pad_transpose(MOE_BF16, dy, d, nullptr, nullptr, f.sh_offsets, p.sh_tile64, 1, pt, d,
-                                 p.dysT, lps, hs);
+        e = launch_pad_transpose(MOE_BF16, dy, nullptr, d, nullptr, nullptr, so, p.sh_tile64, 1,
+                                 pt, d, p.dysT, lps, hs);
+      if (e == hipSuccess)  // h^T with h = SiLU(G) U
+        e = launch_pad_transpose(MOE_F32, p.Gs, p.Us, SM, nullptr, nullptr, so, p.sh_tile64, 1,
+                                 pt, SM, p.hsT, lps, hs);
       if (e == hipSuccess)
-        e = launch_pad_transpose(MOE_F32, p.hs, SM, nullptr, nullptr, f.sh_offsets, p.sh_tile64, 1, pt, SM,
-                                 p.hsT, lps, hs);
+        e = launch_pad_transpose(MOE_BF16, dGUs, nullptr, 2 * SM, nullptr, nullptr, so,
+                                 p.sh_tile64, 1, pt, SM, p.dGsT, lps, hs);
       if (e == hipSuccess)
-        e = launch_pad_transpose(MOE_BF16, dGUs, 2 * SM, nullptr, nullptr, f.sh_offsets, p.sh_tile64, 1, pt,
-                                 SM, p.dGsT, lps, hs);
+        e = launch_pad_transpose(MOE_BF16, dGUs + SM, nullptr, 2 * SM, nullptr, nullptr, so,
+                                 p.sh_tile64, 1, pt, SM, p.dUsT, lps, hs);
       if (e == hipSuccess)
-        e = launch_pad_transpose(MOE_BF16, dGUs + SM, 2 * SM, nullptr, nullptr, f.sh_offsets, p.sh_tile64, 1,
-                                 pt, SM, p.dUsT, lps, hs);
-      if (e == hipSuccess)
-        e = launch_pad_transpose(MOE_BF16, x, d, nullptr, nullptr, f.sh_offsets, p.sh_tile64, 1, pt, d,
-                                 p.xsT, lps, hs);
+        e = launch_pad_transpose(MOE_BF16, x, nullptr, d, nullptr, nullptr, so, p.sh_tile64, 1, pt,
+                                 d, p.xsT, lps, hs);
       if (e == hipSuccess)
         e = launch_gemm_wgrad_bf16(p.dysT, static_cast<int>(lps), p.hsT, static_cast<int>(lps),
                                    p.sh_tile64, 1, d, SM, dWs_down, hs);

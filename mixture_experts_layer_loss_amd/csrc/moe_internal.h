@@ -132,12 +132,14 @@ hipError_t launch_gemm_plain(int dtype, int groups, const void* rows, const int3
                              const void* B, int64_t group_stride, int N, int K, void* C,
                              hipStream_t st);
 
-// Backward (backward.hip). Per kept row: dw [T, k] (slot of the row), dh = w P, and when not
-// NULL dout = w dy_t and wrow = w.
+// Backward (backward.hip). Per kept row, from P = dy_t W_down[e] and the fp32 pre-activations:
+// dw [T, k] (slot of the row) and the SwiGLU derivative of dh = w P, as fp32 dG, dU [R, M] or, when
+// dGU != NULL, one bf16 row [dG | dU] of 2M; when not NULL dout = w dy_t and wrow = w.
 hipError_t launch_bw_rows(int dtype, const int32_t* offsets, int E, int64_t R, int d, int M,
                           int k, const int32_t* perm_token, const int32_t* inv_perm,
-                          const float* topk_w, const void* dy, const float* P, const float* h,
-                          float* dw, float* dh, float* dout, float* wrow, hipStream_t st);
+                          const float* topk_w, const void* dy, const float* P, const float* G,
+                          const float* U, float* dw, float* dG, float* dU, void* dGU, float* dout,
+                          float* wrow, hipStream_t st);
 hipError_t launch_swiglu_fwd(int64_t count, const float* G, const float* U, float* h,
                              hipStream_t st);
 hipError_t launch_bw_router(int64_t T, int E, int k, int renorm, int sigmoid, const float* lcol,
@@ -166,8 +168,9 @@ hipError_t launch_transpose_bf16(const void* src, int rows, int cols, int64_t sr
                                  hipStream_t st);
 // dst [cols][ldp] bf16: column p of group g (64 kt[g] <= p < 64 kt[g+1]) = source row
 // i = offsets[g] + p - 64 kt[g] (row gather[i] of src when gather != NULL), times scale[i] when
-// scale != NULL; zeros past the group's rows.
-hipError_t launch_pad_transpose(int dtype_src, const void* src, int64_t ld_src,
+// scale != NULL; zeros past the group's rows. With src2 != NULL (fp32 only) the source value is
+// SiLU(src) src2 (h from the pre-activations G, U).
+hipError_t launch_pad_transpose(int dtype_src, const void* src, const float* src2, int64_t ld_src,
                                 const int32_t* gather, const float* scale,
                                 const int32_t* offsets, const int32_t* kt, int groups,
                                 int64_t max_ptiles, int cols, void* dst, int64_t ldp,
@@ -175,6 +178,12 @@ hipError_t launch_pad_transpose(int dtype_src, const void* src, int64_t ld_src,
 // dGU [R][2M] bf16 = [dh U SiLU'(G) | dh SiLU(G)] from fp32 [R][M] inputs
 hipError_t launch_swiglu_bw_cat(int64_t R, int M, const float* dh, const float* G, const float* U,
                                 void* dGU, hipStream_t st);
+// G[r] = a_r W_gate[g]^T, U[r] = a_r W_up[g]^T in fp32 (one launch, gate/up tiles paired)
+hipError_t launch_gemm_gu_f32out_bf16(int groups, int d, int Mg, const void* rows,
+                                      const int32_t* gather, const int32_t* offsets,
+                                      const int32_t* tile_off, int64_t max_tiles,
+                                      const void* W_gate, const void* W_up, float* G, float* U,
+                                      hipStream_t st);
 // C_g [Ma][Nb] fp32 = sum over k in [64 kt[g], 64 kt[g+1]) of A[m][k] B[n][k]
 hipError_t launch_gemm_wgrad_bf16(const void* A, int lda, const void* B, int ldb,
                                   const int32_t* kt, int groups, int Ma, int Nb, float* C,

@@ -434,6 +434,116 @@ def layer_backward(x, W_r, W_gate, W_up, W_down, dy, k: int, b=None, shared=(), 
     return out
 
 
+def layer_backward_sampled(x, W_r, W_gate, W_up, W_down, dy, k: int, b=None, shared=(), c=None,
+                           renorm: bool = True, lam: float = 0.01, z_coef: float = 0.0,
+                           scoring: str = "softmax", topk_idx=None, tokens=(), expert_cols=(),
+                           shared_cols=(), expert_weights=None):
+    """Selected entries of layer_backward, each evaluated on its own from the same chain, for
+    layers too large for the whole backward on the host:
+      dx[t] for t in tokens (its kept slots' experts, its router row and the shared experts);
+      for (e, m) in expert_cols: row m of dW_gate[e] and of dW_up[e] (sums over e's kept rows r of
+        dG[r, m] x_t(r), dU[r, m] x_t(r)) and column m of dW_down[e] (sum over r of
+        w_r dy_t(r) h[r, m]) -- G[r, m], U[r, m] and P[r, m] = dy_t(r) W_down[e][:, m] are single
+        dot products, so a column costs O(rows d);
+      for m in shared_cols: row m of the stacked shared gate/up gradients and column m of the
+        stacked down gradient (the S experts of width M side by side).
+    Routing, loads and the balance-loss gradient are computed for all tokens. ``expert_weights``
+    (optional) is a callable e -> (W_gate_e, W_up_e, W_down_e). Returns float64 arrays with the
+    magnitudes (sums of |terms|) of every entry under "magnitude"."""
+    x64 = _f64(x)
+    dy64 = _f64(dy)
+    T, d = x64.shape
+    r = route(x64, W_r, k, b, renorm, scoring)
+    l, g = r["logits"], r["g"]
+    E = g.shape[1]
+    S = r["topk_idx"] if topk_idx is None else np.asarray(topk_idx, dtype=np.int64)
+    w = gate_weights(g, S, renorm)
+    n = expert_loads(S, E)
+    dsp = dispatch(S, E, capacity(c, k, T, E))
+    bl = balance_loss_grad_logits(l, n / float(k * T), lam, z_coef, scoring)
+    W64 = _f64(W_r)
+    weights = expert_weights if expert_weights is not None else (
+        lambda e: (W_gate[e], W_up[e], W_down[e]))
+    tokens = [int(t) for t in tokens]
+    out = {"dx": np.zeros((len(tokens), d)), "magnitude": {"dx": np.zeros((len(tokens), d))}}
+    # ---- dx of the sampled tokens: expert part per kept slot, grouped by expert
+    slots = {}
+    for i, t in enumerate(tokens):
+        for j in range(k):
+            if dsp["row"][t, j] >= 0:
+                slots.setdefault(int(S[t, j]), []).append((i, t, j))
+    dw = np.zeros((len(tokens), k))
+    for e, lst in sorted(slots.items()):
+        Wg, Wu, Wd = (_f64(a) for a in weights(e))
+        for i, t, j in lst:
+            G, U = Wg @ x64[t], Wu @ x64[t]
+            P = dy64[t] @ Wd
+            dw[i, j] = P @ (silu(G) * U)
+            dh = w[t, j] * P
+            dG, dU = dh * U * silu_grad(G), dh * silu(G)
+            out["dx"][i] += dG @ Wg + dU @ Wu
+            out["magnitude"]["dx"][i] += np.abs(dG) @ np.abs(Wg) + np.abs(dU) @ np.abs(Wu)
+    # router part: gates -> scores -> logits, plus the balance-loss gradient
+    for i, t in enumerate(tokens):
+        gt = g[t]
+        dg = np.zeros(E)
+        if renorm:
+            dg[S[t]] = (dw[i] - (w[t] * dw[i]).sum()) / gt[S[t]].sum()
+        else:
+            dg[S[t]] = dw[i]
+        dl = gt * (dg - (gt * dg).sum()) if scoring == "softmax" else gt * (1.0 - gt) * dg
+        dl = dl + bl[t]
+        out["dx"][i] += dl @ W64
+        out["magnitude"]["dx"][i] += np.abs(dl) @ np.abs(W64)
+    for Wg, Wu, Wd in shared:
+        Wg, Wu, Wd = _f64(Wg), _f64(Wu), _f64(Wd)
+        for i, t in enumerate(tokens):
+            G, U = Wg @ x64[t], Wu @ x64[t]
+            dh = dy64[t] @ Wd
+            dG, dU = dh * U * silu_grad(G), dh * silu(G)
+            out["dx"][i] += dG @ Wg + dU @ Wu
+            out["magnitude"]["dx"][i] += np.abs(dG) @ np.abs(Wg) + np.abs(dU) @ np.abs(Wu)
+    # ---- weight-gradient entries of the routed experts
+    for key in ("dW_gate", "dW_up", "dW_down"):
+        out[key], out["magnitude"][key] = [], []
+    for e, m in expert_cols:
+        e, m = int(e), int(m)
+        rows = range(int(dsp["offsets"][e]), int(dsp["offsets"][e + 1]))
+        toks = np.array([int(dsp["perm_token"][rr]) for rr in rows], dtype=np.int64)
+        slot = np.array([int(np.nonzero(dsp["row"][t] == rr)[0][0]) for rr, t in zip(rows, toks)],
+                        dtype=np.int64)
+        Wg, Wu, Wd = weights(e)
+        X, Y = x64[toks], dy64[toks]
+        G, U = X @ _f64(Wg[m]), X @ _f64(Wu[m])
+        wt = w[toks, slot] if len(toks) else np.zeros(0)
+        dh = wt * (Y @ _f64(Wd[:, m]))
+        dG, dU, h = dh * U * silu_grad(G), dh * silu(G), silu(G) * U
+        dO = wt[:, None] * Y
+        for key, val, mag in (("dW_gate", dG @ X, np.abs(dG) @ np.abs(X)),
+                              ("dW_up", dU @ X, np.abs(dU) @ np.abs(X)),
+                              ("dW_down", dO.T @ h, np.abs(dO).T @ np.abs(h))):
+            out[key].append(val)
+            out["magnitude"][key].append(mag)
+    # ---- shared experts: column m of the stacked width S M
+    for key in ("dWs_gate", "dWs_up", "dWs_down"):
+        out[key], out["magnitude"][key] = [], []
+    for m in shared_cols:
+        m = int(m)
+        Wg, Wu, Wd = shared[m // shared[0][0].shape[0]]
+        mm = m % shared[0][0].shape[0]
+        G, U = x64 @ _f64(Wg[mm]), x64 @ _f64(Wu[mm])
+        dh = dy64 @ _f64(Wd[:, mm])
+        dG, dU, h = dh * U * silu_grad(G), dh * silu(G), silu(G) * U
+        for key, val, mag in (("dWs_gate", dG @ x64, np.abs(dG) @ np.abs(x64)),
+                              ("dWs_up", dU @ x64, np.abs(dU) @ np.abs(x64)),
+                              ("dWs_down", dy64.T @ h, np.abs(dy64).T @ np.abs(h))):
+            out[key].append(val)
+            out["magnitude"][key].append(mag)
+    out["topk_idx"] = S
+    out["tokens"] = np.array(tokens, dtype=np.int64)
+    return out
+
+
 def routing_entropy(probs: np.ndarray) -> float:
     """Mean over tokens of H(g(x)) = -sum_e g_e ln g_e ([ATLAS] §9 专业化是否真的发生: the routing
     entropy describes how concentrated the choice is), with 0 ln 0 = 0."""

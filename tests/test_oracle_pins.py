@@ -465,6 +465,39 @@ def test_layer_backward_pins():
     check_layer_backward()
 
 
+def test_layer_backward_sampled_matches_whole():
+    # the per-entry evaluation agrees with the whole backward on every token and every column,
+    # with capacity drops, shared experts, sigmoid scores and a bias
+    T, d, E, k, M = 16, 6, 4, 2, 5
+    rng = np.random.default_rng(91)
+    args = (rng.standard_normal((T, d)), rng.standard_normal((E, d)) * 0.5,
+            rng.standard_normal((E, M, d)) * 0.4, rng.standard_normal((E, M, d)) * 0.4,
+            rng.standard_normal((E, d, M)) * 0.4, rng.standard_normal((T, d)))
+    sh = [tuple(rng.standard_normal(sz) * 0.4 for sz in ((M, d), (M, d), (d, M))) for _ in range(2)]
+    bias = rng.uniform(-0.1, 0.1, E)
+    for scoring, renorm, c, b in (("softmax", True, 0.7, None), ("sigmoid", False, None, bias)):
+        kw = dict(b=b, shared=sh, c=c, renorm=renorm, lam=0.2, z_coef=0.5, scoring=scoring)
+        whole = O.layer_backward(*args, k, magnitudes=True, **kw)
+        cols = [(e, m) for e in range(E) for m in range(M)]
+        part = O.layer_backward_sampled(*args, k, tokens=range(T), expert_cols=cols,
+                                        shared_cols=range(2 * M), **kw)
+        assert np.allclose(part["dx"], whole["dx"], rtol=1e-12, atol=1e-13)
+        assert np.allclose(part["magnitude"]["dx"], whole["magnitude"]["dx"], rtol=1e-12)
+        for i, (e, m) in enumerate(cols):
+            for key, ref, mref in (("dW_gate", whole["dW_gate"][e, m], whole["magnitude"]["dW_gate"][e, m]),
+                                   ("dW_up", whole["dW_up"][e, m], whole["magnitude"]["dW_up"][e, m]),
+                                   ("dW_down", whole["dW_down"][e][:, m], whole["magnitude"]["dW_down"][e][:, m])):
+                assert np.allclose(part[key][i], ref, rtol=1e-12, atol=1e-13), (key, e, m)
+                assert np.allclose(part["magnitude"][key][i], mref, rtol=1e-12), (key, e, m)
+        sg = np.concatenate([t[0] for t in whole["shared"]], 0)
+        su = np.concatenate([t[1] for t in whole["shared"]], 0)
+        sd = np.concatenate([t[2] for t in whole["shared"]], 1)
+        for m in range(2 * M):
+            assert np.allclose(part["dWs_gate"][m], sg[m], rtol=1e-12, atol=1e-13)
+            assert np.allclose(part["dWs_up"][m], su[m], rtol=1e-12, atol=1e-13)
+            assert np.allclose(part["dWs_down"][m], sd[:, m], rtol=1e-12, atol=1e-13)
+
+
 def test_layer_backward_magnitudes_dominate():
     # the rounding-bound scales: same gradients with or without them, and each scale is at least
     # the absolute value of its gradient (a sum is bounded by the sum of its terms' magnitudes)
