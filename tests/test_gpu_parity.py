@@ -552,3 +552,70 @@ def test_full_size_sampled(gpu, name):
     tokens = np.sort(rng.choice(cfg.T, size=min(48, cfg.T), replace=False))
     info = check_layer(cfg, inp, out, tokens=tokens)
     say(f"    {info}")
+
+
+FULL_BW = ["mixtral_8x7b", "deepseekmoe_16b", "deepseek_v2", "skewed_capacity", "sigmoid_v3"]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", FULL_BW)
+def test_full_size_backward_sampled(gpu, name):
+    """The layer backward at full size, in the launch configuration bench.py times: dx on 8
+    sampled tokens; row m of dW_gate[e] and dW_up[e] and column m of dW_down[e] for the most and
+    the least loaded expert and two others (each entry is a sum over that expert's rows, computed
+    on its own by the oracle); three columns of the stacked shared gradients. Each entry within
+    its rounding bound and each sampled set normwise within u, as in test_layer_backward (dW_r,
+    a sum over every token, is covered by the small cases and the balance-loss backward)."""
+    cfg = workloads.CONFIGS[name]
+    say(f"[full backward] {cfg}")
+    inp = workloads.make_inputs(cfg)
+    d_ = to_dev(inp, gpu)
+    dy = torch.randn(cfg.T, cfg.d, generator=torch.Generator().manual_seed(11)).to(torch.bfloat16)
+    out = moe.moe_layer_backward(d_.x, d_.W_r, d_.W_gate, d_.W_up, d_.W_down, dy.to(gpu), cfg.k,
+                                 b=d_.b, shared=d_.shared_fused(), c=cfg.c, renorm=cfg.renorm,
+                                 lam=cfg.lam, z_coef=1.0, scoring=cfg.scoring)
+    torch.cuda.synchronize()
+    gidx = out["topk_idx"].cpu().numpy().astype(np.int64)
+    x64 = O._f64(inp.x)
+    b64 = None if inp.b is None else O._f64(inp.b)
+    check_selection(gidx, O.route(x64, O._f64(inp.W_r), cfg.k, b64, cfg.renorm, cfg.scoring),
+                    cfg.k)
+    rng = np.random.default_rng(3)
+    tokens = np.sort(rng.choice(cfg.T, size=8, replace=False))
+    loads = np.bincount(gidx.ravel(), minlength=cfg.E)
+    used = np.nonzero(loads)[0]
+    experts = [int(np.argmax(loads)), int(used[np.argmin(loads[used])])]
+    experts += [int(e) for e in rng.choice(used, size=2, replace=False)]
+    cols = [(e, int(m)) for e, m in zip(experts, [cfg.M - 1, 0, *rng.integers(0, cfg.M, 2)])]
+    SM = cfg.S * cfg.M
+    scols = [0, SM - 1, int(rng.integers(0, SM))] if cfg.S > 0 else []
+    shared = [tuple(O._f64(t) for t in s_) for s_ in inp.shared]
+    ref = O.layer_backward_sampled(
+        x64, inp.W_r, None, None, None, dy, cfg.k, b=b64, shared=shared, c=cfg.c,
+        renorm=cfg.renorm, lam=cfg.lam, z_coef=1.0, scoring=cfg.scoring, topk_idx=gidx,
+        tokens=tokens, expert_cols=cols, shared_cols=scols,
+        expert_weights=lambda e: (inp.W_gate[e], inp.W_up[e], inp.W_down[e]))
+    got = {"dx": out["dx"][torch.as_tensor(tokens, device=gpu)].cpu().double().numpy()}
+    got["dW_gate"] = [out["dW_gate"][e, m].cpu().double().numpy() for e, m in cols]
+    got["dW_up"] = [out["dW_up"][e, m].cpu().double().numpy() for e, m in cols]
+    got["dW_down"] = [out["dW_down"][e, :, m].cpu().double().numpy() for e, m in cols]
+    if scols:
+        got["dWs_gate"] = [out["dWs_gate"][m].cpu().double().numpy() for m in scols]
+        got["dWs_up"] = [out["dWs_up"][m].cpu().double().numpy() for m in scols]
+        got["dWs_down"] = [out["dWs_down"][:, m].cpu().double().numpy() for m in scols]
+    u = 2.0 ** -8
+    K = max(cfg.T, 2 * SM, 2 * cfg.M, cfg.d)
+    ratio, normwise = {}, {}
+    for key, val in got.items():
+        a = np.asarray(val, dtype=np.float64)
+        r = np.asarray(ref[key], dtype=np.float64)
+        mag = np.asarray(ref["magnitude"][key], dtype=np.float64)
+        err = np.abs(a - r)
+        bound = (u + 1e-5 + K * 2.0 ** -24) * mag
+        ratio[key] = float((err / np.maximum(bound, 1e-300)).max())
+        normwise[key] = float(np.linalg.norm(err) / np.linalg.norm(r))
+        assert (err <= bound).all(), (key, ratio[key])
+        assert normwise[key] <= u, (key, normwise[key])
+    say(f"    experts {cols} shared {scols}")
+    say(f"    max err / bound {ratio}")
+    say(f"    normwise {normwise}")
