@@ -343,7 +343,8 @@ __global__ __launch_bounds__(256) void swiglu_bw_kernel(int64_t count, const flo
   dU[i] = gh * z * sg;
 }
 
-// dx_t += sum_j dx_perm[row(t,j)] (slot order) + dx_sh[t]; one wave per token
+// dx_t += sum_j dx_perm[row(t,j)] (slot order) + dx_sh[t]; one wave per token. With d a multiple
+// of 4 lanes move float4s, 4 chunks apart per pass and all slots' loads issued before use.
 __global__ __launch_bounds__(256) void bw_dx_kernel(int64_t Tn, int d, int k,
                                                      const int32_t* __restrict__ inv_perm,
                                                      const float* __restrict__ dx_perm,
@@ -352,14 +353,50 @@ __global__ __launch_bounds__(256) void bw_dx_kernel(int64_t Tn, int d, int k,
   const int lane = threadIdx.x & 63;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
-  for (int i = lane; i < d; i += 64) {
-    float v = dx[t * d + i];
-    for (int j = 0; j < k; ++j) {
-      const int row = inv_perm[t * k + j];
-      if (row >= 0) v += dx_perm[static_cast<int64_t>(row) * d + i];
+  if ((d & 3) != 0) {
+    for (int i = lane; i < d; i += 64) {
+      float v = dx[t * d + i];
+      for (int j = 0; j < k; ++j) {
+        const int row = inv_perm[t * k + j];
+        if (row >= 0) v += dx_perm[static_cast<int64_t>(row) * d + i];
+      }
+      if (dx_sh != nullptr) v += dx_sh[t * d + i];
+      dx[t * d + i] = v;
     }
-    if (dx_sh != nullptr) v += dx_sh[t * d + i];
-    dx[t * d + i] = v;
+    return;
+  }
+  constexpr int U = 4, STEP = 256;
+  const int my_row = lane < k ? inv_perm[t * k + lane] : -1;  // lane j: slot j's row
+  for (int c0 = lane * 4; c0 < d; c0 += STEP * U) {
+    float4 acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      acc[u] = c0 + u * STEP < d ? *reinterpret_cast<const float4*>(dx + t * d + c0 + u * STEP)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const int row = __builtin_amdgcn_readlane(my_row, j);
+      if (row < 0) continue;
+      float4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        v[u] = c0 + u * STEP < d ? *reinterpret_cast<const float4*>(
+                                       dx_perm + static_cast<int64_t>(row) * d + c0 + u * STEP)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        acc[u].x += v[u].x; acc[u].y += v[u].y; acc[u].z += v[u].z; acc[u].w += v[u].w;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * STEP;
+      if (c >= d) continue;
+      if (dx_sh != nullptr) {
+        const float4 sv = *reinterpret_cast<const float4*>(dx_sh + t * d + c);
+        acc[u].x += sv.x; acc[u].y += sv.y; acc[u].z += sv.z; acc[u].w += sv.w;
+      }
+      *reinterpret_cast<float4*>(dx + t * d + c) = acc[u];
+    }
   }
 }
 

@@ -8,8 +8,8 @@
 //     dG_e^T x_e, dW_up[e] = dU_e^T x_e). Every product thus has one operand that was rounded to
 //     bf16 here (w h, dG, dU) and one exact bf16 input (dy, x, the weights).
 // The SwiGLU derivative ("深入理解 MoE (混合专家模型)：稀疏激活与高效扩展" §10.2) is written here as
-// one bf16 row [dG | dU] per kept row, the A operand of the dx product. All three kernels move
-// 64 x 64 tiles through LDS so that reads and writes are both coalesced.
+// one bf16 row [dG | dU] per kept row, the A operand of the dx product. The transposes keep both
+// their reads and their writes in contiguous runs of 128 bytes or more.
 #include "moe_internal.h"
 
 #include <math.h>
@@ -20,45 +20,40 @@ namespace {
 constexpr int TT = 64;       // tile edge
 constexpr int TP = TT + 2;   // LDS row pitch (elements)
 
-// dst[b][c][coff + r] = src[b][r][c]; rows, cols, ldd and coff multiples of 8.
+// dst[b][c][coff + r] = src[b][r][c]; rows, cols, ldd and coff multiples of 8. No LDS: lane
+// (rc, cc) of a wave loads the 8 x 8 block of rows 8 rc.. and columns 8 cc.. of the wave's 64 x 64
+// tile (eight 16-byte loads, each row's 8 lanes contiguous), transposes it in registers and stores
+// eight 16-byte rows of dst (each dst row's 8 lanes contiguous). A block of 4 waves covers 256 rows.
+__device__ __forceinline__ uint32_t pick16(uint32_t a, uint32_t b, int hi) {
+  // (half `hi` of a) | (half `hi` of b) << 16
+  return hi ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+}
+
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __restrict__ src,
                                                               int rows, int cols,
                                                               int64_t src_batch,
                                                               bf16_t* __restrict__ dst, int ldd,
                                                               int coff, int64_t dst_batch) {
-  __shared__ uint16_t tile[TT][TP];
-  const int tid = threadIdx.x;
-  const int c0 = blockIdx.x * TT, r0 = blockIdx.y * TT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rc = lane >> 3, cc = lane & 7;
+  const int r = blockIdx.y * 256 + wave * 64 + rc * 8;
+  const int c = blockIdx.x * 64 + cc * 8;
+  if (r >= rows || c >= cols) return;
   const bf16_t* s = src + static_cast<int64_t>(blockIdx.z) * src_batch;
   bf16_t* o = dst + static_cast<int64_t>(blockIdx.z) * dst_batch;
-  const int cc = (tid & 7) * 8;
+  uint32_t in[8][4];
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int r = (tid >> 3) + pass * 32;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (r0 + r < rows && c0 + cc < cols)
-      v = *reinterpret_cast<const uint4*>(s + static_cast<int64_t>(r0 + r) * cols + c0 + cc);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tile[r][cc + 2 * i] = static_cast<uint16_t>(w[i] & 0xffffu);
-      tile[r][cc + 2 * i + 1] = static_cast<uint16_t>(w[i] >> 16);
-    }
+  for (int i = 0; i < 8; ++i) {
+    const uint4 v = *reinterpret_cast<const uint4*>(s + static_cast<int64_t>(r + i) * cols + c);
+    in[i][0] = v.x; in[i][1] = v.y; in[i][2] = v.z; in[i][3] = v.w;
   }
-  __syncthreads();
-  const int rr = (tid & 7) * 8;
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int c = (tid >> 3) + pass * 32;
-    if (c0 + c < cols && r0 + rr < rows) {
-      uint32_t w[4];
+  for (int jc = 0; jc < 8; ++jc) {
+    uint32_t w[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[i] = static_cast<uint32_t>(tile[rr + 2 * i][c]) |
-               (static_cast<uint32_t>(tile[rr + 2 * i + 1][c]) << 16);
-      *reinterpret_cast<uint4*>(o + static_cast<int64_t>(c0 + c) * ldd + coff + r0 + rr) =
-          make_uint4(w[0], w[1], w[2], w[3]);
-    }
+    for (int q = 0; q < 4; ++q) w[q] = pick16(in[2 * q][jc >> 1], in[2 * q + 1][jc >> 1], jc & 1);
+    *reinterpret_cast<uint4*>(o + static_cast<int64_t>(c + jc) * ldd + coff + r) =
+        make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -171,7 +166,7 @@ hipError_t launch_transpose_bf16(const void* src, int rows, int cols, int64_t sr
                                  int batch, void* dst, int ldd, int coff, int64_t dst_batch,
                                  hipStream_t st) {
   if (rows <= 0 || cols <= 0 || batch <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(cdiv(cols, TT)), static_cast<unsigned>(cdiv(rows, TT)),
+  const dim3 grid(static_cast<unsigned>(cdiv(cols, 64)), static_cast<unsigned>(cdiv(rows, 256)),
                   static_cast<unsigned>(batch));
   hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, st,
                      static_cast<const bf16_t*>(src), rows, cols, src_batch,

@@ -16,7 +16,9 @@ template <>
 struct Vec<bf16_t> {
   static constexpr int N = 8;
   __device__ __forceinline__ static void load(const bf16_t* p, float* v) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    unpack(*reinterpret_cast<const uint4*>(p), v);
+  }
+  __device__ __forceinline__ static void unpack(const uint4 u, float* v) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -40,10 +42,19 @@ struct Vec<float> {
     const float4 u = *reinterpret_cast<const float4*>(p);
     v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
   }
+  __device__ __forceinline__ static void unpack(const uint4 u, float* v) {
+    v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+    v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+  }
   __device__ __forceinline__ static void store(float* p, const float* v) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   }
 };
+
+// Per lane and pass: U chunks 64 VN elements apart; slots are taken JB at a time with every load
+// of a group issued (as raw 16-byte values) before any is used, so a wave keeps JB U loads in
+// flight at a modest register count.
+constexpr int kU = 4, kJB = 2;
 
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(int64_t Tn, int d, int k,
@@ -52,37 +63,60 @@ __global__ __launch_bounds__(256) void combine_kernel(int64_t Tn, int d, int k,
                                                        const float* __restrict__ topk_w,
                                                        const T* __restrict__ shared_out,
                                                        T* __restrict__ y) {
-  constexpr int VN = Vec<T>::N;
+  constexpr int VN = Vec<T>::N, STEP = 64 * VN;
   const int lane = threadIdx.x & 63;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
-  int rows[MOE_K_MAX];
-  float w[MOE_K_MAX];
+  // lane j holds slot j's row and gate; a slot's values are read out wave-uniformly
+  const int my_row = lane < k ? inv_perm[t * k + lane] : -1;
+  const int my_w = lane < k ? __float_as_int(topk_w[t * k + lane]) : 0;
+  for (int c0 = lane * VN; c0 < d; c0 += STEP * kU) {
+    float acc[kU][VN];
 #pragma unroll
-  for (int j = 0; j < MOE_K_MAX; ++j) {
-    rows[j] = j < k ? inv_perm[t * k + j] : -1;
-    w[j] = j < k ? topk_w[t * k + j] : 0.f;
-  }
-  for (int c = lane * VN; c < d; c += 64 * VN) {
-    float acc[VN];
+    for (int u = 0; u < kU; ++u)
 #pragma unroll
-    for (int i = 0; i < VN; ++i) acc[i] = 0.f;
+      for (int i = 0; i < VN; ++i) acc[u][i] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += kJB) {
+      uint4 raw[kJB][kU];
+      float wj[kJB];
 #pragma unroll
-    for (int j = 0; j < MOE_K_MAX; ++j) {
-      if (rows[j] >= 0) {
-        float v[VN];
-        Vec<T>::load(out_perm + static_cast<int64_t>(rows[j]) * d + c, v);
+      for (int jj = 0; jj < kJB; ++jj) {
+        const int j = j0 + jj;
+        const int row = j < k ? __builtin_amdgcn_readlane(my_row, j) : -1;
+        wj[jj] = row >= 0 ? __int_as_float(__builtin_amdgcn_readlane(my_w, j)) : 0.f;
 #pragma unroll
-        for (int i = 0; i < VN; ++i) acc[i] = fmaf(w[j], v[i], acc[i]);
+        for (int u = 0; u < kU; ++u) {
+          const int c = c0 + u * STEP;
+          raw[jj][u] = (row >= 0 && c < d)
+                           ? *reinterpret_cast<const uint4*>(out_perm +
+                                                             static_cast<int64_t>(row) * d + c)
+                           : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+      // slot order j = 0..k-1 (a dropped slot adds 0 * 0)
+#pragma unroll
+      for (int jj = 0; jj < kJB; ++jj)
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          float v[VN];
+          Vec<T>::unpack(raw[jj][u], v);
+#pragma unroll
+          for (int i = 0; i < VN; ++i) acc[u][i] = fmaf(wj[jj], v[i], acc[u][i]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = c0 + u * STEP;
+      if (c < d) {
+        if (shared_out != nullptr) {
+          float sv[VN];
+          Vec<T>::load(shared_out + t * d + c, sv);
+#pragma unroll
+          for (int i = 0; i < VN; ++i) acc[u][i] += sv[i];
+        }
+        Vec<T>::store(y + t * d + c, acc[u]);
       }
     }
-    if (shared_out != nullptr) {
-      float v[VN];
-      Vec<T>::load(shared_out + t * d + c, v);
-#pragma unroll
-      for (int i = 0; i < VN; ++i) acc[i] += v[i];
-    }
-    Vec<T>::store(y + t * d + c, acc);
   }
 }
 
