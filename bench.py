@@ -46,10 +46,11 @@ def parse():
 
 
 def gemm_source_sha() -> str:
+    """Hash of the grouped-GEMM kernel source the traffic counters were taken on."""
     h = hashlib.sha256()
-    for f in ("gemm_bf16.hip", "moe_internal.h"):
-        with open(os.path.join(ROOT, "mixture_experts_layer_loss_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    with open(os.path.join(ROOT, "mixture_experts_layer_loss_amd", "csrc", "gemm_bf16.hip"),
+              "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 

@@ -90,6 +90,22 @@ __device__ __forceinline__ void sched_substep() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Schedule of a sub-step with both LDS stores and global loads spread over its MFMAs.
+template <int NMF, int NR, int NW, int NL>
+__device__ __forceinline__ void sched_substep_wl() {
+  constexpr int RPER = (NR + NMF - 1) / NMF;
+  constexpr int WPER = (NW + NMF - 1) / NMF;
+  constexpr int LPER = (NL + NMF - 1) / NMF;
+#pragma unroll
+  for (int q = 0; q < NMF; ++q) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    if (q * RPER < NR) __builtin_amdgcn_sched_group_barrier(kSgDsRead, RPER, 0);
+    if (q * WPER < NW) __builtin_amdgcn_sched_group_barrier(kSgDsWrite, WPER, 0);
+    if (q * LPER < NL) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, LPER, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // One MR x 256 output tile of group g: rows [row_begin, row_begin + rows_here), output columns
 // [n0, n0 + BNO). EPI 0: SwiGLU (B0 = W_gate, B1 = W_up); EPI 1: plain (B0 = W_down); EPI 2:
 // plain with fp32 output (C is then float), stored straight from the accumulators; EPI 3: the
@@ -228,23 +244,22 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
     const int cur = kt & 1;
     lfrag(1, cur, 1);
     mfmas(0);
-    sched_substep<NMF, NR, 0, 0>();
-    lfrag(0, cur, 2);
-    mfmas(1);
-    if constexpr (NEXT) {
+    if constexpr (NEXT && LOAD) {
+      lstore(cur ^ 1);
+      gload((kt + 2) * BK);
+      sched_substep_wl<NMF, NR, NX, NX>();
+    } else if constexpr (NEXT) {
       lstore(cur ^ 1);
       sched_substep<NMF, NR, kSgDsWrite, NX>();
     } else {
       sched_substep<NMF, NR, 0, 0>();
     }
+    lfrag(0, cur, 2);
+    mfmas(1);
+    sched_substep<NMF, NR, 0, 0>();
     lfrag(1, cur, 3);
     mfmas(0);
-    if constexpr (LOAD) {
-      gload((kt + 2) * BK);
-      sched_substep<NMF, NR, kSgVmemRead, NX>();
-    } else {
-      sched_substep<NMF, NR, 0, 0>();
-    }
+    sched_substep<NMF, NR, 0, 0>();
     __syncthreads();
     if constexpr (NEXT) {
       lfrag(0, cur ^ 1, 0);

@@ -279,6 +279,12 @@ LAYER_BW_CASES = [
     ("deepseek_v2", dict(T=150, d=200, M=72, scoring="sigmoid")),  # bias, sigmoid, K tail
     ("mixtral_8x7b", dict(T=100, d=64, M=64, E=6, k=3, renorm=False)),
     ("mixtral_8x7b", dict(T=1024, d=512, M=768)),                 # several 256 x 256 tiles
+    ("mixtral_8x7b", dict(T=8, d=64, M=64, E=16, k=1)),           # experts without rows
+    ("mixtral_8x7b", dict(T=70, d=64, M=64, E=1, k=1)),           # one expert: a dense FFN
+    ("mixtral_8x7b", dict(T=50, d=64, M=64, E=4, k=4)),           # k = E
+    ("mixtral_8x7b", dict(T=90, d=64, M=64, E=4, k=2, c=0.01)),   # C = 1: nearly all dropped
+    ("tiny_fp32", dict(T=70, E=1, k=1)),
+    ("tiny_fp32", dict(T=90, E=4, k=2, c=0.01)),
 ]
 
 
@@ -294,11 +300,13 @@ def test_layer_backward(gpu, base, kw):
     bf16 layers run the dx-row and weight-gradient products on bf16 MFMA. Each term of those
     sums has exactly one factor rounded to bf16 once (dG, dU, or w h; the other factor, dy, x or
     a weight, is an exact bf16 input), so every element obeys |gpu - ref| <= (u + eps + K 2^-24)
-    |terms|, u = 2^-8 the bf16 unit roundoff, eps = 1e-5 for the fp32 error of the value before
-    rounding, K 2^-24 for fp32 accumulation over the K terms, and |terms| the sum of the terms'
-    magnitudes (the oracle's `magnitude`). Rounding errors of random sign make the normwise error
-    far smaller than that worst case: ||gpu - ref|| / ||ref|| <= u for every output. dW_r has no
-    rounded factor: max relative error 1e-4."""
+    |terms| + 2^-20 max|terms|, u = 2^-8 the bf16 unit roundoff, eps = 1e-5 for the fp32 error of
+    the value before rounding, K 2^-24 for fp32 accumulation over the K terms, |terms| the sum of
+    the terms' magnitudes (the oracle's `magnitude`), and the absolute floor for a rounded factor
+    that cancels to almost nothing in fp32 (a pre-activation near 0 carries an fp32 error of
+    ~K 2^-24 of its own terms, which is no longer small relative to the factor). Rounding errors
+    of random sign make the normwise error far smaller than that worst case: ||gpu - ref|| / ||ref||
+    <= u for every output. dW_r has no rounded factor: max relative error 1e-4."""
     cfg = cfg_of(base, **kw)
     say(f"[layer backward] {cfg}")
     inp = workloads.make_inputs(cfg)
@@ -343,10 +351,11 @@ def test_layer_backward(gpu, base, kw):
         if key == "dW_r":
             continue
         a = a.detach().cpu().double().numpy() if torch.is_tensor(a) else a
-        bound = (u + 1e-5 + K * 2.0 ** -24) * mags[key]
+        bound = (u + 1e-5 + K * 2.0 ** -24) * mags[key] + 2.0 ** -20 * mags[key].max()
         err = np.abs(a - r)
         ratio[key] = float((err / np.maximum(bound, 1e-300)).max())
-        normwise[key] = float(np.linalg.norm(err) / np.linalg.norm(r))
+        rn = np.linalg.norm(r)
+        normwise[key] = float(np.linalg.norm(err) / rn) if rn > 0 else float(np.linalg.norm(err))
         assert (err <= bound).all(), (key, ratio[key])
         assert normwise[key] <= u, (key, normwise[key])
     say(f"    max err / bound {ratio}")
@@ -611,7 +620,7 @@ def test_full_size_backward_sampled(gpu, name):
         r = np.asarray(ref[key], dtype=np.float64)
         mag = np.asarray(ref["magnitude"][key], dtype=np.float64)
         err = np.abs(a - r)
-        bound = (u + 1e-5 + K * 2.0 ** -24) * mag
+        bound = (u + 1e-5 + K * 2.0 ** -24) * mag + 2.0 ** -20 * mag.max()
         ratio[key] = float((err / np.maximum(bound, 1e-300)).max())
         normwise[key] = float(np.linalg.norm(err) / np.linalg.norm(r))
         assert (err <= bound).all(), (key, ratio[key])
