@@ -232,12 +232,14 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
   constexpr int NMF = MI * NJ, NR = MI + NJ, NX = ACH + BCH;
 
   // ---- one k-step (64 of K) = 4 sub-steps on stage `cur`:
-  //   sub 0: read fragments of sub 1                    | MFMAs of sub 0
-  //   sub 1: read fragments of sub 2, store stage cur^1 | MFMAs of sub 1
-  //   sub 2: read fragments of sub 3, load k-step +2    | MFMAs of sub 2
+  //   sub 0: read fragments of sub 1, store stage cur^1 (no wave reads it since the last
+  //          barrier), then load k-step +2 into the freed registers | MFMAs of sub 0
+  //   sub 1: read fragments of sub 2                                | MFMAs of sub 1
+  //   sub 2: read fragments of sub 3                                | MFMAs of sub 2
   //   barrier (stage cur^1 complete; every read of stage cur issued)
-  //   sub 3: read fragments of sub 0 of stage cur^1     | MFMAs of sub 3
-  // Global loads run ~1.5 k-steps ahead; no LDS read waits on a barrier.
+  //   sub 3: read fragments of sub 0 of stage cur^1                 | MFMAs of sub 3
+  // A global load has four sub-steps to land before its LDS store; no LDS read waits on a
+  // barrier.
   auto kstep = [&](int kt, auto has_next, auto has_load) __attribute__((always_inline)) {
     constexpr bool NEXT = decltype(has_next)::value;  // a following k-step exists
     constexpr bool LOAD = decltype(has_load)::value;  // k-step kt + 2 exists

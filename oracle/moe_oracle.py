@@ -434,6 +434,102 @@ def layer_backward(x, W_r, W_gate, W_up, W_down, dy, k: int, b=None, shared=(), 
     return out
 
 
+def layer_backward_expert_choice(x, W_r, W_gate, W_up, W_down, dy, k: int, shared=(), c=None,
+                                 renorm: bool = True, lam: float = 0.01, z_coef: float = 0.0,
+                                 scoring: str = "softmax", chosen=None, magnitudes: bool = False):
+    """Gradients of <dy, y> + aux + z_coef z for the expert-choice layer of
+    layer_forward_expert_choice, with the selection (each expert's r tokens) held fixed. The chain
+    is that of layer_backward with the set of experts that took token t, E_t, in place of the top-k
+    slots:
+      d w_te = <dy_t, E_e(x_t)> for e in E_t;  renorm: dg_te = (d w_te - sum_{E_t} w dw) / sum_{E_t} g,
+      else dg_te = d w_te;  then the softmax / sigmoid chain to the logits, plus the balance-loss
+      gradient with f_e = n_e / sum n = 1/E held fixed; per expert row: d out = w_te dy_t, etc.
+    ``chosen`` (optional, [E, r]) replaces the oracle's own selection. Returns float64 arrays (and
+    "magnitude" as in layer_backward)."""
+    x64 = _f64(x)
+    dy64 = _f64(dy)
+    T, d = x64.shape
+    r_ = route(x64, W_r, 1, None, renorm, scoring)
+    l, g = r_["logits"], r_["g"]
+    E = g.shape[1]
+    r = expert_choice_capacity(c, k, T, E)
+    chosen = expert_choice(l, r) if chosen is None else np.asarray(chosen, dtype=np.int64)
+    member = np.zeros((T, E), dtype=bool)
+    for e in range(E):
+        member[chosen[e], e] = True
+    gm = np.where(member, g, 0.0)
+    den = gm.sum(axis=1)
+    if renorm:
+        w = np.divide(gm, den[:, None], out=np.zeros_like(gm), where=den[:, None] > 0)
+    else:
+        w = gm
+    out = {"dx": np.zeros((T, d)), "dW_gate": np.zeros_like(_f64(W_gate)),
+           "dW_up": np.zeros_like(_f64(W_up)), "dW_down": np.zeros_like(_f64(W_down))}
+    mag = {key: np.zeros_like(val) for key, val in out.items()}
+    dw = np.zeros((T, E))
+    for e in range(E):
+        toks = chosen[e]
+        if len(toks) == 0:
+            continue
+        Wg, Wu, Wd = _f64(W_gate[e]), _f64(W_up[e]), _f64(W_down[e])
+        X = x64[toks]
+        G, U = X @ Wg.T, X @ Wu.T
+        h = silu(G) * U
+        O = h @ Wd.T
+        wt = w[toks, e]
+        dO = wt[:, None] * dy64[toks]
+        dw[toks, e] = (dy64[toks] * O).sum(axis=1)
+        dh = dO @ Wd
+        dG, dU = dh * U * silu_grad(G), dh * silu(G)
+        out["dW_down"][e] = dO.T @ h
+        out["dW_gate"][e] = dG.T @ X
+        out["dW_up"][e] = dU.T @ X
+        out["dx"][toks] += dG @ Wg + dU @ Wu
+        if magnitudes:
+            mag["dW_down"][e] = np.abs(dO).T @ np.abs(h)
+            mag["dW_gate"][e] = np.abs(dG).T @ np.abs(X)
+            mag["dW_up"][e] = np.abs(dU).T @ np.abs(X)
+            mag["dx"][toks] += np.abs(dG) @ np.abs(Wg) + np.abs(dU) @ np.abs(Wu)
+    # router: gates over E_t -> scores -> logits
+    if renorm:
+        dg = np.where(member, (dw - (w * dw).sum(axis=1, keepdims=True)), 0.0)
+        dg = np.divide(dg, den[:, None], out=np.zeros_like(dg), where=den[:, None] > 0)
+    else:
+        dg = np.where(member, dw, 0.0)
+    if scoring == "softmax":
+        dl = g * (dg - (g * dg).sum(axis=1, keepdims=True))
+    else:
+        dl = g * (1.0 - g) * dg
+    n = np.full(E, r, dtype=np.int64)
+    dl = dl + balance_loss_grad_logits(l, n / float(n.sum()), lam, z_coef, scoring)
+    W64 = _f64(W_r)
+    out["dW_r"] = dl.T @ x64
+    out["dx"] += dl @ W64
+    out["dlogits"] = dl
+    if magnitudes:
+        mag["dW_r"] = np.abs(dl).T @ np.abs(x64)
+        mag["dx"] += np.abs(dl) @ np.abs(W64)
+    sh_grads, sh_mag = [], []
+    for Wg, Wu, Wd in shared:
+        Wg, Wu, Wd = _f64(Wg), _f64(Wu), _f64(Wd)
+        G, U = x64 @ Wg.T, x64 @ Wu.T
+        h = silu(G) * U
+        dh = dy64 @ Wd
+        dG, dU = dh * U * silu_grad(G), dh * silu(G)
+        out["dx"] += dG @ Wg + dU @ Wu
+        sh_grads.append((dG.T @ x64, dU.T @ x64, dy64.T @ h))
+        if magnitudes:
+            mag["dx"] += np.abs(dG) @ np.abs(Wg) + np.abs(dU) @ np.abs(Wu)
+            ax = np.abs(x64)
+            sh_mag.append((np.abs(dG).T @ ax, np.abs(dU).T @ ax, np.abs(dy64).T @ np.abs(h)))
+    out["shared"] = sh_grads
+    out["chosen"] = chosen
+    if magnitudes:
+        mag["shared"] = sh_mag
+        out["magnitude"] = mag
+    return out
+
+
 def layer_backward_sampled(x, W_r, W_gate, W_up, W_down, dy, k: int, b=None, shared=(), c=None,
                            renorm: bool = True, lam: float = 0.01, z_coef: float = 0.0,
                            scoring: str = "softmax", topk_idx=None, tokens=(), expert_cols=(),

@@ -465,6 +465,75 @@ def test_layer_backward_pins():
     check_layer_backward()
 
 
+def _torch_layer_loss_ec(x, Wr, Wg, Wu, Wd, dy, member, f, renorm, lam, zc, scoring, shared):
+    # the expert-choice layer written densely: every expert on every token, masked by the fixed
+    # membership; gates renormalised over the experts that took the token
+    l = x @ Wr.T
+    if scoring == "softmax":
+        g = torch.softmax(l, dim=1)
+        p = g
+    else:
+        g = torch.sigmoid(l)
+        p = g / g.sum(dim=1, keepdim=True)
+    gm = g * member
+    if renorm:
+        den = gm.sum(dim=1, keepdim=True)
+        w = torch.where(den > 0, gm / torch.where(den > 0, den, torch.ones_like(den)), gm)
+    else:
+        w = gm
+    y = torch.zeros_like(x)
+    for e in range(g.shape[1]):
+        h = torch.nn.functional.silu(x @ Wg[e].T) * (x @ Wu[e].T)
+        y = y + w[:, e:e + 1] * (h @ Wd[e].T)
+    for sg, su, sd in shared:
+        y = y + (torch.nn.functional.silu(x @ sg.T) * (x @ su.T)) @ sd.T
+    aux = lam * g.shape[1] * (f * p.mean(dim=0)).sum()
+    z = (torch.logsumexp(l, dim=1) ** 2).mean()
+    return (dy * y).sum() + aux + zc * z
+
+
+def check_layer_backward_ec(mod=O):
+    T, d, E, k, M = 13, 6, 4, 1, 5
+    rng = np.random.default_rng(61)
+    x = rng.standard_normal((T, d))
+    Wr = rng.standard_normal((E, d)) * 0.5
+    Wg = rng.standard_normal((E, M, d)) * 0.4
+    Wu = rng.standard_normal((E, M, d)) * 0.4
+    Wd = rng.standard_normal((E, d, M)) * 0.4
+    dy = rng.standard_normal((T, d))
+    sh = [tuple(rng.standard_normal(sz) * 0.4 for sz in ((M, d), (M, d), (d, M)))]
+    for scoring, renorm, c, shared in (("softmax", True, None, ()), ("sigmoid", False, 1.5, sh),
+                                       ("softmax", True, 0.6, sh)):
+        ref = mod.layer_backward_expert_choice(x, Wr, Wg, Wu, Wd, dy, k, shared=shared, c=c,
+                                               renorm=renorm, lam=0.3, z_coef=0.7, scoring=scoring)
+        fw = O.layer_forward_expert_choice(x, Wr, Wg, Wu, Wd, k, c=c, renorm=renorm,
+                                           scoring=scoring)
+        member = np.zeros((T, E))
+        for e in range(E):
+            member[fw["chosen"][e], e] = 1.0
+        assert (member.sum(axis=1) == 0).any() or c is None or c > 1  # some token uncovered
+        ts = [torch.tensor(a, requires_grad=True) for a in (x, Wr, Wg, Wu, Wd)]
+        tsh = [tuple(torch.tensor(a, requires_grad=True) for a in s_) for s_ in shared]
+        L = _torch_layer_loss_ec(*ts, torch.tensor(dy), torch.tensor(member),
+                                 torch.tensor(fw["f"]), renorm, 0.3, 0.7, scoring, tsh)
+        L.backward()
+        for name, t_ in zip(("dx", "dW_r", "dW_gate", "dW_up", "dW_down"), ts):
+            assert np.allclose(ref[name], t_.grad.numpy(), rtol=1e-10, atol=1e-12), (scoring, name)
+        for (a, b_, c_), (tg, tu, td) in zip(ref["shared"], tsh):
+            assert np.allclose(a, tg.grad.numpy(), rtol=1e-10, atol=1e-12)
+            assert np.allclose(b_, tu.grad.numpy(), rtol=1e-10, atol=1e-12)
+            assert np.allclose(c_, td.grad.numpy(), rtol=1e-10, atol=1e-12)
+        mref = mod.layer_backward_expert_choice(x, Wr, Wg, Wu, Wd, dy, k, shared=shared, c=c,
+                                                renorm=renorm, lam=0.3, z_coef=0.7,
+                                                scoring=scoring, magnitudes=True)["magnitude"]
+        for key in ("dx", "dW_r", "dW_gate", "dW_up", "dW_down"):
+            assert (mref[key] >= np.abs(ref[key]) * (1 - 1e-12)).all(), key
+
+
+def test_layer_backward_expert_choice_pins():
+    check_layer_backward_ec()
+
+
 def test_layer_backward_sampled_matches_whole():
     # the per-entry evaluation agrees with the whole backward on every token and every column,
     # with capacity drops, shared experts, sigmoid scores and a bias
@@ -731,7 +800,8 @@ class _Mutant:
         # layer_forward looks its helpers up in the module, so rebind it to this namespace
         import types
         for name in ("layer_forward", "route", "layer_backward", "balance_loss_backward",
-                     "layer_forward_expert_choice", "diagnostics"):
+                     "layer_forward_expert_choice", "diagnostics", "layer_backward_expert_choice",
+                     "layer_backward_sampled"):
             fn = getattr(O, name)
             self.__dict__[name] = types.FunctionType(fn.__code__, self.__dict__, name, fn.__defaults__)
 
@@ -844,6 +914,9 @@ def _sigmoid_unnormalised_P(g, scoring="softmax"):
     (dict(expert_choice=_ec_smallest), [check_expert_choice]),
     (dict(balance_loss_grad_logits=_grad_no_centering), [check_loss_backward]),
     (dict(silu_grad=_silu_grad_wrong), [check_layer_backward]),
+    (dict(silu_grad=_silu_grad_wrong), [check_layer_backward_ec]),
+    (dict(expert_choice_capacity=lambda c, k, T, E: O.expert_choice_capacity(c, k, T, E) + 1),
+     [check_layer_backward_ec]),
 ])
 def test_planted_mistakes_are_caught(mutant, checks):
     m = _Mutant(**mutant)
