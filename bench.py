@@ -184,17 +184,17 @@ def main():
     # the full layer backward (token choice): gradients of <dy, y> + aux + z for x, W_r and every
     # expert weight, forward recompute included (a separate entry point; not part of a step)
     bw_ms = None
-    if cfg.routing == "token" and not args.no_backward:
+    if not args.no_backward:
         print("[bench] layer backward", file=sys.stderr, flush=True)
         dy = torch.randn(cfg.T, cfg.d, generator=torch.Generator().manual_seed(11)).to(dt).to(dev)
         bw_ws = moe.workspace(moe.make_shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.M, cfg.S, cfg.c,
-                                             cfg.renorm, dt, cfg.scoring),
+                                             cfg.renorm, dt, cfg.scoring, cfg.routing),
                               moe.CALL_LAYER_BACKWARD, dev)
         shared_w = sh
         def bw():
             return moe.moe_layer_backward(x, W_r, Wg, Wu, Wd, dy, cfg.k, b=b, shared=shared_w,
                                           c=cfg.c, renorm=cfg.renorm, lam=cfg.lam, z_coef=1.0,
-                                          scoring=cfg.scoring, ws=bw_ws)
+                                          scoring=cfg.scoring, routing=cfg.routing, ws=bw_ws)
         g = bw()
         torch.cuda.synchronize()
         del g

@@ -257,9 +257,9 @@ moe_status moe_balance_loss_backward(const moe_shape* s, const void* x, const vo
                                      size_t ws_bytes, void* stream);
 
 /*
- * moe_layer_backward -- gradients of <dy, y> + aux + z_coef z for the token-choice layer, with
- * the selection, the capacity cut and f held fixed (they are discrete). Recomputes the forward
- * (the same routing, placement and expert outputs as moe_layer_forward), then:
+ * moe_layer_backward -- gradients of <dy, y> + aux + z_coef z for the layer, with the
+ * selection, the capacity cut and f held fixed (they are discrete). Recomputes the forward (the
+ * same routing and placement as moe_layer_forward, the pre-activations in fp32), then:
  *   d out[row(t,j)] = w_tj dy_t, d w_tj = <dy_t, out[row(t,j)]>; gates through the
  *   renormalisation ("MoE：条件计算与路由" §7 eq. (2)) and the softmax or sigmoid to the logits,
  *   plus the balance-loss gradient of moe_balance_loss_backward; dW_r = dl^T x;
@@ -267,13 +267,17 @@ moe_status moe_balance_loss_backward(const moe_shape* s, const void* x, const vo
  *   dG = dh U SiLU'(G), dU = dh SiLU(G); dW_down[e] = sum d out^T h, dW_gate[e] = sum dG^T x,
  *   dW_up[e] = sum dU^T x; dx_t = (dl W_r)_t + sum_j (dG W_gate + dU W_up)_row(t,j) + shared;
  *   the shared experts take dy_t with weight 1.
- * The recomputed h and out are rounded to dtype as in the forward; gradients are fp32.
+ * Expert choice: the slots of token t are the experts that took it (ascending), gates
+ * renormalised over them; b must be NULL (as in the forward).
+ * The gradient is that of the real-valued chain (h formed in fp32 from fp32 pre-activations);
+ * bf16 layers run the dx-row and weight-gradient products on bf16 MFMA with one factor of every
+ * term rounded to bf16 once (dG, dU or w h); gradients are fp32.
  *   x, W_r, b, W_gate, W_up, W_down, Ws_*: as moe_layer_forward; dy device [T, d] (dtype)
  *   dx [T, d], dW_r [E, d], dW_gate, dW_up [E, M, d], dW_down [E, d, M] fp32 device out;
  *   dWs_gate, dWs_up [S*M, d], dWs_down [d, S*M] fp32 device out (required when S > 0)
- *   topk_idx device out [T, k] int32 or NULL: the selection the gradients were taken at
+ *   topk_idx device out [T, k] int32 or NULL: the token-choice selection the gradients were
+ *     taken at (not written under expert choice)
  *   ws device workspace of moe_workspace_size(s, MOE_CALL_LAYER_BACKWARD) bytes
- * Token choice only (expert choice: MOE_ERR_UNSUPPORTED).
  */
 moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r, const float* b,
                               const void* W_gate, const void* W_up, const void* W_down,

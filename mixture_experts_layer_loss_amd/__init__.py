@@ -313,14 +313,15 @@ def moe_balance_loss_backward(x: torch.Tensor, W_r: torch.Tensor, n: torch.Tenso
 
 def moe_layer_backward(x, W_r, W_gate, W_up, W_down, dy, k: int, b=None, shared=None,
                        c: Optional[float] = None, renorm: bool = True, lam: float = 0.01,
-                       z_coef: float = 0.0, scoring: str = "softmax",
+                       z_coef: float = 0.0, scoring: str = "softmax", routing: str = "token",
                        ws: Optional[torch.Tensor] = None) -> dict:
-    """Gradients (fp32) of <dy, y> + aux + z_coef z for the token-choice layer; ``shared`` is the
-    stacked (Ws_gate, Ws_up, Ws_down) when the layer has shared experts."""
+    """Gradients (fp32) of <dy, y> + aux + z_coef z for the layer; ``shared`` is the stacked
+    (Ws_gate, Ws_up, Ws_down) when the layer has shared experts. ``topk_idx`` is the recomputed
+    token-choice selection (left unwritten under expert choice)."""
     T, d = x.shape
     E, M, _ = W_gate.shape
     S = 0 if shared is None else shared[0].shape[0] // M
-    s = make_shape(T, d, E, k, M, S, c, renorm, x.dtype, scoring)
+    s = make_shape(T, d, E, k, M, S, c, renorm, x.dtype, scoring, routing)
     _check(check_shape(s), "moe_layer_backward")
     dt = x.dtype
     for name, t, shp in (("x", x, (T, d)), ("W_r", W_r, (E, d)), ("W_gate", W_gate, (E, M, d)),

@@ -43,6 +43,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 // and the SwiGLU derivative dG = dh U SiLU'(G), dU = dh SiLU(G) with SiLU'(z) = s (1 + z (1 - s)),
 // s = sigma(z). CAT: one bf16 row [dG | dU] of 2M (M a multiple of 4; lanes take 4 columns at a
 // time); else fp32 rows dG, dU. When not NULL: d out_row = w dy_t, wrow[row] = w.
+// Expert choice (inv_perm == NULL): the row's gate is read from wrow and d w is written per row,
+// dw[row].
 template <typename T, bool CAT>
 __global__ __launch_bounds__(256) void bw_rows_kernel(
     const int32_t* __restrict__ offsets, int E, int d, int M, int k,
@@ -55,10 +57,12 @@ __global__ __launch_bounds__(256) void bw_rows_kernel(
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= offsets[E]) return;
   const int64_t t = perm_token[row];
+  const bool ec = inv_perm == nullptr;
   int slot = 0;
-  for (int j = 0; j < k; ++j)
-    if (inv_perm[t * k + j] == row) slot = j;
-  const float w = topk_w[t * k + slot];
+  if (!ec)
+    for (int j = 0; j < k; ++j)
+      if (inv_perm[t * k + j] == row) slot = j;
+  const float w = ec ? wrow[row] : topk_w[t * k + slot];
   float dot = 0.f;
   auto one = [&](float p, float z, float u, float& vg, float& vu) __attribute__((always_inline)) {
     const float sg = 1.f / (1.f + expf(-z));
@@ -101,8 +105,12 @@ __global__ __launch_bounds__(256) void bw_rows_kernel(
     for (int i = lane; i < d; i += 64) dout[row * d + i] = w * ld<T>(dy, t * d + i);
   dot = wave_sum(dot);
   if (lane == 0) {
-    dw[t * k + slot] = dot;
-    if (wrow != nullptr) wrow[row] = w;
+    if (ec) {
+      dw[row] = dot;
+    } else {
+      dw[t * k + slot] = dot;
+      if (wrow != nullptr) wrow[row] = w;
+    }
   }
 }
 
@@ -118,26 +126,16 @@ __global__ __launch_bounds__(256) void swiglu_fwd_kernel(int64_t count, const fl
 
 constexpr int kEPL = MOE_E_MAX / 64;
 
-// router: gates -> scores -> logits, plus the balance-loss gradient; one wave per token
-__global__ __launch_bounds__(256) void bw_router_kernel(
-    int64_t T, int E, int k, int renorm, int sigmoid, const float* __restrict__ lcol,
-    const float* __restrict__ scol, const int32_t* __restrict__ topk_idx,
-    const int32_t* __restrict__ inv_perm, const float* __restrict__ topk_w,
-    const float* __restrict__ dw, const int32_t* __restrict__ n,
-    double fden, float lambda, float z_coef, float* __restrict__ dl, float* __restrict__ dlT) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  // dg over the chosen experts (wave-uniform, slot order)
-  // d w of a dropped slot is 0 (it adds nothing to y)
-  float gsel = 0.f, wdw = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int e = topk_idx[t * k + j];
-    const float dwj = inv_perm[t * k + j] >= 0 ? dw[t * k + j] : 0.f;
-    gsel += scol[static_cast<int64_t>(e) * T + t];
-    wdw += topk_w[t * k + j] * dwj;
-  }
-  float l[kEPL], s[kEPL], a[kEPL], dg[kEPL];
+// Router tail shared by both routings, one wave per token t: from dg (the gradient at the chosen
+// experts' gates, lane-strided like the columns), the logits and scores: dl = the softmax or sigmoid
+// chain plus the balance-loss gradient, written to dl [T][E] and dlT [E][T].
+__device__ __forceinline__ void router_tail(int64_t T, int E, int sigmoid, int64_t t, int lane,
+                                            const float* __restrict__ lcol,
+                                            const float* __restrict__ scol,
+                                            const int32_t* __restrict__ n, double fden,
+                                            float lambda, float z_coef, const float* dg,
+                                            float* __restrict__ dl, float* __restrict__ dlT) {
+  float l[kEPL], s[kEPL], a[kEPL];
   float m = -INFINITY;
 #pragma unroll
   for (int q = 0; q < kEPL; ++q) {
@@ -148,16 +146,7 @@ __global__ __launch_bounds__(256) void bw_router_kernel(
     a[q] = in ? static_cast<float>(static_cast<double>(lambda) * E *
                                    (static_cast<double>(n[e]) / fden) / static_cast<double>(T))
               : 0.f;
-    dg[q] = 0.f;
     m = fmaxf(m, l[q]);
-  }
-  for (int j = 0; j < k; ++j) {
-    const int e = topk_idx[t * k + j];
-    const float dwj = inv_perm[t * k + j] >= 0 ? dw[t * k + j] : 0.f;
-    const float v = renorm ? (dwj - wdw) / gsel : dwj;
-#pragma unroll
-    for (int q = 0; q < kEPL; ++q)
-      if (e == lane + 64 * q) dg[q] = v;
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
@@ -185,6 +174,91 @@ __global__ __launch_bounds__(256) void bw_router_kernel(
       dl[t * E + e] = v;
       dlT[static_cast<int64_t>(e) * T + t] = v;
     }
+  }
+}
+
+// router (token choice): gates -> scores -> logits, plus the balance-loss gradient; one wave per
+// token
+__global__ __launch_bounds__(256) void bw_router_kernel(
+    int64_t T, int E, int k, int renorm, int sigmoid, const float* __restrict__ lcol,
+    const float* __restrict__ scol, const int32_t* __restrict__ topk_idx,
+    const int32_t* __restrict__ inv_perm, const float* __restrict__ topk_w,
+    const float* __restrict__ dw, const int32_t* __restrict__ n,
+    double fden, float lambda, float z_coef, float* __restrict__ dl, float* __restrict__ dlT) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  // dg over the chosen experts (wave-uniform, slot order)
+  // d w of a dropped slot is 0 (it adds nothing to y)
+  float gsel = 0.f, wdw = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int e = topk_idx[t * k + j];
+    const float dwj = inv_perm[t * k + j] >= 0 ? dw[t * k + j] : 0.f;
+    gsel += scol[static_cast<int64_t>(e) * T + t];
+    wdw += topk_w[t * k + j] * dwj;
+  }
+  float dg[kEPL];
+#pragma unroll
+  for (int q = 0; q < kEPL; ++q) dg[q] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int e = topk_idx[t * k + j];
+    const float dwj = inv_perm[t * k + j] >= 0 ? dw[t * k + j] : 0.f;
+    const float v = renorm ? (dwj - wdw) / gsel : dwj;
+#pragma unroll
+    for (int q = 0; q < kEPL; ++q)
+      if (e == lane + 64 * q) dg[q] = v;
+  }
+  router_tail(T, E, sigmoid, t, lane, lcol, scol, n, fden, lambda, z_coef, dg, dl, dlT);
+}
+
+// Expert choice: the experts that took token t are those with row_of[e][t] >= 0 (lane-strided);
+// gates w = g / sum over them of g (renorm; the sum taken in ascending expert order, as the
+// combine does) or g. GATES: write wrow[row] = w for every taken expert. Otherwise: the router
+// backward from the per-row d w (dw[row]).
+template <bool GATES>
+__global__ __launch_bounds__(256) void ec_token_kernel(
+    int64_t T, int E, int renorm, int sigmoid, const int32_t* __restrict__ row_of,
+    const float* __restrict__ lcol, const float* __restrict__ scol, float* __restrict__ wrow,
+    const float* __restrict__ dw, const int32_t* __restrict__ n, double fden, float lambda,
+    float z_coef, float* __restrict__ dl, float* __restrict__ dlT) {
+  __shared__ float lg[4][MOE_E_MAX];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (t >= T) return;  // whole waves only: no block barrier below
+  int row[kEPL];
+  float g[kEPL];
+#pragma unroll
+  for (int q = 0; q < kEPL; ++q) {
+    const int e = lane + 64 * q;
+    row[q] = e < E ? row_of[static_cast<int64_t>(e) * T + t] : -1;
+    g[q] = row[q] >= 0 ? scol[static_cast<int64_t>(e) * T + t] : 0.f;
+    if (e < E) lg[wave][e] = g[q];
+  }
+  __builtin_amdgcn_wave_barrier();
+  // the gate denominator in ascending expert order (lane 0), as in the combine
+  float den = 0.f;
+  if (lane == 0)
+    for (int e = 0; e < E; ++e) den += lg[wave][e];
+  den = __shfl(den, 0, 64);
+  den = renorm && den > 0.f ? den : 1.f;
+  if constexpr (GATES) {
+#pragma unroll
+    for (int q = 0; q < kEPL; ++q)
+      if (row[q] >= 0) wrow[row[q]] = g[q] / den;
+    return;
+  } else {
+    float dwq[kEPL], wdw = 0.f;
+#pragma unroll
+    for (int q = 0; q < kEPL; ++q) {
+      dwq[q] = row[q] >= 0 ? dw[row[q]] : 0.f;
+      wdw += (g[q] / den) * dwq[q];
+    }
+    wdw = wave_sum(wdw);
+    float dg[kEPL];
+#pragma unroll
+    for (int q = 0; q < kEPL; ++q)
+      dg[q] = row[q] < 0 ? 0.f : (renorm ? (dwq[q] - wdw) / den : dwq[q]);
+    router_tail(T, E, sigmoid, t, lane, lcol, scol, n, fden, lambda, z_coef, dg, dl, dlT);
   }
 }
 
@@ -400,6 +474,34 @@ __global__ __launch_bounds__(256) void bw_dx_kernel(int64_t Tn, int d, int k,
   }
 }
 
+// Expert choice: dx_t += the dx rows of the experts that took t, in ascending expert order
+// (+ dx_sh[t]); one wave per token, the rows compacted into LDS by a ballot per 64 experts.
+__global__ __launch_bounds__(256) void bw_dx_ec_kernel(int64_t Tn, int d, int E,
+                                                        const int32_t* __restrict__ row_of,
+                                                        const float* __restrict__ dx_perm,
+                                                        const float* __restrict__ dx_sh,
+                                                        float* __restrict__ dx) {
+  __shared__ int lrow[4][MOE_E_MAX];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (t >= Tn) return;  // whole waves only: no block barrier below
+  int cnt = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    const int row = e < E ? row_of[static_cast<int64_t>(e) * Tn + t] : -1;
+    const unsigned long long m = __ballot(row >= 0);
+    if (row >= 0) lrow[wave][cnt + __popcll(m & ((1ull << lane) - 1ull))] = row;
+    cnt += __popcll(m);
+  }
+  __builtin_amdgcn_wave_barrier();
+  for (int i = lane; i < d; i += 64) {
+    float v = dx[t * d + i];
+    for (int j = 0; j < cnt; ++j) v += dx_perm[static_cast<int64_t>(lrow[wave][j]) * d + i];
+    if (dx_sh != nullptr) v += dx_sh[t * d + i];
+    dx[t * d + i] = v;
+  }
+}
+
 template <typename TA>
 hipError_t nn_dispatch(int dtype_b, bool two, const void* A, const void* A2,
                        const int32_t* gather_a, const int32_t* offsets, const int32_t* tile_off, int groups,
@@ -495,6 +597,31 @@ hipError_t launch_bw_router(int64_t T, int E, int k, int renorm, int sigmoid, co
   hipLaunchKernelGGL(bw_router_kernel, dim3(static_cast<unsigned>(cdiv(T, 4))), dim3(256), 0, st,
                      T, E, k, renorm, sigmoid, lcol, scol, topk_idx, inv_perm, topk_w, dw, n, fden,
                      lambda, z_coef, dl, dlT);
+  return hipGetLastError();
+}
+
+hipError_t launch_ec_gates(int64_t T, int E, int renorm, const int32_t* row_of,
+                           const float* scol, float* wrow, hipStream_t st) {
+  hipLaunchKernelGGL(ec_token_kernel<true>, dim3(static_cast<unsigned>(cdiv(T, 4))), dim3(256), 0,
+                     st, T, E, renorm, 0, row_of, nullptr, scol, wrow, nullptr, nullptr, 1.0, 0.f,
+                     0.f, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_router_ec(int64_t T, int E, int renorm, int sigmoid, const int32_t* row_of,
+                               const float* lcol, const float* scol, const float* dw,
+                               const int32_t* n, double fden, float lambda, float z_coef,
+                               float* dl, float* dlT, hipStream_t st) {
+  hipLaunchKernelGGL(ec_token_kernel<false>, dim3(static_cast<unsigned>(cdiv(T, 4))), dim3(256),
+                     0, st, T, E, renorm, sigmoid, row_of, lcol, scol, nullptr, dw, n, fden,
+                     lambda, z_coef, dl, dlT);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_dx_ec(int64_t T, int d, int E, const int32_t* row_of, const float* dx_perm,
+                           const float* dx_sh, float* dx, hipStream_t st) {
+  hipLaunchKernelGGL(bw_dx_ec_kernel, dim3(static_cast<unsigned>(cdiv(T, 4))), dim3(256), 0, st,
+                     T, d, E, row_of, dx_perm, dx_sh, dx);
   return hipGetLastError();
 }
 

@@ -252,7 +252,7 @@ LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
   p.h = mfma ? nullptr : c.take<float>(R * M);
   p.P = c.take<float>(R * M);
   p.dout = mfma ? nullptr : c.take<float>(R * d);
-  p.dw = c.take<float>(T * s->k);
+  p.dw = c.take<float>(T * s->k > R ? T * s->k : R);  // per slot, or per row (expert choice)
   p.dl = c.take<float>(T * E);
   p.dlT = c.take<float>(T * E);
   p.dG = mfma ? nullptr : c.take<float>(R * M);
@@ -261,13 +261,12 @@ LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
   p.ldp = 64 * (static_cast<int64_t>(cdiv(static_cast<int64_t>(R), 64)) + s->E);
   p.ldps = 64 * cdiv(s->T, 64);
   const size_t lp = static_cast<size_t>(p.ldp), lps = static_cast<size_t>(p.ldps);
-  p.wrow = nullptr;
+  p.wrow = mfma || expert_choice(s) ? c.take<float>(R) : nullptr;
   p.WdT = p.WguT = p.dGU = p.whT = p.dGT = p.dUT = p.dyT = p.xT = nullptr;
   p.WsdT = p.WsguT = p.dGUs = p.hsT = p.dGsT = p.dUsT = p.dysT = p.xsT = nullptr;
   if (mfma) {
     p.WdT = c.take<bf16_t>(E * M * d);
     p.WguT = c.take<bf16_t>(E * d * 2 * M);
-    p.wrow = c.take<float>(R);
     p.dGU = c.take<bf16_t>(R * 2 * M);
     p.whT = c.take<bf16_t>(M * lp);
     p.dGT = c.take<bf16_t>(M * lp);
@@ -609,7 +608,7 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
                               size_t ws_bytes, void* stream) {
   moe_status st = moe_check_shape(s);
   if (st != MOE_OK) return st;
-  if (expert_choice(s)) return MOE_ERR_UNSUPPORTED;
+  if (expert_choice(s) && b != nullptr) return MOE_ERR_INVALID_ARGUMENT;
   if (!x || !W_r || !W_gate || !W_up || !W_down || !dy) return MOE_ERR_INVALID_ARGUMENT;
   if (!dx || !dW_r || !dW_gate || !dW_up || !dW_down) return MOE_ERR_INVALID_ARGUMENT;
   if (s->S > 0 && (!Ws_gate || !Ws_up || !Ws_down || !dWs_gate || !dWs_up || !dWs_down))
@@ -636,15 +635,29 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
   const int64_t dM = static_cast<int64_t>(s->d) * s->M;
   const size_t ET = static_cast<size_t>(s->E) * s->T;
   // ---- forward recompute: routing, placement, fp32 pre-activations and h, score columns
-  hipError_t e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s), x, W_r, b, idx,
-                              f.topk_w, f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart, nullptr, hs);
-  if (e == hipSuccess)
-    e = launch_scan(s->T, s->E, C, nblk, f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart, f.block_base,
-                    f.n, f.gsum, f.lse2sum, f.hsum, f.kept, f.overflow, f.offsets, f.tile_off, BM,
-                    hs);
-  if (e == hipSuccess)
-    e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx, route_block_tokens(s->dtype, s->E),
-                       f.block_base, f.offsets, nullptr, f.perm_token, f.inv_perm, hs);
+  const bool ec = expert_choice(s);
+  const float* lcol = p.cols;
+  const float* scol = p.cols + ET;
+  hipError_t e = hipSuccess;
+  if (ec) {  // logit and score columns, then every expert's top-r tokens and the tile tables
+    e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s), x, W_r, nullptr, nullptr,
+                     nullptr, f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart, p.cols, hs);
+    if (e == hipSuccess)
+      e = launch_ec_select(s->T, s->E, static_cast<int>(ec_tokens(s)), lcol, f.perm_token,
+                           f.row_of, f.offsets, f.n, f.overflow, hs);
+    if (e == hipSuccess) e = launch_schedule(s->E, f.offsets, f.tile_off, BM, hs);
+  } else {
+    e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s), x, W_r, b, idx, f.topk_w,
+                     f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart, nullptr, hs);
+    if (e == hipSuccess)
+      e = launch_scan(s->T, s->E, C, nblk, f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart,
+                      f.block_base, f.n, f.gsum, f.lse2sum, f.hsum, f.kept, f.overflow, f.offsets,
+                      f.tile_off, BM, hs);
+    if (e == hipSuccess)
+      e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx,
+                         route_block_tokens(s->dtype, s->E), f.block_base, f.offsets, nullptr,
+                         f.perm_token, f.inv_perm, hs);
+  }
   const bool mfma = s->dtype == MOE_BF16;
   if (mfma) {  // G and U in one launch (gate and up tiles paired)
     if (e == hipSuccess)
@@ -659,7 +672,7 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
                             W_up, dM, s->M, s->d, p.U, hs);
     if (e == hipSuccess) e = launch_swiglu_fwd(R * s->M, p.G, p.U, p.h, hs);
   }
-  if (e == hipSuccess)
+  if (e == hipSuccess && !ec)
     e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s) | kRouteExpertChoice, x, W_r,
                      nullptr, nullptr, nullptr, f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart, p.cols,
                      hs);
@@ -680,13 +693,19 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
   else if (e == hipSuccess)
     e = launch_nn_gemm(s->dtype, s->dtype, false, dy, nullptr, f.perm_token, f.offsets, p.tile64,
                        s->E, max_t64, W_down, nullptr, dM, s->M, s->d, p.P, hs);
+  if (e == hipSuccess && ec)  // expert choice: the gate of every row first
+    e = launch_ec_gates(s->T, s->E, s->renorm, f.row_of, scol, p.wrow, hs);
   if (e == hipSuccess)
-    e = launch_bw_rows(s->dtype, f.offsets, s->E, R, s->d, s->M, s->k, f.perm_token, f.inv_perm,
-                       f.topk_w, dy, p.P, p.G, p.U, p.dw, p.dG, p.dU, p.dGU, p.dout, p.wrow, hs);
-  if (e == hipSuccess)
-    e = launch_bw_router(s->T, s->E, s->k, s->renorm, s->scoring == MOE_SCORE_SIGMOID, p.cols,
-                         p.cols + ET, idx, f.inv_perm, f.topk_w, p.dw, f.n, stats_fden(s), lambda,
-                         z_coef, p.dl, p.dlT, hs);
+    e = launch_bw_rows(s->dtype, f.offsets, s->E, R, s->d, s->M, s->k, f.perm_token,
+                       ec ? nullptr : f.inv_perm, f.topk_w, dy, p.P, p.G, p.U, p.dw, p.dG, p.dU,
+                       p.dGU, p.dout, p.wrow, hs);
+  const int sig = s->scoring == MOE_SCORE_SIGMOID;
+  if (e == hipSuccess && ec)
+    e = launch_bw_router_ec(s->T, s->E, s->renorm, sig, f.row_of, lcol, scol, p.dw, f.n,
+                            stats_fden(s), lambda, z_coef, p.dl, p.dlT, hs);
+  else if (e == hipSuccess)
+    e = launch_bw_router(s->T, s->E, s->k, s->renorm, sig, lcol, scol, idx, f.inv_perm, f.topk_w,
+                         p.dw, f.n, stats_fden(s), lambda, z_coef, p.dl, p.dlT, hs);
   // ---- routed experts
   if (mfma) {
     if (e == hipSuccess)  // dx_row = [dG dU] [W_gate[e] W_up[e]]^T^T over K = 2M
@@ -823,7 +842,9 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
     }
   }
   // ---- tokens
-  if (e == hipSuccess)
+  if (e == hipSuccess && ec)
+    e = launch_bw_dx_ec(s->T, s->d, s->E, f.row_of, p.dxr, s->S > 0 ? p.dxs : nullptr, dx, hs);
+  else if (e == hipSuccess)
     e = launch_bw_dx(s->T, s->d, s->k, f.inv_perm, p.dxr, s->S > 0 ? p.dxs : nullptr, dx, hs);
   return hip_status(e);
 }

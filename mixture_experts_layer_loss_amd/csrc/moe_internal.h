@@ -160,6 +160,16 @@ hipError_t launch_swiglu_bw(int dtype, int64_t count, const float* dh, const voi
                             const void* U, float* dG, float* dU, hipStream_t st);
 hipError_t launch_bw_dx(int64_t T, int d, int k, const int32_t* inv_perm, const float* dx_perm,
                         const float* dx_sh, float* dx, hipStream_t st);
+// Expert choice (row_of [E][T], scores scol [E][T]): the row gates wrow [R]; the router backward
+// from per-row d w; dx_t += the token's dx rows in ascending expert order (+ dx_sh).
+hipError_t launch_ec_gates(int64_t T, int E, int renorm, const int32_t* row_of,
+                           const float* scol, float* wrow, hipStream_t st);
+hipError_t launch_bw_router_ec(int64_t T, int E, int renorm, int sigmoid, const int32_t* row_of,
+                               const float* lcol, const float* scol, const float* dw,
+                               const int32_t* n, double fden, float lambda, float z_coef,
+                               float* dl, float* dlT, hipStream_t st);
+hipError_t launch_bw_dx_ec(int64_t T, int d, int E, const int32_t* row_of, const float* dx_perm,
+                           const float* dx_sh, float* dx, hipStream_t st);
 
 // bf16 backward on MFMA (backward_layout.hip, gemm_bf16.hip).
 // dst[b][c][coff + r] = src[b][r][c] for batch matrices [rows][cols] (sizes multiples of 8).

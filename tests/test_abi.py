@@ -220,7 +220,9 @@ def test_layer_backward_rejects_before_launch():
     assert call(z=float("nan")) == 1
     assert call(ws_bytes=ws - 1) == 3
     ec = moe.make_shape(64, 128, 8, 2, 256, S=1, routing="expert")
-    assert call(shape=ctypes.byref(ec)) == 2  # expert choice has no backward here
+    ins = [F(), F(), F(), F(), F(), F(), F(), F(), F(), F()]     # a bias under expert choice
+    assert L.moe_layer_backward(ctypes.byref(ec), *ins, 0.01, 1e-3, *[F() for _ in range(8)], None,
+                                F(), moe.workspace_size(ec, moe.CALL_LAYER_BACKWARD), None) == 1
     bad = moe.make_shape(64, 128, 8, 9, 256)
     assert call(shape=ctypes.byref(bad)) == 1
 

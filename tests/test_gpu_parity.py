@@ -328,6 +328,13 @@ def test_layer_backward(gpu, base, kw):
                            b=None if inp.b is None else O._f64(inp.b), shared=shared, c=cfg.c,
                            renorm=cfg.renorm, lam=cfg.lam, z_coef=0.3, scoring=cfg.scoring,
                            topk_idx=gidx, magnitudes=bf16)
+    compare_backward(cfg, out, ref)
+
+
+def compare_backward(cfg, out, ref):
+    """The bar of test_layer_backward: fp32 layers 1e-4 max relative error; bf16 layers dW_r 1e-4,
+    every other element within its rounding bound and each output normwise within u."""
+    bf16 = cfg.dtype == "bf16"
     pairs = {key: (out[key], ref[key]) for key in ("dx", "dW_r", "dW_gate", "dW_up", "dW_down")}
     mags = dict(ref["magnitude"]) if bf16 else {}
     if cfg.S > 0:
@@ -360,6 +367,43 @@ def test_layer_backward(gpu, base, kw):
         assert normwise[key] <= u, (key, normwise[key])
     say(f"    max err / bound {ratio}")
     say(f"    normwise {normwise}")
+
+
+LAYER_BW_EC_CASES = [
+    ("expert_choice", dict(T=200, d=128, M=136, E=16)),                       # shared experts
+    ("expert_choice", dict(T=150, d=64, M=64, E=8, c=0.5, S=0)),              # uncovered tokens
+    ("expert_choice", dict(T=100, d=64, M=72, E=6, renorm=False, scoring="sigmoid", S=0)),
+    ("tiny_fp32", dict(routing="expert")),
+]
+
+
+@pytest.mark.parametrize("base,kw", LAYER_BW_EC_CASES)
+def test_layer_backward_expert_choice(gpu, base, kw):
+    """The expert-choice backward against the oracle's (its own selection: each case is checked to
+    have no expert whose r-th and (r+1)-th logits are within 1e-4, so fp32 and fp64 logits select
+    the same tokens); the bar of test_layer_backward."""
+    cfg = cfg_of(base, **kw)
+    say(f"[layer backward, expert choice] {cfg}")
+    inp = workloads.make_inputs(cfg)
+    x64 = O._f64(inp.x)
+    l = O.router_logits(x64, O._f64(inp.W_r))
+    r = O.expert_choice_capacity(cfg.c, cfg.k, cfg.T, cfg.E)
+    if r < cfg.T:
+        col = -np.sort(-l, axis=0)
+        assert (col[r - 1] - col[r]).min() > 1e-4, "ambiguous selection: choose another case"
+    d_ = to_dev(inp, gpu)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dy = (torch.randn(cfg.T, cfg.d, generator=torch.Generator().manual_seed(11))).to(dt)
+    out = moe.moe_layer_backward(d_.x, d_.W_r, d_.W_gate, d_.W_up, d_.W_down, dy.to(gpu), cfg.k,
+                                 shared=d_.shared_fused(), c=cfg.c, renorm=cfg.renorm,
+                                 lam=cfg.lam, z_coef=0.3, scoring=cfg.scoring, routing="expert")
+    torch.cuda.synchronize()
+    shared = [tuple(O._f64(t) for t in s_) for s_ in inp.shared]
+    ref = O.layer_backward_expert_choice(
+        x64, O._f64(inp.W_r), O._f64(inp.W_gate), O._f64(inp.W_up), O._f64(inp.W_down),
+        O._f64(dy), cfg.k, shared=shared, c=cfg.c, renorm=cfg.renorm, lam=cfg.lam, z_coef=0.3,
+        scoring=cfg.scoring, magnitudes=cfg.dtype == "bf16")
+    compare_backward(cfg, out, ref)
 
 
 # ------------------------------------------------------------------------------ whole layer
