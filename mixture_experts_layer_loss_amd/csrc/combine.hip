@@ -2,9 +2,9 @@
 // ("MoE：条件计算与路由" §7 eq. (3)), the un-permute and weighted sum of the DeepseekV3MoE
 // listing's last step on the adg.csdn.net notes page (§四), plus the shared-expert term.
 //
-// One wave per token: the k row indices and gates are wave-uniform; lanes walk the hidden
-// dimension in 16-byte chunks, accumulate in fp32 in slot order j = 0..k-1, add the shared term
-// last and round once to the output type.
+// One wave per token: lane j holds slot j's row and gate, which are read out wave-uniformly; lanes
+// walk the hidden dimension in 16-byte chunks, accumulate in fp32 in slot order j = 0..k-1, add the
+// shared term last and round once to the output type.
 #include "moe_internal.h"
 
 namespace moe {
