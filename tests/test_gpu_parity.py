@@ -285,6 +285,8 @@ LAYER_BW_CASES = [
     ("mixtral_8x7b", dict(T=90, d=64, M=64, E=4, k=2, c=0.01)),   # C = 1: nearly all dropped
     ("tiny_fp32", dict(T=70, E=1, k=1)),
     ("tiny_fp32", dict(T=90, E=4, k=2, c=0.01)),
+    ("tiny_fp32", dict(T=120, M=96, S=2, c=1.0)),                         # fp32 shared experts
+    ("tiny_fp32", dict(T=100, S=1, scoring="sigmoid", bias=True, renorm=False)),
 ]
 
 
