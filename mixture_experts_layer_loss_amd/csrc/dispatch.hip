@@ -79,8 +79,9 @@ __global__ __launch_bounds__(1024) void scan_kernel(
     int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off, int BM) {
   __shared__ int psum[1024];
   __shared__ double pg[1024];
-  __shared__ int sbuf[256];
-  const int tid = threadIdx.x;
+  __shared__ int wtot[4][4];
+  __shared__ double wred[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int EP = 1;
   while (EP < E) EP <<= 1;
   const int P = 1024 / EP;
@@ -130,34 +131,39 @@ __global__ __launch_bounds__(1024) void scan_kernel(
     if (kept_out != nullptr) kept_out[e] = kept;
     if (overflow != nullptr) overflow[e] = n - kept;
   }
-  // exclusive scans over experts: expert e's totals sit in thread e (part 0 is threads [0, EP))
+  // exclusive scans over experts: expert e's totals sit in thread e (part 0 is threads [0, EP)).
+  // Four inclusive scans over threads 0..255 at once: within each wave by shuffles, then the
+  // totals of the lower waves added.
   const int ee = tid < 256 ? tid : 0;
   const bool mine = tid < E;
   const int kept_e = mine ? kept : 0;
-  auto scan256 = [&](int v) -> int {
-    if (tid < 256) sbuf[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const int add = (tid < 256 && tid >= off) ? sbuf[tid - off] : 0;
-      __syncthreads();
-      if (tid < 256) sbuf[tid] += add;
-      __syncthreads();
+  // grouped-GEMM tile tables: [E+1] 256-row (or BM-row) tiles, [E+1] 128-row, [E+1] 64-row
+  int c0 = 0, c1 = 0, c2 = 0;
+  if (mine) tile_counts(kept_e, BM, c0, c1, c2);
+  int v[4] = {kept_e, c0, c1, c2};
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = __shfl_up(v[q], off, 64);
+      if (lane >= off) v[q] += t;
     }
-    const int r = tid < 256 ? sbuf[tid] : 0;
-    __syncthreads();
-    return r;
-  };
-  const int incl = scan256(kept_e);
+  }
+  if (lane == 63 && wave < 4) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wtot[wave][q] = v[q];
+  }
+  __syncthreads();
+  if (wave < 4) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      for (int w = 0; w < wave; ++w) v[q] += wtot[w][q];
+  }
+  const int incl = v[0], i0 = v[1], i1 = v[2], i2 = v[3];
   if (mine && offsets != nullptr) {
     offsets[ee] = incl - kept_e;
     if (ee == E - 1) offsets[E] = incl;
   }
-  // grouped-GEMM tile tables: [E+1] 256-row (or BM-row) tiles, [E+1] 128-row, [E+1] 64-row
-  int c0 = 0, c1 = 0, c2 = 0;
-  if (mine) tile_counts(kept_e, BM, c0, c1, c2);
-  const int i0 = scan256(c0);
-  const int i1 = scan256(c1);
-  const int i2 = scan256(c2);
   if (mine && tile_off != nullptr) {
     tile_off[ee] = i0 - c0;
     tile_off[E + 1 + ee] = i1 - c1;
@@ -168,17 +174,20 @@ __global__ __launch_bounds__(1024) void scan_kernel(
       tile_off[3 * E + 2] = i2;
     }
   }
-  // block sums of lse^2 and of the routing entropy: strided partials, then a fixed tree
+  // block sums of lse^2 and of the routing entropy: strided partials, a butterfly in each wave,
+  // then the 16 wave sums in order (a fixed order: bit-reproducible)
   auto tree = [&](const float* part, double* out) {
     double ls = 0.0;
     for (int b = tid; b < nblk_g; b += 1024) ls += static_cast<double>(part[b]);
-    pg[tid] = ls;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ls += __shfl_xor(ls, off, 64);
+    if (lane == 0) wred[wave] = ls;
     __syncthreads();
-    for (int off = 512; off >= 1; off >>= 1) {
-      if (tid < off) pg[tid] += pg[tid + off];
-      __syncthreads();
+    if (tid == 0) {
+      double t = 0.0;
+      for (int w = 0; w < 16; ++w) t += wred[w];
+      *out = t;
     }
-    if (tid == 0) *out = pg[0];
     __syncthreads();
   };
   if (lse2sum != nullptr) tree(lpart, lse2sum);

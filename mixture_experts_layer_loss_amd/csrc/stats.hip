@@ -22,29 +22,30 @@ __global__ __launch_bounds__(256) void stats_kernel(
     float* __restrict__ f, float* __restrict__ P, float* __restrict__ aux, float* __restrict__ z,
     float* __restrict__ diag, const float* __restrict__ b, float* __restrict__ b_new,
     float gamma) {
-  __shared__ double red[256];
-  __shared__ long long ired[256];
-  const int e = threadIdx.x;
-  // fixed-order tree sum over the 256 slots of red (every thread returns the total)
+  __shared__ double wsum[4];
+  __shared__ long long wisum[4];
+  const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+  // fixed-order sums over the 256 threads (every thread returns the total): a butterfly inside
+  // each wave, then the four wave sums in wave order
   auto tree = [&](double v) -> double {
-    red[e] = v;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0) wsum[wave] = v;
     __syncthreads();
-    for (int off = 128; off >= 1; off >>= 1) {
-      if (e < off) red[e] += red[e + off];
-      __syncthreads();
-    }
-    const double r = red[0];
+    const double r = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
     __syncthreads();
     return r;
   };
   auto itree = [&](long long v, bool take_max) -> long long {
-    ired[e] = v;
-    __syncthreads();
-    for (int off = 128; off >= 1; off >>= 1) {
-      if (e < off) ired[e] = take_max ? max(ired[e], ired[e + off]) : ired[e] + ired[e + off];
-      __syncthreads();
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const long long o = __shfl_xor(v, off, 64);
+      v = take_max ? max(v, o) : v + o;
     }
-    const long long r = ired[0];
+    if (lane == 0) wisum[wave] = v;
+    __syncthreads();
+    long long r = wisum[0];
+    for (int w = 1; w < 4; ++w) r = take_max ? max(r, wisum[w]) : r + wisum[w];
     __syncthreads();
     return r;
   };
