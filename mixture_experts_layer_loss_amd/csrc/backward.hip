@@ -1,6 +1,6 @@
-// Backward of the token-choice layer: gradients of <dy, y> + aux + z_coef z with respect to x,
-// W_r and every expert weight, with the selection, the capacity cut and f held fixed (they are
-// discrete). The chain ("MoE：条件计算与路由" §7 eqs. (1)-(3) for y and the gates; "深入理解 MoE
+// Backward of the layer: gradients of <dy, y> + aux + z_coef z with respect to x, W_r and every
+// expert weight, with the selection, the capacity cut and f held fixed (they are discrete). The
+// chain ("MoE：条件计算与路由" §7 eqs. (1)-(3) for y and the gates; "深入理解 MoE
 // (混合专家模型)：稀疏激活与高效扩展" §10.2 for SwiGLU; the balance-loss part as in
 // loss_backward.hip):
 //   combine:  d out[row(t,j)] = w_tj dy_t,  d w_tj = <dy_t, out[row(t,j)]> = <dy_t W_down[e], h>
@@ -11,13 +11,16 @@
 //   SwiGLU:   dG = dh U SiLU'(G),  dU = dh SiLU(G),  SiLU'(z) = sigma(z) (1 + z (1 - sigma(z)))
 //   up:       dx_row = dG W_gate[e] + dU W_up[e],  dW_gate[e] = sum_rows dG^T x,  dW_up likewise
 //   tokens:   dx_t = (dl W_r)_t + sum_j dx_row(t,j) (slot order) + shared experts' dx_t
-// Products run as fp32 SIMT tiles (64 x 64 outputs, 256 threads, 4 x 4 each, K staged 16 at a
-// time in LDS, accumulation in k order): "NN" products read A row-major and the weight K-major
-// (B[k][n]); weight gradients reduce over a group's rows with both operands K-major (rows), the
-// x operand gathered through perm_token. Groups never share a 64-row tile (tile table per group).
-// The pre-activations G, U are recomputed in fp32 and h = SiLU(G) U is formed in fp32 from them,
-// so the gradients follow the real-valued chain (the forward's bf16 roundings of h and of the
+// Under expert choice the slots of token t are the experts that took it (ascending), read from the
+// row map. The pre-activations G, U are recomputed in fp32 and h = SiLU(G) U is formed in fp32 from
+// them, so the gradients follow the real-valued chain (the forward's bf16 roundings of h and of the
 // expert outputs are not differentiated).
+// This file holds the per-row, per-token and elementwise kernels, and the fp32 SIMT products used
+// by fp32 layers (64 x 64 outputs, 256 threads, 4 x 4 each, K staged 16 at a time in LDS,
+// accumulation in k order): "NN" products read A row-major and the weight K-major (B[k][n]); weight
+// gradients reduce over a group's rows with both operands K-major (rows), the x operand gathered
+// through perm_token; groups never share a 64-row tile. bf16 layers run the products on the MFMA
+// grouped GEMM instead (gemm_bf16.hip, operand layouts from backward_layout.hip).
 #include "moe_internal.h"
 
 #include <math.h>
