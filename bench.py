@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--backward-steps", type=int, default=3)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="also run one plain device copy of this many bytes (counter calibration)")
+    ap.add_argument("--blas-reference", action="store_true",
+                    help="also time the vendor GEMM (torch.mm -> hipBLASLt) on one dense matrix of "
+                         "each expert product's shape, as a reference point (bf16 only)")
     return ap.parse_args()
 
 
@@ -65,6 +68,39 @@ def load_traffic(workload: str):
     if not entry or entry.get("source_sha") != gemm_source_sha():
         return None
     return entry.get("bytes_per_launch")
+
+
+def blas_reference(cfg, rows: int, dev):
+    """The vendor library on the dense equivalents of the two routed expert products: all kept
+    rows against ONE weight matrix (no row gather, no per-expert groups, no SwiGLU epilogue), in
+    the same operand layout (both operands contiguous along the reduction). A reference point for
+    the grouped kernels, not part of a step."""
+    import torch
+    d, M = cfg.d, cfg.M
+    g = torch.Generator(device=dev).manual_seed(5)
+    a_up = torch.randn(rows, d, device=dev, dtype=torch.bfloat16, generator=g)
+    w_up = torch.randn(2 * M, d, device=dev, dtype=torch.bfloat16, generator=g)
+    a_dn = torch.randn(rows, M, device=dev, dtype=torch.bfloat16, generator=g)
+    w_dn = torch.randn(d, M, device=dev, dtype=torch.bfloat16, generator=g)
+
+    def timed(fn, n=20):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    up_ms = timed(lambda: torch.mm(a_up, w_up.t()))
+    dn_ms = timed(lambda: torch.mm(a_dn, w_dn.t()))
+    fl_up, fl_dn = 4.0 * d * M * rows, 2.0 * d * M * rows
+    return {"what": "torch.mm (hipBLASLt), dense [rows, K] x [K, N] with the routed products' "
+                    "rows, K and N", "rows": rows,
+            "gemm_up_ms": round(up_ms, 4), "gemm_up_tflops": round(fl_up / up_ms / 1e9, 1),
+            "gemm_down_ms": round(dn_ms, 4), "gemm_down_tflops": round(fl_dn / dn_ms / 1e9, 1)}
 
 
 def cpu_baseline(cfg, inp, seconds: float):
@@ -215,6 +251,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    blas_ref = None
+    if args.blas_reference and cfg.dtype == "bf16":
+        blas_ref = blas_reference(cfg, int((out["counts"] - out["overflow"]).sum().item()), dev)
+
     ms_step = (t1 - t0) * 1e3 / args.steps
     stage_ms = np.zeros(len(moe.STAGES))
     for evs in events:
@@ -281,6 +321,8 @@ def main():
         "balance_loss_backward": {"ms": round(lb_ms, 4),
                                   "flops": 2.0 * 3 * T * d * E},
     }
+    if blas_ref is not None:
+        line["blas_reference"] = blas_ref
     if bw_ms is not None:
         # algorithmic products: gate/up recompute 4dM, P = dy W_down 2dM, dx rows 4dM, weight
         # gradients 6dM per kept row; shared experts the same per token; router 2dE (logits) +
