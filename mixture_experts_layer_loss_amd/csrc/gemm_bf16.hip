@@ -16,6 +16,9 @@
 // Row gather: with a gather list the A rows are read in place from the token matrix (row r of
 // the group layout is x[gather[r]]), so the dispatch never materialises the permuted copy of x.
 //
+// Outputs are written with non-temporal stores: no product re-reads its output soon enough for L2
+// to keep it, and streaming them past L2 leaves it to the operand rows that other tiles re-read.
+//
 // Ragged groups (experts): a group's rows are cut into 256-row tiles; a remainder of 65..128 rows
 // becomes a 128-row tile and one of 1..64 rows a 64-row tile, each with its own wave layout, so
 // padding rows cost at most half of their tile. The three tile tables (exclusive prefixes per
@@ -296,7 +299,7 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
         for (int r = 0; r < 16; ++r) {
           const int row = wm * G::WROWS + i * 32 + (r >> 2) * 8 + lk * 4 + (r & 3);
           if (row < rows_here && col < N)
-            C32[static_cast<int64_t>(row_begin + row) * ldc + col] = acc[i][j][r];
+            __builtin_nontemporal_store(acc[i][j][r], &C32[static_cast<int64_t>(row_begin + row) * ldc + col]);
         }
       }
     return;
@@ -314,8 +317,8 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
           const int row = wm * G::WROWS + i * 32 + (r >> 2) * 8 + lk * 4 + (r & 3);
           if (row < rows_here && col < N) {
             const int64_t o = static_cast<int64_t>(row_begin + row) * ldc + col;
-            Cg[o] = acc[i][jj][r];
-            C2[o] = acc[i][jj + NJ / 2][r];
+            __builtin_nontemporal_store(acc[i][jj][r], &Cg[o]);
+            __builtin_nontemporal_store(acc[i][jj + NJ / 2][r], &C2[o]);
           }
         }
       }
@@ -350,8 +353,8 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
   for (int c = tid; c < MR * CPR; c += NT) {
     const int r = c / CPR, cc = (c % CPR) * 8;
     if (r < rows_here && n0 + cc < N)
-      *reinterpret_cast<uint4*>(C + static_cast<int64_t>(row_begin + r) * ldc + n0 + cc) =
-          *reinterpret_cast<const uint4*>(ct + r * CS + cc);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(ct + r * CS + cc),
+                                  reinterpret_cast<u32x4*>(C + static_cast<int64_t>(row_begin + r) * ldc + n0 + cc));
   }
 }
 
