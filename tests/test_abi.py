@@ -232,3 +232,11 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "_lib_handle", None)
     with pytest.raises(RuntimeError, match="missing"):
         moe.lib()
+
+
+def test_stage_events_hook_checks_its_arguments():
+    h = moe.lib()
+    assert h.moe_set_stage_events(None, 0) == moe.MOE_OK            # off
+    arr = (ctypes.c_void_p * 8)()
+    assert h.moe_set_stage_events(arr, 7) == moe.MOE_ERR_INVALID_ARGUMENT   # fewer than 8
+    assert h.moe_set_stage_events(None, 8) == moe.MOE_OK            # NULL always switches off

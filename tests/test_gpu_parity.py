@@ -579,6 +579,25 @@ def test_layer_is_deterministic(gpu):
         assert torch.equal(a[key], b[key]), key
 
 
+
+def test_stage_events_leave_outputs_unchanged(gpu):
+    # the profiling hook (used by bench.py for per-stage times) records events and nothing else
+    cfg = cfg_of("deepseekmoe_16b", T=512, d=256, M=128)
+    say(f"[stage events] {cfg}")
+    inp, a = run_layer(cfg, gpu)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(moe.STAGE_COUNT)]
+    moe.moe_set_stage_events(evs)
+    try:
+        _, b = run_layer(cfg, gpu, inp)
+    finally:
+        moe.moe_set_stage_events(None)
+    for key in ("y", "topk_idx", "topk_w", "counts", "f", "P", "aux", "z"):
+        assert torch.equal(a[key], b[key]), key
+    stage_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(moe.STAGE_COUNT - 1)]
+    assert all(t >= 0.0 for t in stage_ms), stage_ms
+    total = evs[0].elapsed_time(evs[-1])
+    assert abs(sum(stage_ms) - total) <= 1e-3 + 1e-6 * total, (stage_ms, total)
+
 def test_layer_all_dropped_gives_shared_only(gpu):
     # capacity 1: almost every slot is dropped; a token with no kept slot returns the shared term
     cfg = cfg_of("deepseekmoe_16b", T=256, d=64, M=64, c=1.0 / 128)
