@@ -220,6 +220,7 @@ def main():
     # the full layer backward (token choice): gradients of <dy, y> + aux + z for x, W_r and every
     # expert weight, forward recompute included (a separate entry point; not part of a step)
     bw_ms = None
+    train_saved = None
     if not args.no_backward:
         print("[bench] layer backward", file=sys.stderr, flush=True)
         dy = torch.randn(cfg.T, cfg.d, generator=torch.Generator().manual_seed(11)).to(dt).to(dev)
@@ -242,6 +243,37 @@ def main():
         bw_e.record()
         torch.cuda.synchronize()
         bw_ms = bw_s.elapsed_time(bw_e) / args.backward_steps
+        if cfg.dtype == "bf16":
+            # training pair with the forward keeping its fp32 gate/up pre-activations, so that the
+            # backward skips recomputing them (the gradients are bit-identical)
+            saved = layer.saved_buffer()
+            out_s = layer.alloc_outputs(with_bias=b is not None)
+
+            def fwd_save():
+                layer.forward(x, W_r, Wg, Wu, Wd, b, sh, cfg.lam, cfg.gamma, out=out_s, saved=saved)
+
+            def bw_saved():
+                return moe.moe_layer_backward(x, W_r, Wg, Wu, Wd, dy, cfg.k, b=b, shared=shared_w,
+                                              c=cfg.c, renorm=cfg.renorm, lam=cfg.lam, z_coef=1.0,
+                                              scoring=cfg.scoring, routing=cfg.routing, ws=bw_ws,
+                                              saved=saved)
+            fwd_save()
+            g = bw_saved()
+            torch.cuda.synchronize()
+            del g
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record()
+            for _ in range(args.backward_steps):
+                fwd_save()
+            ev[1].record()
+            for _ in range(args.backward_steps):
+                g = bw_saved()
+                del g
+            ev[2].record()
+            torch.cuda.synchronize()
+            train_saved = (ev[0].elapsed_time(ev[1]) / args.backward_steps,
+                           ev[1].elapsed_time(ev[2]) / args.backward_steps)
+            del saved, out_s
         del bw_ws, dy
 
     if args.copy_bytes > 0:  # one plain copy of known size, for counter calibration
@@ -332,6 +364,16 @@ def main():
         line["layer_backward"] = {"ms": round(bw_ms, 3), "flops": bw_fl,
                                   "tflops": round(bw_tf, 1), "mfma_frac": round(bw_tf / peak, 4),
                                   "steps": args.backward_steps}
+        if train_saved is not None:
+            # forward + backward per training step: recomputing the gate/up pre-activations in the
+            # backward, or keeping them from the forward (moe_saved_size bytes)
+            line["train_step"] = {
+                "recompute": {"forward_ms": round(ms_step, 4), "backward_ms": round(bw_ms, 3),
+                              "total_ms": round(ms_step + bw_ms, 3)},
+                "saved_pre_activations": {"forward_ms": round(train_saved[0], 4),
+                                          "backward_ms": round(train_saved[1], 3),
+                                          "total_ms": round(sum(train_saved), 3),
+                                          "saved_bytes": moe.saved_size(layer.shape)}}
     print(json.dumps(line), flush=True)
 
 

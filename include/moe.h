@@ -110,6 +110,15 @@ int64_t moe_capacity(const moe_shape* s);
 size_t moe_workspace_size(const moe_shape* s, int call);
 
 /*
+ * moe_saved_size -- bytes of the buffer in which moe_layer_forward keeps, for a later
+ * moe_layer_backward on the same inputs, the fp32 gate and up pre-activations of every routed row
+ * and of the shared experts (bf16 layers only; 0 for fp32 layers or an invalid shape). Layout
+ * (256-byte aligned parts): G, U [R, M] each, R = min(T k, E C) rows in the forward's
+ * expert-major row order (expert choice: E r), then Gs, Us [T, S*M] each when S > 0.
+ */
+size_t moe_saved_size(const moe_shape* s);
+
+/*
  * moe_route -- router of "MoE：条件计算与路由" §原理与演进 and §无辅助损失负载均衡（ALF-LB）.
  *
  * For every token t: l_te = sum_i x_ti W_r,ei (no router bias); m = max_e l_te,
@@ -227,6 +236,10 @@ moe_status moe_balance_stats(const moe_shape* s, const int32_t* n, const double*
  * w_te E_e(x_t) over the experts that took it, in ascending e, w_te = g_te (renormalised over
  * those experts when renorm); a token no expert took gets the shared term only. b must be NULL;
  * topk_idx and topk_w are not written; counts = r, overflow = 0, f_e = n_e / (E r).
+ *   saved device out of moe_saved_size(s) bytes, or NULL: the fp32 gate and up pre-activations of
+ *     every kept row and of the shared experts, taken from the same accumulators as h, for a
+ *     moe_layer_backward on the same inputs (training); y and every other output are the same
+ *     with or without it. bf16 layers only (fp32: MOE_ERR_UNSUPPORTED); 16-byte aligned.
  *   ws device workspace of moe_workspace_size(s, MOE_CALL_LAYER) bytes
  */
 moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r, const float* b,
@@ -234,7 +247,8 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
                              const void* Ws_gate, const void* Ws_up, const void* Ws_down, void* y,
                              int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* overflow,
                              float* f, float* P, float* aux, float* z, float* diag, float* b_new,
-                             float lambda, float gamma, void* ws, size_t ws_bytes, void* stream);
+                             float lambda, float gamma, void* saved, void* ws, size_t ws_bytes,
+                             void* stream);
 
 /*
  * moe_balance_loss_backward -- gradient of the layer's balance losses through the router.
@@ -277,6 +291,10 @@ moe_status moe_balance_loss_backward(const moe_shape* s, const void* x, const vo
  *   dWs_gate, dWs_up [S*M, d], dWs_down [d, S*M] fp32 device out (required when S > 0)
  *   topk_idx device out [T, k] int32 or NULL: the token-choice selection the gradients were
  *     taken at (not written under expert choice)
+ *   saved device [moe_saved_size(s) bytes] or NULL: the buffer a moe_layer_forward call on the
+ *     same inputs filled; the gate/up products are then not recomputed (the routing and placement
+ *     still are: they are deterministic, so the rows match). The gradients are bit-identical
+ *     either way. Read only; bf16 layers only (fp32: MOE_ERR_UNSUPPORTED); 16-byte aligned.
  *   ws device workspace of moe_workspace_size(s, MOE_CALL_LAYER_BACKWARD) bytes
  */
 moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r, const float* b,
@@ -284,8 +302,8 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
                               const void* Ws_gate, const void* Ws_up, const void* Ws_down,
                               const void* dy, float lambda, float z_coef, float* dx, float* dW_r,
                               float* dW_gate, float* dW_up, float* dW_down, float* dWs_gate,
-                              float* dWs_up, float* dWs_down, int32_t* topk_idx, void* ws,
-                              size_t ws_bytes, void* stream);
+                              float* dWs_up, float* dWs_down, int32_t* topk_idx,
+                              const void* saved, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_set_stage_events -- profiling aid for moe_layer_forward (not a step of the method).

@@ -48,6 +48,7 @@ _SIG = {
     "moe_check_shape": (ctypes.c_int, [ctypes.POINTER(Shape)]),
     "moe_capacity": (ctypes.c_int64, [ctypes.POINTER(Shape)]),
     "moe_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int]),
+    "moe_saved_size": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "moe_route": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                  ctypes.c_size_t, _P]),
     "moe_dispatch": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -60,14 +61,15 @@ _SIG = {
                                          _P, _P, _P, _P, _P, _P, ctypes.c_float, _P]),
     "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                          _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                         ctypes.c_float, ctypes.c_float, _P, ctypes.c_size_t, _P]),
+                                         ctypes.c_float, ctypes.c_float, _P, _P, ctypes.c_size_t,
+                                         _P]),
     "moe_set_stage_events": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]),
     "moe_balance_loss_backward": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, ctypes.c_float,
                                                  ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t,
                                                  _P]),
     "moe_layer_backward": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                           _P, ctypes.c_float, ctypes.c_float, _P, _P, _P, _P, _P,
-                                          _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+                                          _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
 }
 
 STAGES = ["route", "dispatch", "gemm_up", "gemm_down", "shared", "combine", "stats"]
@@ -311,13 +313,33 @@ def moe_balance_loss_backward(x: torch.Tensor, W_r: torch.Tensor, n: torch.Tenso
     return out
 
 
+def saved_size(s: Shape) -> int:
+    """moe_saved_size: bytes of the pre-activations a forward keeps for the backward (0: fp32)."""
+    return int(lib().moe_saved_size(ctypes.byref(s)))
+
+
+def saved_buffer(s: Shape, device) -> torch.Tensor:
+    n = saved_size(s)
+    if n == 0:
+        raise ValueError("saved pre-activations are kept for bf16 layers only")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _saved_ok(saved, s: Shape, dev) -> None:
+    if saved.device != dev or not saved.is_contiguous() or saved.numel() < saved_size(s):
+        raise ValueError("saved: a contiguous device buffer of saved_size(shape) bytes")
+
+
 def moe_layer_backward(x, W_r, W_gate, W_up, W_down, dy, k: int, b=None, shared=None,
                        c: Optional[float] = None, renorm: bool = True, lam: float = 0.01,
                        z_coef: float = 0.0, scoring: str = "softmax", routing: str = "token",
-                       ws: Optional[torch.Tensor] = None) -> dict:
+                       ws: Optional[torch.Tensor] = None,
+                       saved: Optional[torch.Tensor] = None) -> dict:
     """Gradients (fp32) of <dy, y> + aux + z_coef z for the layer; ``shared`` is the stacked
     (Ws_gate, Ws_up, Ws_down) when the layer has shared experts. ``topk_idx`` is the recomputed
-    token-choice selection (left unwritten under expert choice)."""
+    token-choice selection (left unwritten under expert choice). ``saved``: the buffer a forward
+    on the same inputs filled (``MoELayer.forward(..., saved=...)``); the gate/up pre-activations
+    are then taken from it instead of being recomputed (bf16 layers)."""
     T, d = x.shape
     E, M, _ = W_gate.shape
     S = 0 if shared is None else shared[0].shape[0] // M
@@ -343,12 +365,14 @@ def moe_layer_backward(x, W_r, W_gate, W_up, W_down, dy, k: int, b=None, shared=
                     "dWs_down": torch.empty(d, S * M, **f32)})
     if ws is None:
         ws = workspace(s, CALL_LAYER_BACKWARD, dev)
+    if saved is not None:
+        _saved_ok(saved, s, dev)
     _check(lib().moe_layer_backward(
         ctypes.byref(s), _ptr(x), _ptr(W_r), _ptr(b), _ptr(W_gate), _ptr(W_up), _ptr(W_down),
         _ptr(sg), _ptr(su), _ptr(sd), _ptr(dy), float(lam), float(z_coef), _ptr(out["dx"]),
         _ptr(out["dW_r"]), _ptr(out["dW_gate"]), _ptr(out["dW_up"]), _ptr(out["dW_down"]),
         _ptr(out.get("dWs_gate")), _ptr(out.get("dWs_up")), _ptr(out.get("dWs_down")),
-        _ptr(out["topk_idx"]), _ptr(ws), ws.numel(), _stream()), "moe_layer_backward")
+        _ptr(out["topk_idx"]), _ptr(saved), _ptr(ws), ws.numel(), _stream()), "moe_layer_backward")
     return out
 
 
@@ -380,8 +404,13 @@ class MoELayer:
                 "diag": torch.empty(4, dtype=torch.float32, device=dev),
                 "b_new": torch.empty(E, dtype=torch.float32, device=dev) if with_bias else None}
 
+    def saved_buffer(self) -> torch.Tensor:
+        """A buffer for ``forward(..., saved=...)`` (bf16 layers): moe_saved_size bytes."""
+        return saved_buffer(self.shape, self.device)
+
     def forward(self, x, W_r, W_gate, W_up, W_down, b=None, shared=None, lam: float = 0.01,
-                gamma: float = 1e-3, out: Optional[dict] = None) -> dict:
+                gamma: float = 1e-3, out: Optional[dict] = None,
+                saved: Optional[torch.Tensor] = None) -> dict:
         T, d, E, M, dt = self.T, self.d, self.E, self.M, self.dtype
         _dev(x, "x", dt, (T, d))
         _dev(W_r, "W_r", dt, (E, d))
@@ -401,13 +430,15 @@ class MoELayer:
             _dev(sd, "Ws_down", dt, (d, SM))
         if out is None:
             out = self.alloc_outputs(with_bias=b is not None)
+        if saved is not None:
+            _saved_ok(saved, self.shape, self.device)
         _check(lib().moe_layer_forward(
             ctypes.byref(self.shape), _ptr(x), _ptr(W_r), _ptr(b), _ptr(W_gate), _ptr(W_up),
             _ptr(W_down), _ptr(sg), _ptr(su), _ptr(sd), _ptr(out["y"]), _ptr(out.get("topk_idx")),
             _ptr(out.get("topk_w")), _ptr(out.get("counts")), _ptr(out.get("overflow")),
             _ptr(out.get("f")), _ptr(out.get("P")), _ptr(out.get("aux")), _ptr(out.get("z")),
             _ptr(out.get("diag")), _ptr(out.get("b_new") if b is not None else None), float(lam),
-            float(gamma),
+            float(gamma), _ptr(saved),
             _ptr(self.ws), self.ws.numel(), _stream()), "moe_layer_forward")
         return out
 

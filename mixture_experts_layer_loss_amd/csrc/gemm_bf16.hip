@@ -112,7 +112,8 @@ __device__ __forceinline__ void sched_substep_wl() {
 // One MR x 256 output tile of group g: rows [row_begin, row_begin + rows_here), output columns
 // [n0, n0 + BNO). EPI 0: SwiGLU (B0 = W_gate, B1 = W_up); EPI 1: plain (B0 = W_down); EPI 2:
 // plain with fp32 output (C is then float), stored straight from the accumulators; EPI 3: the
-// gate and up pre-activations of EPI 0 stored as fp32 to C and C2.
+// gate and up pre-activations of EPI 0 stored as fp32 to C and C2; EPI 4: EPI 0 (h to C) after
+// storing those pre-activations to C2 and C3.
 // KTAIL: K is not a multiple of 64 (the last k-slice is zero-padded). Row r of A starts at
 // A + r lda (gathered: A + gather[r] lda), row n of group g's B at B + g group_stride + n ldb, and
 // output row r at C + r ldc.
@@ -122,10 +123,12 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
                                          const bf16_t* __restrict__ B0,
                                          const bf16_t* __restrict__ B1, int64_t group_stride,
                                          int ldb, int N, int K, bf16_t* __restrict__ C, int ldc,
-                                         float* __restrict__ C2, int g, int row_begin,
+                                         float* __restrict__ C2, float* __restrict__ C3, int g,
+                                         int row_begin,
                                          int rows_here, int n0) {
   using G = Geo<MR>;
-  constexpr bool PAIRED = EPI == 0 || EPI == 3;  // B rows: 128 gate + 128 up
+  constexpr bool PAIRED = EPI == 0 || EPI == 3 || EPI == 4;  // B rows: 128 gate + 128 up
+  constexpr bool SWIGLU = EPI == 0 || EPI == 4;               // h = SiLU(gate) * up, bf16
   constexpr int BNO = PAIRED ? BN / 2 : BN;      // output columns per tile
   constexpr int MI = G::MI, NJ = G::NJ, ACH = G::ACH, BCH = G::BCH, RS = G::RSTEP;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -304,9 +307,11 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
       }
     return;
   }
-  if constexpr (EPI == 3) {
-    // fp32 gate (C) and up (C2) pre-activations of the same output columns
-    float* Cg = reinterpret_cast<float*>(C);
+  if constexpr (EPI == 3 || EPI == 4) {
+    // fp32 gate and up pre-activations of the same output columns: to C and C2 (EPI 3), or to C2
+    // and C3 ahead of the SwiGLU epilogue that writes h to C (EPI 4)
+    float* Cg = EPI == 3 ? reinterpret_cast<float*>(C) : C2;
+    float* Cu = EPI == 3 ? C2 : C3;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -318,11 +323,11 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
           if (row < rows_here && col < N) {
             const int64_t o = static_cast<int64_t>(row_begin + row) * ldc + col;
             __builtin_nontemporal_store(acc[i][jj][r], &Cg[o]);
-            __builtin_nontemporal_store(acc[i][jj + NJ / 2][r], &C2[o]);
+            __builtin_nontemporal_store(acc[i][jj + NJ / 2][r], &Cu[o]);
           }
         }
       }
-    return;
+    if constexpr (EPI == 3) return;
   }
   __syncthreads();
 
@@ -334,13 +339,13 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
-    for (int jj = 0; jj < (EPI == 0 ? NJ / 2 : NJ); ++jj) {
-      const int col = (EPI == 0 ? wn * (G::WCOLS / 2) : wn * G::WCOLS) + jj * 32 + l32;
+    for (int jj = 0; jj < (SWIGLU ? NJ / 2 : NJ); ++jj) {
+      const int col = (SWIGLU ? wn * (G::WCOLS / 2) : wn * G::WCOLS) + jj * 32 + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = wm * G::WROWS + i * 32 + (r >> 2) * 8 + lk * 4 + (r & 3);
         float v;
-        if (EPI == 0)
+        if (SWIGLU)
           v = silu(acc[i][jj][r]) * acc[i][jj + NJ / 2][r];
         else
           v = acc[i][jj][r];
@@ -377,8 +382,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tile_off, int groups, int main_blocks,
     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, int64_t group_stride, int N,
-    int K, bf16_t* __restrict__ C, float* __restrict__ C2) {
-  constexpr int BNO = (EPI == 0 || EPI == 3) ? BN / 2 : BN;
+    int K, bf16_t* __restrict__ C, float* __restrict__ C2, float* __restrict__ C3) {
+  constexpr int BNO = (EPI == 0 || EPI == 3 || EPI == 4) ? BN / 2 : BN;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int nb_count = (N + BNO - 1) / BNO;
   const int32_t* t256 = tile_off;
@@ -396,7 +401,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     const int row_begin = offsets[g] + mt * 256;
     const int rows = min(256, offsets[g + 1] - row_begin);
     run_tile<EPI, KTAIL, GATHER, 256>(lds, A, K, gather, B0, B1, group_stride, K, N, K, C, N, C2,
-                                      g, row_begin, rows, nb * BNO);
+                                      C3, g, row_begin, rows, nb * BNO);
     return;
   }
   // a group's remainder tile (at most one per group and class): n-blocks in order
@@ -416,10 +421,10 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
   const int n0 = static_cast<int>(local) * BNO;
   if (table == t128)
     run_tile<EPI, KTAIL, GATHER, 128>(lds, A, K, gather, B0, B1, group_stride, K, N, K, C, N, C2,
-                                      g, row_begin, rows, n0);
+                                      C3, g, row_begin, rows, n0);
   else
     run_tile<EPI, KTAIL, GATHER, 64>(lds, A, K, gather, B0, B1, group_stride, K, N, K, C, N, C2,
-                                     g, row_begin, rows, n0);
+                                     C3, g, row_begin, rows, n0);
 }
 
 // Weight gradients: C_g [Ma][Nb] (fp32) = sum over k in [64 kt[g], 64 kt[g+1]) of A[m][k] B[n][k],
@@ -454,7 +459,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_gemm_kernel(const bf16_t* __restr
     return;
   }
   run_tile<2, false, false, 256>(lds, A + k0, lda, nullptr, B + k0, nullptr, 0, ldb, Nb, K,
-                                 reinterpret_cast<bf16_t*>(Cg), Nb, nullptr, 0, m0,
+                                 reinterpret_cast<bf16_t*>(Cg), Nb, nullptr, nullptr, 0, m0,
                                  min(256, Ma - m0), n0);
 }
 
@@ -463,8 +468,8 @@ hipError_t launch_gemm_t(const bf16_t* A, const int32_t* gather, const int32_t* 
                          const int32_t* tile_off,
                          int groups, int64_t max_tiles, const bf16_t* B0, const bf16_t* B1,
                          int64_t group_stride, int N, int K, bf16_t* C, float* C2,
-                         hipStream_t st) {
-  constexpr int BNO = (EPI == 0 || EPI == 3) ? BN / 2 : BN;
+                         float* C3, hipStream_t st) {
+  constexpr int BNO = (EPI == 0 || EPI == 3 || EPI == 4) ? BN / 2 : BN;
   const int64_t nb = cdiv(N, BNO);
   // the 256-row tiles, then at most one 128-row and one 64-row tile per group
   const int64_t main_blocks = cdiv(max_tiles * nb, NXCD) * NXCD;
@@ -485,7 +490,7 @@ hipError_t launch_gemm_t(const bf16_t* A, const int32_t* gather, const int32_t* 
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((grouped_gemm_kernel<EPI, KTAIL, GATHER>), dim3(static_cast<unsigned>(grid)),
                      dim3(NT), lds, st, A, gather, offsets, tile_off, groups,
-                     static_cast<int>(main_blocks), B0, B1, group_stride, N, K, C, C2);
+                     static_cast<int>(main_blocks), B0, B1, group_stride, N, K, C, C2, C3);
   return hipGetLastError();
 }
 
@@ -493,12 +498,12 @@ template <int EPI, bool GATHER>
 hipError_t launch_gemm(const bf16_t* A, const int32_t* gather, const int32_t* offsets,
                        const int32_t* tile_off, int groups, int64_t max_tiles, const bf16_t* B0,
                        const bf16_t* B1, int64_t group_stride, int N, int K, bf16_t* C,
-                       hipStream_t st, float* C2 = nullptr) {
+                       hipStream_t st, float* C2 = nullptr, float* C3 = nullptr) {
   if (K % BK == 0)
     return launch_gemm_t<EPI, false, GATHER>(A, gather, offsets, tile_off, groups, max_tiles, B0,
-                                             B1, group_stride, N, K, C, C2, st);
+                                             B1, group_stride, N, K, C, C2, C3, st);
   return launch_gemm_t<EPI, true, GATHER>(A, gather, offsets, tile_off, groups, max_tiles, B0, B1,
-                                          group_stride, N, K, C, C2, st);
+                                          group_stride, N, K, C, C2, C3, st);
 }
 
 }  // namespace
@@ -537,6 +542,26 @@ hipError_t launch_gemm_gu_f32out_bf16(int groups, int d, int Mg, const void* row
                                 Gp, st, U);
   return launch_gemm<3, false>(A, nullptr, offsets, tile_off, groups, max_tiles, Wg, Wu, gs, Mg, d,
                                Gp, st, U);
+}
+
+// The SwiGLU GEMM of launch_gemm_up_bf16 that also stores the fp32 gate and up pre-activations
+// G[r] and U[r] (the values launch_gemm_gu_f32out_bf16 computes, from the same accumulators), so
+// that a backward can take them instead of recomputing them; h is unchanged.
+hipError_t launch_gemm_up_save_bf16(int groups, int d, int Mg, const void* rows,
+                                    const int32_t* gather, const int32_t* offsets,
+                                    const int32_t* tile_off, int64_t max_tiles, const void* W_gate,
+                                    const void* W_up, void* h, float* G, float* U,
+                                    hipStream_t st) {
+  const bf16_t* A = static_cast<const bf16_t*>(rows);
+  const bf16_t* Wg = static_cast<const bf16_t*>(W_gate);
+  const bf16_t* Wu = static_cast<const bf16_t*>(W_up);
+  const int64_t gs = static_cast<int64_t>(Mg) * d;
+  bf16_t* H = static_cast<bf16_t*>(h);
+  if (gather != nullptr)
+    return launch_gemm<4, true>(A, gather, offsets, tile_off, groups, max_tiles, Wg, Wu, gs, Mg, d,
+                                H, st, G, U);
+  return launch_gemm<4, false>(A, nullptr, offsets, tile_off, groups, max_tiles, Wg, Wu, gs, Mg, d,
+                               H, st, G, U);
 }
 
 // C[r] = A_r B_g^T for the rows of group g (A_r = rows[gather[r]] when gather != NULL): the plain

@@ -312,6 +312,27 @@ void mark_stage(int i, hipStream_t st) {
   if (g_stage_on && g_stage_events[i] != nullptr) (void)hipEventRecord(g_stage_events[i], st);
 }
 
+// Pre-activations a training forward keeps for the backward (bf16 layers): the fp32 gate and up
+// values of every routed row, [R, M] each with R the workspace's routed-row bound, then those of
+// the shared experts, [T, S M] each.
+struct SavedPlan {
+  float *G, *U, *Gs, *Us;
+};
+SavedPlan plan_saved(Carve& c, const moe_shape* s) {
+  const size_t R = static_cast<size_t>(routed_rows(s)), M = s->M;
+  SavedPlan p;
+  p.G = c.take<float>(R * M);
+  p.U = c.take<float>(R * M);
+  if (s->S > 0) {
+    const size_t TSM = static_cast<size_t>(s->T) * s->S * M;
+    p.Gs = c.take<float>(TSM);
+    p.Us = c.take<float>(TSM);
+  } else {
+    p.Gs = p.Us = nullptr;
+  }
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -351,6 +372,13 @@ moe_status moe_check_shape(const moe_shape* s) {
 int64_t moe_capacity(const moe_shape* s) {
   if (moe_check_shape(s) != MOE_OK) return -1;
   return capacity_of(s);
+}
+
+size_t moe_saved_size(const moe_shape* s) {
+  if (moe_check_shape(s) != MOE_OK || s->dtype != MOE_BF16) return 0;
+  Carve c(nullptr);
+  plan_saved(c, s);
+  return c.used;
 }
 
 size_t moe_workspace_size(const moe_shape* s, int call) {
@@ -478,10 +506,13 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
                              const void* Ws_gate, const void* Ws_up, const void* Ws_down, void* y,
                              int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* overflow,
                              float* f, float* P, float* aux, float* z, float* diag, float* b_new,
-                             float lambda, float gamma, void* ws, size_t ws_bytes, void* stream) {
+                             float lambda, float gamma, void* saved, void* ws, size_t ws_bytes,
+                             void* stream) {
   moe_status st = moe_check_shape(s);
   if (st != MOE_OK) return st;
   if (!x || !W_r || !W_gate || !W_up || !W_down || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (saved != nullptr && s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (saved != nullptr && !aligned16(saved)) return MOE_ERR_INVALID_ARGUMENT;
   if (s->S > 0 && (!Ws_gate || !Ws_up || !Ws_down)) return MOE_ERR_INVALID_ARGUMENT;
   if (b_new != nullptr && b == nullptr) return MOE_ERR_INVALID_ARGUMENT;
   // the load-balancing bias is a token-choice device: a per-expert shift cannot change which
@@ -498,6 +529,8 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
   hipStream_t hs = static_cast<hipStream_t>(stream);
   Carve c(ws);
   LayerPlan p = plan_layer(c, s);
+  Carve cs(saved);
+  const SavedPlan sv = plan_saved(cs, s);  // all NULL when saved is NULL
   int32_t* idx = topk_idx ? topk_idx : p.topk_idx;
   float* w = topk_w ? topk_w : p.topk_w;
   int32_t* n = counts ? counts : p.n;
@@ -533,7 +566,10 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
                          p.block_base, p.offsets, nullptr, p.perm_token, p.inv_perm, hs);
   }
   mark_stage(2, hs);
-  if (e == hipSuccess)
+  if (e == hipSuccess && saved != nullptr)  // h, and G and U kept for the backward
+    e = launch_gemm_up_save_bf16(s->E, s->d, s->M, x, p.perm_token, p.offsets, p.tile_off,
+                                 max_tiles, W_gate, W_up, p.h, sv.G, sv.U, hs);
+  else if (e == hipSuccess)
     e = launch_gemm_up(s->dtype, s->E, s->d, s->M, x, p.perm_token, p.offsets, p.tile_off,
                        max_tiles, W_gate, W_up, p.h, hs);
   mark_stage(3, hs);
@@ -545,7 +581,10 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
     const int SM = s->S * s->M;
     const int64_t sh_tiles = cdiv(s->T, BM);
     e = launch_shared_table(s->T, BM, p.sh_offsets, p.sh_tile_off, hs);
-    if (e == hipSuccess)
+    if (e == hipSuccess && saved != nullptr)
+      e = launch_gemm_up_save_bf16(1, s->d, SM, x, nullptr, p.sh_offsets, p.sh_tile_off, sh_tiles,
+                                   Ws_gate, Ws_up, p.h_sh, sv.Gs, sv.Us, hs);
+    else if (e == hipSuccess)
       e = launch_gemm_up(s->dtype, 1, s->d, SM, x, nullptr, p.sh_offsets, p.sh_tile_off, sh_tiles,
                          Ws_gate, Ws_up, p.h_sh, hs);
     if (e == hipSuccess)
@@ -604,11 +643,13 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
                               const void* Ws_gate, const void* Ws_up, const void* Ws_down,
                               const void* dy, float lambda, float z_coef, float* dx, float* dW_r,
                               float* dW_gate, float* dW_up, float* dW_down, float* dWs_gate,
-                              float* dWs_up, float* dWs_down, int32_t* topk_idx, void* ws,
-                              size_t ws_bytes, void* stream) {
+                              float* dWs_up, float* dWs_down, int32_t* topk_idx,
+                              const void* saved, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = moe_check_shape(s);
   if (st != MOE_OK) return st;
   if (expert_choice(s) && b != nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if (saved != nullptr && s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (saved != nullptr && !aligned16(saved)) return MOE_ERR_INVALID_ARGUMENT;
   if (!x || !W_r || !W_gate || !W_up || !W_down || !dy) return MOE_ERR_INVALID_ARGUMENT;
   if (!dx || !dW_r || !dW_gate || !dW_up || !dW_down) return MOE_ERR_INVALID_ARGUMENT;
   if (s->S > 0 && (!Ws_gate || !Ws_up || !Ws_down || !dWs_gate || !dWs_up || !dWs_down))
@@ -624,6 +665,14 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
   Carve c(ws);
   LayerBackwardPlan p = plan_layer_backward(c, s);
   LayerPlan& f = p.f;
+  if (saved != nullptr) {  // the forward's pre-activations replace the recomputed ones
+    Carve cs(const_cast<void*>(saved));  // read only
+    const SavedPlan sv = plan_saved(cs, s);
+    p.G = sv.G;
+    p.U = sv.U;
+    p.Gs = sv.Gs;
+    p.Us = sv.Us;
+  }
   int32_t* idx = topk_idx ? topk_idx : f.topk_idx;
   const int64_t C = capacity_of(s);
   const int BM = gemm_bm(s);
@@ -659,8 +708,8 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
                          f.perm_token, f.inv_perm, hs);
   }
   const bool mfma = s->dtype == MOE_BF16;
-  if (mfma) {  // G and U in one launch (gate and up tiles paired)
-    if (e == hipSuccess)
+  if (mfma) {  // G and U in one launch (gate and up tiles paired), unless the forward kept them
+    if (e == hipSuccess && saved == nullptr)
       e = launch_gemm_gu_f32out_bf16(s->E, s->d, s->M, x, f.perm_token, f.offsets, f.tile_off,
                                      max_tiles, W_gate, W_up, p.G, p.U, hs);
   } else {
@@ -763,7 +812,7 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
     const int64_t dSM = static_cast<int64_t>(s->d) * SM;
     e = launch_shared_table(s->T, BM, f.sh_offsets, f.sh_tile_off, hs);
     if (mfma) {
-      if (e == hipSuccess)
+      if (e == hipSuccess && saved == nullptr)
         e = launch_gemm_gu_f32out_bf16(1, s->d, SM, x, nullptr, f.sh_offsets, f.sh_tile_off,
                                        sh_tiles, Ws_gate, Ws_up, p.Gs, p.Us, hs);
     } else {

@@ -188,6 +188,12 @@ hipError_t launch_pad_transpose(int dtype_src, const void* src, const float* src
 // dGU [R][2M] bf16 = [dh U SiLU'(G) | dh SiLU(G)] from fp32 [R][M] inputs
 hipError_t launch_swiglu_bw_cat(int64_t R, int M, const float* dh, const float* G, const float* U,
                                 void* dGU, hipStream_t st);
+// h as launch_gemm_up_bf16 writes it, plus G and U as launch_gemm_gu_f32out_bf16 writes them
+hipError_t launch_gemm_up_save_bf16(int groups, int d, int Mg, const void* rows,
+                                    const int32_t* gather, const int32_t* offsets,
+                                    const int32_t* tile_off, int64_t max_tiles, const void* W_gate,
+                                    const void* W_up, void* h, float* G, float* U,
+                                    hipStream_t st);
 // G[r] = a_r W_gate[g]^T, U[r] = a_r W_up[g]^T in fp32 (one launch, gate/up tiles paired)
 hipError_t launch_gemm_gu_f32out_bf16(int groups, int d, int Mg, const void* rows,
                                       const int32_t* gather, const int32_t* offsets,

@@ -88,8 +88,8 @@ def test_routing_flag_and_expert_choice_limits():
     assert L.moe_combine(sp, F(), F(), F(), None, F(), None) == 2
     # and takes no load-balancing bias
     ws = moe.workspace_size(ec, moe.CALL_LAYER)
-    args = [F(), F(), F()] + [F()] * 3 + [None] * 3 + [F()] + [None] * 10 + [0.01, 1e-3, F(), ws,
-                                                                          None]
+    args = [F(), F(), F()] + [F()] * 3 + [None] * 3 + [F()] + [None] * 10 + [0.01, 1e-3, None, F(),
+                                                                          ws, None]
     assert L.moe_layer_forward(sp, *args) == 1
     # its workspace holds the [E, T] score columns and row map
     assert ws > moe.workspace_size(moe.make_shape(64, 128, 8, 2, 256), moe.CALL_LAYER)
@@ -164,13 +164,21 @@ def test_entry_points_reject_before_launch():
     # layer: shared experts required when S > 0; b_new requires b
     s2 = moe.make_shape(64, 128, 8, 2, 256, S=2)
     ws = moe.workspace_size(s2, moe.CALL_LAYER)
-    # x, W_r, b, W_gate, W_up, W_down, Ws_gate/up/down, y, 10 optional outputs, lambda, gamma, ws
-    args = [F()] * 2 + [None] + [F()] * 3 + [None] * 3 + [F()] + [None] * 10 + [0.01, 1e-3, F(), ws,
-                                                                               None]
+    # x, W_r, b, W_gate, W_up, W_down, Ws_gate/up/down, y, 10 optional outputs, lambda, gamma,
+    # saved, ws
+    args = [F()] * 2 + [None] + [F()] * 3 + [None] * 3 + [F()] + [None] * 10 + [0.01, 1e-3, None,
+                                                                               F(), ws, None]
     assert L.moe_layer_forward(ctypes.byref(s2), *args) == 1
     args = [F()] * 2 + [None] + [F()] * 3 + [None] * 3 + [F()] + [None] * 9 + [F(), 0.01, 1e-3,
-                                                                              F(), ws, None]
+                                                                              None, F(), ws, None]
     assert L.moe_layer_forward(sp, *args) == 1
+    # saved pre-activations: bf16 layers only, 16-byte aligned
+    ws = moe.workspace_size(s, moe.CALL_LAYER)
+    base = [F()] * 2 + [None] + [F()] * 3 + [None] * 3 + [F()] + [None] * 10 + [0.01, 1e-3]
+    assert L.moe_layer_forward(sp, *base, ctypes.c_void_p(4096 + 8), F(), ws, None) == 1
+    s32 = moe.make_shape(64, 128, 8, 2, 256, dtype=torch_f32())
+    ws32 = moe.workspace_size(s32, moe.CALL_LAYER)
+    assert L.moe_layer_forward(ctypes.byref(s32), *base, F(), F(), ws32, None) == 2
     # invalid shape short-circuits everything
     bad = moe.make_shape(64, 128, 8, 9, 256)
     assert L.moe_route(ctypes.byref(bad), F(), F(), None, F(), F(), F(), F(), F(), None, F(),
@@ -203,13 +211,13 @@ def test_layer_backward_rejects_before_launch():
     ws = moe.workspace_size(s, moe.CALL_LAYER_BACKWARD)
     assert ws > 0
 
-    def call(shape=sp, ws_bytes=ws, lam=0.01, z=1e-3, drop=None):
+    def call(shape=sp, ws_bytes=ws, lam=0.01, z=1e-3, drop=None, saved=None):
         # x W_r b W_gate W_up W_down Ws_gate Ws_up Ws_down dy | dx dW_r dWg dWu dWd dWsg dWsu dWsd
         ins = [F(), F(), None, F(), F(), F(), F(), F(), F(), F()]
         outs = [F() for _ in range(8)]
         if drop is not None:
             (ins if drop < 10 else outs)[drop if drop < 10 else drop - 10] = None
-        return L.moe_layer_backward(shape, *ins, lam, z, *outs, None, F(), ws_bytes, None)
+        return L.moe_layer_backward(shape, *ins, lam, z, *outs, None, saved, F(), ws_bytes, None)
 
     assert call(drop=0) == 1                 # no x
     assert call(drop=9) == 1                 # no dy
@@ -219,10 +227,15 @@ def test_layer_backward_rejects_before_launch():
     assert call(lam=float("nan")) == 1
     assert call(z=float("nan")) == 1
     assert call(ws_bytes=ws - 1) == 3
+    assert call(saved=ctypes.c_void_p(4096 + 8)) == 1     # misaligned saved buffer
+    s32 = moe.make_shape(64, 128, 8, 2, 256, S=1, dtype=torch_f32())
+    assert call(shape=ctypes.byref(s32), ws_bytes=moe.workspace_size(s32, moe.CALL_LAYER_BACKWARD),
+                saved=F()) == 2                            # saved is for bf16 layers
     ec = moe.make_shape(64, 128, 8, 2, 256, S=1, routing="expert")
     ins = [F(), F(), F(), F(), F(), F(), F(), F(), F(), F()]     # a bias under expert choice
     assert L.moe_layer_backward(ctypes.byref(ec), *ins, 0.01, 1e-3, *[F() for _ in range(8)], None,
-                                F(), moe.workspace_size(ec, moe.CALL_LAYER_BACKWARD), None) == 1
+                                None, F(), moe.workspace_size(ec, moe.CALL_LAYER_BACKWARD),
+                                None) == 1
     bad = moe.make_shape(64, 128, 8, 9, 256)
     assert call(shape=ctypes.byref(bad)) == 1
 
@@ -240,3 +253,26 @@ def test_stage_events_hook_checks_its_arguments():
     arr = (ctypes.c_void_p * 8)()
     assert h.moe_set_stage_events(arr, 7) == moe.MOE_ERR_INVALID_ARGUMENT   # fewer than 8
     assert h.moe_set_stage_events(None, 8) == moe.MOE_OK            # NULL always switches off
+
+
+def torch_f32():
+    import torch
+    return torch.float32
+
+
+def test_saved_size_is_the_pre_activation_layout():
+    # routed G and U [R, M] fp32, then shared Gs and Us [T, S M] fp32, each part 256-byte aligned
+    al = lambda n: (n + 255) // 256 * 256
+    for kw in (dict(), dict(S=2), dict(c=0.5), dict(routing="expert", S=1)):
+        s = moe.make_shape(96, 128, 8, 2, 256, **kw)
+        T, E, k, M = 96, 8, 2, 256
+        C = moe.capacity(s)
+        if kw.get("routing") == "expert":
+            R = E * min(C if C > 0 else -(-k * T // E), T)
+        else:
+            R = T * k if C < 0 else min(T * k, E * C)
+        S = kw.get("S", 0)
+        want = 2 * al(R * M * 4) + (2 * al(T * S * M * 4) if S else 0)
+        assert moe.saved_size(s) == want, (kw, moe.saved_size(s), want)
+    assert moe.saved_size(moe.make_shape(96, 128, 8, 2, 256, dtype=torch_f32())) == 0
+    assert moe.saved_size(moe.make_shape(96, 128, 8, 9, 256)) == 0     # invalid shape

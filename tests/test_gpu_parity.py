@@ -379,6 +379,53 @@ LAYER_BW_EC_CASES = [
 ]
 
 
+SAVED_CASES = [
+    ("deepseekmoe_16b", dict(T=200, d=128, M=136, c=1.0)),        # shared experts, drops, N tail
+    ("deepseek_v2", dict(T=150, d=200, M=72, scoring="sigmoid")),  # bias, sigmoid, K tail
+    ("mixtral_8x7b", dict(T=1024, d=512, M=768)),                 # several 256 x 256 tiles
+    ("mixtral_8x7b", dict(T=8, d=64, M=64, E=16, k=1)),           # experts without rows
+    ("expert_choice", dict(T=200, d=128, M=136, E=16)),           # expert choice, shared experts
+]
+
+
+@pytest.mark.parametrize("base,kw", SAVED_CASES)
+def test_saved_pre_activations_change_nothing(gpu, base, kw):
+    """A forward that keeps the fp32 gate/up pre-activations returns the same outputs bit for bit,
+    and a backward that takes them instead of recomputing returns the same gradients bit for bit
+    (the same GEMM tiles write them from the same accumulators; routing and placement are
+    deterministic, so the rows line up)."""
+    cfg = cfg_of(base, **kw)
+    say(f"[saved pre-activations] {cfg}")
+    inp = workloads.make_inputs(cfg)
+    d_ = to_dev(inp, gpu)
+    layer = moe.MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.M, cfg.S, cfg.c, cfg.renorm,
+                         torch.bfloat16, gpu, cfg.scoring, cfg.routing)
+    saved = layer.saved_buffer()
+    saved.fill_(0xFF)  # NaN patterns wherever the forward would fail to write
+    a = layer.forward(d_.x, d_.W_r, d_.W_gate, d_.W_up, d_.W_down, d_.b, d_.shared_fused(), cfg.lam,
+                      cfg.gamma)
+    b = layer.forward(d_.x, d_.W_r, d_.W_gate, d_.W_up, d_.W_down, d_.b, d_.shared_fused(), cfg.lam,
+                      cfg.gamma, out=layer.alloc_outputs(with_bias=d_.b is not None), saved=saved)
+    torch.cuda.synchronize()
+    keys = ["y", "counts", "f", "P", "aux", "z", "diag"]
+    if cfg.routing == "token":
+        keys += ["topk_idx", "topk_w"]
+    for key in keys:
+        assert torch.equal(a[key], b[key]), key
+    dy = torch.randn(cfg.T, cfg.d, generator=torch.Generator().manual_seed(11)).to(torch.bfloat16)
+    kwargs = dict(b=d_.b, shared=d_.shared_fused(), c=cfg.c, renorm=cfg.renorm, lam=cfg.lam,
+                  z_coef=0.3, scoring=cfg.scoring, routing=cfg.routing)
+    g0 = moe.moe_layer_backward(d_.x, d_.W_r, d_.W_gate, d_.W_up, d_.W_down, dy.to(gpu), cfg.k,
+                                **kwargs)
+    g1 = moe.moe_layer_backward(d_.x, d_.W_r, d_.W_gate, d_.W_up, d_.W_down, dy.to(gpu), cfg.k,
+                                saved=saved, **kwargs)
+    torch.cuda.synchronize()
+    for key, v in g0.items():
+        if key == "topk_idx" and cfg.routing == "expert":
+            continue  # not written under expert choice
+        assert torch.equal(v, g1[key]), key
+
+
 @pytest.mark.parametrize("base,kw", LAYER_BW_EC_CASES)
 def test_layer_backward_expert_choice(gpu, base, kw):
     """The expert-choice backward against the oracle's (its own selection: each case is checked to
