@@ -220,7 +220,8 @@ LossBackwardPlan plan_loss_backward(Carve& c, const moe_shape* s) {
 }
 
 // The backward recomputes the forward (LayerPlan) and keeps, per routed row, the gate and up
-// pre-activations (dtype) and the fp32 gradients d out, dh, dG, dU and dx_row.
+// pre-activations (fp32; recomputed, or read from the buffer a training forward filled) and the
+// fp32 gradients d out, dh, dG, dU and dx_row.
 struct LayerBackwardPlan {
   LayerPlan f;
   float* cols;                    // [2][E][T] logits and scores
