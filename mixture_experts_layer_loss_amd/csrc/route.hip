@@ -383,7 +383,7 @@ constexpr int kLogitsStride = MOE_E_MAX + 4;
 // bf16: logits on MFMA. A block owns TB = 16 MB tokens; its eight waves split the hidden dimension
 // into eight contiguous ranges of 32-wide k-steps and load their MFMA operands straight from
 // global memory (x rows of the block's tokens, W_r rows of every expert), so no barrier sits in
-// the k loop. The four partial logit tiles are summed in LDS in wave order (fixed, so results are
+// the k loop. The eight partial logit tiles are summed in LDS in wave order (fixed, so results are
 // reproducible). Fragment layout of v_mfma_f32_16x16x32_bf16: lane l supplies row (l % 16) of A
 // and column (l % 16) of B with 8 consecutive k of k-group (l / 16); result element
 // (row 4*(l/16) + j, column l % 16) lands in lane l, register j.
@@ -450,8 +450,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
         acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], bb[j], acc[m][j], 0, 0, 0);
   };
   // a ring of PF k-steps of operands in registers: the loads run PF steps ahead of the MFMAs, so a
-  // wave's whole K range (16 steps at d = 4096) is in flight after two turns of the ring
-  constexpr int PF = 8;
+  // wave's whole K range (16 steps at d = 4096) is in flight at once
+  constexpr int PF = 16;
   bf16x8 ra[PF][MB], rb[PF][NEBG];
   static_for<0, PF>([&](auto pc) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
@@ -468,25 +468,32 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
     });
   }
 
-  // sum the partial tiles of each expert group in wave (K) order; groups own disjoint columns
-  for (int w = 0; w < NW; ++w) {
-    if (wave == w) {
+  // sum the partial tiles of each expert group in wave (K) order; groups own disjoint columns.
+  // Every wave parks its tile in LDS, then each element is summed over the K waves in order.
+  __shared__ float part[NW * TB * 16 * NEBG];
 #pragma unroll
-      for (int m = 0; m < MB; ++m)
+  for (int m = 0; m < MB; ++m)
 #pragma unroll
-        for (int j = 0; j < NEBG; ++j) {
-          const int col = (grp * NEBG + j) * 16 + r16;
-          if ((grp * NEBG + j) < NEB) {
+    for (int j = 0; j < NEBG; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              float* dst = &L[(m * 16 + kg * 4 + r) * kLogitsStride + col];
-              *dst = (kw == 0) ? acc[m][j][r] : *dst + acc[m][j][r];
-            }
-          }
-        }
+      for (int r = 0; r < 4; ++r)
+        part[((wave * MB + m) * NEBG + j) * 256 + (kg * 4 + r) * 16 + r16] = acc[m][j][r];
+  __syncthreads();
+  for (int i = tid; i < NG * MB * NEBG * 256; i += kRouteThreads) {
+    const int g = i / (MB * NEBG * 256), rem = i % (MB * NEBG * 256);
+    const int m = rem / (NEBG * 256), j = (rem / 256) % NEBG, e16 = rem % 256;
+    const int row = e16 / 16, c16 = e16 % 16;
+    if (g * NEBG + j < NEB) {
+      float v = 0.f;
+      for (int q = 0; q < NWK; ++q) {
+        const int w = g * NWK + q;
+        v = (q == 0) ? part[((w * MB + m) * NEBG + j) * 256 + row * 16 + c16]
+                     : v + part[((w * MB + m) * NEBG + j) * 256 + row * 16 + c16];
+      }
+      L[(m * 16 + row) * kLogitsStride + (g * NEBG + j) * 16 + c16] = v;
     }
-    __syncthreads();
   }
+  __syncthreads();
   for (int i = tid; i < TB * 4; i += kRouteThreads) {
     const int e = ((E + 3) & ~3) - 4 + (i & 3);
     if (e >= E) L[(i >> 2) * kLogitsStride + e] = -INFINITY;
