@@ -296,6 +296,8 @@ moe_status moe_balance_loss_backward(const moe_shape* s, const void* x, const vo
  *     still are: they are deterministic, so the rows match). The gradients are bit-identical
  *     either way. Read only; bf16 layers only (fp32: MOE_ERR_UNSUPPORTED); 16-byte aligned.
  *   ws device workspace of moe_workspace_size(s, MOE_CALL_LAYER_BACKWARD) bytes
+ * bf16 layers read the weights in place; one expert's W_gate and W_up together (4 M d bytes), and
+ * the shared experts' (4 S M d bytes), must stay under 4 GiB (MOE_ERR_UNSUPPORTED otherwise).
  */
 moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r, const float* b,
                               const void* W_gate, const void* W_up, const void* W_down,

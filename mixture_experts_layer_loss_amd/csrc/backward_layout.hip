@@ -1,7 +1,7 @@
-// Operand layouts for the bf16 backward products on MFMA. The grouped GEMM reads both operands
-// along the reduction dimension, so the backward feeds it transposed copies:
-//   - the weights, once per call: W_down[e]^T [M][d] for P = dy W_down[e], and [W_gate[e] W_up[e]]^T
-//     side by side [d][2M] for dx_row = dG W_gate[e] + dU W_up[e] (one product over K = 2M);
+// Operand layouts for the bf16 backward products on MFMA. The products that reduce over d or M
+// against a weight (P = dy W_down[e], dx_row = dG W_gate[e] + dU W_up[e]) read the weights in place
+// (the grouped GEMM's K-major B path); the weight gradients reduce over rows, so the backward feeds
+// them transposed copies:
 //   - the row operands of the weight gradients, with the rows of each expert as columns, each
 //     expert's column range padded with zeros to a multiple of 64: the gathered dy^T, (w h)^T,
 //     dG^T, dU^T and the gathered x^T (dW_down[e] = sum over its rows of dy_t^T (w h), dW_gate[e] =
@@ -19,43 +19,6 @@ namespace {
 
 constexpr int TT = 64;       // tile edge
 constexpr int TP = TT + 2;   // LDS row pitch (elements)
-
-// dst[b][c][coff + r] = src[b][r][c]; rows, cols, ldd and coff multiples of 8. No LDS: lane
-// (rc, cc) of a wave loads the 8 x 8 block of rows 8 rc.. and columns 8 cc.. of the wave's 64 x 64
-// tile (eight 16-byte loads, each row's 8 lanes contiguous), transposes it in registers and stores
-// eight 16-byte rows of dst (each dst row's 8 lanes contiguous). A block of 4 waves covers 256 rows.
-__device__ __forceinline__ uint32_t pick16(uint32_t a, uint32_t b, int hi) {
-  // (half `hi` of a) | (half `hi` of b) << 16
-  return hi ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-}
-
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __restrict__ src,
-                                                              int rows, int cols,
-                                                              int64_t src_batch,
-                                                              bf16_t* __restrict__ dst, int ldd,
-                                                              int coff, int64_t dst_batch) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rc = lane >> 3, cc = lane & 7;
-  const int r = blockIdx.y * 256 + wave * 64 + rc * 8;
-  const int c = blockIdx.x * 64 + cc * 8;
-  if (r >= rows || c >= cols) return;
-  const bf16_t* s = src + static_cast<int64_t>(blockIdx.z) * src_batch;
-  bf16_t* o = dst + static_cast<int64_t>(blockIdx.z) * dst_batch;
-  uint32_t in[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint4 v = *reinterpret_cast<const uint4*>(s + static_cast<int64_t>(r + i) * cols + c);
-    in[i][0] = v.x; in[i][1] = v.y; in[i][2] = v.z; in[i][3] = v.w;
-  }
-#pragma unroll
-  for (int jc = 0; jc < 8; ++jc) {
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) w[q] = pick16(in[2 * q][jc >> 1], in[2 * q + 1][jc >> 1], jc & 1);
-    *reinterpret_cast<uint4*>(o + static_cast<int64_t>(c + jc) * ldd + coff + r) =
-        make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
 
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float* v);
@@ -161,18 +124,6 @@ __global__ __launch_bounds__(256) void swiglu_bw_cat_kernel(int64_t count, int M
 }
 
 }  // namespace
-
-hipError_t launch_transpose_bf16(const void* src, int rows, int cols, int64_t src_batch,
-                                 int batch, void* dst, int ldd, int coff, int64_t dst_batch,
-                                 hipStream_t st) {
-  if (rows <= 0 || cols <= 0 || batch <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(cdiv(cols, 64)), static_cast<unsigned>(cdiv(rows, 256)),
-                  static_cast<unsigned>(batch));
-  hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, st,
-                     static_cast<const bf16_t*>(src), rows, cols, src_batch,
-                     static_cast<bf16_t*>(dst), ldd, coff, dst_batch);
-  return hipGetLastError();
-}
 
 hipError_t launch_pad_transpose(int dtype_src, const void* src, const float* src2, int64_t ld_src,
                                 const int32_t* gather, const float* scale,

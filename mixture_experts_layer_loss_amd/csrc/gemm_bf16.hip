@@ -117,7 +117,7 @@ __device__ __forceinline__ void sched_substep_wl() {
 // KTAIL: K is not a multiple of 64 (the last k-slice is zero-padded). Row r of A starts at
 // A + r lda (gathered: A + gather[r] lda), row n of group g's B at B + g group_stride + n ldb, and
 // output row r at C + r ldc.
-template <int EPI, bool KTAIL, bool GATHER, int MR>
+template <int EPI, bool KTAIL, bool GATHER, int MR, bool BKN = false>
 __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __restrict__ A,
                                          int lda, const int32_t* __restrict__ gather,
                                          const bf16_t* __restrict__ B0,
@@ -164,6 +164,21 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
     const int rb_ = PAIRED ? (r & (BN / 2 - 1)) : r;
     b_off[i] = static_cast<uint32_t>((min(rb_, b_rows - 1) * ldb + kc_t) * 2);
   }
+  // BKN: B is [K][N] (N contiguous, row stride ldb; with B1, rows K/2.. come from B1): chunk
+  // i * NT + tid of a 64 x 256 slice is row 16 i + tid / 32, columns n0 + 8 (tid % 32). Nothing
+  // loaded is zeroed: a column past N only reaches output columns that are never stored, and a
+  // row past K (clamped to row K - 1, so finite) only meets A chunks that are zero.
+  static_assert(!BKN || (EPI == 2 && NT == 512), "K-major B is wired for the fp32-output products");
+  const char* bk0 = reinterpret_cast<const char*>(B0 + static_cast<int64_t>(g) * group_stride);
+  const int khalf = B1 != nullptr ? K / 2 : K;
+  const uint32_t ldb2 = static_cast<uint32_t>(ldb) * 2u;
+  // byte distance from row kk of B0's group to row kk - K/2 of B1's (rows K/2.. only)
+  const int64_t dB = (BKN && B1 != nullptr)
+                         ? (reinterpret_cast<const char*>(B1 + static_cast<int64_t>(g) * group_stride) -
+                            bk0) - static_cast<int64_t>(khalf) * ldb2
+                         : 0;
+  const int bk_r = tid >> 5;
+  const uint32_t bk_cb = static_cast<uint32_t>(min(n0 + (tid & 31) * 8, N - 8)) * 2u;
   u32x4 ra[ACH], rb[BCH];
   auto gload = [&](int k0) __attribute__((always_inline)) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -176,11 +191,20 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
       const u32x4 v = *reinterpret_cast<const u32x4*>(ap);
       ra[i] = KTAIL ? (in ? v : zero) : v;
     }
+    if constexpr (BKN) {
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-      const char* bb = (PAIRED && i >= BCH / 2) ? b_base1 : b_base0;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(bb + (b_off[i] + kb));
-      rb[i] = KTAIL ? (in ? v : zero) : v;
+      for (int i = 0; i < BCH; ++i) {
+        const int kk = KTAIL ? min(k0 + 16 * i + bk_r, K - 1) : k0 + 16 * i + bk_r;
+        const char* bp = bk0 + (static_cast<uint32_t>(kk) * ldb2 + bk_cb) + (kk >= khalf ? dB : 0);
+        rb[i] = *reinterpret_cast<const u32x4*>(bp);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < BCH; ++i) {
+        const char* bb = (PAIRED && i >= BCH / 2) ? b_base1 : b_base0;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(bb + (b_off[i] + kb));
+        rb[i] = KTAIL ? (in ? v : zero) : v;
+      }
     }
   };
   // LDS byte offset of this thread's chunk of row r0; row r0 + RS i sits RS * 128 B further on
@@ -191,9 +215,19 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
     unsigned char* sa = lds + stage * kStageBytes + st_off;
 #pragma unroll
     for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4*>(sa + i * RS * BK * 2) = ra[i];
+    if constexpr (BKN) {
+      // [64 k][256 n] slice, 512-byte rows, 16-byte chunk c of row r at chunk c ^ 4 (r & 3)
+      // (a 64-byte step, so the 32-byte pieces of a transposing read's two column halves land on
+      // distinct banks); a thread's chunks are rows 16 apart, so r & 3 is the same for all of them
+      unsigned char* sb = lds + stage * kStageBytes + kBBytes + bk_r * 512 +
+                          (((tid & 31) ^ ((bk_r & 3) << 2)) << 4);
 #pragma unroll
-    for (int i = 0; i < BCH; ++i)
-      *reinterpret_cast<u32x4*>(sa + kBBytes + i * RS * BK * 2) = rb[i];
+      for (int i = 0; i < BCH; ++i) *reinterpret_cast<u32x4*>(sb + i * 16 * 512) = rb[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < BCH; ++i)
+        *reinterpret_cast<u32x4*>(sa + kBBytes + i * RS * BK * 2) = rb[i];
+    }
   };
 
   f32x16 acc[MI][NJ];
@@ -218,15 +252,43 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
   for (int j = 0; j < NJ; ++j)
     brow[j] = PAIRED ? ((j < NJ / 2 ? 0 : BN / 2) + wn * (G::WCOLS / 2) + (j % (NJ / 2)) * 32)
                        : (wn * G::WCOLS + j * 32);
+  // BKN fragments by transposing reads (ds_read_b64_tr_b16): in each group of 16 lanes, lane
+  // 4 q + a reads 4 columns (n_base + 4 a ..) of row k_base + q, and lane i receives the 4 rows
+  // k_base .. k_base + 3 of column n_base + i. Lane l's 32x32x16 B operand (8 k of column
+  // l % 32) is two such reads, rows 16 sub + 8 (l / 32) + {0..3} and {4..7}.
+  uint32_t tb_off[BKN ? NJ : 1];
+  if constexpr (BKN) {
+    const int g4 = lane >> 4, i16 = lane & 15;
+    const int trow = 8 * (g4 >> 1) + (i16 >> 2);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int col = brow[j] + 16 * (g4 & 1) + 4 * (i16 & 3);
+      tb_off[j] = static_cast<uint32_t>(kBBytes + trow * 512 +
+                                        (((col >> 3) ^ ((i16 >> 2) << 2)) << 4) +
+                                        (((col >> 2) & 1) << 3));
+    }
+  }
   bf16x8 fa[2][MI], fb[2][NJ];
   auto lfrag = [&](int set, int stage, int sub) __attribute__((always_inline)) {
     const unsigned char* sa = lds + stage * kStageBytes + fo[sub];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
       fa[set][i] = *reinterpret_cast<const bf16x8*>(sa + (wm * G::WROWS + i * 32) * BK * 2);
+    if constexpr (BKN) {
+      typedef short v4i16 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      fb[set][j] = *reinterpret_cast<const bf16x8*>(sa + kBBytes + brow[j] * BK * 2);
+      for (int j = 0; j < NJ; ++j) {
+        const unsigned char* pb = lds + stage * kStageBytes + tb_off[j] + sub * 16 * 512;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(pb));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(pb + 4 * 512));
+        fb[set][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        fb[set][j] = *reinterpret_cast<const bf16x8*>(sa + kBBytes + brow[j] * BK * 2);
+    }
   };
   auto mfmas = [&](int set) __attribute__((always_inline)) {
 #pragma unroll
@@ -235,7 +297,7 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
       for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
   };
-  constexpr int NMF = MI * NJ, NR = MI + NJ, NX = ACH + BCH;
+  constexpr int NMF = MI * NJ, NR = MI + (BKN ? 2 * NJ : NJ), NX = ACH + BCH;
 
   // ---- one k-step (64 of K) = 4 sub-steps on stage `cur`:
   //   sub 0: read fragments of sub 1, store stage cur^1 (no wave reads it since the last
@@ -376,7 +438,7 @@ __device__ __forceinline__ int find_group(const int32_t* __restrict__ table, int
 
 // tile_off: three tables of groups + 1 entries: 256-row tiles, 128-row tiles, 64-row tiles.
 // Blocks [0, main_blocks) serve the 256-row tiles, the rest the smaller ones.
-template <int EPI, bool KTAIL, bool GATHER>
+template <int EPI, bool KTAIL, bool GATHER, bool BKN = false>
 __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ gather,
     const int32_t* __restrict__ offsets,
@@ -400,7 +462,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     const int nb = static_cast<int>(local / mt_g), mt = static_cast<int>(local % mt_g);
     const int row_begin = offsets[g] + mt * 256;
     const int rows = min(256, offsets[g + 1] - row_begin);
-    run_tile<EPI, KTAIL, GATHER, 256>(lds, A, K, gather, B0, B1, group_stride, K, N, K, C, N, C2,
+    run_tile<EPI, KTAIL, GATHER, 256, BKN>(lds, A, K, gather, B0, B1, group_stride, BKN ? N : K, N,
+                                           K, C, N, C2,
                                       C3, g, row_begin, rows, nb * BNO);
     return;
   }
@@ -420,10 +483,12 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
   const int rows = rows_g & 255;
   const int n0 = static_cast<int>(local) * BNO;
   if (table == t128)
-    run_tile<EPI, KTAIL, GATHER, 128>(lds, A, K, gather, B0, B1, group_stride, K, N, K, C, N, C2,
+    run_tile<EPI, KTAIL, GATHER, 128, BKN>(lds, A, K, gather, B0, B1, group_stride, BKN ? N : K, N,
+                                           K, C, N, C2,
                                       C3, g, row_begin, rows, n0);
   else
-    run_tile<EPI, KTAIL, GATHER, 64>(lds, A, K, gather, B0, B1, group_stride, K, N, K, C, N, C2,
+    run_tile<EPI, KTAIL, GATHER, 64, BKN>(lds, A, K, gather, B0, B1, group_stride, BKN ? N : K, N,
+                                          K, C, N, C2,
                                      C3, g, row_begin, rows, n0);
 }
 
@@ -463,7 +528,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_gemm_kernel(const bf16_t* __restr
                                  min(256, Ma - m0), n0);
 }
 
-template <int EPI, bool KTAIL, bool GATHER>
+template <int EPI, bool KTAIL, bool GATHER, bool BKN = false>
 hipError_t launch_gemm_t(const bf16_t* A, const int32_t* gather, const int32_t* offsets,
                          const int32_t* tile_off,
                          int groups, int64_t max_tiles, const bf16_t* B0, const bf16_t* B1,
@@ -481,29 +546,29 @@ hipError_t launch_gemm_t(const bf16_t* A, const int32_t* gather, const int32_t* 
   static std::atomic<bool> attr_set{false};
   if (!attr_set.load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&grouped_gemm_kernel<EPI, KTAIL, GATHER>),
+        reinterpret_cast<const void*>(&grouped_gemm_kernel<EPI, KTAIL, GATHER, BKN>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     attr_set.store(true, std::memory_order_release);
   }
   if (max_tiles <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((grouped_gemm_kernel<EPI, KTAIL, GATHER>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((grouped_gemm_kernel<EPI, KTAIL, GATHER, BKN>), dim3(static_cast<unsigned>(grid)),
                      dim3(NT), lds, st, A, gather, offsets, tile_off, groups,
                      static_cast<int>(main_blocks), B0, B1, group_stride, N, K, C, C2, C3);
   return hipGetLastError();
 }
 
-template <int EPI, bool GATHER>
+template <int EPI, bool GATHER, bool BKN = false>
 hipError_t launch_gemm(const bf16_t* A, const int32_t* gather, const int32_t* offsets,
                        const int32_t* tile_off, int groups, int64_t max_tiles, const bf16_t* B0,
                        const bf16_t* B1, int64_t group_stride, int N, int K, bf16_t* C,
                        hipStream_t st, float* C2 = nullptr, float* C3 = nullptr) {
   if (K % BK == 0)
-    return launch_gemm_t<EPI, false, GATHER>(A, gather, offsets, tile_off, groups, max_tiles, B0,
-                                             B1, group_stride, N, K, C, C2, C3, st);
-  return launch_gemm_t<EPI, true, GATHER>(A, gather, offsets, tile_off, groups, max_tiles, B0, B1,
-                                          group_stride, N, K, C, C2, C3, st);
+    return launch_gemm_t<EPI, false, GATHER, BKN>(A, gather, offsets, tile_off, groups, max_tiles,
+                                                  B0, B1, group_stride, N, K, C, C2, C3, st);
+  return launch_gemm_t<EPI, true, GATHER, BKN>(A, gather, offsets, tile_off, groups, max_tiles, B0,
+                                               B1, group_stride, N, K, C, C2, C3, st);
 }
 
 }  // namespace
@@ -579,6 +644,27 @@ hipError_t launch_gemm_plain_bf16(int groups, const void* rows, const int32_t* g
                                 group_stride, N, K, Cp, st);
   return launch_gemm<2, false>(A, nullptr, offsets, tile_off, groups, max_tiles, Bp, nullptr,
                                group_stride, N, K, Cp, st);
+}
+
+// C[r] = A_r B_g for the rows of group g with B_g [K][N] row-major (N contiguous; no transposed
+// copy): group g's B is B0 + g group_stride, and with B1 != NULL its rows K/2 .. K - 1 are those
+// of B1 + g group_stride (so [dG dU] [W_gate; W_up] runs over K = 2M in one launch). fp32 output.
+hipError_t launch_gemm_kn_bf16(int groups, const void* rows, const int32_t* gather,
+                               const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
+                               const void* B0, const void* B1, int64_t group_stride, int N, int K,
+                               float* C, hipStream_t st) {
+  const bf16_t* A = static_cast<const bf16_t*>(rows);
+  const bf16_t* b0 = static_cast<const bf16_t*>(B0);
+  const bf16_t* b1 = static_cast<const bf16_t*>(B1);
+  bf16_t* Cp = reinterpret_cast<bf16_t*>(C);  // holds floats (EPI 2)
+  // 16-byte column chunks, and a group's row offsets (K rows of N) in 32 bits
+  if (N < 8 || N % 8 != 0 || static_cast<int64_t>(K) * N * 2 >= (int64_t{1} << 32))
+    return hipErrorInvalidValue;
+  if (gather != nullptr)
+    return launch_gemm<2, true, true>(A, gather, offsets, tile_off, groups, max_tiles, b0, b1,
+                                      group_stride, N, K, Cp, st);
+  return launch_gemm<2, false, true>(A, nullptr, offsets, tile_off, groups, max_tiles, b0, b1,
+                                     group_stride, N, K, Cp, st);
 }
 
 // C_g = A_g B_g^T over each group's zero-padded column range (weight gradients, fp32 output)

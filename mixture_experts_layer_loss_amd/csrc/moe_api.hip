@@ -232,12 +232,12 @@ struct LayerBackwardPlan {
   int ks_w;
   float *Gs, *Us;                 // shared experts [T, S M] fp32
   float *hs, *dhs, *dGs, *dUs, *dxs;   // [T, S M] and [T, d]
-  // bf16 layers (MFMA products): transposed weights, [dG | dU] rows, and the weight-gradient
+  // bf16 layers (MFMA products): the [dG | dU] rows, and the weight-gradient
   // operands with each group's rows as a zero-padded column range (ldp / ldps columns)
   int64_t ldp, ldps;
   float* wrow;                                            // gate of each kept row
-  void *WdT, *WguT, *dGU, *whT, *dGT, *dUT, *dyT, *xT;    // routed experts
-  void *WsdT, *WsguT, *dGUs, *hsT, *dGsT, *dUsT, *dysT, *xsT;  // shared experts
+  void *dGU, *whT, *dGT, *dUT, *dyT, *xT;        // routed experts
+  void *dGUs, *hsT, *dGsT, *dUsT, *dysT, *xsT;   // shared experts
 };
 LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
   LayerBackwardPlan p;
@@ -263,11 +263,9 @@ LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
   p.ldps = 64 * cdiv(s->T, 64);
   const size_t lp = static_cast<size_t>(p.ldp), lps = static_cast<size_t>(p.ldps);
   p.wrow = mfma || expert_choice(s) ? c.take<float>(R) : nullptr;
-  p.WdT = p.WguT = p.dGU = p.whT = p.dGT = p.dUT = p.dyT = p.xT = nullptr;
-  p.WsdT = p.WsguT = p.dGUs = p.hsT = p.dGsT = p.dUsT = p.dysT = p.xsT = nullptr;
+  p.dGU = p.whT = p.dGT = p.dUT = p.dyT = p.xT = nullptr;
+  p.dGUs = p.hsT = p.dGsT = p.dUsT = p.dysT = p.xsT = nullptr;
   if (mfma) {
-    p.WdT = c.take<bf16_t>(E * M * d);
-    p.WguT = c.take<bf16_t>(E * d * 2 * M);
     p.dGU = c.take<bf16_t>(R * 2 * M);
     p.whT = c.take<bf16_t>(M * lp);
     p.dGT = c.take<bf16_t>(M * lp);
@@ -287,8 +285,6 @@ LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
     p.dUs = mfma ? nullptr : c.take<float>(T * SM);
     p.dxs = c.take<float>(T * d);
     if (mfma) {
-      p.WsdT = c.take<bf16_t>(SM * d);
-      p.WsguT = c.take<bf16_t>(d * 2 * SM);
       p.dGUs = c.take<bf16_t>(T * 2 * SM);
       p.hsT = c.take<bf16_t>(SM * lps);
       p.dGsT = c.take<bf16_t>(SM * lps);
@@ -657,6 +653,11 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
     return MOE_ERR_INVALID_ARGUMENT;
   if (isnan(lambda) || isnan(z_coef)) return MOE_ERR_INVALID_ARGUMENT;
   if (s->T * static_cast<int64_t>(s->E) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  // bf16 layers read an expert's [W_gate; W_up] (and the shared experts') in place, with 32-bit
+  // byte offsets inside it
+  const int64_t gu_bytes = static_cast<int64_t>(s->M) * s->d * 4;
+  if (s->dtype == MOE_BF16 && (gu_bytes >= (int64_t{1} << 32) || s->S * gu_bytes >= (int64_t{1} << 32)))
+    return MOE_ERR_UNSUPPORTED;
   const void* tensors[] = {x, W_r, W_gate, W_up, W_down, dy};
   for (const void* t : tensors)
     if (!aligned16(t)) return MOE_ERR_INVALID_ARGUMENT;
@@ -728,18 +729,10 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
                      hs);
   if (e == hipSuccess) e = launch_schedule(s->E, f.offsets, p.tile64, 64, hs);
   const int d = s->d, M = s->M;
-  if (mfma) {  // weights transposed for the products that reduce over d or M
-    if (e == hipSuccess)  // W_down[e]^T [M][d]
-      e = launch_transpose_bf16(W_down, d, M, dM, s->E, p.WdT, d, 0, dM, hs);
-    if (e == hipSuccess)  // [W_gate[e] W_up[e]]^T [d][2M]
-      e = launch_transpose_bf16(W_gate, M, d, dM, s->E, p.WguT, 2 * M, 0, 2 * dM, hs);
-    if (e == hipSuccess)
-      e = launch_transpose_bf16(W_up, M, d, dM, s->E, p.WguT, 2 * M, M, 2 * dM, hs);
-  }
   // ---- combine: P_row = dy_t W_down[e] gives d w = <P, h> and dh = w P, hence dG, dU
-  if (e == hipSuccess && mfma)
-    e = launch_gemm_plain(s->dtype, s->E, dy, f.perm_token, f.offsets, f.tile_off, max_tiles,
-                          p.WdT, dM, M, d, p.P, hs);
+  if (e == hipSuccess && mfma)  // W_down[e] read in place as the [d][M] B operand
+    e = launch_gemm_kn_bf16(s->E, dy, f.perm_token, f.offsets, f.tile_off, max_tiles, W_down,
+                            nullptr, dM, M, d, p.P, hs);
   else if (e == hipSuccess)
     e = launch_nn_gemm(s->dtype, s->dtype, false, dy, nullptr, f.perm_token, f.offsets, p.tile64,
                        s->E, max_t64, W_down, nullptr, dM, s->M, s->d, p.P, hs);
@@ -758,9 +751,9 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
                          p.dw, f.n, stats_fden(s), lambda, z_coef, p.dl, p.dlT, hs);
   // ---- routed experts
   if (mfma) {
-    if (e == hipSuccess)  // dx_row = [dG dU] [W_gate[e] W_up[e]]^T^T over K = 2M
-      e = launch_gemm_plain(s->dtype, s->E, p.dGU, nullptr, f.offsets, f.tile_off, max_tiles,
-                            p.WguT, 2 * dM, d, 2 * M, p.dxr, hs);
+    if (e == hipSuccess)  // dx_row = [dG dU] [W_gate[e]; W_up[e]] over K = 2M, weights in place
+      e = launch_gemm_kn_bf16(s->E, p.dGU, nullptr, f.offsets, f.tile_off, max_tiles, W_gate,
+                              W_up, dM, d, 2 * M, p.dxr, hs);
     // weight-gradient operands: each expert's rows as a zero-padded column range
     const int64_t lp = p.ldp;
     const bf16_t* dGU = static_cast<const bf16_t*>(p.dGU);
@@ -831,19 +824,13 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
     if (mfma) {
       const int64_t lps = p.ldps;
       const bf16_t* dGUs = static_cast<const bf16_t*>(p.dGUs);
-      if (e == hipSuccess)  // Ws_down^T [SM][d]
-        e = launch_transpose_bf16(Ws_down, d, SM, 0, 1, p.WsdT, d, 0, 0, hs);
-      if (e == hipSuccess)  // [Ws_gate Ws_up]^T [d][2 SM]
-        e = launch_transpose_bf16(Ws_gate, SM, d, 0, 1, p.WsguT, 2 * SM, 0, 0, hs);
-      if (e == hipSuccess)
-        e = launch_transpose_bf16(Ws_up, SM, d, 0, 1, p.WsguT, 2 * SM, SM, 0, hs);
-      if (e == hipSuccess)  // dhs = dy Ws_down
-        e = launch_gemm_plain(s->dtype, 1, dy, nullptr, f.sh_offsets, f.sh_tile_off, sh_tiles,
-                              p.WsdT, 0, SM, d, p.dhs, hs);
+      if (e == hipSuccess)  // dhs = dy Ws_down (Ws_down [d][SM] read in place)
+        e = launch_gemm_kn_bf16(1, dy, nullptr, f.sh_offsets, f.sh_tile_off, sh_tiles, Ws_down,
+                                nullptr, 0, SM, d, p.dhs, hs);
       if (e == hipSuccess) e = launch_swiglu_bw_cat(s->T, SM, p.dhs, p.Gs, p.Us, p.dGUs, hs);
-      if (e == hipSuccess)
-        e = launch_gemm_plain(s->dtype, 1, p.dGUs, nullptr, f.sh_offsets, f.sh_tile_off, sh_tiles,
-                              p.WsguT, 0, d, 2 * SM, p.dxs, hs);
+      if (e == hipSuccess)  // dxs = [dGs dUs] [Ws_gate; Ws_up] over K = 2 SM
+        e = launch_gemm_kn_bf16(1, p.dGUs, nullptr, f.sh_offsets, f.sh_tile_off, sh_tiles, Ws_gate,
+                                Ws_up, 0, d, 2 * SM, p.dxs, hs);
       const int64_t pt = cdiv(s->T, 64);
       const int32_t* so = f.sh_offsets;
       if (e == hipSuccess)

@@ -172,10 +172,6 @@ hipError_t launch_bw_dx_ec(int64_t T, int d, int E, const int32_t* row_of, const
                            const float* dx_sh, float* dx, hipStream_t st);
 
 // bf16 backward on MFMA (backward_layout.hip, gemm_bf16.hip).
-// dst[b][c][coff + r] = src[b][r][c] for batch matrices [rows][cols] (sizes multiples of 8).
-hipError_t launch_transpose_bf16(const void* src, int rows, int cols, int64_t src_batch,
-                                 int batch, void* dst, int ldd, int coff, int64_t dst_batch,
-                                 hipStream_t st);
 // dst [cols][ldp] bf16: column p of group g (64 kt[g] <= p < 64 kt[g+1]) = source row
 // i = offsets[g] + p - 64 kt[g] (row gather[i] of src when gather != NULL), times scale[i] when
 // scale != NULL; zeros past the group's rows. With src2 != NULL (fp32 only) the source value is
@@ -188,6 +184,11 @@ hipError_t launch_pad_transpose(int dtype_src, const void* src, const float* src
 // dGU [R][2M] bf16 = [dh U SiLU'(G) | dh SiLU(G)] from fp32 [R][M] inputs
 hipError_t launch_swiglu_bw_cat(int64_t R, int M, const float* dh, const float* G, const float* U,
                                 void* dGU, hipStream_t st);
+// C[r] (fp32) = A_r B_g with B_g [K][N] (N contiguous); with B1, rows K/2.. of B_g come from B1
+hipError_t launch_gemm_kn_bf16(int groups, const void* rows, const int32_t* gather,
+                               const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
+                               const void* B0, const void* B1, int64_t group_stride, int N, int K,
+                               float* C, hipStream_t st);
 // h as launch_gemm_up_bf16 writes it, plus G and U as launch_gemm_gu_f32out_bf16 writes them
 hipError_t launch_gemm_up_save_bf16(int groups, int d, int Mg, const void* rows,
                                     const int32_t* gather, const int32_t* offsets,

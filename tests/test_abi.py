@@ -238,6 +238,13 @@ def test_layer_backward_rejects_before_launch():
                                 None) == 1
     bad = moe.make_shape(64, 128, 8, 9, 256)
     assert call(shape=ctypes.byref(bad)) == 1
+    # bf16 weights are read in place with 32-bit offsets inside one expert's [W_gate; W_up]
+    big = moe.make_shape(64, 4096, 8, 2, 262144)                 # 4 M d = 4 GiB
+    assert call(shape=ctypes.byref(big), ws_bytes=0) == 2
+    big_shared = moe.make_shape(64, 4096, 8, 2, 131072, S=2)     # 4 S M d = 4 GiB
+    assert call(shape=ctypes.byref(big_shared), ws_bytes=0) == 2
+    fits = moe.make_shape(64, 4096, 8, 2, 131072, S=1)           # 2 GiB: only the workspace fails
+    assert call(shape=ctypes.byref(fits), ws_bytes=0) == 3
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

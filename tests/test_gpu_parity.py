@@ -279,6 +279,7 @@ LAYER_BW_CASES = [
     ("deepseek_v2", dict(T=150, d=200, M=72, scoring="sigmoid")),  # bias, sigmoid, K tail
     ("mixtral_8x7b", dict(T=100, d=64, M=64, E=6, k=3, renorm=False)),
     ("mixtral_8x7b", dict(T=1024, d=512, M=768)),                 # several 256 x 256 tiles
+    ("mixtral_8x7b", dict(T=120, d=128, M=96)),   # K = 2M = 192, no tail; W_up from mid k-slice
     ("mixtral_8x7b", dict(T=8, d=64, M=64, E=16, k=1)),           # experts without rows
     ("mixtral_8x7b", dict(T=70, d=64, M=64, E=1, k=1)),           # one expert: a dense FFN
     ("mixtral_8x7b", dict(T=50, d=64, M=64, E=4, k=4)),           # k = E
