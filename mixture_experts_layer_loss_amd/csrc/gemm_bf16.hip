@@ -494,9 +494,9 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
 
 // Weight gradients: C_g [Ma][Nb] (fp32) = sum over k in [64 kt[g], 64 kt[g+1]) of A[m][k] B[n][k],
 // for the operands A [Ma][lda] and B [Nb][ldb] whose columns are the rows of the groups, each
-// group padded with zeros to a multiple of 64 (so no k-slice is partial). 256 x 256 output tiles,
-// m fastest (neighbouring tiles share the B slab), dealt to the XCDs in runs; a group without rows
-// gets zeros.
+// group padded with zeros to a multiple of 64 (so no k-slice is partial). 256 x 256 output tiles
+// in bands of 8 m-tiles (neighbouring tiles share A and B slabs), dealt to the XCDs in runs; a group
+// without rows gets zeros.
 __global__ __launch_bounds__(NT, 1) void wgrad_gemm_kernel(const bf16_t* __restrict__ A, int lda,
                                                            const bf16_t* __restrict__ B, int ldb,
                                                            const int32_t* __restrict__ kt,
@@ -511,7 +511,12 @@ __global__ __launch_bounds__(NT, 1) void wgrad_gemm_kernel(const bf16_t* __restr
   if (blockIdx.x / NXCD >= q || L >= ntiles) return;
   const int g = static_cast<int>(L / per_group);
   const int local = static_cast<int>(L % per_group);
-  const int m0 = (local % mt) * 256, n0 = (local / mt) * 256;
+  // bands of kWgBand m-tiles, n fastest within a band's column: the 32 tiles an XCD runs at
+  // once span 8 m x 4 n and read 12 operand slabs instead of 33 (a narrower last band)
+  constexpr int kWgBand = 8;
+  const int band = local / (kWgBand * nt), w = local % (kWgBand * nt);
+  const int bw = min(kWgBand, mt - band * kWgBand);
+  const int m0 = (band * kWgBand + w % bw) * 256, n0 = (w / bw) * 256;
   const int k0 = 64 * kt[g], K = 64 * (kt[g + 1] - kt[g]);
   float* Cg = C + static_cast<int64_t>(g) * Ma * Nb;
   if (K == 0) {
