@@ -730,6 +730,78 @@ def test_layer_pins():
     check_layer()
 
 
+# ------------------------------------------------------------------- combine and shared experts
+
+def check_combine(mod=O):
+    """combine ("MoE：条件计算与路由" §7 eq. (3)) against a sparse-matrix product built by scipy,
+    and against the inline combine of layer_forward."""
+    import scipy.sparse as sp
+    rng = np.random.default_rng(21)
+    T, k, R = 30, 3, 100
+    # distinct rows per slot, about a fifth dropped (-1)
+    row = rng.permutation(R)[: T * k].reshape(T, k).astype(np.int64)
+    row[rng.random((T, k)) < 0.2] = -1
+    w = rng.random((T, k)) + 0.1
+    keep = row >= 0
+    tt, jj = np.nonzero(keep)
+    # one-hot expert outputs (out_perm = I_R): y is the T x R gate matrix W[t, row_tj] = w_tj
+    Wmat = sp.coo_matrix((w[tt, jj], (tt, row[tt, jj])), shape=(T, R)).toarray()
+    y = mod.combine(T, R, row, w, np.eye(R))
+    assert np.array_equal(y, Wmat)
+    # general outputs: y = W out_perm (+ shared), by the sparse product
+    out = rng.standard_normal((R, 9))
+    sh = rng.standard_normal((T, 9))
+    Ws = sp.csr_matrix((w[tt, jj], (tt, row[tt, jj])), shape=(T, R))
+    assert np.allclose(mod.combine(T, 9, row, w, out), Ws @ out, rtol=1e-14, atol=1e-15)
+    assert np.allclose(mod.combine(T, 9, row, w, out, sh), Ws @ out + sh, rtol=1e-14, atol=1e-15)
+    # a token with every slot dropped gets exactly the shared term (0 without it)
+    row[4] = -1
+    assert np.all(mod.combine(T, 9, row, w, out)[4] == 0.0)
+    assert np.array_equal(mod.combine(T, 9, row, w, out, sh)[4], sh[4])
+    # the layer's own combine: out_perm from the dispatch rows, against layer_forward's y
+    x, Wr, Wg, Wu, Wd = _tiny_layer(T=40, E=4, k=2)
+    shs = [(rng.standard_normal((8, 16)), rng.standard_normal((8, 16)), rng.standard_normal((16, 8)))]
+    res = mod.layer_forward(x, Wr, Wg, Wu, Wd, k=2, shared=shs, c=0.5)   # C = 5: drops
+    assert res["overflow"].sum() > 0
+    P = int(res["offsets"][-1])
+    out_perm = np.zeros((P, 16))
+    for e in range(4):
+        lo, hi = int(res["offsets"][e]), int(res["offsets"][e + 1])
+        out_perm[lo:hi] = O.swiglu_expert(x[res["perm_token"][lo:hi]], Wg[e], Wu[e], Wd[e])
+    y2 = mod.combine(40, 16, res["row"], res["topk_w"], out_perm,
+                     O.swiglu_expert(x, *shs[0]))
+    assert np.allclose(y2, res["y"], rtol=1e-13, atol=1e-14)
+
+
+def test_combine_pins():
+    check_combine()
+
+
+def check_shared(mod=O):
+    """Shared experts ("MOE大模型对比篇" §3.3; the DeepseekV3MoE listing of the adg.csdn.net notes
+    page, §四, adds shared_experts(identity) to the routed output): weight 1, every token."""
+    rng = np.random.default_rng(23)
+    x, Wr, Wg, Wu, Wd = _tiny_layer(T=24, E=4, k=2)
+    sh = (rng.standard_normal((8, 16)), rng.standard_normal((8, 16)), rng.standard_normal((16, 8)))
+    ffn = O.swiglu_expert(x, *sh)                 # pinned on its own (check_experts)
+    zero_down = np.zeros_like(Wd)                 # every routed expert outputs 0
+    res = mod.layer_forward(x, Wr, Wg, Wu, zero_down, k=2, shared=[sh])
+    assert np.allclose(res["y"], ffn, rtol=1e-13, atol=1e-14)
+    # S identical shared experts give S times the FFN
+    res3 = mod.layer_forward(x, Wr, Wg, Wu, zero_down, k=2, shared=[sh, sh, sh])
+    assert np.allclose(res3["y"], 3.0 * ffn, rtol=1e-13, atol=1e-13)
+    assert np.allclose(mod.shared_experts(x, [sh]), ffn, rtol=1e-14, atol=0)
+    assert np.all(mod.shared_experts(x, []) == 0.0)
+    # and they add to the routed output: y(shared) - y(no shared) = FFN(x)
+    a = mod.layer_forward(x, Wr, Wg, Wu, Wd, k=2, shared=[sh])["y"]
+    b = mod.layer_forward(x, Wr, Wg, Wu, Wd, k=2)["y"]
+    assert np.allclose(a - b, ffn, rtol=1e-12, atol=1e-13)
+
+
+def test_shared_pins():
+    check_shared()
+
+
 # --------------------------------------------------------------------------------- bias update
 
 def check_bias(mod=O):
@@ -897,6 +969,28 @@ def _sigmoid_unnormalised_P(g, scoring="softmax"):
     return O._f64(g)
 
 
+def _shared_halved(x, shared):
+    return 0.5 * O.shared_experts(x, shared)
+
+
+def _combine_no_gate(T, d, row, w, out_perm, shared_out=None):
+    return O.combine(T, d, row, np.ones_like(O._f64(w)), out_perm, shared_out)
+
+
+def _combine_slots_reversed(T, d, row, w, out_perm, shared_out=None):
+    # rows of the slots taken in reverse order while the gates keep theirs
+    return O.combine(T, d, np.asarray(row)[:, ::-1], w, out_perm, shared_out)
+
+
+def _combine_keeps_dropped(T, d, row, w, out_perm, shared_out=None):
+    # a dropped slot (-1) read as the last row instead of adding nothing
+    y = np.zeros((T, d)) if shared_out is None else O._f64(shared_out).copy()
+    for t in range(T):
+        for j in range(np.asarray(row).shape[1]):
+            y[t] += w[t, j] * out_perm[int(row[t, j])]
+    return y
+
+
 @pytest.mark.parametrize("mutant,checks", [
     (dict(gate_weights=_no_renorm), [check_gates]),
     (dict(top_k=_ties_high), [check_topk]),
@@ -917,6 +1011,10 @@ def _sigmoid_unnormalised_P(g, scoring="softmax"):
     (dict(silu_grad=_silu_grad_wrong), [check_layer_backward_ec]),
     (dict(expert_choice_capacity=lambda c, k, T, E: O.expert_choice_capacity(c, k, T, E) + 1),
      [check_layer_backward_ec]),
+    (dict(shared_experts=_shared_halved), [check_shared]),
+    (dict(combine=_combine_no_gate), [check_combine]),
+    (dict(combine=_combine_slots_reversed), [check_combine]),
+    (dict(combine=_combine_keeps_dropped), [check_combine]),
 ])
 def test_planted_mistakes_are_caught(mutant, checks):
     m = _Mutant(**mutant)
