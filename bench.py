@@ -9,7 +9,14 @@ Prints one JSON line: tokens/s, the dominant kernel's roofline (per-launch durat
 events recorded between the library's stages on its stream), per-stage figures, and the CPU
 oracle timed on a bounded sample of the same workload.
 
+Timing: W untimed warm-up steps, then K steps between two synchronisations with nothing else
+enqueued (``value`` and ``ms_per_step``); then K more steps, each bracketed by two events on the
+stream, for the median and spread of the step time; then K more with the library's stage events
+for the per-stage times and the roofline kernel's per-launch duration (median over the K steps).
+
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --trace-summary kernel_trace.csv [--skip N]   # per-kernel statistics of a
+        rocprofv3 kernel trace, leaving out each kernel's first N launches (the warm-up)
 """
 import argparse
 import hashlib
@@ -31,8 +38,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_up_traffic.json")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -45,7 +52,37 @@ def parse():
     ap.add_argument("--blas-reference", action="store_true",
                     help="also time the vendor GEMM (torch.mm -> hipBLASLt) on one dense matrix of "
                          "each expert product's shape, as a reference point (bf16 only)")
+    ap.add_argument("--trace-summary", default=None,
+                    help="print per-kernel statistics of this rocprofv3 kernel_trace.csv and exit")
+    ap.add_argument("--skip", type=int, default=0,
+                    help="with --trace-summary: leave out each kernel's first N launches")
     return ap.parse_args()
+
+
+def trace_summary(path: str, skip: int) -> None:
+    """Per-kernel launch statistics (µs) of a rocprofv3 kernel trace, each kernel's first `skip`
+    launches (the warm-up) left out; a markdown table on stdout."""
+    import csv
+    import statistics
+    durs = {}
+    with open(path, newline="") as fh:
+        for row in csv.DictReader(fh):
+            name = row["Kernel_Name"]
+            durs.setdefault(name, []).append(
+                (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+    rows = []
+    for name, v in durs.items():
+        kept = v[skip:] if len(v) > skip else v
+        rows.append((sum(kept), name, len(v), len(kept), statistics.mean(kept),
+                     statistics.median(kept), min(kept), max(kept)))
+    rows.sort(reverse=True)
+    total = sum(r[0] for r in rows)
+    print(f"| kernel | launches (kept) | total µs | % | mean µs | median µs | min µs | max µs |")
+    print("|---|---|---|---|---|---|---|---|")
+    for tot, name, n, nk, mean, med, lo, hi in rows:
+        short = name if len(name) < 140 else name[:137] + "..."
+        print(f"| `{short}` | {n} ({nk}) | {tot:.1f} | {100 * tot / total:.2f} | {mean:.2f} | "
+              f"{med:.2f} | {lo:.2f} | {hi:.2f} |")
 
 
 def gemm_source_sha() -> str:
@@ -142,6 +179,9 @@ def cpu_baseline(cfg, inp, seconds: float):
 
 def main():
     args = parse()
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.skip)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the layer on a single MI355X and "
               "has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
@@ -180,23 +220,36 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # stage events for every timed step (recorded by the library on its stream)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.STAGE_COUNT)]
-              for _ in range(args.steps)]
     stream = torch.cuda.current_stream()
-    for evs in events:
-        for ev in evs:
-            ev.record(stream)
-    torch.cuda.synchronize()
-
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        moe.moe_set_stage_events(events[i])
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+
+    # the step-time distribution: every step between two events on the stream
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    for a, b_ in step_ev:
+        a.record(stream)
+        step()
+        b_.record(stream)
+    torch.cuda.synchronize()
+    step_ms_each = np.array([a.elapsed_time(b_) for a, b_ in step_ev])
+
+    # stage events for every step of a third pass (recorded by the library on its stream)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.STAGE_COUNT)]
+              for _ in range(args.steps)]
+    for evs in events:
+        for ev in evs:
+            ev.record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        moe.moe_set_stage_events(events[i])
+        step()
+    torch.cuda.synchronize()
     moe.moe_set_stage_events(None)
 
     # the balance-loss backward through the router (a separate entry point; not part of a step)
@@ -288,11 +341,10 @@ def main():
         blas_ref = blas_reference(cfg, int((out["counts"] - out["overflow"]).sum().item()), dev)
 
     ms_step = (t1 - t0) * 1e3 / args.steps
-    stage_ms = np.zeros(len(moe.STAGES))
-    for evs in events:
-        for s_ in range(1, moe.STAGE_COUNT):
-            stage_ms[s_ - 1] += evs[s_ - 1].elapsed_time(evs[s_])
-    stage_ms /= args.steps
+    # per-stage time of each step; the median over the steps
+    stage_each = np.array([[evs[s_ - 1].elapsed_time(evs[s_]) for s_ in range(1, moe.STAGE_COUNT)]
+                           for evs in events])
+    stage_ms = np.median(stage_each, axis=0)
 
     counts = out["counts"].cpu().numpy().astype(np.int64)
     dg = out["diag"].cpu().numpy().astype(float)
@@ -326,10 +378,15 @@ def main():
     up_ms = float(stage_ms[moe.STAGES.index("gemm_up")])
     achieved = fl["gemm_up"] / (up_ms * 1e-3) / 1e12
     traffic = load_traffic(name)
+    up_each = stage_each[:, moe.STAGES.index("gemm_up")]
     roofline = {"bound": "mfma", "kernel": "grouped_gemm_kernel<0> (routed gate/up + SwiGLU)",
                 "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
-                "flops_per_launch": fl["gemm_up"], "ms_per_launch": round(up_ms, 4)}
+                "flops_per_launch": fl["gemm_up"], "ms_per_launch": round(up_ms, 4),
+                "ms_per_launch_mean": round(float(up_each.mean()), 4),
+                "ms_per_launch_p10_p90": [round(float(np.percentile(up_each, 10)), 4),
+                                          round(float(np.percentile(up_each, 90)), 4)],
+                "launches": int(args.steps)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -340,6 +397,12 @@ def main():
         "metric": METRIC, "value": round(T / (ms_step * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "step_ms": {"median": round(float(np.median(step_ms_each)), 4),
+                    "p10": round(float(np.percentile(step_ms_each, 10)), 4),
+                    "p90": round(float(np.percentile(step_ms_each, 90)), 4),
+                    "min": round(float(step_ms_each.min()), 4),
+                    "max": round(float(step_ms_each.max()), 4), "steps": int(args.steps),
+                    "how": "each step between two events on the stream, a second pass"},
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": name, "T": T, "d": d, "E": E, "k": k, "M": M, "S": S,
                    "capacity_factor": cfg.c, "bias": cfg.bias, "scoring": cfg.scoring,

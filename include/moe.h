@@ -31,6 +31,7 @@
  *     asynchronous faults surface at the caller's synchronisation.
  *   - Results are deterministic: the same inputs give bit-identical outputs on every call.
  *   - Entry points are stateless and re-entrant; concurrent calls must use distinct workspaces.
+ *     The one exception is the profiling hook moe_set_stage_events (process-wide, under a lock).
  *   - dtype MOE_BF16: x, weights, intermediates and y are bf16, products accumulate in fp32, the
  *     routing arithmetic is fp32, h and expert outputs are rounded to bf16, y is rounded once.
  *     dtype MOE_F32: all of these are fp32.
@@ -83,11 +84,12 @@ typedef enum {
 /* Layer sizes, in the pages' notation. */
 typedef struct {
   int64_t T;      /* tokens in the routing batch (B on the pages), >= 1                       */
-  int32_t d;      /* hidden size; multiple of 8 (bf16) or 4 (fp32)                            */
+  int32_t d;      /* hidden size; multiple of 8 (bf16) or 4 (fp32); at most 2^21              */
   int32_t E;      /* routed experts, 1 <= E <= MOE_E_MAX                                      */
   int32_t k;      /* experts chosen per token, 1 <= k <= min(E, MOE_K_MAX)                    */
-  int32_t M;      /* expert intermediate width; multiple of 8 (bf16) or 4 (fp32)              */
-  int32_t S;      /* shared experts, each of width M, >= 0; they run as one expert of width S*M */
+  int32_t M;      /* expert intermediate width; multiple of 8 (bf16) or 4 (fp32); at most 2^20 */
+  int32_t S;      /* shared experts, each of width M, >= 0; they run as one expert of width S*M
+                     (S*M at most 2^20)                                                        */
   float c;        /* capacity factor; <= 0 means no capacity limit; NaN is invalid            */
   int32_t renorm; /* 1: renormalise the chosen gates over S_t; 0: use g_te as is               */
   int32_t dtype;  /* moe_dtype                                                                */
@@ -109,12 +111,18 @@ int64_t moe_capacity(const moe_shape* s);
  * For MOE_CALL_EXPERT_FFN the size is for groups = E (it also covers groups = 1). */
 size_t moe_workspace_size(const moe_shape* s, int call);
 
+/* Rows R of the layer's expert-contiguous routed buffers: min(T k, E C) for token choice (T k
+ * without a capacity), E r for expert choice; -1 if the shape is invalid. perm_token of
+ * moe_layer_forward holds R entries. */
+int64_t moe_routed_rows(const moe_shape* s);
+
 /*
  * moe_saved_size -- bytes of the buffer in which moe_layer_forward keeps, for a later
  * moe_layer_backward on the same inputs, the fp32 gate and up pre-activations of every routed row
  * and of the shared experts (bf16 layers only; 0 for fp32 layers or an invalid shape). Layout
- * (256-byte aligned parts): G, U [R, M] each, R = min(T k, E C) rows in the forward's
- * expert-major row order (expert choice: E r), then Gs, Us [T, S*M] each when S > 0.
+ * (256-byte aligned parts): G, U [R, M] each, R = moe_routed_rows(s) rows in the forward's
+ * expert-major row order, then Gs, Us [T, S*M] each when S > 0, then the bias the forward
+ * selected with, [E] fp32 (zeros when it had none; token choice only).
  */
 size_t moe_saved_size(const moe_shape* s);
 
@@ -228,8 +236,11 @@ moe_status moe_balance_stats(const moe_shape* s, const int32_t* n, const double*
  *   y device out [T, d]
  * Optional device outputs (NULL = not returned): topk_idx [T, k] int32, topk_w [T, k] fp32,
  * counts [E] int32 (n_e), overflow [E] int32, f [E], P [E], aux [1], z [1] fp32, diag [4] fp32
- * (routing diagnostics as in moe_balance_stats), and b_new [E] fp32 = the updated bias
- * (requires b; may alias b: it is written after selection).
+ * (routing diagnostics as in moe_balance_stats), b_new [E] fp32 = the updated bias
+ * (requires b; may alias b: it is written after selection), and the placement of
+ * moe_dispatch ("MoE：条件计算与路由" §3): inv_perm [T, k] int32 (row of (t, j), -1 if dropped;
+ * token choice only, not written under expert choice) and perm_token [moe_routed_rows(s)] int32
+ * (token of each row < offsets_E; other entries unset), both 16-byte aligned.
  * Expert choice (s->routing == MOE_ROUTE_EXPERT_CHOICE; "深入理解 MoE ..." §9.2, "MoE：条件计算与
  * 路由" §路由机制的演进): expert e takes the r = min(ceil(c k T / E), T) tokens of largest logit
  * l_te (c <= 0 reads as 1; equal logits to the lower token index); token t's output sums
@@ -237,9 +248,10 @@ moe_status moe_balance_stats(const moe_shape* s, const int32_t* n, const double*
  * those experts when renorm); a token no expert took gets the shared term only. b must be NULL;
  * topk_idx and topk_w are not written; counts = r, overflow = 0, f_e = n_e / (E r).
  *   saved device out of moe_saved_size(s) bytes, or NULL: the fp32 gate and up pre-activations of
- *     every kept row and of the shared experts, taken from the same accumulators as h, for a
- *     moe_layer_backward on the same inputs (training); y and every other output are the same
- *     with or without it. bf16 layers only (fp32: MOE_ERR_UNSUPPORTED); 16-byte aligned.
+ *     every kept row and of the shared experts, taken from the same accumulators as h, and the
+ *     bias selected with, for a moe_layer_backward on the same inputs (training); y and every
+ *     other output are the same with or without it. bf16 layers only (fp32:
+ *     MOE_ERR_UNSUPPORTED); 16-byte aligned.
  *   ws device workspace of moe_workspace_size(s, MOE_CALL_LAYER) bytes
  */
 moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r, const float* b,
@@ -247,8 +259,8 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
                              const void* Ws_gate, const void* Ws_up, const void* Ws_down, void* y,
                              int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* overflow,
                              float* f, float* P, float* aux, float* z, float* diag, float* b_new,
-                             float lambda, float gamma, void* saved, void* ws, size_t ws_bytes,
-                             void* stream);
+                             int32_t* inv_perm, int32_t* perm_token, float lambda, float gamma,
+                             void* saved, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_balance_loss_backward -- gradient of the layer's balance losses through the router.
@@ -293,11 +305,16 @@ moe_status moe_balance_loss_backward(const moe_shape* s, const void* x, const vo
  *     taken at (not written under expert choice)
  *   saved device [moe_saved_size(s) bytes] or NULL: the buffer a moe_layer_forward call on the
  *     same inputs filled; the gate/up products are then not recomputed (the routing and placement
- *     still are: they are deterministic, so the rows match). The gradients are bit-identical
- *     either way. Read only; bf16 layers only (fp32: MOE_ERR_UNSUPPORTED); 16-byte aligned.
+ *     still are: they are deterministic, so the rows match). Token choice then selects with the
+ *     bias kept in saved, the one the forward used, not with b: an in-place bias step between
+ *     the two calls (b_new aliasing b) leaves the gradients unchanged. The gradients are
+ *     bit-identical to a call without saved given the forward's bias. Read only; bf16 layers only
+ *     (fp32: MOE_ERR_UNSUPPORTED); 16-byte aligned.
  *   ws device workspace of moe_workspace_size(s, MOE_CALL_LAYER_BACKWARD) bytes
  * bf16 layers read the weights in place; one expert's W_gate and W_up together (4 M d bytes), and
- * the shared experts' (4 S M d bytes), must stay under 4 GiB (MOE_ERR_UNSUPPORTED otherwise).
+ * the shared experts' (4 S M d bytes), must stay under 4 GiB, and the weight-gradient operands
+ * (64 (ceil(R / 64) + E) and 64 ceil(T / 64) columns, R = moe_routed_rows(s)) under 2^22 columns
+ * (MOE_ERR_UNSUPPORTED otherwise).
  */
 moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r, const float* b,
                               const void* W_gate, const void* W_up, const void* W_down,
@@ -313,7 +330,10 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
  * owned by the caller, count >= MOE_STAGE_COUNT) on their stream at the end of each stage:
  *   0 start, 1 route, 2 scan + placement, 3 routed gate/up GEMM (SwiGLU, rows gathered from x),
  *   4 routed down GEMM, 5 shared experts (both GEMMs), 6 combine, 7 statistics.
- * NULL turns recording off. Process-wide setting; not thread-safe.
+ * NULL turns recording off. Process-wide setting, read and written under a lock: each forward
+ * copies the handles when it starts. The caller keeps the events alive until recording is off and
+ * every forward that records them has completed. A failed record makes that forward return
+ * MOE_ERR_HIP (its kernels are enqueued).
  */
 #define MOE_STAGE_COUNT 8
 moe_status moe_set_stage_events(void* const* events, int count);

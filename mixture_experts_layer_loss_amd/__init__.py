@@ -49,6 +49,7 @@ _SIG = {
     "moe_capacity": (ctypes.c_int64, [ctypes.POINTER(Shape)]),
     "moe_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int]),
     "moe_saved_size": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
+    "moe_routed_rows": (ctypes.c_int64, [ctypes.POINTER(Shape)]),
     "moe_route": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                  ctypes.c_size_t, _P]),
     "moe_dispatch": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -60,7 +61,7 @@ _SIG = {
     "moe_balance_stats": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, ctypes.c_float, _P,
                                          _P, _P, _P, _P, _P, _P, ctypes.c_float, _P]),
     "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                         _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                         _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                          ctypes.c_float, ctypes.c_float, _P, _P, ctypes.c_size_t,
                                          _P]),
     "moe_set_stage_events": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]),
@@ -139,6 +140,27 @@ def capacity(s: Shape) -> int:
 
 def workspace_size(s: Shape, call: int) -> int:
     return int(lib().moe_workspace_size(ctypes.byref(s), int(call)))
+
+
+def routed_rows(s: Shape) -> int:
+    """moe_routed_rows: rows of the expert-contiguous routed buffers (entries of perm_token)."""
+    return int(lib().moe_routed_rows(ctypes.byref(s)))
+
+
+def _shared_count(shared, M: int, d: int, dtype) -> int:
+    """S from the stacked shared experts (Ws_gate [S*M, d], Ws_up [S*M, d], Ws_down [d, S*M])."""
+    if shared is None:
+        return 0
+    if len(shared) != 3:
+        raise ValueError("shared must be (Ws_gate, Ws_up, Ws_down)")
+    SM = shared[0].shape[0]
+    if shared[0].dim() != 2 or SM == 0 or SM % M != 0:
+        raise ValueError(f"Ws_gate must be [S*M, d] with S >= 1 and M = {M}, got "
+                         f"{tuple(shared[0].shape)}")
+    for name, t, shp in (("Ws_gate", shared[0], (SM, d)), ("Ws_up", shared[1], (SM, d)),
+                         ("Ws_down", shared[2], (d, SM))):
+        _dev(t, name, dtype, shp)
+    return SM // M
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -342,7 +364,7 @@ def moe_layer_backward(x, W_r, W_gate, W_up, W_down, dy, k: int, b=None, shared=
     are then taken from it instead of being recomputed (bf16 layers)."""
     T, d = x.shape
     E, M, _ = W_gate.shape
-    S = 0 if shared is None else shared[0].shape[0] // M
+    S = _shared_count(shared, M, d, x.dtype)
     s = make_shape(T, d, E, k, M, S, c, renorm, x.dtype, scoring, routing)
     _check(check_shape(s), "moe_layer_backward")
     dt = x.dtype
@@ -390,9 +412,16 @@ class MoELayer:
         self.device = torch.device(device)
         self.ws = workspace(self.shape, CALL_LAYER, self.device)
 
-    def alloc_outputs(self, with_bias: bool = False) -> dict:
+    def alloc_outputs(self, with_bias: bool = False, placement: bool = False) -> dict:
+        """Output tensors; ``placement`` adds inv_perm [T, k] (token choice) and perm_token
+        [routed_rows] (the dispatch of "MoE：条件计算与路由" §3 the layer made)."""
         dev, T, E, k = self.device, self.T, self.E, self.k
+        token = self.shape.routing == ROUTING["token"]
         return {"y": torch.empty(T, self.d, dtype=self.dtype, device=dev),
+                "inv_perm": torch.empty(T, k, dtype=torch.int32, device=dev)
+                if placement and token else None,
+                "perm_token": torch.full((max(routed_rows(self.shape), 1),), -1, dtype=torch.int32,
+                                         device=dev) if placement else None,
                 "topk_idx": torch.empty(T, k, dtype=torch.int32, device=dev),
                 "topk_w": torch.empty(T, k, dtype=torch.float32, device=dev),
                 "counts": torch.empty(E, dtype=torch.int32, device=dev),
@@ -437,17 +466,25 @@ class MoELayer:
             _ptr(W_down), _ptr(sg), _ptr(su), _ptr(sd), _ptr(out["y"]), _ptr(out.get("topk_idx")),
             _ptr(out.get("topk_w")), _ptr(out.get("counts")), _ptr(out.get("overflow")),
             _ptr(out.get("f")), _ptr(out.get("P")), _ptr(out.get("aux")), _ptr(out.get("z")),
-            _ptr(out.get("diag")), _ptr(out.get("b_new") if b is not None else None), float(lam),
-            float(gamma), _ptr(saved),
+            _ptr(out.get("diag")), _ptr(out.get("b_new") if b is not None else None),
+            _ptr(out.get("inv_perm")), _ptr(out.get("perm_token")), float(lam), float(gamma),
+            _ptr(saved),
             _ptr(self.ws), self.ws.numel(), _stream()), "moe_layer_forward")
         return out
 
 
+_stage_events_held = None  # the events the library records into, kept alive while it may
+
+
 def moe_set_stage_events(events) -> None:
     """Profiling aid: record ``events`` (8 torch.cuda.Event, timing enabled) at the end of each
-    stage of later moe_layer_forward calls; None switches recording off."""
+    stage of later moe_layer_forward calls; None switches recording off. The events are kept
+    referenced here until recording is switched off."""
+    global _stage_events_held
     if events is None:
         _check(lib().moe_set_stage_events(None, 0), "moe_set_stage_events")
+        torch.cuda.synchronize()  # forwards already enqueued may still record into them
+        _stage_events_held = None
         return
     arr = (ctypes.c_void_p * len(events))()
     stream = torch.cuda.current_stream()
@@ -456,6 +493,7 @@ def moe_set_stage_events(events) -> None:
             ev.record(stream)  # torch creates the HIP event on its first record
         arr[i] = ev.cuda_event
     _check(lib().moe_set_stage_events(arr, len(events)), "moe_set_stage_events")
+    _stage_events_held = list(events)
 
 
 def moe_layer_forward(x, W_r, W_gate, W_up, W_down, k: int, b=None, shared=None,
@@ -464,9 +502,7 @@ def moe_layer_forward(x, W_r, W_gate, W_up, W_down, k: int, b=None, shared=None,
     """One call of the whole layer (allocates its workspace; use MoELayer to reuse one)."""
     T, d = x.shape
     E, M, _ = W_gate.shape
-    S = 0
-    if shared is not None:
-        S = shared[0].shape[0] // M
+    S = _shared_count(shared, M, d, x.dtype)
     layer = MoELayer(T, d, E, k, M, S, c, renorm, x.dtype, x.device, scoring, routing)
     return layer.forward(x, W_r, W_gate, W_up, W_down, b, shared, lam, gamma)
 
@@ -474,4 +510,5 @@ def moe_layer_forward(x, W_r, W_gate, W_up, W_down, k: int, b=None, shared=None,
 __all__ = ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_balance_stats",
            "moe_balance_loss_backward", "moe_layer_backward",
            "moe_layer_forward", "MoELayer", "make_shape", "capacity", "workspace_size",
-           "check_shape", "status_string", "lib", "MoEError", "Shape", "moe_set_stage_events"]
+           "check_shape", "status_string", "lib", "MoEError", "Shape", "moe_set_stage_events",
+           "routed_rows", "saved_size"]

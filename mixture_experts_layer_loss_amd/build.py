@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libmoe.so")
 ARCH = "gfx950"
 
 FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 ops stay off for every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
@@ -28,15 +28,36 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc, *FLAGS, "-I", os.path.join(os.path.dirname(HERE), "include"), *sources(), "-o", tmp]
-    t0 = time.time()
+def _run(cmd):
     proc = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = [l for l in (proc.stdout + proc.stderr).splitlines() if noise not in l]
-    if proc.returncode != 0:
+    return proc.returncode, msgs
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles every source to an object (in parallel), then links the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    inc = ["-I", os.path.join(os.path.dirname(HERE), "include")]
+    tag = f".tmp{os.getpid()}"
+    objs = [os.path.join(CSRC, os.path.basename(src)[:-4] + tag + ".o") for src in sources()]
+    t0 = time.time()
+    jobs = max(1, min(len(objs), int(os.environ.get("MAX_JOBS", "0")) or (os.cpu_count() or 4)))
+    with ThreadPoolExecutor(jobs) as pool:
+        results = list(pool.map(lambda so: _run([hipcc, *FLAGS, *inc, "-c", so[0], "-o", so[1]]),
+                                zip(sources(), objs)))
+    msgs = [m for _, ms in results for m in ms]
+    tmp = LIB + tag
+    rc = max(r for r, _ in results)
+    if rc == 0:
+        rc, link_msgs = _run([hipcc, *FLAGS, "-shared", *objs, "-o", tmp])
+        msgs += link_msgs
+    for o in objs:
+        if os.path.exists(o):
+            os.remove(o)
+    if rc != 0:
         if os.path.exists(tmp):
             os.remove(tmp)
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -67,6 +69,8 @@ using namespace moe;
 namespace {
 
 constexpr size_t kAlign = 256;
+// Largest hidden size d, and largest 2 M and 2 S M (the backward's [dG dU] rows), a layer may have.
+constexpr int64_t kMaxWidth = int64_t{1} << 21;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -301,19 +305,34 @@ LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// Profiling aid: events recorded at the end of each moe_layer_forward stage (see moe.h).
+// Profiling aid: events recorded at the end of each moe_layer_forward stage (see moe.h). The
+// setting is process-wide (the one piece of state the library keeps); it is read and written
+// under a lock, and each forward works on the copy it takes when it starts.
+std::mutex g_stage_mu;
 hipEvent_t g_stage_events[MOE_STAGE_COUNT] = {};
 bool g_stage_on = false;
 
-void mark_stage(int i, hipStream_t st) {
-  if (g_stage_on && g_stage_events[i] != nullptr) (void)hipEventRecord(g_stage_events[i], st);
-}
+struct StageMarks {
+  hipEvent_t ev[MOE_STAGE_COUNT];
+  bool on;
+  hipError_t err = hipSuccess;  // the first failed record
+  StageMarks() {
+    std::lock_guard<std::mutex> lock(g_stage_mu);
+    on = g_stage_on;
+    for (int i = 0; i < MOE_STAGE_COUNT; ++i) ev[i] = g_stage_events[i];
+  }
+  void mark(int i, hipStream_t st) {
+    if (on && ev[i] != nullptr && err == hipSuccess) err = hipEventRecord(ev[i], st);
+  }
+};
 
 // Pre-activations a training forward keeps for the backward (bf16 layers): the fp32 gate and up
 // values of every routed row, [R, M] each with R the workspace's routed-row bound, then those of
 // the shared experts, [T, S M] each.
+// The bias the forward selected with comes last ([E] fp32, zeros without a bias), so that the
+// backward selects exactly as the forward did even if the caller updated b in place in between.
 struct SavedPlan {
-  float *G, *U, *Gs, *Us;
+  float *G, *U, *Gs, *Us, *b;
 };
 SavedPlan plan_saved(Carve& c, const moe_shape* s) {
   const size_t R = static_cast<size_t>(routed_rows(s)), M = s->M;
@@ -327,6 +346,7 @@ SavedPlan plan_saved(Carve& c, const moe_shape* s) {
   } else {
     p.Gs = p.Us = nullptr;
   }
+  p.b = c.take<float>(s->E);
   return p;
 }
 
@@ -362,13 +382,21 @@ moe_status moe_check_shape(const moe_shape* s) {
   // row indices are int32
   if (s->T * static_cast<int64_t>(s->k) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   if (expert_choice(s) && s->T * static_cast<int64_t>(s->E) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
-  if (static_cast<int64_t>(s->S) * s->M > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  // the grouped GEMMs form a tile's operand-row offsets (256 rows of up to 2 max(M, S M) or d
+  // elements) in 32 bits
+  if (s->d > kMaxWidth || s->M > kMaxWidth / 2 || static_cast<int64_t>(s->S) * s->M > kMaxWidth / 2)
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
 int64_t moe_capacity(const moe_shape* s) {
   if (moe_check_shape(s) != MOE_OK) return -1;
   return capacity_of(s);
+}
+
+int64_t moe_routed_rows(const moe_shape* s) {
+  if (moe_check_shape(s) != MOE_OK) return -1;
+  return routed_rows(s);
 }
 
 size_t moe_saved_size(const moe_shape* s) {
@@ -451,6 +479,7 @@ moe_status moe_expert_ffn(const moe_shape* s, int32_t groups, int32_t Mg, const 
   if (groups < 1 || groups > MOE_E_MAX || Mg < 1 || max_rows < 0 || max_rows > INT32_MAX)
     return groups > MOE_E_MAX ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_ARGUMENT;
   if (Mg % (s->dtype == MOE_F32 ? 4 : 8) != 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (Mg > kMaxWidth / 2) return MOE_ERR_UNSUPPORTED;
   if (!rows || !offsets || !W_gate || !W_up || !W_down || !h || !out)
     return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(rows) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_down) ||
@@ -503,8 +532,8 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
                              const void* Ws_gate, const void* Ws_up, const void* Ws_down, void* y,
                              int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* overflow,
                              float* f, float* P, float* aux, float* z, float* diag, float* b_new,
-                             float lambda, float gamma, void* saved, void* ws, size_t ws_bytes,
-                             void* stream) {
+                             int32_t* inv_perm, int32_t* perm_token, float lambda, float gamma,
+                             void* saved, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = moe_check_shape(s);
   if (st != MOE_OK) return st;
   if (!x || !W_r || !W_gate || !W_up || !W_down || !y) return MOE_ERR_INVALID_ARGUMENT;
@@ -516,7 +545,7 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
   // tokens an expert ranks highest
   if (expert_choice(s) && b != nullptr) return MOE_ERR_INVALID_ARGUMENT;
   if (isnan(lambda) || isnan(gamma)) return MOE_ERR_INVALID_ARGUMENT;
-  const void* tensors[] = {x, W_r, W_gate, W_up, W_down, y, topk_idx, topk_w};
+  const void* tensors[] = {x, W_r, W_gate, W_up, W_down, y, topk_idx, topk_w, inv_perm, perm_token};
   for (const void* t : tensors)
     if (t && !aligned16(t)) return MOE_ERR_INVALID_ARGUMENT;
   if (s->S > 0 && (!aligned16(Ws_gate) || !aligned16(Ws_up) || !aligned16(Ws_down)))
@@ -532,6 +561,9 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
   float* w = topk_w ? topk_w : p.topk_w;
   int32_t* n = counts ? counts : p.n;
   int32_t* ovf = overflow ? overflow : p.overflow;
+  // placement outputs the caller asked for are written in place of the workspace's copies
+  if (inv_perm != nullptr && !expert_choice(s)) p.inv_perm = inv_perm;
+  if (perm_token != nullptr) p.perm_token = perm_token;
   const int64_t C = capacity_of(s);
   const int BM = gemm_bm(s);
   const int nblk = static_cast<int>(route_blocks(s));
@@ -539,10 +571,15 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
 
   const int64_t max_tiles = cdiv(routed_rows(s), BM) + s->E;
 
-  mark_stage(0, hs);
-  hipError_t e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s), x, W_r, b, idx, w,
-                              p.r.hist, p.r.gpart, p.r.lpart, p.r.hpart, p.cols, hs);
-  mark_stage(1, hs);
+  StageMarks marks;
+  marks.mark(0, hs);
+  hipError_t e = hipSuccess;
+  if (saved != nullptr && !expert_choice(s))  // the bias this forward selects with, for the backward
+    e = launch_copy_f32(b, sv.b, s->E, hs);
+  if (e == hipSuccess)
+    e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s), x, W_r, b, idx, w,
+                     p.r.hist, p.r.gpart, p.r.lpart, p.r.hpart, p.cols, hs);
+  marks.mark(1, hs);
   if (expert_choice(s)) {
     // the statistics partials, then every expert's top-r tokens and their tile tables
     if (e == hipSuccess)
@@ -562,18 +599,18 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
       e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx, route_block_tokens(s->dtype, s->E),
                          p.block_base, p.offsets, nullptr, p.perm_token, p.inv_perm, hs);
   }
-  mark_stage(2, hs);
+  marks.mark(2, hs);
   if (e == hipSuccess && saved != nullptr)  // h, and G and U kept for the backward
     e = launch_gemm_up_save_bf16(s->E, s->d, s->M, x, p.perm_token, p.offsets, p.tile_off,
                                  max_tiles, W_gate, W_up, p.h, sv.G, sv.U, hs);
   else if (e == hipSuccess)
     e = launch_gemm_up(s->dtype, s->E, s->d, s->M, x, p.perm_token, p.offsets, p.tile_off,
                        max_tiles, W_gate, W_up, p.h, hs);
-  mark_stage(3, hs);
+  marks.mark(3, hs);
   if (e == hipSuccess)
     e = launch_gemm_down(s->dtype, s->E, s->d, s->M, p.offsets, p.tile_off, max_tiles, W_down,
                          p.h, p.out_perm, hs);
-  mark_stage(4, hs);
+  marks.mark(4, hs);
   if (e == hipSuccess && s->S > 0) {
     const int SM = s->S * s->M;
     const int64_t sh_tiles = cdiv(s->T, BM);
@@ -588,7 +625,7 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
       e = launch_gemm_down(s->dtype, 1, s->d, SM, p.sh_offsets, p.sh_tile_off, sh_tiles, Ws_down,
                            p.h_sh, p.sh, hs);
   }
-  mark_stage(5, hs);
+  marks.mark(5, hs);
   if (e == hipSuccess && expert_choice(s))
     e = launch_combine_ec(s->dtype, s->T, s->d, s->E, s->renorm, p.out_perm, p.row_of,
                           p.cols + static_cast<size_t>(s->E) * s->T, s->S > 0 ? p.sh : nullptr, y,
@@ -596,12 +633,13 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
   else if (e == hipSuccess)
     e = launch_combine(s->dtype, s->T, s->d, s->k, p.out_perm, p.inv_perm, w,
                        s->S > 0 ? p.sh : nullptr, y, hs);
-  mark_stage(6, hs);
+  marks.mark(6, hs);
   if (e == hipSuccess && (f || P || aux || z || diag || b_new))
     e = launch_stats(s->T, s->E, stats_fden(s), n, p.gsum, p.lse2sum, p.hsum, lambda, f, P, aux, z,
                      diag,
                      b_new ? b : nullptr, b_new, gamma, hs);
-  mark_stage(7, hs);
+  marks.mark(7, hs);
+  if (e == hipSuccess) e = marks.err;
   return hip_status(e);
 }
 
@@ -661,12 +699,22 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
   const void* tensors[] = {x, W_r, W_gate, W_up, W_down, dy};
   for (const void* t : tensors)
     if (!aligned16(t)) return MOE_ERR_INVALID_ARGUMENT;
+  if (s->S > 0 && (!aligned16(Ws_gate) || !aligned16(Ws_up) || !aligned16(Ws_down)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  // the weight-gradient GEMM reads 256-row slabs of operands padded to ldp (routed) and ldps
+  // (shared) columns with 32-bit byte offsets
+  if (s->dtype == MOE_BF16) {
+    const int64_t R = routed_rows(s);
+    const int64_t ldp = 64 * (cdiv(R, 64) + s->E), ldps = 64 * cdiv(s->T, 64);
+    if (2 * 256 * (ldp > ldps ? ldp : ldps) >= (int64_t{1} << 31)) return MOE_ERR_UNSUPPORTED;
+  }
   if (!ws || ws_bytes < moe_workspace_size(s, MOE_CALL_LAYER_BACKWARD)) return MOE_ERR_WORKSPACE;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   Carve c(ws);
   LayerBackwardPlan p = plan_layer_backward(c, s);
   LayerPlan& f = p.f;
+  const float* b_sel = b;  // the bias the selection is made with
   if (saved != nullptr) {  // the forward's pre-activations replace the recomputed ones
     Carve cs(const_cast<void*>(saved));  // read only
     const SavedPlan sv = plan_saved(cs, s);
@@ -674,6 +722,7 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
     p.U = sv.U;
     p.Gs = sv.Gs;
     p.Us = sv.Us;
+    if (!expert_choice(s)) b_sel = sv.b;  // as the forward selected, whatever b holds now
   }
   int32_t* idx = topk_idx ? topk_idx : f.topk_idx;
   const int64_t C = capacity_of(s);
@@ -698,8 +747,8 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
                            f.row_of, f.offsets, f.n, f.overflow, hs);
     if (e == hipSuccess) e = launch_schedule(s->E, f.offsets, f.tile_off, BM, hs);
   } else {
-    e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s), x, W_r, b, idx, f.topk_w,
-                     f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart, nullptr, hs);
+    e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s), x, W_r, b_sel, idx,
+                     f.topk_w, f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart, nullptr, hs);
     if (e == hipSuccess)
       e = launch_scan(s->T, s->E, C, nblk, f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart,
                       f.block_base, f.n, f.gsum, f.lse2sum, f.hsum, f.kept, f.overflow, f.offsets,
@@ -887,8 +936,10 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
 }
 
 moe_status moe_set_stage_events(void* const* events, int count) {
+  std::lock_guard<std::mutex> lock(g_stage_mu);
   if (events == nullptr) {
     g_stage_on = false;
+    for (int i = 0; i < MOE_STAGE_COUNT; ++i) g_stage_events[i] = nullptr;
     return MOE_OK;
   }
   if (count < MOE_STAGE_COUNT) return MOE_ERR_INVALID_ARGUMENT;

@@ -215,6 +215,9 @@ hipError_t launch_combine(int dtype, int64_t T, int d, int k, const void* out_pe
                           const int32_t* inv_perm, const float* topk_w, const void* shared_out,
                           void* y, hipStream_t st);
 
+// dst[0, n) = src[0, n), or zeros when src is NULL.
+hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t st);
+
 // f, P, aux, z and the bias step from reduced route statistics.
 // fden: the f_e denominator (k T; E r for expert choice). diag (may be NULL) [4]: routing entropy
 // (hsum / T), load Gini, max/mean load, importance CV^2.

@@ -96,7 +96,20 @@ __global__ __launch_bounds__(256) void stats_kernel(
   }
 }
 
+// dst[i] = src[i], or 0 when src is NULL (the bias a training forward keeps for its backward).
+__global__ __launch_bounds__(256) void copy_f32_kernel(const float* __restrict__ src,
+                                                        float* __restrict__ dst, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src != nullptr ? src[i] : 0.f;
+}
+
 }  // namespace
+
+hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_f32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, src, dst, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_stats(int64_t T, int E, double fden, const int32_t* n, const double* gsum,
                         const double* lse2sum, const double* hsum, float lambda, float* f,

@@ -714,9 +714,11 @@ def route(x, W_r, k: int, b=None, renorm: bool = True, scoring: str = "softmax")
 
 def layer_forward_expert_choice(x, W_r, W_gate, W_up, W_down, k: int, shared=(), c=None,
                                 renorm: bool = True, lam: float = 0.01, tokens=None,
-                                expert_weights=None, scoring: str = "softmax"):
+                                expert_weights=None, scoring: str = "softmax",
+                                magnitudes: bool = False):
     """Expert-choice layer: expert e applies E_e to the r tokens it chose; y_t sums w_te E_e(x_t)
-    over the experts that chose t, in ascending expert order, plus the shared experts."""
+    over the experts that chose t, in ascending expert order, plus the shared experts.
+    ``magnitudes``: res["magnitude"] as in layer_forward (sums of |terms| per element of y)."""
     x64 = _f64(x)
     T, d = x64.shape
     r_ = route(x64, W_r, 1, None, renorm, scoring)
@@ -737,6 +739,10 @@ def layer_forward_expert_choice(x, W_r, W_gate, W_up, W_down, k: int, shared=(),
     xs = x64[want]
     if shared:
         y += shared_experts(xs, shared)
+    mag = np.zeros((len(want), d)) if magnitudes else None
+    if magnitudes:
+        for Ws in shared:
+            mag += np.abs(swiglu_expert(xs, *Ws))
     pos = {int(t): i for i, t in enumerate(want)}
     for e in range(E):
         rows = [int(t) for t in chosen[e] if int(t) in pos]
@@ -746,12 +752,15 @@ def layer_forward_expert_choice(x, W_r, W_gate, W_up, W_down, k: int, shared=(),
         O = swiglu_expert(x64[rows], *We)
         for i, t in enumerate(rows):
             y[pos[t]] += w[t, e] * O[i]
+            if magnitudes:
+                mag[pos[t]] += np.abs(w[t, e] * O[i])
     # f_e = n_e / sum_e n_e (equal loads: 1 / E), P_e from the same distribution as token choice
     f = n / float(n.sum())
     P = r_["probs"].sum(axis=0) / float(T)
     aux = float(lam) * E * float((f * P).sum())
     z = float((r_["lse"] ** 2).sum() / float(T))
-    return {"y": y, "tokens": want, "chosen": chosen, "r": r, "w": w, "n": n, "f": f, "P": P,
+    return {"y": y, "magnitude": mag, "tokens": want, "chosen": chosen, "r": r, "w": w, "n": n,
+            "f": f, "P": P,
             "aux": aux, "z": z, "lse": r_["lse"], "g": g, "logits": l,
             "diag": diagnostics(n, r_["probs"]),
             "uncovered": int((~member.any(axis=1)).sum())}
@@ -759,14 +768,18 @@ def layer_forward_expert_choice(x, W_r, W_gate, W_up, W_down, k: int, shared=(),
 
 def layer_forward(x, W_r, W_gate, W_up, W_down, k: int, b=None, shared=(), c=None,
                   renorm: bool = True, lam: float = 0.01, gamma: float = 1e-3,
-                  topk_idx=None, tokens=None, expert_weights=None, scoring: str = "softmax"):
+                  topk_idx=None, tokens=None, expert_weights=None, scoring: str = "softmax",
+                  magnitudes: bool = False):
     """y = sum_{e in S_t} w_te E_e(x_t) + sum_s E^s(x_t), plus loads, drops and statistics.
 
     ``topk_idx`` (optional) replaces the oracle's own selection by a given one (to check the stages
     after routing on exactly the assignments another implementation made); ``tokens`` (optional)
     restricts y to those token indices (y_t depends on token t alone once dispatch is fixed);
     ``expert_weights`` (optional) is a callable e -> (W_gate_e, W_up_e, W_down_e) used instead of
-    indexing the full weight tensors.
+    indexing the full weight tensors. With ``magnitudes``, res["magnitude"] holds, per element of
+    y, the sum of the absolute values of the terms the combine adds, sum_j |w_tj E_j(x_t)_i| +
+    sum_s |E^s(x_t)_i|: the scale of any rounding of those terms, which y itself can undercut
+    when they cancel.
     """
     x64 = _f64(x)
     T, d = x64.shape
@@ -802,7 +815,18 @@ def layer_forward(x, W_r, W_gate, W_up, W_down, k: int, b=None, shared=(), c=Non
             rr = int(dsp["row"][t, j])
             if rr >= 0:
                 y[i] += w[t, j] * out_perm[rr]
-    res = {"y": y, "tokens": want, "topk_idx": S, "topk_w": w, "n": n, "C": C, **dsp, **stats,
+    mag = None
+    if magnitudes:
+        mag = np.zeros((len(want), d))
+        for Ws in shared:
+            mag += np.abs(swiglu_expert(xs, *Ws))
+        for i, t in enumerate(want):
+            for j in range(k):
+                rr = int(dsp["row"][t, j])
+                if rr >= 0:
+                    mag[i] += np.abs(w[t, j] * out_perm[rr])
+    res = {"y": y, "magnitude": mag, "tokens": want, "topk_idx": S, "topk_w": w, "n": n, "C": C,
+           **dsp, **stats,
            "diag": diagnostics(n, r["probs"]),
            "lse": r["lse"], "g": r["g"], "margin": r["margin"], "s": r["s"]}
     if b is not None:

@@ -1,7 +1,10 @@
 """Comparison helpers for GPU-vs-oracle parity.
 
-* ``max_rel_err(a, r)`` = max_i |a_i - r_i| / max(|r_i|, rms(r)): elementwise relative error,
-  floored at the reference RMS so that near-zero reference elements do not dominate.
+* ``max_rel_err(a, r, mag)`` = max_i |a_i - r_i| / max(|r_i|, rms(r), mag_i): elementwise
+  relative error, floored at the reference RMS so that near-zero reference elements do not
+  dominate, and, for the layer output, at the magnitude of the terms summed into it (mag_i =
+  sum of |w E(x)| over the combine's terms plus the shared terms): each term is rounded to bf16
+  before the sum, so an element whose terms cancel carries an error set by the terms, not by y.
 * Tolerances: 2e-2 for bf16 layers (bf16 storage, fp32 accumulation), 1e-4 for fp32 layers,
   1e-5 relative for the balance statistics.
 * Near ties: a token whose k-th and (k+1)-th oracle selection scores are within 1e-3 may pick a
@@ -24,12 +27,14 @@ def f64(t) -> np.ndarray:
     return np.asarray(t, dtype=np.float64)
 
 
-def max_rel_err(a, r) -> float:
+def max_rel_err(a, r, mag=None) -> float:
     a, r = f64(a), f64(r)
     if r.size == 0:
         return 0.0
     rms = float(np.sqrt(np.mean(r * r)))
     den = np.maximum(np.abs(r), rms if rms > 0 else 1.0)
+    if mag is not None:
+        den = np.maximum(den, f64(mag))
     return float(np.max(np.abs(a - r) / den))
 
 

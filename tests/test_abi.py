@@ -88,7 +88,7 @@ def test_routing_flag_and_expert_choice_limits():
     assert L.moe_combine(sp, F(), F(), F(), None, F(), None) == 2
     # and takes no load-balancing bias
     ws = moe.workspace_size(ec, moe.CALL_LAYER)
-    args = [F(), F(), F()] + [F()] * 3 + [None] * 3 + [F()] + [None] * 10 + [0.01, 1e-3, None, F(),
+    args = [F(), F(), F()] + [F()] * 3 + [None] * 3 + [F()] + [None] * 12 + [0.01, 1e-3, None, F(),
                                                                           ws, None]
     assert L.moe_layer_forward(sp, *args) == 1
     # its workspace holds the [E, T] score columns and row map
@@ -164,17 +164,26 @@ def test_entry_points_reject_before_launch():
     # layer: shared experts required when S > 0; b_new requires b
     s2 = moe.make_shape(64, 128, 8, 2, 256, S=2)
     ws = moe.workspace_size(s2, moe.CALL_LAYER)
-    # x, W_r, b, W_gate, W_up, W_down, Ws_gate/up/down, y, 10 optional outputs, lambda, gamma,
+    # x, W_r, b, W_gate, W_up, W_down, Ws_gate/up/down, y, 12 optional outputs, lambda, gamma,
     # saved, ws
-    args = [F()] * 2 + [None] + [F()] * 3 + [None] * 3 + [F()] + [None] * 10 + [0.01, 1e-3, None,
+    args = [F()] * 2 + [None] + [F()] * 3 + [None] * 3 + [F()] + [None] * 12 + [0.01, 1e-3, None,
                                                                                F(), ws, None]
     assert L.moe_layer_forward(ctypes.byref(s2), *args) == 1
-    args = [F()] * 2 + [None] + [F()] * 3 + [None] * 3 + [F()] + [None] * 9 + [F(), 0.01, 1e-3,
-                                                                              None, F(), ws, None]
+    # b_new without b
+    args = [F()] * 2 + [None] + [F()] * 3 + [None] * 3 + [F()] + [None] * 9 + [F(), None, None,
+                                                                              0.01, 1e-3, None,
+                                                                              F(), ws, None]
     assert L.moe_layer_forward(sp, *args) == 1
+    # misaligned placement outputs
+    for pos in (10, 11):
+        opt = [None] * 12
+        opt[pos] = ctypes.c_void_p(4096 + 4)
+        args = [F()] * 2 + [None] + [F()] * 3 + [None] * 3 + [F()] + opt + [0.01, 1e-3, None,
+                                                                            F(), ws, None]
+        assert L.moe_layer_forward(sp, *args) == 1
     # saved pre-activations: bf16 layers only, 16-byte aligned
     ws = moe.workspace_size(s, moe.CALL_LAYER)
-    base = [F()] * 2 + [None] + [F()] * 3 + [None] * 3 + [F()] + [None] * 10 + [0.01, 1e-3]
+    base = [F()] * 2 + [None] + [F()] * 3 + [None] * 3 + [F()] + [None] * 12 + [0.01, 1e-3]
     assert L.moe_layer_forward(sp, *base, ctypes.c_void_p(4096 + 8), F(), ws, None) == 1
     s32 = moe.make_shape(64, 128, 8, 2, 256, dtype=torch_f32())
     ws32 = moe.workspace_size(s32, moe.CALL_LAYER)
@@ -245,6 +254,17 @@ def test_layer_backward_rejects_before_launch():
     assert call(shape=ctypes.byref(big_shared), ws_bytes=0) == 2
     fits = moe.make_shape(64, 4096, 8, 2, 131072, S=1)           # 2 GiB: only the workspace fails
     assert call(shape=ctypes.byref(fits), ws_bytes=0) == 3
+    # the weight-gradient operands hold 64 (ceil(R / 64) + E) columns, addressed in 32 bits
+    rows = moe.make_shape(2**21, 64, 8, 8, 64)                   # R = 2^24 routed rows
+    assert call(shape=ctypes.byref(rows), ws_bytes=0) == 2
+    rows_ok = moe.make_shape(2**17, 64, 8, 8, 64)                # R = 2^20
+    assert call(shape=ctypes.byref(rows_ok), ws_bytes=0) == 3
+    # shared-expert weights must be aligned like the others
+    for pos in (6, 7, 8):
+        ins = [F(), F(), None, F(), F(), F(), F(), F(), F(), F()]
+        ins[pos] = ctypes.c_void_p(4096 + 8)
+        assert L.moe_layer_backward(sp, *ins, 0.01, 1e-3, *[F() for _ in range(8)], None, None,
+                                    F(), ws, None) == 1
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
@@ -279,7 +299,41 @@ def test_saved_size_is_the_pre_activation_layout():
         else:
             R = T * k if C < 0 else min(T * k, E * C)
         S = kw.get("S", 0)
-        want = 2 * al(R * M * 4) + (2 * al(T * S * M * 4) if S else 0)
+        want = 2 * al(R * M * 4) + (2 * al(T * S * M * 4) if S else 0) + al(E * 4)
         assert moe.saved_size(s) == want, (kw, moe.saved_size(s), want)
+        assert moe.routed_rows(s) == R
     assert moe.saved_size(moe.make_shape(96, 128, 8, 2, 256, dtype=torch_f32())) == 0
     assert moe.saved_size(moe.make_shape(96, 128, 8, 9, 256)) == 0     # invalid shape
+    assert moe.routed_rows(moe.make_shape(96, 128, 8, 9, 256)) == -1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=2**21), moe.MOE_OK),
+    (dict(d=2**21 + 8), moe.MOE_ERR_UNSUPPORTED),
+    (dict(M=2**20), moe.MOE_OK),
+    (dict(M=2**20 + 8), moe.MOE_ERR_UNSUPPORTED),
+    (dict(M=2**19, S=2), moe.MOE_OK),
+    (dict(M=2**19, S=3), moe.MOE_ERR_UNSUPPORTED),
+])
+def test_width_limits(kw, status):
+    # a 256-row operand slab of the grouped GEMMs is addressed with 32-bit byte offsets
+    args = dict(T=64, d=128, E=8, k=2, M=256)
+    args.update(kw)
+    assert moe.check_shape(moe.make_shape(**args)) == status
+
+
+def test_shared_stack_is_checked_by_the_binding():
+    import torch
+    T, d, E, k, M = 8, 16, 4, 2, 8
+    x = torch.zeros(T, d, dtype=torch.bfloat16)
+    Wg = torch.zeros(E, M, d, dtype=torch.bfloat16)
+    Wd = torch.zeros(E, d, M, dtype=torch.bfloat16)
+    Wr = torch.zeros(E, d, dtype=torch.bfloat16)
+    stacked3d = (torch.zeros(2, M, d), torch.zeros(2, M, d), torch.zeros(2, d, M))
+    for fn in (moe.moe_layer_forward, moe.moe_layer_backward):
+        extra = (x,) if fn is moe.moe_layer_backward else ()
+        with pytest.raises(ValueError, match="Ws_gate must be"):
+            fn(x, Wr, Wg, Wg, Wd, *extra, k=k, shared=stacked3d)
+        with pytest.raises(ValueError, match="Ws_gate must be"):   # S*M not a multiple of M
+            fn(x, Wr, Wg, Wg, Wd, *extra, k=k,
+               shared=(torch.zeros(12, d), torch.zeros(12, d), torch.zeros(d, 12)))

@@ -724,6 +724,19 @@ def check_layer(mod=O):
     sub = mod.layer_forward(x, Wr, Wg, Wu, Wd, k=2, shared=sh, tokens=[3, 17, 39])
     full = mod.layer_forward(x, Wr, Wg, Wu, Wd, k=2, shared=sh)
     assert np.allclose(sub["y"], full["y"][[3, 17, 39]], rtol=1e-14, atol=0)
+    # term magnitudes: never below |y| (triangle inequality), equal to it without cancellation
+    full = mod.layer_forward(x, Wr, Wg, Wu, Wd, k=2, shared=sh, magnitudes=True)
+    assert np.all(full["magnitude"] >= np.abs(full["y"]) * (1 - 1e-14))
+    assert (full["magnitude"] > np.abs(full["y"]) * (1 + 1e-6)).any()
+    x1, Wr1, Wg1, Wu1, Wd1 = _tiny_layer(E=1)
+    one = mod.layer_forward(x1, Wr1, Wg1, Wu1, Wd1, k=1, magnitudes=True)
+    assert np.allclose(one["magnitude"], np.abs(one["y"]), rtol=1e-14, atol=0)
+    # identical experts with renormalised gates: sum_j w_j |FFN| = |FFN|
+    x, Wr, Wg, Wu, Wd = _tiny_layer(E=5, k=3)
+    Wg[:], Wu[:], Wd[:] = Wg[0], Wu[0], Wd[0]
+    same = mod.layer_forward(x, Wr, Wg, Wu, Wd, k=3, magnitudes=True)
+    assert np.allclose(same["magnitude"], np.abs(mod.swiglu_expert(x, Wg[0], Wu[0], Wd[0])),
+                       rtol=1e-12, atol=1e-14)
 
 
 def test_layer_pins():
@@ -785,8 +798,9 @@ def check_shared(mod=O):
     sh = (rng.standard_normal((8, 16)), rng.standard_normal((8, 16)), rng.standard_normal((16, 8)))
     ffn = O.swiglu_expert(x, *sh)                 # pinned on its own (check_experts)
     zero_down = np.zeros_like(Wd)                 # every routed expert outputs 0
-    res = mod.layer_forward(x, Wr, Wg, Wu, zero_down, k=2, shared=[sh])
+    res = mod.layer_forward(x, Wr, Wg, Wu, zero_down, k=2, shared=[sh], magnitudes=True)
     assert np.allclose(res["y"], ffn, rtol=1e-13, atol=1e-14)
+    assert np.allclose(res["magnitude"], np.abs(ffn), rtol=1e-13, atol=1e-14)
     # S identical shared experts give S times the FFN
     res3 = mod.layer_forward(x, Wr, Wg, Wu, zero_down, k=2, shared=[sh, sh, sh])
     assert np.allclose(res3["y"], 3.0 * ffn, rtol=1e-13, atol=1e-13)
