@@ -51,7 +51,9 @@ typedef enum {
   MOE_ERR_INVALID_ARGUMENT = 1, /* a size, pointer, alignment or flag is invalid            */
   MOE_ERR_UNSUPPORTED = 2,      /* valid, but beyond this build's limits (E, k, dtype)       */
   MOE_ERR_WORKSPACE = 3,        /* workspace missing or smaller than moe_workspace_size()    */
-  MOE_ERR_HIP = 4               /* a kernel launch failed                                   */
+  MOE_ERR_HIP = 4,              /* a kernel launch failed                                   */
+  MOE_ERR_SCRATCH = 5           /* moe_layer_forward_noalloc: the shape needs more workspace
+                                   than its static scratch (MOE_SCRATCH_BYTES)               */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -261,6 +263,30 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
                              float* f, float* P, float* aux, float* z, float* diag, float* b_new,
                              int32_t* inv_perm, int32_t* perm_token, float lambda, float gamma,
                              void* saved, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_layer_forward_noalloc -- moe_layer_forward for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments, outputs and kernels, with the workspace taken from a static device array of
+ * MOE_SCRATCH_BYTES that the library holds on each device it runs on until the process ends.
+ * Nothing is allocated or freed. The array of the current device is used (the stream must belong
+ * to it); its address is looked up on the first call on that device.
+ * Limit: shapes with moe_workspace_size(s, MOE_CALL_LAYER) > MOE_SCRATCH_BYTES return
+ * MOE_ERR_SCRATCH before anything is enqueued (e.g. the Mixtral-shaped layer, d = 4096,
+ * M = 14336, E = 8, k = 2, up to about 900 tokens). No scratch contents carry over between calls
+ * (every part is written before it is read). Calls on one device share its array: calls that
+ * overlap in time on that device (other streams, other threads) race and must be serialised by
+ * the caller. The caller still passes every input and output.
+ */
+#define MOE_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_layer_forward_noalloc(const moe_shape* s, const void* x, const void* W_r,
+                                     const float* b, const void* W_gate, const void* W_up,
+                                     const void* W_down, const void* Ws_gate, const void* Ws_up,
+                                     const void* Ws_down, void* y, int32_t* topk_idx,
+                                     float* topk_w, int32_t* counts, int32_t* overflow, float* f,
+                                     float* P, float* aux, float* z, float* diag, float* b_new,
+                                     int32_t* inv_perm, int32_t* perm_token, float lambda,
+                                     float gamma, void* saved, void* stream);
 
 /*
  * moe_balance_loss_backward -- gradient of the layer's balance losses through the router.

@@ -19,7 +19,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
 
-MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, \
+    MOE_ERR_SCRATCH = range(6)
+SCRATCH_BYTES = 64 << 20  # MOE_SCRATCH_BYTES: static scratch of moe_layer_forward_noalloc
 MOE_F32, MOE_BF16 = 0, 1
 CALL_ROUTE, CALL_DISPATCH, CALL_EXPERT_FFN, CALL_LAYER, CALL_LOSS_BACKWARD, CALL_LAYER_BACKWARD = range(6)
 E_MAX, K_MAX = 256, 16
@@ -64,6 +66,10 @@ _SIG = {
                                          _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                          ctypes.c_float, ctypes.c_float, _P, _P, ctypes.c_size_t,
                                          _P]),
+    "moe_layer_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P,
+                                                 _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                 _P, _P, _P, ctypes.c_float, ctypes.c_float, _P,
+                                                 _P]),
     "moe_set_stage_events": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]),
     "moe_balance_loss_backward": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, ctypes.c_float,
                                                  ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t,
@@ -399,18 +405,21 @@ def moe_layer_backward(x, W_r, W_gate, W_up, W_down, dy, k: int, b=None, shared=
 
 
 class MoELayer:
-    """Holds the sizes and a preallocated workspace; ``forward`` calls moe_layer_forward."""
+    """Holds the sizes and a preallocated workspace; ``forward`` calls moe_layer_forward, or, with
+    ``noalloc=True``, moe_layer_forward_noalloc, which takes its workspace from the library's
+    static scratch (construct with ``with_workspace=False`` and pass preallocated ``out`` tensors
+    to allocate nothing at all)."""
 
     def __init__(self, T: int, d: int, E: int, k: int, M: int, S: int = 0,
                  c: Optional[float] = None, renorm: bool = True,
                  dtype: torch.dtype = torch.bfloat16, device="cuda", scoring: str = "softmax",
-                 routing: str = "token"):
+                 routing: str = "token", with_workspace: bool = True):
         self.shape = make_shape(T, d, E, k, M, S, c, renorm, dtype, scoring, routing)
         _check(check_shape(self.shape), "MoELayer")
         self.T, self.d, self.E, self.k, self.M, self.S = T, d, E, k, M, S
         self.dtype = dtype
         self.device = torch.device(device)
-        self.ws = workspace(self.shape, CALL_LAYER, self.device)
+        self.ws = workspace(self.shape, CALL_LAYER, self.device) if with_workspace else None
 
     def alloc_outputs(self, with_bias: bool = False, placement: bool = False) -> dict:
         """Output tensors; ``placement`` adds inv_perm [T, k] (token choice) and perm_token
@@ -439,7 +448,7 @@ class MoELayer:
 
     def forward(self, x, W_r, W_gate, W_up, W_down, b=None, shared=None, lam: float = 0.01,
                 gamma: float = 1e-3, out: Optional[dict] = None,
-                saved: Optional[torch.Tensor] = None) -> dict:
+                saved: Optional[torch.Tensor] = None, noalloc: bool = False) -> dict:
         T, d, E, M, dt = self.T, self.d, self.E, self.M, self.dtype
         _dev(x, "x", dt, (T, d))
         _dev(W_r, "W_r", dt, (E, d))
@@ -461,15 +470,20 @@ class MoELayer:
             out = self.alloc_outputs(with_bias=b is not None)
         if saved is not None:
             _saved_ok(saved, self.shape, self.device)
-        _check(lib().moe_layer_forward(
-            ctypes.byref(self.shape), _ptr(x), _ptr(W_r), _ptr(b), _ptr(W_gate), _ptr(W_up),
-            _ptr(W_down), _ptr(sg), _ptr(su), _ptr(sd), _ptr(out["y"]), _ptr(out.get("topk_idx")),
-            _ptr(out.get("topk_w")), _ptr(out.get("counts")), _ptr(out.get("overflow")),
-            _ptr(out.get("f")), _ptr(out.get("P")), _ptr(out.get("aux")), _ptr(out.get("z")),
-            _ptr(out.get("diag")), _ptr(out.get("b_new") if b is not None else None),
-            _ptr(out.get("inv_perm")), _ptr(out.get("perm_token")), float(lam), float(gamma),
-            _ptr(saved),
-            _ptr(self.ws), self.ws.numel(), _stream()), "moe_layer_forward")
+        args = (ctypes.byref(self.shape), _ptr(x), _ptr(W_r), _ptr(b), _ptr(W_gate), _ptr(W_up),
+                _ptr(W_down), _ptr(sg), _ptr(su), _ptr(sd), _ptr(out["y"]),
+                _ptr(out.get("topk_idx")), _ptr(out.get("topk_w")), _ptr(out.get("counts")),
+                _ptr(out.get("overflow")), _ptr(out.get("f")), _ptr(out.get("P")),
+                _ptr(out.get("aux")), _ptr(out.get("z")), _ptr(out.get("diag")),
+                _ptr(out.get("b_new") if b is not None else None), _ptr(out.get("inv_perm")),
+                _ptr(out.get("perm_token")), float(lam), float(gamma), _ptr(saved))
+        if noalloc:
+            _check(lib().moe_layer_forward_noalloc(*args, _stream()), "moe_layer_forward_noalloc")
+        else:
+            if self.ws is None:
+                raise ValueError("this layer has no workspace: pass noalloc=True")
+            _check(lib().moe_layer_forward(*args, _ptr(self.ws), self.ws.numel(), _stream()),
+                   "moe_layer_forward")
         return out
 
 

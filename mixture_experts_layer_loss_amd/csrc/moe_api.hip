@@ -305,6 +305,31 @@ LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Static scratch of moe_layer_forward_noalloc: one copy per device, held until the process ends.
+// Host code never uses the array's name as an address (on the host it is only a stand-in): the
+// device address comes from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[MOE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on the first call on that device).
+moe_status current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 // Profiling aid: events recorded at the end of each moe_layer_forward stage (see moe.h). The
 // setting is process-wide (the one piece of state the library keeps); it is read and written
 // under a lock, and each forward works on the copy it takes when it starts.
@@ -361,6 +386,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_SCRATCH: return "shape needs more than the static scratch of the no-allocation call";
     default: return "unknown status";
   }
 }
@@ -641,6 +667,32 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
   marks.mark(7, hs);
   if (e == hipSuccess) e = marks.err;
   return hip_status(e);
+}
+
+moe_status moe_layer_forward_noalloc(const moe_shape* s, const void* x, const void* W_r,
+                                     const float* b, const void* W_gate, const void* W_up,
+                                     const void* W_down, const void* Ws_gate, const void* Ws_up,
+                                     const void* Ws_down, void* y, int32_t* topk_idx,
+                                     float* topk_w, int32_t* counts, int32_t* overflow, float* f,
+                                     float* P, float* aux, float* z, float* diag, float* b_new,
+                                     int32_t* inv_perm, int32_t* perm_token, float lambda,
+                                     float gamma, void* saved, void* stream) {
+  moe_status st = moe_check_shape(s);
+  if (st != MOE_OK) return st;
+  const size_t need = moe_workspace_size(s, MOE_CALL_LAYER);
+  if (need > MOE_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  // every argument check of the allocating call, before the scratch is looked up: a dry run with
+  // a null workspace fails only on the workspace if everything else is valid
+  st = moe_layer_forward(s, x, W_r, b, W_gate, W_up, W_down, Ws_gate, Ws_up, Ws_down, y, topk_idx,
+                         topk_w, counts, overflow, f, P, aux, z, diag, b_new, inv_perm,
+                         perm_token, lambda, gamma, saved, nullptr, 0, stream);
+  if (st != MOE_ERR_WORKSPACE) return st == MOE_OK ? MOE_ERR_HIP : st;
+  void* ws = nullptr;
+  st = current_scratch(&ws);
+  if (st != MOE_OK) return st;
+  return moe_layer_forward(s, x, W_r, b, W_gate, W_up, W_down, Ws_gate, Ws_up, Ws_down, y,
+                           topk_idx, topk_w, counts, overflow, f, P, aux, z, diag, b_new, inv_perm,
+                           perm_token, lambda, gamma, saved, ws, MOE_SCRATCH_BYTES, stream);
 }
 
 moe_status moe_balance_loss_backward(const moe_shape* s, const void* x, const void* W_r,

@@ -267,6 +267,31 @@ def test_layer_backward_rejects_before_launch():
                                     F(), ws, None) == 1
 
 
+def test_noalloc_forward_limits_and_checks():
+    # the no-allocation forward refuses shapes whose workspace exceeds its static scratch, and
+    # makes every argument check of moe_layer_forward, all before touching a device
+    L = moe.lib()
+    F = _fake
+    big = moe.make_shape(4096, 4096, 8, 2, 14336)
+    assert moe.workspace_size(big, moe.CALL_LAYER) > moe.SCRATCH_BYTES
+    opt = [None] * 12
+    args = [F()] * 2 + [None] + [F()] * 3 + [None] * 3 + [F()] + opt + [0.01, 1e-3, None, None]
+    assert L.moe_layer_forward_noalloc(ctypes.byref(big), *args) == moe.MOE_ERR_SCRATCH
+    assert "scratch" in moe.status_string(moe.MOE_ERR_SCRATCH)
+    small = moe.make_shape(256, 4096, 8, 2, 14336)
+    assert moe.workspace_size(small, moe.CALL_LAYER) <= moe.SCRATCH_BYTES
+    bad = list(args)
+    bad[0] = None                                                # no x
+    assert L.moe_layer_forward_noalloc(ctypes.byref(small), *bad) == 1
+    bad = list(args)
+    bad[1] = ctypes.c_void_p(4096 + 2)                           # misaligned W_r
+    assert L.moe_layer_forward_noalloc(ctypes.byref(small), *bad) == 1
+    s2 = moe.make_shape(64, 128, 8, 2, 256, S=2)                 # shared experts missing
+    assert L.moe_layer_forward_noalloc(ctypes.byref(s2), *args) == 1
+    assert L.moe_layer_forward_noalloc(ctypes.byref(moe.make_shape(64, 128, 8, 9, 256)),
+                                       *args) == 1               # invalid shape
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(moe, "_lib_handle", None)
