@@ -68,8 +68,8 @@ __device__ int block_scan_256(int v, int* buf) {
 }
 
 // One block of 1024 threads. Thread (p, e) owns expert e (< EP, the power of two >= E) and part p
-// of the block range; parts are summed, scanned over p and walked again to write the per-block
-// bases, so every sum is taken in a fixed order.
+// of the block range; parts are summed, scanned over p in log2(P) rounds and walked again to
+// write the per-block bases, so every sum is taken in a fixed order.
 __global__ __launch_bounds__(1024) void scan_kernel(
     int64_t T, int E, int64_t C, int nblk, const int32_t* __restrict__ hist,
     const float* __restrict__ gpart, int nblk_g, const float* __restrict__ lpart,
@@ -106,25 +106,30 @@ __global__ __launch_bounds__(1024) void scan_kernel(
   }
   pg[tid] = gs;
   __syncthreads();
-  if (e < E) {
-    int base = 0;
-    for (int q = 0; q < p; ++q) base += psum[q * EP + e];
-    if (block_base != nullptr) {
+  // over the parts of each expert, in log2(P) rounds: an inclusive prefix of the counts
+  // (Hillis-Steele) and a pairwise tree sum of g (pairs fixed by the part index: reproducible)
+  for (int off = 1; off < P; off <<= 1) {
+    const int add = p >= off ? psum[tid - off * EP] : 0;
+    const int half = P / (2 * off);
+    const double gadd = p < half ? pg[tid + half * EP] : 0.0;
+    __syncthreads();
+    psum[tid] += add;
+    if (p < half) pg[tid] += gadd;
+    __syncthreads();
+  }
+  if (e < E && block_base != nullptr) {
+    int base = psum[tid] - cnt;  // the counts of the lower parts
 #pragma unroll 16
-      for (int b = b0; b < b1; ++b) {
-        block_base[static_cast<int64_t>(b) * E + e] = base;
-        base += hist[static_cast<int64_t>(b) * E + e];
-      }
+    for (int b = b0; b < b1; ++b) {
+      block_base[static_cast<int64_t>(b) * E + e] = base;
+      base += hist[static_cast<int64_t>(b) * E + e];
     }
   }
   // per-expert totals (threads of part 0)
   int n = 0, kept = 0;
   if (p == 0 && e < E) {
-    double g = 0.0;
-    for (int q = 0; q < P; ++q) {
-      n += psum[q * EP + e];
-      g += pg[q * EP + e];
-    }
+    n = psum[(P - 1) * EP + e];
+    const double g = pg[e];
     kept = (C < 0 || n <= C) ? n : static_cast<int>(C);
     if (n_out != nullptr) n_out[e] = n;
     if (gsum != nullptr) gsum[e] = g;

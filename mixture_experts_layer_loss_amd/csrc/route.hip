@@ -544,12 +544,22 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
 // ------------------------------------------------------------------------------------------
 // bf16 with many experts (E > 16): W_r is shared through LDS. A block owns 64 tokens; its eight
 // waves are 4 token blocks of 16 x 2 expert halves and each runs the whole hidden dimension, so
-// x is streamed once per block and W_r once per block. The x and W_r k-slices (64 wide) pass
-// through two LDS stages (row stride 72 bf16 = 144 bytes: the 16x16x32 fragment reads are bank-
-// conflict-free) with the next slice prefetched into registers; one barrier per k-step.
+// x is streamed once per block and W_r once per block. The x and W_r k-slices (128 wide where two
+// stages fit in 120 KB, else 64: longer contiguous row reads) pass through two LDS stages (rows
+// padded by 8 bf16: the 16x16x32 fragment reads are bank-conflict-free) with the next slices
+// prefetched into a register ring two deep; one barrier per k-step.
 // ------------------------------------------------------------------------------------------
-constexpr int kSK = 64;         // k per step
-constexpr int kSKP = kSK + 8;   // padded LDS row (bf16 elements)
+#ifndef MOE_ROUTE_SK
+#define MOE_ROUTE_SK 128
+#endif
+#ifndef MOE_ROUTE_PF
+#define MOE_ROUTE_PF 2
+#endif
+// k per step: MOE_ROUTE_SK where two stages of (64 + 16 NEB) padded rows fit in 120 KB, else 64
+template <int NEB>
+constexpr int route_sk() {
+  return 2 * (64 + 16 * NEB) * (MOE_ROUTE_SK + 8) * 2 <= 120 * 1024 ? MOE_ROUTE_SK : 64;
+}
 
 // SPLIT: per-token routing by all waves (route_tokens_split) rather than one lane per token; its
 // exchange buffers are only allocated then, so that the other variant keeps two blocks per CU.
@@ -560,9 +570,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
     float* __restrict__ topk_w, int32_t* __restrict__ hist, float* __restrict__ gpart,
     float* __restrict__ lpart, float* __restrict__ hpart, float* __restrict__ cols) {
   constexpr int TB = 64;
+  constexpr int kSK = route_sk<NEB>();  // k per step
+  constexpr int kSKP = kSK + 8;         // padded LDS row (bf16 elements)
   constexpr int ROWS = TB + 16 * NEB;                 // x rows then W_r rows of a stage
   constexpr int STAGE = ROWS * kSKP;                  // bf16 elements
-  constexpr int CH = ROWS * (kSK / 8);                // 16-byte chunks per stage
+  constexpr int CPR = kSK / 8;                        // 16-byte chunks per row of a stage
+  constexpr int CH = ROWS * CPR;                      // 16-byte chunks per stage
   constexpr int CPT = (CH + kRouteThreads - 1) / kRouteThreads;
   constexpr int NEBH = (NEB + 1) / 2;                 // expert blocks per wave
   constexpr int kStagesBytes = 2 * STAGE * 2;
@@ -581,12 +594,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TB;
   const int r16 = lane & 15, kg = lane >> 4;
 
-  // chunk c of a stage: row c / 8 (x rows 0..63, then W_r rows), 8 bf16 at column (c % 8) * 8
+  // chunk c of a stage: row c / CPR (x rows 0..63, then W_r rows), 8 bf16 at column (c % CPR) * 8
   const bf16_t* src[CPT];
   bool ok[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int c = i * kRouteThreads + tid, r = c >> 3, col = (c & 7) * 8;
+    const int c = i * kRouteThreads + tid, r = c / CPR, col = (c % CPR) * 8;
     ok[i] = c < CH;
     if (r < TB) {
       int64_t t = t0 + r;
@@ -601,13 +614,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   // a ring of PF k-slices in registers ahead of the two LDS stages: a k-step's MFMA work is short
   // next to the memory latency, so several slices must be in flight
-  constexpr int PF = 4;
+  constexpr int PF = MOE_ROUTE_PF;
   u32x4 rg[PF][CPT];
   auto gload = [&](u32x4 (&r)[CPT], int k0) __attribute__((always_inline)) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int col = ((i * kRouteThreads + tid) & 7) * 8;
+      const int col = ((i * kRouteThreads + tid) % CPR) * 8;
       r[i] = (ok[i] && k0 + col < d) ? *reinterpret_cast<const u32x4*>(src[i] + k0) : zero;
     }
   };
@@ -615,7 +628,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = i * kRouteThreads + tid;
-      if (c < CH) *reinterpret_cast<u32x4*>(st + stage * STAGE + (c >> 3) * kSKP + (c & 7) * 8) = r[i];
+      if (c < CH) *reinterpret_cast<u32x4*>(st + stage * STAGE + (c / CPR) * kSKP + (c % CPR) * 8) = r[i];
     }
   };
   f32x4 acc[NEBH];
