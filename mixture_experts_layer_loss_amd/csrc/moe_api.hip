@@ -12,10 +12,10 @@ namespace moe {
 hipError_t launch_gemm_up_bf16(int groups, int d, int Mg, const void* rows,
                                const int32_t* gather, const int32_t* offsets,
                                const int32_t* tile_off, int64_t max_tiles, const void* W_gate,
-                               const void* W_up, void* h, hipStream_t st);
+                               const void* W_up, void* h, hipStream_t st, int64_t a_rows);
 hipError_t launch_gemm_down_bf16(int groups, int d, int Mg, const int32_t* offsets,
                                  const int32_t* tile_off, int64_t max_tiles, const void* W_down,
-                                 const void* h, void* out, hipStream_t st);
+                                 const void* h, void* out, hipStream_t st, int64_t a_rows);
 hipError_t launch_gemm_up_f32(int groups, int d, int Mg, const void* rows,
                               const int32_t* gather, const int32_t* offsets,
                               const int32_t* tile_off, int64_t max_tiles, const void* W_gate,
@@ -46,21 +46,21 @@ hipError_t launch_gemm_down_f32(int groups, int d, int Mg, const int32_t* offset
 hipError_t launch_gemm_up(int dtype, int groups, int d, int Mg, const void* rows,
                           const int32_t* gather, const int32_t* offsets, const int32_t* tile_off,
                           int64_t max_tiles, const void* W_gate, const void* W_up, void* h,
-                          hipStream_t st) {
+                          hipStream_t st, int64_t a_rows) {
   return dtype == MOE_F32
              ? launch_gemm_up_f32(groups, d, Mg, rows, gather, offsets, tile_off, max_tiles,
                                   W_gate, W_up, h, st)
              : launch_gemm_up_bf16(groups, d, Mg, rows, gather, offsets, tile_off, max_tiles,
-                                   W_gate, W_up, h, st);
+                                   W_gate, W_up, h, st, a_rows);
 }
 
 hipError_t launch_gemm_down(int dtype, int groups, int d, int Mg, const int32_t* offsets,
                             const int32_t* tile_off, int64_t max_tiles, const void* W_down,
-                            const void* h, void* out, hipStream_t st) {
+                            const void* h, void* out, hipStream_t st, int64_t a_rows) {
   return dtype == MOE_F32 ? launch_gemm_down_f32(groups, d, Mg, offsets, tile_off, max_tiles,
                                                  W_down, h, out, st)
                           : launch_gemm_down_bf16(groups, d, Mg, offsets, tile_off, max_tiles,
-                                                  W_down, h, out, st);
+                                                  W_down, h, out, st, a_rows);
 }
 }  // namespace moe
 
@@ -520,10 +520,10 @@ moe_status moe_expert_ffn(const moe_shape* s, int32_t groups, int32_t Mg, const 
   if (e != hipSuccess) return MOE_ERR_HIP;
   const int64_t max_tiles = cdiv(max_rows, BM) + groups;
   e = launch_gemm_up(s->dtype, groups, s->d, Mg, rows, nullptr, offsets, tile_off, max_tiles,
-                     W_gate, W_up, h, hs);
+                     W_gate, W_up, h, hs, max_rows);
   if (e == hipSuccess)
     e = launch_gemm_down(s->dtype, groups, s->d, Mg, offsets, tile_off, max_tiles, W_down, h, out,
-                         hs);
+                         hs, max_rows);
   return hip_status(e);
 }
 
@@ -631,11 +631,11 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
                                  max_tiles, W_gate, W_up, p.h, sv.G, sv.U, hs);
   else if (e == hipSuccess)
     e = launch_gemm_up(s->dtype, s->E, s->d, s->M, x, p.perm_token, p.offsets, p.tile_off,
-                       max_tiles, W_gate, W_up, p.h, hs);
+                       max_tiles, W_gate, W_up, p.h, hs, s->T);
   marks.mark(3, hs);
   if (e == hipSuccess)
     e = launch_gemm_down(s->dtype, s->E, s->d, s->M, p.offsets, p.tile_off, max_tiles, W_down,
-                         p.h, p.out_perm, hs);
+                         p.h, p.out_perm, hs, routed_rows(s));
   marks.mark(4, hs);
   if (e == hipSuccess && s->S > 0) {
     const int SM = s->S * s->M;
@@ -646,10 +646,10 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
                                    Ws_gate, Ws_up, p.h_sh, sv.Gs, sv.Us, hs);
     else if (e == hipSuccess)
       e = launch_gemm_up(s->dtype, 1, s->d, SM, x, nullptr, p.sh_offsets, p.sh_tile_off, sh_tiles,
-                         Ws_gate, Ws_up, p.h_sh, hs);
+                         Ws_gate, Ws_up, p.h_sh, hs, s->T);
     if (e == hipSuccess)
       e = launch_gemm_down(s->dtype, 1, s->d, SM, p.sh_offsets, p.sh_tile_off, sh_tiles, Ws_down,
-                           p.h_sh, p.sh, hs);
+                           p.h_sh, p.sh, hs, s->T);
   }
   marks.mark(5, hs);
   if (e == hipSuccess && expert_choice(s))

@@ -20,12 +20,10 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays a (quiet) NaN.
+// fp32 -> bf16, round to nearest, ties to even (gfx950 converts in hardware: v_cvt_pk_bf16_f32);
+// NaN stays a NaN.
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
 template <typename T> struct Elem;
@@ -105,13 +103,15 @@ hipError_t launch_schedule(int groups, const int32_t* offsets, int32_t* tile_off
 //   gate/up: h[r] = SiLU(a_r W_gate[g]^T) * (a_r W_up[g]^T), a_r = rows[r], or rows[gather[r]]
 //            when gather != NULL (rows is then the token matrix)
 //   down:    out[r] = h[r] W_down[g]^T
+// a_rows: rows of the matrix the product reads (rows, or h), which lets the bf16 kernels address
+// it with 32-bit offsets when it spans less than 4 GiB.
 hipError_t launch_gemm_up(int dtype, int groups, int d, int Mg, const void* rows,
                           const int32_t* gather, const int32_t* offsets, const int32_t* tile_off,
                           int64_t max_tiles, const void* W_gate, const void* W_up, void* h,
-                          hipStream_t st);
+                          hipStream_t st, int64_t a_rows);
 hipError_t launch_gemm_down(int dtype, int groups, int d, int Mg, const int32_t* offsets,
                             const int32_t* tile_off, int64_t max_tiles, const void* W_down,
-                            const void* h, void* out, hipStream_t st);
+                            const void* h, void* out, hipStream_t st, int64_t a_rows);
 
 // Gradient of aux + z_coef z with respect to the logits, from the router's logit and score
 // columns [E][T]; n [E] loads, fden the f_e denominator. dl [T][E] and dlT [E][T] fp32.
