@@ -356,6 +356,14 @@ def main():
     eb = 2 if cfg.dtype == "bf16" else 4
     fl = {"gemm_up": 4.0 * d * M * kept, "gemm_down": 2.0 * d * M * kept,
           "shared": 6.0 * d * S * M * T, "route": 2.0 * d * E * T}
+    # bf16 layers run their shared experts inside the routed grouped launches (a second product
+    # of one group): the shared stage then reads ~0 and its flops belong to the GEMM stages
+    sh_ms = float(stage_ms[moe.STAGES.index("shared")])
+    shared_folded = S > 0 and sh_ms < 0.02 * float(stage_ms[moe.STAGES.index("gemm_up")])
+    if shared_folded:
+        fl["gemm_up"] += 4.0 * d * S * M * T
+        fl["gemm_down"] += 2.0 * d * S * M * T
+        fl["shared"] = 0.0
     by = {"route": T * d * eb + E * d * eb + T * k * 8,
           # placement only (indices); the gate/up GEMM gathers the x rows itself
           "dispatch": T * k * 8 + kept * 4,
@@ -379,7 +387,9 @@ def main():
     achieved = fl["gemm_up"] / (up_ms * 1e-3) / 1e12
     traffic = load_traffic(name)
     up_each = stage_each[:, moe.STAGES.index("gemm_up")]
-    roofline = {"bound": "mfma", "kernel": "grouped_gemm_kernel<0> (routed gate/up + SwiGLU)",
+    roofline = {"bound": "mfma",
+                "kernel": "grouped gate/up GEMM + SwiGLU (routed" +
+                          (" and shared experts, one launch)" if shared_folded else ")"),
                 "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "flops_per_launch": fl["gemm_up"], "ms_per_launch": round(up_ms, 4),

@@ -511,21 +511,35 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
                                              group_stride, N, K, C, C2, C3);
 }
 
+// One grouped product of the persistent kernel: groups of rows [offsets[g], offsets[g+1]) of A
+// (row r is A[gather[r]] when gather is set), weights B0 (and B1 for the paired gate/up columns)
+// at group_stride per group, N output columns, reduction K, output C [rows][N].
+struct GemmProb {
+  const bf16_t* A;
+  const int32_t* gather;
+  const int32_t* offsets;
+  const int32_t* tile_off;  // three tile tables of groups + 1 entries
+  const bf16_t* B0;
+  const bf16_t* B1;
+  int64_t group_stride;
+  bf16_t* C;
+  int groups, N, K;
+};
+
 // Persistent form of the forward products (EPI 0: SwiGLU to bf16 h; EPI 1: plain bf16) for K of
-// 2..128 k-slices. A block runs a strided list of the 256-row tiles of its XCD's range (slot s of
-// S takes tiles x q + s, x q + s + S, ...), and the k-step pipeline runs on across tiles: the last
-// two k-steps of a tile load the first two k-slices of the block's next tile, the last one stores
-// the first of them and reads its first fragments, so the next tile's MFMAs start right after this
-// tile's epilogue with no memory round trip, tile lookup or block launch in between. The next
-// tile's group, rows and A-row offsets are looked up at the start of the current tile. The
-// epilogue goes through the LDS stage the tile's last k-step read; the other stage holds the next
-// tile's first slice.
+// 2..128 k-slices, over the 256-row tiles of one or two products (the routed experts, and the
+// shared experts as a second product of one group). Each XCD x owns the tiles [x q_p, (x+1) q_p)
+// of each product p (the second product's first: its tiles are the longer ones when K differs);
+// slot s of its S blocks takes entries s, s + S, ... of that list, and the k-step pipeline runs on
+// across tiles: the last two k-steps of a tile load the first two k-slices of the block's next
+// tile, the last one stores the first of them and reads its first fragments, so the next tile's
+// MFMAs start right after this tile's epilogue with no memory round trip, tile lookup or block
+// launch in between. The next tile's product, group, rows and A-row offsets are looked up at the
+// start of the current tile. The epilogue goes through the LDS stage the tile's last k-step read;
+// the other stage holds the next tile's first slice.
 template <int EPI, bool KTAIL, bool GATHER>
-__device__ __forceinline__ void run_tiles_persistent(
-    unsigned char* lds, const bf16_t* __restrict__ A, const int32_t* __restrict__ gather,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ t256, int groups,
-    const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, int64_t group_stride, int N,
-    int K, bf16_t* __restrict__ C, int nblocks) {
+__device__ __forceinline__ void run_tiles_persistent(unsigned char* lds, const GemmProb& P0,
+                                                     const GemmProb& P1, int nblocks) {
   static_assert(EPI == 0 || EPI == 1, "persistent tiles serve the forward products");
   using G = Geo<256>;
   constexpr bool PAIRED = EPI == 0, SWIGLU = EPI == 0;
@@ -533,71 +547,85 @@ __device__ __forceinline__ void run_tiles_persistent(
   constexpr int MI = G::MI, NJ = G::NJ, ACH = G::ACH, BCH = G::BCH, RS = G::RSTEP;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / G::WN, wn = wave % G::WN;
-  const int lda = K, ldb = K, ldc = N;
-  const int nb_count = (N + BNO - 1) / BNO;
 
-  const int64_t ntiles = static_cast<int64_t>(t256[groups]) * nb_count;
-  const int64_t q = (ntiles + NXCD - 1) / NXCD;
+  const int nb0 = (P0.N + BNO - 1) / BNO;
+  const int nb1 = P1.groups > 0 ? (P1.N + BNO - 1) / BNO : 0;
+  const int64_t nt0 = static_cast<int64_t>(P0.tile_off[P0.groups]) * nb0;
+  const int64_t nt1 = P1.groups > 0 ? static_cast<int64_t>(P1.tile_off[P1.groups]) * nb1 : 0;
+  const int64_t q0 = (nt0 + NXCD - 1) / NXCD, q1 = (nt1 + NXCD - 1) / NXCD;
   const int S = nblocks / NXCD;
   const int xcd = static_cast<int>(blockIdx.x) % NXCD, slot = static_cast<int>(blockIdx.x) / NXCD;
-  const int64_t xend = min(static_cast<int64_t>(xcd + 1) * q, ntiles);
-  int64_t L = static_cast<int64_t>(xcd) * q + slot;
-  if (L >= xend) return;
+  const int64_t b1 = static_cast<int64_t>(xcd) * q1, b0 = static_cast<int64_t>(xcd) * q0;
+  const int64_t n1x = max(int64_t{0}, min(b1 + q1, nt1) - b1);
+  const int64_t n0x = max(int64_t{0}, min(b0 + q0, nt0) - b0);
+  const int64_t xend = n1x + n0x;  // entries of this XCD's list
+  int64_t J = slot;
+  if (J >= xend) return;
 
   struct Tile {
-    int g, row_begin, rows, n0;
+    int p, g, row_begin, rows, n0;
   };
-  auto describe = [&](int64_t Lt) __attribute__((always_inline)) {
+  auto describe = [&](int64_t Jt) __attribute__((always_inline)) {
     Tile t;
-    t.g = find_group(t256, groups, nb_count, Lt);
-    const int mt_g = t256[t.g + 1] - t256[t.g];
-    const int64_t local = Lt - static_cast<int64_t>(t256[t.g]) * nb_count;
-    const int nb = static_cast<int>(local / mt_g), mt = static_cast<int>(local % mt_g);
-    t.row_begin = offsets[t.g] + mt * 256;
-    t.rows = min(256, offsets[t.g + 1] - t.row_begin);
-    t.n0 = nb * BNO;
+    t.p = Jt < n1x ? 1 : 0;
+    const GemmProb& P = t.p ? P1 : P0;
+    const int nb = t.p ? nb1 : nb0;
+    const int64_t Lt = t.p ? b1 + Jt : b0 + (Jt - n1x);
+    t.g = find_group(P.tile_off, P.groups, nb, Lt);
+    const int mt_g = P.tile_off[t.g + 1] - P.tile_off[t.g];
+    const int64_t local = Lt - static_cast<int64_t>(P.tile_off[t.g]) * nb;
+    const int nbi = static_cast<int>(local / mt_g), mt = static_cast<int>(local % mt_g);
+    t.row_begin = P.offsets[t.g] + mt * 256;
+    t.rows = min(256, P.offsets[t.g + 1] - t.row_begin);
+    t.n0 = nbi * BNO;
     return t;
   };
 
   // ---- load addressing of the tile whose k-slices are being loaded (as in run_tile, with every
-  // A row as a 32-bit byte offset from A: the launcher checks that A spans less than 4 GiB)
+  // A row as a 32-bit byte offset from its A: the launcher checks that each A spans < 4 GiB)
   const int r0 = tid >> 3, kc_t = (tid & 7) * 8;
-  const char* const a_base = reinterpret_cast<const char*>(A);
+  const char* a_base = nullptr;
+  int ldK = 0;  // K (and the row stride of A and B) of that tile
   uint32_t a_off[ACH], b_off[BCH];
   const char* b_base0 = nullptr;
   const char* b_base1 = nullptr;
   uint32_t gn[ACH];  // byte offsets of this thread's A rows in the next tile (gathered or not)
   auto fetch_gather = [&](const Tile& t) __attribute__((always_inline)) {
+    const GemmProb& P = t.p ? P1 : P0;
+    const int32_t* gth = (GATHER && t.p == 0) ? P0.gather : nullptr;
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
       const int r = t.row_begin + min(i * RS + r0, t.rows - 1);
-      gn[i] = static_cast<uint32_t>(GATHER ? gather[r] : r) * static_cast<uint32_t>(lda * 2) +
+      gn[i] = static_cast<uint32_t>(gth != nullptr ? gth[r] : r) * static_cast<uint32_t>(P.K * 2) +
               static_cast<uint32_t>(kc_t * 2);
     }
   };
   auto set_ld = [&](const Tile& t) __attribute__((always_inline)) {
+    const GemmProb& P = t.p ? P1 : P0;
 #pragma unroll
     for (int i = 0; i < ACH; ++i) a_off[i] = gn[i];
+    a_base = reinterpret_cast<const char*>(P.A);
+    ldK = P.K;
     const bf16_t* Bg0 =
-        B0 + static_cast<int64_t>(t.g) * group_stride + static_cast<int64_t>(t.n0) * ldb;
-    const bf16_t* Bg1 = PAIRED ? B1 + static_cast<int64_t>(t.g) * group_stride +
-                                     static_cast<int64_t>(t.n0) * ldb
+        P.B0 + static_cast<int64_t>(t.g) * P.group_stride + static_cast<int64_t>(t.n0) * P.K;
+    const bf16_t* Bg1 = PAIRED ? P.B1 + static_cast<int64_t>(t.g) * P.group_stride +
+                                     static_cast<int64_t>(t.n0) * P.K
                                : Bg0;
     b_base0 = reinterpret_cast<const char*>(Bg0);
     b_base1 = reinterpret_cast<const char*>(Bg1);
-    const int b_rows = min(PAIRED ? BN / 2 : BN, N - t.n0);
+    const int b_rows = min(PAIRED ? BN / 2 : BN, P.N - t.n0);
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
       const int r = i * RS + r0;
       const int rb_ = PAIRED ? (r & (BN / 2 - 1)) : r;
-      b_off[i] = static_cast<uint32_t>((min(rb_, b_rows - 1) * ldb + kc_t) * 2);
+      b_off[i] = static_cast<uint32_t>((min(rb_, b_rows - 1) * P.K + kc_t) * 2);
     }
   };
   u32x4 ra[ACH], rb[BCH];
   auto gload = [&](int k0) __attribute__((always_inline)) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    const bool in = !KTAIL || k0 + kc_t < K;
-    const uint32_t kb = static_cast<uint32_t>((in ? k0 : K - 8 - kc_t) * 2);
+    const bool in = !KTAIL || k0 + kc_t < ldK;
+    const uint32_t kb = static_cast<uint32_t>((in ? k0 : ldK - 8 - kc_t) * 2);
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(a_base + (a_off[i] + kb));
@@ -652,21 +680,12 @@ __device__ __forceinline__ void run_tiles_persistent(
   constexpr int NMF = MI * NJ, NR = MI + NJ, NX = ACH + BCH;
   // one k-step on stage `cur`, with the same sub-step schedule as run_tile; the slice stored and
   // the one loaded are the next two of the block's slice stream, of this tile or the next
-  auto kstep = [&](int cur, int k0, auto has_next, auto has_load) __attribute__((always_inline)) {
-    constexpr bool NEXT = decltype(has_next)::value;
-    constexpr bool LOAD = decltype(has_load)::value;
+  auto kstep = [&](int cur, int k0) __attribute__((always_inline)) {
     lfrag(1, cur, 1);
     mfmas(0);
-    if constexpr (NEXT && LOAD) {
-      lstore(cur ^ 1);
-      gload(k0);
-      sched_substep_wl<NMF, NR, NX, NX>();
-    } else if constexpr (NEXT) {
-      lstore(cur ^ 1);
-      sched_substep<NMF, NR, kSgDsWrite, NX>();
-    } else {
-      sched_substep<NMF, NR, 0, 0>();
-    }
+    lstore(cur ^ 1);
+    gload(k0);
+    sched_substep_wl<NMF, NR, NX, NX>();
     lfrag(0, cur, 2);
     mfmas(1);
     sched_substep<NMF, NR, 0, 0>();
@@ -674,13 +693,9 @@ __device__ __forceinline__ void run_tiles_persistent(
     mfmas(0);
     sched_substep<NMF, NR, 0, 0>();
     __syncthreads();
-    if constexpr (NEXT) {
-      lfrag(0, cur ^ 1, 0);
-      mfmas(1);
-      sched_substep<NMF, NR, 0, 0>();
-    } else {
-      mfmas(1);
-    }
+    lfrag(0, cur ^ 1, 0);
+    mfmas(1);
+    sched_substep<NMF, NR, 0, 0>();
   };
   // Epilogue through LDS: each wave writes its outputs as bf16 into a private 8 KB region of the
   // stage the tile's last k-step read (free once that k-step's barrier has passed), reads them
@@ -694,6 +709,9 @@ __device__ __forceinline__ void run_tiles_persistent(
   constexpr int PCH = PC / 8;                   // 16-byte chunks per row
   constexpr int PI = PR / 32;                   // 32-row blocks per pass
   auto epilogue = [&](const Tile& t, int free_stage) __attribute__((always_inline)) {
+    const GemmProb& P = t.p ? P1 : P0;
+    bf16_t* C = P.C;
+    const int N = P.N, ldc = P.N;
     unsigned char* reg = lds + free_stage * kStageBytes + wave * 8192;
     const bool full = t.rows == 256 && t.n0 + BNO <= N;
     int lrow = lk * 4, lcol = l32, ln = lane;
@@ -725,9 +743,7 @@ __device__ __forceinline__ void run_tiles_persistent(
     __syncthreads();
   };
 
-  using T_ = std::true_type;
-  const int nk = (K + BK - 1) / BK;  // >= 2
-  Tile cur = describe(L);
+  Tile cur = describe(J);
   fetch_gather(cur);
   set_ld(cur);
   gload(0);
@@ -737,11 +753,11 @@ __device__ __forceinline__ void run_tiles_persistent(
   lfrag(0, 0, 0);
   int sb = 0;  // stage of the tile's first k-slice
   for (;;) {
-    const int64_t Ln = L + S;
-    const bool has_next = Ln < xend;
+    const int64_t Jn = J + S;
+    const bool has_next = Jn < xend;
     Tile nxt = cur;
     if (has_next) {
-      nxt = describe(Ln);
+      nxt = describe(Jn);
       fetch_gather(nxt);
     }
 #pragma unroll
@@ -750,38 +766,49 @@ __device__ __forceinline__ void run_tiles_persistent(
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    const int nk = ((cur.p ? P1.K : P0.K) + BK - 1) / BK;  // >= 2
     // the last two k-steps load the next tile's first two slices (the block's last tile loads its
     // own again, unused)
     for (int kt = 0; kt < nk; ++kt) {
       if (kt == nk - 2) set_ld(nxt);
       const int k0 = (kt + 2 < nk ? kt + 2 : kt + 2 - nk) * BK;
-      kstep((sb + kt) & 1, k0, T_{}, T_{});
+      kstep((sb + kt) & 1, k0);
     }
     epilogue(cur, (sb + nk - 1) & 1);
     if (!has_next) break;
     sb ^= nk & 1;
     cur = nxt;
-    L = Ln;
+    J = Jn;
   }
   // the last tile's final two k-steps re-read its own first slices; let them land before exit
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Blocks [0, main_blocks) run the persistent tile lists; the rest run the remainder tiles of the
+// first product, then of the second (at most one 128-row and one 64-row tile per group).
 template <int EPI, bool KTAIL, bool GATHER>
-__global__ __launch_bounds__(NT, 1) void grouped_gemm_persistent_kernel(
-    const bf16_t* __restrict__ A, const int32_t* __restrict__ gather,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off, int groups,
-    int main_blocks, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
-    int64_t group_stride, int N, int K, bf16_t* __restrict__ C) {
+__global__ __launch_bounds__(NT, 1) void grouped_gemm_persistent_kernel(GemmProb P0, GemmProb P1,
+                                                                        int main_blocks) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   if (static_cast<int>(blockIdx.x) < main_blocks) {
-    run_tiles_persistent<EPI, KTAIL, GATHER>(lds, A, gather, offsets, tile_off, groups, B0, B1,
-                                             group_stride, N, K, C, main_blocks);
+    run_tiles_persistent<EPI, KTAIL, GATHER>(lds, P0, P1, main_blocks);
     return;
   }
-  run_remainder_tile<EPI, KTAIL, GATHER, false>(lds, static_cast<int64_t>(blockIdx.x) - main_blocks,
-                                                A, gather, offsets, tile_off, groups, B0, B1,
-                                                group_stride, N, K, C, nullptr, nullptr);
+  constexpr int BNO = EPI == 0 ? BN / 2 : BN;
+  int64_t L = static_cast<int64_t>(blockIdx.x) - main_blocks;
+  const int64_t r0 = 2 * static_cast<int64_t>(P0.groups) * ((P0.N + BNO - 1) / BNO);
+  if (L < r0) {
+    run_remainder_tile<EPI, KTAIL, GATHER, false>(lds, L, P0.A, P0.gather, P0.offsets,
+                                                  P0.tile_off, P0.groups, P0.B0, P0.B1,
+                                                  P0.group_stride, P0.N, P0.K, P0.C, nullptr,
+                                                  nullptr);
+    return;
+  }
+  if (P1.groups > 0)
+    run_remainder_tile<EPI, KTAIL, false, false>(lds, L - r0, P1.A, nullptr, P1.offsets,
+                                                 P1.tile_off, P1.groups, P1.B0, P1.B1,
+                                                 P1.group_stride, P1.N, P1.K, P1.C, nullptr,
+                                                 nullptr);
 }
 
 // Weight gradients: C_g [Ma][Nb] (fp32) = sum over k in [64 kt[g], 64 kt[g+1]) of A[m][k] B[n][k],
@@ -841,6 +868,46 @@ int persistent_blocks() {
   return v;
 }
 
+// Whether the persistent kernel serves a forward product: 2..128 k-slices (long-K tiles keep the
+// one-tile blocks: their per-tile costs are small, and the persistent loop measured ~2% slower per
+// k-step on the 224-step down projection of the Mixtral layer), A (a_rows rows of K) spanning less
+// than 4 GiB (32-bit row offsets), and a known compute-unit count.
+bool persistent_ok(const GemmProb& P, int64_t a_rows) {
+  return P.K >= 2 * BK && P.K <= 128 * BK && a_rows >= 0 &&
+         a_rows * P.K * 2 < (int64_t{1} << 32) && persistent_blocks() >= NXCD;
+}
+
+// One launch of the persistent kernel over one product (P1.groups == 0) or two.
+template <int EPI, bool KTAIL, bool GATHER>
+hipError_t launch_persistent(const GemmProb& P0, int64_t max_tiles0, const GemmProb& P1,
+                             int64_t max_tiles1, hipStream_t st) {
+  constexpr int BNO = EPI == 0 ? BN / 2 : BN;
+  constexpr size_t kMainP = 2 * Geo<256>::STAGE;
+  constexpr size_t kEpiR = static_cast<size_t>(128) * (BNO + 8) * sizeof(bf16_t);
+  constexpr size_t ldsp = kMainP > kEpiR ? kMainP : kEpiR;
+  static std::atomic<bool> attr_p{false};
+  if (!attr_p.load(std::memory_order_acquire)) {
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&grouped_gemm_persistent_kernel<EPI, KTAIL, GATHER>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(ldsp));
+    if (e != hipSuccess) return e;
+    attr_p.store(true, std::memory_order_release);
+  }
+  const int64_t nb0 = cdiv(P0.N, BNO), nb1 = P1.groups > 0 ? cdiv(P1.N, BNO) : 0;
+  const int64_t tiles = max_tiles0 * nb0 + (P1.groups > 0 ? max_tiles1 * nb1 : 0);
+  if (tiles <= 0) return hipSuccess;
+  const int64_t pb = persistent_blocks();
+  const int64_t upper = cdiv(tiles, NXCD) * NXCD;
+  const int64_t main_blocks = upper < pb ? upper : pb;
+  const int64_t grid = main_blocks + 2 * static_cast<int64_t>(P0.groups) * nb0 +
+                       2 * static_cast<int64_t>(P1.groups) * nb1;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((grouped_gemm_persistent_kernel<EPI, KTAIL, GATHER>),
+                     dim3(static_cast<unsigned>(grid)), dim3(NT), ldsp, st, P0, P1,
+                     static_cast<int>(main_blocks));
+  return hipGetLastError();
+}
+
 template <int EPI, bool KTAIL, bool GATHER, bool BKN = false>
 hipError_t launch_gemm_t(const bf16_t* A, const int32_t* gather, const int32_t* offsets,
                          const int32_t* tile_off,
@@ -850,35 +917,10 @@ hipError_t launch_gemm_t(const bf16_t* A, const int32_t* gather, const int32_t* 
   constexpr int BNO = (EPI == 0 || EPI == 3 || EPI == 4) ? BN / 2 : BN;
   const int64_t nb = cdiv(N, BNO);
   if constexpr ((EPI == 0 || EPI == 1) && !BKN) {
-    // forward products of 2..128 k-slices, whose A (a_rows rows of K) the persistent kernel
-    // addresses with 32-bit byte offsets: persistent blocks over the 256-row tiles
-    const int pb = persistent_blocks();
-    // (long-K tiles keep the one-tile blocks: their per-tile costs are small, and the persistent
-    // loop measured ~2% slower per k-step on the 224-step down projection of the Mixtral layer)
-    if (K >= 2 * BK && K <= 128 * BK && pb >= NXCD && a_rows >= 0 &&
-        a_rows * K * 2 < (int64_t{1} << 32)) {
-      constexpr size_t kMainP = 2 * Geo<256>::STAGE;
-      constexpr size_t kEpiR = static_cast<size_t>(128) * (BNO + 8) * sizeof(bf16_t);
-      const size_t ldsp = kMainP > kEpiR ? kMainP : kEpiR;
-      static std::atomic<bool> attr_p{false};
-      if (!attr_p.load(std::memory_order_acquire)) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&grouped_gemm_persistent_kernel<EPI, KTAIL, GATHER>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(ldsp));
-        if (e != hipSuccess) return e;
-        attr_p.store(true, std::memory_order_release);
-      }
-      if (max_tiles <= 0) return hipSuccess;
-      const int64_t upper = cdiv(max_tiles * nb, NXCD) * NXCD;
-      const int64_t main_blocks = upper < pb ? upper : pb;
-      const int64_t grid = main_blocks + 2 * static_cast<int64_t>(groups) * nb;
-      if (grid > 0x7fffffff) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((grouped_gemm_persistent_kernel<EPI, KTAIL, GATHER>),
-                         dim3(static_cast<unsigned>(grid)), dim3(NT), ldsp, st, A, gather, offsets,
-                         tile_off, groups, static_cast<int>(main_blocks), B0, B1, group_stride, N,
-                         K, C);
-      return hipGetLastError();
-    }
+    GemmProb P0{A, gather, offsets, tile_off, B0, B1, group_stride, C, groups, N, K};
+    GemmProb none{};
+    if (persistent_ok(P0, a_rows))
+      return launch_persistent<EPI, KTAIL, GATHER>(P0, max_tiles, none, 0, st);
   }
   // the 256-row tiles, then at most one 128-row and one 64-row tile per group
   const int64_t main_blocks = cdiv(max_tiles * nb, NXCD) * NXCD;
@@ -1044,6 +1086,62 @@ hipError_t launch_gemm_down_bf16(int groups, int d, int Mg, const int32_t* offse
                                max_tiles, static_cast<const bf16_t*>(W_down), nullptr,
                                static_cast<int64_t>(Mg) * d, d, Mg, static_cast<bf16_t*>(out), st,
                                nullptr, nullptr, a_rows);
+}
+
+// The routed gate/up product (rows of x gathered through `gather`) and the shared experts' (all T
+// rows of x, one group of width SMg) in one launch, when the persistent kernel serves both;
+// otherwise as two launches of launch_gemm_up_bf16.
+hipError_t launch_gemm_up_shared_bf16(int groups, int d, int Mg, const void* x,
+                                      const int32_t* gather, const int32_t* offsets,
+                                      const int32_t* tile_off, int64_t max_tiles,
+                                      const void* W_gate, const void* W_up, void* h, int64_t T,
+                                      int SMg, const int32_t* sh_offsets,
+                                      const int32_t* sh_tile_off, int64_t sh_tiles,
+                                      const void* Ws_gate, const void* Ws_up, void* h_sh,
+                                      hipStream_t st) {
+  const bf16_t* X = static_cast<const bf16_t*>(x);
+  GemmProb P0{X, gather, offsets, tile_off, static_cast<const bf16_t*>(W_gate),
+              static_cast<const bf16_t*>(W_up), static_cast<int64_t>(Mg) * d,
+              static_cast<bf16_t*>(h), groups, Mg, d};
+  GemmProb P1{X, nullptr, sh_offsets, sh_tile_off, static_cast<const bf16_t*>(Ws_gate),
+              static_cast<const bf16_t*>(Ws_up), static_cast<int64_t>(SMg) * d,
+              static_cast<bf16_t*>(h_sh), 1, SMg, d};
+  if (gather != nullptr && persistent_ok(P0, T) && persistent_ok(P1, T)) {
+    if (d % BK == 0) return launch_persistent<0, false, true>(P0, max_tiles, P1, sh_tiles, st);
+    return launch_persistent<0, true, true>(P0, max_tiles, P1, sh_tiles, st);
+  }
+  hipError_t e = launch_gemm_up_bf16(groups, d, Mg, x, gather, offsets, tile_off, max_tiles, W_gate,
+                                     W_up, h, st, T);
+  if (e != hipSuccess) return e;
+  return launch_gemm_up_bf16(1, d, SMg, x, nullptr, sh_offsets, sh_tile_off, sh_tiles, Ws_gate,
+                             Ws_up, h_sh, st, T);
+}
+
+// The routed down product (R rows of h) and the shared experts' (T rows of h_sh, K = SMg) in one
+// launch when the persistent kernel serves both; otherwise as two launches.
+hipError_t launch_gemm_down_shared_bf16(int groups, int d, int Mg, const int32_t* offsets,
+                                        const int32_t* tile_off, int64_t max_tiles,
+                                        const void* W_down, const void* h, void* out, int64_t R,
+                                        int64_t T, int SMg, const int32_t* sh_offsets,
+                                        const int32_t* sh_tile_off, int64_t sh_tiles,
+                                        const void* Ws_down, const void* h_sh, void* sh,
+                                        hipStream_t st) {
+  GemmProb P0{static_cast<const bf16_t*>(h), nullptr, offsets, tile_off,
+              static_cast<const bf16_t*>(W_down), nullptr, static_cast<int64_t>(Mg) * d,
+              static_cast<bf16_t*>(out), groups, d, Mg};
+  GemmProb P1{static_cast<const bf16_t*>(h_sh), nullptr, sh_offsets, sh_tile_off,
+              static_cast<const bf16_t*>(Ws_down), nullptr, static_cast<int64_t>(SMg) * d,
+              static_cast<bf16_t*>(sh), 1, d, SMg};
+  if (persistent_ok(P0, R) && persistent_ok(P1, T)) {
+    if (Mg % BK == 0 && SMg % BK == 0)
+      return launch_persistent<1, false, false>(P0, max_tiles, P1, sh_tiles, st);
+    return launch_persistent<1, true, false>(P0, max_tiles, P1, sh_tiles, st);
+  }
+  hipError_t e = launch_gemm_down_bf16(groups, d, Mg, offsets, tile_off, max_tiles, W_down, h, out,
+                                       st, R);
+  if (e != hipSuccess) return e;
+  return launch_gemm_down_bf16(1, d, SMg, sh_offsets, sh_tile_off, sh_tiles, Ws_down, h_sh, sh, st,
+                               T);
 }
 
 }  // namespace moe

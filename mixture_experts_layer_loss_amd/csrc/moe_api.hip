@@ -16,6 +16,21 @@ hipError_t launch_gemm_up_bf16(int groups, int d, int Mg, const void* rows,
 hipError_t launch_gemm_down_bf16(int groups, int d, int Mg, const int32_t* offsets,
                                  const int32_t* tile_off, int64_t max_tiles, const void* W_down,
                                  const void* h, void* out, hipStream_t st, int64_t a_rows);
+hipError_t launch_gemm_up_shared_bf16(int groups, int d, int Mg, const void* x,
+                                      const int32_t* gather, const int32_t* offsets,
+                                      const int32_t* tile_off, int64_t max_tiles,
+                                      const void* W_gate, const void* W_up, void* h, int64_t T,
+                                      int SMg, const int32_t* sh_offsets,
+                                      const int32_t* sh_tile_off, int64_t sh_tiles,
+                                      const void* Ws_gate, const void* Ws_up, void* h_sh,
+                                      hipStream_t st);
+hipError_t launch_gemm_down_shared_bf16(int groups, int d, int Mg, const int32_t* offsets,
+                                        const int32_t* tile_off, int64_t max_tiles,
+                                        const void* W_down, const void* h, void* out, int64_t R,
+                                        int64_t T, int SMg, const int32_t* sh_offsets,
+                                        const int32_t* sh_tile_off, int64_t sh_tiles,
+                                        const void* Ws_down, const void* h_sh, void* sh,
+                                        hipStream_t st);
 hipError_t launch_gemm_up_f32(int groups, int d, int Mg, const void* rows,
                               const int32_t* gather, const int32_t* offsets,
                               const int32_t* tile_off, int64_t max_tiles, const void* W_gate,
@@ -626,20 +641,37 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
                          p.block_base, p.offsets, nullptr, p.perm_token, p.inv_perm, hs);
   }
   marks.mark(2, hs);
-  if (e == hipSuccess && saved != nullptr)  // h, and G and U kept for the backward
-    e = launch_gemm_up_save_bf16(s->E, s->d, s->M, x, p.perm_token, p.offsets, p.tile_off,
-                                 max_tiles, W_gate, W_up, p.h, sv.G, sv.U, hs);
-  else if (e == hipSuccess)
-    e = launch_gemm_up(s->dtype, s->E, s->d, s->M, x, p.perm_token, p.offsets, p.tile_off,
-                       max_tiles, W_gate, W_up, p.h, hs, s->T);
-  marks.mark(3, hs);
-  if (e == hipSuccess)
-    e = launch_gemm_down(s->dtype, s->E, s->d, s->M, p.offsets, p.tile_off, max_tiles, W_down,
-                         p.h, p.out_perm, hs, routed_rows(s));
-  marks.mark(4, hs);
-  if (e == hipSuccess && s->S > 0) {
-    const int SM = s->S * s->M;
-    const int64_t sh_tiles = cdiv(s->T, BM);
+  // bf16 inference with shared experts: the shared experts run as a second product of the routed
+  // grouped launches (one group of all T rows), so they fill the routed products' last rounds
+  const bool fold_shared = s->S > 0 && s->dtype == MOE_BF16 && saved == nullptr;
+  const int SM = s->S * s->M;
+  const int64_t sh_tiles = cdiv(s->T, BM);
+  if (e == hipSuccess && fold_shared) {
+    e = launch_shared_table(s->T, BM, p.sh_offsets, p.sh_tile_off, hs);
+    if (e == hipSuccess)
+      e = launch_gemm_up_shared_bf16(s->E, s->d, s->M, x, p.perm_token, p.offsets, p.tile_off,
+                                     max_tiles, W_gate, W_up, p.h, s->T, SM, p.sh_offsets,
+                                     p.sh_tile_off, sh_tiles, Ws_gate, Ws_up, p.h_sh, hs);
+    marks.mark(3, hs);
+    if (e == hipSuccess)
+      e = launch_gemm_down_shared_bf16(s->E, s->d, s->M, p.offsets, p.tile_off, max_tiles, W_down,
+                                       p.h, p.out_perm, routed_rows(s), s->T, SM, p.sh_offsets,
+                                       p.sh_tile_off, sh_tiles, Ws_down, p.h_sh, p.sh, hs);
+    marks.mark(4, hs);
+  } else {
+    if (e == hipSuccess && saved != nullptr)  // h, and G and U kept for the backward
+      e = launch_gemm_up_save_bf16(s->E, s->d, s->M, x, p.perm_token, p.offsets, p.tile_off,
+                                   max_tiles, W_gate, W_up, p.h, sv.G, sv.U, hs);
+    else if (e == hipSuccess)
+      e = launch_gemm_up(s->dtype, s->E, s->d, s->M, x, p.perm_token, p.offsets, p.tile_off,
+                         max_tiles, W_gate, W_up, p.h, hs, s->T);
+    marks.mark(3, hs);
+    if (e == hipSuccess)
+      e = launch_gemm_down(s->dtype, s->E, s->d, s->M, p.offsets, p.tile_off, max_tiles, W_down,
+                           p.h, p.out_perm, hs, routed_rows(s));
+    marks.mark(4, hs);
+  }
+  if (e == hipSuccess && s->S > 0 && !fold_shared) {
     e = launch_shared_table(s->T, BM, p.sh_offsets, p.sh_tile_off, hs);
     if (e == hipSuccess && saved != nullptr)
       e = launch_gemm_up_save_bf16(1, s->d, SM, x, nullptr, p.sh_offsets, p.sh_tile_off, sh_tiles,
