@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--blas-reference", action="store_true",
                     help="also time the vendor GEMM (torch.mm -> hipBLASLt) on one dense matrix of "
                          "each expert product's shape, as a reference point (bf16 only)")
+    ap.add_argument("--power-probe", action="store_true",
+                    help="time moe_expert_ffn on the workload's expert shapes (E groups of kT/E "
+                         "rows) with random operands, then with constant ones, and exit")
     ap.add_argument("--trace-summary", default=None,
                     help="print per-kernel statistics of this rocprofv3 kernel_trace.csv and exit")
     ap.add_argument("--skip", type=int, default=0,
@@ -83,6 +86,47 @@ def trace_summary(path: str, skip: int) -> None:
         short = name if len(name) < 140 else name[:137] + "..."
         print(f"| `{short}` | {n} ({nk}) | {tot:.1f} | {100 * tot / total:.2f} | {mean:.2f} | "
               f"{med:.2f} | {lo:.2f} | {hi:.2f} |")
+
+
+def power_probe(cfg, reps: int = 6) -> None:
+    """The grouped expert products (moe_expert_ffn: gate/up + SwiGLU, then down) on E balanced
+    groups of kT/E rows at the workload's d and M, with random operands, then all-constant ones
+    (same instructions and addresses, far less switching). Prints one JSON line per operand kind
+    with the median time of the whole call (both products)."""
+    import torch
+
+    import mixture_experts_layer_loss_amd as moe
+    dev = torch.device("cuda:0")
+    E, d, M = cfg.E, cfg.d, cfg.M
+    rows = cfg.k * cfg.T // cfg.E
+    offs = torch.arange(0, E + 1, dtype=torch.int32, device=dev) * rows
+    g = torch.Generator(device=dev).manual_seed(7)
+    for kind in ("random", "constant", "random"):
+        if kind == "random":
+            X = torch.randn(E * rows, d, device=dev, generator=g).to(torch.bfloat16)
+            Wg = (torch.randn(E, M, d, device=dev, generator=g) / d ** 0.5).to(torch.bfloat16)
+            Wu = (torch.randn(E, M, d, device=dev, generator=g) / d ** 0.5).to(torch.bfloat16)
+            Wd = (torch.randn(E, d, M, device=dev, generator=g) / M ** 0.5).to(torch.bfloat16)
+        else:
+            X = torch.full((E * rows, d), 0.5, device=dev, dtype=torch.bfloat16)
+            Wg = torch.full((E, M, d), 0.01, device=dev, dtype=torch.bfloat16)
+            Wu = Wg.clone()
+            Wd = torch.full((E, d, M), 0.01, device=dev, dtype=torch.bfloat16)
+        ms = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            moe.moe_expert_ffn(X, offs, Wg, Wu, Wd)
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        ms.sort()
+        med = ms[len(ms) // 2]
+        flops = 6.0 * d * M * E * rows
+        print(json.dumps({"probe": "expert_ffn", "operands": kind, "groups": E, "rows": rows,
+                          "d": d, "M": M, "ms_median": round(med, 4),
+                          "tflops": round(flops / (med * 1e-3) / 1e12, 1)}), flush=True)
+        del X, Wg, Wu, Wd
 
 
 def gemm_source_sha() -> str:
@@ -195,6 +239,9 @@ def main():
 
     name = args.workload or workloads.HEADLINE
     cfg = workloads.CONFIGS[name]
+    if args.power_probe:
+        power_probe(cfg)
+        return
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     print(f"[bench] generating {name} inputs", file=sys.stderr, flush=True)
