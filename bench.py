@@ -213,12 +213,24 @@ def cpu_baseline(cfg, inp, seconds: float):
     n = int(min(cfg.T, max(p2, (seconds - fixed) / per_tok)))
     n = max(32, (n // 32) * 32)
     dt = run(n)
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    pools = threadpool_info()
+    threads = max([p.get("num_threads", 1) for p in pools] or [1])
+    blas = ", ".join(sorted({f"{p.get('internal_api', '?')} {p.get('version', '')}".strip()
+                             for p in pools if p.get("user_api") == "blas"})) or "unknown"
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     note = "" if cfg.c is None else "; capacity applied within the sample"
     return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {n} of {cfg.T} tokens of the same layer (all {cfg.E} experts' weights), "
                       f"fp64 NumPy oracle, {dt:.1f} s{note}",
-            "affinity_cpus": len(os.sched_getaffinity(0))}
+            "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model, "blas": blas}
 
 
 def main():
