@@ -264,12 +264,14 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(int64_t T, int k, int64_
 }
 
 __global__ __launch_bounds__(256) void schedule_kernel(int groups, const int32_t* __restrict__ offsets,
-                                                        int32_t* __restrict__ tile_off, int BM) {
+                                                        int32_t* __restrict__ tile_off, int BM,
+                                                        int min_tiles) {
   __shared__ int sbuf[256];
   const int g = threadIdx.x;
   const int rows = g < groups ? offsets[g + 1] - offsets[g] : 0;
   int c0 = 0, c1 = 0, c2 = 0;
   if (g < groups && rows > 0) tile_counts(rows, BM, c0, c1, c2);
+  if (g < groups) c0 = max(c0, min_tiles);
   const int i0 = block_scan_256(c0, sbuf);
   const int i1 = block_scan_256(c1, sbuf);
   const int i2 = block_scan_256(c2, sbuf);
@@ -465,8 +467,10 @@ hipError_t launch_scatter(int64_t T, int d, int E, int k, int64_t C, int elem_by
 }
 
 hipError_t launch_schedule(int groups, const int32_t* offsets, int32_t* tile_off, int BM,
-                           hipStream_t st) {
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(256), 0, st, groups, offsets, tile_off, BM);
+                           hipStream_t st, int min_tiles) {
+  if (groups > 256 || (min_tiles > 0 && BM == 256)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(256), 0, st, groups, offsets, tile_off, BM,
+                     min_tiles);
   return hipGetLastError();
 }
 

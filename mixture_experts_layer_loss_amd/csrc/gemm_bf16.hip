@@ -852,6 +852,224 @@ __global__ __launch_bounds__(NT, 1) void wgrad_gemm_kernel(const bf16_t* __restr
                                  min(256, Ma - m0), n0);
 }
 
+// Persistent form of the weight gradients: one block per CU walks its XCD's run of the same
+// band-ordered tile list as wgrad_gemm_kernel (runs of equal work), and the k-step pipeline runs on from one tile into
+// the next, as in run_tiles_persistent (the last two k-steps of a tile load the next tile's first
+// two k-slices). Every group spans at least two k-slices (the schedule pads an empty or one-slice
+// group with zero columns), so each tile has the two k-steps that carry the hand-over. The fp32
+// tile leaves through the free LDS stage: each wave stages 32 x 64 floats of its 128 x 64 block
+// at a time in a private 8 KB region and stores them as 16-byte row pieces, 32 stores per lane
+// per tile, so the next tile's first loads can be waited on while those stores are still in
+// flight. Operand rows are 32-bit byte offsets from the tile's first row (the launcher checks
+// 256 rows of either operand span < 2 GiB).
+__device__ __forceinline__ void run_wgrad_persistent(unsigned char* lds,
+                                                     const bf16_t* __restrict__ A, int lda,
+                                                     const bf16_t* __restrict__ B, int ldb,
+                                                     const int32_t* __restrict__ kt, int groups,
+                                                     int Ma, int Nb, float* __restrict__ C,
+                                                     int nblocks) {
+  using G = Geo<256>;
+  constexpr int MI = G::MI, NJ = G::NJ, ACH = G::ACH, BCH = G::BCH, RS = G::RSTEP;
+  static_assert(G::WCOLS == 64 && MI * 32 == G::WROWS, "fp32 epilogue passes are 32 x 64");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / G::WN, wn = wave % G::WN;
+  const int mt = (Ma + 255) / 256, nt = (Nb + 255) / 256;
+  const int64_t per_group = static_cast<int64_t>(mt) * nt;
+  const int S = nblocks / NXCD;
+  const int xcd = static_cast<int>(blockIdx.x) % NXCD, slot = static_cast<int>(blockIdx.x) / NXCD;
+  // the XCDs split the list by work, not by tile count: the tiles before tile L (group g, local
+  // index l) hold per_group kt[g] + l (kt[g+1] - kt[g]) k-steps, and XCD x takes the tiles that
+  // start in [x W / 8, (x + 1) W / 8) of the total W
+  auto first_tile = [&](int64_t work) __attribute__((always_inline)) {
+    int lo = 0, hi = groups;  // largest g with per_group kt[g] <= work
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (per_group * kt[mid] <= work) lo = mid; else hi = mid;
+    }
+    const int64_t nk = kt[lo + 1] - kt[lo];  // >= 2
+    const int64_t l = min(per_group, (work - per_group * kt[lo] + nk - 1) / nk);
+    return static_cast<int64_t>(lo) * per_group + l;
+  };
+  const int64_t W = per_group * kt[groups];
+  const int64_t b0 = first_tile(W * xcd / NXCD);
+  const int64_t xend = first_tile(W * (xcd + 1) / NXCD) - b0;
+  int64_t J = slot;
+  if (J >= xend) return;
+
+  struct Tile {
+    int g, m0, n0, k0, nk;
+  };
+  constexpr int kWgBand = 8;  // as wgrad_gemm_kernel: bands of 8 m-tiles, n fastest in a band
+  auto describe = [&](int64_t Jt) __attribute__((always_inline)) {
+    Tile t;
+    const int64_t L = b0 + Jt;
+    t.g = static_cast<int>(L / per_group);
+    const int local = static_cast<int>(L % per_group);
+    const int band = local / (kWgBand * nt), w = local % (kWgBand * nt);
+    const int bw = min(kWgBand, mt - band * kWgBand);
+    t.m0 = (band * kWgBand + w % bw) * 256;
+    t.n0 = (w / bw) * 256;
+    t.k0 = 64 * kt[t.g];
+    t.nk = kt[t.g + 1] - kt[t.g];  // >= 2
+    return t;
+  };
+
+  const int r0 = tid >> 3, kc_t = (tid & 7) * 8;
+  const char* a_base = nullptr;
+  const char* b_base = nullptr;
+  uint32_t a_off[ACH], b_off[BCH];
+  auto set_ld = [&](const Tile& t) __attribute__((always_inline)) {
+    a_base = reinterpret_cast<const char*>(A + static_cast<int64_t>(t.m0) * lda + t.k0);
+    b_base = reinterpret_cast<const char*>(B + static_cast<int64_t>(t.n0) * ldb + t.k0);
+    const int ar = min(256, Ma - t.m0) - 1, br = min(256, Nb - t.n0) - 1;
+#pragma unroll
+    for (int i = 0; i < ACH; ++i)
+      a_off[i] = static_cast<uint32_t>((min(i * RS + r0, ar) * lda + kc_t) * 2);
+#pragma unroll
+    for (int i = 0; i < BCH; ++i)
+      b_off[i] = static_cast<uint32_t>((min(i * RS + r0, br) * ldb + kc_t) * 2);
+  };
+  u32x4 ra[ACH], rb[BCH];
+  auto gload = [&](int k0) __attribute__((always_inline)) {
+    const uint32_t kb = static_cast<uint32_t>(k0 * 2);
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_base + (a_off[i] + kb));
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b_base + (b_off[i] + kb));
+  };
+  const uint32_t st_off = static_cast<uint32_t>(swz(r0, tid & 7) * 2);
+  constexpr uint32_t kStageBytes = G::STAGE, kBBytes = 256 * BK * 2;
+  auto lstore = [&](int stage) __attribute__((always_inline)) {
+    unsigned char* sa = lds + stage * kStageBytes + st_off;
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4*>(sa + i * RS * BK * 2) = ra[i];
+#pragma unroll
+    for (int i = 0; i < BCH; ++i)
+      *reinterpret_cast<u32x4*>(sa + kBBytes + i * RS * BK * 2) = rb[i];
+  };
+
+  f32x16 acc[MI][NJ];
+  const int l32 = lane & 31, lk = lane >> 5, sw = (l32 >> 1) & 7;
+  uint32_t fo[4];
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub)
+    fo[sub] = static_cast<uint32_t>((l32 * BK + (((sub * 2 + lk) ^ sw) << 3)) * 2);
+  bf16x8 fa[2][MI], fb[2][NJ];
+  auto lfrag = [&](int set, int stage, int sub) __attribute__((always_inline)) {
+    const unsigned char* sa = lds + stage * kStageBytes + fo[sub];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      fa[set][i] = *reinterpret_cast<const bf16x8*>(sa + (wm * G::WROWS + i * 32) * BK * 2);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      fb[set][j] = *reinterpret_cast<const bf16x8*>(sa + kBBytes + (wn * G::WCOLS + j * 32) * BK * 2);
+  };
+  auto mfmas = [&](int set) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+  };
+  constexpr int NMF = MI * NJ, NR = MI + NJ, NX = ACH + BCH;
+  auto kstep = [&](int cur, int k0) __attribute__((always_inline)) {
+    lfrag(1, cur, 1);
+    mfmas(0);
+    lstore(cur ^ 1);
+    gload(k0);
+    sched_substep_wl<NMF, NR, NX, NX>();
+    lfrag(0, cur, 2);
+    mfmas(1);
+    sched_substep<NMF, NR, 0, 0>();
+    lfrag(1, cur, 3);
+    mfmas(0);
+    sched_substep<NMF, NR, 0, 0>();
+    __syncthreads();
+    lfrag(0, cur ^ 1, 0);
+    mfmas(1);
+    sched_substep<NMF, NR, 0, 0>();
+  };
+  // Epilogue: pass i stages the wave's rows 32 i .. 32 i + 31 (64 columns) as fp32 in its 8 KB
+  // region, 16-byte chunk c of row r at chunk c ^ 8 ((r >> 2) & 1) (a store instruction's two
+  // half-waves write rows 4 apart, which then fall on different banks), and stores them as 16
+  // chunks per row. A barrier follows before the next tile's first k-step stores into the stage.
+  auto epilogue = [&](const Tile& t, int free_stage) __attribute__((always_inline)) {
+    float* Cg = C + static_cast<int64_t>(t.g) * Ma * Nb;
+    unsigned char* reg = lds + free_stage * kStageBytes + wave * 8192;
+    const int rows = min(256, Ma - t.m0), cols = min(256, Nb - t.n0);
+    const bool full = rows == 256 && cols == 256;
+    int lrow = lk * 4, lcol = l32, ln = lane;
+    asm volatile("" : "+v"(lrow), "+v"(lcol), "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = (r >> 2) * 8 + lrow + (r & 3);
+          const int col = j * 32 + lcol;
+          *reinterpret_cast<float*>(reg + row * 256 + (((col >> 2) ^ (((row >> 2) & 1) << 3)) << 4) +
+                                    (col & 3) * 4) = acc[i][j][r];
+        }
+#pragma unroll
+      for (int qq = 0; qq < 8; ++qq) {
+        const int idx = qq * 64 + ln, rr = idx >> 4, c = idx & 15;
+        const u32x4 v =
+            *reinterpret_cast<const u32x4*>(reg + rr * 256 + ((c ^ (((rr >> 2) & 1) << 3)) << 4));
+        const int row = wm * G::WROWS + i * 32 + rr;
+        const int col = wn * G::WCOLS + c * 4;
+        if (full || (row < rows && col < cols))
+          __builtin_nontemporal_store(
+              v, reinterpret_cast<u32x4*>(Cg + static_cast<int64_t>(t.m0 + row) * Nb + t.n0 + col));
+      }
+    }
+    __syncthreads();
+  };
+
+  Tile cur = describe(J);
+  set_ld(cur);
+  gload(0);
+  lstore(0);
+  gload(BK);
+  __syncthreads();
+  lfrag(0, 0, 0);
+  int sb = 0;  // stage of the tile's first k-slice
+  for (;;) {
+    const int64_t Jn = J + S;
+    const bool has_next = Jn < xend;
+    const Tile nxt = has_next ? describe(Jn) : cur;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    const int nk = cur.nk;
+    for (int k = 0; k < nk; ++k) {
+      if (k == nk - 2) set_ld(nxt);
+      const int k0 = (k + 2 < nk ? k + 2 : k + 2 - nk) * BK;
+      kstep((sb + k) & 1, k0);
+    }
+    epilogue(cur, (sb + nk - 1) & 1);
+    if (!has_next) break;
+    sb ^= nk & 1;
+    cur = nxt;
+    J = Jn;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+__global__ __launch_bounds__(NT, 1) void wgrad_persistent_kernel(const bf16_t* __restrict__ A,
+                                                                 int lda,
+                                                                 const bf16_t* __restrict__ B,
+                                                                 int ldb,
+                                                                 const int32_t* __restrict__ kt,
+                                                                 int groups, int Ma, int Nb,
+                                                                 float* __restrict__ C) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  run_wgrad_persistent(lds, A, lda, B, ldb, kt, groups, Ma, Nb, C, static_cast<int>(gridDim.x));
+}
+
 // Compute units of the current device, rounded down to a multiple of the XCD count (0 if unknown).
 int persistent_blocks() {
   static std::atomic<int> cached[64];
@@ -1056,11 +1274,30 @@ hipError_t launch_gemm_kn_bf16(int groups, const void* rows, const int32_t* gath
                                      group_stride, N, K, Cp, st);
 }
 
-// C_g = A_g B_g^T over each group's zero-padded column range (weight gradients, fp32 output)
+// C_g = A_g B_g^T over each group's zero-padded column range (weight gradients, fp32 output).
+// two_slices: the schedule kt gives every group at least two k-slices (the persistent form).
 hipError_t launch_gemm_wgrad_bf16(const void* A, int lda, const void* B, int ldb,
                                   const int32_t* kt, int groups, int Ma, int Nb, float* C,
-                                  hipStream_t st) {
+                                  hipStream_t st, bool two_slices) {
   constexpr size_t lds = 2 * Geo<256>::STAGE;
+  const int64_t pb = persistent_blocks();
+  if (two_slices && pb >= NXCD && groups > 0) {
+    static std::atomic<bool> attr_p{false};
+    if (!attr_p.load(std::memory_order_acquire)) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_persistent_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+      attr_p.store(true, std::memory_order_release);
+    }
+    const int64_t tiles = static_cast<int64_t>(groups) * cdiv(Ma, 256) * cdiv(Nb, 256);
+    const int64_t upper = cdiv(tiles, NXCD) * NXCD;
+    const int64_t grid = upper < pb ? upper : pb;
+    hipLaunchKernelGGL(wgrad_persistent_kernel, dim3(static_cast<unsigned>(grid)), dim3(NT), lds,
+                       st, static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B), ldb,
+                       kt, groups, Ma, Nb, C);
+    return hipGetLastError();
+  }
   static std::atomic<bool> attr_set{false};
   if (!attr_set.load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_gemm_kernel),

@@ -258,6 +258,14 @@ struct LayerBackwardPlan {
   void *dGU, *whT, *dGT, *dUT, *dyT, *xT;        // routed experts
   void *dGUs, *hsT, *dGsT, *dUsT, *dysT, *xsT;   // shared experts
 };
+// Columns of a weight-gradient operand: each of `groups` groups of `rows` rows in total padded to
+// whole 64-column k-slices, at least two per group (the persistent weight-gradient kernel hands
+// two k-slices from tile to tile), so sum_g max(2, ceil(rows_g / 64)) <= ceil(rows / 64) + 2 groups.
+int64_t wgrad_cols(int64_t rows, int groups) {
+  const int64_t t = cdiv(rows, 64);
+  return 64 * (groups == 1 ? (t > 2 ? t : 2) : t + 2 * static_cast<int64_t>(groups));
+}
+
 LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
   LayerBackwardPlan p;
   p.f = plan_layer(c, s);
@@ -278,8 +286,8 @@ LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
   p.dG = mfma ? nullptr : c.take<float>(R * M);
   p.dU = mfma ? nullptr : c.take<float>(R * M);
   p.dxr = c.take<float>(R * d);
-  p.ldp = 64 * (static_cast<int64_t>(cdiv(static_cast<int64_t>(R), 64)) + s->E);
-  p.ldps = 64 * cdiv(s->T, 64);
+  p.ldp = wgrad_cols(static_cast<int64_t>(R), s->E);
+  p.ldps = wgrad_cols(s->T, 1);
   const size_t lp = static_cast<size_t>(p.ldp), lps = static_cast<size_t>(p.ldps);
   p.wrow = mfma || expert_choice(s) ? c.take<float>(R) : nullptr;
   p.dGU = p.whT = p.dGT = p.dUT = p.dyT = p.xT = nullptr;
@@ -789,7 +797,7 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
   // (shared) columns with 32-bit byte offsets
   if (s->dtype == MOE_BF16) {
     const int64_t R = routed_rows(s);
-    const int64_t ldp = 64 * (cdiv(R, 64) + s->E), ldps = 64 * cdiv(s->T, 64);
+    const int64_t ldp = wgrad_cols(R, s->E), ldps = wgrad_cols(s->T, 1);
     if (2 * 256 * (ldp > ldps ? ldp : ldps) >= (int64_t{1} << 31)) return MOE_ERR_UNSUPPORTED;
   }
   if (!ws || ws_bytes < moe_workspace_size(s, MOE_CALL_LAYER_BACKWARD)) return MOE_ERR_WORKSPACE;
@@ -842,8 +850,7 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
                          route_block_tokens(s->dtype, s->E), f.block_base, f.offsets, nullptr,
                          f.perm_token, f.inv_perm, hs);
   }
-  const bool mfma = s->dtype == MOE_BF16;
-  if (mfma) {  // G and U in one launch (gate and up tiles paired), unless the forward kept them
+  if (s->dtype == MOE_BF16) {  // G and U in one launch (gate and up tiles paired), unless kept
     if (e == hipSuccess && saved == nullptr)
       e = launch_gemm_gu_f32out_bf16(s->E, s->d, s->M, x, f.perm_token, f.offsets, f.tile_off,
                                      max_tiles, W_gate, W_up, p.G, p.U, hs);
@@ -860,7 +867,10 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
     e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s) | kRouteExpertChoice, x, W_r,
                      nullptr, nullptr, nullptr, f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart, p.cols,
                      hs);
-  if (e == hipSuccess) e = launch_schedule(s->E, f.offsets, p.tile64, 64, hs);
+  // 64-row tiles; on MFMA the weight-gradient column ranges, at least two k-slices per expert
+  const bool mfma = s->dtype == MOE_BF16;
+  if (e == hipSuccess) e = launch_schedule(s->E, f.offsets, p.tile64, 64, hs, mfma ? 2 : 0);
+  const int64_t max_w64 = p.ldp / 64;
   const int d = s->d, M = s->M;
   // ---- combine: P_row = dy_t W_down[e] gives d w = <P, h> and dh = w P, hence dG, dU
   if (e == hipSuccess && mfma)  // W_down[e] read in place as the [d][M] B operand
@@ -892,28 +902,28 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
     const bf16_t* dGU = static_cast<const bf16_t*>(p.dGU);
     if (e == hipSuccess)  // (w h)^T with h = SiLU(G) U
       e = launch_pad_transpose(MOE_F32, p.G, p.U, M, nullptr, p.wrow, f.offsets, p.tile64, s->E,
-                               max_t64, M, p.whT, lp, hs);
+                               max_w64, M, p.whT, lp, hs);
     if (e == hipSuccess)
       e = launch_pad_transpose(MOE_BF16, dGU, nullptr, 2 * M, nullptr, nullptr, f.offsets,
-                               p.tile64, s->E, max_t64, M, p.dGT, lp, hs);
+                               p.tile64, s->E, max_w64, M, p.dGT, lp, hs);
     if (e == hipSuccess)
       e = launch_pad_transpose(MOE_BF16, dGU + M, nullptr, 2 * M, nullptr, nullptr, f.offsets,
-                               p.tile64, s->E, max_t64, M, p.dUT, lp, hs);
+                               p.tile64, s->E, max_w64, M, p.dUT, lp, hs);
     if (e == hipSuccess)  // dy rows of the kept slots (exact bf16)
       e = launch_pad_transpose(MOE_BF16, dy, nullptr, d, f.perm_token, nullptr, f.offsets,
-                               p.tile64, s->E, max_t64, d, p.dyT, lp, hs);
+                               p.tile64, s->E, max_w64, d, p.dyT, lp, hs);
     if (e == hipSuccess)
       e = launch_pad_transpose(MOE_BF16, x, nullptr, d, f.perm_token, nullptr, f.offsets,
-                               p.tile64, s->E, max_t64, d, p.xT, lp, hs);
+                               p.tile64, s->E, max_w64, d, p.xT, lp, hs);
     if (e == hipSuccess)  // dW_down[e] = sum over its rows of dy_t^T (w h)
       e = launch_gemm_wgrad_bf16(p.dyT, static_cast<int>(lp), p.whT, static_cast<int>(lp),
-                                 p.tile64, s->E, d, M, dW_down, hs);
+                                 p.tile64, s->E, d, M, dW_down, hs, true);
     if (e == hipSuccess)  // dW_gate[e] = dG_e^T x_e
       e = launch_gemm_wgrad_bf16(p.dGT, static_cast<int>(lp), p.xT, static_cast<int>(lp),
-                                 p.tile64, s->E, M, d, dW_gate, hs);
+                                 p.tile64, s->E, M, d, dW_gate, hs, true);
     if (e == hipSuccess)
       e = launch_gemm_wgrad_bf16(p.dUT, static_cast<int>(lp), p.xT, static_cast<int>(lp),
-                                 p.tile64, s->E, M, d, dW_up, hs);
+                                 p.tile64, s->E, M, d, dW_up, hs, true);
   }
   if (e == hipSuccess && !mfma)  // dx_row = dG W_gate[e] + dU W_up[e]
     e = launch_nn_gemm(MOE_F32, s->dtype, true, p.dG, p.dU, nullptr, f.offsets, p.tile64, s->E,
@@ -952,7 +962,7 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
       if (e == hipSuccess)
         e = launch_swiglu_fwd(static_cast<int64_t>(s->T) * SM, p.Gs, p.Us, p.hs, hs);
     }
-    if (e == hipSuccess) e = launch_schedule(1, f.sh_offsets, p.sh_tile64, 64, hs);
+    if (e == hipSuccess) e = launch_schedule(1, f.sh_offsets, p.sh_tile64, 64, hs, mfma ? 2 : 0);
     const int64_t sh_t64 = cdiv(s->T, 64) + 1;
     if (mfma) {
       const int64_t lps = p.ldps;
@@ -964,7 +974,7 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
       if (e == hipSuccess)  // dxs = [dGs dUs] [Ws_gate; Ws_up] over K = 2 SM
         e = launch_gemm_kn_bf16(1, p.dGUs, nullptr, f.sh_offsets, f.sh_tile_off, sh_tiles, Ws_gate,
                                 Ws_up, 0, d, 2 * SM, p.dxs, hs);
-      const int64_t pt = cdiv(s->T, 64);
+      const int64_t pt = p.ldps / 64;
       const int32_t* so = f.sh_offsets;
       if (e == hipSuccess)
         e = launch_pad_transpose(MOE_BF16, dy, nullptr, d, nullptr, nullptr, so, p.sh_tile64, 1,
@@ -983,13 +993,13 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
                                  d, p.xsT, lps, hs);
       if (e == hipSuccess)
         e = launch_gemm_wgrad_bf16(p.dysT, static_cast<int>(lps), p.hsT, static_cast<int>(lps),
-                                   p.sh_tile64, 1, d, SM, dWs_down, hs);
+                                   p.sh_tile64, 1, d, SM, dWs_down, hs, true);
       if (e == hipSuccess)
         e = launch_gemm_wgrad_bf16(p.dGsT, static_cast<int>(lps), p.xsT, static_cast<int>(lps),
-                                   p.sh_tile64, 1, SM, d, dWs_gate, hs);
+                                   p.sh_tile64, 1, SM, d, dWs_gate, hs, true);
       if (e == hipSuccess)
         e = launch_gemm_wgrad_bf16(p.dUsT, static_cast<int>(lps), p.xsT, static_cast<int>(lps),
-                                   p.sh_tile64, 1, SM, d, dWs_up, hs);
+                                   p.sh_tile64, 1, SM, d, dWs_up, hs, true);
     } else {
       if (e == hipSuccess)
         e = launch_nn_gemm(s->dtype, s->dtype, false, dy, nullptr, nullptr, f.sh_offsets,

@@ -96,8 +96,10 @@ hipError_t launch_combine_ec(int dtype, int64_t T, int d, int E, int renorm, con
                              void* y, hipStream_t st);
 
 // Tile tables [3 (groups+1)] of a grouped GEMM from device row offsets (stand-alone expert FFN).
+// min_tiles > 0 (BM != 256 only): every group, empty ones included, gets at least that many tiles
+// in the first table (the weight gradients' zero-padded column ranges).
 hipError_t launch_schedule(int groups, const int32_t* offsets, int32_t* tile_off, int BM,
-                           hipStream_t st);
+                           hipStream_t st, int min_tiles = 0);
 
 // Grouped SwiGLU FFN in two launches. max_tiles = upper bound of sum_g ceil(rows_g / BM).
 //   gate/up: h[r] = SiLU(a_r W_gate[g]^T) * (a_r W_up[g]^T), a_r = rows[r], or rows[gather[r]]
@@ -201,10 +203,11 @@ hipError_t launch_gemm_gu_f32out_bf16(int groups, int d, int Mg, const void* row
                                       const int32_t* tile_off, int64_t max_tiles,
                                       const void* W_gate, const void* W_up, float* G, float* U,
                                       hipStream_t st);
-// C_g [Ma][Nb] fp32 = sum over k in [64 kt[g], 64 kt[g+1]) of A[m][k] B[n][k]
+// C_g [Ma][Nb] fp32 = sum over k in [64 kt[g], 64 kt[g+1]) of A[m][k] B[n][k]; two_slices:
+// kt gives every group at least two k-slices (then the persistent kernel runs)
 hipError_t launch_gemm_wgrad_bf16(const void* A, int lda, const void* B, int ldb,
                                   const int32_t* kt, int groups, int Ma, int Nb, float* C,
-                                  hipStream_t st);
+                                  hipStream_t st, bool two_slices);
 
 // Tile table of the shared experts (one group of all T rows).
 hipError_t launch_shared_table(int64_t T, int BM, int32_t* offsets, int32_t* tile_off,

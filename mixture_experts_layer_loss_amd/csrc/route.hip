@@ -8,11 +8,11 @@
 // A block owns TB consecutive tokens (bf16: 8 waves, 16 tokens when E <= 16, else 64; fp32: 4
 // waves, 64 tokens). The logits tile [TB x E] never leaves the chip: bf16 inputs go through
 // v_mfma_f32_16x16x32_bf16 with the hidden dimension split across the waves; fp32 inputs use
-// plain FMA loops. Then one lane per token walks the experts in index order (softmax maximum and
-// sum, then a sorted top-k insertion in registers), so equal scores go to the lower expert index
-// and no cross-lane operation sits on the per-token path. Statistics leave as per-block partials
-// (expert histogram, sum of g, sum of lse^2) reduced later in a fixed order, so every result is
-// bit-reproducible.
+// plain FMA loops. Then every thread of the block works on the routing: a group of lanes shares a
+// token, each lane walking a strided share of the experts, and butterflies combine the group's
+// maximum, exp-sum and top-k (equal scores go to the lower expert index). Statistics leave as
+// per-block partials (expert histogram, sum of g, sum of lse^2) reduced later in a fixed order, so
+// every result is bit-reproducible.
 #include "moe_internal.h"
 
 #include <math.h>
@@ -53,331 +53,201 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// XOR butterflies over aligned groups of G lanes: every lane of a group ends with the same bits
+// (each step combines the same two values, in either order, with a commutative operation).
+template <int G>
+__device__ __forceinline__ float bfly_max(float v) {
+#pragma unroll
+  for (int s = 1; s < G; s <<= 1) v = fmaxf(v, __shfl_xor(v, s));
+  return v;
+}
+template <int G>
+__device__ __forceinline__ float bfly_sum(float v) {
+#pragma unroll
+  for (int s = 1; s < G; s <<= 1) v += __shfl_xor(v, s);
+  return v;
+}
+
 // ------------------------------------------------------------------------------------------
-// Per-token routing over the logits tile in LDS, shared by both dtypes. One lane per token:
-// wave w takes tokens [w TB/4, (w+1) TB/4) of the block's TB. The lane walks the experts in index
-// order: maximum, sum of exp(l - m) (so lse = m + ln sum), then g_e = exp(l_e - lse) or, with
-// sigmoid scoring, g_e = 1 / (1 + exp(-l_e)) (written back over the logit), s_e = g_e + b_e and the
-// sorted top-KM insertion; k <= KM. Block partials: the expert histogram (LDS integer atomics:
-// order-free), sum over tokens of g_e (sigmoid: g_e / sum_e' g_e') per expert and sum of lse^2,
-// the latter two summed in token order.
-//   L: [TB][Ls] fp32; scratch: >= MOE_E_MAX ints + 64 floats. flags: kRouteRenorm | kRouteSigmoid.
+// Per-token routing over the logits tile in LDS, shared by every router kernel. G consecutive
+// lanes share a token (G = threads / TB, a power of two up to 64, so a token's lanes sit in one
+// wave) and lane j of the group owns experts j, j + G, j + 2G, ... . The maximum m and the sum of
+// exp(l - m) over the experts (lse = m + ln sum) are formed per lane in index order and combined by
+// butterflies. Each lane then writes its scores g_e = exp(l_e - lse) (sigmoid scoring:
+// 1 / (1 + exp(-l_e))) back over the logits and keeps its best KM selection scores s_e = g_e + b_e,
+// sorted. The top-k is k rounds of a butterfly arg-max under one total order, higher s first and
+// equal s to the lower expert index (the order a walk over the experts in index order with a
+// strict comparison selects in): each lane offers its best expert not yet taken and the winner's
+// owner drops it, so slot j holds the j-th expert of that order. Block partials: the expert
+// histogram (LDS integer atomics: order-free), per expert the sum over the block's tokens of g_e
+// (sigmoid: g_e / sum_e' g_e'), and the sums of lse^2 and of the routing entropy, each reduced in
+// a fixed tree, so every result is bit-reproducible.
+//   L: [TB][Ls] fp32 logits; hcnt: >= E ints; lsq, hsq: TB floats.
+//   flags: kRouteRenorm | kRouteSigmoid | kRouteExpertChoice (score columns instead of top-k).
 // ------------------------------------------------------------------------------------------
-template <int KM>
+template <int KM, int G>
 __device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, int E, int k,
                              int flags, const float* __restrict__ b,
                              int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
                              int32_t* __restrict__ hist, float* __restrict__ gpart,
                              float* __restrict__ lpart, float* __restrict__ hpart,
                              float* __restrict__ cols, int* hcnt, float* lsq, float* hsq) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const int tpw = TB / nw;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) hcnt[e] = 0;
-  __syncthreads();
-  if (lane < tpw) {
-    const int tl = wave * tpw + lane;
-    const int64_t t = t0 + tl;
-    float lse2 = 0.f, ent = 0.f;
-    if (t < T) {
-      float* row = L + tl * Ls;  // Ls % 4 == 0: 16-byte aligned; the pad past E holds -inf
-      const int E4 = (E + 3) & ~3;
-      float m = -INFINITY;
-#pragma unroll 4
-      for (int e = 0; e < E4; e += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(row + e);
-        m = fmaxf(m, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
-      }
-      float sum = 0.f;
-#pragma unroll 4
-      for (int e = 0; e < E4; e += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(row + e);
-        sum += expf(v.x - m);
-        sum += expf(v.y - m);
-        sum += expf(v.z - m);
-        sum += expf(v.w - m);
-      }
-      const float lse = m + logf(sum);
-      lse2 = lse * lse;
-      float tv[KM];
-      int ti[KM];
-#pragma unroll
-      for (int j = 0; j < KM; ++j) {
-        tv[j] = -INFINITY;
-        ti[j] = 0;
-      }
-      const bool sig = (flags & kRouteSigmoid) != 0;
-      const bool ec = (flags & kRouteExpertChoice) != 0;
-      float ssum = 0.f;  // sigmoid: sum of the scores over the experts (the pad adds 0)
-      float hacc = 0.f;  // entropy term: softmax sum g (l - lse); sigmoid sum s ln s
-      for (int e = 0; e < E4; e += 4) {
-        float4 v = *reinterpret_cast<const float4*>(row + e);
-        const float l4[4] = {v.x, v.y, v.z, v.w};
-        if (sig) {
-          v.x = 1.f / (1.f + expf(-v.x));
-          v.y = 1.f / (1.f + expf(-v.y));
-          v.z = 1.f / (1.f + expf(-v.z));
-          v.w = 1.f / (1.f + expf(-v.w));
-          ssum += v.x;
-          ssum += v.y;
-          ssum += v.z;
-          ssum += v.w;
-        } else {
-          v.x = expf(v.x - lse);
-          v.y = expf(v.y - lse);
-          v.z = expf(v.z - lse);
-          v.w = expf(v.w - lse);
-        }
-        *reinterpret_cast<float4*>(row + e) = v;
-        const float g4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int ee = e + q;
-          if (ee < E) {
-            if (ec) {  // expert choice: columns of logits and scores for the per-expert selection
-              cols[static_cast<int64_t>(ee) * T + t] = l4[q];
-              cols[(static_cast<int64_t>(E) + ee) * T + t] = g4[q];
-            } else {
-              topk_insert<KM>(b != nullptr ? g4[q] + b[ee] : g4[q], ee, tv, ti);
-            }
-            hacc += sig ? (g4[q] > 0.f ? g4[q] * logf(g4[q]) : 0.f) : g4[q] * (l4[q] - lse);
-          }
-        }
-      }
-      // routing entropy of the token's distribution (softmax g, or s / sum s)
-      ent = sig ? logf(ssum) - hacc / ssum : -hacc;
-      float wsum = 0.f;
-#pragma unroll
-      for (int j = 0; j < KM; ++j)
-        if (j < k) wsum += row[ti[j]];
-#pragma unroll
-      for (int j = 0; j < KM; ++j) {
-        if (j < k && !ec) {
-          const float gj = row[ti[j]];
-          topk_idx[t * k + j] = ti[j];
-          topk_w[t * k + j] = (flags & kRouteRenorm) ? gj / wsum : gj;
-          atomicAdd(&hcnt[ti[j]], 1);
-        }
-      }
-      if (sig) {  // the probability statistic uses the scores normalised over the experts
-        const float inv = 1.f / ssum;
-        for (int e = 0; e < E4; ++e) row[e] *= inv;
-      }
-    }
-    lsq[tl] = lse2;
-    hsq[tl] = ent;
-  }
-  __syncthreads();
-  const int64_t blk = blockIdx.x;
-  const int nt = static_cast<int>(min<int64_t>(TB, T - t0));
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    float gs = 0.f;
-    for (int tl = 0; tl < nt; ++tl) gs += L[tl * Ls + e];
-    gpart[blk * E + e] = gs;
-    hist[blk * E + e] = hcnt[e];
-  }
-  if (threadIdx.x == 0) {
-    float ls = 0.f, hs = 0.f;
-    for (int tl = 0; tl < nt; ++tl) {
-      ls += lsq[tl];
-      hs += hsq[tl];
-    }
-    lpart[blk] = ls;
-    hpart[blk] = hs;
-  }
-}
-
-// ------------------------------------------------------------------------------------------
-// Per-token routing of a 64-token block by all eight waves (many experts): lane l owns token l
-// and wave w a slice of the experts, so every lane works. Each wave forms its slice's partial
-// maximum and exp-sum (combined over the waves in wave order, so lse is the same in every wave and
-// reproducible), writes g back over its logits and keeps a sorted top-KM list of its slice. The
-// lists then merge pairwise in three rounds through LDS: the list of the lower expert range takes
-// the other's entries by strict-greater insertion, so equal scores still go to the lower expert
-// index and the merged order is the one a single walk over all experts gives. Wave 0 ends with
-// every token's list and writes the gates. Same outputs and partials as route_tokens.
-//   L: [64][Ls] fp32; part: [8][64] floats; xv/xi: [4][64][KM] exchange lists.
-// ------------------------------------------------------------------------------------------
-template <int KM>
-__device__ void route_tokens_split(float* L, int Ls, int64_t t0, int64_t T, int E, int k,
-                                   int flags, const float* __restrict__ b,
-                                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-                                   int32_t* __restrict__ hist, float* __restrict__ gpart,
-                                   float* __restrict__ lpart, float* __restrict__ hpart,
-                                   float* __restrict__ cols, int* hcnt, float* lsq, float* hsq,
-                                   float* part, float* part2,
-                                   float* xv, int* xi) {
-  constexpr int TB = 64, NW = 8;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tl = lane;
+  static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "lanes per token");
+  const int tid = threadIdx.x;
+  const int tl = tid / G, j = tid % G;  // blockDim.x == TB G
   const int64_t t = t0 + tl;
   const bool live = t < T;
-  const int E4 = (E + 3) & ~3;
-  const int SL = ((E4 / 4 + NW - 1) / NW) * 4;  // experts per wave, a multiple of 4
-  const int e0 = min(wave * SL, E4), e1 = min(e0 + SL, E4);
-  float* row = L + tl * Ls;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) hcnt[e] = 0;
-  // maximum over the experts: slice partials, combined in wave order
-  float m = -INFINITY;
-  for (int e = e0; e < e1; e += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(row + e);
-    m = fmaxf(m, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
-  }
-  part[wave * TB + tl] = m;
-  __syncthreads();
-  m = part[tl];
-  for (int w = 1; w < NW; ++w) m = fmaxf(m, part[w * TB + tl]);
-  float sum = 0.f;
-  for (int e = e0; e < e1; e += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(row + e);
-    sum += expf(v.x - m);
-    sum += expf(v.y - m);
-    sum += expf(v.z - m);
-    sum += expf(v.w - m);
-  }
-  __syncthreads();  // every wave has read the maxima
-  part[wave * TB + tl] = sum;
-  __syncthreads();
-  sum = 0.f;
-  for (int w = 0; w < NW; ++w) sum += part[w * TB + tl];
-  const float lse = m + logf(sum);
-  // scores of the slice, written back over the logits, and the slice's sorted top-KM
   const bool sig = (flags & kRouteSigmoid) != 0;
   const bool ec = (flags & kRouteExpertChoice) != 0;
-  float ssum = 0.f;
-  float hacc = 0.f;  // entropy term of the slice: softmax sum g (l - lse); sigmoid sum s ln s
-  float tv[KM];
-  int ti[KM];
-#pragma unroll
-  for (int j = 0; j < KM; ++j) {
-    tv[j] = -INFINITY;
-    ti[j] = 0;
-  }
-  for (int e = e0; e < e1; e += 4) {
-    float4 v = *reinterpret_cast<const float4*>(row + e);
-    const float l4[4] = {v.x, v.y, v.z, v.w};
-    if (sig) {
-      v.x = 1.f / (1.f + expf(-v.x));
-      v.y = 1.f / (1.f + expf(-v.y));
-      v.z = 1.f / (1.f + expf(-v.z));
-      v.w = 1.f / (1.f + expf(-v.w));
-      ssum += v.x;
-      ssum += v.y;
-      ssum += v.z;
-      ssum += v.w;
-    } else {
-      v.x = expf(v.x - lse);
-      v.y = expf(v.y - lse);
-      v.z = expf(v.z - lse);
-      v.w = expf(v.w - lse);
-    }
-    *reinterpret_cast<float4*>(row + e) = v;
-    const float g4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int ee = e + q;
-      if (ee < E) {
-        if (ec) {  // expert choice: columns of logits and scores for the per-expert selection
-          if (live) {
-            cols[static_cast<int64_t>(ee) * T + t] = l4[q];
-            cols[(static_cast<int64_t>(E) + ee) * T + t] = g4[q];
-          }
-        } else {
-          topk_insert<KM>(b != nullptr ? g4[q] + b[ee] : g4[q], ee, tv, ti);
-        }
-        hacc += sig ? (g4[q] > 0.f ? g4[q] * logf(g4[q]) : 0.f) : g4[q] * (l4[q] - lse);
-      }
-    }
-  }
-  // pairwise merges: round r, waves w with w % 2^(r+1) == 0 take the list of wave w + 2^r
-  for (int r = 0; r < 3; ++r) {
-    const int stride = 1 << r;
-    __syncthreads();  // the exchange buffer is free (and, first time, the partials were read)
-    const bool sender = (wave & (2 * stride - 1)) == stride;
-    const int slot = wave >> (r + 1);  // 0..3 at most
-    if (sender) {
-#pragma unroll
-      for (int j = 0; j < KM; ++j) {
-        xv[(slot * TB + tl) * KM + j] = tv[j];
-        xi[(slot * TB + tl) * KM + j] = ti[j];
-      }
-    }
-    __syncthreads();
-    if ((wave & (2 * stride - 1)) == 0) {
-#pragma unroll
-      for (int j = 0; j < KM; ++j) {
-        const float v = xv[(slot * TB + tl) * KM + j];
-        if (v > tv[KM - 1]) topk_insert<KM>(v, xi[(slot * TB + tl) * KM + j], tv, ti);
-      }
-    }
-  }
-  // slice partials of the score sum (sigmoid) and of the entropy term, combined in wave order
-  part[wave * TB + tl] = ssum;
-  part2[wave * TB + tl] = hacc;
+  for (int e = tid; e < E; e += blockDim.x) hcnt[e] = 0;
   __syncthreads();
-  if (wave == 0 && live && !ec) {
+  float* row = L + tl * Ls;
+  float m = -INFINITY;
+  for (int e = j; e < E; e += G) m = fmaxf(m, row[e]);
+  m = bfly_max<G>(m);
+  float sum = 0.f;
+  for (int e = j; e < E; e += G) sum += expf(row[e] - m);
+  sum = bfly_sum<G>(sum);
+  const float lse = m + logf(sum);
+  float cv[KM], cg[KM];  // this lane's best selection scores and their g, best first
+  int ci[KM];
+#pragma unroll
+  for (int q = 0; q < KM; ++q) {
+    cv[q] = -INFINITY;
+    cg[q] = 0.f;
+    ci[q] = 0x7fffffff;
+  }
+  float ssum = 0.f;  // sigmoid: sum of the scores over the experts
+  float hacc = 0.f;  // entropy term: softmax sum g (l - lse); sigmoid sum s ln s
+  for (int e = j; e < E; e += G) {
+    const float l = row[e];
+    const float g = sig ? 1.f / (1.f + expf(-l)) : expf(l - lse);
+    row[e] = g;
+    if (sig) ssum += g;
+    hacc += sig ? (g > 0.f ? g * logf(g) : 0.f) : g * (l - lse);
+    if (ec) {  // expert choice: columns of logits and scores for the per-expert selection
+      if (live) {
+        cols[static_cast<int64_t>(e) * T + t] = l;
+        cols[(static_cast<int64_t>(E) + e) * T + t] = g;
+      }
+    } else {
+      // sorted insertion; this lane's experts arrive in ascending index order, so a strict
+      // comparison keeps equal scores in index order
+      const float v = b != nullptr ? g + b[e] : g;
+#pragma unroll
+      for (int q = KM - 1; q >= 1; --q) {
+        const bool up = v > cv[q - 1], here = v > cv[q];
+        cv[q] = up ? cv[q - 1] : (here ? v : cv[q]);
+        cg[q] = up ? cg[q - 1] : (here ? g : cg[q]);
+        ci[q] = up ? ci[q - 1] : (here ? e : ci[q]);
+      }
+      const bool top = v > cv[0];
+      cv[0] = top ? v : cv[0];
+      cg[0] = top ? g : cg[0];
+      ci[0] = top ? e : ci[0];
+    }
+  }
+  ssum = bfly_sum<G>(ssum);
+  hacc = bfly_sum<G>(hacc);
+  if (!ec) {
+    int we[KM];
+    float wg[KM];
     float wsum = 0.f;
 #pragma unroll
-    for (int j = 0; j < KM; ++j)
-      if (j < k) wsum += row[ti[j]];
+    for (int r = 0; r < KM; ++r) {
+      we[r] = 0;
+      wg[r] = 0.f;
+      if (r < k) {
+        float v = cv[0], g = cg[0];
+        int e = ci[0];
 #pragma unroll
-    for (int j = 0; j < KM; ++j) {
-      if (j < k) {
-        const float gj = row[ti[j]];
-        topk_idx[t * k + j] = ti[j];
-        topk_w[t * k + j] = (flags & kRouteRenorm) ? gj / wsum : gj;
-        atomicAdd(&hcnt[ti[j]], 1);
+        for (int sh = 1; sh < G; sh <<= 1) {
+          const float v2 = __shfl_xor(v, sh), g2 = __shfl_xor(g, sh);
+          const int e2 = __shfl_xor(e, sh);
+          const bool take = v2 > v || (v2 == v && e2 < e);
+          v = take ? v2 : v;
+          g = take ? g2 : g;
+          e = take ? e2 : e;
+        }
+        we[r] = e;
+        wg[r] = g;
+        wsum += g;  // slot order
+        const bool mine = ci[0] == e;  // expert e has one owner
+#pragma unroll
+        for (int q = 0; q + 1 < KM; ++q) {
+          cv[q] = mine ? cv[q + 1] : cv[q];
+          cg[q] = mine ? cg[q + 1] : cg[q];
+          ci[q] = mine ? ci[q + 1] : ci[q];
+        }
+        cv[KM - 1] = mine ? -INFINITY : cv[KM - 1];
+        ci[KM - 1] = mine ? 0x7fffffff : ci[KM - 1];
+      }
+    }
+    const bool renorm = (flags & kRouteRenorm) != 0;
+#pragma unroll
+    for (int r = 0; r < KM; ++r) {
+      if (r < k && r % G == j && live) {
+        topk_idx[t * k + r] = we[r];
+        topk_w[t * k + r] = renorm ? wg[r] / wsum : wg[r];
+        atomicAdd(&hcnt[we[r]], 1);
       }
     }
   }
-  float tot = 0.f, htot = 0.f;
-  for (int w = 0; w < NW; ++w) {
-    tot += part[w * TB + tl];
-    htot += part2[w * TB + tl];
+  if (sig) {  // the probability statistic uses the scores normalised over the experts
+    const float inv = 1.f / ssum;
+    for (int e = j; e < E; e += G) row[e] *= inv;
   }
-  if (wave == 0) {
+  if (j == 0) {
     lsq[tl] = live ? lse * lse : 0.f;
-    hsq[tl] = live ? (sig ? logf(tot) - htot / tot : -htot) : 0.f;
-  }
-  if (sig) {  // the sigmoid probability statistic normalises by the sum over all experts
-    __syncthreads();  // wave 0 has read the raw scores of every slice
-    const float inv = 1.f / tot;
-    for (int e = e0; e < e1; ++e) row[e] *= inv;
+    // routing entropy of the token's distribution (softmax g, or s / sum s)
+    hsq[tl] = live ? (sig ? logf(ssum) - hacc / ssum : -hacc) : 0.f;
   }
   __syncthreads();
+  // per-expert sums over the block's tokens: 8 lanes per expert each sum a run of tokens in order,
+  // then a butterfly
   const int64_t blk = blockIdx.x;
   const int nt = static_cast<int>(min<int64_t>(TB, T - t0));
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+  constexpr int PE = 8;
+  const int per = (TB + PE - 1) / PE;
+  const int ep = tid / PE, pp = tid % PE;
+  for (int base = 0; base < E; base += static_cast<int>(blockDim.x) / PE) {
+    const int e = base + ep;
     float gs = 0.f;
-    for (int q = 0; q < nt; ++q) gs += L[q * Ls + e];
-    gpart[blk * E + e] = gs;
-    hist[blk * E + e] = hcnt[e];
-  }
-  if (threadIdx.x == 0) {
-    float ls = 0.f, hs = 0.f;
-    for (int q = 0; q < nt; ++q) {
-      ls += lsq[q];
-      hs += hsq[q];
+    if (e < E) {
+      for (int q = 0; q < per; ++q) {
+        const int tq = pp * per + q;
+        if (tq < nt) gs += L[tq * Ls + e];
+      }
     }
-    lpart[blk] = ls;
-    hpart[blk] = hs;
+    gs = bfly_sum<PE>(gs);
+    if (pp == 0 && e < E) {
+      gpart[blk * E + e] = gs;
+      hist[blk * E + e] = hcnt[e];
+    }
+  }
+  if (tid < 64) {  // TB <= 64
+    const float ls = bfly_sum<64>(tid < nt ? lsq[tid] : 0.f);
+    const float hs = bfly_sum<64>(tid < nt ? hsq[tid] : 0.f);
+    if (tid == 0) {
+      lpart[blk] = ls;
+      hpart[blk] = hs;
+    }
   }
 }
 
-// the top-k list length used for k (2, 8 or 16 slots)
-#define MOE_ROUTE_TOKENS_KM(CALL) \
-  do {                            \
-    if (k <= 2) {                 \
-      CALL(2);                    \
-    } else if (k <= 8) {          \
-      CALL(8);                    \
-    } else {                      \
-      CALL(16);                   \
-    }                             \
-  } while (0)
+// The top-k list length of a kernel (KM = 2, 8 or 16 slots, k <= KM) is a template argument
+// chosen on the host: one per-token routine per kernel keeps each kernel small (three inlined
+// copies in one kernel take the device compiler tens of minutes).
+template <typename F>
+hipError_t with_km(int k, F&& f) {
+  if (k <= 2) return f(std::integral_constant<int, 2>{});
+  if (k <= 8) return f(std::integral_constant<int, 8>{});
+  return f(std::integral_constant<int, 16>{});
+}
 
-// logits row stride: a multiple of 4 floats (16-byte reads); with at most 16 lanes walking 16
-// rows, the rows' 4-bank groups are all distinct
-constexpr int kLogitsStride = MOE_E_MAX + 4;
+// logits row stride: 8 banks apart, so the 8 lanes of each of a wave's 8 tokens (lane j reading
+// expert j + 8 i of its token's row) hit 64 distinct banks
+constexpr int kLogitsStride = MOE_E_MAX + 8;
 
 // ------------------------------------------------------------------------------------------
 // bf16: logits on MFMA. A block owns TB = 16 MB tokens; its eight waves split the hidden dimension
@@ -390,7 +260,7 @@ constexpr int kLogitsStride = MOE_E_MAX + 4;
 // ------------------------------------------------------------------------------------------
 constexpr int kRouteThreads = 512;  // 8 waves: K is split 8 ways, two waves per SIMD
 
-template <int MB, int NEB, int NG>
+template <int MB, int NEB, int NG, int KM>
 __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ b,
     int64_t T, int d, int E, int k, int flags, int32_t* __restrict__ topk_idx,
@@ -494,21 +364,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
     }
   }
   __syncthreads();
-  for (int i = tid; i < TB * 4; i += kRouteThreads) {
-    const int e = ((E + 3) & ~3) - 4 + (i & 3);
-    if (e >= E) L[(i >> 2) * kLogitsStride + e] = -INFINITY;
-  }
-  __syncthreads();
-#define MOE_CALL(KM) \
-  route_tokens<KM>(L, kLogitsStride, TB, t0, T, E, k, flags, b, topk_idx, topk_w, hist, gpart, \
-                   lpart, hpart, cols, hcnt, lsq, hsq)
-  MOE_ROUTE_TOKENS_KM(MOE_CALL);
-#undef MOE_CALL
+  route_tokens<KM, kRouteThreads / TB>(L, kLogitsStride, TB, t0, T, E, k, flags, b, topk_idx,
+                                       topk_w, hist, gpart, lpart, hpart, cols, hcnt, lsq, hsq);
 }
 
 // ------------------------------------------------------------------------------------------
 // fp32: logits by sequential FMA over the hidden dimension (one (token, expert) pair per thread).
 // ------------------------------------------------------------------------------------------
+template <int KM>
 __global__ __launch_bounds__(256) void route_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ W, const float* __restrict__ b,
     int64_t T, int d, int E, int k, int flags, int32_t* __restrict__ topk_idx,
@@ -529,16 +392,9 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
     for (int i = 0; i < d; ++i) acc = fmaf(xr[i], wr[i], acc);
     L[tl * kLogitsStride + e] = acc;
   }
-  for (int i = threadIdx.x; i < RT * 4; i += blockDim.x) {
-    const int e = ((E + 3) & ~3) - 4 + (i & 3);
-    if (e >= E) L[(i >> 2) * kLogitsStride + e] = -INFINITY;
-  }
   __syncthreads();
-#define MOE_CALL(KM) \
-  route_tokens<KM>(L, kLogitsStride, RT, t0, T, E, k, flags, b, topk_idx, topk_w, hist, gpart, \
-                   lpart, hpart, cols, hcnt, lsq, hsq)
-  MOE_ROUTE_TOKENS_KM(MOE_CALL);
-#undef MOE_CALL
+  route_tokens<KM, 256 / RT>(L, kLogitsStride, RT, t0, T, E, k, flags, b, topk_idx, topk_w, hist,
+                             gpart, lpart, hpart, cols, hcnt, lsq, hsq);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -561,9 +417,7 @@ constexpr int route_sk() {
   return 2 * (64 + 16 * NEB) * (MOE_ROUTE_SK + 8) * 2 <= 120 * 1024 ? MOE_ROUTE_SK : 64;
 }
 
-// SPLIT: per-token routing by all waves (route_tokens_split) rather than one lane per token; its
-// exchange buffers are only allocated then, so that the other variant keeps two blocks per CU.
-template <int NEB, bool SPLIT>
+template <int NEB, int KM>
 __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ b,
     int64_t T, int d, int E, int k, int flags, int32_t* __restrict__ topk_idx,
@@ -584,10 +438,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
   __shared__ int hcnt[MOE_E_MAX];
   __shared__ float lsq[TB];
   __shared__ float hsq[TB];
-  __shared__ float part[SPLIT ? 8 * TB : 1];         // per-wave partials of the split routing
-  __shared__ float part2[SPLIT ? 8 * TB : 1];
-  __shared__ float xv[SPLIT ? 4 * TB * 16 : 1];      // its exchange lists (KM <= 16)
-  __shared__ int xi[SPLIT ? 4 * TB * 16 : 1];
   bf16_t* st = reinterpret_cast<bf16_t*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tb = wave & 3, eh = wave >> 2;
@@ -652,13 +502,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
     }
   };
   const int nk = (d + kSK - 1) / kSK;
+#ifndef MOE_ROUTE_ROT
+#define MOE_ROUTE_ROT 0
+#endif
+  const int rot = MOE_ROUTE_ROT ? static_cast<int>(blockIdx.x % nk) : 0;
+  auto kof = [&](int j) __attribute__((always_inline)) {
+    const int q = j + rot;
+    return (q >= nk ? q - nk : q) * kSK;
+  };
   // k-slice j sits in ring slot j % PF from its load until its LDS store one k-step before use
   static_for<0, PF>([&](auto pc) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
-    if (P < nk) gload(rg[P], P * kSK);
+    if (P < nk) gload(rg[P], kof(P));
   });
   lstore(rg[0], 0);
-  if (PF < nk) gload(rg[0], PF * kSK);
+  if (PF < nk) gload(rg[0], kof(PF));
   __syncthreads();
   for (int base = 0; base < nk; base += PF) {
     static_for<0, PF>([&](auto jc) __attribute__((always_inline)) {
@@ -668,7 +526,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
       if (ks < nk) {
         if (ks + 1 < nk) {
           lstore(rg[NEXT], (ks + 1) & 1);  // stage read by k-step ks - 1, behind the barrier
-          if (ks + 1 + PF < nk) gload(rg[NEXT], (ks + 1 + PF) * kSK);
+          if (ks + 1 + PF < nk) gload(rg[NEXT], kof(ks + 1 + PF));
         }
         compute(ks & 1);
         __syncthreads();
@@ -685,20 +543,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
     }
   }
   __syncthreads();
-  for (int i = tid; i < TB * 4; i += kRouteThreads) {
-    const int e = ((E + 3) & ~3) - 4 + (i & 3);
-    if (e >= E) L[(i >> 2) * kLogitsStride + e] = -INFINITY;
-  }
-  __syncthreads();
-#define MOE_CALL(KM)                                                                           \
-  if constexpr (SPLIT)                                                                         \
-    route_tokens_split<KM>(L, kLogitsStride, t0, T, E, k, flags, b, topk_idx, topk_w, hist,     \
-                           gpart, lpart, hpart, cols, hcnt, lsq, hsq, part, part2, xv, xi);                             \
-  else                                                                                         \
-    route_tokens<KM>(L, kLogitsStride, TB, t0, T, E, k, flags, b, topk_idx, topk_w, hist, gpart, \
-                     lpart, hpart, cols, hcnt, lsq, hsq)
-  MOE_ROUTE_TOKENS_KM(MOE_CALL);
-#undef MOE_CALL
+  route_tokens<KM, kRouteThreads / TB>(L, kLogitsStride, TB, t0, T, E, k, flags, b, topk_idx,
+                                       topk_w, hist, gpart, lpart, hpart, cols, hcnt, lsq, hsq);
 }
 
 template <int NEB>
@@ -706,17 +552,14 @@ hipError_t launch_bf16_lds(hipStream_t st, const void* x, const void* W, const f
                            int d, int E, int k, int flags, int32_t* topk_idx, float* topk_w,
                            int32_t* hist, float* gpart, float* lpart, float* hpart,
                            float* cols) {
-  // short lists over at most 128 experts stay one lane per token (cheaper than the merge rounds)
   const dim3 grid(static_cast<unsigned>(cdiv(T, 64)));
-  if (NEB <= 8 && k <= 2)
-    hipLaunchKernelGGL((route_bf16_lds_kernel<NEB, false>), grid, dim3(kRouteThreads), 0, st,
-                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W), b, T, d, E,
-                       k, flags, topk_idx, topk_w, hist, gpart, lpart, hpart, cols);
-  else
-    hipLaunchKernelGGL((route_bf16_lds_kernel<NEB, true>), grid, dim3(kRouteThreads), 0, st,
-                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W), b, T, d, E,
-                       k, flags, topk_idx, topk_w, hist, gpart, lpart, hpart, cols);
-  return hipGetLastError();
+  return with_km(k, [&](auto km) {
+    hipLaunchKernelGGL((route_bf16_lds_kernel<NEB, decltype(km)::value>), grid,
+                       dim3(kRouteThreads), 0, st, static_cast<const bf16_t*>(x),
+                       static_cast<const bf16_t*>(W), b, T, d, E, k, flags, topk_idx, topk_w, hist,
+                       gpart, lpart, hpart, cols);
+    return hipGetLastError();
+  });
 }
 
 template <int MB, int NEB, int NG>
@@ -725,11 +568,13 @@ hipError_t launch_bf16(hipStream_t st, const void* x, const void* W, const float
                        float* topk_w, int32_t* hist, float* gpart, float* lpart, float* hpart,
                            float* cols) {
   const int64_t nblk = cdiv(T, 16 * MB);
-  hipLaunchKernelGGL((route_bf16_kernel<MB, NEB, NG>), dim3(static_cast<unsigned>(nblk)),
-                     dim3(kRouteThreads), 0, st,
-                     static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W), b, T, d, E, k,
-                     flags, topk_idx, topk_w, hist, gpart, lpart, hpart, cols);
-  return hipGetLastError();
+  return with_km(k, [&](auto km) {
+    hipLaunchKernelGGL((route_bf16_kernel<MB, NEB, NG, decltype(km)::value>),
+                       dim3(static_cast<unsigned>(nblk)), dim3(kRouteThreads), 0, st,
+                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W), b, T, d, E,
+                       k, flags, topk_idx, topk_w, hist, gpart, lpart, hpart, cols);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace
@@ -742,10 +587,13 @@ hipError_t launch_route(int dtype, int64_t T, int d, int E, int k, int flags, co
                         float* cols, hipStream_t st) {
   if (dtype == MOE_F32) {
     const int64_t nblk = cdiv(T, RT);
-    hipLaunchKernelGGL(route_f32_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
-                       static_cast<const float*>(x), static_cast<const float*>(W_r), b, T, d, E,
-                       k, flags, topk_idx, topk_w, hist, gpart, lpart, hpart, cols);
-    return hipGetLastError();
+    return with_km(k, [&](auto km) {
+      hipLaunchKernelGGL((route_f32_kernel<decltype(km)::value>), dim3(static_cast<unsigned>(nblk)),
+                         dim3(256), 0, st, static_cast<const float*>(x),
+                         static_cast<const float*>(W_r), b, T, d, E, k, flags, topk_idx, topk_w,
+                         hist, gpart, lpart, hpart, cols);
+      return hipGetLastError();
+    });
   }
   const int neb = static_cast<int>(cdiv(E, 16));
 #define MOE_ROUTE_CASE(N)                                                                   \
