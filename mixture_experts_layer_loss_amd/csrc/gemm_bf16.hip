@@ -477,6 +477,43 @@ __device__ __forceinline__ void run_remainder_tile(
                                           K, C, N, C2, C3, g, row_begin, rows, n0);
 }
 
+// K chunk ks of `split` of remainder tile L of a plain product (the long-K down projection): the
+// tile's rows times the chunk's k-slices, as fp32 partial sums into
+// part[((ks groups + g) 128 + r) N + n] for remainder row r of group g. Every chunk is a whole
+// number of k-slices except perhaps the last (KTAIL). finish_split_kernel adds the chunks.
+template <bool KTAIL>
+__device__ __forceinline__ void run_remainder_split(
+    unsigned char* lds, int64_t L, int ks, int split, const bf16_t* __restrict__ A,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off, int groups,
+    const bf16_t* __restrict__ B0, int64_t group_stride, int N, int K, float* __restrict__ part) {
+  const int nb_count = (N + BN - 1) / BN;
+  const int32_t* t128 = tile_off + (groups + 1);
+  const int32_t* t64 = tile_off + 2 * (groups + 1);
+  const int64_t n128 = static_cast<int64_t>(t128[groups]) * nb_count;
+  const int64_t n64 = static_cast<int64_t>(t64[groups]) * nb_count;
+  const int32_t* table = L < n128 ? t128 : t64;
+  if (L >= n128) {
+    L -= n128;
+    if (L >= n64) return;
+  }
+  const int g = find_group(table, groups, nb_count, L);
+  const int64_t local = L - static_cast<int64_t>(table[g]) * nb_count;
+  const int rows_g = offsets[g + 1] - offsets[g];
+  const int row_begin = offsets[g] + (rows_g & ~255);
+  const int rows = rows_g & 255;
+  const int n0 = static_cast<int>(local) * BN;
+  const int nk = (K + BK - 1) / BK;
+  const int k_lo = nk * ks / split * BK, k_hi = min(K, nk * (ks + 1) / split * BK);
+  const bf16_t* Ak = A + static_cast<int64_t>(row_begin) * K + k_lo;
+  bf16_t* P = reinterpret_cast<bf16_t*>(part + (static_cast<int64_t>(ks) * groups + g) * 128 * N);
+  if (table == t128)
+    run_tile<2, KTAIL, false, 128>(lds, Ak, K, nullptr, B0 + k_lo, nullptr, group_stride, K, N,
+                                   k_hi - k_lo, P, N, nullptr, nullptr, g, 0, rows, n0);
+  else
+    run_tile<2, KTAIL, false, 64>(lds, Ak, K, nullptr, B0 + k_lo, nullptr, group_stride, K, N,
+                                  k_hi - k_lo, P, N, nullptr, nullptr, g, 0, rows, n0);
+}
+
 // tile_off: three tables of groups + 1 entries: 256-row tiles, 128-row tiles, 64-row tiles.
 // Blocks [0, main_blocks) serve the 256-row tiles, the rest the smaller ones.
 template <int EPI, bool KTAIL, bool GATHER, bool BKN = false>
@@ -485,7 +522,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tile_off, int groups, int main_blocks,
     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, int64_t group_stride, int N,
-    int K, bf16_t* __restrict__ C, float* __restrict__ C2, float* __restrict__ C3) {
+    int K, bf16_t* __restrict__ C, float* __restrict__ C2, float* __restrict__ C3,
+    float* __restrict__ part, int split) {
   constexpr int BNO = (EPI == 0 || EPI == 3 || EPI == 4) ? BN / 2 : BN;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int nb_count = (N + BNO - 1) / BNO;
@@ -506,9 +544,49 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
                                       C3, g, row_begin, rows, nb * BNO);
     return;
   }
+  if constexpr (EPI == 1 && !GATHER && !BKN) {
+    if (split > 1) {  // remainder tiles in K chunks: fp32 partials, summed by finish_split_kernel
+      const int64_t Lr = static_cast<int64_t>(blockIdx.x) - main_blocks;
+      run_remainder_split<KTAIL>(lds, Lr / split, static_cast<int>(Lr % split), split, A, offsets,
+                                 tile_off, groups, B0, group_stride, N, K, part);
+      return;
+    }
+  }
   run_remainder_tile<EPI, KTAIL, GATHER, BKN>(lds, static_cast<int64_t>(blockIdx.x) - main_blocks,
                                              A, gather, offsets, tile_off, groups, B0, B1,
                                              group_stride, N, K, C, C2, C3);
+}
+
+// The rows of the split remainder tiles: out row = bf16(sum over the K chunks, in chunk order, of
+// the fp32 partials), for each group's 1..128 rows past its 256-row tiles. One block per (group,
+// remainder row), 8 columns per thread.
+__global__ __launch_bounds__(256) void finish_split_kernel(const int32_t* __restrict__ offsets,
+                                                           int groups, int N, int split,
+                                                           const float* __restrict__ part,
+                                                           bf16_t* __restrict__ out) {
+  const int g = static_cast<int>(blockIdx.x) / 128, r = static_cast<int>(blockIdx.x) % 128;
+  const int rows_g = offsets[g + 1] - offsets[g];
+  const int rem = rows_g & 255;
+  if (rem == 0 || rem > 128 || r >= rem) return;
+  const int c = (static_cast<int>(blockIdx.y) * 256 + static_cast<int>(threadIdx.x)) * 8;
+  if (c >= N) return;
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  for (int ks = 0; ks < split; ++ks) {
+    const float* p = part + ((static_cast<int64_t>(ks) * groups + g) * 128 + r) * N + c;
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+    v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
+           (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+  const int64_t row = offsets[g] + (rows_g & ~255) + r;
+  *reinterpret_cast<uint4*>(out + row * N + c) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // One grouped product of the persistent kernel: groups of rows [offsets[g], offsets[g+1]) of A
@@ -1131,7 +1209,7 @@ hipError_t launch_gemm_t(const bf16_t* A, const int32_t* gather, const int32_t* 
                          const int32_t* tile_off,
                          int groups, int64_t max_tiles, const bf16_t* B0, const bf16_t* B1,
                          int64_t group_stride, int N, int K, bf16_t* C, float* C2,
-                         float* C3, hipStream_t st, int64_t a_rows) {
+                         float* C3, hipStream_t st, int64_t a_rows, float* part) {
   constexpr int BNO = (EPI == 0 || EPI == 3 || EPI == 4) ? BN / 2 : BN;
   const int64_t nb = cdiv(N, BNO);
   if constexpr ((EPI == 0 || EPI == 1) && !BKN) {
@@ -1140,9 +1218,12 @@ hipError_t launch_gemm_t(const bf16_t* A, const int32_t* gather, const int32_t* 
     if (persistent_ok(P0, a_rows))
       return launch_persistent<EPI, KTAIL, GATHER>(P0, max_tiles, none, 0, st);
   }
+  // the remainder tiles of a plain long-K product in two K chunks, so that they spread over all
+  // CUs instead of running as a short last round on a few (part: [2][groups][128][N] fp32)
+  const int split = (EPI == 1 && !GATHER && !BKN && part != nullptr) ? 2 : 1;
   // the 256-row tiles, then at most one 128-row and one 64-row tile per group
   const int64_t main_blocks = cdiv(max_tiles * nb, NXCD) * NXCD;
-  const int64_t grid = main_blocks + 2 * static_cast<int64_t>(groups) * nb;
+  const int64_t grid = main_blocks + 2 * static_cast<int64_t>(groups) * nb * split;
   // two K stages of the 256-row class or its epilogue tile, whichever is larger
   constexpr size_t kMain = 2 * Geo<256>::STAGE;
   constexpr size_t kEpi = static_cast<size_t>(256) * (BNO + 8) * sizeof(bf16_t);
@@ -1159,7 +1240,13 @@ hipError_t launch_gemm_t(const bf16_t* A, const int32_t* gather, const int32_t* 
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((grouped_gemm_kernel<EPI, KTAIL, GATHER, BKN>), dim3(static_cast<unsigned>(grid)),
                      dim3(NT), lds, st, A, gather, offsets, tile_off, groups,
-                     static_cast<int>(main_blocks), B0, B1, group_stride, N, K, C, C2, C3);
+                     static_cast<int>(main_blocks), B0, B1, group_stride, N, K, C, C2, C3, part,
+                     split);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || split == 1) return e;
+  hipLaunchKernelGGL(finish_split_kernel,
+                     dim3(static_cast<unsigned>(groups) * 128u, static_cast<unsigned>(cdiv(N / 8, 256))),
+                     dim3(256), 0, st, offsets, groups, N, split, part, C);
   return hipGetLastError();
 }
 
@@ -1169,13 +1256,14 @@ hipError_t launch_gemm(const bf16_t* A, const int32_t* gather, const int32_t* of
                        const int32_t* tile_off, int groups, int64_t max_tiles, const bf16_t* B0,
                        const bf16_t* B1, int64_t group_stride, int N, int K, bf16_t* C,
                        hipStream_t st, float* C2 = nullptr, float* C3 = nullptr,
-                       int64_t a_rows = -1) {
+                       int64_t a_rows = -1, float* part = nullptr) {
   if (K % BK == 0)
     return launch_gemm_t<EPI, false, GATHER, BKN>(A, gather, offsets, tile_off, groups, max_tiles,
                                                   B0, B1, group_stride, N, K, C, C2, C3, st,
-                                                  a_rows);
+                                                  a_rows, part);
   return launch_gemm_t<EPI, true, GATHER, BKN>(A, gather, offsets, tile_off, groups, max_tiles, B0,
-                                               B1, group_stride, N, K, C, C2, C3, st, a_rows);
+                                               B1, group_stride, N, K, C, C2, C3, st, a_rows,
+                                               part);
 }
 
 }  // namespace
@@ -1316,13 +1404,15 @@ hipError_t launch_gemm_wgrad_bf16(const void* A, int lda, const void* B, int ldb
   return hipGetLastError();
 }
 
+// part: NULL, or [2][groups][128][d] fp32 for the remainder tiles of a long-K product in K chunks
 hipError_t launch_gemm_down_bf16(int groups, int d, int Mg, const int32_t* offsets,
                                  const int32_t* tile_off, int64_t max_tiles, const void* W_down,
-                                 const void* h, void* out, hipStream_t st, int64_t a_rows) {
+                                 const void* h, void* out, hipStream_t st, int64_t a_rows,
+                                 float* part) {
   return launch_gemm<1, false>(static_cast<const bf16_t*>(h), nullptr, offsets, tile_off, groups,
                                max_tiles, static_cast<const bf16_t*>(W_down), nullptr,
                                static_cast<int64_t>(Mg) * d, d, Mg, static_cast<bf16_t*>(out), st,
-                               nullptr, nullptr, a_rows);
+                               nullptr, nullptr, a_rows, part);
 }
 
 // The routed gate/up product (rows of x gathered through `gather`) and the shared experts' (all T
@@ -1362,7 +1452,7 @@ hipError_t launch_gemm_down_shared_bf16(int groups, int d, int Mg, const int32_t
                                         int64_t T, int SMg, const int32_t* sh_offsets,
                                         const int32_t* sh_tile_off, int64_t sh_tiles,
                                         const void* Ws_down, const void* h_sh, void* sh,
-                                        hipStream_t st) {
+                                        hipStream_t st, float* part) {
   GemmProb P0{static_cast<const bf16_t*>(h), nullptr, offsets, tile_off,
               static_cast<const bf16_t*>(W_down), nullptr, static_cast<int64_t>(Mg) * d,
               static_cast<bf16_t*>(out), groups, d, Mg};
@@ -1375,10 +1465,10 @@ hipError_t launch_gemm_down_shared_bf16(int groups, int d, int Mg, const int32_t
     return launch_persistent<1, true, false>(P0, max_tiles, P1, sh_tiles, st);
   }
   hipError_t e = launch_gemm_down_bf16(groups, d, Mg, offsets, tile_off, max_tiles, W_down, h, out,
-                                       st, R);
+                                       st, R, part);
   if (e != hipSuccess) return e;
   return launch_gemm_down_bf16(1, d, SMg, sh_offsets, sh_tile_off, sh_tiles, Ws_down, h_sh, sh, st,
-                               T);
+                               T, nullptr);
 }
 
 }  // namespace moe

@@ -15,7 +15,8 @@ hipError_t launch_gemm_up_bf16(int groups, int d, int Mg, const void* rows,
                                const void* W_up, void* h, hipStream_t st, int64_t a_rows);
 hipError_t launch_gemm_down_bf16(int groups, int d, int Mg, const int32_t* offsets,
                                  const int32_t* tile_off, int64_t max_tiles, const void* W_down,
-                                 const void* h, void* out, hipStream_t st, int64_t a_rows);
+                                 const void* h, void* out, hipStream_t st, int64_t a_rows,
+                                 float* part);
 hipError_t launch_gemm_up_shared_bf16(int groups, int d, int Mg, const void* x,
                                       const int32_t* gather, const int32_t* offsets,
                                       const int32_t* tile_off, int64_t max_tiles,
@@ -30,7 +31,7 @@ hipError_t launch_gemm_down_shared_bf16(int groups, int d, int Mg, const int32_t
                                         int64_t T, int SMg, const int32_t* sh_offsets,
                                         const int32_t* sh_tile_off, int64_t sh_tiles,
                                         const void* Ws_down, const void* h_sh, void* sh,
-                                        hipStream_t st);
+                                        hipStream_t st, float* part);
 hipError_t launch_gemm_up_f32(int groups, int d, int Mg, const void* rows,
                               const int32_t* gather, const int32_t* offsets,
                               const int32_t* tile_off, int64_t max_tiles, const void* W_gate,
@@ -71,11 +72,12 @@ hipError_t launch_gemm_up(int dtype, int groups, int d, int Mg, const void* rows
 
 hipError_t launch_gemm_down(int dtype, int groups, int d, int Mg, const int32_t* offsets,
                             const int32_t* tile_off, int64_t max_tiles, const void* W_down,
-                            const void* h, void* out, hipStream_t st, int64_t a_rows) {
+                            const void* h, void* out, hipStream_t st, int64_t a_rows,
+                            float* part) {
   return dtype == MOE_F32 ? launch_gemm_down_f32(groups, d, Mg, offsets, tile_off, max_tiles,
                                                  W_down, h, out, st)
                           : launch_gemm_down_bf16(groups, d, Mg, offsets, tile_off, max_tiles,
-                                                  W_down, h, out, st, a_rows);
+                                                  W_down, h, out, st, a_rows, part);
 }
 }  // namespace moe
 
@@ -181,6 +183,7 @@ struct LayerPlan {
   void *h, *out_perm, *h_sh, *sh;
   float* cols;      // expert choice: [2][E][T] logits and scores
   int32_t* row_of;  // expert choice: [E][T] row of (t, e) or -1
+  float* part;      // [2][E][128][d] fp32 partials of the down product's split remainder tiles
 };
 LayerPlan plan_layer(Carve& c, const moe_shape* s) {
   const size_t P = static_cast<size_t>(s->T) * s->k;
@@ -218,7 +221,22 @@ LayerPlan plan_layer(Carve& c, const moe_shape* s) {
     p.cols = nullptr;
     p.row_of = nullptr;
   }
+  p.part = nullptr;
   return p;
+}
+
+// Whether the layer forward splits the routed down product's remainder tiles (1..128 rows past
+// each expert's 256-row tiles) into two K chunks: bf16 products too long for the persistent kernel
+// (M over 128 k-slices), with at least 512 routed rows per expert on average, so that the partial
+// buffer stays small next to h.
+bool down_split(const moe_shape* s) {
+  return s->dtype == MOE_BF16 && s->M > 128 * 64 &&
+         routed_rows(s) >= static_cast<int64_t>(512) * s->E;
+}
+
+// The partial buffer, carved after everything else of the layer forward's workspace.
+float* plan_split(Carve& c, const moe_shape* s) {
+  return down_split(s) ? c.take<float>(static_cast<size_t>(2) * s->E * 128 * s->d) : nullptr;
 }
 
 struct LossBackwardPlan {
@@ -462,7 +480,7 @@ size_t moe_workspace_size(const moe_shape* s, int call) {
     case MOE_CALL_ROUTE: plan_route(c, s); break;
     case MOE_CALL_DISPATCH: plan_dispatch(c, s); break;
     case MOE_CALL_EXPERT_FFN: c.take<int32_t>(3 * (MOE_E_MAX + 1)); break;
-    case MOE_CALL_LAYER: plan_layer(c, s); break;
+    case MOE_CALL_LAYER: plan_layer(c, s); plan_split(c, s); break;
     case MOE_CALL_LOSS_BACKWARD: plan_loss_backward(c, s); break;
     case MOE_CALL_LAYER_BACKWARD: plan_layer_backward(c, s); break;
     default: return 0;
@@ -599,11 +617,16 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
     if (t && !aligned16(t)) return MOE_ERR_INVALID_ARGUMENT;
   if (s->S > 0 && (!aligned16(Ws_gate) || !aligned16(Ws_up) || !aligned16(Ws_down)))
     return MOE_ERR_INVALID_ARGUMENT;
-  if (!ws || ws_bytes < moe_workspace_size(s, MOE_CALL_LAYER)) return MOE_ERR_WORKSPACE;
+  // the workspace must hold plan_layer; the split partials (carved last) are used when it also
+  // holds them, as a workspace of moe_workspace_size bytes does
+  Carve c0(nullptr);
+  plan_layer(c0, s);
+  if (!ws || ws_bytes < c0.used) return MOE_ERR_WORKSPACE;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   Carve c(ws);
   LayerPlan p = plan_layer(c, s);
+  if (ws_bytes >= moe_workspace_size(s, MOE_CALL_LAYER)) p.part = plan_split(c, s);
   Carve cs(saved);
   const SavedPlan sv = plan_saved(cs, s);  // all NULL when saved is NULL
   int32_t* idx = topk_idx ? topk_idx : p.topk_idx;
@@ -664,7 +687,7 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
     if (e == hipSuccess)
       e = launch_gemm_down_shared_bf16(s->E, s->d, s->M, p.offsets, p.tile_off, max_tiles, W_down,
                                        p.h, p.out_perm, routed_rows(s), s->T, SM, p.sh_offsets,
-                                       p.sh_tile_off, sh_tiles, Ws_down, p.h_sh, p.sh, hs);
+                                       p.sh_tile_off, sh_tiles, Ws_down, p.h_sh, p.sh, hs, p.part);
     marks.mark(4, hs);
   } else {
     if (e == hipSuccess && saved != nullptr)  // h, and G and U kept for the backward
@@ -676,7 +699,7 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
     marks.mark(3, hs);
     if (e == hipSuccess)
       e = launch_gemm_down(s->dtype, s->E, s->d, s->M, p.offsets, p.tile_off, max_tiles, W_down,
-                           p.h, p.out_perm, hs, routed_rows(s));
+                           p.h, p.out_perm, hs, routed_rows(s), p.part);
     marks.mark(4, hs);
   }
   if (e == hipSuccess && s->S > 0 && !fold_shared) {
@@ -719,8 +742,10 @@ moe_status moe_layer_forward_noalloc(const moe_shape* s, const void* x, const vo
                                      float gamma, void* saved, void* stream) {
   moe_status st = moe_check_shape(s);
   if (st != MOE_OK) return st;
-  const size_t need = moe_workspace_size(s, MOE_CALL_LAYER);
-  if (need > MOE_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  // the scratch must hold the layer's plan; the split partials are used when they fit as well
+  Carve c0(nullptr);
+  plan_layer(c0, s);
+  if (c0.used > MOE_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
   // every argument check of the allocating call, before the scratch is looked up: a dry run with
   // a null workspace fails only on the workspace if everything else is valid
   st = moe_layer_forward(s, x, W_r, b, W_gate, W_up, W_down, Ws_gate, Ws_up, Ws_down, y, topk_idx,

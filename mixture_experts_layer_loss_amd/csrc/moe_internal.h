@@ -111,9 +111,12 @@ hipError_t launch_gemm_up(int dtype, int groups, int d, int Mg, const void* rows
                           const int32_t* gather, const int32_t* offsets, const int32_t* tile_off,
                           int64_t max_tiles, const void* W_gate, const void* W_up, void* h,
                           hipStream_t st, int64_t a_rows);
+// part: NULL, or [2][groups][128][d] fp32 in which a bf16 product too long for the persistent
+// kernel computes its remainder tiles (1..128 rows past each group's 256-row tiles) in two K chunks
 hipError_t launch_gemm_down(int dtype, int groups, int d, int Mg, const int32_t* offsets,
                             const int32_t* tile_off, int64_t max_tiles, const void* W_down,
-                            const void* h, void* out, hipStream_t st, int64_t a_rows);
+                            const void* h, void* out, hipStream_t st, int64_t a_rows,
+                            float* part = nullptr);
 
 // Gradient of aux + z_coef z with respect to the logits, from the router's logit and score
 // columns [E][T]; n [E] loads, fden the f_e denominator. dl [T][E] and dlT [E][T] fp32.

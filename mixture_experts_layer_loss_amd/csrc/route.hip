@@ -502,21 +502,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
     }
   };
   const int nk = (d + kSK - 1) / kSK;
-#ifndef MOE_ROUTE_ROT
-#define MOE_ROUTE_ROT 0
-#endif
-  const int rot = MOE_ROUTE_ROT ? static_cast<int>(blockIdx.x % nk) : 0;
-  auto kof = [&](int j) __attribute__((always_inline)) {
-    const int q = j + rot;
-    return (q >= nk ? q - nk : q) * kSK;
-  };
   // k-slice j sits in ring slot j % PF from its load until its LDS store one k-step before use
   static_for<0, PF>([&](auto pc) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
-    if (P < nk) gload(rg[P], kof(P));
+    if (P < nk) gload(rg[P], P * kSK);
   });
   lstore(rg[0], 0);
-  if (PF < nk) gload(rg[0], kof(PF));
+  if (PF < nk) gload(rg[0], PF * kSK);
   __syncthreads();
   for (int base = 0; base < nk; base += PF) {
     static_for<0, PF>([&](auto jc) __attribute__((always_inline)) {
@@ -526,7 +518,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
       if (ks < nk) {
         if (ks + 1 < nk) {
           lstore(rg[NEXT], (ks + 1) & 1);  // stage read by k-step ks - 1, behind the barrier
-          if (ks + 1 + PF < nk) gload(rg[NEXT], kof(ks + 1 + PF));
+          if (ks + 1 + PF < nk) gload(rg[NEXT], (ks + 1 + PF) * kSK);
         }
         compute(ks & 1);
         __syncthreads();

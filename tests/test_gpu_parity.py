@@ -604,6 +604,10 @@ LAYER_CASES = [
     ("tiny_fp32", dict(scoring="sigmoid")),
     ("deepseek_v2", dict(T=600, d=320, M=136, scoring="sigmoid")),
     ("sigmoid_v3", dict(T=700, d=256, M=128)),
+    # down products over 128 k-slices with >= 512 rows per expert: remainder tiles in two K chunks
+    # (64-row class, N tail 264 = 256 + 8; skewed loads with 64- and 128-row classes, K tail 8200)
+    ("mixtral_8x7b", dict(T=2100, d=264, M=8256, E=4, k=2)),
+    ("skewed_capacity", dict(T=2400, d=128, M=8200, E=4, k=2, c=None)),
     # expert choice: shared experts; fp32; ragged K/N tails with uncovered tokens; sigmoid scores
     ("expert_choice", dict(T=600, d=256, M=128)),
     ("tiny_fp32", dict(routing="expert")),
