@@ -338,9 +338,7 @@ moe_status moe_balance_loss_backward(const moe_shape* s, const void* x, const vo
  *     (fp32: MOE_ERR_UNSUPPORTED); 16-byte aligned.
  *   ws device workspace of moe_workspace_size(s, MOE_CALL_LAYER_BACKWARD) bytes
  * bf16 layers read the weights in place; one expert's W_gate and W_up together (4 M d bytes), and
- * the shared experts' (4 S M d bytes), must stay under 4 GiB, and the weight-gradient operands
- * (64 (ceil(R / 64) + E) and 64 ceil(T / 64) columns, R = moe_routed_rows(s)) under 2^22 columns
- * (MOE_ERR_UNSUPPORTED otherwise).
+ * the shared experts' (4 S M d bytes), must stay under 4 GiB (MOE_ERR_UNSUPPORTED otherwise).
  */
 moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r, const float* b,
                               const void* W_gate, const void* W_up, const void* W_down,

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void bw_rows_kernel(
     const float* __restrict__ topk_w, const T* __restrict__ dy, const float* __restrict__ P,
     const float* __restrict__ G, const float* __restrict__ U, float* __restrict__ dw,
     float* __restrict__ dG, float* __restrict__ dU, bf16_t* __restrict__ dGU,
-    float* __restrict__ dout, float* __restrict__ wrow) {
+    bf16_t* __restrict__ wh, float* __restrict__ dout, float* __restrict__ wrow) {
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= offsets[E]) return;
@@ -94,6 +94,18 @@ __global__ __launch_bounds__(256) void bw_rows_kernel(
           static_cast<uint32_t>(f32_to_bf16(vu[2])) | (static_cast<uint32_t>(f32_to_bf16(vu[3])) << 16));
       *reinterpret_cast<uint2*>(dGU + row * 2 * M + m) = og;
       *reinterpret_cast<uint2*>(dGU + row * 2 * M + M + m) = ou;
+      if (wh != nullptr) {  // w SiLU(G) U, rounded once: an operand of dW_down
+        const float zz[4] = {z.x, z.y, z.z, z.w}, uu[4] = {u.x, u.y, u.z, u.w};
+        float hv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          hv[q] = zz[q] / (1.f + expf(-zz[q])) * uu[q];
+          hv[q] *= w;
+        }
+        *reinterpret_cast<uint2*>(wh + row * M + m) = make_uint2(
+            static_cast<uint32_t>(f32_to_bf16(hv[0])) | (static_cast<uint32_t>(f32_to_bf16(hv[1])) << 16),
+            static_cast<uint32_t>(f32_to_bf16(hv[2])) | (static_cast<uint32_t>(f32_to_bf16(hv[3])) << 16));
+      }
     }
   } else {
     for (int m = lane; m < M; m += 64) {
@@ -560,27 +572,28 @@ hipError_t kk_dispatch(int dtype_b, const void* A, int Ma, const void* B, int Nb
 hipError_t launch_bw_rows(int dtype, const int32_t* offsets, int E, int64_t R, int d, int M,
                           int k, const int32_t* perm_token, const int32_t* inv_perm,
                           const float* topk_w, const void* dy, const float* P, const float* G,
-                          const float* U, float* dw, float* dG, float* dU, void* dGU, float* dout,
-                          float* wrow, hipStream_t st) {
+                          const float* U, float* dw, float* dG, float* dU, void* dGU, void* whp,
+                          float* dout, float* wrow, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(cdiv(R, 4)));
   if (R <= 0) return hipSuccess;
   bf16_t* cat = static_cast<bf16_t*>(dGU);
+  bf16_t* wh = static_cast<bf16_t*>(whp);
   if (dtype == MOE_F32) {
     const float* y = static_cast<const float*>(dy);
     if (cat != nullptr)
       hipLaunchKernelGGL((bw_rows_kernel<float, true>), grid, dim3(256), 0, st, offsets, E, d, M, k,
-                         perm_token, inv_perm, topk_w, y, P, G, U, dw, dG, dU, cat, dout, wrow);
+                         perm_token, inv_perm, topk_w, y, P, G, U, dw, dG, dU, cat, wh, dout, wrow);
     else
       hipLaunchKernelGGL((bw_rows_kernel<float, false>), grid, dim3(256), 0, st, offsets, E, d, M,
-                         k, perm_token, inv_perm, topk_w, y, P, G, U, dw, dG, dU, cat, dout, wrow);
+                         k, perm_token, inv_perm, topk_w, y, P, G, U, dw, dG, dU, cat, wh, dout, wrow);
   } else {
     const bf16_t* y = static_cast<const bf16_t*>(dy);
     if (cat != nullptr)
       hipLaunchKernelGGL((bw_rows_kernel<bf16_t, true>), grid, dim3(256), 0, st, offsets, E, d, M,
-                         k, perm_token, inv_perm, topk_w, y, P, G, U, dw, dG, dU, cat, dout, wrow);
+                         k, perm_token, inv_perm, topk_w, y, P, G, U, dw, dG, dU, cat, wh, dout, wrow);
     else
       hipLaunchKernelGGL((bw_rows_kernel<bf16_t, false>), grid, dim3(256), 0, st, offsets, E, d, M,
-                         k, perm_token, inv_perm, topk_w, y, P, G, U, dw, dG, dU, cat, dout, wrow);
+                         k, perm_token, inv_perm, topk_w, y, P, G, U, dw, dG, dU, cat, wh, dout, wrow);
   }
   return hipGetLastError();
 }

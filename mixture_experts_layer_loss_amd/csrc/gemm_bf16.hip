@@ -889,75 +889,40 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_persistent_kernel(GemmProb
                                                  nullptr);
 }
 
-// Weight gradients: C_g [Ma][Nb] (fp32) = sum over k in [64 kt[g], 64 kt[g+1]) of A[m][k] B[n][k],
-// for the operands A [Ma][lda] and B [Nb][ldb] whose columns are the rows of the groups, each
-// group padded with zeros to a multiple of 64 (so no k-slice is partial). 256 x 256 output tiles
-// in bands of 8 m-tiles (neighbouring tiles share A and B slabs), dealt to the XCDs in runs; a group
-// without rows gets zeros.
-__global__ __launch_bounds__(NT, 1) void wgrad_gemm_kernel(const bf16_t* __restrict__ A, int lda,
-                                                           const bf16_t* __restrict__ B, int ldb,
-                                                           const int32_t* __restrict__ kt,
-                                                           int groups, int Ma, int Nb,
-                                                           float* __restrict__ C) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  const int mt = (Ma + 255) / 256, nt = (Nb + 255) / 256;
-  const int64_t per_group = static_cast<int64_t>(mt) * nt;
-  const int64_t ntiles = static_cast<int64_t>(groups) * per_group;
-  const int64_t q = (ntiles + NXCD - 1) / NXCD;
-  const int64_t L = static_cast<int64_t>(blockIdx.x % NXCD) * q + blockIdx.x / NXCD;
-  if (blockIdx.x / NXCD >= q || L >= ntiles) return;
-  const int g = static_cast<int>(L / per_group);
-  const int local = static_cast<int>(L % per_group);
-  // bands of kWgBand m-tiles, n fastest within a band's column: the 32 tiles an XCD runs at
-  // once span 8 m x 4 n and read 12 operand slabs instead of 33 (a narrower last band)
-  constexpr int kWgBand = 8;
-  const int band = local / (kWgBand * nt), w = local % (kWgBand * nt);
-  const int bw = min(kWgBand, mt - band * kWgBand);
-  const int m0 = (band * kWgBand + w % bw) * 256, n0 = (w / bw) * 256;
-  const int k0 = 64 * kt[g], K = 64 * (kt[g + 1] - kt[g]);
-  float* Cg = C + static_cast<int64_t>(g) * Ma * Nb;
-  if (K == 0) {
-    for (int c = threadIdx.x; c < 256 * 64; c += NT) {
-      const int r = m0 + c / 64, cc = n0 + (c % 64) * 4;
-      if (r < Ma && cc < Nb)
-        *reinterpret_cast<float4*>(Cg + static_cast<int64_t>(r) * Nb + cc) =
-            make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    return;
-  }
-  run_tile<2, false, false, 256>(lds, A + k0, lda, nullptr, B + k0, nullptr, 0, ldb, Nb, K,
-                                 reinterpret_cast<bf16_t*>(Cg), Nb, nullptr, nullptr, 0, m0,
-                                 min(256, Ma - m0), n0);
-}
-
-// Persistent form of the weight gradients: one block per CU walks its XCD's run of the same
-// band-ordered tile list as wgrad_gemm_kernel (runs of equal work), and the k-step pipeline runs on from one tile into
-// the next, as in run_tiles_persistent (the last two k-steps of a tile load the next tile's first
-// two k-slices). Every group spans at least two k-slices (the schedule pads an empty or one-slice
-// group with zero columns), so each tile has the two k-steps that carry the hand-over. The fp32
-// tile leaves through the free LDS stage: each wave stages 32 x 64 floats of its 128 x 64 block
-// at a time in a private 8 KB region and stores them as 16-byte row pieces, 32 stores per lane
-// per tile, so the next tile's first loads can be waited on while those stores are still in
-// flight. Operand rows are 32-bit byte offsets from the tile's first row (the launcher checks
-// 256 rows of either operand span < 2 GiB).
+// Weight gradients, with both operands read in place K-major: C_g [Ma][Nb] (fp32) = sum over the
+// rows r of group g, [offsets[g], offsets[g+1]), of A[r][m] B[r][n], for row-major A [rows][lda]
+// and B [rows][ldb] (the rows of all groups, `rows` in total). Persistent, as the forward
+// products: one block per CU walks its XCD's run of the tile list (256 x 256 output tiles of each
+// group in bands of 8 m-tiles, n fastest in a band, so that concurrent tiles share operand slabs;
+// the XCDs split the list by k-steps, as the groups' row counts differ), and the last two k-steps
+// of a tile load the next tile's first two k-slices. A k-slice is 64 rows of the tile's 256 A
+// columns and 256 B columns, staged as two [64 k][256] LDS slices (512-byte rows, 16-byte chunks
+// XOR-swizzled by 64 bytes); rows past the group's end are stored as zeros, and both MFMA operands
+// come from transposing LDS reads (ds_read_b64_tr_b16). A group spans kt[g+1] - kt[g] >= 2
+// k-slices (the schedule gives short and empty groups zero slices), so every tile has the two
+// k-steps that hand over to the next. The fp32 tile leaves through the free LDS stage: each wave
+// stages 32 x 64 floats of its 128 x 64 block at a time in a private 8 KB region and stores them
+// as 16-byte row pieces (32 stores per lane), so the next tile's loads can be waited on while those
+// stores are still in flight.
 __device__ __forceinline__ void run_wgrad_persistent(unsigned char* lds,
                                                      const bf16_t* __restrict__ A, int lda,
                                                      const bf16_t* __restrict__ B, int ldb,
+                                                     int rows, const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ kt, int groups,
                                                      int Ma, int Nb, float* __restrict__ C,
                                                      int nblocks) {
   using G = Geo<256>;
-  constexpr int MI = G::MI, NJ = G::NJ, ACH = G::ACH, BCH = G::BCH, RS = G::RSTEP;
-  static_assert(G::WCOLS == 64 && MI * 32 == G::WROWS, "fp32 epilogue passes are 32 x 64");
+  constexpr int MI = G::MI, NJ = G::NJ;
+  static_assert(NT == 512 && G::WCOLS == 64 && MI * 32 == G::WROWS, "wave layout of the tiles");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / G::WN, wn = wave % G::WN;
   const int mt = (Ma + 255) / 256, nt = (Nb + 255) / 256;
   const int64_t per_group = static_cast<int64_t>(mt) * nt;
   const int S = nblocks / NXCD;
   const int xcd = static_cast<int>(blockIdx.x) % NXCD, slot = static_cast<int>(blockIdx.x) / NXCD;
-  // the XCDs split the list by work, not by tile count: the tiles before tile L (group g, local
-  // index l) hold per_group kt[g] + l (kt[g+1] - kt[g]) k-steps, and XCD x takes the tiles that
-  // start in [x W / 8, (x + 1) W / 8) of the total W
+  // the XCDs split the list by work: the tiles before tile L (group g, local index l) hold
+  // per_group kt[g] + l (kt[g+1] - kt[g]) k-steps, and XCD x takes the tiles that start in
+  // [x W / 8, (x + 1) W / 8) of the total W
   auto first_tile = [&](int64_t work) __attribute__((always_inline)) {
     int lo = 0, hi = groups;  // largest g with per_group kt[g] <= work
     while (hi - lo > 1) {
@@ -975,9 +940,9 @@ __device__ __forceinline__ void run_wgrad_persistent(unsigned char* lds,
   if (J >= xend) return;
 
   struct Tile {
-    int g, m0, n0, k0, nk;
+    int g, m0, n0, r_lo, r_hi, nk;
   };
-  constexpr int kWgBand = 8;  // as wgrad_gemm_kernel: bands of 8 m-tiles, n fastest in a band
+  constexpr int kWgBand = 8;
   auto describe = [&](int64_t Jt) __attribute__((always_inline)) {
     Tile t;
     const int64_t L = b0 + Jt;
@@ -987,60 +952,85 @@ __device__ __forceinline__ void run_wgrad_persistent(unsigned char* lds,
     const int bw = min(kWgBand, mt - band * kWgBand);
     t.m0 = (band * kWgBand + w % bw) * 256;
     t.n0 = (w / bw) * 256;
-    t.k0 = 64 * kt[t.g];
+    t.r_lo = offsets[t.g];
+    t.r_hi = offsets[t.g + 1];
     t.nk = kt[t.g + 1] - kt[t.g];  // >= 2
     return t;
   };
 
-  const int r0 = tid >> 3, kc_t = (tid & 7) * 8;
-  const char* a_base = nullptr;
-  const char* b_base = nullptr;
-  uint32_t a_off[ACH], b_off[BCH];
+  // ---- loads: thread tid moves the 16-byte chunk (tid % 32) of rows 16 i + tid / 32 (i < 4) of
+  // both slices. Columns past Ma or Nb re-read the last 8 (they only reach outputs never stored);
+  // a row past the group reads a valid row and is stored as zeros.
+  const int krow = tid >> 5, kc = tid & 31;
+  const char* a_col = nullptr;
+  const char* b_col = nullptr;
+  int64_t r_base = 0, r_end = 0;  // first row of the loading tile's group, and its end
   auto set_ld = [&](const Tile& t) __attribute__((always_inline)) {
-    a_base = reinterpret_cast<const char*>(A + static_cast<int64_t>(t.m0) * lda + t.k0);
-    b_base = reinterpret_cast<const char*>(B + static_cast<int64_t>(t.n0) * ldb + t.k0);
-    const int ar = min(256, Ma - t.m0) - 1, br = min(256, Nb - t.n0) - 1;
-#pragma unroll
-    for (int i = 0; i < ACH; ++i)
-      a_off[i] = static_cast<uint32_t>((min(i * RS + r0, ar) * lda + kc_t) * 2);
-#pragma unroll
-    for (int i = 0; i < BCH; ++i)
-      b_off[i] = static_cast<uint32_t>((min(i * RS + r0, br) * ldb + kc_t) * 2);
+    a_col = reinterpret_cast<const char*>(A + min(t.m0 + kc * 8, Ma - 8));
+    b_col = reinterpret_cast<const char*>(B + min(t.n0 + kc * 8, Nb - 8));
+    r_base = t.r_lo + krow;
+    r_end = t.r_hi;
   };
-  u32x4 ra[ACH], rb[BCH];
+  u32x4 ra[4], rb[4];
+  uint32_t live = 0;  // bit i: row 16 i + krow of the slice belongs to the group
   auto gload = [&](int k0) __attribute__((always_inline)) {
-    const uint32_t kb = static_cast<uint32_t>(k0 * 2);
+    live = 0;
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_base + (a_off[i] + kb));
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b_base + (b_off[i] + kb));
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = r_base + k0 + 16 * i;
+      live |= (r < r_end ? 1u : 0u) << i;
+      const int64_t rr = r < rows ? r : rows - 1;
+      ra[i] = *reinterpret_cast<const u32x4*>(a_col + rr * lda * 2);
+      rb[i] = *reinterpret_cast<const u32x4*>(b_col + rr * ldb * 2);
+    }
   };
-  const uint32_t st_off = static_cast<uint32_t>(swz(r0, tid & 7) * 2);
+  // LDS: [64 k][256] slices of 512-byte rows, chunk c of row r at chunk c ^ 4 (r & 3); a thread's
+  // rows are 16 apart, so r & 3 is the same for all of them
   constexpr uint32_t kStageBytes = G::STAGE, kBBytes = 256 * BK * 2;
+  const uint32_t st_off = static_cast<uint32_t>(krow * 512 + ((kc ^ ((krow & 3) << 2)) << 4));
   auto lstore = [&](int stage) __attribute__((always_inline)) {
     unsigned char* sa = lds + stage * kStageBytes + st_off;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4*>(sa + i * RS * BK * 2) = ra[i];
-#pragma unroll
-    for (int i = 0; i < BCH; ++i)
-      *reinterpret_cast<u32x4*>(sa + kBBytes + i * RS * BK * 2) = rb[i];
+    for (int i = 0; i < 4; ++i) {
+      const bool in = (live >> i) & 1u;
+      *reinterpret_cast<u32x4*>(sa + i * 16 * 512) = in ? ra[i] : zero;
+      *reinterpret_cast<u32x4*>(sa + kBBytes + i * 16 * 512) = in ? rb[i] : zero;
+    }
   };
 
+  // ---- fragments by transposing reads: in each group of 16 lanes, lane 4 q + a reads 4 columns
+  // (c_base + 4 a ..) of row k_base + q, and lane i receives rows k_base .. k_base + 3 of column
+  // c_base + i. Lane l's 32x32x16 operand (8 k of row or column l % 32) is two such reads, rows
+  // 16 sub + 8 (l / 32) + {0..3} and {4..7}; the A operand (rows m of C) reads the A slice the same
+  // way the B operand reads the B slice.
   f32x16 acc[MI][NJ];
-  const int l32 = lane & 31, lk = lane >> 5, sw = (l32 >> 1) & 7;
-  uint32_t fo[4];
+  const int g4 = lane >> 4, i16 = lane & 15;
+  const int trow = 8 * (g4 >> 1) + (i16 >> 2);
+  auto tr_off = [&](int col) {
+    return static_cast<uint32_t>(trow * 512 + (((col >> 3) ^ ((i16 >> 2) << 2)) << 4) +
+                                 (((col >> 2) & 1) << 3));
+  };
+  uint32_t ta_off[MI], tb_off[NJ];
 #pragma unroll
-  for (int sub = 0; sub < 4; ++sub)
-    fo[sub] = static_cast<uint32_t>((l32 * BK + (((sub * 2 + lk) ^ sw) << 3)) * 2);
+  for (int i = 0; i < MI; ++i) ta_off[i] = tr_off(wm * G::WROWS + i * 32 + 16 * (g4 & 1) + 4 * (i16 & 3));
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    tb_off[j] = kBBytes + tr_off(wn * G::WCOLS + j * 32 + 16 * (g4 & 1) + 4 * (i16 & 3));
   bf16x8 fa[2][MI], fb[2][NJ];
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  auto trpair = [&](const unsigned char* p) __attribute__((always_inline)) {
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * 512));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
   auto lfrag = [&](int set, int stage, int sub) __attribute__((always_inline)) {
-    const unsigned char* sa = lds + stage * kStageBytes + fo[sub];
+    const unsigned char* sb = lds + stage * kStageBytes + sub * 16 * 512;
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
-      fa[set][i] = *reinterpret_cast<const bf16x8*>(sa + (wm * G::WROWS + i * 32) * BK * 2);
+    for (int i = 0; i < MI; ++i) fa[set][i] = trpair(sb + ta_off[i]);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      fb[set][j] = *reinterpret_cast<const bf16x8*>(sa + kBBytes + (wn * G::WCOLS + j * 32) * BK * 2);
+    for (int j = 0; j < NJ; ++j) fb[set][j] = trpair(sb + tb_off[j]);
   };
   auto mfmas = [&](int set) __attribute__((always_inline)) {
 #pragma unroll
@@ -1049,7 +1039,7 @@ __device__ __forceinline__ void run_wgrad_persistent(unsigned char* lds,
       for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
   };
-  constexpr int NMF = MI * NJ, NR = MI + NJ, NX = ACH + BCH;
+  constexpr int NMF = MI * NJ, NR = 2 * (MI + NJ), NX = 8;
   auto kstep = [&](int cur, int k0) __attribute__((always_inline)) {
     lfrag(1, cur, 1);
     mfmas(0);
@@ -1074,8 +1064,9 @@ __device__ __forceinline__ void run_wgrad_persistent(unsigned char* lds,
   auto epilogue = [&](const Tile& t, int free_stage) __attribute__((always_inline)) {
     float* Cg = C + static_cast<int64_t>(t.g) * Ma * Nb;
     unsigned char* reg = lds + free_stage * kStageBytes + wave * 8192;
-    const int rows = min(256, Ma - t.m0), cols = min(256, Nb - t.n0);
-    const bool full = rows == 256 && cols == 256;
+    const int orows = min(256, Ma - t.m0), ocols = min(256, Nb - t.n0);
+    const bool full = orows == 256 && ocols == 256;
+    const int l32 = lane & 31, lk = lane >> 5;
     int lrow = lk * 4, lcol = l32, ln = lane;
     asm volatile("" : "+v"(lrow), "+v"(lcol), "+v"(ln));
 #pragma unroll
@@ -1096,7 +1087,7 @@ __device__ __forceinline__ void run_wgrad_persistent(unsigned char* lds,
             *reinterpret_cast<const u32x4*>(reg + rr * 256 + ((c ^ (((rr >> 2) & 1) << 3)) << 4));
         const int row = wm * G::WROWS + i * 32 + rr;
         const int col = wn * G::WCOLS + c * 4;
-        if (full || (row < rows && col < cols))
+        if (full || (row < orows && col < ocols))
           __builtin_nontemporal_store(
               v, reinterpret_cast<u32x4*>(Cg + static_cast<int64_t>(t.m0 + row) * Nb + t.n0 + col));
       }
@@ -1134,18 +1125,17 @@ __device__ __forceinline__ void run_wgrad_persistent(unsigned char* lds,
     cur = nxt;
     J = Jn;
   }
+  // the last tile's final two k-steps re-read its own first slices; let them land before exit
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-__global__ __launch_bounds__(NT, 1) void wgrad_persistent_kernel(const bf16_t* __restrict__ A,
-                                                                 int lda,
-                                                                 const bf16_t* __restrict__ B,
-                                                                 int ldb,
-                                                                 const int32_t* __restrict__ kt,
-                                                                 int groups, int Ma, int Nb,
-                                                                 float* __restrict__ C) {
+__global__ __launch_bounds__(NT, 1) void wgrad_persistent_kernel(
+    const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B, int ldb, int rows,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ kt, int groups, int Ma,
+    int Nb, float* __restrict__ C) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  run_wgrad_persistent(lds, A, lda, B, ldb, kt, groups, Ma, Nb, C, static_cast<int>(gridDim.x));
+  run_wgrad_persistent(lds, A, lda, B, ldb, rows, offsets, kt, groups, Ma, Nb, C,
+                       static_cast<int>(gridDim.x));
 }
 
 // Compute units of the current device, rounded down to a multiple of the XCD count (0 if unknown).
@@ -1362,45 +1352,30 @@ hipError_t launch_gemm_kn_bf16(int groups, const void* rows, const int32_t* gath
                                      group_stride, N, K, Cp, st);
 }
 
-// C_g = A_g B_g^T over each group's zero-padded column range (weight gradients, fp32 output).
-// two_slices: the schedule kt gives every group at least two k-slices (the persistent form).
-hipError_t launch_gemm_wgrad_bf16(const void* A, int lda, const void* B, int ldb,
-                                  const int32_t* kt, int groups, int Ma, int Nb, float* C,
-                                  hipStream_t st, bool two_slices) {
+// C_g [Ma][Nb] (fp32) = sum over the rows of group g of A[r][m] B[r][n] (weight gradients): the
+// persistent K-major kernel, one block per CU
+hipError_t launch_gemm_wgrad_bf16(const void* A, int lda, const void* B, int ldb, int64_t rows,
+                                  const int32_t* offsets, const int32_t* kt, int groups, int Ma,
+                                  int Nb, float* C, hipStream_t st) {
   constexpr size_t lds = 2 * Geo<256>::STAGE;
   const int64_t pb = persistent_blocks();
-  if (two_slices && pb >= NXCD && groups > 0) {
-    static std::atomic<bool> attr_p{false};
-    if (!attr_p.load(std::memory_order_acquire)) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_persistent_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         static_cast<int>(lds));
-      if (e != hipSuccess) return e;
-      attr_p.store(true, std::memory_order_release);
-    }
-    const int64_t tiles = static_cast<int64_t>(groups) * cdiv(Ma, 256) * cdiv(Nb, 256);
-    const int64_t upper = cdiv(tiles, NXCD) * NXCD;
-    const int64_t grid = upper < pb ? upper : pb;
-    hipLaunchKernelGGL(wgrad_persistent_kernel, dim3(static_cast<unsigned>(grid)), dim3(NT), lds,
-                       st, static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B), ldb,
-                       kt, groups, Ma, Nb, C);
-    return hipGetLastError();
-  }
-  static std::atomic<bool> attr_set{false};
-  if (!attr_set.load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_gemm_kernel),
+  if (pb < NXCD || rows < 1 || rows > INT32_MAX || Ma < 8 || Nb < 8 || Ma % 8 || Nb % 8)
+    return hipErrorInvalidValue;
+  if (groups <= 0) return hipSuccess;
+  static std::atomic<bool> attr{false};
+  if (!attr.load(std::memory_order_acquire)) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_persistent_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    attr_set.store(true, std::memory_order_release);
+    attr.store(true, std::memory_order_release);
   }
   const int64_t tiles = static_cast<int64_t>(groups) * cdiv(Ma, 256) * cdiv(Nb, 256);
-  if (tiles <= 0) return hipSuccess;
-  const int64_t grid = cdiv(tiles, NXCD) * NXCD;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(wgrad_gemm_kernel, dim3(static_cast<unsigned>(grid)), dim3(NT), lds, st,
-                     static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B), ldb, kt,
-                     groups, Ma, Nb, C);
+  const int64_t upper = cdiv(tiles, NXCD) * NXCD;
+  const int64_t grid = upper < pb ? upper : pb;
+  hipLaunchKernelGGL(wgrad_persistent_kernel, dim3(static_cast<unsigned>(grid)), dim3(NT), lds, st,
+                     static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B), ldb,
+                     static_cast<int>(rows), offsets, kt, groups, Ma, Nb, C);
   return hipGetLastError();
 }
 

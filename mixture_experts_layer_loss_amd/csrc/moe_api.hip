@@ -269,21 +269,12 @@ struct LayerBackwardPlan {
   int ks_w;
   float *Gs, *Us;                 // shared experts [T, S M] fp32
   float *hs, *dhs, *dGs, *dUs, *dxs;   // [T, S M] and [T, d]
-  // bf16 layers (MFMA products): the [dG | dU] rows, and the weight-gradient
-  // operands with each group's rows as a zero-padded column range (ldp / ldps columns)
-  int64_t ldp, ldps;
-  float* wrow;                                            // gate of each kept row
-  void *dGU, *whT, *dGT, *dUT, *dyT, *xT;        // routed experts
-  void *dGUs, *hsT, *dGsT, *dUsT, *dysT, *xsT;   // shared experts
+  // bf16 layers (MFMA products): the [dG | dU] rows, and the weight gradients' other row
+  // operands: w h per kept row, and the dy and x rows of the kept rows in routed order
+  float* wrow;                   // gate of each kept row
+  void *dGU, *wh, *dyr, *xr;     // routed experts
+  void *dGUs, *hsb;              // shared experts: [dGs | dUs] rows and h rows (bf16)
 };
-// Columns of a weight-gradient operand: each of `groups` groups of `rows` rows in total padded to
-// whole 64-column k-slices, at least two per group (the persistent weight-gradient kernel hands
-// two k-slices from tile to tile), so sum_g max(2, ceil(rows_g / 64)) <= ceil(rows / 64) + 2 groups.
-int64_t wgrad_cols(int64_t rows, int groups) {
-  const int64_t t = cdiv(rows, 64);
-  return 64 * (groups == 1 ? (t > 2 ? t : 2) : t + 2 * static_cast<int64_t>(groups));
-}
-
 LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
   LayerBackwardPlan p;
   p.f = plan_layer(c, s);
@@ -304,19 +295,14 @@ LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
   p.dG = mfma ? nullptr : c.take<float>(R * M);
   p.dU = mfma ? nullptr : c.take<float>(R * M);
   p.dxr = c.take<float>(R * d);
-  p.ldp = wgrad_cols(static_cast<int64_t>(R), s->E);
-  p.ldps = wgrad_cols(s->T, 1);
-  const size_t lp = static_cast<size_t>(p.ldp), lps = static_cast<size_t>(p.ldps);
   p.wrow = mfma || expert_choice(s) ? c.take<float>(R) : nullptr;
-  p.dGU = p.whT = p.dGT = p.dUT = p.dyT = p.xT = nullptr;
-  p.dGUs = p.hsT = p.dGsT = p.dUsT = p.dysT = p.xsT = nullptr;
+  p.dGU = p.wh = p.dyr = p.xr = nullptr;
+  p.dGUs = p.hsb = nullptr;
   if (mfma) {
     p.dGU = c.take<bf16_t>(R * 2 * M);
-    p.whT = c.take<bf16_t>(M * lp);
-    p.dGT = c.take<bf16_t>(M * lp);
-    p.dUT = c.take<bf16_t>(M * lp);
-    p.dyT = c.take<bf16_t>(d * lp);
-    p.xT = c.take<bf16_t>(d * lp);
+    p.wh = c.take<bf16_t>(R * M);
+    p.dyr = c.take<bf16_t>(R * d);
+    p.xr = c.take<bf16_t>(R * d);
   }
   p.ks_w = kmajor_splits(s->E, s->d, s->T);
   p.partial = c.take<float>(p.ks_w > 1 ? static_cast<size_t>(p.ks_w) * E * d : 1);
@@ -331,11 +317,7 @@ LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
     p.dxs = c.take<float>(T * d);
     if (mfma) {
       p.dGUs = c.take<bf16_t>(T * 2 * SM);
-      p.hsT = c.take<bf16_t>(SM * lps);
-      p.dGsT = c.take<bf16_t>(SM * lps);
-      p.dUsT = c.take<bf16_t>(SM * lps);
-      p.dysT = c.take<bf16_t>(d * lps);
-      p.xsT = c.take<bf16_t>(d * lps);
+      p.hsb = c.take<bf16_t>(T * SM);
     }
   } else {
     p.Gs = p.Us = nullptr;
@@ -818,13 +800,6 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
     if (!aligned16(t)) return MOE_ERR_INVALID_ARGUMENT;
   if (s->S > 0 && (!aligned16(Ws_gate) || !aligned16(Ws_up) || !aligned16(Ws_down)))
     return MOE_ERR_INVALID_ARGUMENT;
-  // the weight-gradient GEMM reads 256-row slabs of operands padded to ldp (routed) and ldps
-  // (shared) columns with 32-bit byte offsets
-  if (s->dtype == MOE_BF16) {
-    const int64_t R = routed_rows(s);
-    const int64_t ldp = wgrad_cols(R, s->E), ldps = wgrad_cols(s->T, 1);
-    if (2 * 256 * (ldp > ldps ? ldp : ldps) >= (int64_t{1} << 31)) return MOE_ERR_UNSUPPORTED;
-  }
   if (!ws || ws_bytes < moe_workspace_size(s, MOE_CALL_LAYER_BACKWARD)) return MOE_ERR_WORKSPACE;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -895,7 +870,6 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
   // 64-row tiles; on MFMA the weight-gradient column ranges, at least two k-slices per expert
   const bool mfma = s->dtype == MOE_BF16;
   if (e == hipSuccess) e = launch_schedule(s->E, f.offsets, p.tile64, 64, hs, mfma ? 2 : 0);
-  const int64_t max_w64 = p.ldp / 64;
   const int d = s->d, M = s->M;
   // ---- combine: P_row = dy_t W_down[e] gives d w = <P, h> and dh = w P, hence dG, dU
   if (e == hipSuccess && mfma)  // W_down[e] read in place as the [d][M] B operand
@@ -909,7 +883,7 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
   if (e == hipSuccess)
     e = launch_bw_rows(s->dtype, f.offsets, s->E, R, s->d, s->M, s->k, f.perm_token,
                        ec ? nullptr : f.inv_perm, f.topk_w, dy, p.P, p.G, p.U, p.dw, p.dG, p.dU,
-                       p.dGU, p.dout, p.wrow, hs);
+                       p.dGU, p.wh, p.dout, p.wrow, hs);
   const int sig = s->scoring == MOE_SCORE_SIGMOID;
   if (e == hipSuccess && ec)
     e = launch_bw_router_ec(s->T, s->E, s->renorm, sig, f.row_of, lcol, scol, p.dw, f.n,
@@ -922,33 +896,20 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
     if (e == hipSuccess)  // dx_row = [dG dU] [W_gate[e]; W_up[e]] over K = 2M, weights in place
       e = launch_gemm_kn_bf16(s->E, p.dGU, nullptr, f.offsets, f.tile_off, max_tiles, W_gate,
                               W_up, dM, d, 2 * M, p.dxr, hs);
-    // weight-gradient operands: each expert's rows as a zero-padded column range
-    const int64_t lp = p.ldp;
+    // the weight gradients read their row operands in place, K-major: w h (written by bw_rows),
+    // [dG | dU], and the dy and x rows of the kept rows, gathered into routed order
     const bf16_t* dGU = static_cast<const bf16_t*>(p.dGU);
-    if (e == hipSuccess)  // (w h)^T with h = SiLU(G) U
-      e = launch_pad_transpose(MOE_F32, p.G, p.U, M, nullptr, p.wrow, f.offsets, p.tile64, s->E,
-                               max_w64, M, p.whT, lp, hs);
-    if (e == hipSuccess)
-      e = launch_pad_transpose(MOE_BF16, dGU, nullptr, 2 * M, nullptr, nullptr, f.offsets,
-                               p.tile64, s->E, max_w64, M, p.dGT, lp, hs);
-    if (e == hipSuccess)
-      e = launch_pad_transpose(MOE_BF16, dGU + M, nullptr, 2 * M, nullptr, nullptr, f.offsets,
-                               p.tile64, s->E, max_w64, M, p.dUT, lp, hs);
-    if (e == hipSuccess)  // dy rows of the kept slots (exact bf16)
-      e = launch_pad_transpose(MOE_BF16, dy, nullptr, d, f.perm_token, nullptr, f.offsets,
-                               p.tile64, s->E, max_w64, d, p.dyT, lp, hs);
-    if (e == hipSuccess)
-      e = launch_pad_transpose(MOE_BF16, x, nullptr, d, f.perm_token, nullptr, f.offsets,
-                               p.tile64, s->E, max_w64, d, p.xT, lp, hs);
+    if (e == hipSuccess) e = launch_gather_rows(dy, d, f.perm_token, f.offsets, s->E, R, p.dyr, hs);
+    if (e == hipSuccess) e = launch_gather_rows(x, d, f.perm_token, f.offsets, s->E, R, p.xr, hs);
     if (e == hipSuccess)  // dW_down[e] = sum over its rows of dy_t^T (w h)
-      e = launch_gemm_wgrad_bf16(p.dyT, static_cast<int>(lp), p.whT, static_cast<int>(lp),
-                                 p.tile64, s->E, d, M, dW_down, hs, true);
+      e = launch_gemm_wgrad_bf16(p.dyr, d, p.wh, M, R, f.offsets, p.tile64, s->E, d, M, dW_down,
+                                 hs);
     if (e == hipSuccess)  // dW_gate[e] = dG_e^T x_e
-      e = launch_gemm_wgrad_bf16(p.dGT, static_cast<int>(lp), p.xT, static_cast<int>(lp),
-                                 p.tile64, s->E, M, d, dW_gate, hs, true);
+      e = launch_gemm_wgrad_bf16(dGU, 2 * M, p.xr, d, R, f.offsets, p.tile64, s->E, M, d, dW_gate,
+                                 hs);
     if (e == hipSuccess)
-      e = launch_gemm_wgrad_bf16(p.dUT, static_cast<int>(lp), p.xT, static_cast<int>(lp),
-                                 p.tile64, s->E, M, d, dW_up, hs, true);
+      e = launch_gemm_wgrad_bf16(dGU + M, 2 * M, p.xr, d, R, f.offsets, p.tile64, s->E, M, d,
+                                 dW_up, hs);
   }
   if (e == hipSuccess && !mfma)  // dx_row = dG W_gate[e] + dU W_up[e]
     e = launch_nn_gemm(MOE_F32, s->dtype, true, p.dG, p.dU, nullptr, f.offsets, p.tile64, s->E,
@@ -990,41 +951,25 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
     if (e == hipSuccess) e = launch_schedule(1, f.sh_offsets, p.sh_tile64, 64, hs, mfma ? 2 : 0);
     const int64_t sh_t64 = cdiv(s->T, 64) + 1;
     if (mfma) {
-      const int64_t lps = p.ldps;
       const bf16_t* dGUs = static_cast<const bf16_t*>(p.dGUs);
       if (e == hipSuccess)  // dhs = dy Ws_down (Ws_down [d][SM] read in place)
         e = launch_gemm_kn_bf16(1, dy, nullptr, f.sh_offsets, f.sh_tile_off, sh_tiles, Ws_down,
                                 nullptr, 0, SM, d, p.dhs, hs);
-      if (e == hipSuccess) e = launch_swiglu_bw_cat(s->T, SM, p.dhs, p.Gs, p.Us, p.dGUs, hs);
+      if (e == hipSuccess)
+        e = launch_swiglu_bw_cat(s->T, SM, p.dhs, p.Gs, p.Us, p.dGUs, p.hsb, hs);
       if (e == hipSuccess)  // dxs = [dGs dUs] [Ws_gate; Ws_up] over K = 2 SM
         e = launch_gemm_kn_bf16(1, p.dGUs, nullptr, f.sh_offsets, f.sh_tile_off, sh_tiles, Ws_gate,
                                 Ws_up, 0, d, 2 * SM, p.dxs, hs);
-      const int64_t pt = p.ldps / 64;
+      // the weight gradients over all T rows, read in place: dy, h, [dGs | dUs] and x
       const int32_t* so = f.sh_offsets;
       if (e == hipSuccess)
-        e = launch_pad_transpose(MOE_BF16, dy, nullptr, d, nullptr, nullptr, so, p.sh_tile64, 1,
-                                 pt, d, p.dysT, lps, hs);
-      if (e == hipSuccess)  // h^T with h = SiLU(G) U
-        e = launch_pad_transpose(MOE_F32, p.Gs, p.Us, SM, nullptr, nullptr, so, p.sh_tile64, 1,
-                                 pt, SM, p.hsT, lps, hs);
+        e = launch_gemm_wgrad_bf16(dy, d, p.hsb, SM, s->T, so, p.sh_tile64, 1, d, SM, dWs_down, hs);
       if (e == hipSuccess)
-        e = launch_pad_transpose(MOE_BF16, dGUs, nullptr, 2 * SM, nullptr, nullptr, so,
-                                 p.sh_tile64, 1, pt, SM, p.dGsT, lps, hs);
+        e = launch_gemm_wgrad_bf16(dGUs, 2 * SM, x, d, s->T, so, p.sh_tile64, 1, SM, d, dWs_gate,
+                                   hs);
       if (e == hipSuccess)
-        e = launch_pad_transpose(MOE_BF16, dGUs + SM, nullptr, 2 * SM, nullptr, nullptr, so,
-                                 p.sh_tile64, 1, pt, SM, p.dUsT, lps, hs);
-      if (e == hipSuccess)
-        e = launch_pad_transpose(MOE_BF16, x, nullptr, d, nullptr, nullptr, so, p.sh_tile64, 1, pt,
-                                 d, p.xsT, lps, hs);
-      if (e == hipSuccess)
-        e = launch_gemm_wgrad_bf16(p.dysT, static_cast<int>(lps), p.hsT, static_cast<int>(lps),
-                                   p.sh_tile64, 1, d, SM, dWs_down, hs, true);
-      if (e == hipSuccess)
-        e = launch_gemm_wgrad_bf16(p.dGsT, static_cast<int>(lps), p.xsT, static_cast<int>(lps),
-                                   p.sh_tile64, 1, SM, d, dWs_gate, hs, true);
-      if (e == hipSuccess)
-        e = launch_gemm_wgrad_bf16(p.dUsT, static_cast<int>(lps), p.xsT, static_cast<int>(lps),
-                                   p.sh_tile64, 1, SM, d, dWs_up, hs, true);
+        e = launch_gemm_wgrad_bf16(dGUs + SM, 2 * SM, x, d, s->T, so, p.sh_tile64, 1, SM, d,
+                                   dWs_up, hs);
     } else {
       if (e == hipSuccess)
         e = launch_nn_gemm(s->dtype, s->dtype, false, dy, nullptr, nullptr, f.sh_offsets,

@@ -139,12 +139,13 @@ hipError_t launch_gemm_plain(int dtype, int groups, const void* rows, const int3
 
 // Backward (backward.hip). Per kept row, from P = dy_t W_down[e] and the fp32 pre-activations:
 // dw [T, k] (slot of the row) and the SwiGLU derivative of dh = w P, as fp32 dG, dU [R, M] or, when
-// dGU != NULL, one bf16 row [dG | dU] of 2M; when not NULL dout = w dy_t and wrow = w.
+// dGU != NULL, one bf16 row [dG | dU] of 2M; when not NULL wh [R, M] bf16 = w SiLU(G) U,
+// dout = w dy_t and wrow = w.
 hipError_t launch_bw_rows(int dtype, const int32_t* offsets, int E, int64_t R, int d, int M,
                           int k, const int32_t* perm_token, const int32_t* inv_perm,
                           const float* topk_w, const void* dy, const float* P, const float* G,
-                          const float* U, float* dw, float* dG, float* dU, void* dGU, float* dout,
-                          float* wrow, hipStream_t st);
+                          const float* U, float* dw, float* dG, float* dU, void* dGU, void* wh,
+                          float* dout, float* wrow, hipStream_t st);
 hipError_t launch_swiglu_fwd(int64_t count, const float* G, const float* U, float* h,
                              hipStream_t st);
 hipError_t launch_bw_router(int64_t T, int E, int k, int renorm, int sigmoid, const float* lcol,
@@ -177,18 +178,13 @@ hipError_t launch_bw_dx_ec(int64_t T, int d, int E, const int32_t* row_of, const
                            const float* dx_sh, float* dx, hipStream_t st);
 
 // bf16 backward on MFMA (backward_layout.hip, gemm_bf16.hip).
-// dst [cols][ldp] bf16: column p of group g (64 kt[g] <= p < 64 kt[g+1]) = source row
-// i = offsets[g] + p - 64 kt[g] (row gather[i] of src when gather != NULL), times scale[i] when
-// scale != NULL; zeros past the group's rows. With src2 != NULL (fp32 only) the source value is
-// SiLU(src) src2 (h from the pre-activations G, U).
-hipError_t launch_pad_transpose(int dtype_src, const void* src, const float* src2, int64_t ld_src,
-                                const int32_t* gather, const float* scale,
-                                const int32_t* offsets, const int32_t* kt, int groups,
-                                int64_t max_ptiles, int cols, void* dst, int64_t ldp,
-                                hipStream_t st);
-// dGU [R][2M] bf16 = [dh U SiLU'(G) | dh SiLU(G)] from fp32 [R][M] inputs
+// dst [r] (bf16 [rows][d]) = src [gather[r]] for the kept rows r < offsets[groups] (of at most R)
+hipError_t launch_gather_rows(const void* src, int d, const int32_t* gather,
+                              const int32_t* offsets, int groups, int64_t R, void* dst,
+                              hipStream_t st);
+// dGU [R][2M] bf16 = [dh U SiLU'(G) | dh SiLU(G)] and h [R][M] bf16 = SiLU(G) U from fp32 [R][M]
 hipError_t launch_swiglu_bw_cat(int64_t R, int M, const float* dh, const float* G, const float* U,
-                                void* dGU, hipStream_t st);
+                                void* dGU, void* h, hipStream_t st);
 // C[r] (fp32) = A_r B_g with B_g [K][N] (N contiguous); with B1, rows K/2.. of B_g come from B1
 hipError_t launch_gemm_kn_bf16(int groups, const void* rows, const int32_t* gather,
                                const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
@@ -206,11 +202,12 @@ hipError_t launch_gemm_gu_f32out_bf16(int groups, int d, int Mg, const void* row
                                       const int32_t* tile_off, int64_t max_tiles,
                                       const void* W_gate, const void* W_up, float* G, float* U,
                                       hipStream_t st);
-// C_g [Ma][Nb] fp32 = sum over k in [64 kt[g], 64 kt[g+1]) of A[m][k] B[n][k]; two_slices:
-// kt gives every group at least two k-slices (then the persistent kernel runs)
-hipError_t launch_gemm_wgrad_bf16(const void* A, int lda, const void* B, int ldb,
-                                  const int32_t* kt, int groups, int Ma, int Nb, float* C,
-                                  hipStream_t st, bool two_slices);
+// C_g [Ma][Nb] fp32 = sum over the rows r of group g ([offsets[g], offsets[g+1]) of `rows`) of
+// A[r][m] B[r][n], A [rows][lda] and B [rows][ldb] bf16 read in place (Ma, Nb multiples of 8); kt:
+// the groups' k-slice prefix from launch_schedule with BM 64 and min_tiles 2
+hipError_t launch_gemm_wgrad_bf16(const void* A, int lda, const void* B, int ldb, int64_t rows,
+                                  const int32_t* offsets, const int32_t* kt, int groups, int Ma,
+                                  int Nb, float* C, hipStream_t st);
 
 // Tile table of the shared experts (one group of all T rows).
 hipError_t launch_shared_table(int64_t T, int BM, int32_t* offsets, int32_t* tile_off,
