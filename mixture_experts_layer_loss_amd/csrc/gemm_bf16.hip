@@ -602,10 +602,12 @@ struct GemmProb {
   int64_t group_stride;
   bf16_t* C;
   int groups, N, K;
+  float* C2;  // EPI 3: U (C holds G as floats)
+  float* C3;
 };
 
-// Persistent form of the forward products (EPI 0: SwiGLU to bf16 h; EPI 1: plain bf16) for K of
-// 2..128 k-slices, over the 256-row tiles of one or two products (the routed experts, and the
+// Persistent form of the products with bf16 or fp32 row outputs (EPI 0: SwiGLU to bf16 h; EPI 1:
+// plain bf16; EPI 3: the fp32 gate and up pre-activations) for K of 2..128 k-slices, over the 256-row tiles of one or two products (the routed experts, and the
 // shared experts as a second product of one group). Each XCD x owns the tiles [x q_p, (x+1) q_p)
 // of each product p (the second product's first: its tiles are the longer ones when K differs);
 // slot s of its S blocks takes entries s, s + S, ... of that list, and the k-step pipeline runs on
@@ -618,9 +620,10 @@ struct GemmProb {
 template <int EPI, bool KTAIL, bool GATHER>
 __device__ __forceinline__ void run_tiles_persistent(unsigned char* lds, const GemmProb& P0,
                                                      const GemmProb& P1, int nblocks) {
-  static_assert(EPI == 0 || EPI == 1, "persistent tiles serve the forward products");
+  static_assert(EPI == 0 || EPI == 1 || EPI == 3, "persistent epilogues");
   using G = Geo<256>;
-  constexpr bool PAIRED = EPI == 0, SWIGLU = EPI == 0;
+  constexpr bool PAIRED = EPI != 1, SWIGLU = EPI == 0 || EPI == 4;
+  constexpr bool F32PAIR = EPI == 3;  // fp32 gate and up pre-activations out
   constexpr int BNO = PAIRED ? BN / 2 : BN;
   constexpr int MI = G::MI, NJ = G::NJ, ACH = G::ACH, BCH = G::BCH, RS = G::RSTEP;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -782,7 +785,7 @@ __device__ __forceinline__ void run_tiles_persistent(unsigned char* lds, const G
   // A barrier follows, before the next tile's first k-step stores into that stage. The lane's row
   // and column pass through an empty asm statement, so that its LDS offsets are formed here, tile
   // by tile, rather than hoisted out of the tile loop into registers.
-  constexpr int PC = SWIGLU ? 32 : 64;          // columns of a wave's pass
+  constexpr int PC = SWIGLU ? 32 : 64;          // columns of a wave's bf16 pass
   constexpr int PR = 4096 / PC;                 // rows of a pass (8 KB of bf16)
   constexpr int PCH = PC / 8;                   // 16-byte chunks per row
   constexpr int PI = PR / 32;                   // 32-row blocks per pass
@@ -794,8 +797,41 @@ __device__ __forceinline__ void run_tiles_persistent(unsigned char* lds, const G
     const bool full = t.rows == 256 && t.n0 + BNO <= N;
     int lrow = lk * 4, lcol = l32, ln = lane;
     asm volatile("" : "+v"(lrow), "+v"(lcol), "+v"(ln));
+    if constexpr (F32PAIR) {
+      // fp32 G (accumulators jj) then U (jj + NJ / 2), 64 rows x 32 columns per pass: row r of
+      // the region at byte (128 r) ^ 128 ((r >> 2) & 1), so that the half-waves of a store (rows
+      // 4 apart) use different banks; 8 chunks of 16 bytes per row on the way out
+      static_assert(NJ / 2 == 1 && MI % 2 == 0, "one 32-column block per wave and operand");
+      float* Cg = reinterpret_cast<float*>(P.C);
+      float* Cu = P.C2;
 #pragma unroll
-    for (int i0 = 0; i0 < MI; i0 += PI) {
+      for (int i0 = 0; i0 < MI; i0 += 2)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = ii * 32 + (r >> 2) * 8 + lrow + (r & 3);
+              *reinterpret_cast<float*>(reg + ((row * 128) ^ (((row >> 2) & 1) << 7)) + lcol * 4) =
+                  acc[i0 + ii][q * (NJ / 2)][r];
+            }
+          float* Co = q ? Cu : Cg;
+#pragma unroll
+          for (int qq = 0; qq < 8; ++qq) {
+            const int idx = qq * 64 + ln, rr = idx >> 3, c = idx & 7;
+            const u32x4 v =
+                *reinterpret_cast<const u32x4*>(reg + ((rr * 128) ^ (((rr >> 2) & 1) << 7)) + c * 16);
+            const int row = wm * G::WROWS + i0 * 32 + rr;
+            const int col = t.n0 + wn * (G::WCOLS / 2) + c * 4;
+            if (full || (row < t.rows && col < N))
+              __builtin_nontemporal_store(
+                  v, reinterpret_cast<u32x4*>(Co + static_cast<int64_t>(t.row_begin + row) * ldc + col));
+          }
+        }
+    }
+#pragma unroll
+    for (int i0 = 0; i0 < (EPI == 3 ? 0 : MI); i0 += PI) {
 #pragma unroll
       for (int i = i0; i < i0 + PI; ++i)
 #pragma unroll
@@ -872,21 +908,21 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_persistent_kernel(GemmProb
     run_tiles_persistent<EPI, KTAIL, GATHER>(lds, P0, P1, main_blocks);
     return;
   }
-  constexpr int BNO = EPI == 0 ? BN / 2 : BN;
+  constexpr int BNO = EPI != 1 ? BN / 2 : BN;
   int64_t L = static_cast<int64_t>(blockIdx.x) - main_blocks;
   const int64_t r0 = 2 * static_cast<int64_t>(P0.groups) * ((P0.N + BNO - 1) / BNO);
   if (L < r0) {
     run_remainder_tile<EPI, KTAIL, GATHER, false>(lds, L, P0.A, P0.gather, P0.offsets,
                                                   P0.tile_off, P0.groups, P0.B0, P0.B1,
-                                                  P0.group_stride, P0.N, P0.K, P0.C, nullptr,
-                                                  nullptr);
+                                                  P0.group_stride, P0.N, P0.K, P0.C, P0.C2,
+                                                  P0.C3);
     return;
   }
   if (P1.groups > 0)
     run_remainder_tile<EPI, KTAIL, false, false>(lds, L - r0, P1.A, nullptr, P1.offsets,
                                                  P1.tile_off, P1.groups, P1.B0, P1.B1,
-                                                 P1.group_stride, P1.N, P1.K, P1.C, nullptr,
-                                                 nullptr);
+                                                 P1.group_stride, P1.N, P1.K, P1.C, P1.C2,
+                                                 P1.C3);
 }
 
 // Weight gradients, with both operands read in place K-major: C_g [Ma][Nb] (fp32) = sum over the
@@ -1167,7 +1203,7 @@ bool persistent_ok(const GemmProb& P, int64_t a_rows) {
 template <int EPI, bool KTAIL, bool GATHER>
 hipError_t launch_persistent(const GemmProb& P0, int64_t max_tiles0, const GemmProb& P1,
                              int64_t max_tiles1, hipStream_t st) {
-  constexpr int BNO = EPI == 0 ? BN / 2 : BN;
+  constexpr int BNO = EPI != 1 ? BN / 2 : BN;
   constexpr size_t kMainP = 2 * Geo<256>::STAGE;
   constexpr size_t kEpiR = static_cast<size_t>(128) * (BNO + 8) * sizeof(bf16_t);
   constexpr size_t ldsp = kMainP > kEpiR ? kMainP : kEpiR;
@@ -1202,8 +1238,9 @@ hipError_t launch_gemm_t(const bf16_t* A, const int32_t* gather, const int32_t* 
                          float* C3, hipStream_t st, int64_t a_rows, float* part) {
   constexpr int BNO = (EPI == 0 || EPI == 3 || EPI == 4) ? BN / 2 : BN;
   const int64_t nb = cdiv(N, BNO);
-  if constexpr ((EPI == 0 || EPI == 1) && !BKN) {
-    GemmProb P0{A, gather, offsets, tile_off, B0, B1, group_stride, C, groups, N, K};
+  // (the training forward's EPI 4 stays one tile per block: its persistent form spills registers)
+  if constexpr ((EPI == 0 || EPI == 1 || EPI == 3) && !BKN) {
+    GemmProb P0{A, gather, offsets, tile_off, B0, B1, group_stride, C, groups, N, K, C2, C3};
     GemmProb none{};
     if (persistent_ok(P0, a_rows))
       return launch_persistent<EPI, KTAIL, GATHER>(P0, max_tiles, none, 0, st);
@@ -1281,7 +1318,7 @@ hipError_t launch_gemm_gu_f32out_bf16(int groups, int d, int Mg, const void* row
                                       const int32_t* gather, const int32_t* offsets,
                                       const int32_t* tile_off, int64_t max_tiles,
                                       const void* W_gate, const void* W_up, float* G, float* U,
-                                      hipStream_t st) {
+                                      hipStream_t st, int64_t a_rows) {
   const bf16_t* A = static_cast<const bf16_t*>(rows);
   const bf16_t* Wg = static_cast<const bf16_t*>(W_gate);
   const bf16_t* Wu = static_cast<const bf16_t*>(W_up);
@@ -1289,9 +1326,9 @@ hipError_t launch_gemm_gu_f32out_bf16(int groups, int d, int Mg, const void* row
   bf16_t* Gp = reinterpret_cast<bf16_t*>(G);  // holds floats (EPI 3)
   if (gather != nullptr)
     return launch_gemm<3, true>(A, gather, offsets, tile_off, groups, max_tiles, Wg, Wu, gs, Mg, d,
-                                Gp, st, U);
+                                Gp, st, U, nullptr, a_rows);
   return launch_gemm<3, false>(A, nullptr, offsets, tile_off, groups, max_tiles, Wg, Wu, gs, Mg, d,
-                               Gp, st, U);
+                               Gp, st, U, nullptr, a_rows);
 }
 
 // The SwiGLU GEMM of launch_gemm_up_bf16 that also stores the fp32 gate and up pre-activations
@@ -1301,7 +1338,7 @@ hipError_t launch_gemm_up_save_bf16(int groups, int d, int Mg, const void* rows,
                                     const int32_t* gather, const int32_t* offsets,
                                     const int32_t* tile_off, int64_t max_tiles, const void* W_gate,
                                     const void* W_up, void* h, float* G, float* U,
-                                    hipStream_t st) {
+                                    hipStream_t st, int64_t a_rows) {
   const bf16_t* A = static_cast<const bf16_t*>(rows);
   const bf16_t* Wg = static_cast<const bf16_t*>(W_gate);
   const bf16_t* Wu = static_cast<const bf16_t*>(W_up);
@@ -1309,9 +1346,9 @@ hipError_t launch_gemm_up_save_bf16(int groups, int d, int Mg, const void* rows,
   bf16_t* H = static_cast<bf16_t*>(h);
   if (gather != nullptr)
     return launch_gemm<4, true>(A, gather, offsets, tile_off, groups, max_tiles, Wg, Wu, gs, Mg, d,
-                                H, st, G, U);
+                                H, st, G, U, a_rows);
   return launch_gemm<4, false>(A, nullptr, offsets, tile_off, groups, max_tiles, Wg, Wu, gs, Mg, d,
-                               H, st, G, U);
+                               H, st, G, U, a_rows);
 }
 
 // C[r] = A_r B_g^T for the rows of group g (A_r = rows[gather[r]] when gather != NULL): the plain

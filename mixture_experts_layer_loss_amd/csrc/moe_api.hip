@@ -674,7 +674,7 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
   } else {
     if (e == hipSuccess && saved != nullptr)  // h, and G and U kept for the backward
       e = launch_gemm_up_save_bf16(s->E, s->d, s->M, x, p.perm_token, p.offsets, p.tile_off,
-                                   max_tiles, W_gate, W_up, p.h, sv.G, sv.U, hs);
+                                   max_tiles, W_gate, W_up, p.h, sv.G, sv.U, hs, s->T);
     else if (e == hipSuccess)
       e = launch_gemm_up(s->dtype, s->E, s->d, s->M, x, p.perm_token, p.offsets, p.tile_off,
                          max_tiles, W_gate, W_up, p.h, hs, s->T);
@@ -688,7 +688,7 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
     e = launch_shared_table(s->T, BM, p.sh_offsets, p.sh_tile_off, hs);
     if (e == hipSuccess && saved != nullptr)
       e = launch_gemm_up_save_bf16(1, s->d, SM, x, nullptr, p.sh_offsets, p.sh_tile_off, sh_tiles,
-                                   Ws_gate, Ws_up, p.h_sh, sv.Gs, sv.Us, hs);
+                                   Ws_gate, Ws_up, p.h_sh, sv.Gs, sv.Us, hs, s->T);
     else if (e == hipSuccess)
       e = launch_gemm_up(s->dtype, 1, s->d, SM, x, nullptr, p.sh_offsets, p.sh_tile_off, sh_tiles,
                          Ws_gate, Ws_up, p.h_sh, hs, s->T);
@@ -853,7 +853,7 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
   if (s->dtype == MOE_BF16) {  // G and U in one launch (gate and up tiles paired), unless kept
     if (e == hipSuccess && saved == nullptr)
       e = launch_gemm_gu_f32out_bf16(s->E, s->d, s->M, x, f.perm_token, f.offsets, f.tile_off,
-                                     max_tiles, W_gate, W_up, p.G, p.U, hs);
+                                     max_tiles, W_gate, W_up, p.G, p.U, hs, s->T);
   } else {
     if (e == hipSuccess)
       e = launch_gemm_plain(s->dtype, s->E, x, f.perm_token, f.offsets, f.tile_off, max_tiles,
@@ -937,7 +937,7 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
     if (mfma) {
       if (e == hipSuccess && saved == nullptr)
         e = launch_gemm_gu_f32out_bf16(1, s->d, SM, x, nullptr, f.sh_offsets, f.sh_tile_off,
-                                       sh_tiles, Ws_gate, Ws_up, p.Gs, p.Us, hs);
+                                       sh_tiles, Ws_gate, Ws_up, p.Gs, p.Us, hs, s->T);
     } else {
       if (e == hipSuccess)
         e = launch_gemm_plain(s->dtype, 1, x, nullptr, f.sh_offsets, f.sh_tile_off, sh_tiles,

@@ -195,13 +195,13 @@ hipError_t launch_gemm_up_save_bf16(int groups, int d, int Mg, const void* rows,
                                     const int32_t* gather, const int32_t* offsets,
                                     const int32_t* tile_off, int64_t max_tiles, const void* W_gate,
                                     const void* W_up, void* h, float* G, float* U,
-                                    hipStream_t st);
+                                    hipStream_t st, int64_t a_rows);
 // G[r] = a_r W_gate[g]^T, U[r] = a_r W_up[g]^T in fp32 (one launch, gate/up tiles paired)
 hipError_t launch_gemm_gu_f32out_bf16(int groups, int d, int Mg, const void* rows,
                                       const int32_t* gather, const int32_t* offsets,
                                       const int32_t* tile_off, int64_t max_tiles,
                                       const void* W_gate, const void* W_up, float* G, float* U,
-                                      hipStream_t st);
+                                      hipStream_t st, int64_t a_rows);
 // C_g [Ma][Nb] fp32 = sum over the rows r of group g ([offsets[g], offsets[g+1]) of `rows`) of
 // A[r][m] B[r][n], A [rows][lda] and B [rows][ldb] bf16 read in place (Ma, Nb multiples of 8); kt:
 // the groups' k-slice prefix from launch_schedule with BM 64 and min_tiles 2
