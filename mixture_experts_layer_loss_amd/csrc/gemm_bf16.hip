@@ -297,12 +297,16 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
         fb[set][j] = *reinterpret_cast<const bf16x8*>(sa + kBBytes + brow[j] * BK * 2);
     }
   };
+  // MFMA order: the B fragment runs backwards on odd row blocks, so consecutive MFMAs share an
+  // operand across the row-block boundary too (fewer operand bits switch: a power-limited clock)
   auto mfmas = [&](int set) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+      for (int jj = 0; jj < NJ; ++jj) {
+        const int j = (i & 1) ? NJ - 1 - jj : jj;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+      }
   };
   constexpr int NMF = MI * NJ, NR = MI + (BKN ? 2 * NJ : NJ), NX = ACH + BCH;
 
@@ -477,15 +481,18 @@ __device__ __forceinline__ void run_remainder_tile(
                                           K, C, N, C2, C3, g, row_begin, rows, n0);
 }
 
-// K chunk ks of `split` of remainder tile L of a plain product (the long-K down projection): the
-// tile's rows times the chunk's k-slices, as fp32 partial sums into
-// part[((ks groups + g) 128 + r) N + n] for remainder row r of group g. Every chunk is a whole
-// number of k-slices except perhaps the last (KTAIL). finish_split_kernel adds the chunks.
-template <bool KTAIL>
+// K chunk ks of `split` of remainder tile L of a plain long-K product (the forward down
+// projection, EPI 1, or a backward product with a K-major B, EPI 2): the tile's rows times the
+// chunk's k-slices, as fp32 partial sums into part[((ks groups + g) 128 + r) N + n] for remainder
+// row r of group g. Every chunk is a whole number of k-slices except perhaps the last (KTAIL);
+// with two B matrices (rows K/2.. from B1) the two chunks are the halves, K/2 a multiple of 64.
+// finish_split_kernel adds the chunks.
+template <int EPI, bool KTAIL, bool GATHER, bool BKN>
 __device__ __forceinline__ void run_remainder_split(
     unsigned char* lds, int64_t L, int ks, int split, const bf16_t* __restrict__ A,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off, int groups,
-    const bf16_t* __restrict__ B0, int64_t group_stride, int N, int K, float* __restrict__ part) {
+    const int32_t* __restrict__ gather, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ tile_off, int groups, const bf16_t* __restrict__ B0,
+    const bf16_t* __restrict__ B1, int64_t group_stride, int N, int K, float* __restrict__ part) {
   const int nb_count = (N + BN - 1) / BN;
   const int32_t* t128 = tile_off + (groups + 1);
   const int32_t* t64 = tile_off + 2 * (groups + 1);
@@ -503,15 +510,29 @@ __device__ __forceinline__ void run_remainder_split(
   const int rows = rows_g & 255;
   const int n0 = static_cast<int>(local) * BN;
   const int nk = (K + BK - 1) / BK;
-  const int k_lo = nk * ks / split * BK, k_hi = min(K, nk * (ks + 1) / split * BK);
-  const bf16_t* Ak = A + static_cast<int64_t>(row_begin) * K + k_lo;
+  int k_lo = nk * ks / split * BK, k_hi = min(K, nk * (ks + 1) / split * BK);
+  const bf16_t* Bk;
+  if constexpr (BKN) {  // B [K][N], rows k_lo.. of B0, or all of B0 / B1 for the two halves
+    if (B1 != nullptr) {
+      k_lo = ks * (K / 2);
+      k_hi = k_lo + K / 2;
+      Bk = ks == 0 ? B0 : B1;
+    } else {
+      Bk = B0 + static_cast<int64_t>(k_lo) * N;
+    }
+  } else {
+    Bk = B0 + k_lo;
+  }
+  // the tile's rows start at row 0 of the partial block: A (or the gather list) moves instead
+  const bf16_t* Ak = GATHER ? A + k_lo : A + static_cast<int64_t>(row_begin) * K + k_lo;
+  const int32_t* gk = GATHER ? gather + row_begin : nullptr;
   bf16_t* P = reinterpret_cast<bf16_t*>(part + (static_cast<int64_t>(ks) * groups + g) * 128 * N);
   if (table == t128)
-    run_tile<2, KTAIL, false, 128>(lds, Ak, K, nullptr, B0 + k_lo, nullptr, group_stride, K, N,
-                                   k_hi - k_lo, P, N, nullptr, nullptr, g, 0, rows, n0);
+    run_tile<2, KTAIL, GATHER, 128, BKN>(lds, Ak, K, gk, Bk, nullptr, group_stride, BKN ? N : K, N,
+                                         k_hi - k_lo, P, N, nullptr, nullptr, g, 0, rows, n0);
   else
-    run_tile<2, KTAIL, false, 64>(lds, Ak, K, nullptr, B0 + k_lo, nullptr, group_stride, K, N,
-                                  k_hi - k_lo, P, N, nullptr, nullptr, g, 0, rows, n0);
+    run_tile<2, KTAIL, GATHER, 64, BKN>(lds, Ak, K, gk, Bk, nullptr, group_stride, BKN ? N : K, N,
+                                        k_hi - k_lo, P, N, nullptr, nullptr, g, 0, rows, n0);
 }
 
 // tile_off: three tables of groups + 1 entries: 256-row tiles, 128-row tiles, 64-row tiles.
@@ -544,11 +565,12 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
                                       C3, g, row_begin, rows, nb * BNO);
     return;
   }
-  if constexpr (EPI == 1 && !GATHER && !BKN) {
+  if constexpr ((EPI == 1 && !GATHER && !BKN) || (EPI == 2 && BKN)) {
     if (split > 1) {  // remainder tiles in K chunks: fp32 partials, summed by finish_split_kernel
       const int64_t Lr = static_cast<int64_t>(blockIdx.x) - main_blocks;
-      run_remainder_split<KTAIL>(lds, Lr / split, static_cast<int>(Lr % split), split, A, offsets,
-                                 tile_off, groups, B0, group_stride, N, K, part);
+      run_remainder_split<EPI, KTAIL, GATHER, BKN>(lds, Lr / split, static_cast<int>(Lr % split),
+                                                   split, A, gather, offsets, tile_off, groups, B0,
+                                                   B1, group_stride, N, K, part);
       return;
     }
   }
@@ -557,9 +579,10 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
                                              group_stride, N, K, C, C2, C3);
 }
 
-// The rows of the split remainder tiles: out row = bf16(sum over the K chunks, in chunk order, of
-// the fp32 partials), for each group's 1..128 rows past its 256-row tiles. One block per (group,
-// remainder row), 8 columns per thread.
+// The rows of the split remainder tiles: out row = the sum over the K chunks, in chunk order, of
+// the fp32 partials (rounded once to bf16, or fp32 with OUT_F32), for each group's 1..128 rows
+// past its 256-row tiles. One block per (group, remainder row), 8 columns per thread.
+template <bool OUT_F32>
 __global__ __launch_bounds__(256) void finish_split_kernel(const int32_t* __restrict__ offsets,
                                                            int groups, int N, int split,
                                                            const float* __restrict__ part,
@@ -580,13 +603,19 @@ __global__ __launch_bounds__(256) void finish_split_kernel(const int32_t* __rest
     v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
     v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
   }
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
-           (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
   const int64_t row = offsets[g] + (rows_g & ~255) + r;
-  *reinterpret_cast<uint4*>(out + row * N + c) = make_uint4(w[0], w[1], w[2], w[3]);
+  if constexpr (OUT_F32) {
+    float* o = reinterpret_cast<float*>(out) + row * N + c;
+    *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(out + row * N + c) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
 }
 
 // One grouped product of the persistent kernel: groups of rows [offsets[g], offsets[g+1]) of A
@@ -751,12 +780,16 @@ __device__ __forceinline__ void run_tiles_persistent(unsigned char* lds, const G
     for (int j = 0; j < NJ; ++j)
       fb[set][j] = *reinterpret_cast<const bf16x8*>(sa + kBBytes + brow[j] * BK * 2);
   };
+  // MFMA order: the B fragment runs backwards on odd row blocks, so consecutive MFMAs share an
+  // operand across the row-block boundary too (fewer operand bits switch: a power-limited clock)
   auto mfmas = [&](int set) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+      for (int jj = 0; jj < NJ; ++jj) {
+        const int j = (i & 1) ? NJ - 1 - jj : jj;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+      }
   };
   constexpr int NMF = MI * NJ, NR = MI + NJ, NX = ACH + BCH;
   // one k-step on stage `cur`, with the same sub-step schedule as run_tile; the slice stored and
@@ -1068,12 +1101,16 @@ __device__ __forceinline__ void run_wgrad_persistent(unsigned char* lds,
 #pragma unroll
     for (int j = 0; j < NJ; ++j) fb[set][j] = trpair(sb + tb_off[j]);
   };
+  // MFMA order: the B fragment runs backwards on odd row blocks, so consecutive MFMAs share an
+  // operand across the row-block boundary too (fewer operand bits switch: a power-limited clock)
   auto mfmas = [&](int set) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+      for (int jj = 0; jj < NJ; ++jj) {
+        const int j = (i & 1) ? NJ - 1 - jj : jj;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+      }
   };
   constexpr int NMF = MI * NJ, NR = 2 * (MI + NJ), NX = 8;
   auto kstep = [&](int cur, int k0) __attribute__((always_inline)) {
@@ -1247,7 +1284,10 @@ hipError_t launch_gemm_t(const bf16_t* A, const int32_t* gather, const int32_t* 
   }
   // the remainder tiles of a plain long-K product in two K chunks, so that they spread over all
   // CUs instead of running as a short last round on a few (part: [2][groups][128][N] fp32)
-  const int split = (EPI == 1 && !GATHER && !BKN && part != nullptr) ? 2 : 1;
+  const int split = (((EPI == 1 && !GATHER && !BKN) || (EPI == 2 && BKN)) && part != nullptr &&
+                     (B1 == nullptr || !BKN || (K / 2) % BK == 0))
+                        ? 2
+                        : 1;
   // the 256-row tiles, then at most one 128-row and one 64-row tile per group
   const int64_t main_blocks = cdiv(max_tiles * nb, NXCD) * NXCD;
   const int64_t grid = main_blocks + 2 * static_cast<int64_t>(groups) * nb * split;
@@ -1271,7 +1311,7 @@ hipError_t launch_gemm_t(const bf16_t* A, const int32_t* gather, const int32_t* 
                      split);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || split == 1) return e;
-  hipLaunchKernelGGL(finish_split_kernel,
+  hipLaunchKernelGGL(finish_split_kernel<EPI == 2>,
                      dim3(static_cast<unsigned>(groups) * 128u, static_cast<unsigned>(cdiv(N / 8, 256))),
                      dim3(256), 0, st, offsets, groups, N, split, part, C);
   return hipGetLastError();
@@ -1374,7 +1414,7 @@ hipError_t launch_gemm_plain_bf16(int groups, const void* rows, const int32_t* g
 hipError_t launch_gemm_kn_bf16(int groups, const void* rows, const int32_t* gather,
                                const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
                                const void* B0, const void* B1, int64_t group_stride, int N, int K,
-                               float* C, hipStream_t st) {
+                               float* C, hipStream_t st, float* part) {
   const bf16_t* A = static_cast<const bf16_t*>(rows);
   const bf16_t* b0 = static_cast<const bf16_t*>(B0);
   const bf16_t* b1 = static_cast<const bf16_t*>(B1);
@@ -1384,9 +1424,9 @@ hipError_t launch_gemm_kn_bf16(int groups, const void* rows, const int32_t* gath
     return hipErrorInvalidValue;
   if (gather != nullptr)
     return launch_gemm<2, true, true>(A, gather, offsets, tile_off, groups, max_tiles, b0, b1,
-                                      group_stride, N, K, Cp, st);
+                                      group_stride, N, K, Cp, st, nullptr, nullptr, -1, part);
   return launch_gemm<2, false, true>(A, nullptr, offsets, tile_off, groups, max_tiles, b0, b1,
-                                     group_stride, N, K, Cp, st);
+                                     group_stride, N, K, Cp, st, nullptr, nullptr, -1, part);
 }
 
 // C_g [Ma][Nb] (fp32) = sum over the rows of group g of A[r][m] B[r][n] (weight gradients): the

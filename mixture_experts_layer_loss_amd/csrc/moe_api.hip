@@ -273,6 +273,7 @@ struct LayerBackwardPlan {
   // operands: w h per kept row, and the dy and x rows of the kept rows in routed order
   float* wrow;                   // gate of each kept row
   void *dGU, *wh, *dyr, *xr;     // routed experts
+  float* part_dx;                // [2][E][128][d]: the dx-row product's split remainder tiles
   void *dGUs, *hsb;              // shared experts: [dGs | dUs] rows and h rows (bf16)
 };
 LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
@@ -298,11 +299,16 @@ LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
   p.wrow = mfma || expert_choice(s) ? c.take<float>(R) : nullptr;
   p.dGU = p.wh = p.dyr = p.xr = nullptr;
   p.dGUs = p.hsb = nullptr;
+  p.part_dx = nullptr;
   if (mfma) {
     p.dGU = c.take<bf16_t>(R * 2 * M);
     p.wh = c.take<bf16_t>(R * M);
     p.dyr = c.take<bf16_t>(R * d);
     p.xr = c.take<bf16_t>(R * d);
+    // the dx-row product over K = 2M as for the forward down product: halves of whole k-slices,
+    // at least 512 rows per expert
+    if (2 * s->M > 128 * 64 && s->M % 64 == 0 && R >= static_cast<size_t>(512) * E)
+      p.part_dx = c.take<float>(2 * E * 128 * d);
   }
   p.ks_w = kmajor_splits(s->E, s->d, s->T);
   p.partial = c.take<float>(p.ks_w > 1 ? static_cast<size_t>(p.ks_w) * E * d : 1);
@@ -895,7 +901,7 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
   if (mfma) {
     if (e == hipSuccess)  // dx_row = [dG dU] [W_gate[e]; W_up[e]] over K = 2M, weights in place
       e = launch_gemm_kn_bf16(s->E, p.dGU, nullptr, f.offsets, f.tile_off, max_tiles, W_gate,
-                              W_up, dM, d, 2 * M, p.dxr, hs);
+                              W_up, dM, d, 2 * M, p.dxr, hs, p.part_dx);
     // the weight gradients read their row operands in place, K-major: w h (written by bw_rows),
     // [dG | dU], and the dy and x rows of the kept rows, gathered into routed order
     const bf16_t* dGU = static_cast<const bf16_t*>(p.dGU);

@@ -185,11 +185,13 @@ hipError_t launch_gather_rows(const void* src, int d, const int32_t* gather,
 // dGU [R][2M] bf16 = [dh U SiLU'(G) | dh SiLU(G)] and h [R][M] bf16 = SiLU(G) U from fp32 [R][M]
 hipError_t launch_swiglu_bw_cat(int64_t R, int M, const float* dh, const float* G, const float* U,
                                 void* dGU, void* h, hipStream_t st);
-// C[r] (fp32) = A_r B_g with B_g [K][N] (N contiguous); with B1, rows K/2.. of B_g come from B1
+// C[r] (fp32) = A_r B_g with B_g [K][N] (N contiguous); with B1, rows K/2.. of B_g come from B1.
+// part: NULL, or [2][groups][128][N] fp32 in which the remainder tiles (1..128 rows past each
+// group's 256-row tiles) run in two K chunks (with B1: the halves, K/2 a multiple of 64)
 hipError_t launch_gemm_kn_bf16(int groups, const void* rows, const int32_t* gather,
                                const int32_t* offsets, const int32_t* tile_off, int64_t max_tiles,
                                const void* B0, const void* B1, int64_t group_stride, int N, int K,
-                               float* C, hipStream_t st);
+                               float* C, hipStream_t st, float* part = nullptr);
 // h as launch_gemm_up_bf16 writes it, plus G and U as launch_gemm_gu_f32out_bf16 writes them
 hipError_t launch_gemm_up_save_bf16(int groups, int d, int Mg, const void* rows,
                                     const int32_t* gather, const int32_t* offsets,

@@ -284,6 +284,8 @@ LAYER_BW_CASES = [
     ("mixtral_8x7b", dict(T=70, d=64, M=64, E=1, k=1)),           # one expert: a dense FFN
     ("mixtral_8x7b", dict(T=50, d=64, M=64, E=4, k=4)),           # k = E
     ("mixtral_8x7b", dict(T=90, d=64, M=64, E=4, k=2, c=0.01)),   # C = 1: nearly all dropped
+    # dx rows over K = 2M = 8320 with >= 512 rows per expert: remainder tiles in two K halves
+    ("mixtral_8x7b", dict(T=1100, d=128, M=4160, E=4, k=2)),
     ("tiny_fp32", dict(T=70, E=1, k=1)),
     ("tiny_fp32", dict(T=90, E=4, k=2, c=0.01)),
     ("tiny_fp32", dict(T=120, M=96, S=2, c=1.0)),                         # fp32 shared experts
