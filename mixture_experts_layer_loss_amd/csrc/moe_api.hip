@@ -105,7 +105,7 @@ int route_flags(const moe_shape* s) {
 }
 int gemm_bm(const moe_shape* s) { return s->dtype == MOE_F32 ? kGemmF32BM : kGemmBM; }
 int64_t nblocks(const moe_shape* s) { return cdiv(s->T, kRouteTokens); }
-int64_t route_blocks(const moe_shape* s) { return cdiv(s->T, route_block_tokens(s->dtype, s->E)); }
+int64_t route_blocks(const moe_shape* s) { return cdiv(s->T, route_block_tokens(s->dtype, s->E, s->T)); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -661,7 +661,7 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
                       want_stats ? &sa : nullptr);
     // placement only: the gate/up GEMM gathers its rows from x through perm_token
     if (e == hipSuccess)
-      e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx, route_block_tokens(s->dtype, s->E),
+      e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx, route_block_tokens(s->dtype, s->E, s->T),
                          p.block_base, p.offsets, nullptr, p.perm_token, p.inv_perm, hs);
   }
   marks.mark(2, hs);
@@ -858,7 +858,7 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
                       f.tile_off, BM, hs);
     if (e == hipSuccess)
       e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx,
-                         route_block_tokens(s->dtype, s->E), f.block_base, f.offsets, nullptr,
+                         route_block_tokens(s->dtype, s->E, s->T), f.block_base, f.offsets, nullptr,
                          f.perm_token, f.inv_perm, hs);
   }
   if (s->dtype == MOE_BF16) {  // G and U in one launch (gate and up tiles paired), unless kept

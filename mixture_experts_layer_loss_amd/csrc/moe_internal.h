@@ -44,7 +44,7 @@ __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 
 
 // Tokens per router block: the router writes its partial statistics and expert histogram per
 // block of this many tokens (a divisor of kRouteTokens).
-int route_block_tokens(int dtype, int E);
+int route_block_tokens(int dtype, int E, int64_t T);
 
 // Router flags: renormalise the chosen gates; score the experts with a sigmoid (else softmax);
 // expert choice (no per-token top-k: the logits and scores leave as [E][T] columns instead).

@@ -411,27 +411,29 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
 #ifndef MOE_ROUTE_PF
 #define MOE_ROUTE_PF 2
 #endif
-// k per step: MOE_ROUTE_SK where two stages of (64 + 16 NEB) padded rows fit in 120 KB, else 64
-template <int NEB>
+// k per step: MOE_ROUTE_SK where two stages of (TB + 16 NEB) padded rows fit in 120 KB, else 64
+template <int NEB, int TB>
 constexpr int route_sk() {
-  return 2 * (64 + 16 * NEB) * (MOE_ROUTE_SK + 8) * 2 <= 120 * 1024 ? MOE_ROUTE_SK : 64;
+  return 2 * (TB + 16 * NEB) * (MOE_ROUTE_SK + 8) * 2 <= 120 * 1024 ? MOE_ROUTE_SK : 64;
 }
 
-template <int NEB, int KM>
+template <int NEB, int KM, int TB>
 __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const float* __restrict__ b,
     int64_t T, int d, int E, int k, int flags, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ hist, float* __restrict__ gpart,
     float* __restrict__ lpart, float* __restrict__ hpart, float* __restrict__ cols) {
-  constexpr int TB = 64;
-  constexpr int kSK = route_sk<NEB>();  // k per step
+  static_assert(TB == 32 || TB == 64, "token blocks of the many-expert router");
+  constexpr int kSK = route_sk<NEB, TB>();  // k per step
   constexpr int kSKP = kSK + 8;         // padded LDS row (bf16 elements)
   constexpr int ROWS = TB + 16 * NEB;                 // x rows then W_r rows of a stage
   constexpr int STAGE = ROWS * kSKP;                  // bf16 elements
   constexpr int CPR = kSK / 8;                        // 16-byte chunks per row of a stage
   constexpr int CH = ROWS * CPR;                      // 16-byte chunks per stage
   constexpr int CPT = (CH + kRouteThreads - 1) / kRouteThreads;
-  constexpr int NEBH = (NEB + 1) / 2;                 // expert blocks per wave
+  constexpr int TBLK = TB / 16;                       // 16-token blocks: 4 or 2
+  constexpr int EG = 8 / TBLK;                        // expert groups over the waves: 2 or 4
+  constexpr int NEBH = (NEB + EG - 1) / EG;           // expert blocks per wave
   constexpr int kStagesBytes = 2 * STAGE * 2;
   constexpr int kLBytes = TB * kLogitsStride * 4;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStagesBytes > kLBytes ? kStagesBytes : kLBytes];
@@ -440,7 +442,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
   __shared__ float hsq[TB];
   bf16_t* st = reinterpret_cast<bf16_t*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tb = wave & 3, eh = wave >> 2;
+  const int tb = wave % TBLK, eh = wave / TBLK;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TB;
   const int r16 = lane & 15, kg = lane >> 4;
 
@@ -544,12 +546,19 @@ hipError_t launch_bf16_lds(hipStream_t st, const void* x, const void* W, const f
                            int d, int E, int k, int flags, int32_t* topk_idx, float* topk_w,
                            int32_t* hist, float* gpart, float* lpart, float* hpart,
                            float* cols) {
-  const dim3 grid(static_cast<unsigned>(cdiv(T, 64)));
+  const int tbt = route_block_tokens(MOE_BF16, E, T);
+  const dim3 grid(static_cast<unsigned>(cdiv(T, tbt)));
   return with_km(k, [&](auto km) {
-    hipLaunchKernelGGL((route_bf16_lds_kernel<NEB, decltype(km)::value>), grid,
-                       dim3(kRouteThreads), 0, st, static_cast<const bf16_t*>(x),
-                       static_cast<const bf16_t*>(W), b, T, d, E, k, flags, topk_idx, topk_w, hist,
-                       gpart, lpart, hpart, cols);
+    if (tbt == 32)
+      hipLaunchKernelGGL((route_bf16_lds_kernel<NEB, decltype(km)::value, 32>), grid,
+                         dim3(kRouteThreads), 0, st, static_cast<const bf16_t*>(x),
+                         static_cast<const bf16_t*>(W), b, T, d, E, k, flags, topk_idx, topk_w,
+                         hist, gpart, lpart, hpart, cols);
+    else
+      hipLaunchKernelGGL((route_bf16_lds_kernel<NEB, decltype(km)::value, 64>), grid,
+                         dim3(kRouteThreads), 0, st, static_cast<const bf16_t*>(x),
+                         static_cast<const bf16_t*>(W), b, T, d, E, k, flags, topk_idx, topk_w,
+                         hist, gpart, lpart, hpart, cols);
     return hipGetLastError();
   });
 }
@@ -571,7 +580,15 @@ hipError_t launch_bf16(hipStream_t st, const void* x, const void* W, const float
 
 }  // namespace
 
-int route_block_tokens(int dtype, int E) { return dtype == MOE_F32 ? RT : (E <= 16 ? 16 : 64); }
+// Tokens per router block: fp32 64; bf16 16 for E <= 16, else 64, or 32 when 64-token blocks would
+// leave CUs idle (fewer than 512 blocks, two per CU) and W_r is small (E <= 64: every block streams
+// all of it, so halving the blocks' tokens doubles that traffic; with 160 or 256 experts that cost
+// more than the idle CUs did)
+int route_block_tokens(int dtype, int E, int64_t T) {
+  if (dtype == MOE_F32) return RT;
+  if (E <= 16) return 16;
+  return (E <= 64 && cdiv(T, 64) < 512) ? 32 : 64;
+}
 
 hipError_t launch_route(int dtype, int64_t T, int d, int E, int k, int flags, const void* x,
                         const void* W_r, const float* b, int32_t* topk_idx, float* topk_w,
