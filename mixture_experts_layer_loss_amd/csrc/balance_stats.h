@@ -9,8 +9,7 @@
 //   entropy = hsum / T, Gini = sum_ij |n_i - n_j| / (2 E sum_e n_e) (integer sums, exact),
 //   max/mean = max_e n_e E / sum_e n_e, CV^2 = Var_e(gsum) / Mean_e(gsum)^2 (population variance).
 // Computed by NTH threads of one block (E <= NTH <= 1024, a multiple of 64), every one of which must
-// call it (it has barriers): stats.hip's kernel, and the tail of the dispatch scan, which has the
-// reduced route statistics at hand; fp64 inside, sums over experts are fixed-order trees, outputs are fp32. The sign
+// call it (it has barriers); fp64 inside, sums over experts are fixed-order trees, outputs are fp32. The sign
 // compares the integers k T and n_e E, so it is exact; the bias step is a single fp32 addition of
 // +-gamma or 0.
 #pragma once
@@ -54,7 +53,9 @@ __device__ __forceinline__ void balance_stats(
     __syncthreads();
     return r;
   };
+  __shared__ int nl[NTH];  // the loads, for the pairwise Gini sum
   const long long ne = e < E ? n[e] : 0;
+  nl[e] = static_cast<int>(ne);
   double prod = 0.0;
   float bnew = 0.f;
   if (e < E) {
@@ -81,8 +82,9 @@ __device__ __forceinline__ void balance_stats(
   // Gini: sum over pairs of |n_i - n_j| (integers), over 2 E sum_e n_e
   long long pairs = 0;
   if (e < E)
+#pragma unroll 8
     for (int j = 0; j < E; ++j) {
-      const long long d = ne - static_cast<long long>(n[j]);
+      const long long d = ne - static_cast<long long>(nl[j]);
       pairs += d < 0 ? -d : d;
     }
   const long long psum = itree(pairs, false);

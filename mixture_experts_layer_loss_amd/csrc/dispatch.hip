@@ -9,7 +9,7 @@
 // its tokens that chose the expert (LDS atomicOr is order-independent), so the in-block rank is a
 // popcount of the lower bits; the cross-block part is an exclusive scan of the block histograms
 // in block order. The result is identical on every run.
-#include "balance_stats.h"
+#include "moe_internal.h"
 
 namespace moe {
 namespace {
@@ -76,8 +76,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(
     const float* __restrict__ hpart, int32_t* __restrict__ block_base,
     int32_t* __restrict__ n_out, double* __restrict__ gsum, double* __restrict__ lse2sum,
     double* __restrict__ hsum, int32_t* __restrict__ kept_out, int32_t* __restrict__ overflow,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off, int BM, bool stats_on,
-    StatsArgs sa) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off, int BM) {
   __shared__ int psum[1024];
   __shared__ double pg[1024];
   __shared__ int wtot[4][4];
@@ -198,11 +197,6 @@ __global__ __launch_bounds__(1024) void scan_kernel(
   };
   if (lse2sum != nullptr) tree(lpart, lse2sum);
   if (hsum != nullptr) tree(hpart, hsum);
-  if (stats_on) {  // the statistics from the totals just written (one launch fewer)
-    __syncthreads();
-    balance_stats<1024>(T, E, sa.fden, n_out, gsum, lse2sum, hsum, sa.lambda, sa.f, sa.P, sa.aux,
-                        sa.z, sa.diag, sa.b, sa.b_new, sa.gamma);
-  }
 }
 
 // Ranks and rows of one block of 64 tokens: inv_perm [T,k] and perm_token [rows].
@@ -449,15 +443,10 @@ hipError_t launch_scan(int64_t T, int E, int64_t C, int nblk, const int32_t* his
                        const float* gpart, const float* lpart, const float* hpart,
                        int32_t* block_base, int32_t* n_out, double* gsum, double* lse2sum,
                        double* hsum, int32_t* kept, int32_t* overflow, int32_t* offsets,
-                       int32_t* tile_off, int BM, hipStream_t st, const StatsArgs* stats) {
-  if (stats != nullptr && (n_out == nullptr || gsum == nullptr || lse2sum == nullptr ||
-                           hsum == nullptr || gpart == nullptr || lpart == nullptr ||
-                           hpart == nullptr))
-    return hipErrorInvalidValue;
-  const StatsArgs none{};
+                       int32_t* tile_off, int BM, hipStream_t st) {
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, T, E, C, nblk, hist, gpart, nblk,
                      lpart, hpart, block_base, n_out, gsum, lse2sum, hsum, kept, overflow, offsets,
-                     tile_off, BM, stats != nullptr, stats != nullptr ? *stats : none);
+                     tile_off, BM);
   return hipGetLastError();
 }
 

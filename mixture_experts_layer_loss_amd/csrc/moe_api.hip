@@ -652,13 +652,9 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
                            p.row_of, p.offsets, n, ovf, hs);
     if (e == hipSuccess) e = launch_schedule(s->E, p.offsets, p.tile_off, BM, hs);
   } else {
-    // token choice: the scan also ends with the statistics and the bias step (after the routing,
-    // which has read b, so b_new may alias it)
-    const StatsArgs sa{stats_fden(s), lambda, gamma, f, P, aux, z, diag, b_new ? b : nullptr, b_new};
     if (e == hipSuccess)
       e = launch_scan(s->T, s->E, C, nblk, p.r.hist, p.r.gpart, p.r.lpart, p.r.hpart, p.block_base,
-                      n, p.gsum, p.lse2sum, p.hsum, p.kept, ovf, p.offsets, p.tile_off, BM, hs,
-                      want_stats ? &sa : nullptr);
+                      n, p.gsum, p.lse2sum, p.hsum, p.kept, ovf, p.offsets, p.tile_off, BM, hs);
     // placement only: the gate/up GEMM gathers its rows from x through perm_token
     if (e == hipSuccess)
       e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx, route_block_tokens(s->dtype, s->E, s->T),
@@ -716,7 +712,7 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
     e = launch_combine(s->dtype, s->T, s->d, s->k, p.out_perm, p.inv_perm, w,
                        s->S > 0 ? p.sh : nullptr, y, hs);
   marks.mark(6, hs);
-  if (e == hipSuccess && want_stats && expert_choice(s))  // token choice: done by the scan
+  if (e == hipSuccess && want_stats)
     e = launch_stats(s->T, s->E, stats_fden(s), n, p.gsum, p.lse2sum, p.hsum, lambda, f, P, aux, z,
                      diag,
                      b_new ? b : nullptr, b_new, gamma, hs);

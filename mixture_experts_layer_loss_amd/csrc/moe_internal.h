@@ -68,21 +68,11 @@ hipError_t launch_count(int64_t T, int E, int k, const int32_t* topk_idx, int32_
 //   block_base [nblk, E]; gsum/lse2sum/hsum/gpart/lpart/hpart may be NULL (dispatch-only use).
 //   tile_off [3 (E+1)]: grouped-GEMM tile tables (exclusive prefixes over groups) of 256-row,
 //   128-row and 64-row tiles when BM = 256, else of BM-row tiles and two zero tables.
-// With stats, the scan ends with the balance statistics and the bias step (launch_stats's outputs,
-// from n_out, gsum, lse2sum and hsum, which must then be set).
-struct StatsArgs {
-  double fden;
-  float lambda, gamma;
-  float *f, *P, *aux, *z, *diag;
-  const float* b;
-  float* b_new;
-};
 hipError_t launch_scan(int64_t T, int E, int64_t C, int nblk, const int32_t* hist,
                        const float* gpart, const float* lpart, const float* hpart,
                        int32_t* block_base, int32_t* n_out, double* gsum, double* lse2sum,
                        double* hsum, int32_t* kept, int32_t* overflow, int32_t* offsets,
-                       int32_t* tile_off, int BM, hipStream_t st,
-                       const StatsArgs* stats = nullptr);
+                       int32_t* tile_off, int BM, hipStream_t st);
 
 // Places assignments: inv_perm, perm_token and (when x_perm != NULL) the x row copies.
 // block_base holds one row per histogram block of hist_block_tokens tokens (a divisor of

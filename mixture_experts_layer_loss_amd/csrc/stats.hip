@@ -1,5 +1,4 @@
-// The balance statistics as a kernel of their own (balance_stats.h), for the stand-alone call and
-// expert choice, and a plain fp32 copy.
+// The balance statistics as a kernel of their own (balance_stats.h), and a plain fp32 copy.
 #include "balance_stats.h"
 
 namespace moe {
