@@ -186,8 +186,14 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
                          : 0;
   const int bk_r = tid >> 5;
   const uint32_t bk_cb = static_cast<uint32_t>(min(n0 + (tid & 31) * 8, N - 8)) * 2u;
-  u32x4 ra[ACH], rb[BCH];
-  auto gload = [&](int k0) __attribute__((always_inline)) {
+  // The 64- and 128-row tiles keep two k-slices in registers (their k-steps are short, so one
+  // k-step is not enough to cover a load from HBM): slot q holds k-slices q, q + 2, ...
+  constexpr bool RING = MR < 256;
+  u32x4 rga[RING ? 2 : 1][ACH], rgb[RING ? 2 : 1][BCH];
+  auto gload_to = [&](int k0, auto slot) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
+    u32x4 (&ra)[ACH] = rga[S];
+    u32x4 (&rb)[BCH] = rgb[S];
     const u32x4 zero = {0u, 0u, 0u, 0u};
     const bool in = !KTAIL || k0 + kc_t < K;
     // a chunk past K re-reads the row's last chunk and is then zeroed
@@ -218,7 +224,10 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
   // (the swizzle term depends on (r >> 1) & 7, which is the same for all i)
   const uint32_t st_off = static_cast<uint32_t>(swz(r0, tid & 7) * 2);
   constexpr uint32_t kStageBytes = G::STAGE, kBBytes = MR * BK * 2;
-  auto lstore = [&](int stage) __attribute__((always_inline)) {
+  auto lstore_from = [&](int stage, auto slot) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
+    const u32x4 (&ra)[ACH] = rga[S];
+    const u32x4 (&rb)[BCH] = rgb[S];
     unsigned char* sa = lds + stage * kStageBytes + st_off;
 #pragma unroll
     for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4*>(sa + i * RS * BK * 2) = ra[i];
@@ -319,18 +328,20 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
   //   sub 3: read fragments of sub 0 of stage cur^1                 | MFMAs of sub 3
   // A global load has four sub-steps to land before its LDS store; no LDS read waits on a
   // barrier.
-  auto kstep = [&](int kt, auto has_next, auto has_load) __attribute__((always_inline)) {
+  // slot: the register slot holding k-slice kt + 1 (always 0 without the ring); with the ring the
+  // k-step loads k-slice kt + 3 into it once it is stored, else k-slice kt + 2
+  auto kstep = [&](int kt, auto has_next, auto has_load, auto slot, int nk) __attribute__((always_inline)) {
     constexpr bool NEXT = decltype(has_next)::value;  // a following k-step exists
-    constexpr bool LOAD = decltype(has_load)::value;  // k-step kt + 2 exists
+    constexpr bool LOAD = decltype(has_load)::value;  // the k-slice to load exists
     const int cur = kt & 1;
     lfrag(1, cur, 1);
     mfmas(0);
     if constexpr (NEXT && LOAD) {
-      lstore(cur ^ 1);
-      gload((kt + 2) * BK);
+      lstore_from(cur ^ 1, slot);
+      gload_to((RING ? min(kt + 3, nk - 1) : kt + 2) * BK, slot);
       sched_substep_wl<NMF, NR, NX, NX>();
     } else if constexpr (NEXT) {
-      lstore(cur ^ 1);
+      lstore_from(cur ^ 1, slot);
       sched_substep<NMF, NR, kSgDsWrite, NX>();
     } else {
       sched_substep<NMF, NR, 0, 0>();
@@ -354,15 +365,40 @@ __device__ __forceinline__ void run_tile(unsigned char* lds, const bf16_t* __res
   const int nk = (K + BK - 1) / BK;
   using T_ = std::true_type;
   using F_ = std::false_type;
-  gload(0);
-  lstore(0);
-  if (nk > 1) gload(BK);
-  __syncthreads();
-  lfrag(0, 0, 0);
-  int kt = 0;
-  for (; kt + 2 < nk; ++kt) kstep(kt, T_{}, T_{});
-  if (kt + 1 < nk) kstep(kt++, T_{}, F_{});
-  kstep(kt, F_{}, F_{});
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, RING ? 1 : 0>;
+  if constexpr (RING) {
+    // unconditional (clamped) loads keep the wait for slot 0 from covering slot 1's loads
+    gload_to(0, S0{});
+    gload_to(min(1, nk - 1) * BK, S1{});
+    lstore_from(0, S0{});
+    gload_to(min(2, nk - 1) * BK, S0{});
+    __syncthreads();
+    lfrag(0, 0, 0);
+    // k-step kt stores k-slice kt + 1 (slot (kt + 1) % 2) and loads k-slice kt + 3 into that slot;
+    // past the last k-slice it loads the last one again (in bounds, never stored)
+    int kt = 0;
+    for (; kt + 2 < nk; kt += 2) {
+      kstep(kt, T_{}, T_{}, S1{}, nk);
+      kstep(kt + 1, T_{}, T_{}, S0{}, nk);
+    }
+    if (kt + 1 < nk) {
+      kstep(kt, T_{}, F_{}, S1{}, nk);
+      kstep(kt + 1, F_{}, F_{}, S0{}, nk);
+    } else {
+      kstep(kt, F_{}, F_{}, S1{}, nk);
+    }
+  } else {
+    gload_to(0, S0{});
+    lstore_from(0, S0{});
+    if (nk > 1) gload_to(BK, S0{});
+    __syncthreads();
+    lfrag(0, 0, 0);
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) kstep(kt, T_{}, T_{}, S0{}, nk);
+    if (kt + 1 < nk) kstep(kt++, T_{}, F_{}, S0{}, nk);
+    kstep(kt, F_{}, F_{}, S0{}, nk);
+  }
   if constexpr (EPI == 2) {
     // fp32 output: each lane stores its accumulators (32 consecutive columns per row and wave)
     float* C32 = reinterpret_cast<float*>(C);
