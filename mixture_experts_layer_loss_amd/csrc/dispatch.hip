@@ -71,7 +71,7 @@ __device__ int block_scan_256(int v, int* buf) {
 // of the block range; parts are summed, scanned over p in log2(P) rounds and walked again to
 // write the per-block bases, so every sum is taken in a fixed order.
 __global__ __launch_bounds__(1024) void scan_kernel(
-    int64_t T, int E, int64_t C, int nblk, const int32_t* __restrict__ hist,
+    int64_t /*T*/, int E, int64_t C, int nblk, const int32_t* __restrict__ hist,
     const float* __restrict__ gpart, int nblk_g, const float* __restrict__ lpart,
     const float* __restrict__ hpart, int32_t* __restrict__ block_base,
     int32_t* __restrict__ n_out, double* __restrict__ gsum, double* __restrict__ lse2sum,
