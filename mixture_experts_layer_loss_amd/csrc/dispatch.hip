@@ -309,10 +309,7 @@ __global__ void shared_table_kernel(int64_t T, int BM, int32_t* __restrict__ off
 // picks its top tokens by its score column; "MoE：条件计算与路由" §路由机制的演进): one block per
 // expert takes the r tokens of largest logit, equal logits to the lower token index, and lays
 // them out in ascending token order at rows [e r, (e + 1) r).
-//   The r-th largest key is found by a 4-pass MSB-first radix select over order-preserving
-//   uint32 keys (8 bits a pass, LDS histograms); then the tokens are walked in chunks of 1024
-//   in index order with two block scans per chunk: the rank among keys equal to the threshold
-//   (ties: the lowest indices are taken) and the row of each taken token.
+//   Keys are the logits as order-preserving uint32 (ec_select_kernel below has the steps).
 //   lcol [E][T] logits; perm_token [E r]; row_of [E][T] (row or -1); offsets [E+1]; counts,
 //   overflow [E].
 // ------------------------------------------------------------------------------------------
@@ -322,25 +319,29 @@ __device__ __forceinline__ uint32_t order_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// exclusive prefix sum of v over the 1024 threads of the block, and the block total
-__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
+// inclusive prefix sum of v over the 64 lanes of a wave
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
+    const int y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
   }
+  return v;
+}
+
+// exclusive prefix sum of v over the 1024 threads of the block, and the block total; wave 0 scans
+// the 16 wave totals (wsum: 17 ints of LDS, free again on return)
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int x = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int w = 0; w < 16; ++w) {
-      const int c = wsum[w];
-      wsum[w] = acc;
-      acc += c;
-    }
-    wsum[16] = acc;
+  if (wave == 0) {
+    const int w = lane < 16 ? wsum[lane] : 0;
+    const int wi = wave_incl_scan(w);
+    if (lane < 16) wsum[lane] = wi - w;
+    if (lane == 15) wsum[16] = wi;
   }
   __syncthreads();
   const int r = wsum[wave] + x - v;
@@ -349,6 +350,13 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
   return r;
 }
 
+// The r-th largest key by a 4-pass MSB-first radix select (8 bits a pass): each wave counts into
+// its own LDS histogram (the keys of a column share their top bits, so one shared histogram made
+// every atomic of a pass queue on a few addresses), the 16 counts of a bin are summed by one of
+// 256 threads, and a scan over the bins from the top finds the bin holding the r-th key. Then the
+// column is walked in chunks of 1024 x 8 tokens, 8 consecutive tokens per thread, with two block
+// scans per chunk: the rank among keys equal to the threshold (ties: the lowest indices are taken)
+// and the row of each taken token.
 __global__ __launch_bounds__(1024) void ec_select_kernel(int64_t T, int E, int r,
                                                           const float* __restrict__ lcol,
                                                           int32_t* __restrict__ perm_token,
@@ -356,30 +364,39 @@ __global__ __launch_bounds__(1024) void ec_select_kernel(int64_t T, int E, int r
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ overflow) {
-  __shared__ int hist[256];
+  __shared__ int hist[16][256];
   __shared__ int wsum[17];
   __shared__ int sel[2];
-  const int e = blockIdx.x, tid = threadIdx.x;
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* col = lcol + static_cast<int64_t>(e) * T;
-  // radix select of the r-th largest key
   uint32_t prefix = 0, pmask = 0;
   int remaining = r;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
+    for (int i = tid; i < 16 * 256; i += 1024) hist[i >> 8][i & 255] = 0;
     __syncthreads();
     for (int64_t t = tid; t < T; t += 1024) {
       const uint32_t key = order_key(col[t]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+      if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int above = 0, bin = 255;
-      for (; bin > 0; --bin) {
-        if (above + hist[bin] >= remaining) break;
-        above += hist[bin];
+    // thread j < 256 holds bin 255 - j; the keys in the bins above it are its exclusive prefix
+    int c = 0, incl = 0;
+    if (tid < 256) {
+#pragma unroll
+      for (int w = 0; w < 16; ++w) c += hist[w][255 - tid];
+      incl = wave_incl_scan(c);
+      if (lane == 63) wsum[wave] = incl;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      int base = 0;
+      for (int w = 0; w < wave; ++w) base += wsum[w];
+      const int bin = 255 - tid, above = base + incl - c;
+      // the bin where the count from the top reaches `remaining` (bin 0 if none does)
+      if ((remaining <= base + incl || bin == 0) && (above < remaining || bin == 255)) {
+        sel[0] = bin;
+        sel[1] = remaining - above;
       }
-      sel[0] = bin;
-      sel[1] = remaining - above;
     }
     __syncthreads();
     prefix |= static_cast<uint32_t>(sel[0]) << shift;
@@ -388,21 +405,43 @@ __global__ __launch_bounds__(1024) void ec_select_kernel(int64_t T, int E, int r
     __syncthreads();
   }
   // prefix is the threshold key; `remaining` tokens equal to it are taken, lowest indices first
+  constexpr int KPT = 8;
   int eq_carry = 0, row_carry = 0;
-  for (int64_t base = 0; base < T; base += 1024) {
-    const int64_t t = base + tid;
-    const uint32_t key = t < T ? order_key(col[t]) : 0u;
-    const int eq = (t < T && key == prefix) ? 1 : 0;
+  for (int64_t base = 0; base < T; base += 1024 * KPT) {
+    const int64_t t0 = base + static_cast<int64_t>(tid) * KPT;
+    uint32_t key[KPT];
+    int neq = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      key[i] = t0 + i < T ? order_key(col[t0 + i]) : 0u;
+      neq += (t0 + i < T && key[i] == prefix) ? 1 : 0;
+    }
     int eq_tot = 0;
-    const int eq_rank = eq_carry + block_excl_scan(eq, wsum, eq_tot);
-    const int take = (t < T && (key > prefix || (eq && eq_rank < remaining))) ? 1 : 0;
+    int eq_rank = eq_carry + block_excl_scan(neq, wsum, eq_tot);
+    int take_mask = 0, ntake = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      if (t0 + i < T) {
+        const bool eq = key[i] == prefix;
+        if (key[i] > prefix || (eq && eq_rank < remaining)) {
+          take_mask |= 1 << i;
+          ++ntake;
+        }
+        eq_rank += eq ? 1 : 0;
+      }
+    }
     int take_tot = 0;
-    const int row = row_carry + block_excl_scan(take, wsum, take_tot);
-    if (t < T) {
-      const bool kept = take && row < r;  // exactly r are taken; the bound guards the row buffer
-      const int out = kept ? e * r + row : -1;
-      row_of[static_cast<int64_t>(e) * T + t] = out;
-      if (kept) perm_token[out] = static_cast<int32_t>(t);
+    int row = row_carry + block_excl_scan(ntake, wsum, take_tot);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      if (t0 + i < T) {
+        const bool take = (take_mask >> i) & 1;
+        const bool kept = take && row < r;  // exactly r are taken; the bound guards the row buffer
+        const int out = kept ? e * r + row : -1;
+        row_of[static_cast<int64_t>(e) * T + t0 + i] = out;
+        if (kept) perm_token[out] = static_cast<int32_t>(t0 + i);
+        row += take ? 1 : 0;
+      }
     }
     eq_carry += eq_tot;
     row_carry += take_tot;
