@@ -398,23 +398,20 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
-// bf16 with many experts (E > 16): W_r is shared through LDS. A block owns 64 tokens; its eight
-// waves are 4 token blocks of 16 x 2 expert halves and each runs the whole hidden dimension, so
-// x is streamed once per block and W_r once per block. The x and W_r k-slices (128 wide where two
+// bf16 with many experts (E > 16): W_r is shared through LDS. A block owns TB tokens (64, or 32
+// when E <= 64 and 64-token blocks would leave CUs idle); its eight waves are TB / 16 token blocks
+// of 16 times 8 / (TB / 16) expert groups, and each runs the whole hidden dimension, so x is
+// streamed once and W_r once per block. The x and W_r k-slices (128 wide where two
 // stages fit in 120 KB, else 64: longer contiguous row reads) pass through two LDS stages (rows
 // padded by 8 bf16: the 16x16x32 fragment reads are bank-conflict-free) with the next slices
 // prefetched into a register ring two deep; one barrier per k-step.
 // ------------------------------------------------------------------------------------------
-#ifndef MOE_ROUTE_SK
-#define MOE_ROUTE_SK 128
-#endif
-#ifndef MOE_ROUTE_PF
-#define MOE_ROUTE_PF 2
-#endif
-// k per step: MOE_ROUTE_SK where two stages of (TB + 16 NEB) padded rows fit in 120 KB, else 64
+// k per step: 128 where two stages of (TB + 16 NEB) padded rows fit in 120 KB, else 64; and the
+// depth of the register ring of k-slices in flight
+constexpr int kRouteSliceK = 128, kRouteRing = 2;
 template <int NEB, int TB>
 constexpr int route_sk() {
-  return 2 * (TB + 16 * NEB) * (MOE_ROUTE_SK + 8) * 2 <= 120 * 1024 ? MOE_ROUTE_SK : 64;
+  return 2 * (TB + 16 * NEB) * (kRouteSliceK + 8) * 2 <= 120 * 1024 ? kRouteSliceK : 64;
 }
 
 template <int NEB, int KM, int TB>
@@ -466,7 +463,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_lds_kernel(
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   // a ring of PF k-slices in registers ahead of the two LDS stages: a k-step's MFMA work is short
   // next to the memory latency, so several slices must be in flight
-  constexpr int PF = MOE_ROUTE_PF;
+  constexpr int PF = kRouteRing;
   u32x4 rg[PF][CPT];
   auto gload = [&](u32x4 (&r)[CPT], int k0) __attribute__((always_inline)) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
