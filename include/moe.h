@@ -353,7 +353,8 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
  * When `events` is non-NULL, later moe_layer_forward calls record events[i] (hipEvent_t handles
  * owned by the caller, count >= MOE_STAGE_COUNT) on their stream at the end of each stage:
  *   0 start, 1 route, 2 scan + placement, 3 routed gate/up GEMM (SwiGLU, rows gathered from x),
- *   4 routed down GEMM, 5 shared experts (both GEMMs), 6 combine, 7 statistics.
+ *   4 routed down GEMM, 5 shared experts (both GEMMs), 6 combine and statistics (one launch),
+ *   7 end (the interval 6..7 holds no work: the statistics are computed inside the combine launch).
  * NULL turns recording off. Process-wide setting, read and written under a lock: each forward
  * copies the handles when it starts. The caller keeps the events alive until recording is off and
  * every forward that records them has completed. A failed record makes that forward return

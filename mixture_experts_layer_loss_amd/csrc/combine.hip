@@ -5,7 +5,12 @@
 // One wave per token: lane j holds slot j's row and gate, which are read out wave-uniformly; lanes
 // walk the hidden dimension in 16-byte chunks, accumulate in fp32 in slot order j = 0..k-1, add the
 // shared term last and round once to the output type.
-#include "moe_internal.h"
+//
+// With balance statistics to compute (a layer forward), block 0 of either combine computes them
+// (balance_stats.h) while the other blocks combine: the statistics need nothing the combine
+// writes, and one block of 256 threads finishes well inside the HBM-bound combine, so they cost no
+// launch of their own.
+#include "balance_stats.h"
 
 namespace moe {
 namespace {
@@ -56,16 +61,27 @@ struct Vec<float> {
 // flight at a modest register count.
 constexpr int kU = 4, kJB = 2;
 
+// block 0 of a combine launch that carries the statistics
+__device__ __forceinline__ void stats_block(const StatsArgs& sa) {
+  balance_stats<256>(sa.T, sa.E, sa.fden, sa.n, sa.gsum, sa.lse2sum, sa.hsum, sa.lambda, sa.f,
+                     sa.P, sa.aux, sa.z, sa.diag, sa.b, sa.b_new, sa.gamma);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(int64_t Tn, int d, int k,
                                                        const T* __restrict__ out_perm,
                                                        const int32_t* __restrict__ inv_perm,
                                                        const float* __restrict__ topk_w,
                                                        const T* __restrict__ shared_out,
-                                                       T* __restrict__ y) {
+                                                       T* __restrict__ y, StatsArgs sa,
+                                                       int with_stats) {
   constexpr int VN = Vec<T>::N, STEP = 64 * VN;
+  if (with_stats && blockIdx.x == 0) {
+    stats_block(sa);
+    return;
+  }
   const int lane = threadIdx.x & 63;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t t = (static_cast<int64_t>(blockIdx.x) - with_stats) * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
   // lane j holds slot j's row and gate; a slot's values are read out wave-uniformly
   const int my_row = lane < k ? inv_perm[t * k + lane] : -1;
@@ -132,13 +148,18 @@ __global__ __launch_bounds__(256) void combine_ec_kernel(int64_t Tn, int d, int 
                                                           const int32_t* __restrict__ row_of,
                                                           const float* __restrict__ gcol,
                                                           const T* __restrict__ shared_out,
-                                                          T* __restrict__ y) {
+                                                          T* __restrict__ y, StatsArgs sa,
+                                                          int with_stats) {
   constexpr int VN = Vec<T>::N;
   __shared__ int lrow[4][MOE_E_MAX];
   __shared__ float lw[4][MOE_E_MAX];
   __shared__ float lden[4];
+  if (with_stats && blockIdx.x == 0) {
+    stats_block(sa);
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  const int64_t t = (static_cast<int64_t>(blockIdx.x) - with_stats) * 4 + wave;
   if (t >= Tn) return;  // whole waves only: no block barrier below
   int cnt = 0;
   for (int e0 = 0; e0 < E; e0 += 64) {
@@ -186,31 +207,34 @@ __global__ __launch_bounds__(256) void combine_ec_kernel(int64_t Tn, int d, int 
 
 hipError_t launch_combine_ec(int dtype, int64_t T, int d, int E, int renorm, const void* out_perm,
                              const int32_t* row_of, const float* gcol, const void* shared_out,
-                             void* y, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(cdiv(T, 4)));
+                             void* y, hipStream_t st, const StatsArgs* stats) {
+  const int ws = stats != nullptr ? 1 : 0;
+  const StatsArgs sa = stats != nullptr ? *stats : StatsArgs{};
+  const dim3 grid(static_cast<unsigned>(cdiv(T, 4) + ws));
   if (dtype == MOE_F32)
     hipLaunchKernelGGL(combine_ec_kernel<float>, grid, dim3(256), 0, st, T, d, E, renorm,
                        static_cast<const float*>(out_perm), row_of, gcol,
-                       static_cast<const float*>(shared_out), static_cast<float*>(y));
+                       static_cast<const float*>(shared_out), static_cast<float*>(y), sa, ws);
   else
     hipLaunchKernelGGL(combine_ec_kernel<bf16_t>, grid, dim3(256), 0, st, T, d, E, renorm,
                        static_cast<const bf16_t*>(out_perm), row_of, gcol,
-                       static_cast<const bf16_t*>(shared_out), static_cast<bf16_t*>(y));
+                       static_cast<const bf16_t*>(shared_out), static_cast<bf16_t*>(y), sa, ws);
   return hipGetLastError();
 }
-
 hipError_t launch_combine(int dtype, int64_t T, int d, int k, const void* out_perm,
                           const int32_t* inv_perm, const float* topk_w, const void* shared_out,
-                          void* y, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(cdiv(T, 4)));
+                          void* y, hipStream_t st, const StatsArgs* stats) {
+  const int ws = stats != nullptr ? 1 : 0;
+  const StatsArgs sa = stats != nullptr ? *stats : StatsArgs{};
+  const dim3 grid(static_cast<unsigned>(cdiv(T, 4) + ws));
   if (dtype == MOE_F32)
     hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, st, T, d, k,
                        static_cast<const float*>(out_perm), inv_perm, topk_w,
-                       static_cast<const float*>(shared_out), static_cast<float*>(y));
+                       static_cast<const float*>(shared_out), static_cast<float*>(y), sa, ws);
   else
     hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(256), 0, st, T, d, k,
                        static_cast<const bf16_t*>(out_perm), inv_perm, topk_w,
-                       static_cast<const bf16_t*>(shared_out), static_cast<bf16_t*>(y));
+                       static_cast<const bf16_t*>(shared_out), static_cast<bf16_t*>(y), sa, ws);
   return hipGetLastError();
 }
 

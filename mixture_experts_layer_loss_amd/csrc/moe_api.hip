@@ -704,19 +704,20 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
                            p.h_sh, p.sh, hs, s->T);
   }
   marks.mark(5, hs);
+  // the combine launch computes the balance statistics in one extra block (the router has read
+  // b by now, so b_new may alias it)
+  const StatsArgs sa{s->T, s->E, stats_fden(s), n, p.gsum, p.lse2sum, p.hsum, lambda, f, P, aux,
+                     z, diag, b_new ? b : nullptr, b_new, gamma};
+  const StatsArgs* stats = want_stats ? &sa : nullptr;
   if (e == hipSuccess && expert_choice(s))
     e = launch_combine_ec(s->dtype, s->T, s->d, s->E, s->renorm, p.out_perm, p.row_of,
                           p.cols + static_cast<size_t>(s->E) * s->T, s->S > 0 ? p.sh : nullptr, y,
-                          hs);
+                          hs, stats);
   else if (e == hipSuccess)
     e = launch_combine(s->dtype, s->T, s->d, s->k, p.out_perm, p.inv_perm, w,
-                       s->S > 0 ? p.sh : nullptr, y, hs);
+                       s->S > 0 ? p.sh : nullptr, y, hs, stats);
   marks.mark(6, hs);
-  if (e == hipSuccess && want_stats)
-    e = launch_stats(s->T, s->E, stats_fden(s), n, p.gsum, p.lse2sum, p.hsum, lambda, f, P, aux, z,
-                     diag,
-                     b_new ? b : nullptr, b_new, gamma, hs);
-  marks.mark(7, hs);
+  marks.mark(7, hs);  // (the statistics stage: inside the combine launch)
   if (e == hipSuccess) e = marks.err;
   return hip_status(e);
 }

@@ -89,11 +89,33 @@ hipError_t launch_ec_select(int64_t T, int E, int r, const float* lcol, int32_t*
                             int32_t* row_of, int32_t* offsets, int32_t* counts,
                             int32_t* overflow, hipStream_t st);
 
+// The inputs and outputs of the balance statistics (launch_stats below), for a combine launch to
+// compute them in one extra block beside its own blocks.
+struct StatsArgs {
+  int64_t T;
+  int E;
+  double fden;
+  const int32_t* n;
+  const double* gsum;
+  const double* lse2sum;
+  const double* hsum;
+  float lambda;
+  float* f;
+  float* P;
+  float* aux;
+  float* z;
+  float* diag;
+  const float* b;
+  float* b_new;
+  float gamma;
+};
+
 // Expert-choice combine: y_t = sum over experts e (ascending) with row_of[e][t] >= 0 of
 // w_te out_perm[row] + shared_t, w_te = gcol[e][t] (renormalised over those experts if renorm).
+// stats: NULL, or the balance statistics to compute in the same launch.
 hipError_t launch_combine_ec(int dtype, int64_t T, int d, int E, int renorm, const void* out_perm,
                              const int32_t* row_of, const float* gcol, const void* shared_out,
-                             void* y, hipStream_t st);
+                             void* y, hipStream_t st, const StatsArgs* stats = nullptr);
 
 // Tile tables [3 (groups+1)] of a grouped GEMM from device row offsets (stand-alone expert FFN).
 // min_tiles > 0 (BM != 256 only): every group, empty ones included, gets at least that many tiles
@@ -215,10 +237,10 @@ hipError_t launch_gemm_wgrad_bf16(const void* A, int lda, const void* B, int ldb
 hipError_t launch_shared_table(int64_t T, int BM, int32_t* offsets, int32_t* tile_off,
                                hipStream_t st);
 
-// y_t = sum_j w_tj out_perm[inv_tj] (+ shared_t).
+// y_t = sum_j w_tj out_perm[inv_tj] (+ shared_t). stats: as for launch_combine_ec.
 hipError_t launch_combine(int dtype, int64_t T, int d, int k, const void* out_perm,
                           const int32_t* inv_perm, const float* topk_w, const void* shared_out,
-                          void* y, hipStream_t st);
+                          void* y, hipStream_t st, const StatsArgs* stats = nullptr);
 
 // dst[0, n) = src[0, n), or zeros when src is NULL.
 hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t st);
