@@ -182,24 +182,58 @@ __global__ __launch_bounds__(256) void combine_ec_kernel(int64_t Tn, int d, int 
   }
   __builtin_amdgcn_wave_barrier();
   const float den = lden[wave];
-  for (int c = lane * VN; c < d; c += 64 * VN) {
-    float acc[VN];
+  // as in combine_kernel: kJB experts and kU chunks per lane loaded before any is used
+  constexpr int STEP = 64 * VN;
+  for (int c0 = lane * VN; c0 < d; c0 += STEP * kU) {
+    float acc[kU][VN];
 #pragma unroll
-    for (int i = 0; i < VN; ++i) acc[i] = 0.f;
-    for (int j = 0; j < cnt; ++j) {
-      const float w = lw[wave][j] / den;
-      float v[VN];
-      Vec<T>::load(out_perm + static_cast<int64_t>(lrow[wave][j]) * d + c, v);
+    for (int u = 0; u < kU; ++u)
 #pragma unroll
-      for (int i = 0; i < VN; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+      for (int i = 0; i < VN; ++i) acc[u][i] = 0.f;
+    for (int j0 = 0; j0 < cnt; j0 += kJB) {
+      uint4 raw[kJB][kU];
+      float wj[kJB];
+#pragma unroll
+      for (int jj = 0; jj < kJB; ++jj) {
+        const int j = j0 + jj;
+        const int row = j < cnt ? lrow[wave][j] : -1;
+        wj[jj] = row >= 0 ? lw[wave][j] / den : 0.f;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int c = c0 + u * STEP;
+          raw[jj][u] = (row >= 0 && c < d)
+                           ? *reinterpret_cast<const uint4*>(out_perm +
+                                                             static_cast<int64_t>(row) * d + c)
+                           : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+      // experts in ascending order; past the token's last one nothing is added
+#pragma unroll
+      for (int jj = 0; jj < kJB; ++jj) {
+        if (j0 + jj < cnt) {
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            float v[VN];
+            Vec<T>::unpack(raw[jj][u], v);
+#pragma unroll
+            for (int i = 0; i < VN; ++i) acc[u][i] = fmaf(wj[jj], v[i], acc[u][i]);
+          }
+        }
+      }
     }
-    if (shared_out != nullptr) {
-      float v[VN];
-      Vec<T>::load(shared_out + t * d + c, v);
 #pragma unroll
-      for (int i = 0; i < VN; ++i) acc[i] += v[i];
+    for (int u = 0; u < kU; ++u) {
+      const int c = c0 + u * STEP;
+      if (c < d) {
+        if (shared_out != nullptr) {
+          float v[VN];
+          Vec<T>::load(shared_out + t * d + c, v);
+#pragma unroll
+          for (int i = 0; i < VN; ++i) acc[u][i] += v[i];
+        }
+        Vec<T>::store(y + t * d + c, acc[u]);
+      }
     }
-    Vec<T>::store(y + t * d + c, acc);
   }
 }
 

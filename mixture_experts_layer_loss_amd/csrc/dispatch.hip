@@ -311,7 +311,7 @@ __global__ void shared_table_kernel(int64_t T, int BM, int32_t* __restrict__ off
 // them out in ascending token order at rows [e r, (e + 1) r).
 //   Keys are the logits as order-preserving uint32 (ec_select_kernel below has the steps).
 //   lcol [E][T] logits; perm_token [E r]; row_of [E][T] (row or -1); offsets [E+1]; counts,
-//   overflow [E].
+//   overflow [E]; tile_off [3 (E+1)]: the grouped GEMMs' tile tables for BM-row tiles.
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t order_key(float v) {
   if (v == 0.f) v = 0.f;  // -0 and +0 compare equal: one key
@@ -363,7 +363,8 @@ __global__ __launch_bounds__(1024) void ec_select_kernel(int64_t T, int E, int r
                                                           int32_t* __restrict__ row_of,
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ overflow) {
+                                                          int32_t* __restrict__ overflow,
+                                                          int32_t* __restrict__ tile_off, int BM) {
   __shared__ int hist[16][256];
   __shared__ int wsum[17];
   __shared__ int sel[2];
@@ -451,6 +452,18 @@ __global__ __launch_bounds__(1024) void ec_select_kernel(int64_t T, int E, int r
     if (e == E - 1) offsets[E] = E * r;
     counts[e] = r;
     overflow[e] = 0;
+    // the grouped GEMMs' tile tables: every expert has r rows, so its tiles of each class are
+    // e times one expert's
+    int c0 = 0, c1 = 0, c2 = 0;
+    if (r > 0) tile_counts(r, BM, c0, c1, c2);
+    tile_off[e] = e * c0;
+    tile_off[E + 1 + e] = e * c1;
+    tile_off[2 * (E + 1) + e] = e * c2;
+    if (e == E - 1) {
+      tile_off[E] = E * c0;
+      tile_off[2 * E + 1] = E * c1;
+      tile_off[3 * E + 2] = E * c2;
+    }
   }
 }
 
@@ -458,9 +471,9 @@ __global__ __launch_bounds__(1024) void ec_select_kernel(int64_t T, int E, int r
 
 hipError_t launch_ec_select(int64_t T, int E, int r, const float* lcol, int32_t* perm_token,
                             int32_t* row_of, int32_t* offsets, int32_t* counts,
-                            int32_t* overflow, hipStream_t st) {
+                            int32_t* overflow, int32_t* tile_off, int BM, hipStream_t st) {
   hipLaunchKernelGGL(ec_select_kernel, dim3(E), dim3(1024), 0, st, T, E, r, lcol, perm_token,
-                     row_of, offsets, counts, overflow);
+                     row_of, offsets, counts, overflow, tile_off, BM);
   return hipGetLastError();
 }
 

@@ -649,8 +649,7 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
                       hs);
     if (e == hipSuccess)
       e = launch_ec_select(s->T, s->E, static_cast<int>(ec_tokens(s)), p.cols, p.perm_token,
-                           p.row_of, p.offsets, n, ovf, hs);
-    if (e == hipSuccess) e = launch_schedule(s->E, p.offsets, p.tile_off, BM, hs);
+                           p.row_of, p.offsets, n, ovf, p.tile_off, BM, hs);
   } else {
     if (e == hipSuccess)
       e = launch_scan(s->T, s->E, C, nblk, p.r.hist, p.r.gpart, p.r.lpart, p.r.hpart, p.block_base,
@@ -844,8 +843,7 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
                      nullptr, f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart, p.cols, hs);
     if (e == hipSuccess)
       e = launch_ec_select(s->T, s->E, static_cast<int>(ec_tokens(s)), lcol, f.perm_token,
-                           f.row_of, f.offsets, f.n, f.overflow, hs);
-    if (e == hipSuccess) e = launch_schedule(s->E, f.offsets, f.tile_off, BM, hs);
+                           f.row_of, f.offsets, f.n, f.overflow, f.tile_off, BM, hs);
   } else {
     e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s), x, W_r, b_sel, idx,
                      f.topk_w, f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart, nullptr, hs);

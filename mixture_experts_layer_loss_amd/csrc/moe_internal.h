@@ -84,10 +84,11 @@ hipError_t launch_scatter(int64_t T, int d, int E, int k, int64_t C, int elem_by
 
 // Expert-choice selection: expert e takes the r tokens of largest lcol[e][t] (ties: lower t) at
 // rows e r .. e r + r - 1 in ascending token order; row_of [E][T] = row or -1; offsets [E+1] = e r;
-// counts = r, overflow = 0.
+// counts = r, overflow = 0; tile_off: the grouped GEMMs' tile tables for BM-row tiles (as
+// launch_schedule writes them for these offsets).
 hipError_t launch_ec_select(int64_t T, int E, int r, const float* lcol, int32_t* perm_token,
                             int32_t* row_of, int32_t* offsets, int32_t* counts,
-                            int32_t* overflow, hipStream_t st);
+                            int32_t* overflow, int32_t* tile_off, int BM, hipStream_t st);
 
 // The inputs and outputs of the balance statistics (launch_stats below), for a combine launch to
 // compute them in one extra block beside its own blocks.
