@@ -616,6 +616,8 @@ LAYER_CASES = [
     ("expert_choice", dict(T=333, d=200, M=136, E=5, k=2, S=0, c=0.5)),
     ("expert_choice", dict(T=300, d=128, M=64, E=8, S=1, scoring="sigmoid")),
     ("expert_choice", dict(T=200, d=64, M=64, E=256, k=8, S=0)),
+    # expert choice over more than one 8192-token chunk of the selection walk
+    ("expert_choice", dict(T=9000, d=64, M=64, E=8, k=2, S=0)),
 ]
 
 
