@@ -1,4 +1,5 @@
-// The balance statistics as a kernel of their own (balance_stats.h), and a plain fp32 copy.
+// The balance statistics as a kernel of their own (balance_stats.h) for moe_balance_stats (the
+// layer forward computes them in an extra block of its combine launch), and a plain fp32 copy.
 #include "balance_stats.h"
 
 namespace moe {
