@@ -357,6 +357,58 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
 // column is walked in chunks of 1024 x 8 tokens, 8 consecutive tokens per thread, with two block
 // scans per chunk: the rank among keys equal to the threshold (ties: the lowest indices are taken)
 // and the row of each taken token.
+// The scan kernel's reductions of the router's per-block statistics partials, by a block of 1024
+// threads (every thread calls it), in the same order: thread (p, e) sums g of expert e over part p
+// of the blocks, the parts are added in a pairwise tree, and lse^2 and entropy are strided sums
+// over the threads, a butterfly in each wave and the 16 wave sums in order. pg: 1024 doubles of
+// LDS, wred: 16.
+__device__ void reduce_route_partials(int E, int nblk_g, const float* __restrict__ gpart,
+                                      const float* __restrict__ lpart,
+                                      const float* __restrict__ hpart, double* __restrict__ gsum,
+                                      double* __restrict__ lse2sum, double* __restrict__ hsum,
+                                      double* pg, double* wred) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int EP = 1;
+  while (EP < E) EP <<= 1;
+  const int P = 1024 / EP;
+  const int e = tid % EP, p = tid / EP;
+  double gs = 0.0;
+  if (e < E) {
+    const int g0 = static_cast<int>(static_cast<int64_t>(p) * nblk_g / P);
+    const int g1 = static_cast<int>(static_cast<int64_t>(p + 1) * nblk_g / P);
+#pragma unroll 16
+    for (int b = g0; b < g1; ++b) gs += static_cast<double>(gpart[static_cast<int64_t>(b) * E + e]);
+  }
+  pg[tid] = gs;
+  __syncthreads();
+  for (int off = 1; off < P; off <<= 1) {
+    const int half = P / (2 * off);
+    const double gadd = p < half ? pg[tid + half * EP] : 0.0;
+    __syncthreads();
+    if (p < half) pg[tid] += gadd;
+    __syncthreads();
+  }
+  if (p == 0 && e < E) gsum[e] = pg[tid];
+  auto tree = [&](const float* part, double* out) {
+    double ls = 0.0;
+    for (int b = tid; b < nblk_g; b += 1024) ls += static_cast<double>(part[b]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ls += __shfl_xor(ls, off, 64);
+    if (lane == 0) wred[wave] = ls;
+    __syncthreads();
+    if (tid == 0) {
+      double t = 0.0;
+      for (int w = 0; w < 16; ++w) t += wred[w];
+      *out = t;
+    }
+    __syncthreads();
+  };
+  tree(lpart, lse2sum);
+  if (hsum != nullptr) tree(hpart, hsum);
+}
+
+// Blocks 0..E-1 select; with the router's statistics partials given (gpart non-null), block E
+// reduces them meanwhile (reduce_route_partials), on a CU the E selecting blocks leave free.
 __global__ __launch_bounds__(1024) void ec_select_kernel(int64_t T, int E, int r,
                                                           const float* __restrict__ lcol,
                                                           int32_t* __restrict__ perm_token,
@@ -364,10 +416,17 @@ __global__ __launch_bounds__(1024) void ec_select_kernel(int64_t T, int E, int r
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ overflow,
-                                                          int32_t* __restrict__ tile_off, int BM) {
-  __shared__ int hist[16][256];
+                                                          int32_t* __restrict__ tile_off, int BM,
+                                                          RoutePartials rp) {
+  __shared__ __attribute__((aligned(16))) int hist[16][256];
   __shared__ int wsum[17];
   __shared__ int sel[2];
+  __shared__ double wred[16];
+  if (static_cast<int>(blockIdx.x) == E) {  // (hist is free in this block: pg in its 16 KB)
+    reduce_route_partials(E, rp.nblk, rp.gpart, rp.lpart, rp.hpart, rp.gsum, rp.lse2sum, rp.hsum,
+                          reinterpret_cast<double*>(&hist[0][0]), wred);
+    return;
+  }
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* col = lcol + static_cast<int64_t>(e) * T;
   uint32_t prefix = 0, pmask = 0;
@@ -471,9 +530,13 @@ __global__ __launch_bounds__(1024) void ec_select_kernel(int64_t T, int E, int r
 
 hipError_t launch_ec_select(int64_t T, int E, int r, const float* lcol, int32_t* perm_token,
                             int32_t* row_of, int32_t* offsets, int32_t* counts,
-                            int32_t* overflow, int32_t* tile_off, int BM, hipStream_t st) {
-  hipLaunchKernelGGL(ec_select_kernel, dim3(E), dim3(1024), 0, st, T, E, r, lcol, perm_token,
-                     row_of, offsets, counts, overflow, tile_off, BM);
+                            int32_t* overflow, int32_t* tile_off, int BM, hipStream_t st,
+                            const RoutePartials* rp) {
+  const RoutePartials none{};
+  const bool red = rp != nullptr && rp->gpart != nullptr;
+  hipLaunchKernelGGL(ec_select_kernel, dim3(E + (red ? 1 : 0)), dim3(1024), 0, st, T, E, r, lcol,
+                     perm_token, row_of, offsets, counts, overflow, tile_off, BM,
+                     red ? *rp : none);
   return hipGetLastError();
 }
 

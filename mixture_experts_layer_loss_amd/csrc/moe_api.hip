@@ -642,14 +642,12 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
                      p.r.hist, p.r.gpart, p.r.lpart, p.r.hpart, p.cols, hs);
   marks.mark(1, hs);
   if (expert_choice(s)) {
-    // the statistics partials, then every expert's top-r tokens and their tile tables
-    if (e == hipSuccess)
-      e = launch_scan(s->T, s->E, -1, nblk, p.r.hist, p.r.gpart, p.r.lpart, p.r.hpart, nullptr,
-                      nullptr, p.gsum, p.lse2sum, p.hsum, nullptr, nullptr, nullptr, nullptr, BM,
-                      hs);
+    // every expert's top-r tokens and their tile tables; one more block of the same launch
+    // reduces the statistics partials meanwhile
+    const RoutePartials rp{p.r.gpart, p.r.lpart, p.r.hpart, nblk, p.gsum, p.lse2sum, p.hsum};
     if (e == hipSuccess)
       e = launch_ec_select(s->T, s->E, static_cast<int>(ec_tokens(s)), p.cols, p.perm_token,
-                           p.row_of, p.offsets, n, ovf, p.tile_off, BM, hs);
+                           p.row_of, p.offsets, n, ovf, p.tile_off, BM, hs, &rp);
   } else {
     if (e == hipSuccess)
       e = launch_scan(s->T, s->E, C, nblk, p.r.hist, p.r.gpart, p.r.lpart, p.r.hpart, p.block_base,
@@ -848,9 +846,8 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
     e = launch_route(s->dtype, s->T, s->d, s->E, s->k, route_flags(s), x, W_r, b_sel, idx,
                      f.topk_w, f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart, nullptr, hs);
     if (e == hipSuccess)
-      e = launch_scan(s->T, s->E, C, nblk, f.r.hist, f.r.gpart, f.r.lpart, f.r.hpart,
-                      f.block_base, f.n, f.gsum, f.lse2sum, f.hsum, f.kept, f.overflow, f.offsets,
-                      f.tile_off, BM, hs);
+      e = launch_scan(s->T, s->E, C, nblk, f.r.hist, nullptr, nullptr, nullptr, f.block_base, f.n,
+                      nullptr, nullptr, nullptr, f.kept, f.overflow, f.offsets, f.tile_off, BM, hs);
     if (e == hipSuccess)
       e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx,
                          route_block_tokens(s->dtype, s->E, s->T), f.block_base, f.offsets, nullptr,

@@ -86,9 +86,22 @@ hipError_t launch_scatter(int64_t T, int d, int E, int k, int64_t C, int elem_by
 // rows e r .. e r + r - 1 in ascending token order; row_of [E][T] = row or -1; offsets [E+1] = e r;
 // counts = r, overflow = 0; tile_off: the grouped GEMMs' tile tables for BM-row tiles (as
 // launch_schedule writes them for these offsets).
+// The router's per-block statistics partials (gpart [nblk][E], lpart and hpart [nblk]) and where
+// their reductions go (as the scan kernel computes them; hpart / hsum may be NULL).
+struct RoutePartials {
+  const float* gpart;
+  const float* lpart;
+  const float* hpart;
+  int nblk;
+  double* gsum;
+  double* lse2sum;
+  double* hsum;
+};
+// rp: NULL, or partials to reduce in an extra block of the same launch.
 hipError_t launch_ec_select(int64_t T, int E, int r, const float* lcol, int32_t* perm_token,
                             int32_t* row_of, int32_t* offsets, int32_t* counts,
-                            int32_t* overflow, int32_t* tile_off, int BM, hipStream_t st);
+                            int32_t* overflow, int32_t* tile_off, int BM, hipStream_t st,
+                            const RoutePartials* rp = nullptr);
 
 // The inputs and outputs of the balance statistics (launch_stats below), for a combine launch to
 // compute them in one extra block beside its own blocks.
