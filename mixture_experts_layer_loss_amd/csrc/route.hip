@@ -27,23 +27,6 @@ constexpr int RT = kRouteTokens;  // 64 tokens per fp32 block
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Insert score v of expert e into a list of KM scores sorted in descending order. Experts arrive
-// in ascending index order and only a strictly larger score moves an entry down, so equal scores
-// stay ordered by index (ties go to the lower expert index). Branch-free; NaN never enters.
-template <int KM>
-__device__ __forceinline__ void topk_insert(float v, int e, float (&tv)[KM], int (&ti)[KM]) {
-#pragma unroll
-  for (int j = KM - 1; j >= 1; --j) {
-    const bool beats_prev = v > tv[j - 1];  // entry j-1 moves down to j
-    const bool beats = v > tv[j];
-    tv[j] = beats_prev ? tv[j - 1] : (beats ? v : tv[j]);
-    ti[j] = beats_prev ? ti[j - 1] : (beats ? e : ti[j]);
-  }
-  const bool top = v > tv[0];
-  tv[0] = top ? v : tv[0];
-  ti[0] = top ? e : ti[0];
-}
-
 // Calls f(std::integral_constant<int, I>) for I = B .. E-1 (register rings need constant slots).
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -134,13 +117,13 @@ __device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, in
       // sorted insertion; this lane's experts arrive in ascending index order, so a strict
       // comparison keeps equal scores in index order
       const float v = b != nullptr ? g + b[e] : g;
-#pragma unroll
-      for (int q = KM - 1; q >= 1; --q) {
+      static_for<1, KM>([&](auto qc) __attribute__((always_inline)) {
+        constexpr int q = KM - decltype(qc)::value;  // KM - 1 down to 1
         const bool up = v > cv[q - 1], here = v > cv[q];
         cv[q] = up ? cv[q - 1] : (here ? v : cv[q]);
         cg[q] = up ? cg[q - 1] : (here ? g : cg[q]);
         ci[q] = up ? ci[q - 1] : (here ? e : ci[q]);
-      }
+      });
       const bool top = v > cv[0];
       cv[0] = top ? v : cv[0];
       cg[0] = top ? g : cg[0];
@@ -153,8 +136,8 @@ __device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, in
     int we[KM];
     float wg[KM];
     float wsum = 0.f;
-#pragma unroll
-    for (int r = 0; r < KM; ++r) {
+    static_for<0, KM>([&](auto rc) __attribute__((always_inline)) {
+      constexpr int r = decltype(rc)::value;
       we[r] = 0;
       wg[r] = 0.f;
       if (r < k) {
@@ -173,25 +156,28 @@ __device__ void route_tokens(float* L, int Ls, int TB, int64_t t0, int64_t T, in
         wg[r] = g;
         wsum += g;  // slot order
         const bool mine = ci[0] == e;  // expert e has one owner
-#pragma unroll
-        for (int q = 0; q + 1 < KM; ++q) {
+        // the shift is spelled with constant indices throughout: a select between neighbouring
+        // elements under a loop index is otherwise folded into a variable index, which sends the
+        // whole list to scratch memory
+        static_for<0, KM - 1>([&](auto qc) __attribute__((always_inline)) {
+          constexpr int q = decltype(qc)::value;
           cv[q] = mine ? cv[q + 1] : cv[q];
           cg[q] = mine ? cg[q + 1] : cg[q];
           ci[q] = mine ? ci[q + 1] : ci[q];
-        }
+        });
         cv[KM - 1] = mine ? -INFINITY : cv[KM - 1];
         ci[KM - 1] = mine ? 0x7fffffff : ci[KM - 1];
       }
-    }
+    });
     const bool renorm = (flags & kRouteRenorm) != 0;
-#pragma unroll
-    for (int r = 0; r < KM; ++r) {
+    static_for<0, KM>([&](auto rc) __attribute__((always_inline)) {
+      constexpr int r = decltype(rc)::value;
       if (r < k && r % G == j && live) {
         topk_idx[t * k + r] = we[r];
         topk_w[t * k + r] = renorm ? wg[r] / wsum : wg[r];
         atomicAdd(&hcnt[we[r]], 1);
       }
-    }
+    });
   }
   if (sig) {  // the probability statistic uses the scores normalised over the experts
     const float inv = 1.f / ssum;
