@@ -28,11 +28,36 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+# the compiler's per-kernel resource remarks (registers, scratch, LDS), kept in a report beside the
+# library; no kernel may use scratch memory (tests/test_abi.py reads the report)
+RESOURCE_FLAGS = ["-Rpass-analysis=kernel-resource-usage", "-fno-caret-diagnostics"]
+REPORT = os.path.join(HERE, "libmoe.resources.json")
+
+
 def _run(cmd):
     proc = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = [l for l in (proc.stdout + proc.stderr).splitlines() if noise not in l]
     return proc.returncode, msgs
+
+
+def _resources(msgs):
+    """Splits the resource remarks off the compiler messages: {function: {field: value}}."""
+    res, other, cur = {}, [], None
+    for line in msgs:
+        if "[-Rpass-analysis=kernel-resource-usage]" not in line:
+            other.append(line)
+            continue
+        body = line.split("remark:", 1)[-1].replace("[-Rpass-analysis=kernel-resource-usage]", "")
+        key, _, val = body.strip().partition(":")
+        if key == "Function Name":
+            cur = res.setdefault(val.strip(), {})
+        elif cur is not None and key:
+            try:
+                cur[key.strip()] = int(val.strip())
+            except ValueError:
+                cur[key.strip()] = val.strip()
+    return res, other
 
 
 def build(verbose: bool = False) -> str:
@@ -46,9 +71,14 @@ def build(verbose: bool = False) -> str:
     t0 = time.time()
     jobs = max(1, min(len(objs), int(os.environ.get("MAX_JOBS", "0")) or (os.cpu_count() or 4)))
     with ThreadPoolExecutor(jobs) as pool:
-        results = list(pool.map(lambda so: _run([hipcc, *FLAGS, *inc, "-c", so[0], "-o", so[1]]),
-                                zip(sources(), objs)))
-    msgs = [m for _, ms in results for m in ms]
+        results = list(pool.map(
+            lambda so: _run([hipcc, *FLAGS, *RESOURCE_FLAGS, *inc, "-c", so[0], "-o", so[1]]),
+            zip(sources(), objs)))
+    resources, msgs = {}, []
+    for _, ms in results:
+        r, other = _resources(ms)
+        resources.update(r)
+        msgs += other
     tmp = LIB + tag
     rc = max(r for r, _ in results)
     if rc == 0:
@@ -62,6 +92,12 @@ def build(verbose: bool = False) -> str:
             os.remove(tmp)
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     os.replace(tmp, LIB)
+    import hashlib
+    import json
+    with open(LIB, "rb") as fh:
+        digest = hashlib.sha256(fh.read()).hexdigest()
+    with open(REPORT, "w") as fh:
+        json.dump({"library_sha256": digest, "functions": resources}, fh, indent=1, sort_keys=True)
     if verbose:
         if msgs:
             print("\n".join(msgs))

@@ -361,3 +361,28 @@ def test_shared_stack_is_checked_by_the_binding():
         with pytest.raises(ValueError, match="Ws_gate must be"):   # S*M not a multiple of M
             fn(x, Wr, Wg, Wg, Wd, *extra, k=k,
                shared=(torch.zeros(12, d), torch.zeros(12, d), torch.zeros(d, 12)))
+
+
+def test_no_kernel_uses_scratch_memory():
+    """The compiler's resource report of the library as built: no kernel or device function keeps
+    anything in scratch memory (a spilled register or an array the compiler could not keep in
+    registers turns into per-lane memory traffic inside the hot loops)."""
+    import hashlib
+    import json
+    import os
+    from mixture_experts_layer_loss_amd import build as B
+    if not os.path.exists(B.REPORT):
+        pytest.skip("no resource report: the library was not built by build.py")
+    rep = json.load(open(B.REPORT))
+    with open(moe.LIB_PATH, "rb") as fh:
+        if hashlib.sha256(fh.read()).hexdigest() != rep["library_sha256"]:
+            pytest.skip("the resource report belongs to another build of the library")
+    funcs = rep["functions"]
+    names = " ".join(funcs)
+    for kernel in ("route_bf16_lds_kernel", "grouped_gemm_persistent_kernel", "wgrad_persistent_kernel",
+                   "combine_kernel", "scan_kernel", "bw_rows_kernel"):
+        assert kernel in names, f"{kernel} missing from the resource report"
+    bad = {n: (f.get("ScratchSize [bytes/lane]"), f.get("VGPRs Spill"))
+           for n, f in funcs.items()
+           if f.get("ScratchSize [bytes/lane]", 0) != 0 or f.get("VGPRs Spill", 0) != 0}
+    assert not bad, f"functions using scratch memory: {bad}"
