@@ -51,6 +51,23 @@ __device__ __forceinline__ void tile_counts(int rows, int BM, int& t_main, int& 
   t64 = (rem > 0 && rem <= 64) ? 1 : 0;
 }
 
+// The shared experts' offsets {0, T} and tile tables (one group of all T rows), written by one
+// thread: the scan and expert-choice kernels of a layer forward write them, so they take no
+// launch of their own.
+__device__ __forceinline__ void write_shared_table(int64_t T, int BM, int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ tile_off) {
+  int c0, c1, c2;
+  tile_counts(static_cast<int>(T), BM, c0, c1, c2);
+  offsets[0] = 0;
+  offsets[1] = static_cast<int32_t>(T);
+  tile_off[0] = 0;
+  tile_off[1] = c0;
+  tile_off[2] = 0;
+  tile_off[3] = c1;
+  tile_off[4] = 0;
+  tile_off[5] = c2;
+}
+
 // Inclusive scan over 256 ints in LDS (Hillis-Steele); every thread of the block must call it.
 __device__ int block_scan_256(int v, int* buf) {
   const int tid = threadIdx.x;
@@ -71,13 +88,15 @@ __device__ int block_scan_256(int v, int* buf) {
 // of the block range; parts are summed, scanned over p in log2(P) rounds and walked again to
 // write the per-block bases, so every sum is taken in a fixed order.
 __global__ __launch_bounds__(1024) void scan_kernel(
-    int64_t /*T*/, int E, int64_t C, int nblk, const int32_t* __restrict__ hist,
+    int64_t T, int E, int64_t C, int nblk, const int32_t* __restrict__ hist,
     const float* __restrict__ gpart, int nblk_g, const float* __restrict__ lpart,
     const float* __restrict__ hpart, int32_t* __restrict__ block_base,
     int32_t* __restrict__ n_out, double* __restrict__ gsum, double* __restrict__ lse2sum,
     double* __restrict__ hsum, int32_t* __restrict__ kept_out, int32_t* __restrict__ overflow,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off, int BM) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off, int BM,
+    int32_t* __restrict__ sh_offsets, int32_t* __restrict__ sh_tile_off) {
   __shared__ int psum[1024];
+  if (sh_offsets != nullptr && threadIdx.x == 0) write_shared_table(T, BM, sh_offsets, sh_tile_off);
   __shared__ double pg[1024];
   __shared__ int wtot[4][4];
   __shared__ double wred[16];
@@ -290,18 +309,7 @@ __global__ __launch_bounds__(256) void schedule_kernel(int groups, const int32_t
 // Tile tables of the shared experts: one group of all T rows.
 __global__ void shared_table_kernel(int64_t T, int BM, int32_t* __restrict__ offsets,
                                     int32_t* __restrict__ tile_off) {
-  if (threadIdx.x == 0) {
-    int c0, c1, c2;
-    tile_counts(static_cast<int>(T), BM, c0, c1, c2);
-    offsets[0] = 0;
-    offsets[1] = static_cast<int32_t>(T);
-    tile_off[0] = 0;
-    tile_off[1] = c0;
-    tile_off[2] = 0;
-    tile_off[3] = c1;
-    tile_off[4] = 0;
-    tile_off[5] = c2;
-  }
+  if (threadIdx.x == 0) write_shared_table(T, BM, offsets, tile_off);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -417,11 +425,15 @@ __global__ __launch_bounds__(1024) void ec_select_kernel(int64_t T, int E, int r
                                                           int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ overflow,
                                                           int32_t* __restrict__ tile_off, int BM,
-                                                          RoutePartials rp) {
+                                                          RoutePartials rp,
+                                                          int32_t* __restrict__ sh_offsets,
+                                                          int32_t* __restrict__ sh_tile_off) {
   __shared__ __attribute__((aligned(16))) int hist[16][256];
   __shared__ int wsum[17];
   __shared__ int sel[2];
   __shared__ double wred[16];
+  if (sh_offsets != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
+    write_shared_table(T, BM, sh_offsets, sh_tile_off);
   if (static_cast<int>(blockIdx.x) == E) {  // (hist is free in this block: pg in its 16 KB)
     reduce_route_partials(E, rp.nblk, rp.gpart, rp.lpart, rp.hpart, rp.gsum, rp.lse2sum, rp.hsum,
                           reinterpret_cast<double*>(&hist[0][0]), wred);
@@ -531,12 +543,12 @@ __global__ __launch_bounds__(1024) void ec_select_kernel(int64_t T, int E, int r
 hipError_t launch_ec_select(int64_t T, int E, int r, const float* lcol, int32_t* perm_token,
                             int32_t* row_of, int32_t* offsets, int32_t* counts,
                             int32_t* overflow, int32_t* tile_off, int BM, hipStream_t st,
-                            const RoutePartials* rp) {
+                            const RoutePartials* rp, int32_t* sh_offsets, int32_t* sh_tile_off) {
   const RoutePartials none{};
   const bool red = rp != nullptr && rp->gpart != nullptr;
   hipLaunchKernelGGL(ec_select_kernel, dim3(E + (red ? 1 : 0)), dim3(1024), 0, st, T, E, r, lcol,
                      perm_token, row_of, offsets, counts, overflow, tile_off, BM,
-                     red ? *rp : none);
+                     red ? *rp : none, sh_offsets, sh_tile_off);
   return hipGetLastError();
 }
 
@@ -558,10 +570,11 @@ hipError_t launch_scan(int64_t T, int E, int64_t C, int nblk, const int32_t* his
                        const float* gpart, const float* lpart, const float* hpart,
                        int32_t* block_base, int32_t* n_out, double* gsum, double* lse2sum,
                        double* hsum, int32_t* kept, int32_t* overflow, int32_t* offsets,
-                       int32_t* tile_off, int BM, hipStream_t st) {
+                       int32_t* tile_off, int BM, hipStream_t st, int32_t* sh_offsets,
+                       int32_t* sh_tile_off) {
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, T, E, C, nblk, hist, gpart, nblk,
                      lpart, hpart, block_base, n_out, gsum, lse2sum, hsum, kept, overflow, offsets,
-                     tile_off, BM);
+                     tile_off, BM, sh_offsets, sh_tile_off);
   return hipGetLastError();
 }
 

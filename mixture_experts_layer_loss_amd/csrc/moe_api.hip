@@ -632,6 +632,9 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
   const int64_t max_tiles = cdiv(routed_rows(s), BM) + s->E;
 
   const bool want_stats = f || P || aux || z || diag || b_new;
+  // the shared experts' tile tables come from the selection launch (scan or expert choice)
+  int32_t* sh_off = s->S > 0 ? p.sh_offsets : nullptr;
+  int32_t* sh_tab = s->S > 0 ? p.sh_tile_off : nullptr;
   StageMarks marks;
   marks.mark(0, hs);
   hipError_t e = hipSuccess;
@@ -647,11 +650,12 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
     const RoutePartials rp{p.r.gpart, p.r.lpart, p.r.hpart, nblk, p.gsum, p.lse2sum, p.hsum};
     if (e == hipSuccess)
       e = launch_ec_select(s->T, s->E, static_cast<int>(ec_tokens(s)), p.cols, p.perm_token,
-                           p.row_of, p.offsets, n, ovf, p.tile_off, BM, hs, &rp);
+                           p.row_of, p.offsets, n, ovf, p.tile_off, BM, hs, &rp, sh_off, sh_tab);
   } else {
     if (e == hipSuccess)
       e = launch_scan(s->T, s->E, C, nblk, p.r.hist, p.r.gpart, p.r.lpart, p.r.hpart, p.block_base,
-                      n, p.gsum, p.lse2sum, p.hsum, p.kept, ovf, p.offsets, p.tile_off, BM, hs);
+                      n, p.gsum, p.lse2sum, p.hsum, p.kept, ovf, p.offsets, p.tile_off, BM, hs,
+                      sh_off, sh_tab);
     // placement only: the gate/up GEMM gathers its rows from x through perm_token
     if (e == hipSuccess)
       e = launch_scatter(s->T, s->d, s->E, s->k, C, eb, x, idx, route_block_tokens(s->dtype, s->E, s->T),
@@ -664,9 +668,7 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
   const int SM = s->S * s->M;
   const int64_t sh_tiles = cdiv(s->T, BM);
   if (e == hipSuccess && fold_shared) {
-    e = launch_shared_table(s->T, BM, p.sh_offsets, p.sh_tile_off, hs);
-    if (e == hipSuccess)
-      e = launch_gemm_up_shared_bf16(s->E, s->d, s->M, x, p.perm_token, p.offsets, p.tile_off,
+    e = launch_gemm_up_shared_bf16(s->E, s->d, s->M, x, p.perm_token, p.offsets, p.tile_off,
                                      max_tiles, W_gate, W_up, p.h, s->T, SM, p.sh_offsets,
                                      p.sh_tile_off, sh_tiles, Ws_gate, Ws_up, p.h_sh, hs);
     marks.mark(3, hs);
@@ -689,11 +691,10 @@ moe_status moe_layer_forward(const moe_shape* s, const void* x, const void* W_r,
     marks.mark(4, hs);
   }
   if (e == hipSuccess && s->S > 0 && !fold_shared) {
-    e = launch_shared_table(s->T, BM, p.sh_offsets, p.sh_tile_off, hs);
-    if (e == hipSuccess && saved != nullptr)
+    if (saved != nullptr)
       e = launch_gemm_up_save_bf16(1, s->d, SM, x, nullptr, p.sh_offsets, p.sh_tile_off, sh_tiles,
                                    Ws_gate, Ws_up, p.h_sh, sv.Gs, sv.Us, hs, s->T);
-    else if (e == hipSuccess)
+    else
       e = launch_gemm_up(s->dtype, 1, s->d, SM, x, nullptr, p.sh_offsets, p.sh_tile_off, sh_tiles,
                          Ws_gate, Ws_up, p.h_sh, hs, s->T);
     if (e == hipSuccess)

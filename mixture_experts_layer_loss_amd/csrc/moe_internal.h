@@ -68,11 +68,14 @@ hipError_t launch_count(int64_t T, int E, int k, const int32_t* topk_idx, int32_
 //   block_base [nblk, E]; gsum/lse2sum/hsum/gpart/lpart/hpart may be NULL (dispatch-only use).
 //   tile_off [3 (E+1)]: grouped-GEMM tile tables (exclusive prefixes over groups) of 256-row,
 //   128-row and 64-row tiles when BM = 256, else of BM-row tiles and two zero tables.
+//   sh_offsets [2], sh_tile_off [6]: NULL, or where to write the shared experts' offsets and tile
+//   tables as launch_shared_table does.
 hipError_t launch_scan(int64_t T, int E, int64_t C, int nblk, const int32_t* hist,
                        const float* gpart, const float* lpart, const float* hpart,
                        int32_t* block_base, int32_t* n_out, double* gsum, double* lse2sum,
                        double* hsum, int32_t* kept, int32_t* overflow, int32_t* offsets,
-                       int32_t* tile_off, int BM, hipStream_t st);
+                       int32_t* tile_off, int BM, hipStream_t st, int32_t* sh_offsets = nullptr,
+                       int32_t* sh_tile_off = nullptr);
 
 // Places assignments: inv_perm, perm_token and (when x_perm != NULL) the x row copies.
 // block_base holds one row per histogram block of hist_block_tokens tokens (a divisor of
@@ -97,11 +100,13 @@ struct RoutePartials {
   double* lse2sum;
   double* hsum;
 };
-// rp: NULL, or partials to reduce in an extra block of the same launch.
+// rp: NULL, or partials to reduce in an extra block of the same launch. sh_offsets, sh_tile_off:
+// as for launch_scan.
 hipError_t launch_ec_select(int64_t T, int E, int r, const float* lcol, int32_t* perm_token,
                             int32_t* row_of, int32_t* offsets, int32_t* counts,
                             int32_t* overflow, int32_t* tile_off, int BM, hipStream_t st,
-                            const RoutePartials* rp = nullptr);
+                            const RoutePartials* rp = nullptr, int32_t* sh_offsets = nullptr,
+                            int32_t* sh_tile_off = nullptr);
 
 // The inputs and outputs of the balance statistics (launch_stats below), for a combine launch to
 // compute them in one extra block beside its own blocks.
