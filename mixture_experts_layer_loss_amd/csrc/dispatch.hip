@@ -441,14 +441,33 @@ __global__ __launch_bounds__(1024) void ec_select_kernel(int64_t T, int E, int r
   }
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* col = lcol + static_cast<int64_t>(e) * T;
+  // up to 1024 KPT tokens (one chunk of the final walk below), each thread's KPT consecutive keys
+  // are read once and kept in registers through the four histogram passes and that walk
+  constexpr int KPT = 8;
+  const bool in_regs = T <= 1024 * KPT;
+  uint32_t rkey[KPT];
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int64_t t = static_cast<int64_t>(tid) * KPT + i;
+      rkey[i] = t < T ? order_key(col[t]) : 0u;
+    }
+  }
   uint32_t prefix = 0, pmask = 0;
   int remaining = r;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = tid; i < 16 * 256; i += 1024) hist[i >> 8][i & 255] = 0;
     __syncthreads();
-    for (int64_t t = tid; t < T; t += 1024) {
-      const uint32_t key = order_key(col[t]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1);
+    if (in_regs) {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i)
+        if (static_cast<int64_t>(tid) * KPT + i < T && (rkey[i] & pmask) == prefix)
+          atomicAdd(&hist[wave][(rkey[i] >> shift) & 255u], 1);
+    } else {
+      for (int64_t t = tid; t < T; t += 1024) {
+        const uint32_t key = order_key(col[t]);
+        if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1);
+      }
     }
     __syncthreads();
     // thread j < 256 holds bin 255 - j; the keys in the bins above it are its exclusive prefix
@@ -477,7 +496,6 @@ __global__ __launch_bounds__(1024) void ec_select_kernel(int64_t T, int E, int r
     __syncthreads();
   }
   // prefix is the threshold key; `remaining` tokens equal to it are taken, lowest indices first
-  constexpr int KPT = 8;
   int eq_carry = 0, row_carry = 0;
   for (int64_t base = 0; base < T; base += 1024 * KPT) {
     const int64_t t0 = base + static_cast<int64_t>(tid) * KPT;
@@ -485,7 +503,7 @@ __global__ __launch_bounds__(1024) void ec_select_kernel(int64_t T, int E, int r
     int neq = 0;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      key[i] = t0 + i < T ? order_key(col[t0 + i]) : 0u;
+      key[i] = in_regs ? rkey[i] : (t0 + i < T ? order_key(col[t0 + i]) : 0u);
       neq += (t0 + i < T && key[i] == prefix) ? 1 : 0;
     }
     int eq_tot = 0;
