@@ -312,6 +312,16 @@ __global__ void shared_table_kernel(int64_t T, int BM, int32_t* __restrict__ off
   if (threadIdx.x == 0) write_shared_table(T, BM, offsets, tile_off);
 }
 
+// Offsets of ks row ranges over T rows, cut at multiples of 64 rows: [0, c, 2c, .., T] with
+// c = 64 ceil(T / (64 ks)) (a range may be empty).
+__global__ void row_splits_kernel(int64_t T, int ks, int32_t* __restrict__ offsets) {
+  const int i = threadIdx.x;
+  if (i <= ks) {
+    const int64_t c = ((T + 64 * ks - 1) / (64 * ks)) * 64;
+    offsets[i] = static_cast<int32_t>(i == ks ? T : (i * c < T ? i * c : T));
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // Expert-choice selection ("深入理解 MoE (混合专家模型)：稀疏激活与高效扩展" §9.2: every expert
 // picks its top tokens by its score column; "MoE：条件计算与路由" §路由机制的演进): one block per
@@ -567,6 +577,11 @@ hipError_t launch_ec_select(int64_t T, int E, int r, const float* lcol, int32_t*
   hipLaunchKernelGGL(ec_select_kernel, dim3(E + (red ? 1 : 0)), dim3(1024), 0, st, T, E, r, lcol,
                      perm_token, row_of, offsets, counts, overflow, tile_off, BM,
                      red ? *rp : none, sh_offsets, sh_tile_off);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_splits(int64_t T, int ks, int32_t* offsets, hipStream_t st) {
+  hipLaunchKernelGGL(row_splits_kernel, dim3(1), dim3(64), 0, st, T, ks, offsets);
   return hipGetLastError();
 }
 

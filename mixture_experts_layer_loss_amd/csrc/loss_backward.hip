@@ -181,6 +181,13 @@ hipError_t launch_kmajor(int64_t M, int64_t N, int64_t K, int KS, const float* A
 
 }  // namespace
 
+hipError_t launch_sum_ranges(int64_t count, int KS, const float* P, float* C, hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sum_ranges_kernel, dim3(static_cast<unsigned>(cdiv(count, 256))), dim3(256),
+                     0, st, count, KS, P, C);
+  return hipGetLastError();
+}
+
 hipError_t launch_loss_grad(int64_t T, int E, int sigmoid, const float* lcol, const float* scol,
                             const int32_t* n, double fden, float lambda, float z_coef, float* dl,
                             float* dlT, hipStream_t st) {

@@ -275,7 +275,25 @@ struct LayerBackwardPlan {
   void *dGU, *wh, *dyr, *xr;     // routed experts
   float* part_dx;                // [2][E][128][d]: the dx-row product's split remainder tiles
   void *dGUs, *hsb;              // shared experts: [dGs | dUs] rows and h rows (bf16)
+  // the shared experts' weight gradients over ks_sh row ranges of the T rows (bf16 layers): the
+  // range offsets, their k-slice table and the ranges' fp32 partials [ks_sh][S M][d]
+  int ks_sh;
+  int32_t *sh_split_off, *sh_split_kt;
+  float* sh_wpart;
 };
+
+// Row ranges of the shared experts' weight gradients. Each of the three products has
+// ceil(S M / 256) ceil(d / 256) output tiles over all T rows; when those tiles fill under half of
+// the chip's 256 compute units, the rows are cut into ks_sh ranges (at least 256 rows each) whose
+// partial products run side by side and are summed in range order.
+int shared_wgrad_splits(const moe_shape* s) {
+  if (s->S <= 0 || s->dtype != MOE_BF16) return 1;
+  const int64_t tiles = cdiv(static_cast<int64_t>(s->S) * s->M, 256) * cdiv(s->d, 256);
+  int64_t ks = 256 / (tiles > 0 ? tiles : 1);
+  ks = ks < 4 ? ks : 4;
+  ks = ks < s->T / 256 ? ks : s->T / 256;
+  return ks > 1 ? static_cast<int>(ks) : 1;
+}
 LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
   LayerBackwardPlan p;
   p.f = plan_layer(c, s);
@@ -300,6 +318,9 @@ LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
   p.dGU = p.wh = p.dyr = p.xr = nullptr;
   p.dGUs = p.hsb = nullptr;
   p.part_dx = nullptr;
+  p.ks_sh = 1;
+  p.sh_split_off = p.sh_split_kt = nullptr;
+  p.sh_wpart = nullptr;
   if (mfma) {
     p.dGU = c.take<bf16_t>(R * 2 * M);
     p.wh = c.take<bf16_t>(R * M);
@@ -324,6 +345,12 @@ LayerBackwardPlan plan_layer_backward(Carve& c, const moe_shape* s) {
     if (mfma) {
       p.dGUs = c.take<bf16_t>(T * 2 * SM);
       p.hsb = c.take<bf16_t>(T * SM);
+    }
+    p.ks_sh = shared_wgrad_splits(s);
+    if (p.ks_sh > 1) {
+      p.sh_split_off = c.take<int32_t>(p.ks_sh + 1);
+      p.sh_split_kt = c.take<int32_t>(3 * (p.ks_sh + 1));
+      p.sh_wpart = c.take<float>(static_cast<size_t>(p.ks_sh) * SM * d);
     }
   } else {
     p.Gs = p.Us = nullptr;
@@ -964,16 +991,25 @@ moe_status moe_layer_backward(const moe_shape* s, const void* x, const void* W_r
       if (e == hipSuccess)  // dxs = [dGs dUs] [Ws_gate; Ws_up] over K = 2 SM
         e = launch_gemm_kn_bf16(1, p.dGUs, nullptr, f.sh_offsets, f.sh_tile_off, sh_tiles, Ws_gate,
                                 Ws_up, 0, d, 2 * SM, p.dxs, hs);
-      // the weight gradients over all T rows, read in place: dy, h, [dGs | dUs] and x
-      const int32_t* so = f.sh_offsets;
-      if (e == hipSuccess)
-        e = launch_gemm_wgrad_bf16(dy, d, p.hsb, SM, s->T, so, p.sh_tile64, 1, d, SM, dWs_down, hs);
-      if (e == hipSuccess)
-        e = launch_gemm_wgrad_bf16(dGUs, 2 * SM, x, d, s->T, so, p.sh_tile64, 1, SM, d, dWs_gate,
-                                   hs);
-      if (e == hipSuccess)
-        e = launch_gemm_wgrad_bf16(dGUs + SM, 2 * SM, x, d, s->T, so, p.sh_tile64, 1, SM, d,
-                                   dWs_up, hs);
+      // the weight gradients over all T rows, read in place: dy, h, [dGs | dUs] and x; over
+      // ks_sh row ranges when one range's tiles would leave most compute units idle, each range
+      // a group of the persistent product writing its own partial, summed in range order
+      const int ks = p.ks_sh;
+      const int32_t* so = ks > 1 ? p.sh_split_off : f.sh_offsets;
+      const int32_t* skt = ks > 1 ? p.sh_split_kt : p.sh_tile64;
+      if (e == hipSuccess && ks > 1) e = launch_row_splits(s->T, ks, p.sh_split_off, hs);
+      if (e == hipSuccess && ks > 1) e = launch_schedule(ks, p.sh_split_off, p.sh_split_kt, 64, hs, 2);
+      auto sh_wgrad = [&](const void* A, int lda, const void* B, int ldb, int Ma, int Nb,
+                          float* out) {
+        hipError_t r = launch_gemm_wgrad_bf16(A, lda, B, ldb, s->T, so, skt, ks, Ma, Nb,
+                                              ks > 1 ? p.sh_wpart : out, hs);
+        if (r == hipSuccess && ks > 1)
+          r = launch_sum_ranges(static_cast<int64_t>(Ma) * Nb, ks, p.sh_wpart, out, hs);
+        return r;
+      };
+      if (e == hipSuccess) e = sh_wgrad(dy, d, p.hsb, SM, d, SM, dWs_down);
+      if (e == hipSuccess) e = sh_wgrad(dGUs, 2 * SM, x, d, SM, d, dWs_gate);
+      if (e == hipSuccess) e = sh_wgrad(dGUs + SM, 2 * SM, x, d, SM, d, dWs_up);
     } else {
       if (e == hipSuccess)
         e = launch_nn_gemm(s->dtype, s->dtype, false, dy, nullptr, nullptr, f.sh_offsets,

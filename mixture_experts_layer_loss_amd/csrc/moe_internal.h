@@ -252,6 +252,12 @@ hipError_t launch_gemm_wgrad_bf16(const void* A, int lda, const void* B, int ldb
                                   const int32_t* offsets, const int32_t* kt, int groups, int Ma,
                                   int Nb, float* C, hipStream_t st);
 
+// Offsets [ks + 1] of ks row ranges over T rows, cut at multiples of 64 rows (ks <= 63).
+hipError_t launch_row_splits(int64_t T, int ks, int32_t* offsets, hipStream_t st);
+
+// C[i] = sum over s = 0..KS-1, in that order, of P[s count + i].
+hipError_t launch_sum_ranges(int64_t count, int KS, const float* P, float* C, hipStream_t st);
+
 // Tile table of the shared experts (one group of all T rows).
 hipError_t launch_shared_table(int64_t T, int BM, int32_t* offsets, int32_t* tile_off,
                                hipStream_t st);

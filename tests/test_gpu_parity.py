@@ -286,6 +286,9 @@ LAYER_BW_CASES = [
     ("mixtral_8x7b", dict(T=90, d=64, M=64, E=4, k=2, c=0.01)),   # C = 1: nearly all dropped
     # dx rows over K = 2M = 8320 with >= 512 rows per expert: remainder tiles in two K halves
     ("mixtral_8x7b", dict(T=1100, d=128, M=4160, E=4, k=2)),
+    # shared experts' weight gradients over four row ranges (two output tiles per product; the
+    # last range ragged), summed in range order
+    ("deepseekmoe_16b", dict(T=1100, d=128, M=136, c=1.0)),
     ("tiny_fp32", dict(T=70, E=1, k=1)),
     ("tiny_fp32", dict(T=90, E=4, k=2, c=0.01)),
     ("tiny_fp32", dict(T=120, M=96, S=2, c=1.0)),                         # fp32 shared experts
